@@ -1,0 +1,277 @@
+"""ctypes wrapper over the CPU oracle (liboracle.so, built from fp8_oracle.c).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the tests, the smoke check and the
+benchmark's CPU-baseline leg import this module. It takes and returns numpy
+arrays; it never touches torch, the GPU or the HIP library.
+
+Format codes: 0 = E4M3 (OCP e4m3fn), 1 = E5M2 (OCP), 2 = E4M3 FNUZ, 3 = E5M2 FNUZ.
+bf16 tensors are passed as uint16 bit patterns; FP8 tensors as uint8 codes.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+E4M3, E5M2, E4M3_FNUZ, E5M2_FNUZ = 0, 1, 2, 3
+FORMATS = (E4M3, E5M2, E4M3_FNUZ, E5M2_FNUZ)
+AMAX_MOST_RECENT, AMAX_MAX = 0, 1
+AXIS_TENSOR, AXIS_ROW, AXIS_COL = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build():
+    """Compile liboracle.so with make (gcc, OpenMP)."""
+    subprocess.run(["make", "-s", "-C", _HERE], check=True)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    F = ctypes.c_float
+    sig = {
+        "orc_fmt_info": (I, [I, P, P, P, P]),
+        "orc_decode": (ctypes.c_double, [I, ctypes.c_uint8]),
+        "orc_encode": (ctypes.c_uint8, [I, F]),
+        "orc_encode_array": (None, [I, P, I64, P]),
+        "orc_decode_array": (None, [I, P, I64, P]),
+        "orc_scale_current": (F, [I, F, I]),
+        "orc_reciprocal": (F, [F]),
+        "orc_quantize_value": (ctypes.c_uint8, [I, ctypes.c_uint16, F]),
+        "orc_amax": (None, [P, I64, I64, I64, I, P]),
+        "orc_quantize_row": (None, [P, I64, I64, I64, I, I, P, I64, P, P]),
+        "orc_quantize_col": (None, [P, I64, I64, I64, I, I, P, I64, P, P]),
+        "orc_quantize_tensor_scaled": (None, [P, I64, I64, I64, I, F, P, I64, P, P]),
+        "orc_quantize_tensor_current": (None, [P, I64, I64, I64, I, I, P, I64, P, P]),
+        "orc_delayed_update": (None, [P, P, P, I64, I, I, I, I, P, P]),
+        "orc_gemm": (None, [P, I, I64, P, I, I64, I64, I64, I64, P, I, P, I, P, P, P, I64, P]),
+        "orc_gemm_entries": (None, [P, I, I64, P, I, I64, I64, P, I, P, I, P, P, I64, P, P]),
+        "orc_grouped_gemm_entries": (None, [P, I, I64, P, I, I64, I64, P, I, I64, I64, P, P,
+                                            P, P, I64, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _vec_mode(scale, rows):
+    """1 if scale holds one value per row, 0 if it is a single value."""
+    if scale.size == rows:
+        return 1
+    if scale.size == 1:
+        return 0
+    raise ValueError(f"scale has {scale.size} entries for {rows} rows")
+
+
+def fmt_info(fmt):
+    """(fmax, ebits, mbits, bias) of an encoding."""
+    fmax = ctypes.c_double()
+    e, m, b = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    if _load().orc_fmt_info(fmt, ctypes.byref(fmax), ctypes.byref(e), ctypes.byref(m), ctypes.byref(b)):
+        raise ValueError(f"unknown format {fmt}")
+    return fmax.value, e.value, m.value, b.value
+
+
+def decode(fmt, codes):
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    _load().orc_decode_array(fmt, _p(codes), codes.size, _p(out))
+    return out
+
+
+def decode_table(fmt):
+    return decode(fmt, np.arange(256, dtype=np.uint8))
+
+
+def encode(fmt, values_f32):
+    v = _c(values_f32, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().orc_encode_array(fmt, _p(v), v.size, _p(out))
+    return out
+
+
+def scale_current(fmt, amax, margin=0):
+    return np.float32(_load().orc_scale_current(fmt, float(np.float32(amax)), margin))
+
+
+def reciprocal(s):
+    return np.float32(_load().orc_reciprocal(float(np.float32(s))))
+
+
+def quantize_value(fmt, x_bf16_bits, s):
+    return _load().orc_quantize_value(fmt, int(x_bf16_bits), float(np.float32(s)))
+
+
+def amax(x_bf16, axis):
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    n = {AXIS_TENSOR: 1, AXIS_ROW: rows, AXIS_COL: cols}[axis]
+    out = np.empty(n, np.float32)
+    _load().orc_amax(_p(x), rows, cols, cols, axis, _p(out))
+    return out
+
+
+def quantize_row(x_bf16, fmt, margin=0):
+    """Per-row scales: returns (q [rows x cols] uint8, scale_inv [rows], amax [rows])."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    si = np.empty(rows, np.float32)
+    am = np.empty(rows, np.float32)
+    _load().orc_quantize_row(_p(x), rows, cols, cols, fmt, margin, _p(q), cols, _p(si), _p(am))
+    return q, si, am
+
+
+def quantize_col(x_bf16, fmt, margin=0):
+    """Per-column scales, transposed output: returns (qt [cols x rows], scale_inv [cols], amax [cols])."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    qt = np.empty((cols, rows), np.uint8)
+    si = np.empty(cols, np.float32)
+    am = np.empty(cols, np.float32)
+    _load().orc_quantize_col(_p(x), rows, cols, cols, fmt, margin, _p(qt), rows, _p(si), _p(am))
+    return qt, si, am
+
+
+def quantize_tensor_scaled(x_bf16, fmt, s, amax_in=0.0):
+    """Given scale s: returns (q, scale_inv_used, amax_acc) with amax_acc = max(amax_in, amax(x))."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    si = np.empty(1, np.float32)
+    am = np.array([amax_in], np.float32)
+    _load().orc_quantize_tensor_scaled(_p(x), rows, cols, cols, fmt, float(np.float32(s)), _p(q), cols,
+                                       _p(si), _p(am))
+    return q, si[0], am[0]
+
+
+def quantize_tensor_current(x_bf16, fmt, margin=0):
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    si = np.empty(1, np.float32)
+    am = np.empty(1, np.float32)
+    _load().orc_quantize_tensor_current(_p(x), rows, cols, cols, fmt, margin, _p(q), cols, _p(si), _p(am))
+    return q, si[0], am[0]
+
+
+class DelayedState:
+    """n delayed-scaling states in the layout the library uses: history [n x L]
+    ring with a shared head, scale[n], scale_inv[n], cur_amax[n]."""
+
+    def __init__(self, n, L):
+        self.n, self.L = n, L
+        self.history = np.zeros((n, L), np.float32)
+        self.head = np.zeros(1, np.int32)
+        self.scale = np.ones(n, np.float32)
+        self.scale_inv = np.ones(n, np.float32)
+        self.cur_amax = np.zeros(n, np.float32)
+
+    def update(self, algo, margin, fmt):
+        _load().orc_delayed_update(_p(self.cur_amax), _p(self.history), _p(self.head), self.n, self.L, algo,
+                                   margin, fmt, _p(self.scale), _p(self.scale_inv))
+
+
+def gemm(a, fa, b, fb, a_scale, b_scale, with_bound=True):
+    """Y = (A B^T) * sa * sb in fp64; a [m x k], b [n x k] uint8 codes; scales are
+    fp32 vectors ([m] / [n]) or single values. Returns (y, bound)."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    m, k = a.shape
+    n, k2 = b.shape
+    assert k == k2
+    sa = _c(np.atleast_1d(a_scale), np.float32)
+    sb = _c(np.atleast_1d(b_scale), np.float32)
+    a_vec = _vec_mode(sa, m)
+    b_vec = _vec_mode(sb, n)
+    ad = np.empty(max(m * k, 1), np.float64)
+    bd = np.empty(max(n * k, 1), np.float64)
+    y = np.empty((m, n), np.float64)
+    bound = np.empty((m, n), np.float64) if with_bound else None
+    _load().orc_gemm(_p(a), fa, k, _p(b), fb, k, m, n, k, _p(sa), a_vec, _p(sb), b_vec, _p(ad), _p(bd),
+                     _p(y), n, _p(bound))
+    return y, bound
+
+
+def gemm_entries(a, fa, b, fb, a_scale, b_scale, ii, jj):
+    """Selected outputs Y[ii[e], jj[e]] of the dense product; returns (y, bound)."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    m, k = a.shape
+    n = b.shape[0]
+    sa = _c(np.atleast_1d(a_scale), np.float32)
+    sb = _c(np.atleast_1d(b_scale), np.float32)
+    a_vec = _vec_mode(sa, m)
+    b_vec = _vec_mode(sb, n)
+    ii = _c(ii, np.int64)
+    jj = _c(jj, np.int64)
+    y = np.empty(ii.size, np.float64)
+    bound = np.empty(ii.size, np.float64)
+    _load().orc_gemm_entries(_p(a), fa, k, _p(b), fb, k, k, _p(sa), a_vec, _p(sb), b_vec, _p(ii), _p(jj),
+                             ii.size, _p(y), _p(bound))
+    return y, bound
+
+
+def grouped_gemm_entries(a, fa, b, fb, offsets, a_scale, b_scale, ii, jj):
+    """Selected outputs of the grouped product. a [total_m x k], b [g x n x k],
+    offsets int64 [g+1], a_scale [total_m], b_scale [g x n]."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    g, n, k = b.shape
+    offsets = _c(offsets, np.int64)
+    sa = _c(a_scale, np.float32)
+    sb = _c(b_scale, np.float32).reshape(-1)
+    ii = _c(ii, np.int64)
+    jj = _c(jj, np.int64)
+    y = np.empty(ii.size, np.float64)
+    bound = np.empty(ii.size, np.float64)
+    _load().orc_grouped_gemm_entries(_p(a), fa, k, _p(b), fb, k, n * k, _p(offsets), g, n, k, _p(sa), _p(sb),
+                                     _p(ii), _p(jj), ii.size, _p(y), _p(bound))
+    return y, bound
+
+
+def grouped_gemm(a, fa, b, fb, offsets, a_scale, b_scale):
+    """Whole grouped product as the per-group dense oracle: rows of group g are
+    A[offsets[g]:offsets[g+1]] times B_g^T with scales a_scale[rows], b_scale[g]."""
+    a = _c(a, np.uint8)
+    g, n, k = b.shape
+    total_m = a.shape[0]
+    y = np.full((total_m, n), np.nan)
+    bound = np.full((total_m, n), np.nan)
+    for gg in range(g):
+        lo, hi = int(offsets[gg]), int(offsets[gg + 1])
+        if hi > lo:
+            y[lo:hi], bound[lo:hi] = gemm(a[lo:hi], fa, b[gg], fb, a_scale[lo:hi], b_scale[gg])
+    return y, bound
+
+
+def gemm_within_bound(gpu, y, bound, out_bf16=True):
+    """The acceptance rule: |gpu - y| <= 1e-3 * bound + 2^-8 |y| (the last term only
+    for bf16 output). NaN matches NaN. Returns a boolean array."""
+    gpu = np.asarray(gpu, np.float64)
+    tol = 1e-3 * bound + (2.0 ** -8 * np.abs(y) if out_bf16 else 0.0)
+    ok = np.abs(gpu - y) <= tol
+    both_nan = np.isnan(gpu) & np.isnan(y)
+    same_inf = np.isinf(gpu) & np.isinf(y) & (np.sign(gpu) == np.sign(y))
+    return ok | both_nan | same_inf
