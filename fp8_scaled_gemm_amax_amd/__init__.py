@@ -1,0 +1,190 @@
+"""Python binding of libfp8amax (the MI355X FP8 linear-layer library).
+
+Thin ctypes marshalling over the C ABI declared in include/fp8amax.h: the
+functions below carry the same names and arguments; torch tensors supply
+device memory (data_ptr, strides) and the stream (torch's current stream).
+Every step of the computation runs in the library's HIP kernels. If the
+library is missing or fails to load, importing this package raises.
+
+bf16 inputs are torch.bfloat16 tensors; FP8 codes are any 1-byte tensors
+(torch.uint8 or a torch.float8_* dtype); scales and amax are float32.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "E4M3", "E5M2", "E4M3_FNUZ", "E5M2_FNUZ", "AXIS_TENSOR", "AXIS_ROW", "AXIS_COL",
+    "AMAX_MOST_RECENT", "AMAX_MAX", "SCALE_TENSOR", "SCALE_VECTOR", "OUT_BF16", "OUT_F32",
+    "Fp8Error", "LIB_PATH", "lib", "fp8_query_device", "fp8_status_string", "fp8_amax",
+    "fp8_quantize_tensor", "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update",
+    "fp8_gemm_scaled", "fp8_grouped_gemm_scaled", "EXPORTED_SYMBOLS",
+]
+
+E4M3, E5M2, E4M3_FNUZ, E5M2_FNUZ = 0, 1, 2, 3
+AXIS_TENSOR, AXIS_ROW, AXIS_COL = 0, 1, 2
+AMAX_MOST_RECENT, AMAX_MAX = 0, 1
+SCALE_TENSOR, SCALE_VECTOR = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "fp8_query_device", "fp8_status_string", "fp8_last_error", "fp8_amax", "fp8_quantize_tensor",
+    "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update", "fp8_gemm_scaled",
+    "fp8_grouped_gemm_scaled",
+)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8amax.so")
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class _DeviceInfo(ctypes.Structure):
+    _fields_ = [("arch", ctypes.c_char * 64), ("is_gfx950", ctypes.c_int32), ("native_e4m3", ctypes.c_int32),
+                ("native_e5m2", ctypes.c_int32), ("compute_units", ctypes.c_int32),
+                ("lds_bytes_per_block", ctypes.c_int32), ("global_mem_bytes", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (or make -C "
+                          f"{os.path.dirname(LIB_PATH)}) first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    sigs = {
+        "fp8_query_device": [I, ctypes.POINTER(_DeviceInfo)],
+        "fp8_amax": [P, I64, I64, I64, I, P, P],
+        "fp8_quantize_tensor": [P, I64, I64, I64, I, I32, P, P, I64, P, P, P],
+        "fp8_quantize_row": [P, I64, I64, I64, I, I32, P, I64, P, P, P, P],
+        "fp8_quantize_col": [P, I64, I64, I64, I, I32, P, I64, P, P, I32, P],
+        "fp8_delayed_scale_update": [P, P, P, I64, I32, I, I32, I, P, P, P],
+        "fp8_gemm_scaled": [P, I, I64, P, I, I64, I64, I64, I64, P, I, P, I, P, I, I64, P],
+        "fp8_grouped_gemm_scaled": [P, I, I64, P, I, I64, I64, P, I32, I64, I64, I64, P, P, P, I, I64, P],
+    }
+    for name, args in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = I
+    L.fp8_status_string.argtypes = [I]
+    L.fp8_status_string.restype = ctypes.c_char_p
+    L.fp8_last_error.argtypes = []
+    L.fp8_last_error.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _status_name(status):
+    return lib.fp8_status_string(status).decode()
+
+
+def fp8_status_string(status):
+    return _status_name(status)
+
+
+def _check(status):
+    if status != 0:
+        raise Fp8Error(status, lib.fp8_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t=None):
+    dev = t.device if t is not None and t.is_cuda else None
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _mat(t, name, elem_size=None):
+    """(rows, cols, ld) of a 2-D row-major tensor with unit column stride."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise ValueError(f"{name} must have {elem_size}-byte elements, got {t.dtype}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+    return t.shape[0], t.shape[1], max(t.stride(0), t.shape[1], 1)
+
+
+def _bf16(t, name="x"):
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be torch.bfloat16, got {t.dtype}")
+    return _mat(t, name, 2)
+
+
+def fp8_query_device(device=0):
+    """Properties of HIP device `device` as a dict."""
+    info = _DeviceInfo()
+    _check(lib.fp8_query_device(int(device), ctypes.byref(info)))
+    return {"arch": info.arch.decode(), "is_gfx950": bool(info.is_gfx950), "native_e4m3": info.native_e4m3,
+            "native_e5m2": info.native_e5m2, "compute_units": info.compute_units,
+            "lds_bytes_per_block": info.lds_bytes_per_block, "global_mem_bytes": info.global_mem_bytes}
+
+
+def fp8_amax(x, axis, amax_out):
+    rows, cols, ldx = _bf16(x)
+    _check(lib.fp8_amax(_ptr(x), rows, cols, ldx, axis, _ptr(amax_out), _stream(x)))
+
+
+def fp8_quantize_tensor(x, fmt, margin, scale, q, scale_inv_out, amax_out):
+    rows, cols, ldx = _bf16(x)
+    _, _, ldq = _mat(q, "q", 1)
+    _check(lib.fp8_quantize_tensor(_ptr(x), rows, cols, ldx, fmt, margin, _ptr(scale), _ptr(q), ldq,
+                                   _ptr(scale_inv_out), _ptr(amax_out), _stream(x)))
+
+
+def fp8_quantize_row(x, fmt, margin, q, scale_inv_out, amax_out=None, col_amax_out=None):
+    rows, cols, ldx = _bf16(x)
+    _, _, ldq = _mat(q, "q", 1)
+    _check(lib.fp8_quantize_row(_ptr(x), rows, cols, ldx, fmt, margin, _ptr(q), ldq, _ptr(scale_inv_out),
+                                _ptr(amax_out), _ptr(col_amax_out), _stream(x)))
+
+
+def fp8_quantize_col(x, fmt, margin, qt, scale_inv_out, col_amax, col_amax_ready=False):
+    rows, cols, ldx = _bf16(x)
+    _, _, ldqt = _mat(qt, "qt", 1)
+    _check(lib.fp8_quantize_col(_ptr(x), rows, cols, ldx, fmt, margin, _ptr(qt), ldqt, _ptr(scale_inv_out),
+                                _ptr(col_amax), int(bool(col_amax_ready)), _stream(x)))
+
+
+def fp8_delayed_scale_update(cur_amax, history, head, algo, margin, fmt, scale, scale_inv):
+    """history: float32 [n x L]; head: int32 [1]; cur_amax, scale, scale_inv: float32 [n]."""
+    n, L = history.shape
+    _check(lib.fp8_delayed_scale_update(_ptr(cur_amax), _ptr(history), _ptr(head), n, L, algo, margin, fmt,
+                                        _ptr(scale), _ptr(scale_inv), _stream(history)))
+
+
+def fp8_gemm_scaled(a, fa, b, fb, a_scale_inv, a_mode, b_scale_inv, b_mode, d):
+    """d [m x n] = (a [m x k] codes) * (b [n x k] codes)^T, scaled; d bf16 or float32."""
+    m, k, lda = _mat(a, "a", 1)
+    n, kb, ldb = _mat(b, "b", 1)
+    if kb != k:
+        raise ValueError(f"a has k = {k} but b has k = {kb}")
+    _, _, ldd = _mat(d, "d")
+    d_type = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[d.dtype]
+    _check(lib.fp8_gemm_scaled(_ptr(a), fa, lda, _ptr(b), fb, ldb, m, n, k, _ptr(a_scale_inv), a_mode,
+                               _ptr(b_scale_inv), b_mode, _ptr(d), d_type, ldd, _stream(a)))
+
+
+def fp8_grouped_gemm_scaled(a, fa, b, fb, group_offsets, a_scale_inv, b_scale_inv, d):
+    """a [total_m x k] codes sorted by group; b [g x n x k] codes; group_offsets int64 [g+1]
+    on the device; a_scale_inv [total_m]; b_scale_inv [g x n]; d [total_m x n]."""
+    total_m, k, lda = _mat(a, "a", 1)
+    if b.dim() != 3 or b.element_size() != 1 or b.stride(2) != 1:
+        raise ValueError("b must be a [g x n x k] 1-byte tensor with unit last stride")
+    g, n, kb = b.shape
+    if kb != k:
+        raise ValueError(f"a has k = {k} but b has k = {kb}")
+    _, _, ldd = _mat(d, "d")
+    d_type = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[d.dtype]
+    if group_offsets.dtype != torch.int64 or group_offsets.numel() != g + 1:
+        raise ValueError("group_offsets must be int64 with g + 1 entries")
+    _check(lib.fp8_grouped_gemm_scaled(_ptr(a), fa, lda, _ptr(b), fb, max(b.stride(1), k), b.stride(0),
+                                       _ptr(group_offsets), g, total_m, n, k, _ptr(a_scale_inv),
+                                       _ptr(b_scale_inv), _ptr(d), d_type, ldd, _stream(a)))

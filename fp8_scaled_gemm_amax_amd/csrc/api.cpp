@@ -1,0 +1,300 @@
+// api.cpp - the C ABI of include/fp8amax.h: argument validation (before any
+// launch), the per-device properties cache, and dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/fp8amax.h"
+#include "kernels.hpp"
+
+namespace fp8amax {
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp8_status_t fail(fp8_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+fp8_status_t ok() {
+    g_err[0] = '\0';
+    return FP8_OK;
+}
+
+constexpr int kMaxDevices = 64;
+struct PropsSlot {
+    std::once_flag once;
+    DeviceProps props{};
+    bool gfx950 = false;
+    hipError_t err = hipSuccess;
+};
+PropsSlot g_props[kMaxDevices];
+
+PropsSlot* slot_for_current(int* dev_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    PropsSlot& s = g_props[dev];
+    std::call_once(s.once, [&s, dev]() {
+        hipDeviceProp_t p;
+        s.err = hipGetDeviceProperties(&p, dev);
+        if (s.err == hipSuccess) {
+            s.props.cus = p.multiProcessorCount;
+            s.gfx950 = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        }
+    });
+    if (dev_out) *dev_out = dev;
+    return &s;
+}
+
+bool valid_fmt(int f) { return f >= FP8_E4M3 && f <= FP8_E5M2_FNUZ; }
+bool ocp_fmt(int f) { return f == FP8_E4M3 || f == FP8_E5M2; }
+bool aligned(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Device check shared by every compute entry point (after argument checks).
+fp8_status_t check_device() {
+    int dev = 0;
+    PropsSlot* s = slot_for_current(&dev);
+    if (!s) return fail(FP8_ERR_HIP, "cannot query the current HIP device");
+    if (s->err != hipSuccess) return fail(FP8_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(s->err));
+    if (!s->gfx950) return fail(FP8_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X); this library is built for gfx950 only", dev);
+    return FP8_OK;
+}
+
+fp8_status_t launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FP8_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+fp8_status_t check_matrix(const char* fn, const char* name, const void* p, int64_t rows, int64_t cols, int64_t ld) {
+    if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "%s: %s has negative size %lld x %lld", fn, name,
+                                          (long long)rows, (long long)cols);
+    if (ld < cols || ld < 1) return fail(FP8_ERR_INVALID_ARG, "%s: leading dimension of %s (%lld) < max(cols, 1) (%lld)",
+                                        fn, name, (long long)ld, (long long)cols);
+    if (!p && rows > 0 && cols > 0) return fail(FP8_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+    return FP8_OK;
+}
+
+#define FP8_TRY(expr)                          \
+    do {                                       \
+        fp8_status_t _s = (expr);              \
+        if (_s != FP8_OK) return _s;           \
+    } while (0)
+
+fp8_status_t check_common_quant(const char* fn, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                int margin) {
+    FP8_TRY(check_matrix(fn, "x", x, rows, cols, ldx));
+    if (!valid_fmt(fmt)) return fail(FP8_ERR_INVALID_ARG, "%s: unknown format %d", fn, fmt);
+    if (margin < 0 || margin > 32) return fail(FP8_ERR_INVALID_ARG, "%s: margin %d outside 0..32", fn, margin);
+    if (!aligned(x, 2)) return fail(FP8_ERR_ALIGNMENT, "%s: x is not 2-byte aligned", fn);
+    return FP8_OK;
+}
+
+fp8_status_t check_gemm_operands(const char* fn, const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb,
+                                 int64_t ldb, int64_t m, int64_t n, int64_t k, const void* d, int d_type, int64_t ldd) {
+    if (m < 0 || n < 0 || k < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative size m=%lld n=%lld k=%lld", fn,
+                                             (long long)m, (long long)n, (long long)k);
+    if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8_ERR_INVALID_ARG, "%s: unknown format (%d, %d)", fn, fa, fb);
+    if (d_type != FP8_OUT_BF16 && d_type != FP8_OUT_F32) return fail(FP8_ERR_INVALID_ARG, "%s: unknown output type %d", fn, d_type);
+    if (k % 16 != 0) return fail(FP8_ERR_INVALID_ARG, "%s: k = %lld is not a multiple of 16", fn, (long long)k);
+    if (lda < k || ldb < k || ldd < n) return fail(FP8_ERR_INVALID_ARG, "%s: leading dimension smaller than the row", fn);
+    if (m > 0 && n > 0) {
+        if (!d) return fail(FP8_ERR_INVALID_ARG, "%s: d is NULL", fn);
+        if (k > 0 && (!a || !b)) return fail(FP8_ERR_INVALID_ARG, "%s: a or b is NULL", fn);
+    }
+    if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0)
+        return fail(FP8_ERR_ALIGNMENT, "%s: a, b must be 16-byte aligned with lda, ldb multiples of 16", fn);
+    if (!aligned(d, 4)) return fail(FP8_ERR_ALIGNMENT, "%s: d must be 4-byte aligned", fn);
+    if (!ocp_fmt(fa) || !ocp_fmt(fb))
+        return fail(FP8_ERR_UNSUPPORTED,
+                    "%s: fnuz operands (%d, %d): gfx950 matrix cores consume the OCP e4m3/e5m2 encodings", fn, fa, fb);
+    return FP8_OK;
+}
+
+}  // namespace
+
+const DeviceProps& current_device_props() {
+    static DeviceProps fallback{256};
+    PropsSlot* s = slot_for_current(nullptr);
+    return (s && s->err == hipSuccess) ? s->props : fallback;
+}
+
+}  // namespace fp8amax
+
+using namespace fp8amax;
+
+extern "C" {
+
+const char* fp8_status_string(fp8_status_t status) {
+    switch (status) {
+        case FP8_OK: return "FP8_OK";
+        case FP8_ERR_INVALID_ARG: return "FP8_ERR_INVALID_ARG";
+        case FP8_ERR_ALIGNMENT: return "FP8_ERR_ALIGNMENT";
+        case FP8_ERR_UNSUPPORTED: return "FP8_ERR_UNSUPPORTED";
+        case FP8_ERR_HIP: return "FP8_ERR_HIP";
+    }
+    return "FP8_ERR_UNKNOWN";
+}
+
+const char* fp8_last_error(void) { return g_err; }
+
+fp8_status_t fp8_query_device(int device, fp8_device_info_t* info) {
+    if (!info) return fail(FP8_ERR_INVALID_ARG, "fp8_query_device: info is NULL");
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess) return fail(FP8_ERR_HIP, "hipGetDeviceCount: %s", hipGetErrorString(e));
+    if (device < 0 || device >= count)
+        return fail(FP8_ERR_INVALID_ARG, "fp8_query_device: device %d outside [0, %d)", device, count);
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, device);
+    if (e != hipSuccess) return fail(FP8_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    std::memset(info, 0, sizeof *info);
+    std::strncpy(info->arch, p.gcnArchName, sizeof info->arch - 1);
+    info->is_gfx950 = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    const bool fnuz_native = std::strncmp(p.gcnArchName, "gfx94", 5) == 0;
+    info->native_e4m3 = fnuz_native ? FP8_E4M3_FNUZ : FP8_E4M3;
+    info->native_e5m2 = fnuz_native ? FP8_E5M2_FNUZ : FP8_E5M2;
+    info->compute_units = p.multiProcessorCount;
+    info->lds_bytes_per_block = (int32_t)p.sharedMemPerBlock;
+    info->global_mem_bytes = (int64_t)p.totalGlobalMem;
+    return ok();
+}
+
+fp8_status_t fp8_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_axis_t axis, float* amax_out,
+                      void* stream) {
+    const char* fn = "fp8_amax";
+    FP8_TRY(check_matrix(fn, "x", x, rows, cols, ldx));
+    if (axis != FP8_AXIS_TENSOR && axis != FP8_AXIS_ROW && axis != FP8_AXIS_COL)
+        return fail(FP8_ERR_INVALID_ARG, "%s: unknown axis %d", fn, (int)axis);
+    const int64_t nout = axis == FP8_AXIS_TENSOR ? 1 : (axis == FP8_AXIS_ROW ? rows : cols);
+    if (nout > 0 && !amax_out) return fail(FP8_ERR_INVALID_ARG, "%s: amax_out is NULL", fn);
+    if (!aligned(x, 2) || !aligned(amax_out, 4)) return fail(FP8_ERR_ALIGNMENT, "%s: misaligned pointer", fn);
+    FP8_TRY(check_device());
+    return launched(launch_amax(x, rows, cols, ldx, (int)axis, amax_out, (hipStream_t)stream), fn);
+}
+
+fp8_status_t fp8_quantize_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                                 int32_t margin, const float* scale, uint8_t* q, int64_t ldq, float* scale_inv_out,
+                                 float* amax_out, void* stream) {
+    const char* fn = "fp8_quantize_tensor";
+    FP8_TRY(check_common_quant(fn, x, rows, cols, ldx, (int)fmt, margin));
+    FP8_TRY(check_matrix(fn, "q", q, rows, cols, ldq));
+    if (!scale_inv_out || !amax_out) return fail(FP8_ERR_INVALID_ARG, "%s: scale_inv_out and amax_out are required", fn);
+    if (!aligned(scale_inv_out, 4) || !aligned(amax_out, 4) || !aligned(scale, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer", fn);
+    FP8_TRY(check_device());
+    return launched(launch_quant_tensor(x, rows, cols, ldx, (int)fmt, margin, scale, q, ldq, scale_inv_out, amax_out,
+                                        (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                              int32_t margin, uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out,
+                              float* col_amax_out, void* stream) {
+    const char* fn = "fp8_quantize_row";
+    FP8_TRY(check_common_quant(fn, x, rows, cols, ldx, (int)fmt, margin));
+    FP8_TRY(check_matrix(fn, "q", q, rows, cols, ldq));
+    if (rows > 0 && !scale_inv_out) return fail(FP8_ERR_INVALID_ARG, "%s: scale_inv_out is NULL", fn);
+    if (!aligned(scale_inv_out, 4) || !aligned(amax_out, 4) || !aligned(col_amax_out, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer", fn);
+    FP8_TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_quant_row(x, rows, cols, ldx, (int)fmt, margin, q, ldq, scale_inv_out, amax_out, st);
+    if (e == hipSuccess && col_amax_out) e = launch_amax(x, rows, cols, ldx, FP8_AXIS_COL, col_amax_out, st);
+    return launched(e, fn);
+}
+
+fp8_status_t fp8_quantize_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                              int32_t margin, uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* col_amax,
+                              int32_t col_amax_ready, void* stream) {
+    const char* fn = "fp8_quantize_col";
+    FP8_TRY(check_common_quant(fn, x, rows, cols, ldx, (int)fmt, margin));
+    FP8_TRY(check_matrix(fn, "qt", qt, cols, rows, ldqt));
+    if (cols > 0 && (!scale_inv_out || !col_amax))
+        return fail(FP8_ERR_INVALID_ARG, "%s: scale_inv_out and col_amax are required", fn);
+    if (col_amax_ready != 0 && col_amax_ready != 1)
+        return fail(FP8_ERR_INVALID_ARG, "%s: col_amax_ready must be 0 or 1", fn);
+    if (!aligned(scale_inv_out, 4) || !aligned(col_amax, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer", fn);
+    FP8_TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (!col_amax_ready) e = launch_amax(x, rows, cols, ldx, FP8_AXIS_COL, col_amax, st);
+    if (e == hipSuccess) e = launch_quant_col(x, rows, cols, ldx, (int)fmt, margin, qt, ldqt, scale_inv_out, col_amax, st);
+    return launched(e, fn);
+}
+
+fp8_status_t fp8_delayed_scale_update(float* cur_amax, float* history, int32_t* head, int64_t n, int32_t L,
+                                      fp8_amax_algo_t algo, int32_t margin, fp8_format_t fmt, float* scale,
+                                      float* scale_inv, void* stream) {
+    const char* fn = "fp8_delayed_scale_update";
+    if (n < 0) return fail(FP8_ERR_INVALID_ARG, "%s: n < 0", fn);
+    if (L < 1 || L > 65536) return fail(FP8_ERR_INVALID_ARG, "%s: history length %d outside 1..65536", fn, L);
+    if (algo != FP8_AMAX_MOST_RECENT && algo != FP8_AMAX_MAX)
+        return fail(FP8_ERR_INVALID_ARG, "%s: unknown amax algo %d", fn, (int)algo);
+    if (margin < 0 || margin > 32) return fail(FP8_ERR_INVALID_ARG, "%s: margin %d outside 0..32", fn, margin);
+    if (!valid_fmt((int)fmt)) return fail(FP8_ERR_INVALID_ARG, "%s: unknown format %d", fn, (int)fmt);
+    if (!head) return fail(FP8_ERR_INVALID_ARG, "%s: head is NULL", fn);
+    if (n > 0 && (!cur_amax || !history || !scale || !scale_inv))
+        return fail(FP8_ERR_INVALID_ARG, "%s: state pointer is NULL", fn);
+    if (!aligned(cur_amax, 4) || !aligned(history, 4) || !aligned(head, 4) || !aligned(scale, 4) ||
+        !aligned(scale_inv, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned state pointer", fn);
+    FP8_TRY(check_device());
+    return launched(launch_delayed_update(cur_amax, history, head, n, L, (int)algo, margin, (int)fmt, scale, scale_inv,
+                                          (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b, fp8_format_t fb,
+                             int64_t ldb, int64_t m, int64_t n, int64_t k, const float* a_scale_inv,
+                             fp8_scale_mode_t a_mode, const float* b_scale_inv, fp8_scale_mode_t b_mode, void* d,
+                             fp8_out_t d_type, int64_t ldd, void* stream) {
+    const char* fn = "fp8_gemm_scaled";
+    FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, m, n, k, d, (int)d_type, ldd));
+    if ((a_mode != FP8_SCALE_TENSOR && a_mode != FP8_SCALE_VECTOR) ||
+        (b_mode != FP8_SCALE_TENSOR && b_mode != FP8_SCALE_VECTOR))
+        return fail(FP8_ERR_INVALID_ARG, "%s: unknown scale mode", fn);
+    if (m > 0 && n > 0 && (!a_scale_inv || !b_scale_inv)) return fail(FP8_ERR_INVALID_ARG, "%s: scale is NULL", fn);
+    if (!aligned(a_scale_inv, 4) || !aligned(b_scale_inv, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned scale pointer", fn);
+    FP8_TRY(check_device());
+    return launched(launch_gemm(a, (int)fa, lda, b, (int)fb, ldb, m, n, k, a_scale_inv, a_mode == FP8_SCALE_VECTOR,
+                                b_scale_inv, b_mode == FP8_SCALE_VECTOR, d, d_type == FP8_OUT_F32, ldd,
+                                (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_grouped_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b,
+                                     fp8_format_t fb, int64_t ldb, int64_t b_group_stride,
+                                     const int64_t* group_offsets, int32_t g, int64_t total_m, int64_t n, int64_t k,
+                                     const float* a_scale_inv, const float* b_scale_inv, void* d, fp8_out_t d_type,
+                                     int64_t ldd, void* stream) {
+    const char* fn = "fp8_grouped_gemm_scaled";
+    FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, total_m, n, k, d, (int)d_type, ldd));
+    if (g < 1 || g > 4096) return fail(FP8_ERR_INVALID_ARG, "%s: group count %d outside 1..4096", fn, g);
+    if (!group_offsets) return fail(FP8_ERR_INVALID_ARG, "%s: group_offsets is NULL", fn);
+    if (!aligned(group_offsets, 8)) return fail(FP8_ERR_ALIGNMENT, "%s: group_offsets must be 8-byte aligned", fn);
+    if (b_group_stride < n * ldb && g > 1 && n > 0)
+        return fail(FP8_ERR_INVALID_ARG, "%s: b_group_stride %lld < n * ldb", fn, (long long)b_group_stride);
+    if (b_group_stride % 16 != 0) return fail(FP8_ERR_ALIGNMENT, "%s: b_group_stride must be a multiple of 16", fn);
+    if (total_m > 0 && n > 0 && (!a_scale_inv || !b_scale_inv))
+        return fail(FP8_ERR_INVALID_ARG, "%s: scale is NULL", fn);
+    if (!aligned(a_scale_inv, 4) || !aligned(b_scale_inv, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned scale pointer", fn);
+    FP8_TRY(check_device());
+    return launched(launch_grouped_gemm(a, (int)fa, lda, b, (int)fb, ldb, b_group_stride, group_offsets, g, total_m,
+                                        n, k, a_scale_inv, b_scale_inv, d, d_type == FP8_OUT_F32, ldd,
+                                        (hipStream_t)stream),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// kernels.hpp - host-side launchers of the device kernels (internal to the
+// library; the public interface is include/fp8amax.h). Each launcher assumes
+// its arguments were validated by the C ABI layer and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8amax {
+
+struct DeviceProps {
+    int cus;
+};
+const DeviceProps& current_device_props();
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
+
+hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis, float* out,
+                       hipStream_t st);
+
+hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
+                            uint8_t* q, int64_t ldq, float* scale_inv, float* amax_out, hipStream_t st);
+
+hipError_t launch_quant_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
+                            uint8_t* qt, int64_t ldqt, float* scale_inv, const float* col_amax, hipStream_t st);
+
+hipError_t launch_quant_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
+                               const float* scale, uint8_t* q, int64_t ldq, float* scale_inv, float* amax,
+                               hipStream_t st);
+
+hipError_t launch_delayed_update(float* cur_amax, float* history, int32_t* head, int64_t n, int32_t L, int algo,
+                                 int margin, int fmt, float* scale, float* scale_inv, hipStream_t st);
+
+hipError_t launch_gemm(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb, int64_t m,
+                       int64_t n, int64_t k, const float* sa, int sa_vec, const float* sb, int sb_vec, void* d,
+                       int out_f32, int64_t ldd, hipStream_t st);
+
+hipError_t launch_grouped_gemm(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb,
+                               int64_t b_group_stride, const int64_t* offsets, int g, int64_t total_m, int64_t n,
+                               int64_t k, const float* sa, const float* sb, void* d, int out_f32, int64_t ldd,
+                               hipStream_t st);
+
+}  // namespace fp8amax

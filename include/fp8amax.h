@@ -1,0 +1,207 @@
+/*
+ * fp8amax.h - C ABI of the MI355X (gfx950) FP8 linear-layer library.
+ *
+ * The operations are the hot path of the FP8 linear layer of FP8 training:
+ * amax reduction, scale computation (current and delayed), a saturating
+ * round-to-nearest-even cast to FP8, and the FP8 GEMM with fp32 accumulation and
+ * a scale-applying epilogue, dense and grouped over MoE experts. Sources:
+ *   [Flux]  "FP8 training for Flux models" (ROCm Primus docs): section
+ *           "Configuration" (fp8 e4m3/hybrid, recipes delayed/tensorwise,
+ *           fp8_margin, fp8_amax_history_len, fp8_amax_compute_algo, fp8_wgrad),
+ *           section "Troubleshooting / NaN or inf in losses", section "Testing /
+ *           Numerical verification status" (fused delayed-scale update).
+ *   [MI300] "FP8 Training on MI300X": section on the AMD FP8 dtype difference
+ *           (e4m3fn/e5m2 with e4m3 max 448 vs e4m3fnuz/e5m2fnuz with max 240 and
+ *           unsigned zero; e4m3 forward, e5m2 backward).
+ *   [Titan] "FP8 Training on AMD GPUs with TorchTitan and TorchAO": summary
+ *           (rowwise FP8, fused quantization kernels, colwise scales, grouped
+ *           GEMM for MoE) and its answers on the wrong-max corruption and on
+ *           the non-coalesced colwise-scale writes.
+ *
+ * Conventions common to every entry point
+ *  - Pointers named x, q, qt, amax*, scale*, history, head, a, b, d and
+ *    group_offsets are DEVICE pointers owned by the caller. The library
+ *    allocates nothing and keeps no state between calls except a per-device
+ *    properties cache.
+ *  - Matrices are row-major with an explicit leading dimension counted in
+ *    elements (ldx for bf16 inputs, ldq/lda/ldb for FP8 codes, ldd for the
+ *    output). A bf16 tensor is passed as its 16-bit patterns.
+ *  - stream is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on it and returns; there is no host synchronisation and
+ *    no device-to-host copy.
+ *  - Errors: arguments are checked on the host before anything is launched;
+ *    on error nothing is enqueued and the call returns a non-zero status.
+ *    fp8_last_error() then describes it (thread-local). No exception crosses
+ *    the ABI.
+ *  - The cast, for every encoding (readings of [Flux]/[MI300]/[Titan], which
+ *    do not spell out the arithmetic): with s the scale, p = fl32(x * s), then
+ *    p is clamped to +-fmax (Inf saturates), rounded to the nearest FP8 value
+ *    with ties to even, NaN -> NaN code (sign|0x7F for OCP, 0x80 for fnuz);
+ *    a zero result keeps its sign in OCP and is 0x00 in fnuz.
+ *  - Current scaling: s = fl32(fmax / amax) * 2^-margin (fmax / amax rounded
+ *    once to fp32, FLT_MAX if it overflows); s = 1 if amax is 0 or not finite.
+ *    Quantizers store scale_inv = fl32(1 / s), the factor that dequantises.
+ *  - amax is max |x| over the reduction domain, returned in fp32; a NaN in the
+ *    domain makes it NaN.
+ */
+#ifndef FP8AMAX_H
+#define FP8AMAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* FP8 encodings [MI300]. OCP: e4m3 (max 448, no Inf, NaN = S.1111.111, signed
+ * zero), e5m2 (max 57344, Inf and NaN in the top exponent, signed zero).
+ * fnuz: e4m3 (bias 8, max 240) and e5m2 (bias 16, max 57344), no Inf, a single
+ * zero, NaN = 0x80. gfx950's matrix cores consume the OCP encodings. */
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1, FP8_E4M3_FNUZ = 2, FP8_E5M2_FNUZ = 3 } fp8_format_t;
+
+typedef enum { FP8_AXIS_TENSOR = 0, FP8_AXIS_ROW = 1, FP8_AXIS_COL = 2 } fp8_axis_t;
+
+/* fp8_amax_compute_algo of [Flux] "Configuration". */
+typedef enum { FP8_AMAX_MOST_RECENT = 0, FP8_AMAX_MAX = 1 } fp8_amax_algo_t;
+
+/* A GEMM operand's dequantisation factor: one value, or one per row of the operand. */
+typedef enum { FP8_SCALE_TENSOR = 0, FP8_SCALE_VECTOR = 1 } fp8_scale_mode_t;
+
+typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1 } fp8_out_t;
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_INVALID_ARG = 1,  /* null pointer, negative size, ld < width, bad enum, margin out of range */
+    FP8_ERR_ALIGNMENT = 2,    /* a pointer or leading dimension breaks a stated alignment */
+    FP8_ERR_UNSUPPORTED = 3,  /* valid request this build does not run (device not gfx950, fnuz GEMM operands) */
+    FP8_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} fp8_status_t;
+
+typedef struct {
+    char arch[64];                /* gcnArchName, e.g. "gfx950:sramecc+:xnack-" */
+    int32_t is_gfx950;            /* 1 if this library's kernels run on the device */
+    int32_t native_e4m3;          /* encoding the matrix cores consume: FP8_E4M3 on gfx950, FP8_E4M3_FNUZ on gfx942 */
+    int32_t native_e5m2;
+    int32_t compute_units;
+    int32_t lds_bytes_per_block;  /* sharedMemPerBlock */
+    int64_t global_mem_bytes;
+} fp8_device_info_t;
+
+/* Availability probe (the role of [Flux]'s is_fp8_available check): fills
+ * *info for HIP device `device`. Returns FP8_ERR_INVALID_ARG for a bad index
+ * or NULL info, FP8_ERR_HIP if the runtime fails. Host-synchronous. */
+fp8_status_t fp8_query_device(int device, fp8_device_info_t* info);
+
+/* Static string naming a status code. */
+const char* fp8_status_string(fp8_status_t status);
+
+/* Message of the last error returned on the calling thread ("" if none). */
+const char* fp8_last_error(void);
+
+/* amax reduction ([Titan] rowwise and colwise scales; [Flux] tensorwise/delayed).
+ * x: bf16 [rows x cols], row stride ldx >= cols. axis selects the domain:
+ *   FP8_AXIS_TENSOR -> amax_out[0]; FP8_AXIS_ROW -> amax_out[rows];
+ *   FP8_AXIS_COL -> amax_out[cols]. amax_out (fp32) is overwritten.
+ * Alignment: x 2-byte aligned; 16-byte aligned x with ldx % 8 == 0 takes the
+ * vector path. Empty domains give 0. */
+fp8_status_t fp8_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_axis_t axis,
+                      float* amax_out, void* stream);
+
+/* Tensorwise quantization ([Flux] recipes "delayed" and "tensorwise").
+ * x: bf16 [rows x cols] (ldx); q: codes [rows x cols] (ldq >= cols).
+ *  - scale != NULL (delayed scaling): *scale (device fp32) is the scale to
+ *    use; writes scale_inv_out[0] = fl32(1 / *scale) (the factor actually
+ *    used, so it cannot disagree with a later state update), and FOLDS the
+ *    tensor's amax into amax_out[0] (amax_out[0] = max(amax_out[0], amax(x))):
+ *    amax_out is the delayed state's cur_amax, cleared by
+ *    fp8_delayed_scale_update. margin is ignored (the state applies it).
+ *  - scale == NULL (current scaling): amax_out[0] is overwritten with amax(x),
+ *    s is computed from it with `margin`, scale_inv_out[0] = fl32(1 / s).
+ * margin: 0..32. amax_out and scale_inv_out are required. */
+fp8_status_t fp8_quantize_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                                 int32_t margin, const float* scale, uint8_t* q, int64_t ldq,
+                                 float* scale_inv_out, float* amax_out, void* stream);
+
+/* Rowwise quantization ([Titan] rowwise FP8: one scale per row, e.g. per token
+ * of an activation or per output row of a weight). One pass over x: row amax,
+ * scale, cast. x: bf16 [rows x cols] (ldx); q: codes [rows x cols] (ldq).
+ * scale_inv_out[rows] (required); amax_out[rows] (optional, NULL to skip);
+ * col_amax_out[cols] (optional): if given, it is overwritten with the
+ * per-column amax of x, a side output for a later colwise quantization of the
+ * same tensor (fp8_quantize_col with col_amax_ready = 1).
+ * margin: 0..32. Vector path when x, q are 16/8-byte aligned and ldx, ldq,
+ * cols are multiples of 8; any other layout takes a scalar path. */
+fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                              int32_t margin, uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out,
+                              float* col_amax_out, void* stream);
+
+/* Colwise quantization with transposed output ([Titan] colwise scales, whose
+ * non-coalesced writes the post singles out). One scale per column of x
+ * (reduction over the rows, e.g. over tokens), and the codes are written
+ * transposed so that the next GEMM's contraction dimension is contiguous:
+ * qt[j * ldqt + i] = cast(x[i * ldx + j] * s_j), qt is [cols x rows], ldqt >= rows.
+ * col_amax[cols]: if col_amax_ready == 0 it is overwritten with the column
+ * amax (computed by a first pass over x); if 1 it is read as already holding
+ * it (from fp8_amax(FP8_AXIS_COL) or fp8_quantize_row's side output).
+ * scale_inv_out[cols] (required). margin: 0..32. */
+fp8_status_t fp8_quantize_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                              int32_t margin, uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* col_amax,
+                              int32_t col_amax_ready, void* stream);
+
+/* Fused end-of-step update of n delayed-scaling states ([Flux] "Configuration":
+ * fp8_amax_history_len, fp8_amax_compute_algo, fp8_margin; [Flux] "Testing":
+ * the fused delayed-scale update). State layout, all device memory:
+ *   cur_amax[n]   amax recorded this step (fp8_quantize_tensor folds into it);
+ *   history[n*L]  ring of the last L recorded amaxes per tensor (row i at i*L);
+ *   head[1]       int32 next ring slot, shared by the n tensors, in [0, L);
+ *   scale[n], scale_inv[n].
+ * For each tensor: history[i*L + head] = cur_amax[i]; amax_eff = cur_amax[i]
+ * (MOST_RECENT) or the max over the L slots (MAX); if amax_eff is finite and
+ * > 0: scale[i] = fl32(fmax / amax_eff) * 2^-margin (FLT_MAX on overflow),
+ * scale_inv[i] = fl32(1 / scale[i]); otherwise both are kept. cur_amax[i] = 0.
+ * Then head = (head + 1) % L. Initial state: history 0, head 0, scale 1,
+ * scale_inv 1, cur_amax 0. L: 1..65536; margin 0..32. */
+fp8_status_t fp8_delayed_scale_update(float* cur_amax, float* history, int32_t* head, int64_t n, int32_t L,
+                                      fp8_amax_algo_t algo, int32_t margin, fp8_format_t fmt, float* scale,
+                                      float* scale_inv, void* stream);
+
+/* Scaled FP8 GEMM ([Titan] FP8 linear layers; [Flux] FP8 wgrad):
+ *   d[i, j] = out( fp32acc( sum_k dec(a[i, k]) * dec(b[j, k]) ) * sa_i * sb_j )
+ * a: codes [m x k] (lda), b: codes [n x k] (ldb): both K-contiguous, d = a * b^T
+ * (for y = x * w^T, a = x and b = w). sa_i = a_scale_inv[i] (VECTOR, [m]) or
+ * a_scale_inv[0] (TENSOR); likewise sb_j with b_scale_inv ([n]). The scales
+ * are the quantizers' scale_inv outputs (device fp32). out: bf16
+ * (round-to-nearest-even) or fp32, d [m x n] with row stride ldd >= n.
+ * Formats: fa, fb in {FP8_E4M3, FP8_E5M2}, mixed allowed ([Flux] "hybrid":
+ * e4m3 activations and weights, e5m2 gradients). fnuz operands return
+ * FP8_ERR_UNSUPPORTED (gfx950's matrix cores consume OCP encodings).
+ * Requirements: k % 16 == 0; a, b 16-byte aligned; lda, ldb multiples of 16;
+ * d 4-byte aligned. m, n >= 0 arbitrary (ragged tiles are masked); k == 0
+ * writes zeros times the scales. */
+fp8_status_t fp8_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b, fp8_format_t fb,
+                             int64_t ldb, int64_t m, int64_t n, int64_t k, const float* a_scale_inv,
+                             fp8_scale_mode_t a_mode, const float* b_scale_inv, fp8_scale_mode_t b_mode, void* d,
+                             fp8_out_t d_type, int64_t ldd, void* stream);
+
+/* Grouped (MoE) scaled FP8 GEMM ([Titan]: FP8 grouped GEMM for mixture-of-experts
+ * layers). Rows of a are sorted by expert: rows group_offsets[g] ..
+ * group_offsets[g+1]-1 belong to expert g, whose weight is
+ * b_g = b + g * b_group_stride (codes [n x k], row stride ldb). For those rows:
+ *   d[i, j] = out( fp32acc( sum_k dec(a[i, k]) * dec(b_g[j, k]) ) * a_scale_inv[i] * b_scale_inv[g*n + j] ).
+ * group_offsets: DEVICE int64 [g+1], non-decreasing, offsets[0] = 0,
+ * offsets[g] = total_m (the library cannot read it without a host sync, so
+ * it is not checked; rows outside [0, total_m) are never touched). Empty groups
+ * produce nothing. a: [total_m x k]; a_scale_inv [total_m]; b_scale_inv [g x n];
+ * d [total_m x n]. Formats and alignment as fp8_gemm_scaled; g: 1..4096. */
+fp8_status_t fp8_grouped_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b,
+                                     fp8_format_t fb, int64_t ldb, int64_t b_group_stride,
+                                     const int64_t* group_offsets, int32_t g, int64_t total_m, int64_t n, int64_t k,
+                                     const float* a_scale_inv, const float* b_scale_inv, void* d, fp8_out_t d_type,
+                                     int64_t ldd, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8AMAX_H */

@@ -181,9 +181,17 @@ uint8_t orc_quantize_value(int fmt, uint16_t x_bf16, float s) {
 /* axis 0: whole tensor -> out[0]; axis 1: per row -> out[rows]; axis 2: per column -> out[cols] */
 void orc_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis, float* out) {
     if (axis == 0) {
+        /* the tensor's amax is the amax of its row amaxes */
         float acc = 0.0f;
-        for (int64_t i = 0; i < rows; ++i)
-            for (int64_t j = 0; j < cols; ++j) acc = amax_combine(acc, bf16_value(x[i * ldx + j]));
+        #pragma omp parallel
+        {
+            float part = 0.0f;
+            #pragma omp for schedule(static)
+            for (int64_t i = 0; i < rows; ++i)
+                for (int64_t j = 0; j < cols; ++j) part = amax_combine(part, bf16_value(x[i * ldx + j]));
+            #pragma omp critical
+            acc = amax_combine(acc, part);
+        }
         out[0] = acc;
     } else if (axis == 1) {
         #pragma omp parallel for schedule(static)
@@ -193,9 +201,12 @@ void orc_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int ax
             out[i] = acc;
         }
     } else {
-        for (int64_t j = 0; j < cols; ++j) out[j] = 0.0f;
-        for (int64_t i = 0; i < rows; ++i)
-            for (int64_t j = 0; j < cols; ++j) out[j] = amax_combine(out[j], bf16_value(x[i * ldx + j]));
+        #pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < cols; ++j) {
+            float acc = 0.0f;
+            for (int64_t i = 0; i < rows; ++i) acc = amax_combine(acc, bf16_value(x[i * ldx + j]));
+            out[j] = acc;
+        }
     }
 }
 
@@ -235,14 +246,12 @@ void orc_quantize_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx
  * into *amax_acc (max with what it already holds). */
 void orc_quantize_tensor_scaled(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                 float s, uint8_t* q, int64_t ldq, float* scale_inv_used, float* amax_acc) {
-    float a = *amax_acc;
+    #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i)
-        for (int64_t j = 0; j < cols; ++j) {
-            uint16_t v = x[i * ldx + j];
-            a = amax_combine(a, bf16_value(v));
-            q[i * ldq + j] = orc_quantize_value(fmt, v, s);
-        }
-    *amax_acc = a;
+        for (int64_t j = 0; j < cols; ++j) q[i * ldq + j] = orc_quantize_value(fmt, x[i * ldx + j], s);
+    float a;
+    orc_amax(x, rows, cols, ldx, 0, &a);
+    *amax_acc = amax_combine(*amax_acc, a);
     *scale_inv_used = orc_reciprocal(s);
 }
 
@@ -252,6 +261,7 @@ void orc_quantize_tensor_current(const uint16_t* x, int64_t rows, int64_t cols, 
     float a;
     orc_amax(x, rows, cols, ldx, 0, &a);
     float s = orc_scale_current(fmt, a, margin);
+    #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i)
         for (int64_t j = 0; j < cols; ++j) q[i * ldq + j] = orc_quantize_value(fmt, x[i * ldx + j], s);
     *scale_inv = orc_reciprocal(s);

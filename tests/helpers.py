@@ -1,0 +1,91 @@
+"""Shared helpers of the GPU parity tests: moving the generators' bit patterns
+to the device, allocating outputs with guard bands, and printing the case
+before each GPU step."""
+import sys
+
+import numpy as np
+import torch
+
+SENTINEL = 0x5A
+
+
+def say(*args):
+    """Name the case (flushed) before a GPU step, so a failure can be located."""
+    print("[case]", *args, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits):
+    """uint16 bf16 bit patterns (numpy) -> torch.bfloat16 tensor on cuda:0."""
+    bits = np.ascontiguousarray(bits, np.uint16)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def host_bits(t):
+    """torch.bfloat16 tensor -> uint16 numpy bit patterns."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to("cuda:0")
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda:0")
+
+
+def guarded(rows, cols, dtype, ld=None, pad_rows=2, fill=SENTINEL):
+    """A [rows x cols] view with row stride ld inside a larger buffer whose
+    surroundings hold a sentinel: check_guard() afterwards detects any write
+    outside the view. Returns (view, buffer, (r0, c0))."""
+    ld = ld if ld is not None else cols
+    r0, c0 = pad_rows, 0
+    buf_rows = rows + 2 * pad_rows
+    buf = torch.empty((buf_rows, ld + 32), dtype=dtype, device="cuda:0")
+    if dtype.is_floating_point:
+        buf.view(torch.uint8 if buf.element_size() == 1 else (torch.int16 if buf.element_size() == 2 else torch.int32)).fill_(fill)
+    else:
+        buf.fill_(fill)
+    view = buf[r0:r0 + rows, c0:c0 + cols]
+    return view, buf, (r0, c0)
+
+
+def check_guard(buf, origin, rows, cols, fill=SENTINEL):
+    """Every element of buf outside the [rows x cols] view at origin still holds the sentinel."""
+    r0, c0 = origin
+    host = buf.detach().cpu()
+    if host.element_size() == 1:
+        raw = host.view(torch.uint8).numpy()
+        expect = fill
+    elif host.element_size() == 2:
+        raw = host.view(torch.int16).numpy().view(np.uint16)
+        expect = np.array(fill, np.int16).view(np.uint16)
+    else:
+        raw = host.view(torch.int32).numpy().view(np.uint32)
+        expect = np.array(fill, np.int32).view(np.uint32)
+    mask = np.ones(raw.shape, bool)
+    mask[r0:r0 + rows, c0:c0 + cols] = False
+    bad = np.nonzero(raw[mask] != expect)[0]
+    assert bad.size == 0, f"{bad.size} writes outside the output view"
+
+
+def assert_codes_equal(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    if bad.size:
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} mismatches, first at {i}: gpu {got[i]!r} oracle {want[i]!r}")
+
+
+def assert_f32_bits_equal(got, want, what):
+    """Bitwise equality of fp32 arrays, treating any NaN as equal to any NaN."""
+    g = np.asarray(got, np.float32)
+    w = np.asarray(want, np.float32)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    same = (g.view(np.uint32) == w.view(np.uint32)) | (np.isnan(g) & np.isnan(w))
+    bad = np.argwhere(~same)
+    if bad.size:
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} mismatches, first at {i}: gpu {g[i]!r} oracle {w[i]!r}")

@@ -1,0 +1,136 @@
+"""The C ABI library loads, exports every function include/fp8amax.h declares,
+and rejects bad arguments on the host before anything is launched. CPU only:
+no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8amax.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fp8_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    import fp8_scaled_gemm_amax_amd as m
+    return m
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("fp8_amax", "fp8_quantize_tensor", "fp8_quantize_row", "fp8_quantize_col",
+                     "fp8_delayed_scale_update", "fp8_gemm_scaled", "fp8_grouped_gemm_scaled",
+                     "fp8_query_device", "fp8_status_string", "fp8_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(fp8):
+    lib = ctypes.CDLL(fp8.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fp8.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\bT (fp8_\w+)", out.stdout))
+    assert set(declared_functions()) <= exported
+    assert set(fp8.EXPORTED_SYMBOLS) == set(declared_functions())
+
+
+def test_library_has_gfx950_code_object(fp8):
+    """The embedded offload bundle carries a gfx950 code object (bundle entry id)."""
+    blob = open(fp8.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_status_strings(fp8):
+    assert fp8.fp8_status_string(0) == "FP8_OK"
+    assert fp8.fp8_status_string(1) == "FP8_ERR_INVALID_ARG"
+    assert fp8.fp8_status_string(3) == "FP8_ERR_UNSUPPORTED"
+
+
+def _call(fp8, name, *args):
+    st = getattr(fp8.lib, name)(*args)
+    return st, fp8.lib.fp8_last_error().decode()
+
+
+FAKE = ctypes.c_void_p(0x10000)     # never dereferenced: every call below fails validation first
+
+
+def test_gemm_rejects_bad_arguments(fp8):
+    g = "fp8_gemm_scaled"
+    # k not a multiple of 16
+    st, msg = _call(fp8, g, FAKE, 0, 32, FAKE, 0, 32, 8, 8, 24, FAKE, 1, FAKE, 1, FAKE, 0, 8, None)
+    assert st == 1 and "multiple of 16" in msg
+    # negative size
+    st, _ = _call(fp8, g, FAKE, 0, 32, FAKE, 0, 32, -1, 8, 32, FAKE, 1, FAKE, 1, FAKE, 0, 8, None)
+    assert st == 1
+    # misaligned operand
+    st, _ = _call(fp8, g, ctypes.c_void_p(0x10001), 0, 32, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 0, 8, None)
+    assert st == 2
+    # lda not a multiple of 16
+    st, _ = _call(fp8, g, FAKE, 0, 40, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 0, 8, None)
+    assert st == 2
+    # fnuz operands: valid request, not run on gfx950 matrix cores
+    st, msg = _call(fp8, g, FAKE, 2, 32, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 0, 8, None)
+    assert st == 3 and "fnuz" in msg
+    # unknown format / output type / scale mode
+    assert _call(fp8, g, FAKE, 7, 32, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 0, 8, None)[0] == 1
+    assert _call(fp8, g, FAKE, 0, 32, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 5, 8, None)[0] == 1
+    assert _call(fp8, g, FAKE, 0, 32, FAKE, 0, 32, 8, 8, 32, FAKE, 4, FAKE, 1, FAKE, 0, 8, None)[0] == 1
+    # NULL output
+    assert _call(fp8, g, FAKE, 0, 32, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, None, 0, 8, None)[0] == 1
+
+
+def test_grouped_gemm_rejects_bad_arguments(fp8):
+    g = "fp8_grouped_gemm_scaled"
+    ok_args = [FAKE, 0, 32, FAKE, 0, 32, 8 * 32, FAKE, 4, 64, 8, 32, FAKE, FAKE, FAKE, 0, 8, None]
+    bad = list(ok_args)
+    bad[8] = 0                      # no groups
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[7] = None                   # no offsets
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[6] = 8                      # group stride smaller than one weight
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[7] = ctypes.c_void_p(0x10004)
+    assert _call(fp8, g, *bad)[0] == 2
+
+
+def test_quantizers_reject_bad_arguments(fp8):
+    # margin out of range
+    st, msg = _call(fp8, "fp8_quantize_row", FAKE, 4, 16, 16, 0, 33, FAKE, 16, FAKE, None, None, None)
+    assert st == 1 and "margin" in msg
+    # ld smaller than the row
+    assert _call(fp8, "fp8_quantize_row", FAKE, 4, 16, 8, 0, 0, FAKE, 16, FAKE, None, None, None)[0] == 1
+    # unknown format
+    assert _call(fp8, "fp8_quantize_row", FAKE, 4, 16, 16, 9, 0, FAKE, 16, FAKE, None, None, None)[0] == 1
+    # x misaligned for bf16
+    assert _call(fp8, "fp8_quantize_row", ctypes.c_void_p(0x10001), 4, 16, 16, 0, 0, FAKE, 16, FAKE, None, None,
+                 None)[0] == 2
+    # tensorwise needs scale_inv_out and amax_out
+    assert _call(fp8, "fp8_quantize_tensor", FAKE, 4, 16, 16, 0, 0, None, FAKE, 16, None, FAKE, None)[0] == 1
+    # colwise: transposed output needs ldqt >= rows; col_amax_ready must be 0/1
+    assert _call(fp8, "fp8_quantize_col", FAKE, 64, 16, 16, 0, 0, FAKE, 32, FAKE, FAKE, 0, None)[0] == 1
+    assert _call(fp8, "fp8_quantize_col", FAKE, 64, 16, 16, 0, 0, FAKE, 64, FAKE, FAKE, 2, None)[0] == 1
+    # amax: unknown axis
+    assert _call(fp8, "fp8_amax", FAKE, 4, 16, 16, 3, FAKE, None)[0] == 1
+
+
+def test_delayed_update_rejects_bad_arguments(fp8):
+    f = "fp8_delayed_scale_update"
+    assert _call(fp8, f, FAKE, FAKE, FAKE, 2, 0, 1, 0, 0, FAKE, FAKE, None)[0] == 1        # L = 0
+    assert _call(fp8, f, FAKE, FAKE, FAKE, 2, 1024, 2, 0, 0, FAKE, FAKE, None)[0] == 1     # algo
+    assert _call(fp8, f, FAKE, FAKE, None, 2, 1024, 1, 0, 0, FAKE, FAKE, None)[0] == 1     # head
+    assert _call(fp8, f, FAKE, FAKE, FAKE, 2, 1024, 1, -1, 0, FAKE, FAKE, None)[0] == 1    # margin
+
+
+def test_query_device_rejects_null(fp8):
+    assert fp8.lib.fp8_query_device(0, None) == 1

@@ -1,0 +1,171 @@
+"""GPU parity of the scaled FP8 GEMM and grouped GEMM against the CPU oracle,
+through the C ABI. Acceptance per output element:
+    |gpu - oracle| <= 1e-3 * sa*sb*sum_k |a_ik b_jk|  +  2^-8 |oracle|   (bf16 out)
+(the second term is dropped for fp32 output): the first covers fp32
+accumulation over k <= 16384, the second bf16 rounding of the result."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from helpers import check_guard, dev_f32, dev_u8, guarded, say
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(0, 0), (1, 0), (0, 1), (1, 1)]
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    import fp8_scaled_gemm_amax_amd as m
+    return m
+
+
+def operands(orc, rows, k, fmt, seed, spread=4):
+    """FP8 codes and per-row scale_inv of a random bf16 matrix (quantized by the oracle)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, k)).astype(np.float32)
+    x *= np.exp2(rng.integers(-spread, spread + 1, size=(rows, 1))).astype(np.float32)
+    q, si, _ = orc.quantize_row(workloads.bf16_bits(x), fmt)
+    return q, si
+
+
+def gpu_gemm(fp8, a, fa, b, fb, sa, sb, a_mode, b_mode, out_f32=False, ldd=None):
+    m, n = a.shape[0], b.shape[0]
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    d, dbuf, org = guarded(m, n, dt, ld=ldd)
+    fp8.fp8_gemm_scaled(dev_u8(a), fa, dev_u8(b), fb, dev_f32(sa), a_mode, dev_f32(sb), b_mode, d)
+    torch.cuda.synchronize()
+    check_guard(dbuf, org, m, n)
+    return d.float().cpu().numpy().astype(np.float64)
+
+
+def assert_within(orc, got, y, bound, out_bf16, what):
+    ok = orc.gemm_within_bound(got, y, bound, out_bf16=out_bf16)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} of {ok.size} outside the bound; first {i}: gpu {got[i]!r} "
+                             f"oracle {y[i]!r} bound {bound[i]!r}")
+
+
+def test_layout_identity(fp8, orc):
+    """B = identity: d must be dequant(A) times the scales, element for element
+    (pins the operand and accumulator lane layouts)."""
+    rng = np.random.default_rng(0)
+    m, k = 96, 64
+    a = rng.integers(0, 0x7E, (m, k)).astype(np.uint8)
+    a |= (rng.integers(0, 2, (m, k)) << 7).astype(np.uint8)
+    one = 0x38                                          # e4m3 1.0
+    b = np.zeros((k, k), np.uint8)
+    b[np.arange(k), np.arange(k)] = one
+    sa = np.exp2(rng.integers(-2, 3, m)).astype(np.float32)
+    say("layout identity")
+    got = gpu_gemm(fp8, a, 0, b, 0, sa, np.float32([1.0]), 1, 0, out_f32=True)
+    want = orc.decode(0, a) * sa[:, None].astype(np.float64)
+    assert np.array_equal(got, want)
+
+
+def test_layout_single_entries(fp8, orc):
+    """One nonzero per operand row at distinct k: each output is a single product."""
+    m, n, k = 64, 64, 128
+    a = np.zeros((m, k), np.uint8)
+    b = np.zeros((n, k), np.uint8)
+    for i in range(m):
+        a[i, (3 * i) % k] = 0x38 + (i % 8)              # 1.0 .. 1.875
+    for j in range(n):
+        b[j, (3 * j) % k] = 0x40                        # 2.0
+    say("layout single entries")
+    got = gpu_gemm(fp8, a, 0, b, 0, np.float32([1.0]), np.float32([1.0]), 0, 0, out_f32=True)
+    y, bound = orc.gemm(a, 0, b, 0, np.float32(1.0), np.float32(1.0))
+    assert np.array_equal(got, y)
+
+
+SHAPES = [(32, 32, 64), (128, 128, 128), (256, 512, 512), (300, 520, 1040), (1, 1, 16), (17, 33, 48),
+          (129, 257, 272), (255, 130, 4096), (0, 5, 16), (5, 0, 16), (4, 4, 0)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("fa,fb", PAIRS)
+def test_gemm_parity(fp8, orc, shape, fa, fb):
+    m, n, k = shape
+    a, sa = operands(orc, m, k, fa, seed=m + 3 * k)
+    b, sb = operands(orc, n, k, fb, seed=n + 5 * k + 1)
+    y, bound = orc.gemm(a, fa, b, fb, sa, sb)
+    say("gemm", shape, fa, fb, "bf16")
+    got = gpu_gemm(fp8, a, fa, b, fb, sa, sb, 1, 1, ldd=n + 8)
+    assert_within(orc, got, y, bound, True, f"{shape} {fa}x{fb} bf16")
+    say("gemm", shape, fa, fb, "f32 tensor scales")
+    sa0, sb0 = np.float32([0.37]), np.float32([2.5])
+    y0, bound0 = orc.gemm(a, fa, b, fb, sa0, sb0)
+    got = gpu_gemm(fp8, a, fa, b, fb, sa0, sb0, 0, 0, out_f32=True)
+    assert_within(orc, got, y0, bound0, False, f"{shape} {fa}x{fb} f32")
+
+
+def test_gemm_mixed_scale_modes(fp8, orc):
+    m, n, k = 200, 136, 320
+    a, sa = operands(orc, m, k, 0, seed=1)
+    b, sb = operands(orc, n, k, 1, seed=2)
+    for sa_x, am, sb_x, bm in ((sa, 1, np.float32([3.0]), 0), (np.float32([0.5]), 0, sb, 1)):
+        say("gemm mixed modes", am, bm)
+        y, bound = orc.gemm(a, 0, b, 1, sa_x, sb_x)
+        got = gpu_gemm(fp8, a, 0, b, 1, sa_x, sb_x, am, bm)
+        assert_within(orc, got, y, bound, True, f"modes {am}{bm}")
+
+
+def test_gemm_nan_inf_codes(fp8, orc):
+    """NaN codes propagate to their output row/column; e5m2 Inf codes give Inf or NaN as in fp64."""
+    m, n, k = 64, 64, 64
+    a, sa = operands(orc, m, k, 1, seed=3)
+    b, sb = operands(orc, n, k, 1, seed=4)
+    a[3, 5] = 0x7F          # e5m2 NaN
+    b[7, 9] = 0x7C          # e5m2 +Inf
+    say("gemm nan/inf")
+    y, bound = orc.gemm(a, 1, b, 1, sa, sb)
+    got = gpu_gemm(fp8, a, 1, b, 1, sa, sb, 1, 1, out_f32=True)
+    assert np.array_equal(np.isnan(got), np.isnan(y))
+    fin = np.isfinite(y)
+    assert_within(orc, np.where(fin, got, 0), np.where(fin, y, 0), np.where(fin, bound, 0), False, "finite part")
+
+
+def test_gemm_deterministic(fp8, orc):
+    a, sa = operands(orc, 300, 1040, 0, seed=5)
+    b, sb = operands(orc, 520, 1040, 0, seed=6)
+    say("gemm determinism")
+    g1 = gpu_gemm(fp8, a, 0, b, 0, sa, sb, 1, 1)
+    g2 = gpu_gemm(fp8, a, 0, b, 0, sa, sb, 1, 1)
+    assert np.array_equal(g1, g2)
+
+
+# ------------------------------------------------------------------- grouped --
+
+def gpu_grouped(fp8, a, fa, b, fb, offsets, sa, sb, out_f32=False):
+    total, n = a.shape[0], b.shape[1]
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    d, dbuf, org = guarded(total, n, dt)
+    fp8.fp8_grouped_gemm_scaled(dev_u8(a), fa, dev_u8(b), fb, torch.from_numpy(offsets).to("cuda:0"),
+                                dev_f32(sa), dev_f32(sb), d)
+    torch.cuda.synchronize()
+    check_guard(dbuf, org, total, n)
+    return d.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("sizes", [[0, 1, 17, 255, 257], [300], [0, 0, 129, 0], [128, 128, 1, 0, 127],
+                                   [5] * 40])
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0)])
+def test_grouped_gemm_parity(fp8, orc, sizes, fa, fb):
+    g, n, k = len(sizes), 136, 272
+    offsets = np.zeros(g + 1, np.int64)
+    offsets[1:] = np.cumsum(sizes)
+    total = int(offsets[-1])
+    a, sa = operands(orc, total, k, fa, seed=7)
+    bq = [operands(orc, n, k, fb, seed=100 + e) for e in range(g)]
+    b = np.stack([q for q, _ in bq])
+    sb = np.stack([s for _, s in bq])
+    say("grouped", sizes, fa, fb)
+    y, bound = orc.grouped_gemm(a, fa, b, fb, offsets, sa, sb)
+    got = gpu_grouped(fp8, a, fa, b, fb, offsets, sa, sb)
+    assert_within(orc, got, y, bound, True, f"grouped {sizes}")
+    if g == 1:
+        dense = gpu_gemm(fp8, a, fa, b[0], fb, sa, sb[0], 1, 1)
+        assert np.array_equal(dense, got), "one group equals the dense GEMM"

@@ -1,0 +1,317 @@
+"""GPU parity of the amax, quantizer and delayed-update kernels against the CPU
+oracle, through the C ABI. Codes, scales, amax and the delayed state must be
+bit-identical (the cast has a unique result)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from helpers import (assert_codes_equal, assert_f32_bits_equal, check_guard, dev_bf16, dev_f32, guarded,
+                     host_bits, say)
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [0, 1, 2, 3]
+NAMES = {0: "e4m3", 1: "e5m2", 2: "e4m3fnuz", 3: "e5m2fnuz"}
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    import fp8_scaled_gemm_amax_amd as m
+    return m
+
+
+def rand_bf16(rows, cols, seed, spread=8):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(-spread, spread + 1, size=(rows, 1))).astype(np.float32)
+    return workloads.bf16_bits(x)
+
+
+def gpu_row(fp8, xb, fmt, margin=0, ldq=None, col_amax=False):
+    x = dev_bf16(xb)
+    rows, cols = xb.shape
+    q, qbuf, org = guarded(rows, cols, torch.uint8, ld=ldq)
+    si = torch.full((rows,), -1.0, device="cuda:0")
+    am = torch.full((rows,), -1.0, device="cuda:0")
+    ca = torch.full((cols,), -1.0, device="cuda:0") if col_amax else None
+    fp8.fp8_quantize_row(x, fmt, margin, q, si, am, ca)
+    torch.cuda.synchronize()
+    check_guard(qbuf, org, rows, cols)
+    return q.cpu().numpy(), si.cpu().numpy(), am.cpu().numpy(), (ca.cpu().numpy() if col_amax else None)
+
+
+def gpu_col(fp8, xb, fmt, margin=0, ldqt=None, ready=None):
+    x = dev_bf16(xb)
+    rows, cols = xb.shape
+    qt, qbuf, org = guarded(cols, rows, torch.uint8, ld=ldqt)
+    si = torch.full((cols,), -1.0, device="cuda:0")
+    ca = dev_f32(ready) if ready is not None else torch.full((cols,), -1.0, device="cuda:0")
+    fp8.fp8_quantize_col(x, fmt, margin, qt, si, ca, col_amax_ready=ready is not None)
+    torch.cuda.synchronize()
+    check_guard(qbuf, org, cols, rows)
+    return qt.cpu().numpy(), si.cpu().numpy(), ca.cpu().numpy()
+
+
+# ------------------------------------------------------------------- the cast --
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_cast_every_bf16_value_times_scales(fp8, orc, fmt):
+    """All 65536 bf16 values (NaN, Inf, subnormals, both zeros, every tie
+    between FP8 neighbours) cast with a range of scales, through the tensorwise
+    quantizer with a given (delayed) scale."""
+    xb = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    x = dev_bf16(xb)
+    rng = np.random.default_rng(fmt)
+    scales = [1.0, 2.0 ** -7, 2.0 ** 9, 0.75, 1.0 / 3.0, 3.0e-5, 1.0e5, float(np.float32(448.0 / 3.0)),
+              float(np.float32(0.6)), 1.2e-38] + rng.uniform(0.01, 100.0, 6).tolist()
+    for s in scales:
+        s32 = np.float32(s)
+        say("cast", NAMES[fmt], "scale", float(s32))
+        q = torch.empty((256, 256), dtype=torch.uint8, device="cuda:0")
+        si = torch.empty(1, device="cuda:0")
+        am = torch.zeros(1, device="cuda:0")
+        fp8.fp8_quantize_tensor(x, fmt, 0, dev_f32([s32]), q, si, am)
+        torch.cuda.synchronize()
+        oq, osi, oam = orc.quantize_tensor_scaled(xb, fmt, s32)
+        assert_codes_equal(q.cpu().numpy(), oq, f"{NAMES[fmt]} s={s32}")
+        assert_f32_bits_equal(si.cpu().numpy(), [osi], "scale_inv")
+        assert_f32_bits_equal(am.cpu().numpy(), [oam], "amax")
+
+
+# ----------------------------------------------------------------------- rows --
+
+ROW_SHAPES = [(1, 16), (3, 48), (37, 200), (256, 512), (300, 4104), (64, 14336), (9, 16392), (5, 0)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("shape", ROW_SHAPES)
+def test_quantize_row_parity(fp8, orc, fmt, shape):
+    rows, cols = shape
+    xb = rand_bf16(rows, cols, seed=rows * 7 + cols)
+    for margin in (0, 1, 2) if rows * cols < 2e5 else (0,):
+        say("row", NAMES[fmt], shape, "margin", margin)
+        q, si, am, _ = gpu_row(fp8, xb, fmt, margin)
+        oq, osi, oam = orc.quantize_row(xb, fmt, margin)
+        assert_codes_equal(q, oq, f"codes {shape}")
+        assert_f32_bits_equal(si, osi, "scale_inv")
+        assert_f32_bits_equal(am, oam, "amax")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("shape", [(5, 37), (33, 203), (2, 1)])
+def test_quantize_row_unaligned_layouts(fp8, orc, fmt, shape):
+    """Widths that are not a multiple of 8 and a padded output stride take the
+    scalar kernels."""
+    rows, cols = shape
+    xb = rand_bf16(rows, cols, seed=3)
+    say("row scalar", NAMES[fmt], shape)
+    q, si, am, _ = gpu_row(fp8, xb, fmt, 1, ldq=cols + 3)
+    oq, osi, oam = orc.quantize_row(xb, fmt, 1)
+    assert_codes_equal(q, oq, "codes")
+    assert_f32_bits_equal(si, osi, "scale_inv")
+    assert_f32_bits_equal(am, oam, "amax")
+
+
+def special_rows():
+    """Rows of zeros, NaN, +-Inf, bf16 subnormals, a single nonzero, huge and tiny values."""
+    f = np.float32
+    rows = [
+        [0.0] * 16,
+        [-0.0] * 8 + [0.0] * 8,
+        [1.0, np.nan] + [2.0] * 14,
+        [np.inf, -1.0] + [0.5] * 14,
+        [-np.inf] + [0.0] * 15,
+        [1e-40, -3e-41, 9e-39, 0.0] * 4,                     # bf16 subnormals
+        [0.0] * 15 + [-7.0],
+        [3.0e38, -1.0, 1.0, 2.0] * 4,
+        [2.0 ** -133] + [0.0] * 15,                          # smallest bf16 subnormal: s overflows to FLT_MAX
+        [448.0, 464.0, 480.0, 57344.0, 61440.0, -240.0, -232.0, 0.001] * 2,
+    ]
+    return workloads.bf16_bits(np.array(rows, dtype=f))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_quantize_row_special_values(fp8, orc, fmt):
+    xb = special_rows()
+    for margin in (0, 2):
+        say("row specials", NAMES[fmt], margin)
+        q, si, am, ca = gpu_row(fp8, xb, fmt, margin, col_amax=True)
+        oq, osi, oam = orc.quantize_row(xb, fmt, margin)
+        assert_codes_equal(q, oq, "codes")
+        assert_f32_bits_equal(si, osi, "scale_inv")
+        assert_f32_bits_equal(am, oam, "amax")
+        assert_f32_bits_equal(ca, orc.amax(xb, orc.AXIS_COL), "col amax side output")
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (130, 72), (1, 8)])
+def test_quantize_row_col_amax_side_output(fp8, orc, shape):
+    xb = rand_bf16(*shape, seed=11)
+    say("row + col amax", shape)
+    q, si, am, ca = gpu_row(fp8, xb, 0, 0, col_amax=True)
+    assert_f32_bits_equal(ca, orc.amax(xb, orc.AXIS_COL), "col amax")
+    assert_codes_equal(q, orc.quantize_row(xb, 0)[0], "codes")
+
+
+# -------------------------------------------------------------------- columns --
+
+COL_SHAPES = [(1, 8), (128, 64), (130, 72), (257, 136), (1000, 520), (64, 4104), (3, 48)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("shape", COL_SHAPES)
+def test_quantize_col_parity(fp8, orc, fmt, shape):
+    rows, cols = shape
+    xb = rand_bf16(rows, cols, seed=rows + 13 * cols)
+    say("col", NAMES[fmt], shape)
+    qt, si, ca = gpu_col(fp8, xb, fmt, margin=1)
+    oqt, osi, oam = orc.quantize_col(xb, fmt, 1)
+    assert_codes_equal(qt, oqt, f"codes {shape}")
+    assert_f32_bits_equal(si, osi, "scale_inv")
+    assert_f32_bits_equal(ca, oam, "col amax")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("shape,ldqt", [((130, 72), 136), ((100, 40), 103), ((33, 37), None), ((17, 3), None)])
+def test_quantize_col_layouts(fp8, orc, fmt, shape, ldqt):
+    """Output strides that break 16-byte stores, and widths off the 8-column
+    grid (scalar kernel)."""
+    rows, cols = shape
+    xb = rand_bf16(rows, cols, seed=5)
+    say("col layout", NAMES[fmt], shape, ldqt)
+    qt, si, ca = gpu_col(fp8, xb, fmt, ldqt=ldqt)
+    oqt, osi, oam = orc.quantize_col(xb, fmt, 0)
+    assert_codes_equal(qt, oqt, "codes")
+    assert_f32_bits_equal(si, osi, "scale_inv")
+
+
+def test_quantize_col_with_ready_amax(fp8, orc):
+    xb = rand_bf16(300, 136, seed=9)
+    ready = orc.amax(xb, orc.AXIS_COL)
+    say("col ready amax")
+    qt, si, ca = gpu_col(fp8, xb, 1, ready=ready)
+    oqt, osi, _ = orc.quantize_col(xb, 1, 0)
+    assert_codes_equal(qt, oqt, "codes")
+    assert_f32_bits_equal(si, osi, "scale_inv")
+
+
+def test_quantize_col_special_values(fp8, orc):
+    xb = np.ascontiguousarray(special_rows().T)      # specials down the columns
+    for fmt in FORMATS:
+        say("col specials", NAMES[fmt])
+        qt, si, ca = gpu_col(fp8, xb, fmt)
+        oqt, osi, oam = orc.quantize_col(xb, fmt, 0)
+        assert_codes_equal(qt, oqt, "codes")
+        assert_f32_bits_equal(si, osi, "scale_inv")
+        assert_f32_bits_equal(ca, oam, "amax")
+
+
+# ----------------------------------------------------------------------- amax --
+
+@pytest.mark.parametrize("shape", [(1, 8), (37, 200), (513, 1032), (7, 13), (0, 16), (16, 0)])
+def test_amax_all_axes(fp8, orc, shape):
+    xb = rand_bf16(*shape, seed=17) if shape[0] * shape[1] else np.zeros(shape, np.uint16)
+    if xb.size:
+        xb[shape[0] // 2, shape[1] // 3] = workloads.bf16_bits(np.float32([-1e30]))[0]
+    x = dev_bf16(xb) if xb.size else torch.zeros(shape, dtype=torch.bfloat16, device="cuda:0")
+    for axis, n in ((0, 1), (1, shape[0]), (2, shape[1])):
+        say("amax", shape, "axis", axis)
+        out = torch.full((max(n, 1),), -1.0, device="cuda:0")
+        fp8.fp8_amax(x, axis, out)
+        torch.cuda.synchronize()
+        want = orc.amax(xb, axis) if xb.size else np.zeros(n, np.float32)
+        assert_f32_bits_equal(out.cpu().numpy()[:n], want, f"axis {axis}")
+
+
+# ----------------------------------------------------------------- tensorwise --
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("shape", [(37, 200), (300, 4104), (5, 37)])
+def test_quantize_tensor_current(fp8, orc, fmt, shape):
+    xb = rand_bf16(*shape, seed=23)
+    x = dev_bf16(xb)
+    say("tensor current", NAMES[fmt], shape)
+    q = torch.empty(shape, dtype=torch.uint8, device="cuda:0")
+    si = torch.empty(1, device="cuda:0")
+    am = torch.full((1,), 123.0, device="cuda:0")      # overwritten in current mode
+    fp8.fp8_quantize_tensor(x, fmt, 1, None, q, si, am)
+    torch.cuda.synchronize()
+    oq, osi, oam = orc.quantize_tensor_current(xb, fmt, 1)
+    assert_codes_equal(q.cpu().numpy(), oq, "codes")
+    assert_f32_bits_equal(si.cpu().numpy(), [osi], "scale_inv")
+    assert_f32_bits_equal(am.cpu().numpy(), [oam], "amax")
+
+
+def test_quantize_tensor_delayed_folds_amax(fp8, orc):
+    xb = rand_bf16(64, 96, seed=29)
+    x = dev_bf16(xb)
+    q = torch.empty((64, 96), dtype=torch.uint8, device="cuda:0")
+    si = torch.empty(1, device="cuda:0")
+    am = dev_f32([1e9])                                  # larger than the tensor's amax: kept
+    say("tensor delayed fold")
+    fp8.fp8_quantize_tensor(x, 0, 0, dev_f32([3.5]), q, si, am)
+    torch.cuda.synchronize()
+    oq, osi, oam = orc.quantize_tensor_scaled(xb, 0, np.float32(3.5), amax_in=1e9)
+    assert am.item() == oam == np.float32(1e9)
+    assert_codes_equal(q.cpu().numpy(), oq, "codes")
+
+
+# ----------------------------------------------------------- delayed scaling --
+
+def run_delayed(fp8, orc, amaxes, n, L, algo, margin, fmt):
+    hist = torch.zeros((n, L), device="cuda:0")
+    head = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    scale = torch.ones(n, device="cuda:0")
+    scale_inv = torch.ones(n, device="cuda:0")
+    cur = torch.zeros(n, device="cuda:0")
+    st = orc.DelayedState(n, L)
+    for t, a in enumerate(amaxes):
+        cur.copy_(torch.from_numpy(np.asarray(a, np.float32)))
+        st.cur_amax[:] = a
+        fp8.fp8_delayed_scale_update(cur, hist, head, algo, margin, fmt, scale, scale_inv)
+        st.update(algo, margin, fmt)
+        if t % 97 == 0 or t == len(amaxes) - 1:
+            torch.cuda.synchronize()
+            assert_f32_bits_equal(scale.cpu().numpy(), st.scale, f"scale step {t}")
+            assert_f32_bits_equal(scale_inv.cpu().numpy(), st.scale_inv, f"scale_inv step {t}")
+            assert_f32_bits_equal(hist.cpu().numpy(), st.history, f"history step {t}")
+            assert head.item() == st.head[0]
+            assert not cur.any().item()
+
+
+@pytest.mark.parametrize("algo", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_delayed_update_hand_sequence(fp8, orc, algo, fmt):
+    say("delayed hand", algo, fmt)
+    seq = [[8.0], [1.0], [1.0], [1.0], [1.0], [1.0], [0.0], [np.nan], [np.inf], [2.0]]
+    run_delayed(fp8, orc, seq, 1, 4, algo, 1, fmt)
+
+
+def test_delayed_update_wraps_at_1024(fp8, orc):
+    rng = np.random.default_rng(2)
+    amaxes = np.exp2(rng.uniform(-6, 6, (1100, 3))).astype(np.float32)
+    amaxes[5] = [900.0, 1e-3, 0.0]
+    say("delayed 1024 wrap")
+    run_delayed(fp8, orc, amaxes, 3, 1024, 1, 0, 0)
+
+
+def test_delayed_update_many_tensors(fp8, orc):
+    rng = np.random.default_rng(3)
+    amaxes = np.exp2(rng.uniform(-6, 6, (20, 37))).astype(np.float32)
+    say("delayed 37 tensors")
+    run_delayed(fp8, orc, amaxes, 37, 16, 1, 2, 1)
+
+
+# ------------------------------------------------------------- determinism --
+
+def test_quantizers_deterministic(fp8):
+    xb = rand_bf16(1000, 520, seed=31)
+    say("determinism")
+    a = gpu_row(fp8, xb, 0, col_amax=True)
+    b = gpu_row(fp8, xb, 0, col_amax=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    c = gpu_col(fp8, xb, 1)
+    d = gpu_col(fp8, xb, 1)
+    for u, v in zip(c, d):
+        assert np.array_equal(u, v)
