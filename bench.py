@@ -1,0 +1,305 @@
+"""Benchmark of the FP8 linear layer hot path on one MI355X.
+
+A step is one pass of the layer over one batch of synthetic input, inputs
+resident in HBM: quantize the activation and the weight (amax -> scale ->
+saturating cast) and run the scaled FP8 GEMM. The default workload is the
+Llama3-8B FFN up-projection, rowwise e4m3: X bf16 [8192 x 4096] (Student-t,
+unit variance), W bf16 [14336 x 4096] ~ N(0, 0.02^2), bf16 output.
+
+Prints one JSON line: value = 2*M*N*K / (time per step) in TFLOP/s including
+the quantizers; per-kernel durations come from HIP events recorded on the
+stream the kernels run on; `roofline` is for the GEMM (the dominant kernel)
+against MI355X's dense FP8 peak; `quantizers` gives each quantizer's
+algorithmic GB/s (2 B read + 1 B written per element + 4 B per scale) against
+8 TB/s; `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload on this host's cores.
+
+Other workloads (--workload c1|c3|c4|c5) print the same line for the other
+shapes (c3 tensorwise delayed, c4 MoE grouped GEMM, c5 hybrid backward).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 scaled-GEMM TFLOP/s incl. quantize; quantizer GB/s; % of MI355X peak"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 matrix throughput (no sparsity)
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the CPU-oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def bf16_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+class Step:
+    """Holds device buffers of one workload and enqueues one step, recording an
+    event after each kernel-level call."""
+
+    def __init__(self, name):
+        import torch
+
+        import fp8_scaled_gemm_amax_amd as fp8
+        import workloads
+        self.fp8, self.torch, self.name = fp8, torch, name
+        dev = "cuda:0"
+        E = torch.empty
+        if name in ("c1", "c2"):
+            w = workloads.c1() if name == "c1" else workloads.c2()
+            self.x, self.w = bf16_dev(w["x"]), bf16_dev(w["w"])
+            self.cpu_sample = (w["x"], 0, w["w"], 0)
+            m, k = self.x.shape
+            n = self.w.shape[0]
+            self.qx, self.qw = E((m, k), dtype=torch.uint8, device=dev), E((n, k), dtype=torch.uint8, device=dev)
+            self.sx, self.sw = E(m, device=dev), E(n, device=dev)
+            self.d = E((m, n), dtype=torch.bfloat16, device=dev)
+            self.mnk = [(m, n, k)]
+            self.calls = [("quantize_row X", m * k, m), ("quantize_row W", n * k, n), ("gemm", None, 0)]
+            self.desc = {"c1": "rowwise FP8 linear Y = X W^T, X bf16 [256x512] N(0,1) with 2 rows x50, "
+                               "W bf16 [512x512] N(0,0.02^2); e4m3 rowwise both operands; bf16 out",
+                         "c2": "Llama3-8B FFN up-proj rowwise FP8: X bf16 [8192x4096] Student-t(4)/sqrt(2), "
+                               "W bf16 [14336x4096] N(0,0.02^2); e4m3 row/col scales; bf16 out"}[name]
+            self.scales = {"recipe": "rowwise", "format": "e4m3"}
+        elif name == "c3":
+            w = workloads.c3()
+            self.w = bf16_dev(w["w"])
+            _, xb = next(w["x_steps"]())
+            self.x = bf16_dev(xb)
+            self.cpu_sample = (xb, 0, w["w"], 0)
+            m, k = self.x.shape
+            n = self.w.shape[0]
+            self.qx, self.qw = E((m, k), dtype=torch.uint8, device=dev), E((n, k), dtype=torch.uint8, device=dev)
+            self.six, self.siw = E(1, device=dev), E(1, device=dev)
+            self.hist = torch.zeros((2, 1024), device=dev)
+            self.head = torch.zeros(1, dtype=torch.int32, device=dev)
+            self.scale = torch.ones(2, device=dev)
+            self.scale_inv = torch.ones(2, device=dev)
+            self.cur = torch.zeros(2, device=dev)
+            self.d = E((m, n), dtype=torch.bfloat16, device=dev)
+            self.mnk = [(m, n, k)]
+            self.calls = [("quantize_tensor X (delayed)", m * k, 1), ("quantize_tensor W (delayed)", n * k, 1),
+                          ("gemm", None, 0), ("delayed_scale_update", 0, 0)]
+            self.desc = ("Flux-12B MLP linear, tensorwise delayed scaling: X bf16 [4608x3072] N(0,1), "
+                         "W bf16 [12288x3072] N(0,0.02^2); history 1024, algo max, margin 0; bf16 out")
+            self.scales = {"recipe": "delayed", "format": "e4m3"}
+        elif name == "c4":
+            w = workloads.c4()
+            g, n, k = w["w"].shape
+            self.x = bf16_dev(w["x"])
+            self.w = bf16_dev(w["w"].reshape(g * n, k))
+            self.offsets = torch.from_numpy(w["offsets"]).to(dev)
+            self.cpu_sample = (w["x"], 0, w["w"][0], 0)
+            m = self.x.shape[0]
+            self.g, self.n, self.k = g, n, k
+            self.qx, self.qw = E((m, k), dtype=torch.uint8, device=dev), E((g * n, k), dtype=torch.uint8, device=dev)
+            self.sx, self.sw = E(m, device=dev), E(g * n, device=dev)
+            self.d = E((m, n), dtype=torch.bfloat16, device=dev)
+            self.mnk = [(m, n, k)]
+            self.calls = [("quantize_row tokens", m * k, m), ("quantize_row expert W", g * n * k, g * n),
+                          ("grouped_gemm", None, 0)]
+            self.desc = ("DeepSeek-V3 MoE grouped GEMM, one GPU's share: 32 experts Zipf(1.1) counts (3 empty), "
+                         "tokens bf16 [16384x7168] N(0,1), W_e bf16 [2048x7168] N(0,0.006^2); e4m3 rowwise; bf16 out")
+            self.scales = {"recipe": "rowwise", "format": "e4m3"}
+        else:
+            w = workloads.c5()
+            self.x, self.w, self.dy = bf16_dev(w["x"]), bf16_dev(w["w"]), bf16_dev(w["dy"])
+            self.cpu_sample = (w["dy"], 1, np.ascontiguousarray(w["w"].T), 0)   # dgrad: dY rows, W^T rows
+            m, k = self.x.shape
+            n = self.w.shape[0]
+            self.qdy, self.sdy = E((m, n), dtype=torch.uint8, device=dev), E(m, device=dev)
+            self.cady = E(n, device=dev)
+            self.qdyt, self.sdyt = E((n, m), dtype=torch.uint8, device=dev), E(n, device=dev)
+            self.qwt, self.swt, self.caw = E((k, n), dtype=torch.uint8, device=dev), E(k, device=dev), E(k, device=dev)
+            self.qxt, self.sxt, self.cax = E((k, m), dtype=torch.uint8, device=dev), E(k, device=dev), E(k, device=dev)
+            self.dx = E((m, k), dtype=torch.bfloat16, device=dev)
+            self.dw = E((n, k), dtype=torch.bfloat16, device=dev)
+            self.mnk = [(m, k, n), (n, k, m)]
+            self.calls = [("quantize_row dY e5m2 (+col amax)", m * n, m), ("quantize_col dY^T e5m2", m * n, n),
+                          ("quantize_col W^T e4m3", n * k, k), ("quantize_col X^T e4m3", m * k, k),
+                          ("gemm dgrad", None, 0), ("gemm wgrad", None, 0)]
+            self.desc = ("hybrid backward of the Llama3-8B up-proj: dY bf16 [8192x14336] N(0,1e-3^2) e5m2; "
+                         "dgrad dX = dY W, wgrad dW = dY^T X with colwise token scales; bf16 out")
+            self.scales = {"recipe": "rowwise+colwise", "format": "e5m2 x e4m3"}
+        self.flops = sum(2.0 * m * n * k for m, n, k in self.mnk)
+
+    def run(self, ev):
+        """Enqueue one step; ev[i] is recorded after call i (ev[0] before the first)."""
+        f = self.fp8
+        ev[0].record()
+        if self.name in ("c1", "c2"):
+            f.fp8_quantize_row(self.x, f.E4M3, 0, self.qx, self.sx)
+            ev[1].record()
+            f.fp8_quantize_row(self.w, f.E4M3, 0, self.qw, self.sw)
+            ev[2].record()
+            f.fp8_gemm_scaled(self.qx, f.E4M3, self.qw, f.E4M3, self.sx, f.SCALE_VECTOR, self.sw, f.SCALE_VECTOR,
+                              self.d)
+            ev[3].record()
+        elif self.name == "c3":
+            f.fp8_quantize_tensor(self.x, f.E4M3, 0, self.scale[0:1], self.qx, self.six, self.cur[0:1])
+            ev[1].record()
+            f.fp8_quantize_tensor(self.w, f.E4M3, 0, self.scale[1:2], self.qw, self.siw, self.cur[1:2])
+            ev[2].record()
+            f.fp8_gemm_scaled(self.qx, f.E4M3, self.qw, f.E4M3, self.six, f.SCALE_TENSOR, self.siw, f.SCALE_TENSOR,
+                              self.d)
+            ev[3].record()
+            f.fp8_delayed_scale_update(self.cur, self.hist, self.head, f.AMAX_MAX, 0, f.E4M3, self.scale,
+                                       self.scale_inv)
+            ev[4].record()
+        elif self.name == "c4":
+            f.fp8_quantize_row(self.x, f.E4M3, 0, self.qx, self.sx)
+            ev[1].record()
+            f.fp8_quantize_row(self.w, f.E4M3, 0, self.qw, self.sw)
+            ev[2].record()
+            f.fp8_grouped_gemm_scaled(self.qx, f.E4M3, self.qw.view(self.g, self.n, self.k), f.E4M3, self.offsets,
+                                      self.sx, self.sw.view(self.g, self.n), self.d)
+            ev[3].record()
+        else:
+            f.fp8_quantize_row(self.dy, f.E5M2, 0, self.qdy, self.sdy, None, self.cady)
+            ev[1].record()
+            f.fp8_quantize_col(self.dy, f.E5M2, 0, self.qdyt, self.sdyt, self.cady, col_amax_ready=True)
+            ev[2].record()
+            f.fp8_quantize_col(self.w, f.E4M3, 0, self.qwt, self.swt, self.caw)
+            ev[3].record()
+            f.fp8_quantize_col(self.x, f.E4M3, 0, self.qxt, self.sxt, self.cax)
+            ev[4].record()
+            f.fp8_gemm_scaled(self.qdy, f.E5M2, self.qwt, f.E4M3, self.sdy, f.SCALE_VECTOR, self.swt, f.SCALE_VECTOR,
+                              self.dx)
+            ev[5].record()
+            f.fp8_gemm_scaled(self.qdyt, f.E5M2, self.qxt, f.E4M3, self.sdyt, f.SCALE_VECTOR, self.sxt,
+                              f.SCALE_VECTOR, self.dw)
+            ev[6].record()
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "fp8_scaled_gemm_amax_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(kernel_key)
+    if not rec or rec.get("source_digest") != source_digest(*rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(sample, target_s):
+    """The CPU oracle on a bounded sample of the workload's own tensors: the
+    first ms rows of the activation and the first ns rows of the weight
+    (K-contiguous) quantized rowwise, then the oracle's fp64
+    dequantize-and-matmul of the sample. Reported as 2*ms*ns*K / time in TFLOP/s."""
+    from oracle import oracle as orc
+    act, fa, wgt, fw = sample
+    k = act.shape[1]
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+
+    def run(ms, ns):
+        t0 = time.perf_counter()
+        qx, sx, _ = orc.quantize_row(act[:ms], fa)
+        qw, sw, _ = orc.quantize_row(wgt[:ns], fw)
+        orc.gemm(qx, fa, qw, fw, sx, sw, with_bound=False)
+        return time.perf_counter() - t0
+
+    ms = min(act.shape[0], 2048)
+    ns = min(wgt.shape[0], 512)
+    t = run(ms, ns)
+    if t < 0.5 * target_s and ns < wgt.shape[0]:      # scale the sample up to about target_s
+        ns = int(min(wgt.shape[0], max(ns, ns * target_s / t)))
+        t = run(ms, ns)
+    return {"value": round(2.0 * ms * ns * k / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{ms} activation rows x {ns} weight rows x K={k} of the workload's tensors: rowwise "
+                      f"quantize of both (oracle) + fp64 dequantize-and-matmul, {t:.1f} s on {threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    step = Step(args.workload)
+    ncalls = len(step.calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(args.steps)]
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)]
+    for _ in range(args.warmup):
+        step.run(wev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.run(ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_call_ms = [float(np.mean([ev[i][c].elapsed_time(ev[i][c + 1]) for i in range(args.steps)]))
+                   for c in range(ncalls)]
+    ms_step = elapsed / args.steps * 1e3
+    value = step.flops / (ms_step * 1e-3) / 1e12
+
+    gemm_idx = [i for i, (nm, _, _) in enumerate(step.calls) if "gemm" in nm]
+    g = gemm_idx[0]
+    gemm_flops = 2.0 * np.prod(step.mnk[0])
+    gemm_tflops = gemm_flops / (per_call_ms[g] * 1e-3) / 1e12
+    kernel_key = "grouped_gemm" if args.workload == "c4" else "gemm"
+    traffic = measured_traffic(f"{kernel_key}:{args.workload}")
+    roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                "kernel": step.calls[g][0], "avg_ms": round(per_call_ms[g], 5),
+                "flops_per_launch": gemm_flops}
+    quant = []
+    for i, (nm, elems, nscales) in enumerate(step.calls):
+        if elems:
+            nbytes = 3.0 * elems + 4.0 * nscales
+            gbps = nbytes / (per_call_ms[i] * 1e-3) / 1e9
+            quant.append({"kernel": nm, "avg_ms": round(per_call_ms[i], 5), "algorithmic_bytes": nbytes,
+                          "gbps": round(gbps, 1), "frac_of_hbm": round(gbps / PEAK_HBM_GBPS, 4)})
+    other = [{"kernel": nm, "avg_ms": round(per_call_ms[i], 5)} for i, (nm, e, _) in enumerate(step.calls)
+             if e == 0 or ("gemm" in nm and i != g)]
+    for o in other:
+        if "gemm" in o["kernel"]:
+            j = [i for i, (nm, _, _) in enumerate(step.calls) if nm == o["kernel"]][0]
+            m, n, k = step.mnk[1]
+            o["tflops"] = round(2.0 * m * n * k / (per_call_ms[j] * 1e-3) / 1e12, 2)
+    m, n, k = step.mnk[0]
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3" if args.workload != "c5" else "fp8_e5m2xe4m3",
+        "data": "synthetic",
+        "config": {"workload": step.desc, "m": m, "n": n, "k": k, **step.scales, "out": "bf16",
+                   "flops_per_step": step.flops},
+        "roofline": roofline, "quantizers": quant, "other_kernels": other,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(step.cpu_sample, args.cpu_seconds),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -107,7 +107,7 @@ def _mat(t, name, elem_size=None):
         raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
     if elem_size is not None and t.element_size() != elem_size:
         raise ValueError(f"{name} must have {elem_size}-byte elements, got {t.dtype}")
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    if t.numel() > 0 and t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit stride along its last dimension")
     return t.shape[0], t.shape[1], max(t.stride(0), t.shape[1], 1)
 
@@ -176,7 +176,7 @@ def fp8_grouped_gemm_scaled(a, fa, b, fb, group_offsets, a_scale_inv, b_scale_in
     """a [total_m x k] codes sorted by group; b [g x n x k] codes; group_offsets int64 [g+1]
     on the device; a_scale_inv [total_m]; b_scale_inv [g x n]; d [total_m x n]."""
     total_m, k, lda = _mat(a, "a", 1)
-    if b.dim() != 3 or b.element_size() != 1 or b.stride(2) != 1:
+    if b.dim() != 3 or b.element_size() != 1 or (b.numel() > 0 and b.shape[2] > 1 and b.stride(2) != 1):
         raise ValueError("b must be a [g x n x k] 1-byte tensor with unit last stride")
     g, n, kb = b.shape
     if kb != k:

@@ -105,12 +105,13 @@ fp8_status_t check_gemm_operands(const char* fn, const uint8_t* a, int fa, int64
     if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8_ERR_INVALID_ARG, "%s: unknown format (%d, %d)", fn, fa, fb);
     if (d_type != FP8_OUT_BF16 && d_type != FP8_OUT_F32) return fail(FP8_ERR_INVALID_ARG, "%s: unknown output type %d", fn, d_type);
     if (k % 16 != 0) return fail(FP8_ERR_INVALID_ARG, "%s: k = %lld is not a multiple of 16", fn, (long long)k);
-    if (lda < k || ldb < k || ldd < n) return fail(FP8_ERR_INVALID_ARG, "%s: leading dimension smaller than the row", fn);
+    if (lda < k || ldb < k || ldd < n || ldd < 1)
+        return fail(FP8_ERR_INVALID_ARG, "%s: leading dimension smaller than the row", fn);
     if (m > 0 && n > 0) {
         if (!d) return fail(FP8_ERR_INVALID_ARG, "%s: d is NULL", fn);
         if (k > 0 && (!a || !b)) return fail(FP8_ERR_INVALID_ARG, "%s: a or b is NULL", fn);
     }
-    if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0)
+    if (k > 0 && (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0))
         return fail(FP8_ERR_ALIGNMENT, "%s: a, b must be 16-byte aligned with lda, ldb multiples of 16", fn);
     if (!aligned(d, 4)) return fail(FP8_ERR_ALIGNMENT, "%s: d must be 4-byte aligned", fn);
     if (!ocp_fmt(fa) || !ocp_fmt(fb))

@@ -46,13 +46,12 @@ template <> struct FmtTraits<kE5M2Fnuz> {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Saturating clamp that leaves NaN as NaN. (fminf/fmaxf would turn NaN into a
-// bound, and the compiler folds them into v_med3_f32, so NaN is selected back.)
+// Saturating clamp for inputs known not to be NaN (the compiler folds it into
+// v_med3_f32; Inf saturates to +-fmax).
 template <int F>
 __device__ __forceinline__ float sat(float p) {
     constexpr float m = FmtTraits<F>::fmax;
-    float c = fminf(fmaxf(p, -m), m);
-    return __builtin_isnan(p) ? p : c;
+    return fminf(fmaxf(p, -m), m);
 }
 
 // Bit-level saturating round-to-nearest-even encode of one fp32 value; the
@@ -84,15 +83,22 @@ __device__ __forceinline__ uint32_t encode_sw(float p) {
 }
 
 // Encode four fp32 values (already multiplied by the scale) into one 32-bit
-// word, byte i = code of v_i. OCP encodings use gfx950's conversion
-// instructions (round to nearest even) on saturated inputs; fnuz uses encode_sw.
-template <int F>
+// word, byte i = code of v_i.
+//  - NAN_FREE: the caller knows none of the inputs is NaN (it checked the
+//    amax of the data). OCP encodings then use gfx950's conversion
+//    instructions (round to nearest even) on clamped inputs; their results
+//    equal encode_sw for every non-NaN input. (For NaN the instructions
+//    return one canonical code whatever the sign, while the cast defined here
+//    keeps the sign: sign|0x7F.)
+//  - otherwise, and for fnuz (which the conversion instructions do not
+//    produce), the bit-level encoder.
+template <int F, bool NAN_FREE>
 __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float v3) {
-    if constexpr (F == kE4M3) {
+    if constexpr (NAN_FREE && F == kE4M3) {
         int r = __builtin_amdgcn_cvt_pk_fp8_f32(sat<F>(v0), sat<F>(v1), 0, false);
         r = __builtin_amdgcn_cvt_pk_fp8_f32(sat<F>(v2), sat<F>(v3), r, true);
         return (uint32_t)r;
-    } else if constexpr (F == kE5M2) {
+    } else if constexpr (NAN_FREE && F == kE5M2) {
         int r = __builtin_amdgcn_cvt_pk_bf8_f32(sat<F>(v0), sat<F>(v1), 0, false);
         r = __builtin_amdgcn_cvt_pk_bf8_f32(sat<F>(v2), sat<F>(v3), r, true);
         return (uint32_t)r;
@@ -100,6 +106,9 @@ __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float 
         return encode_sw<F>(v0) | (encode_sw<F>(v1) << 8) | (encode_sw<F>(v2) << 16) | (encode_sw<F>(v3) << 24);
     }
 }
+
+// A bf16 magnitude (16 bits) above the Inf pattern is a NaN.
+__device__ __forceinline__ bool nan_bits16(uint32_t mag16) { return mag16 > 0x7f80u; }
 
 // Scale from amax for current scaling: fl32(fmax / amax) * 2^-margin, FLT_MAX if
 // the quotient overflows, 1 if amax is zero or not finite. The division is the

@@ -25,7 +25,7 @@ constexpr int kWaves = kBlock / 64;
 
 template <int F>
 __device__ __forceinline__ uint32_t encode1(float v) {
-    return encode4<F>(v, 0.0f, 0.0f, 0.0f) & 0xffu;
+    return encode_sw<F>(v);
 }
 
 __device__ __forceinline__ uint32_t word_absmax(uint32_t acc, uint4 v) {
@@ -35,11 +35,12 @@ __device__ __forceinline__ uint32_t word_absmax(uint32_t acc, uint4 v) {
     return pk_absmax(acc, v.w);
 }
 
-template <int F>
+// Eight bf16 values (one 16-byte chunk) times s -> eight codes.
+template <int F, bool NAN_FREE>
 __device__ __forceinline__ uint2 encode8(uint4 v, float s) {
     uint2 o;
-    o.x = encode4<F>(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
-    o.y = encode4<F>(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
+    o.x = encode4<F, NAN_FREE>(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+    o.y = encode4<F, NAN_FREE>(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
     return o;
 }
 
@@ -212,10 +213,18 @@ __global__ __launch_bounds__(kBlock) void k_quant_row_reg(const uint16_t* __rest
         if (amax_out) amax_out[row] = amax;
     }
     uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+    if (!__builtin_isnan(amax)) {
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        const int ch = lane + c * 64;
-        if (ch < nch) qr[ch] = encode8<F>(v[c], s);
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = lane + c * 64;
+            if (ch < nch) qr[ch] = encode8<F, true>(v[c], s);
+        }
+    } else {   // a NaN in the row (then s = 1): the bit-level encoder keeps NaN signs
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = lane + c * 64;
+            if (ch < nch) qr[ch] = encode8<F, false>(v[c], s);
+        }
     }
 }
 
@@ -251,8 +260,13 @@ __global__ __launch_bounds__(kBlock) void k_quant_row_2pass(const uint16_t* __re
     }
     if (VEC) {
         const int64_t nch = cols >> 3;
-        for (int64_t c = lane; c < nch; c += 64)
-            reinterpret_cast<uint2*>(qr)[c] = encode8<F>(reinterpret_cast<const uint4*>(xr)[c], s);
+        if (!__builtin_isnan(amax)) {
+            for (int64_t c = lane; c < nch; c += 64)
+                reinterpret_cast<uint2*>(qr)[c] = encode8<F, true>(reinterpret_cast<const uint4*>(xr)[c], s);
+        } else {
+            for (int64_t c = lane; c < nch; c += 64)
+                reinterpret_cast<uint2*>(qr)[c] = encode8<F, false>(reinterpret_cast<const uint4*>(xr)[c], s);
+        }
     } else {
         for (int64_t c = lane; c < cols; c += 64) qr[c] = (uint8_t)encode1<F>(bf16_lo(xr[c]) * s);
     }
@@ -273,6 +287,7 @@ __global__ __launch_bounds__(kBlock) void k_quant_tensor(const uint16_t* __restr
     const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const float s = DELAYED ? *scale : scale_from_amax<F>(*amax_io, margin);
+    const bool tensor_nan = DELAYED ? false : __builtin_isnan(*amax_io);
     if (blockIdx.x == 0 && threadIdx.x == 0) scale_inv[0] = 1.0f / s;
     uint32_t mx = 0;
     for (int64_t row = wave_id; row < rows; row += nwaves) {
@@ -282,8 +297,17 @@ __global__ __launch_bounds__(kBlock) void k_quant_tensor(const uint16_t* __restr
             const int64_t nch = cols >> 3;
             for (int64_t c = lane; c < nch; c += 64) {
                 const uint4 v = reinterpret_cast<const uint4*>(xr)[c];
-                if (DELAYED) mx = word_absmax(mx, v);
-                reinterpret_cast<uint2*>(qr)[c] = encode8<F>(v, s);
+                // NaN check: the running max of this lane turns NaN with the
+                // first NaN it sees (without the delayed amax, the tensor's
+                // amax from the first pass decides for the whole tensor)
+                bool nan_seen;
+                if (DELAYED) {
+                    mx = word_absmax(mx, v);
+                    nan_seen = nan_bits16(pk_fold(mx));
+                } else {
+                    nan_seen = tensor_nan;
+                }
+                reinterpret_cast<uint2*>(qr)[c] = nan_seen ? encode8<F, false>(v, s) : encode8<F, true>(v, s);
             }
         } else {
             for (int64_t c = lane; c < cols; c += 64) {
@@ -305,11 +329,14 @@ __global__ __launch_bounds__(kBlock) void k_quant_tensor(const uint16_t* __restr
 // Scales of the workgroup's 64 columns, computed once into LDS.
 template <int F>
 __device__ __forceinline__ void col_scales_to_lds(const float* __restrict__ col_amax, int64_t c0, int64_t cols,
-                                                  int margin, float* __restrict__ scale_inv, float* s_lds) {
+                                                  int margin, float* __restrict__ scale_inv, float* s_lds,
+                                                  int* nan_lds) {
     if (threadIdx.x < 64) {
         const int64_t c = c0 + threadIdx.x;
-        const float s = c < cols ? scale_from_amax<F>(col_amax[c], margin) : 1.0f;
+        const float a = c < cols ? col_amax[c] : 0.0f;
+        const float s = scale_from_amax<F>(a, margin);
         s_lds[threadIdx.x] = s;
+        nan_lds[threadIdx.x] = __builtin_isnan(a) ? 1 : 0;
         if (blockIdx.y == 0 && c < cols) scale_inv[c] = 1.0f / s;
     }
     __syncthreads();
@@ -333,25 +360,46 @@ __global__ __launch_bounds__(kBlock) void k_quant_col_tiled(const uint16_t* __re
                                                             float* __restrict__ scale_inv,
                                                             const float* __restrict__ col_amax, int vec_store) {
     __shared__ float s_lds[kColTileC];
+    __shared__ int nan_lds[kColTileC];
     __shared__ __attribute__((aligned(16))) uint32_t tile[kColTileC * kColTileR / 4];
     const int64_t c0 = (int64_t)blockIdx.x * kColTileC;
     const int64_t r0 = (int64_t)blockIdx.y * kColTileR;
-    col_scales_to_lds<F>(col_amax, c0, cols, margin, scale_inv, s_lds);
+    col_scales_to_lds<F>(col_amax, c0, cols, margin, scale_inv, s_lds, nan_lds);
 
     const int t = threadIdx.x;
     const int cc = t & 7, rg = t >> 3;
     const int64_t col = c0 + cc * 8;
     uint32_t w[4][2];
     float s[8];
+    int any_nan = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s[j] = s_lds[cc * 8 + j];
+    for (int j = 0; j < 8; ++j) {
+        s[j] = s_lds[cc * 8 + j];
+        any_nan |= nan_lds[cc * 8 + j];
+    }
+    uint4 v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int64_t row = r0 + rg * 4 + r;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (row < rows && col < cols) v = *reinterpret_cast<const uint4*>(x + row * ldx + col);
-        w[r][0] = encode4<F>(bf16_lo(v.x) * s[0], bf16_hi(v.x) * s[1], bf16_lo(v.y) * s[2], bf16_hi(v.y) * s[3]);
-        w[r][1] = encode4<F>(bf16_lo(v.z) * s[4], bf16_hi(v.z) * s[5], bf16_lo(v.w) * s[6], bf16_hi(v.w) * s[7]);
+        v[r] = make_uint4(0u, 0u, 0u, 0u);
+        if (row < rows && col < cols) v[r] = *reinterpret_cast<const uint4*>(x + row * ldx + col);
+    }
+    if (!any_nan) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            w[r][0] = encode4<F, true>(bf16_lo(v[r].x) * s[0], bf16_hi(v[r].x) * s[1], bf16_lo(v[r].y) * s[2],
+                                       bf16_hi(v[r].y) * s[3]);
+            w[r][1] = encode4<F, true>(bf16_lo(v[r].z) * s[4], bf16_hi(v[r].z) * s[5], bf16_lo(v[r].w) * s[6],
+                                       bf16_hi(v[r].w) * s[7]);
+        }
+    } else {   // a column of this chunk holds a NaN: bit-level encoder
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            w[r][0] = encode4<F, false>(bf16_lo(v[r].x) * s[0], bf16_hi(v[r].x) * s[1], bf16_lo(v[r].y) * s[2],
+                                        bf16_hi(v[r].y) * s[3]);
+            w[r][1] = encode4<F, false>(bf16_lo(v[r].z) * s[4], bf16_hi(v[r].z) * s[5], bf16_lo(v[r].w) * s[6],
+                                        bf16_hi(v[r].w) * s[7]);
+        }
     }
     const int chunk = ((rg >> 2) ^ cc) & 7;       // swizzled 16-byte row chunk
 #pragma unroll

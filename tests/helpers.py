@@ -35,17 +35,16 @@ def dev_f32(a):
 
 
 def guarded(rows, cols, dtype, ld=None, pad_rows=2, fill=SENTINEL):
-    """A [rows x cols] view with row stride ld inside a larger buffer whose
-    surroundings hold a sentinel: check_guard() afterwards detects any write
-    outside the view. Returns (view, buffer, (r0, c0))."""
-    ld = ld if ld is not None else cols
+    """A [rows x cols] view with row stride ld (default cols + 32) inside a
+    buffer with pad_rows extra rows above and below; everything outside the
+    view holds a sentinel, so check_guard() afterwards detects any write outside
+    the view. Returns (view, buffer, (r0, c0))."""
+    ld = ld if ld is not None else cols + 32
+    assert ld >= cols
     r0, c0 = pad_rows, 0
-    buf_rows = rows + 2 * pad_rows
-    buf = torch.empty((buf_rows, ld + 32), dtype=dtype, device="cuda:0")
-    if dtype.is_floating_point:
-        buf.view(torch.uint8 if buf.element_size() == 1 else (torch.int16 if buf.element_size() == 2 else torch.int32)).fill_(fill)
-    else:
-        buf.fill_(fill)
+    buf = torch.empty((rows + 2 * pad_rows, max(ld, 1)), dtype=dtype, device="cuda:0")
+    ints = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[buf.element_size()]
+    buf.view(ints).fill_(fill)
     view = buf[r0:r0 + rows, c0:c0 + cols]
     return view, buf, (r0, c0)
 

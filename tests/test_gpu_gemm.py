@@ -169,3 +169,23 @@ def test_grouped_gemm_parity(fp8, orc, sizes, fa, fb):
     if g == 1:
         dense = gpu_gemm(fp8, a, fa, b[0], fb, sa, sb[0], 1, 1)
         assert np.array_equal(dense, got), "one group equals the dense GEMM"
+
+
+LARGE = [((2100, 4100, 256), 0, 0, False, 4104), ((4096, 2048, 384), 1, 0, False, 2048),
+         ((1024, 8192, 128), 0, 1, True, 8200), ((2304, 3100, 256), 1, 1, False, 3107),
+         ((2304, 3100, 256), 0, 0, False, 3104)]
+
+
+@pytest.mark.parametrize("shape,fa,fb,out_f32,ldd", LARGE)
+def test_gemm_parity_large_tiles(fp8, orc, shape, fa, fb, out_f32, ldd):
+    """Shapes with >= 128 output tiles of 256 x 256 and k % 128 == 0 take the
+    large-tile kernel (direct-to-LDS loads, LDS-staged epilogue); ragged m / n,
+    fp32 output and an output stride off the 8-element grid cover its other
+    store paths."""
+    m, n, k = shape
+    a, sa = operands(orc, m, k, fa, seed=m + k)
+    b, sb = operands(orc, n, k, fb, seed=n + k + 9)
+    say("gemm large", shape, fa, fb, out_f32, ldd)
+    y, bound = orc.gemm(a, fa, b, fb, sa, sb)
+    got = gpu_gemm(fp8, a, fa, b, fb, sa, sb, 1, 1, out_f32=out_f32, ldd=ldd)
+    assert_within(orc, got, y, bound, not out_f32, f"large {shape}")
