@@ -227,11 +227,12 @@ def cpu_baseline(sample, target_s):
         orc.gemm(qx, fa, qw, fw, sx, sw, with_bound=False)
         return time.perf_counter() - t0
 
-    ms = min(act.shape[0], 2048)
-    ns = min(wgt.shape[0], 512)
+    ms, ns = min(act.shape[0], 1024), min(wgt.shape[0], 512)
     t = run(ms, ns)
-    if t < 0.5 * target_s and ns < wgt.shape[0]:      # scale the sample up to about target_s
-        ns = int(min(wgt.shape[0], max(ns, ns * target_s / t)))
+    if t < 0.5 * target_s:                 # scale the sample up to about target_s (weight rows first)
+        pairs = ms * ns * target_s / t
+        ns = int(min(wgt.shape[0], max(ns, pairs / ms)))
+        ms = int(min(act.shape[0], max(ms, pairs / ns)))
         t = run(ms, ns)
     return {"value": round(2.0 * ms * ns * k / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",

@@ -23,6 +23,9 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int kThreads = 256;
@@ -230,60 +233,112 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm(const uint8_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile kernel: 256 x 256 x 128 per workgroup, one 128 x 128 quadrant per
-// wavefront (4 x 4 blocks of 32x32x64, 256 fp32 accumulators per lane), two
-// LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4: each
-// lane's 16 bytes land at stage base + 16 * lane, so the XOR swizzle of the
-// LDS layout is produced by choosing which global chunk each lane fetches).
-// Requires k % 128 == 0 (no K tail); rows past m / n are clamped to the last
-// valid row on load and never stored.
+// Large-tile kernel: 256 x 256 output tile per workgroup, one 128 x 128
+// quadrant per wavefront (4 x 4 blocks of 32x32x64, 256 fp32 accumulators per
+// lane). K advances in steps of 64 through four LDS stages of 32 KB (A: 256
+// rows x 64 B, then B), filled by direct global->LDS loads issued three steps
+// ahead of use. Step t:
+//   wait until stage t+1's loads have landed; barrier
+//   issue the loads of stage t+4 into the buffer stage t used (its fragments
+//   were read during step t-1)
+//   read step t+1's B fragments
+//   4 x (4 MFMAs on A block mi, then read step t+1's A block mi into its registers)
+// The direct loads are issued from inline assembly: the compiler cannot see
+// that they write LDS, so it does not make later LDS reads wait for them; the
+// explicit vmcnt waits below do that at the right depth instead. Requires
+// k % 64 == 0; rows past m / n are clamped to the last valid row on load and
+// never stored.
 namespace big {
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int kStage = (BM + BN) * BK;              // 64 KB: A tile then B tile
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kStages = 4;
+constexpr int kStage = (BM + BN) * BK;              // 32 KB: A tile then B tile
+constexpr int kLoadsPerStage = 8;                   // direct loads per thread per stage (4 A + 4 B)
 constexpr int kEpiPitch = 256 + 16;                 // bytes per staged bf16 output row (128 cols + pad)
 constexpr int kEpiWave = 128 * kEpiPitch;           // one wavefront's 128 x 128 bf16 block
-constexpr int kSmem = 4 * kEpiWave > 2 * kStage ? 4 * kEpiWave : 2 * kStage;
+constexpr int kMain = 4 * kEpiWave > kStages * kStage ? 4 * kEpiWave : kStages * kStage;
+constexpr int kScaleOff = kMain;                    // 256 row scales, then 256 column scales (fp32)
+constexpr int kSmem = kMain + 2 * 256 * 4;
 }  // namespace big
 
-typedef __attribute__((address_space(3))) void lds_void;
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): wait for vmcnt <= N, leave the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
 
-// Issue this thread's share of one stage: A rows [0, 256) and B rows [0, 256)
-// of the K slice starting at k0. Wave w, instruction i fills LDS row group
-// g = w*8 + i (8 rows of 128 bytes); lane l fills row 8g + l/8, slot l%8,
-// which holds K chunk (l%8) ^ (row & 7).
-__device__ __forceinline__ void big_issue_stage(uint8_t* stage, const uint8_t* a, int64_t lda, int64_t a_rows,
-                                                const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k0) {
+// LDS layout of a stage: 64-byte rows of four 16-byte K chunks; chunk c of row r
+// sits in slot c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1). A fragment read touches one
+// chunk of each of 16 consecutive rows per 16 lanes; with this map those land
+// in 16 distinct 16-byte bank groups (and 8 consecutive rows in 8 distinct
+// groups of a 128-byte bank window).
+__device__ __forceinline__ int big_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+// Per-lane byte offsets of this thread's four A (or B) rows within a tile,
+// relative to the tile's first row: wavefront w, load i fills LDS rows
+// 16g .. 16g+15 with g = w*4 + i (1 KB: 16 bytes per lane, lane l at 16 l);
+// lane l fills row 16g + l/4, slot l%4, so it fetches the K chunk that belongs
+// in that slot. Rows past the last valid one are clamped to it (never stored).
+__device__ __forceinline__ void big_lane_offsets(uint32_t (&off)[4], int64_t ld, int64_t valid_rows) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int rl = lane >> 3;
-    const int chunk = (lane & 7) ^ rl;                  // row & 7 == rl for rows 8g + rl
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int g = wave * 8 + i;
-        int64_t r = g * 8 + rl;
-        r = r < a_rows ? r : a_rows - 1;
-        __builtin_amdgcn_global_load_lds(a + r * lda + k0 + chunk * 16, (lds_void*)(stage + g * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int g = wave * 8 + i;
-        int64_t r = g * 8 + rl;
-        r = r < b_rows ? r : b_rows - 1;
-        __builtin_amdgcn_global_load_lds(b + r * ldb + k0 + chunk * 16, (lds_void*)(stage + big::BM * big::BK + g * 1024),
-                                         16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+        const int row = (wave * 4 + i) * 16 + (lane >> 2);
+        const int chunk = big_slot(row, lane & 3);      // the slot map is an involution
+        int64_t r = row < valid_rows ? row : valid_rows - 1;
+        off[i] = (uint32_t)(r * ld + chunk * 16);
     }
 }
 
-__device__ __forceinline__ v8i big_frag(const uint8_t* tile, int row, int kk) {
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at
+// LDS address lds_base + 16 l (lds_base wave-uniform, set through M0).
+__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const uint8_t* gptr) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(gptr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Issue the 8 loads of one stage (K slice at k0) into the buffer at `stage`.
+__device__ __forceinline__ void big_issue_stage(const uint8_t* stage, const uint8_t* a, const uint32_t (&aoff)[4],
+                                                const uint8_t* b, const uint32_t (&boff)[4], int64_t k0) {
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage)) + wave * 4096;
+    const uint8_t* ak = a + k0;
+    const uint8_t* bk = b + k0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(base + i * 1024, ak + aoff[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(base + big::BM * big::BK + i * 1024, bk + boff[i]);
+}
+
+// Fragment of the 32x32x64 instruction (row `row` of the stage, lanes 0-31 K
+// bytes 0-31, lanes 32-63 K bytes 32-63).
+__device__ __forceinline__ v8i big_frag(const uint8_t* tile, int row) {
     const int lane = threadIdx.x & 63;
-    const int c0 = kk * 4 + (lane >> 5) * 2;
-    const uint8_t* rp = tile + row * 128;
-    const uint4 lo = *reinterpret_cast<const uint4*>(rp + ((c0 ^ (row & 7)) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(rp + (((c0 + 1) ^ (row & 7)) << 4));
+    const int c0 = (lane >> 5) * 2;
+    const uint8_t* rp = tile + row * 64;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + (big_slot(row, c0) << 4));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + (big_slot(row, c0 + 1) << 4));
     v8i f;
-    f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
-    f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+    f[0] = (int)lo[0]; f[1] = (int)lo[1]; f[2] = (int)lo[2]; f[3] = (int)lo[3];
+    f[4] = (int)hi[0]; f[5] = (int)hi[1]; f[6] = (int)hi[2]; f[7] = (int)hi[3];
     return f;
+}
+
+__device__ __forceinline__ v8i big_frag_a(const uint8_t* stage, int mi) {
+    const int wm = threadIdx.x >> 7;
+    return big_frag(stage, wm * 128 + mi * 32 + (threadIdx.x & 31));
+}
+__device__ __forceinline__ v8i big_frag_b(const uint8_t* stage, int ni) {
+    const int wn = (threadIdx.x >> 6) & 1;
+    return big_frag(stage + big::BM * big::BK, wn * 128 + ni * 32 + (threadIdx.x & 31));
 }
 
 // Logical tile of workgroup `bid` among `nt` tiles: the hardware deals
@@ -304,47 +359,79 @@ __device__ __forceinline__ void big_tile_coords(int64_t bid, int64_t tiles_m, in
     *pn = (t % (gm * tiles_n)) / gsize;
 }
 
+// Step t with t % 4 = S (compile-time): computes with fa/fb (step t's
+// fragments, read during step t-1) and reads step t+1's (B into fbn, each A
+// block into fa[mi] once its four instructions are issued). The loads are
+// unconditional so that the vmcnt depth stays fixed: past the last stage they
+// re-read the last K slice into buffers that are not read again.
+// sched_barrier(0) keeps the compiler from moving instructions across these
+// phase boundaries.
+template <int FA, int FB, int S>
+__device__ __forceinline__ void big_step(uint8_t* smem, v16f (&acc)[4][4], v8i (&fa)[4], const v8i (&fb)[4],
+                                         v8i (&fbn)[4], const uint8_t* a, const uint32_t (&aoff)[4],
+                                         const uint8_t* b, const uint32_t (&boff)[4], int64_t k4) {
+    const uint8_t* nxt = smem + ((S + 1) & 3) * big::kStage;
+    wait_vmcnt<2 * big::kLoadsPerStage>();               // stage t+1 landed (t+2, t+3 may be in flight)
+    __syncthreads();
+    big_issue_stage(smem + S * big::kStage, a, aoff, b, boff, k4);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) fbn[ni] = big_frag_b(nxt, ni);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[mi], fb[ni], acc[mi][ni],
+                                                                          MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fa[mi] = big_frag_a(nxt, mi);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int FA, int FB>
 __device__ __forceinline__ void big_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
                                              const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k,
                                              v16f (&acc)[4][4]) {
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-    const int64_t nk = k / big::BK;
-    big_issue_stage(smem, a, lda, a_rows, b, ldb, b_rows, 0);
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        uint8_t* cur = smem + (kt & 1) * big::kStage;
-        // this stage's loads have landed for every wavefront
-        __builtin_amdgcn_s_waitcnt(0x0f70);             // vmcnt(0)
-        __syncthreads();
-        if (kt + 1 < nk)
-            big_issue_stage(smem + ((kt + 1) & 1) * big::kStage, a, lda, a_rows, b, ldb, b_rows, (kt + 1) * big::BK);
-        const uint8_t* As = cur;
-        const uint8_t* Bs = cur + big::BM * big::BK;
+    uint32_t aoff[4], boff[4];
+    big_lane_offsets(aoff, lda, a_rows);
+    big_lane_offsets(boff, ldb, b_rows);
+    constexpr int64_t BK = big::BK;
+    const int64_t nk = k / BK;
+    const int64_t last = (nk - 1) * BK;
+    auto kof = [&](int64_t s) { return s < nk ? s * BK : last; };
+    // prologue: stages 0..3 in flight; wait for stage 0 and read step 0's fragments
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            v8i fa[4], fb[4];
+    for (int s = 0; s < 4; ++s) big_issue_stage(smem + s * big::kStage, a, aoff, b, boff, kof(s));
+    wait_vmcnt<3 * big::kLoadsPerStage>();
+    __syncthreads();
+    v8i fa[4], fb0[4], fb1[4];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) fa[mi] = big_frag(As, wm * 128 + mi * 32 + (lane & 31), kk);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) fb[ni] = big_frag(Bs, wn * 128 + ni * 32 + (lane & 31), kk);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fa[mi], fb[ni], acc[mi][ni], MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 0, 0, 0);
-        }
-        // the next iteration's barrier also guarantees every wavefront is done
-        // reading this stage before it is refilled two iterations later
+    for (int i = 0; i < 4; ++i) {
+        fa[i] = big_frag_a(smem, i);
+        fb0[i] = big_frag_b(smem, i);
     }
+    // four steps per iteration: the stage index (t % 4) and the B fragment set
+    // (t % 2) stay compile-time
+    int64_t t = 0;
+    for (; t + 4 <= nk; t += 4) {
+        big_step<FA, FB, 0>(smem, acc, fa, fb0, fb1, a, aoff, b, boff, kof(t + 4));
+        big_step<FA, FB, 1>(smem, acc, fa, fb1, fb0, a, aoff, b, boff, kof(t + 5));
+        big_step<FA, FB, 2>(smem, acc, fa, fb0, fb1, a, aoff, b, boff, kof(t + 6));
+        big_step<FA, FB, 3>(smem, acc, fa, fb1, fb0, a, aoff, b, boff, kof(t + 7));
+    }
+    // remaining 0..3 steps (t % 4 == 0 here); their loads are past the end
+    const int64_t left = nk - t;
+    if (left >= 1) big_step<FA, FB, 0>(smem, acc, fa, fb0, fb1, a, aoff, b, boff, last);
+    if (left >= 2) big_step<FA, FB, 1>(smem, acc, fa, fb1, fb0, a, aoff, b, boff, last);
+    if (left >= 3) big_step<FA, FB, 2>(smem, acc, fa, fb0, fb1, a, aoff, b, boff, last);
+    wait_vmcnt<0>();                                     // no load may still land in LDS after this
 }
 
 template <int FA, int FB, bool OUT_F32>
@@ -358,6 +445,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
     int64_t pm, pn;
     big_tile_coords(blockIdx.x, tiles_m, tiles_n, &pm, &pn);
     const int64_t row0 = pm * big::BM, col0 = pn * big::BN;
+    // this tile's scales, fetched now and parked in LDS after the main loop
+    const int t = threadIdx.x;
+    const float my_sa = sa[sa_vec ? (row0 + t < m ? row0 + t : m - 1) : 0];
+    const float my_sb = sb[sb_vec ? (col0 + t < n ? col0 + t : n - 1) : 0];
     v16f acc[4][4];
     big_mainloop<FA, FB>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, acc);
 
@@ -366,13 +457,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t wrow0 = row0 + wm * 128, wcol0 = col0 + wn * 128;
     const int64_t rows_valid = m - wrow0, cols_valid = n - wcol0;
+    __syncthreads();                                     // all wavefronts are done with the stages
+    float* s_rows = reinterpret_cast<float*>(smem + big::kScaleOff);
+    float* s_cols = s_rows + 256;
+    s_rows[t] = my_sa;
+    s_cols[t] = my_sb;
+    __syncthreads();
     float sbj[4];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-        int64_t j = ni * 32 + (lane & 31);
-        j = j < cols_valid ? j : cols_valid - 1;
-        sbj[ni] = sb[sb_vec ? (cols_valid > 0 ? wcol0 + j : 0) : 0];
-    }
+    for (int ni = 0; ni < 4; ++ni) sbj[ni] = s_cols[wn * 128 + ni * 32 + (lane & 31)];
     if (OUT_F32 || !vec_out) {
         // direct stores from registers
 #pragma unroll
@@ -381,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
             for (int r = 0; r < 16; ++r) {
                 const int lr = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (lr >= rows_valid) continue;
-                const float sai = sa[sa_vec ? wrow0 + lr : 0];
+                const float sai = s_rows[wm * 128 + lr];
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni) {
                     const int lc = ni * 32 + (lane & 31);
@@ -397,22 +490,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
         return;
     }
     // bf16 through LDS: each wavefront stages its 128 x 128 block row-major
-    // (padded rows), then streams it out 16 bytes per lane, 4 rows of 256
-    // contiguous bytes per store instruction.
-    __syncthreads();                                     // all wavefronts are done with the stages
+    // (padded rows), two values per hardware conversion, then streams it out
+    // 16 bytes per lane, 4 rows of 256 contiguous bytes per store instruction.
     uint8_t* ep = smem + wave * big::kEpiWave;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int lr = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            int64_t gr = lr < rows_valid ? wrow0 + lr : (rows_valid > 0 ? wrow0 + rows_valid - 1 : wrow0);
-            const float sai = sa[sa_vec ? gr : 0];
+        for (int q = 0; q < 4; ++q) {
+            const int lr0 = mi * 32 + 8 * q + 4 * (lane >> 5);     // rows lr0 .. lr0+3
+            const u32x4 s4 = *reinterpret_cast<const u32x4*>(&s_rows[wm * 128 + lr0]);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const int lc = ni * 32 + (lane & 31);
-                const float v = acc[mi][ni][r] * sai * sbj[ni];
-                *reinterpret_cast<uint16_t*>(ep + lr * big::kEpiPitch + lc * 2) = (uint16_t)f32_to_bf16(v);
+            for (int i = 0; i < 4; ++i) {
+                const float sai = __uint_as_float(s4[i]);
+                const int r = 4 * q + i;
+#pragma unroll
+                for (int ni = 0; ni < 4; ni += 2) {
+                    v2f v = {acc[mi][ni][r] * sai * sbj[ni], acc[mi][ni + 1][r] * sai * sbj[ni + 1]};
+                    const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, v2bf));
+                    uint8_t* rowp = ep + (lr0 + i) * big::kEpiPitch + (lane & 31) * 2;
+                    *reinterpret_cast<uint16_t*>(rowp + ni * 64) = (uint16_t)w;
+                    *reinterpret_cast<uint16_t*>(rowp + (ni + 1) * 64) = (uint16_t)(w >> 16);
+                }
             }
         }
     __syncthreads();
@@ -421,13 +519,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
         const int lr = it * 4 + (lane >> 4);
         const int ch = lane & 15;                        // 8 bf16 columns
         if (lr >= rows_valid) continue;
-        const uint4 val = *reinterpret_cast<const uint4*>(ep + lr * big::kEpiPitch + ch * 16);
+        const u32x4 val = *reinterpret_cast<const u32x4*>(ep + lr * big::kEpiPitch + ch * 16);
         uint16_t* dst = reinterpret_cast<uint16_t*>(d) + (wrow0 + lr) * ldd + wcol0 + ch * 8;
         if (ch * 8 + 8 <= cols_valid) {
-            *reinterpret_cast<uint4*>(dst) = val;
+            *reinterpret_cast<u32x4*>(dst) = val;
         } else {
-            const uint32_t w[4] = {val.x, val.y, val.z, val.w};
-            for (int e = 0; e < 8 && ch * 8 + e < cols_valid; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            for (int e = 0; e < 8 && ch * 8 + e < cols_valid; ++e) dst[e] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
         }
     }
 }
@@ -439,7 +536,7 @@ hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t l
     const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     if (tiles == 0) return hipSuccess;
     const int64_t big_tiles = ((m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
-    if (k > 0 && k % big::BK == 0 && big_tiles >= 128) {
+    if (k > 0 && k % big::BK == 0 && big_tiles >= 128) {   // k % 64 == 0
         const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
         hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT_F32>), dim3((unsigned)big_tiles), dim3(256), 0, st, a, lda, b, ldb,
                            m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out);
