@@ -246,8 +246,8 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm(const uint8_t* __rest
 // The direct loads are issued from inline assembly: the compiler cannot see
 // that they write LDS, so it does not make later LDS reads wait for them; the
 // explicit vmcnt waits below do that at the right depth instead. Requires
-// k % 64 == 0; rows past m / n are clamped to the last valid row on load and
-// never stored.
+// k % 256 == 0 (whole four-step iterations); rows past m / n are clamped to
+// the last valid row on load and never stored.
 namespace big {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kStages = 4;
@@ -261,11 +261,11 @@ constexpr int kSmem = kMain + 2 * 256 * 4;
 }  // namespace big
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8): wait for vmcnt <= N, leave the other counters alone.
-template <int N>
+// 6:4, lgkmcnt 11:8): wait for vmcnt <= N (and lgkmcnt <= L), leave expcnt alone.
+template <int N, int L = 15>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+    static_assert(N >= 0 && N < 64 && L >= 0 && L < 16, "counter range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | (L << 8));
 }
 
 // LDS layout of a stage: 64-byte rows of four 16-byte K chunks; chunk c of row r
@@ -293,13 +293,18 @@ __device__ __forceinline__ void big_lane_offsets(uint32_t (&off)[4], int64_t ld,
 }
 
 // One direct global->LDS load of 16 bytes per lane: lane l's bytes land at
-// LDS address lds_base + 16 l (lds_base wave-uniform, set through M0).
+// LDS address lds_base + 16 l (lds_base wave-uniform, set through M0; one
+// wait state between the M0 write and the load). M0 is clobbered: the kernels
+// that use this have no other M0 user (the build's ISA check test asserts it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const uint8_t* gptr) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(lds_base), "v"(gptr)
                  : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -318,27 +323,21 @@ __device__ __forceinline__ void big_issue_stage(const uint8_t* stage, const uint
     for (int i = 0; i < 4; ++i) lds_dma16(base + big::BM * big::BK + i * 1024, bk + boff[i]);
 }
 
-// Fragment of the 32x32x64 instruction (row `row` of the stage, lanes 0-31 K
-// bytes 0-31, lanes 32-63 K bytes 32-63).
-__device__ __forceinline__ v8i big_frag(const uint8_t* tile, int row) {
-    const int lane = threadIdx.x & 63;
-    const int c0 = (lane >> 5) * 2;
-    const uint8_t* rp = tile + row * 64;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + (big_slot(row, c0) << 4));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + (big_slot(row, c0 + 1) << 4));
+// Fragment of the 32x32x64 instruction: row `row` of a stage, lanes 0-31 hold
+// K bytes 0-31, lanes 32-63 K bytes 32-63 (two 16-byte halves).
+__device__ __forceinline__ u32x4 big_half(const uint8_t* tile, int row, int h) {
+    const int c = ((threadIdx.x & 63) >> 5) * 2 + h;
+    return *reinterpret_cast<const u32x4*>(tile + row * 64 + (big_slot(row, c) << 4));
+}
+__device__ __forceinline__ int big_row(int j) {   // j < 4: A block j; j >= 4: B block j-4 (row in its tile)
+    const int w = threadIdx.x >> 6;
+    return (j < 4 ? (w >> 1) * 128 + j * 32 : (w & 1) * 128 + (j - 4) * 32) + (threadIdx.x & 31);
+}
+__device__ __forceinline__ v8i big_join(u32x4 lo, u32x4 hi) {
     v8i f;
     f[0] = (int)lo[0]; f[1] = (int)lo[1]; f[2] = (int)lo[2]; f[3] = (int)lo[3];
     f[4] = (int)hi[0]; f[5] = (int)hi[1]; f[6] = (int)hi[2]; f[7] = (int)hi[3];
     return f;
-}
-
-__device__ __forceinline__ v8i big_frag_a(const uint8_t* stage, int mi) {
-    const int wm = threadIdx.x >> 7;
-    return big_frag(stage, wm * 128 + mi * 32 + (threadIdx.x & 31));
-}
-__device__ __forceinline__ v8i big_frag_b(const uint8_t* stage, int ni) {
-    const int wn = (threadIdx.x >> 6) & 1;
-    return big_frag(stage + big::BM * big::BK, wn * 128 + ni * 32 + (threadIdx.x & 31));
 }
 
 // Logical tile of workgroup `bid` among `nt` tiles: the hardware deals
@@ -359,33 +358,49 @@ __device__ __forceinline__ void big_tile_coords(int64_t bid, int64_t tiles_m, in
     *pn = (t % (gm * tiles_n)) / gsize;
 }
 
-// Step t with t % 4 = S (compile-time): computes with fa/fb (step t's
-// fragments, read during step t-1) and reads step t+1's (B into fbn, each A
-// block into fa[mi] once its four instructions are issued). The loads are
-// unconditional so that the vmcnt depth stays fixed: past the last stage they
-// re-read the last K slice into buffers that are not read again.
-// sched_barrier(0) keeps the compiler from moving instructions across these
-// phase boundaries.
+// Step t with t % 4 = S (compile-time): 16 matrix instructions on fc (step
+// t's fragments: A blocks 0-3, B blocks 4-7, read during step t-1). After each
+// one the wavefront issues one 16-byte half of step t+1's fragments into fn
+// and, every other slot, one of the 8 direct loads of stage t+4: the LDS
+// queue never backs up in front of a matrix instruction (issue is in order).
+// The loads are unconditional so that the vmcnt depth stays fixed: past the
+// last stage they re-read the last K slice into buffers that are not read
+// again. sched_barrier(0) pins this order.
 template <int FA, int FB, int S>
-__device__ __forceinline__ void big_step(uint8_t* smem, v16f (&acc)[4][4], v8i (&fa)[4], const v8i (&fb)[4],
-                                         v8i (&fbn)[4], const uint8_t* a, const uint32_t (&aoff)[4],
-                                         const uint8_t* b, const uint32_t (&boff)[4], int64_t k4) {
+__device__ __forceinline__ void big_step(uint8_t* smem, v16f (&acc)[4][4], const v8i (&fc)[8], v8i (&fn)[8],
+                                         const uint8_t* a, const uint32_t (&aoff)[4], const uint8_t* b,
+                                         const uint32_t (&boff)[4], int64_t k4) {
     const uint8_t* nxt = smem + ((S + 1) & 3) * big::kStage;
-    wait_vmcnt<2 * big::kLoadsPerStage>();               // stage t+1 landed (t+2, t+3 may be in flight)
+    const uint8_t* nxt_b = nxt + big::BM * big::BK;
+    // stage t+1 landed (t+2, t+3 may be in flight) and this wavefront's LDS
+    // reads are done: after the barrier other wavefronts load into the buffer
+    // this one read during step t-1
+    wait_vmcnt<2 * big::kLoadsPerStage, 0>();
     __syncthreads();
-    big_issue_stage(smem + S * big::kStage, a, aoff, b, boff, k4);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(smem + S * big::kStage)) + wave * 4096;
+    u32x4 half[16];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) fbn[ni] = big_frag_b(nxt, ni);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[mi], fb[ni], acc[mi][ni],
-                                                                          MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 0, 0, 0);
+    for (int i = 0; i < 16; ++i) {
+        const int mi = i >> 2, ni = i & 3;
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc[mi], fc[4 + ni], acc[mi][ni], MfmaFmt<FA>::v,
+                                                                      MfmaFmt<FB>::v, 0, 0, 0, 0);
+        // half i of fragment j = i / 2 (B fragments first: the B tile is needed by every A block)
+        const int j = (i >> 1) < 4 ? 4 + (i >> 1) : (i >> 1) - 4;
+        half[i] = big_half(j < 4 ? nxt : nxt_b, big_row(j), i & 1);
+        if ((i & 1) == 0) {
+            const int l = i >> 1;                        // load l: A rows for l < 4, B rows for l >= 4
+            if (l < 4)
+                lds_dma16(dma_base + l * 1024, a + k4 + aoff[l]);
+            else
+                lds_dma16(dma_base + big::BM * big::BK + (l - 4) * 1024, b + k4 + boff[l - 4]);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        fa[mi] = big_frag_a(nxt, mi);
-        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        const int j = f < 4 ? 4 + f : f - 4;            // fragment f was read in halves 2f, 2f+1
+        fn[j] = big_join(half[2 * f], half[2 * f + 1]);
     }
 }
 
@@ -411,26 +426,22 @@ __device__ __forceinline__ void big_mainloop(uint8_t* smem, const uint8_t* a, in
     for (int s = 0; s < 4; ++s) big_issue_stage(smem + s * big::kStage, a, aoff, b, boff, kof(s));
     wait_vmcnt<3 * big::kLoadsPerStage>();
     __syncthreads();
-    v8i fa[4], fb0[4], fb1[4];
+    v8i f0[8], f1[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        fa[i] = big_frag_a(smem, i);
-        fb0[i] = big_frag_b(smem, i);
+    for (int j = 0; j < 8; ++j) {
+        const uint8_t* t0 = j < 4 ? smem : smem + big::BM * big::BK;
+        f0[j] = big_join(big_half(t0, big_row(j), 0), big_half(t0, big_row(j), 1));
     }
-    // four steps per iteration: the stage index (t % 4) and the B fragment set
+    // four steps per iteration: the stage index (t % 4) and the fragment set
     // (t % 2) stay compile-time
-    int64_t t = 0;
-    for (; t + 4 <= nk; t += 4) {
-        big_step<FA, FB, 0>(smem, acc, fa, fb0, fb1, a, aoff, b, boff, kof(t + 4));
-        big_step<FA, FB, 1>(smem, acc, fa, fb1, fb0, a, aoff, b, boff, kof(t + 5));
-        big_step<FA, FB, 2>(smem, acc, fa, fb0, fb1, a, aoff, b, boff, kof(t + 6));
-        big_step<FA, FB, 3>(smem, acc, fa, fb1, fb0, a, aoff, b, boff, kof(t + 7));
+    for (int64_t t = 0; t < nk; t += 4) {
+        big_step<FA, FB, 0>(smem, acc, f0, f1, a, aoff, b, boff, kof(t + 4));
+        big_step<FA, FB, 1>(smem, acc, f1, f0, a, aoff, b, boff, kof(t + 5));
+        big_step<FA, FB, 2>(smem, acc, f0, f1, a, aoff, b, boff, kof(t + 6));
+        big_step<FA, FB, 3>(smem, acc, f1, f0, a, aoff, b, boff, kof(t + 7));
     }
-    // remaining 0..3 steps (t % 4 == 0 here); their loads are past the end
-    const int64_t left = nk - t;
-    if (left >= 1) big_step<FA, FB, 0>(smem, acc, fa, fb0, fb1, a, aoff, b, boff, last);
-    if (left >= 2) big_step<FA, FB, 1>(smem, acc, fa, fb1, fb0, a, aoff, b, boff, last);
-    if (left >= 3) big_step<FA, FB, 2>(smem, acc, fa, fb0, fb1, a, aoff, b, boff, last);
+    // (k % 256 == 0: whole iterations only; a remainder's join costs
+    // accumulator spills at the epilogue)
     wait_vmcnt<0>();                                     // no load may still land in LDS after this
 }
 
@@ -536,7 +547,7 @@ hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t l
     const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     if (tiles == 0) return hipSuccess;
     const int64_t big_tiles = ((m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
-    if (k > 0 && k % big::BK == 0 && big_tiles >= 128) {   // k % 64 == 0
+    if (k > 0 && k % (4 * big::BK) == 0 && big_tiles >= 128) {
         const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
         hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT_F32>), dim3((unsigned)big_tiles), dim3(256), 0, st, a, lda, b, ldb,
                            m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out);

@@ -171,17 +171,17 @@ def test_grouped_gemm_parity(fp8, orc, sizes, fa, fb):
         assert np.array_equal(dense, got), "one group equals the dense GEMM"
 
 
-LARGE = [((2100, 4100, 256), 0, 0, False, 4104), ((4096, 2048, 384), 1, 0, False, 2048),
-         ((1024, 8192, 128), 0, 1, True, 8200), ((2304, 3100, 256), 1, 1, False, 3107),
-         ((2304, 3100, 256), 0, 0, False, 3104)]
+LARGE = [((2100, 4100, 256), 0, 0, False, 4104), ((4096, 2048, 512), 1, 0, False, 2048),
+         ((1024, 8192, 768), 0, 1, True, 8200), ((2304, 3100, 256), 1, 1, False, 3107),
+         ((2304, 3100, 256), 0, 0, False, 3104), ((4096, 2048, 384), 1, 0, False, 2048)]
 
 
 @pytest.mark.parametrize("shape,fa,fb,out_f32,ldd", LARGE)
 def test_gemm_parity_large_tiles(fp8, orc, shape, fa, fb, out_f32, ldd):
-    """Shapes with >= 128 output tiles of 256 x 256 and k % 128 == 0 take the
+    """Shapes with >= 128 output tiles of 256 x 256 and k % 256 == 0 take the
     large-tile kernel (direct-to-LDS loads, LDS-staged epilogue); ragged m / n,
     fp32 output and an output stride off the 8-element grid cover its other
-    store paths."""
+    store paths; k = 384 falls back to the 128 x 128 kernel."""
     m, n, k = shape
     a, sa = operands(orc, m, k, fa, seed=m + k)
     b, sb = operands(orc, n, k, fb, seed=n + k + 9)
