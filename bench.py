@@ -18,7 +18,6 @@ Other workloads (--workload c1|c3|c4|c5) print the same line for the other
 shapes (c3 tensorwise delayed, c4 MoE grouped GEMM, c5 hybrid backward).
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,6 +41,8 @@ def parse():
     p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="time a plain 1 GiB copy kernel instead (for scaling rocprofv3 byte counters)")
     return p.parse_args()
 
 
@@ -188,26 +189,45 @@ class Step:
             ev[6].record()
 
 
-def source_digest(*names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "fp8_scaled_gemm_amax_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel_key):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; otherwise None."""
+    from fp8_scaled_gemm_amax_amd.profiling import source_digest
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         table = json.load(f)
     rec = table.get(kernel_key)
-    if not rec or rec.get("source_digest") != source_digest(*rec.get("sources", [])):
+    if not rec or rec.get("source_digest") != source_digest(rec.get("sources", [])):
         return None
     return rec.get("bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(args):
+    """A plain copy kernel of known size for scaling the HBM byte counters:
+    y = x * 1 over 2^28 fp32 values (reads and writes exactly COPY_BYTES each).
+    Also prints the copy's own bandwidth, the practical HBM ceiling."""
+    import torch
+    n = COPY_BYTES // 4
+    x = torch.rand(n, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(args.warmup):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        torch.mul(x, 1.0, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"calibration": "copy y = x * 1 (fp32)", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "avg_ms": round(ms, 5), "gbps": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1),
+                      "steps": args.steps}), flush=True)
 
 
 def cpu_baseline(sample, target_s):
@@ -247,6 +267,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
     step = Step(args.workload)
     ncalls = len(step.calls)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(args.steps)]

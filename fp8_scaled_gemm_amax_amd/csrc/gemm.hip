@@ -304,6 +304,13 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const uint8_t* gptr
                  : "s"(lds_base), "v"(gptr)
                  : "memory", "m0");
 }
+// Same with 4 bytes per lane: lane l's dword lands at lds_base + 4 l.
+__device__ __forceinline__ void lds_dma4(uint32_t lds_base, const void* gptr) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(lds_base), "v"(gptr)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -404,10 +411,13 @@ __device__ __forceinline__ void big_step(uint8_t* smem, v16f (&acc)[4][4], const
     }
 }
 
+// sa_lane / sb_lane: this thread's row / column scale (thread t: tile row t,
+// tile column t). They are loaded straight into the scale area of LDS with the
+// first loads of the tile, so no register holds them across the main loop.
 template <int FA, int FB>
 __device__ __forceinline__ void big_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
                                              const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k,
-                                             v16f (&acc)[4][4]) {
+                                             const float* sa_lane, const float* sb_lane, v16f (&acc)[4][4]) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -421,7 +431,14 @@ __device__ __forceinline__ void big_mainloop(uint8_t* smem, const uint8_t* a, in
     const int64_t nk = k / BK;
     const int64_t last = (nk - 1) * BK;
     auto kof = [&](int64_t s) { return s < nk ? s * BK : last; };
-    // prologue: stages 0..3 in flight; wait for stage 0 and read step 0's fragments
+    // prologue: the scales, then stages 0..3 in flight; wait for the scales and
+    // stage 0 (loads complete in order) and read step 0's fragments
+    {
+        const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kScaleOff)) + wave * 256;
+        lds_dma4(sbase, sa_lane);
+        lds_dma4(sbase + 1024, sb_lane);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) big_issue_stage(smem + s * big::kStage, a, aoff, b, boff, kof(s));
     wait_vmcnt<3 * big::kLoadsPerStage>();
@@ -445,35 +462,29 @@ __device__ __forceinline__ void big_mainloop(uint8_t* smem, const uint8_t* a, in
     wait_vmcnt<0>();                                     // no load may still land in LDS after this
 }
 
-template <int FA, int FB, bool OUT_F32>
-__global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__ a, int64_t lda,
-                                                     const uint8_t* __restrict__ b, int64_t ldb, int64_t m, int64_t n,
-                                                     int64_t k, const float* __restrict__ sa, int sa_vec,
-                                                     const float* __restrict__ sb, int sb_vec, void* __restrict__ d,
-                                                     int64_t ldd, int vec_out) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[big::kSmem];
-    const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
-    int64_t pm, pn;
-    big_tile_coords(blockIdx.x, tiles_m, tiles_n, &pm, &pn);
-    const int64_t row0 = pm * big::BM, col0 = pn * big::BN;
-    // this tile's scales, fetched now and parked in LDS after the main loop
-    const int t = threadIdx.x;
-    const float my_sa = sa[sa_vec ? (row0 + t < m ? row0 + t : m - 1) : 0];
-    const float my_sb = sb[sb_vec ? (col0 + t < n ? col0 + t : n - 1) : 0];
-    v16f acc[4][4];
-    big_mainloop<FA, FB>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, acc);
-
+// Epilogue of a 256 x 256 tile at (row0, col0) with rows_total / cols_total
+// valid rows / columns from there: d = acc * sa_row * sb_col, the 256 row and
+// 256 column scales of the tile sitting in the scale area of LDS.
+template <bool OUT_F32>
+__device__ __forceinline__ void big_epilogue(uint8_t* smem, v16f (&acc)[4][4], void* __restrict__ d,
+                                             int64_t ldd, int64_t row0, int64_t rows_total, int64_t col0,
+                                             int64_t cols_total, int vec_out) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t wrow0 = row0 + wm * 128, wcol0 = col0 + wn * 128;
-    const int64_t rows_valid = m - wrow0, cols_valid = n - wcol0;
-    __syncthreads();                                     // all wavefronts are done with the stages
-    float* s_rows = reinterpret_cast<float*>(smem + big::kScaleOff);
-    float* s_cols = s_rows + 256;
-    s_rows[t] = my_sa;
-    s_cols[t] = my_sb;
+    const int64_t rows_valid = rows_total - wm * 128, cols_valid = cols_total - wn * 128;
+    // The accumulators stay in AGPRs until each is used: without this the
+    // compiler copies all 256 to VGPRs at once at the end of the loop and spills.
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
+    // every wavefront is done with the stages (the staging below reuses them),
+    // and every lane's scale load has landed (the main loop ends with vmcnt 0)
     __syncthreads();
+    const float* s_rows = reinterpret_cast<const float*>(smem + big::kScaleOff);
+    const float* s_cols = s_rows + 256;
     float sbj[4];
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) sbj[ni] = s_cols[wn * 128 + ni * 32 + (lane & 31)];
@@ -541,6 +552,121 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
 }
 
 template <int FA, int FB, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__ a, int64_t lda,
+                                                     const uint8_t* __restrict__ b, int64_t ldb, int64_t m, int64_t n,
+                                                     int64_t k, const float* __restrict__ sa, int sa_vec,
+                                                     const float* __restrict__ sb, int sb_vec, void* __restrict__ d,
+                                                     int64_t ldd, int vec_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[big::kSmem];
+    const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
+    int64_t pm, pn;
+    big_tile_coords(blockIdx.x, tiles_m, tiles_n, &pm, &pn);
+    const int64_t row0 = pm * big::BM, col0 = pn * big::BN;
+    const int t = threadIdx.x;
+    const float* sa_lane = sa + (sa_vec ? (row0 + t < m ? row0 + t : m - 1) : 0);
+    const float* sb_lane = sb + (sb_vec ? (col0 + t < n ? col0 + t : n - 1) : 0);
+    v16f acc[4][4];
+    big_mainloop<FA, FB>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, sa_lane, sb_lane,
+                         acc);
+    big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, m - row0, col0, n - col0, vec_out);
+}
+
+// Grouped large-tile kernel. Group e owns rows lo_e .. hi_e of a and d (the
+// offsets clamped to [0, total_m], hi_e >= lo_e) and the n x k matrix
+// b + e * b_group_stride; its tiles are the ceil((hi_e - lo_e) / 256) x
+// ceil(n / 256) tiles of that row range. The grid is an upper bound computed
+// on the host without reading the offsets (sum_e ceil(m_e / 256) <=
+// ceil(total / 256) + g). Each workgroup builds the exclusive prefix sum of the
+// per-group tile counts in LDS (256 threads, g / 256 groups each, then a block
+// scan), so it knows the real tile count nt: workgroups at or past nt exit (they
+// are dispatched last); the others take the XCD-aware order of the dense
+// kernel over the concatenated per-group tile lists (a run of workgroups on one
+// XCD covers neighbouring tiles of one group: shared b panels and a rows in
+// that XCD's L2) and find their group by binary search in the prefix sums.
+constexpr int kMaxGroupsBig = 4096;
+static_assert((kMaxGroupsBig + 1) * 8 <= big::kStages * big::kStage, "group prefix sums fit in the stage buffers");
+
+template <int FA, int FB, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
+    const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb, int64_t b_group_stride,
+    const int64_t* __restrict__ offsets, int g, int64_t total_m, int64_t n, int64_t k, const float* __restrict__ sa,
+    const float* __restrict__ sb, void* __restrict__ d, int64_t ldd, int vec_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[big::kSmem];
+    const int64_t tiles_n = (n + big::BN - 1) / big::BN;
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    auto bounds = [&](int e, int64_t* lo, int64_t* hi) {
+        int64_t s = offsets[e], u = offsets[e + 1];
+        s = s < 0 ? 0 : (s > total_m ? total_m : s);
+        u = u < s ? s : (u > total_m ? total_m : u);
+        *lo = s;
+        *hi = u;
+    };
+    auto tiles_of = [&](int e) {
+        int64_t lo, hi;
+        bounds(e, &lo, &hi);
+        return ((hi - lo + big::BM - 1) / big::BM) * tiles_n;
+    };
+    int64_t* pre = reinterpret_cast<int64_t*>(smem);                       // g + 1 prefix sums
+    int64_t* wsum = reinterpret_cast<int64_t*>(smem + big::kScaleOff);     // 4 wavefront totals
+    const int per = (g + 255) / 256;
+    const int e0 = t * per, e1 = e0 + per < g ? e0 + per : g;
+    int64_t mine = 0;
+    for (int e = e0; e < e1; ++e) mine += tiles_of(e);
+    int64_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int64_t run = incl - mine;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+    for (int e = e0; e < e1; ++e) {
+        pre[e] = run;
+        run += tiles_of(e);
+    }
+    if (t == 255) pre[g] = run;
+    __syncthreads();
+    const int64_t nt = pre[g];
+    const int64_t bid = blockIdx.x;
+    if (bid >= nt) return;                               // uniform over the workgroup
+    const int64_t q = nt / 8, rem = nt % 8;
+    const int64_t xcd = bid % 8, idx = bid / 8;
+    int64_t lt = xcd * q + (xcd < rem ? xcd : rem) + idx;     // logical tile, < nt
+    // last group e with pre[e] <= lt: a non-empty group (an empty one has pre[e+1] == pre[e])
+    int lo_e = 0, hi_e = g;                              // pre[lo_e] <= lt < pre[hi_e]
+    while (hi_e - lo_e > 1) {
+        const int mid = (lo_e + hi_e) >> 1;
+        if (pre[mid] <= lt)
+            lo_e = mid;
+        else
+            hi_e = mid;
+    }
+    const int grp = lo_e;
+    lt -= pre[grp];
+    __syncthreads();                                     // the prefix sums are dead: the stages reuse LDS
+    int64_t lo, hi;
+    bounds(grp, &lo, &hi);
+    // within the group: runs of 4 m-tiles sweep the n-tiles
+    const int64_t tiles_m = (hi - lo + big::BM - 1) / big::BM;
+    constexpr int64_t gm = 4;
+    const int64_t first_m = (lt / (gm * tiles_n)) * gm;
+    const int64_t gsize = tiles_m - first_m < gm ? tiles_m - first_m : gm;
+    const int64_t pm = first_m + (lt % (gm * tiles_n)) % gsize;
+    const int64_t pn = (lt % (gm * tiles_n)) / gsize;
+    const int64_t row0 = lo + pm * big::BM, col0 = pn * big::BN;
+    const float* sa_lane = sa + (row0 + t < hi ? row0 + t : hi - 1);
+    const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
+    const uint8_t* bg = b + (int64_t)grp * b_group_stride;
+    v16f acc[4][4];
+    big_mainloop<FA, FB>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, sa_lane, sb_lane,
+                         acc);
+    big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, hi - row0, col0, n - col0, vec_out);
+}
+
+template <int FA, int FB, bool OUT_F32>
 hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m, int64_t n, int64_t k,
                       const float* sa, int sa_vec, const float* sb, int sb_vec, void* d, int64_t ldd,
                       hipStream_t st) {
@@ -564,6 +690,14 @@ hipError_t grouped_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_
                          const float* sb, void* d, int64_t ldd, hipStream_t st) {
     const int64_t tiles = ((total_m + BM - 1) / BM + g) * ((n + BN - 1) / BN);
     if (total_m == 0 || n == 0) return hipSuccess;
+    const int64_t big_est = ((total_m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
+    if (k > 0 && k % (4 * big::BK) == 0 && big_est >= 128 && g <= kMaxGroupsBig) {
+        const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
+        const int64_t grid = ((total_m + big::BM - 1) / big::BM + g) * ((n + big::BN - 1) / big::BN);
+        hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32>), dim3((unsigned)grid), dim3(256), 0, st, a, lda, b,
+                           ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_grouped_gemm<FA, FB, OUT_F32>), dim3((unsigned)tiles), dim3(kThreads), 0, st, a, lda, b, ldb,
                        stride, offsets, g, total_m, n, k, sa, sb, d, ldd);
     return hipGetLastError();

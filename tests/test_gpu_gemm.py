@@ -189,3 +189,51 @@ def test_gemm_parity_large_tiles(fp8, orc, shape, fa, fb, out_f32, ldd):
     y, bound = orc.gemm(a, fa, b, fb, sa, sb)
     got = gpu_gemm(fp8, a, fa, b, fb, sa, sb, 1, 1, out_f32=out_f32, ldd=ldd)
     assert_within(orc, got, y, bound, not out_f32, f"large {shape}")
+
+
+def random_codes(rng, shape, fmt):
+    """Uniformly random finite FP8 codes of format fmt (no NaN or Inf codes)."""
+    top = 0x7E if fmt == 0 else 0x7B          # e4m3: 0x7F is NaN; e5m2: 0x7C.. are Inf / NaN
+    c = rng.integers(0, top + 1, size=shape, dtype=np.uint8)
+    c |= rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    return c
+
+
+def many_groups(g=300, seed=11):
+    rng = np.random.default_rng(seed)
+    sizes = rng.integers(1, 30, g)
+    sizes[::3] = 0                              # every third expert gets no rows
+    sizes[7] = 1300                             # one large expert spanning several tiles
+    return [int(x) for x in sizes]
+
+
+GROUPED_LARGE = [([0, 1000, 1, 255, 257, 0, 2583], 2048, 512, 0, 0, False),
+                 (many_groups(), 2048, 256, 1, 0, False),
+                 ([4096], 2048, 256, 0, 1, True),
+                 ([3000, 0, 1100], 2200, 768, 1, 1, False)]
+
+
+@pytest.mark.parametrize("sizes,n,k,fa,fb,out_f32", GROUPED_LARGE, ids=["ragged", "g300", "one", "ragged_n"])
+def test_grouped_gemm_parity_large_tiles(fp8, orc, sizes, n, k, fa, fb, out_f32):
+    """Shapes that take the 256 x 256 grouped kernel (k % 256 == 0, at least 128
+    tiles of 256 x 256 estimated from the total row count): empty groups, a
+    one-row group, groups spanning several m-tiles, more groups than threads of
+    a workgroup (the per-group tile counts are summed in parallel), ragged n."""
+    g = len(sizes)
+    offsets = np.zeros(g + 1, np.int64)
+    offsets[1:] = np.cumsum(sizes)
+    total = int(offsets[-1])
+    assert -(-total // 256) * -(-n // 256) >= 128 and k % 256 == 0
+    rng = np.random.default_rng(total + n + k)
+    a = random_codes(rng, (total, k), fa)
+    b = random_codes(rng, (g, n, k), fb)
+    sa = np.exp2(rng.integers(-8, 2, total)).astype(np.float32) * np.float32(1.375)
+    sb = np.exp2(rng.integers(-8, 2, (g, n))).astype(np.float32)
+    say("grouped large", g, total, n, k, fa, fb, out_f32)
+    y, bound = orc.grouped_gemm(a, fa, b, fb, offsets, sa, sb)
+    got = gpu_grouped(fp8, a, fa, b, fb, offsets, sa, sb, out_f32=out_f32)
+    assert_within(orc, got, y, bound, not out_f32, f"grouped large {g} groups")
+    if g == 1:
+        say("grouped large: one group vs dense")
+        dense = gpu_gemm(fp8, a, fa, b[0], fb, sa, sb[0], 1, 1, out_f32=out_f32, ldd=n + 32)
+        assert np.array_equal(dense, got), "one group equals the dense GEMM"

@@ -46,4 +46,4 @@ def test_m0_only_feeds_direct_loads(asm):
         for i, l in enumerate(lines):
             if re.search(r"\bm0\b", l):
                 assert re.match(r"s_mov_b32 m0, s\d+$", l), (kname, l)
-                assert lines[i + 1] == "s_nop 0" and lines[i + 2].startswith("global_load_lds_dwordx4"), (kname, l)
+                assert lines[i + 1] == "s_nop 0" and re.match(r"global_load_lds_dword(x4)? ", lines[i + 2]), (kname, l)
