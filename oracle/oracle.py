@@ -266,6 +266,70 @@ def grouped_gemm(a, fa, b, fb, offsets, a_scale, b_scale):
     return y, bound
 
 
+# ---------------------------------------------------------------- MoE backward --
+# The MoE backward ("FP8 Training on AMD GPUs with TorchTitan and TorchAO": the
+# backward-pass speedup of the MoE model, colwise scales, grouped GEMM) needs the
+# expert-local transposed operands of the weight gradient: for expert g with
+# tokens offsets[g] .. offsets[g+1], dW_g = dY_g^T X_g contracts over that
+# group's tokens. Reading used here (the pages give no layout): each group's
+# codes sit transposed in one matrix, group g at columns P_g .. P_g + m_g, where
+# P_g = sum over h < g of roundup(m_h, align); columns m_g .. roundup(m_g, align)
+# of the group hold zero codes, which add nothing to a contraction.
+
+def padded_offsets(offsets, align):
+    """P_g = sum_{h<g} roundup(m_h, align), g = 0..G (int64 [G+1])."""
+    offsets = np.asarray(offsets, np.int64)
+    sizes = np.diff(offsets)
+    padded = (sizes + align - 1) // align * align
+    out = np.zeros(offsets.size, np.int64)
+    out[1:] = np.cumsum(padded)
+    return out
+
+
+def grouped_quantize_col(x_bf16, fmt, offsets, align, margin=0):
+    """Colwise quantization per group of rows: group g's rows get their own
+    per-column scales (amax over the group's rows only) and are written
+    transposed at columns P_g .. P_g + m_g of qt [cols x P_G], zero codes after.
+    An empty group has amax 0, hence scale 1. Returns (qt, scale_inv [G x cols],
+    amax [G x cols])."""
+    x = _c(x_bf16, np.uint16)
+    offsets = np.asarray(offsets, np.int64)
+    G = offsets.size - 1
+    cols = x.shape[1]
+    P = padded_offsets(offsets, align)
+    qt = np.zeros((cols, int(P[-1])), np.uint8)
+    si = np.ones((G, cols), np.float32)
+    am = np.zeros((G, cols), np.float32)
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi > lo:
+            qg, si[g], am[g] = quantize_col(x[lo:hi], fmt, margin)
+            qt[:, P[g]:P[g] + (hi - lo)] = qg
+    return qt, si, am
+
+
+def grouped_gemm_ragged_k(a_t, fa, b_t, fb, offsets, align, a_scale, b_scale):
+    """Weight-gradient form of the grouped product: for each group g,
+    D_g = (A[:, P_g : P_g + m_g] . B[:, P_g : P_g + m_g]^T) * a_scale[g][:, None] * b_scale[g][None, :]
+    in fp64, with a_t [m x L] and b_t [n x L] codes in the padded grouped
+    layout and a_scale [G x m], b_scale [G x n]. An empty group gives zeros.
+    Returns (d [G x m x n], bound [G x m x n])."""
+    a_t = _c(a_t, np.uint8)
+    b_t = _c(b_t, np.uint8)
+    offsets = np.asarray(offsets, np.int64)
+    G = offsets.size - 1
+    m, n = a_t.shape[0], b_t.shape[0]
+    P = padded_offsets(offsets, align)
+    d = np.zeros((G, m, n))
+    bound = np.zeros((G, m, n))
+    for g in range(G):
+        kg = int(offsets[g + 1] - offsets[g])
+        if kg > 0:
+            sl = slice(int(P[g]), int(P[g]) + kg)
+            d[g], bound[g] = gemm(a_t[:, sl], fa, b_t[:, sl], fb, a_scale[g], b_scale[g])
+    return d, bound
+
+
 def gemm_within_bound(gpu, y, bound, out_bf16=True):
     """The acceptance rule: |gpu - y| <= 1e-3 * bound + 2^-8 |y| (the last term only
     for bf16 output). NaN matches NaN. Returns a boolean array."""
