@@ -14,8 +14,9 @@ algorithmic GB/s (2 B read + 1 B written per element + 4 B per scale) against
 8 TB/s; `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload on this host's cores.
 
-Other workloads (--workload c1|c3|c4|c5) print the same line for the other
-shapes (c3 tensorwise delayed, c4 MoE grouped GEMM, c5 hybrid backward).
+Other workloads (--workload c1|c3|c4|c4b|c5) print the same line for the
+other shapes (c3 tensorwise delayed, c4 MoE grouped GEMM, c4b the MoE expert
+layer's backward, c5 hybrid backward).
 """
 import argparse
 import json
@@ -38,7 +39,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c4b", "c5"])
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -119,6 +120,36 @@ class Step:
             self.desc = ("DeepSeek-V3 MoE grouped GEMM, one GPU's share: 32 experts Zipf(1.1) counts (3 empty), "
                          "tokens bf16 [16384x7168] N(0,1), W_e bf16 [2048x7168] N(0,0.006^2); e4m3 rowwise; bf16 out")
             self.scales = {"recipe": "rowwise", "format": "e4m3"}
+        elif name == "c4b":
+            w = workloads.c4b()
+            g, n, k = w["w"].shape
+            t = w["x"].shape[0]
+            self.g, self.n, self.k, self.t = g, n, k, t
+            self.x, self.dy = bf16_dev(w["x"]), bf16_dev(w["dy"])
+            self.w = bf16_dev(w["w"].reshape(g * n, k))
+            self.offsets = torch.from_numpy(w["offsets"]).to(dev)
+            woff = np.arange(g + 1, dtype=np.int64) * n
+            self.woffsets = torch.from_numpy(woff).to(dev)
+            self.cpu_sample = (w["dy"], 1, np.ascontiguousarray(w["w"][0].T), 0)   # dgrad: dY rows, W_0^T rows
+            L = fp8.grouped_layout_width(t, g)
+            self.dyq, self.dys = E((t, n), dtype=torch.uint8, device=dev), E(t, device=dev)
+            self.wt = E((k, g * n), dtype=torch.uint8, device=dev)
+            self.wts, self.wta = E((g, k), device=dev), E((g, k), device=dev)
+            self.dx = E((t, k), dtype=torch.bfloat16, device=dev)
+            self.dyt = torch.zeros((n, L), dtype=torch.uint8, device=dev)
+            self.xt = torch.zeros((k, L), dtype=torch.uint8, device=dev)
+            self.dyts, self.dyta = E((g, n), device=dev), E((g, n), device=dev)
+            self.xts, self.xta = E((g, k), device=dev), E((g, k), device=dev)
+            self.dw = E((g, n, k), dtype=torch.bfloat16, device=dev)
+            self.mnk = [(t, k, n), (n, k, t)]
+            self.calls = [("quantize_row dY e5m2", t * n, t), ("grouped_quantize_col W^T e4m3", g * n * k, g * k),
+                          ("grouped_quantize_col dY^T e5m2", t * n, g * n),
+                          ("grouped_quantize_col X^T e4m3", t * k, g * k),
+                          ("grouped_gemm dgrad", None, 0), ("grouped_gemm_ragged_k wgrad", None, 0)]
+            self.desc = ("DeepSeek-V3 MoE expert layer backward, one GPU's share: c4's experts and tokens, "
+                         "dY bf16 [16384x2048] N(0,1e-3^2) e5m2; dgrad dX_g = dY_g W_g (grouped GEMM), "
+                         "wgrad dW_g = dY_g^T X_g over each expert's tokens (ragged-K grouped GEMM); bf16 out")
+            self.scales = {"recipe": "rowwise+grouped colwise", "format": "e5m2 x e4m3"}
         else:
             w = workloads.c5()
             self.x, self.w, self.dy = bf16_dev(w["x"]), bf16_dev(w["w"]), bf16_dev(w["dy"])
@@ -172,6 +203,22 @@ class Step:
             f.fp8_grouped_gemm_scaled(self.qx, f.E4M3, self.qw.view(self.g, self.n, self.k), f.E4M3, self.offsets,
                                       self.sx, self.sw.view(self.g, self.n), self.d)
             ev[3].record()
+        elif self.name == "c4b":
+            g, n, k = self.g, self.n, self.k
+            f.fp8_quantize_row(self.dy, f.E5M2, 0, self.dyq, self.dys)
+            ev[1].record()
+            f.fp8_grouped_quantize_col(self.w, f.E4M3, 0, self.woffsets, self.wt, self.wts, self.wta)
+            ev[2].record()
+            f.fp8_grouped_quantize_col(self.dy, f.E5M2, 0, self.offsets, self.dyt, self.dyts, self.dyta)
+            ev[3].record()
+            f.fp8_grouped_quantize_col(self.x, f.E4M3, 0, self.offsets, self.xt, self.xts, self.xta)
+            ev[4].record()
+            b_view = self.torch.as_strided(self.wt, (g, k, n), (n, g * n, 1))   # expert g: columns g*n.. of W^T
+            f.fp8_grouped_gemm_scaled(self.dyq, f.E5M2, b_view, f.E4M3, self.offsets, self.dys, self.wts, self.dx)
+            ev[5].record()
+            f.fp8_grouped_gemm_ragged_k(self.dyt, f.E5M2, self.xt, f.E4M3, self.offsets, self.t, self.dyts, self.xts,
+                                        self.dw)
+            ev[6].record()
         else:
             f.fp8_quantize_row(self.dy, f.E5M2, 0, self.qdy, self.sdy, None, self.cady)
             ev[1].record()
@@ -291,7 +338,7 @@ def main():
     g = gemm_idx[0]
     gemm_flops = 2.0 * np.prod(step.mnk[0])
     gemm_tflops = gemm_flops / (per_call_ms[g] * 1e-3) / 1e12
-    kernel_key = "grouped_gemm" if args.workload == "c4" else "gemm"
+    kernel_key = "grouped_gemm" if args.workload in ("c4", "c4b") else "gemm"
     traffic = measured_traffic(f"{kernel_key}:{args.workload}")
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
@@ -315,7 +362,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8_e4m3" if args.workload != "c5" else "fp8_e5m2xe4m3",
+        "vs_baseline": None, "dtype": "fp8_e4m3" if args.workload not in ("c4b", "c5") else "fp8_e5m2xe4m3",
         "data": "synthetic",
         "config": {"workload": step.desc, "m": m, "n": n, "k": k, **step.scales, "out": "bf16",
                    "flops_per_step": step.flops},

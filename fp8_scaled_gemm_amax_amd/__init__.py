@@ -31,8 +31,10 @@ OUT_BF16, OUT_F32 = 0, 1
 EXPORTED_SYMBOLS = (
     "fp8_query_device", "fp8_status_string", "fp8_last_error", "fp8_amax", "fp8_quantize_tensor",
     "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update", "fp8_gemm_scaled",
-    "fp8_grouped_gemm_scaled",
+    "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
 )
+
+GROUP_K_ALIGN = 256     # FP8_GROUP_K_ALIGN of the C header
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8amax.so")
 
@@ -64,6 +66,8 @@ def _load():
         "fp8_delayed_scale_update": [P, P, P, I64, I32, I, I32, I, P, P, P],
         "fp8_gemm_scaled": [P, I, I64, P, I, I64, I64, I64, I64, P, I, P, I, P, I, I64, P],
         "fp8_grouped_gemm_scaled": [P, I, I64, P, I, I64, I64, P, I32, I64, I64, I64, P, P, P, I, I64, P],
+        "fp8_grouped_quantize_col": [P, I64, I64, I64, I, I32, P, I32, P, I64, P, P, I32, P],
+        "fp8_grouped_gemm_ragged_k": [P, I, I64, P, I, I64, P, I32, I64, I64, I64, P, P, P, I, I64, I64, P],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -188,3 +192,44 @@ def fp8_grouped_gemm_scaled(a, fa, b, fb, group_offsets, a_scale_inv, b_scale_in
     _check(lib.fp8_grouped_gemm_scaled(_ptr(a), fa, lda, _ptr(b), fb, max(b.stride(1), k), b.stride(0),
                                        _ptr(group_offsets), g, total_m, n, k, _ptr(a_scale_inv),
                                        _ptr(b_scale_inv), _ptr(d), d_type, ldd, _stream(a)))
+
+
+def grouped_layout_width(total_m, g):
+    """Columns that always hold the grouped transposed layout of total_m rows in
+    g groups (each group padded to GROUP_K_ALIGN), rounded up to 16."""
+    w = total_m + g * (GROUP_K_ALIGN - 1)
+    return (w + 15) // 16 * 16
+
+
+def fp8_grouped_quantize_col(x, fmt, margin, group_offsets, qt, scale_inv_out, col_amax, col_amax_ready=False):
+    """x bf16 [total_m x cols], rows sorted by group; group_offsets int64 [g+1] on the
+    device; qt codes [cols x L] with L >= the layout width (grouped_layout_width
+    always suffices); scale_inv_out and col_amax fp32 [g x cols]."""
+    total_m, cols, ldx = _bf16(x)
+    qr, _, ldqt = _mat(qt, "qt", 1)
+    if qr != cols:
+        raise ValueError(f"qt must have {cols} rows (one per column of x), got {qr}")
+    if group_offsets.dtype != torch.int64 or group_offsets.dim() != 1:
+        raise ValueError("group_offsets must be a 1-D int64 tensor")
+    g = group_offsets.numel() - 1
+    _check(lib.fp8_grouped_quantize_col(_ptr(x), total_m, cols, ldx, fmt, margin, _ptr(group_offsets), g, _ptr(qt),
+                                        ldqt, _ptr(scale_inv_out), _ptr(col_amax), int(bool(col_amax_ready)),
+                                        _stream(x)))
+
+
+def fp8_grouped_gemm_ragged_k(a, fa, b, fb, group_offsets, total_m, a_scale_inv, b_scale_inv, d):
+    """a codes [m x L], b codes [n x L] in the grouped transposed layout of total_m
+    rows; group_offsets int64 [g+1] on the device; a_scale_inv fp32 [g x m],
+    b_scale_inv fp32 [g x n]; d [g x m x n] bf16 or fp32 (unit last stride)."""
+    m, _, lda = _mat(a, "a", 1)
+    n, _, ldb = _mat(b, "b", 1)
+    if d.dim() != 3 or (d.numel() > 0 and d.shape[2] > 1 and d.stride(2) != 1):
+        raise ValueError("d must be a [g x m x n] tensor with unit last stride")
+    g = group_offsets.numel() - 1
+    if tuple(d.shape) != (g, m, n):
+        raise ValueError(f"d must have shape {(g, m, n)}, got {tuple(d.shape)}")
+    d_type = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[d.dtype]
+    ldd = max(d.stride(1), n, 1)
+    _check(lib.fp8_grouped_gemm_ragged_k(_ptr(a), fa, lda, _ptr(b), fb, ldb, _ptr(group_offsets), g, total_m, m, n,
+                                         _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(d), d_type, ldd, d.stride(0),
+                                         _stream(a)))

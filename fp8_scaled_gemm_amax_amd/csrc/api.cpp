@@ -284,8 +284,7 @@ fp8_status_t fp8_grouped_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t 
     if (g < 1 || g > 4096) return fail(FP8_ERR_INVALID_ARG, "%s: group count %d outside 1..4096", fn, g);
     if (!group_offsets) return fail(FP8_ERR_INVALID_ARG, "%s: group_offsets is NULL", fn);
     if (!aligned(group_offsets, 8)) return fail(FP8_ERR_ALIGNMENT, "%s: group_offsets must be 8-byte aligned", fn);
-    if (b_group_stride < n * ldb && g > 1 && n > 0)
-        return fail(FP8_ERR_INVALID_ARG, "%s: b_group_stride %lld < n * ldb", fn, (long long)b_group_stride);
+    if (b_group_stride < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative b_group_stride", fn);
     if (b_group_stride % 16 != 0) return fail(FP8_ERR_ALIGNMENT, "%s: b_group_stride must be a multiple of 16", fn);
     if (total_m > 0 && n > 0 && (!a_scale_inv || !b_scale_inv))
         return fail(FP8_ERR_INVALID_ARG, "%s: scale is NULL", fn);
@@ -295,6 +294,61 @@ fp8_status_t fp8_grouped_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t 
     return launched(launch_grouped_gemm(a, (int)fa, lda, b, (int)fb, ldb, b_group_stride, group_offsets, g, total_m,
                                         n, k, a_scale_inv, b_scale_inv, d, d_type == FP8_OUT_F32, ldd,
                                         (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_grouped_quantize_col(const uint16_t* x, int64_t total_m, int64_t cols, int64_t ldx,
+                                      fp8_format_t fmt, int32_t margin, const int64_t* group_offsets, int32_t g,
+                                      uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* col_amax,
+                                      int32_t col_amax_ready, void* stream) {
+    const char* fn = "fp8_grouped_quantize_col";
+    FP8_TRY(check_common_quant(fn, x, total_m, cols, ldx, (int)fmt, margin));
+    FP8_TRY(check_matrix(fn, "qt", qt, cols, total_m, ldqt));
+    if (g < 1 || g > 4096) return fail(FP8_ERR_INVALID_ARG, "%s: group count %d outside 1..4096", fn, g);
+    if (!group_offsets) return fail(FP8_ERR_INVALID_ARG, "%s: group_offsets is NULL", fn);
+    if (!aligned(group_offsets, 8)) return fail(FP8_ERR_ALIGNMENT, "%s: group_offsets must be 8-byte aligned", fn);
+    if (cols > 0 && (!scale_inv_out || !col_amax))
+        return fail(FP8_ERR_INVALID_ARG, "%s: scale_inv_out and col_amax are required", fn);
+    if (col_amax_ready != 0 && col_amax_ready != 1)
+        return fail(FP8_ERR_INVALID_ARG, "%s: col_amax_ready must be 0 or 1", fn);
+    if (!aligned(scale_inv_out, 4) || !aligned(col_amax, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer", fn);
+    if (!aligned(x, 16) || ldx % 8 != 0 || cols % 8 != 0 || !aligned(qt, 16) || ldqt % 16 != 0)
+        return fail(FP8_ERR_ALIGNMENT, "%s: x must be 16-byte aligned with ldx, cols multiples of 8, "
+                    "qt 16-byte aligned with ldqt a multiple of 16", fn);
+    FP8_TRY(check_device());
+    return launched(launch_grouped_quant_col(x, total_m, cols, ldx, (int)fmt, margin, group_offsets, g, qt, ldqt,
+                                             scale_inv_out, col_amax, col_amax_ready, (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_grouped_gemm_ragged_k(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b,
+                                       fp8_format_t fb, int64_t ldb, const int64_t* group_offsets, int32_t g,
+                                       int64_t total_m, int64_t m, int64_t n, const float* a_scale_inv,
+                                       const float* b_scale_inv, void* d, fp8_out_t d_type, int64_t ldd,
+                                       int64_t d_group_stride, void* stream) {
+    const char* fn = "fp8_grouped_gemm_ragged_k";
+    if (total_m < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative total_m", fn);
+    // the contraction runs over the grouped layout's columns: lda, ldb >= total_m
+    // (checked as k = total_m rounded down to 16, the operand width requirement)
+    FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, m, n, total_m / 16 * 16, d, (int)d_type, ldd));
+    if (lda < total_m || ldb < total_m) return fail(FP8_ERR_INVALID_ARG, "%s: lda, ldb must be >= total_m", fn);
+    if (m > 0 && n > 0 && (!a || !b)) return fail(FP8_ERR_INVALID_ARG, "%s: a or b is NULL", fn);
+    if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0)
+        return fail(FP8_ERR_ALIGNMENT, "%s: a, b must be 16-byte aligned with lda, ldb multiples of 16", fn);
+    if (g < 1 || g > 4096) return fail(FP8_ERR_INVALID_ARG, "%s: group count %d outside 1..4096", fn, g);
+    if (!group_offsets) return fail(FP8_ERR_INVALID_ARG, "%s: group_offsets is NULL", fn);
+    if (!aligned(group_offsets, 8)) return fail(FP8_ERR_ALIGNMENT, "%s: group_offsets must be 8-byte aligned", fn);
+    if (g > 1 && m > 0 && d_group_stride < m * ldd)
+        return fail(FP8_ERR_INVALID_ARG, "%s: d_group_stride %lld < m * ldd", fn, (long long)d_group_stride);
+    if (d_group_stride < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative d_group_stride", fn);
+    if (m > 0 && n > 0 && (!a_scale_inv || !b_scale_inv)) return fail(FP8_ERR_INVALID_ARG, "%s: scale is NULL", fn);
+    if (!aligned(a_scale_inv, 4) || !aligned(b_scale_inv, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned scale pointer", fn);
+    FP8_TRY(check_device());
+    return launched(launch_grouped_gemm_ragged_k(a, (int)fa, lda, b, (int)fb, ldb, group_offsets, g, total_m, m, n,
+                                                 a_scale_inv, b_scale_inv, d, d_type == FP8_OUT_F32, ldd,
+                                                 d_group_stride, (hipStream_t)stream),
                     fn);
 }
 

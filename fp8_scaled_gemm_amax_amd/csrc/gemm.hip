@@ -253,8 +253,7 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kStages = 4;
 constexpr int kStage = (BM + BN) * BK;              // 32 KB: A tile then B tile
 constexpr int kLoadsPerStage = 8;                   // direct loads per thread per stage (4 A + 4 B)
-constexpr int kEpiPitch = 256 + 16;                 // bytes per staged bf16 output row (128 cols + pad)
-constexpr int kEpiWave = 128 * kEpiPitch;           // one wavefront's 128 x 128 bf16 block
+constexpr int kEpiWave = 32 * 1024;                 // one wavefront's staged 128 x 128 bf16 block
 constexpr int kMain = 4 * kEpiWave > kStages * kStage ? 4 * kEpiWave : kStages * kStage;
 constexpr int kScaleOff = kMain;                    // 256 row scales, then 256 column scales (fp32)
 constexpr int kSmem = kMain + 2 * 256 * 4;
@@ -462,6 +461,16 @@ __device__ __forceinline__ void big_mainloop(uint8_t* smem, const uint8_t* a, in
     wait_vmcnt<0>();                                     // no load may still land in LDS after this
 }
 
+// Staged bf16 block of the epilogue: group g of 4 rows, column c -> 8 bytes
+// (the 4 rows' values) at g * 1024 + unit * 16 + (c % 2) * 8, where the 16-byte
+// unit c / 2 = u is stored at (u & ~3) | ((u ^ (u >> 4)) & 3): the 16 lanes of
+// one 16-byte read (units 4i + k, i = 0..15) then hit 16 distinct bank groups,
+// and the 32 lanes of one 8-byte write still cover 256 contiguous bytes.
+__device__ __forceinline__ int epi_off(int g, int c) {
+    const int u = c >> 1;
+    return g * 1024 + (((u & ~3) | ((u ^ (u >> 4)) & 3)) << 4) + ((c & 1) << 3);
+}
+
 // Epilogue of a 256 x 256 tile at (row0, col0) with rows_total / cols_total
 // valid rows / columns from there: d = acc * sa_row * sb_col, the 256 row and
 // 256 column scales of the tile sitting in the scale area of LDS.
@@ -488,7 +497,7 @@ __device__ __forceinline__ void big_epilogue(uint8_t* smem, v16f (&acc)[4][4], v
     float sbj[4];
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) sbj[ni] = s_cols[wn * 128 + ni * 32 + (lane & 31)];
-    if (OUT_F32 || !vec_out) {
+    if (OUT_F32) {
         // direct stores from registers
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
@@ -503,50 +512,65 @@ __device__ __forceinline__ void big_epilogue(uint8_t* smem, v16f (&acc)[4][4], v
                     if (lc >= cols_valid) continue;
                     const float v = acc[mi][ni][r] * sai * sbj[ni];
                     const int64_t off = (wrow0 + lr) * ldd + wcol0 + lc;
-                    if (OUT_F32)
-                        reinterpret_cast<float*>(d)[off] = v;
-                    else
-                        reinterpret_cast<uint16_t*>(d)[off] = (uint16_t)f32_to_bf16(v);
+                    reinterpret_cast<float*>(d)[off] = v;
                 }
             }
         return;
     }
-    // bf16 through LDS: each wavefront stages its 128 x 128 block row-major
-    // (padded rows), two values per hardware conversion, then streams it out
-    // 16 bytes per lane, 4 rows of 256 contiguous bytes per store instruction.
+    // bf16 through LDS, each wavefront on its own 128 x 128 block (no barrier
+    // between writing and reading it back: a wavefront's LDS operations are
+    // done in order). A lane's registers hold 4 consecutive rows of one column
+    // (acc[mi][ni][4q .. 4q+3]); they go out as one 8-byte write per column.
+    // The read-back takes 8 columns x 4 rows per lane (four 16-byte reads) and
+    // byte-permutes them into four row chunks of 8 columns: 16-byte stores, 16
+    // lanes per 256 contiguous bytes of a row.
     uint8_t* ep = smem + wave * big::kEpiWave;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int lr0 = mi * 32 + 8 * q + 4 * (lane >> 5);     // rows lr0 .. lr0+3
-            const u32x4 s4 = *reinterpret_cast<const u32x4*>(&s_rows[wm * 128 + lr0]);
+            const int g = 8 * mi + 2 * q + (lane >> 5);              // rows 4g .. 4g+3 of the block
+            const u32x4 s4 = *reinterpret_cast<const u32x4*>(&s_rows[wm * 128 + 4 * g]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float sai = __uint_as_float(s4[i]);
-                const int r = 4 * q + i;
-#pragma unroll
-                for (int ni = 0; ni < 4; ni += 2) {
-                    v2f v = {acc[mi][ni][r] * sai * sbj[ni], acc[mi][ni + 1][r] * sai * sbj[ni + 1]};
-                    const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, v2bf));
-                    uint8_t* rowp = ep + (lr0 + i) * big::kEpiPitch + (lane & 31) * 2;
-                    *reinterpret_cast<uint16_t*>(rowp + ni * 64) = (uint16_t)w;
-                    *reinterpret_cast<uint16_t*>(rowp + (ni + 1) * 64) = (uint16_t)(w >> 16);
-                }
+            for (int ni = 0; ni < 4; ++ni) {
+                const int r = 4 * q;
+                v2f v01 = {acc[mi][ni][r] * __uint_as_float(s4[0]) * sbj[ni],
+                           acc[mi][ni][r + 1] * __uint_as_float(s4[1]) * sbj[ni]};
+                v2f v23 = {acc[mi][ni][r + 2] * __uint_as_float(s4[2]) * sbj[ni],
+                           acc[mi][ni][r + 3] * __uint_as_float(s4[3]) * sbj[ni]};
+                uint2 w;
+                w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, v2bf));
+                w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, v2bf));
+                *reinterpret_cast<uint2*>(ep + epi_off(g, 32 * ni + (lane & 31))) = w;
             }
         }
-    __syncthreads();
-#pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-        const int lr = it * 4 + (lane >> 4);
-        const int ch = lane & 15;                        // 8 bf16 columns
-        if (lr >= rows_valid) continue;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(ep + lr * big::kEpiPitch + ch * 16);
-        uint16_t* dst = reinterpret_cast<uint16_t*>(d) + (wrow0 + lr) * ldd + wcol0 + ch * 8;
-        if (ch * 8 + 8 <= cols_valid) {
-            *reinterpret_cast<u32x4*>(dst) = val;
-        } else {
-            for (int e = 0; e < 8 && ch * 8 + e < cols_valid; ++e) dst[e] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
+    wait_vmcnt<63, 0>();                                 // this wavefront's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int cc = lane & 15;                            // columns 8cc .. 8cc+7
+    const bool full_cols = vec_out && 8 * cc + 8 <= cols_valid;
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+        const int g = 4 * it + (lane >> 4);
+        u32x4 un[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) un[k] = *reinterpret_cast<const u32x4*>(ep + epi_off(g, 8 * cc + 2 * k));
+        // unit k: column 8cc+2k in words 0 (rows 0, 1) and 1 (rows 2, 3), column 8cc+2k+1 in words 2 and 3
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int lr = 4 * g + r;
+            if (lr >= rows_valid) continue;
+            const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
+            const int wlo = (r >> 1), whi = 2 + (r >> 1);
+            u32x4 row;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) row[k] = __builtin_amdgcn_perm(un[k][whi], un[k][wlo], sel);
+            uint16_t* dst = reinterpret_cast<uint16_t*>(d) + (wrow0 + lr) * ldd + wcol0 + 8 * cc;
+            if (full_cols) {
+                *reinterpret_cast<u32x4*>(dst) = row;
+            } else {
+                for (int e = 0; e < 8 && 8 * cc + e < cols_valid; ++e)
+                    dst[e] = (uint16_t)(row[e >> 1] >> (16 * (e & 1)));
+            }
         }
     }
 }
@@ -666,6 +690,78 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, hi - row0, col0, n - col0, vec_out);
 }
 
+// Grouped product over ragged contraction ranges (the MoE weight gradient):
+// D_g = A[:, P_g : P_g + K_g] B[:, P_g : P_g + K_g]^T * sa_g * sb_g with
+// K_g = roundup(m_g, 256) over the grouped transposed layout (its zero padding
+// adds nothing) and P_g the sum of the earlier groups' K_h. The grid holds
+// G x per8 slots, per8 = tiles_m * tiles_n rounded up to 8: group g's tiles are
+// dealt evenly to the 8 XCDs (slot w goes to XCD w % 8), contiguous within an
+// XCD, so groups of very different K_g keep the XCDs balanced; slots past a
+// group's tile count exit. Contraction columns at or past min(lda, ldb) are
+// never read.
+template <int FA, int FB, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
+    const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb,
+    const int64_t* __restrict__ offsets, int G, int64_t total, int64_t m, int64_t n, const float* __restrict__ sa,
+    const float* __restrict__ sb, void* __restrict__ d, int64_t ldd, int64_t d_group_stride, int vec_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[big::kSmem];
+    __shared__ int64_t wsum[4];
+    const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
+    const int64_t per = tiles_m * tiles_n, per8 = (per + 7) / 8 * 8;
+    const int grp = (int)(blockIdx.x / per8);
+    const int64_t wp = blockIdx.x % per8;
+    const int64_t xcd = wp % 8, idx = wp / 8, q = per / 8, rem = per % 8;
+    if (idx >= q + (xcd < rem ? 1 : 0)) return;        // uniform over the workgroup
+    const int64_t lt = xcd * q + (xcd < rem ? xcd : rem) + idx;
+    constexpr int64_t gm = 4;
+    const int64_t first_m = (lt / (gm * tiles_n)) * gm;
+    const int64_t gsize = tiles_m - first_m < gm ? tiles_m - first_m : gm;
+    const int64_t pm = first_m + (lt % (gm * tiles_n)) % gsize;
+    const int64_t pn = (lt % (gm * tiles_n)) / gsize;
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    auto kpad = [&](int h) {
+        int64_t lo = offsets[h], hi = offsets[h + 1];
+        lo = lo < 0 ? 0 : (lo > total ? total : lo);
+        hi = hi < lo ? lo : (hi > total ? total : hi);
+        return (hi - lo + 255) / 256 * 256;
+    };
+    // P_grp: the groups before grp shared over the workgroup's threads
+    int64_t part = 0;
+    for (int h = t; h < grp; h += 256) part += kpad(h);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    if (lane == 0) wsum[wave] = part;
+    __syncthreads();
+    const int64_t P = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    int64_t K = kpad(grp);
+    const int64_t lim = lda < ldb ? lda : ldb;
+    if (P >= lim)
+        K = 0;
+    else if (P + K > lim)
+        K = (lim - P) / 256 * 256;
+    const int64_t row0 = pm * big::BM, col0 = pn * big::BN;
+    const float* sa_lane = sa + (int64_t)grp * m + (row0 + t < m ? row0 + t : m - 1);
+    const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
+    v16f acc[4][4];
+    if (K > 0) {
+        big_mainloop<FA, FB>(smem, a + row0 * lda + P, lda, m - row0, b + col0 * ldb + P, ldb, n - col0, K, sa_lane,
+                             sb_lane, acc);
+    } else {                                             // empty group: 0 * sa * sb
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+        float* s_rows = reinterpret_cast<float*>(smem + big::kScaleOff);
+        s_rows[t] = *sa_lane;
+        s_rows[256 + t] = *sb_lane;
+    }
+    uint8_t* dg = reinterpret_cast<uint8_t*>(d) + (int64_t)grp * d_group_stride * (OUT_F32 ? 4 : 2);
+    big_epilogue<OUT_F32>(smem, acc, dg, ldd, row0, m - row0, col0, n - col0, vec_out);
+}
+
 template <int FA, int FB, bool OUT_F32>
 hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m, int64_t n, int64_t k,
                       const float* sa, int sa_vec, const float* sb, int sb_vec, void* d, int64_t ldd,
@@ -703,7 +799,35 @@ hipError_t grouped_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_
     return hipGetLastError();
 }
 
+template <int FA, int FB, bool OUT_F32>
+hipError_t ragged_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, const int64_t* offsets, int g,
+                        int64_t total, int64_t m, int64_t n, const float* sa, const float* sb, void* d, int64_t ldd,
+                        int64_t dgs, hipStream_t st) {
+    if (m == 0 || n == 0) return hipSuccess;
+    const int64_t per = ((m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
+    const int64_t grid = (int64_t)g * ((per + 7) / 8 * 8);
+    const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0 && dgs % 8 == 0;
+    hipLaunchKernelGGL((k_grouped_gemm_ragged_k<FA, FB, OUT_F32>), dim3((unsigned)grid), dim3(256), 0, st, a, lda, b,
+                       ldb, offsets, g, total, m, n, sa, sb, d, ldd, dgs, vec_out);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_grouped_gemm_ragged_k(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb,
+                                        const int64_t* offsets, int g, int64_t total_m, int64_t m, int64_t n,
+                                        const float* sa, const float* sb, void* d, int out_f32, int64_t ldd,
+                                        int64_t d_group_stride, hipStream_t st) {
+#define CALL(FA, FB, OF) \
+    ragged_typed<FA, FB, OF>(a, lda, b, ldb, offsets, g, total_m, m, n, sa, sb, d, ldd, d_group_stride, st)
+#define BY_OUT(FA, FB) return out_f32 ? CALL(FA, FB, true) : CALL(FA, FB, false)
+    if (fa == kE4M3 && fb == kE4M3) BY_OUT(kE4M3, kE4M3);
+    if (fa == kE4M3 && fb == kE5M2) BY_OUT(kE4M3, kE5M2);
+    if (fa == kE5M2 && fb == kE4M3) BY_OUT(kE5M2, kE4M3);
+    BY_OUT(kE5M2, kE5M2);
+#undef BY_OUT
+#undef CALL
+}
 
 hipError_t launch_gemm(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb, int64_t m,
                        int64_t n, int64_t k, const float* sa, int sa_vec, const float* sb, int sb_vec, void* d,

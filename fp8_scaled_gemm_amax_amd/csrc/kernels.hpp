@@ -40,4 +40,17 @@ hipError_t launch_grouped_gemm(const uint8_t* a, int fa, int64_t lda, const uint
                                int64_t k, const float* sa, const float* sb, void* d, int out_f32, int64_t ldd,
                                hipStream_t st);
 
+// MoE backward: per-group colwise quantization into the grouped transposed
+// layout, and the grouped product over ragged contraction ranges.
+constexpr int64_t kGroupKAlign = 256;
+
+hipError_t launch_grouped_quant_col(const uint16_t* x, int64_t total_m, int64_t cols, int64_t ldx, int fmt,
+                                    int margin, const int64_t* offsets, int g, uint8_t* qt, int64_t ldqt,
+                                    float* scale_inv, float* col_amax, int col_amax_ready, hipStream_t st);
+
+hipError_t launch_grouped_gemm_ragged_k(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb,
+                                        const int64_t* offsets, int g, int64_t total_m, int64_t m, int64_t n,
+                                        const float* sa, const float* sb, void* d, int out_f32, int64_t ldd,
+                                        int64_t d_group_stride, hipStream_t st);
+
 }  // namespace fp8amax

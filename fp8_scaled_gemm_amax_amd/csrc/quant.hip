@@ -90,41 +90,66 @@ __global__ __launch_bounds__(kBlock) void k_amax_rows(const uint16_t* __restrict
     if (lane == 0) out[row] = amax_from_bits16(mx);
 }
 
+// Row amax with the row in registers (MAXC 16-byte chunks per lane, all loads
+// in flight together), one wavefront per row.
+template <int MAXC>
+__global__ __launch_bounds__(kBlock) void k_amax_rows_reg(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                          int64_t ldx, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int nch = (int)(cols >> 3);
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
+    uint4 v[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk (a max ignores it)
+    }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) mx = word_absmax(mx, v[c]);
+    mx = wave_max_u32(pk_fold(mx));
+    if (lane == 0) out[row] = amax_from_bits16(mx);
+}
+
 // Column amax: a workgroup covers 512 columns (64 lanes x 8) of a band of
-// kColRows rows, four rows at a time (one per wavefront); partial maxima meet
-// in LDS and each column is folded into out[] by one atomic max (out cleared
-// beforehand).
-constexpr int kColRows = 256;
+// kColAmaxRows rows; wavefront w takes rows w, w + 4, .., sixteen 16-byte
+// loads per lane in flight at a time. Partial maxima meet in LDS and each
+// column is folded into out[] (cleared beforehand) by one atomic max per
+// workgroup.
+constexpr int kColRows = 256;       // row band of the scalar kernels
+constexpr int kColAmaxRows = 256;   // row band of the vector column-amax kernel
+constexpr int kColAmaxUnroll = 16;
 
 __global__ __launch_bounds__(kBlock) void k_amax_cols_vec(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                           int64_t ldx, float* __restrict__ out) {
     __shared__ uint32_t part[kWaves][256];   // packed u16 pairs: 512 columns
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t ch = (int64_t)blockIdx.x * 64 + lane;        // 8-column chunk index
+    const int64_t ch = (int64_t)blockIdx.y * 64 + lane;        // 8-column chunk index
     const int64_t nch = cols >> 3;
-    const int64_t r0 = (int64_t)blockIdx.y * kColRows;
-    const int64_t r1 = r0 + kColRows < rows ? r0 + kColRows : rows;
+    const int64_t r0 = (int64_t)blockIdx.x * kColAmaxRows;
+    const int64_t r1 = r0 + kColAmaxRows < rows ? r0 + kColAmaxRows : rows;
     uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
     if (ch < nch) {
         const uint16_t* base = x + ch * 8;
-        int64_t r = r0 + wave;
-        for (; r + 3 * kWaves < r1; r += 4 * kWaves) {
-            uint4 v0 = *reinterpret_cast<const uint4*>(base + r * ldx);
-            uint4 v1 = *reinterpret_cast<const uint4*>(base + (r + kWaves) * ldx);
-            uint4 v2 = *reinterpret_cast<const uint4*>(base + (r + 2 * kWaves) * ldx);
-            uint4 v3 = *reinterpret_cast<const uint4*>(base + (r + 3 * kWaves) * ldx);
-            m0 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m0, v0.x), v1.x), v2.x), v3.x);
-            m1 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m1, v0.y), v1.y), v2.y), v3.y);
-            m2 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m2, v0.z), v1.z), v2.z), v3.z);
-            m3 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m3, v0.w), v1.w), v2.w), v3.w);
-        }
-        for (; r < r1; r += kWaves) {
-            uint4 v = *reinterpret_cast<const uint4*>(base + r * ldx);
-            m0 = pk_absmax(m0, v.x);
-            m1 = pk_absmax(m1, v.y);
-            m2 = pk_absmax(m2, v.z);
-            m3 = pk_absmax(m3, v.w);
+        for (int64_t rb = r0 + wave; rb < r1; rb += kColAmaxUnroll * kWaves) {
+            uint4 v[kColAmaxUnroll];
+#pragma unroll
+            for (int u = 0; u < kColAmaxUnroll; ++u) {
+                const int64_t r = rb + u * kWaves;
+                // rows past the band re-read its last row (a max ignores duplicates); the
+                // loads stay unconditional, so all of them are in flight together
+                v[u] = *reinterpret_cast<const uint4*>(base + (r < r1 ? r : r1 - 1) * ldx);
+            }
+#pragma unroll
+            for (int u = 0; u < kColAmaxUnroll; ++u) {
+                m0 = pk_absmax(m0, v[u].x);
+                m1 = pk_absmax(m1, v[u].y);
+                m2 = pk_absmax(m2, v[u].z);
+                m3 = pk_absmax(m3, v[u].w);
+            }
         }
     }
     part[wave][lane * 4 + 0] = m0;
@@ -137,16 +162,16 @@ __global__ __launch_bounds__(kBlock) void k_amax_cols_vec(const uint16_t* __rest
     uint32_t w = part[0][t];
 #pragma unroll
     for (int k = 1; k < kWaves; ++k) w = pk_absmax(w, part[k][t]);
-    const int64_t col = (int64_t)blockIdx.x * 512 + 2 * t;
+    const int64_t col = (int64_t)blockIdx.y * 512 + 2 * t;
     if (col < cols) atomic_max_bits(out + col, (w & 0xffffu) << 16);
     if (col + 1 < cols) atomic_max_bits(out + col + 1, w & 0xffff0000u);
 }
 
 __global__ __launch_bounds__(kBlock) void k_amax_cols_scalar(const uint16_t* __restrict__ x, int64_t rows,
                                                              int64_t cols, int64_t ldx, float* __restrict__ out) {
-    const int64_t col = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t col = (int64_t)blockIdx.y * kBlock + threadIdx.x;
     if (col >= cols) return;
-    const int64_t r0 = (int64_t)blockIdx.y * kColRows;
+    const int64_t r0 = (int64_t)blockIdx.x * kColRows;
     const int64_t r1 = r0 + kColRows < rows ? r0 + kColRows : rows;
     uint32_t mx = 0;
     for (int64_t r = r0; r < r1; ++r) {
@@ -183,6 +208,32 @@ __global__ __launch_bounds__(kBlock) void k_amax_tensor(const uint16_t* __restri
     if (threadIdx.x == 0) atomic_max_bits(out, mx << 16);
 }
 
+// Whole-tensor amax: wavefronts stride over rows, each row loaded whole into
+// registers (MAXC 16-byte chunks per lane, all in flight at once); one atomic
+// per workgroup.
+template <int MAXC>
+__global__ __launch_bounds__(kBlock) void k_amax_tensor_reg(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, int64_t ldx, float* __restrict__ out) {
+    __shared__ uint32_t red[kWaves];
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int nch = (int)(cols >> 3);
+    uint32_t mx = 0;
+    for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < rows; row += nwaves) {
+        const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
+        uint4 v[MAXC];
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = lane + c * 64;
+            v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk, never stored
+        }
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) mx = word_absmax(mx, v[c]);
+    }
+    mx = block_max_u32(pk_fold(mx), red);
+    if (threadIdx.x == 0) atomic_max_bits(out, mx << 16);
+}
+
 // ---------------------------------------------------------- rowwise quantizer --
 
 // One wavefront per row, the whole row held in registers (MAXC 16-byte chunks
@@ -201,7 +252,7 @@ __global__ __launch_bounds__(kBlock) void k_quant_row_reg(const uint16_t* __rest
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         const int ch = lane + c * 64;
-        v[c] = ch < nch ? xr[ch] : make_uint4(0u, 0u, 0u, 0u);
+        v[c] = xr[ch < nch ? ch : nch - 1];         // past the row: a duplicate chunk, never stored
     }
     uint32_t mx = 0;
 #pragma unroll
@@ -324,6 +375,64 @@ __global__ __launch_bounds__(kBlock) void k_quant_tensor(const uint16_t* __restr
     }
 }
 
+// Tensorwise cast with the row in registers (one wavefront per row, MAXC
+// 16-byte chunks per lane). DELAYED: the scale comes from the state and the
+// tensor's amax is folded into amax_io (the row's own amax picks the encoder:
+// a row holding a NaN takes the bit-level one); otherwise the scale comes from
+// amax_io, which the amax pass filled, and a NaN amax sends every row to the
+// bit-level encoder.
+template <int F, int MAXC, bool DELAYED>
+__global__ __launch_bounds__(kBlock) void k_quant_tensor_reg(const uint16_t* __restrict__ x, int64_t rows,
+                                                             int64_t cols, int64_t ldx, int margin,
+                                                             const float* __restrict__ scale, uint8_t* __restrict__ q,
+                                                             int64_t ldq, float* __restrict__ scale_inv,
+                                                             float* __restrict__ amax_io) {
+    __shared__ uint32_t red[kWaves];
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const float s = DELAYED ? *scale : scale_from_amax<F>(*amax_io, margin);
+    const bool tensor_nan = DELAYED ? false : __builtin_isnan(*amax_io);
+    if (blockIdx.x == 0 && threadIdx.x == 0) scale_inv[0] = 1.0f / s;
+    const int nch = (int)(cols >> 3);
+    uint32_t mx = 0;
+    for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < rows; row += nwaves) {
+        const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
+        uint4 v[MAXC];
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = lane + c * 64;
+            v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk, never stored
+        }
+        bool nan_row = tensor_nan;
+        if (DELAYED) {
+            uint32_t rm = 0;
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) rm = word_absmax(rm, v[c]);
+            rm = pk_fold(rm);
+            mx = rm > mx ? rm : mx;
+            nan_row = nan_bits16(wave_max_u32(rm));
+        }
+        uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+        if (!nan_row) {
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) {
+                const int ch = lane + c * 64;
+                if (ch < nch) qr[ch] = encode8<F, true>(v[c], s);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) {
+                const int ch = lane + c * 64;
+                if (ch < nch) qr[ch] = encode8<F, false>(v[c], s);
+            }
+        }
+    }
+    if (DELAYED) {
+        mx = block_max_u32(mx, red);
+        if (threadIdx.x == 0) atomic_max_bits(amax_io, mx << 16);
+    }
+}
+
 // ---------------------------------------------------------- colwise quantizer --
 
 // Scales of the workgroup's 64 columns, computed once into LDS.
@@ -337,7 +446,7 @@ __device__ __forceinline__ void col_scales_to_lds(const float* __restrict__ col_
         const float s = scale_from_amax<F>(a, margin);
         s_lds[threadIdx.x] = s;
         nan_lds[threadIdx.x] = __builtin_isnan(a) ? 1 : 0;
-        if (blockIdx.y == 0 && c < cols) scale_inv[c] = 1.0f / s;
+        if (scale_inv && c < cols) scale_inv[c] = 1.0f / s;
     }
     __syncthreads();
 }
@@ -353,19 +462,15 @@ __device__ __forceinline__ void col_scales_to_lds(const float* __restrict__ col_
 // (= input column) as 128 contiguous bytes.
 constexpr int kColTileR = 128, kColTileC = 64;
 
+// One 128 x 64 tile: source rows r0 .. r0+127 (rows at or past src_end read as
+// row src_end-1, or as zeros when zero_past_end), columns c0 .. c0+63 scaled by
+// s_lds / nan_lds; written transposed to qt rows c0 .. (one per column) at
+// columns d0 .. d0+127, none at or past d_end.
 template <int F>
-__global__ __launch_bounds__(kBlock) void k_quant_col_tiled(const uint16_t* __restrict__ x, int64_t rows,
-                                                            int64_t cols, int64_t ldx, int margin,
-                                                            uint8_t* __restrict__ qt, int64_t ldqt,
-                                                            float* __restrict__ scale_inv,
-                                                            const float* __restrict__ col_amax, int vec_store) {
-    __shared__ float s_lds[kColTileC];
-    __shared__ int nan_lds[kColTileC];
-    __shared__ __attribute__((aligned(16))) uint32_t tile[kColTileC * kColTileR / 4];
-    const int64_t c0 = (int64_t)blockIdx.x * kColTileC;
-    const int64_t r0 = (int64_t)blockIdx.y * kColTileR;
-    col_scales_to_lds<F>(col_amax, c0, cols, margin, scale_inv, s_lds, nan_lds);
-
+__device__ __forceinline__ void col_tile(const uint16_t* __restrict__ x, int64_t ldx, int64_t r0, int64_t src_end,
+                                         bool zero_past_end, int64_t c0, int64_t cols, const float* s_lds,
+                                         const int* nan_lds, uint32_t* tile, uint8_t* __restrict__ qt, int64_t ldqt,
+                                         int64_t d0, int64_t d_end, int vec_store) {
     const int t = threadIdx.x;
     const int cc = t & 7, rg = t >> 3;
     const int64_t col = c0 + cc * 8;
@@ -377,12 +482,16 @@ __global__ __launch_bounds__(kBlock) void k_quant_col_tiled(const uint16_t* __re
         s[j] = s_lds[cc * 8 + j];
         any_nan |= nan_lds[cc * 8 + j];
     }
+    // rows / columns past the end re-read the last row / chunk, so the loads stay
+    // unconditional (all four in flight together); those codes are never stored,
+    // or become zeros when zero_past_end
     uint4 v[4];
+    const int64_t lcol = col < cols ? col : cols - 8;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int64_t row = r0 + rg * 4 + r;
-        v[r] = make_uint4(0u, 0u, 0u, 0u);
-        if (row < rows && col < cols) v[r] = *reinterpret_cast<const uint4*>(x + row * ldx + col);
+        v[r] = *reinterpret_cast<const uint4*>(x + (row < src_end ? row : src_end - 1) * ldx + lcol);
+        if (zero_past_end && row >= src_end) v[r] = make_uint4(0u, 0u, 0u, 0u);
     }
     if (!any_nan) {
 #pragma unroll
@@ -429,15 +538,187 @@ __global__ __launch_bounds__(kBlock) void k_quant_col_tiled(const uint16_t* __re
         if (ocol >= cols) continue;
         const int sw = (rc ^ (lc >> 3)) & 7;
         const uint4 val = *reinterpret_cast<const uint4*>(&tile[lc * (kColTileR / 4) + sw * 4]);
-        const int64_t orow = r0 + rc * 16;
+        const int64_t orow = d0 + rc * 16;
         uint8_t* dst = qt + ocol * ldqt + orow;
-        if (vec_store && orow + 16 <= rows) {
+        if (vec_store && orow + 16 <= d_end) {
             *reinterpret_cast<uint4*>(dst) = val;
         } else {
             const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
-            for (int b = 0; b < 16 && orow + b < rows; ++b) dst[b] = (uint8_t)(wv[b >> 2] >> (8 * (b & 3)));
+            for (int b = 0; b < 16 && orow + b < d_end; ++b) dst[b] = (uint8_t)(wv[b >> 2] >> (8 * (b & 3)));
         }
     }
+}
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_quant_col_tiled(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, int64_t ldx, int margin,
+                                                            uint8_t* __restrict__ qt, int64_t ldqt,
+                                                            float* __restrict__ scale_inv,
+                                                            const float* __restrict__ col_amax, int vec_store) {
+    __shared__ float s_lds[kColTileC];
+    __shared__ int nan_lds[kColTileC];
+    __shared__ __attribute__((aligned(16))) uint32_t tile[kColTileC * kColTileR / 4];
+    const int64_t c0 = (int64_t)blockIdx.y * kColTileC;
+    const int64_t r0 = (int64_t)blockIdx.x * kColTileR;
+    col_scales_to_lds<F>(col_amax, c0, cols, margin, blockIdx.x == 0 ? scale_inv : nullptr, s_lds, nan_lds);
+    col_tile<F>(x, ldx, r0, rows, false, c0, cols, s_lds, nan_lds, tile, qt, ldqt, r0, rows, vec_store);
+}
+
+// ------------------------------------------------- grouped colwise (MoE) --
+
+// Row range of group g: offsets clamped to [0, total], hi >= lo.
+__device__ __forceinline__ void group_rows(const int64_t* __restrict__ off, int g, int64_t total, int64_t* lo,
+                                           int64_t* hi) {
+    int64_t a = off[g], b = off[g + 1];
+    a = a < 0 ? 0 : (a > total ? total : a);
+    b = b < a ? a : (b > total ? total : b);
+    *lo = a;
+    *hi = b;
+}
+
+// Per-group column amax. A workgroup covers 512 columns of a band of 256 rows
+// and walks the groups that meet the band (the first by binary search over the
+// offsets): for each, the rows of the band inside the group are reduced as in
+// k_amax_cols_vec and folded by one atomic per column into out[g * cols + c]
+// (cleared beforehand).
+__global__ __launch_bounds__(kBlock) void k_grouped_amax_cols(const uint16_t* __restrict__ x, int64_t total,
+                                                              int64_t cols, int64_t ldx,
+                                                              const int64_t* __restrict__ off, int G,
+                                                              float* __restrict__ out) {
+    __shared__ uint32_t part[kWaves][256];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t ch = (int64_t)blockIdx.y * 64 + lane;
+    const int64_t nch = cols >> 3;
+    int64_t r0 = (int64_t)blockIdx.x * kColAmaxRows;
+    const int64_t r1 = r0 + kColAmaxRows < total ? r0 + kColAmaxRows : total;
+    // first group whose rows reach past r0: the last g with a clamped start <= r0
+    int glo = 0, ghi = G;
+    while (ghi - glo > 1) {
+        const int mid = (glo + ghi) >> 1;
+        int64_t a = off[mid];
+        a = a < 0 ? 0 : (a > total ? total : a);
+        if (a <= r0)
+            glo = mid;
+        else
+            ghi = mid;
+    }
+    for (int g = glo; g < G && r0 < r1; ++g) {
+        int64_t lo, hi;
+        group_rows(off, g, total, &lo, &hi);
+        const int64_t a = r0 > lo ? r0 : lo, b = r1 < hi ? r1 : hi;
+        if (b <= a) continue;                            // (uniform: the whole workgroup skips)
+        uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+        if (ch < nch) {
+            const uint16_t* base = x + ch * 8;
+            for (int64_t rb = a + wave; rb < b; rb += kColAmaxUnroll * kWaves) {
+                uint4 v[kColAmaxUnroll];
+#pragma unroll
+                for (int u = 0; u < kColAmaxUnroll; ++u) {
+                    const int64_t r = rb + u * kWaves;
+                    v[u] = *reinterpret_cast<const uint4*>(base + (r < b ? r : b - 1) * ldx);   // duplicates are harmless
+                }
+#pragma unroll
+                for (int u = 0; u < kColAmaxUnroll; ++u) {
+                    m0 = pk_absmax(m0, v[u].x);
+                    m1 = pk_absmax(m1, v[u].y);
+                    m2 = pk_absmax(m2, v[u].z);
+                    m3 = pk_absmax(m3, v[u].w);
+                }
+            }
+        }
+        part[wave][lane * 4 + 0] = m0;
+        part[wave][lane * 4 + 1] = m1;
+        part[wave][lane * 4 + 2] = m2;
+        part[wave][lane * 4 + 3] = m3;
+        __syncthreads();
+        const int t = threadIdx.x;
+        uint32_t w = part[0][t];
+#pragma unroll
+        for (int k = 1; k < kWaves; ++k) w = pk_absmax(w, part[k][t]);
+        const int64_t col = (int64_t)blockIdx.y * 512 + 2 * t;
+        float* og = out + (int64_t)g * cols;
+        if (col < cols) atomic_max_bits(og + col, (w & 0xffffu) << 16);
+        if (col + 1 < cols) atomic_max_bits(og + col + 1, w & 0xffff0000u);
+        __syncthreads();                                 // part[] is reused by the next group
+        r0 = b;
+    }
+}
+
+// scale_inv[i] = 1 / s(amax[i]) for every group and column (empty groups: 1).
+template <int F>
+__global__ void k_scale_inv_from_amax(const float* __restrict__ amax, int64_t n, int margin,
+                                      float* __restrict__ scale_inv) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        scale_inv[i] = 1.0f / scale_from_amax<F>(amax[i], margin);
+}
+
+// Grouped transposed cast. Group g is cut into rt_g = roundup(m_g, 256) / 128
+// row tiles of 128; tile t of group g covers its rows t*128 .. t*128+127
+// (zeros past m_g: the padding) and lands at qt columns P_g + t*128 .., where
+// P_g = 128 * (rt_0 + .. + rt_{g-1}). Every workgroup forms those prefix sums
+// in LDS (256 threads, then a block scan), exits if blockIdx.x is past the last
+// tile (the grid is a host-side upper bound), and finds its group by binary
+// search.
+constexpr int kMaxGroups = 4096;
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_grouped_quant_col_tiled(const uint16_t* __restrict__ x, int64_t total,
+                                                                    int64_t cols, int64_t ldx, int margin,
+                                                                    const int64_t* __restrict__ off, int G,
+                                                                    uint8_t* __restrict__ qt, int64_t ldqt,
+                                                                    const float* __restrict__ col_amax,
+                                                                    int vec_store) {
+    __shared__ float s_lds[kColTileC];
+    __shared__ int nan_lds[kColTileC];
+    __shared__ __attribute__((aligned(16))) uint32_t tile[kColTileC * kColTileR / 4];
+    __shared__ int32_t pre[kMaxGroups + 1];
+    __shared__ int32_t wsum[kWaves];
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    auto row_tiles = [&](int g) {
+        int64_t lo, hi;
+        group_rows(off, g, total, &lo, &hi);
+        return (int32_t)(2 * ((hi - lo + 255) / 256));
+    };
+    const int per = (G + kBlock - 1) / kBlock;
+    const int e0 = t * per, e1 = e0 + per < G ? e0 + per : G;
+    int32_t mine = 0;
+    for (int e = e0; e < e1; ++e) mine += row_tiles(e);
+    int32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int32_t run = incl - mine;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+    for (int e = e0; e < e1; ++e) {
+        pre[e] = run;
+        run += row_tiles(e);
+    }
+    if (t == kBlock - 1) pre[G] = run;
+    __syncthreads();
+    const int32_t y = (int32_t)blockIdx.x;
+    if (y >= pre[G]) return;                             // uniform over the workgroup
+    int glo = 0, ghi = G;                                // pre[glo] <= y < pre[ghi]
+    while (ghi - glo > 1) {
+        const int mid = (glo + ghi) >> 1;
+        if (pre[mid] <= y)
+            glo = mid;
+        else
+            ghi = mid;
+    }
+    const int g = glo;
+    const int64_t tt = y - pre[g];
+    int64_t lo, hi;
+    group_rows(off, g, total, &lo, &hi);
+    const int64_t c0 = (int64_t)blockIdx.y * kColTileC;
+    col_scales_to_lds<F>(col_amax + (int64_t)g * cols, c0, cols, margin, nullptr, s_lds, nan_lds);
+    const int64_t d0 = (int64_t)pre[g] * kColTileR + tt * kColTileR;
+    col_tile<F>(x, ldx, lo + tt * kColTileR, hi, true, c0, cols, s_lds, nan_lds, tile, qt, ldqt, d0, ldqt, vec_store);
 }
 
 // Any layout: one thread per column of a band of rows (reads coalesce across
@@ -448,11 +729,11 @@ __global__ __launch_bounds__(kBlock) void k_quant_col_scalar(const uint16_t* __r
                                                              uint8_t* __restrict__ qt, int64_t ldqt,
                                                              float* __restrict__ scale_inv,
                                                              const float* __restrict__ col_amax) {
-    const int64_t col = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t col = (int64_t)blockIdx.y * kBlock + threadIdx.x;
     if (col >= cols) return;
     const float s = scale_from_amax<F>(col_amax[col], margin);
-    if (blockIdx.y == 0) scale_inv[col] = 1.0f / s;
-    const int64_t r0 = (int64_t)blockIdx.y * kColRows;
+    if (blockIdx.x == 0) scale_inv[col] = 1.0f / s;
+    const int64_t r0 = (int64_t)blockIdx.x * kColRows;
     const int64_t r1 = r0 + kColRows < rows ? r0 + kColRows : rows;
     for (int64_t r = r0; r < r1; ++r) qt[col * ldqt + r] = (uint8_t)encode1<F>(bf16_lo(x[r * ldx + col]) * s);
 }
@@ -462,23 +743,29 @@ __global__ __launch_bounds__(kBlock) void k_quant_col_scalar(const uint16_t* __r
 // One wavefront per tensor. The effective amax combines the value being
 // recorded with the other L-1 ring slots (the slot at head is the one being
 // overwritten), so no lane reads a slot another lane is writing.
+__device__ __forceinline__ int ring_head(const int32_t* head, int L) {
+    return ((*head % L) + L) % L;            // a corrupt head cannot index outside the ring
+}
+
 template <int F>
-__global__ __launch_bounds__(kBlock) void k_delayed_update(float* __restrict__ cur_amax, float* __restrict__ history,
-                                                           const int32_t* __restrict__ head, int64_t n, int L,
-                                                           int algo, int margin, float* __restrict__ scale,
-                                                           float* __restrict__ scale_inv) {
+__device__ __forceinline__ void delayed_update_one(float* __restrict__ cur_amax, float* __restrict__ history, int h,
+                                                   int64_t i, int L, int algo, int margin, float* __restrict__ scale,
+                                                   float* __restrict__ scale_inv) {
     const int lane = threadIdx.x & 63;
-    const int64_t i = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (i >= n) return;
-    const int h = ((*head % L) + L) % L;     // a corrupt head cannot index outside the ring
     const float cur = cur_amax[i];
     float* hist = history + i * (int64_t)L;
     uint32_t mx = __float_as_uint(cur) & 0x7fffffffu;
     if (algo == 1) {
-        for (int t = lane; t < L; t += 64) {
-            if (t == h) continue;
-            const uint32_t b = __float_as_uint(hist[t]) & 0x7fffffffu;
-            mx = b > mx ? b : mx;
+        // eight independent loads per lane in flight per pass over 512 slots
+        for (int t0 = 0; t0 < L; t0 += 512) {
+            uint32_t b[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + u * 64 + lane;
+                b[u] = (t < L && t != h) ? (__float_as_uint(hist[t]) & 0x7fffffffu) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) mx = b[u] > mx ? b[u] : mx;
         }
         mx = wave_max_u32(mx);
     }
@@ -493,8 +780,36 @@ __global__ __launch_bounds__(kBlock) void k_delayed_update(float* __restrict__ c
     }
 }
 
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_delayed_update(float* __restrict__ cur_amax, float* __restrict__ history,
+                                                           const int32_t* __restrict__ head, int64_t n, int L,
+                                                           int algo, int margin, float* __restrict__ scale,
+                                                           float* __restrict__ scale_inv) {
+    const int64_t i = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (i >= n) return;
+    delayed_update_one<F>(cur_amax, history, ring_head(head, L), i, L, algo, margin, scale, scale_inv);
+}
+
 __global__ void k_advance_head(int32_t* head, int L) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) *head = (((*head % L) + L) % L + 1) % L;
+    if (threadIdx.x == 0 && blockIdx.x == 0) *head = (ring_head(head, L) + 1) % L;
+}
+
+// Few tensors: one workgroup updates all of them (wavefront w takes tensors
+// w, w + 4, ..) and then advances the head, after a barrier, so every
+// wavefront has read the old head first. One launch instead of two.
+constexpr int64_t kDelayedFusedMax = 64;
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_delayed_update_fused(float* __restrict__ cur_amax,
+                                                                 float* __restrict__ history, int32_t* head,
+                                                                 int64_t n, int L, int algo, int margin,
+                                                                 float* __restrict__ scale,
+                                                                 float* __restrict__ scale_inv) {
+    const int h = ring_head(head, L);
+    for (int64_t i = threadIdx.x >> 6; i < n; i += kWaves)
+        delayed_update_one<F>(cur_amax, history, h, i, L, algo, margin, scale, scale_inv);
+    __syncthreads();
+    if (threadIdx.x == 0) *head = (h + 1) % L;
 }
 
 // ------------------------------------------------------------------ helpers --
@@ -513,7 +828,9 @@ template <int F>
 hipError_t quant_row_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int margin, uint8_t* q,
                          int64_t ldq, float* scale_inv, float* amax_out, hipStream_t st) {
     const dim3 grid(grid_for_rows(rows)), block(kBlock);
-    const bool vec = is_aligned(x, 16) && is_aligned(q, 8) && ldx % 8 == 0 && ldq % 8 == 0 && cols % 8 == 0;
+    // (cols > 0: the register kernels read at least one chunk per row)
+    const bool vec =
+        cols > 0 && is_aligned(x, 16) && is_aligned(q, 8) && ldx % 8 == 0 && ldq % 8 == 0 && cols % 8 == 0;
     if (!vec) {
         hipLaunchKernelGGL((k_quant_row_2pass<F, false>), grid, block, 0, st, x, rows, cols, ldx, margin, q, ldq,
                            scale_inv, amax_out);
@@ -544,14 +861,55 @@ hipError_t quant_col_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
     const bool vec_in = is_aligned(x, 16) && ldx % 8 == 0 && cols % 8 == 0;
     if (vec_in) {
         const int vec_store = is_aligned(qt, 16) && ldqt % 16 == 0;
-        const dim3 grid((unsigned)((cols + kColTileC - 1) / kColTileC), (unsigned)((rows + kColTileR - 1) / kColTileR));
+        const dim3 grid((unsigned)((rows + kColTileR - 1) / kColTileR), (unsigned)((cols + kColTileC - 1) / kColTileC));
         hipLaunchKernelGGL((k_quant_col_tiled<F>), grid, dim3(kBlock), 0, st, x, rows, cols, ldx, margin, qt, ldqt,
                            scale_inv, col_amax, vec_store);
     } else {
-        const dim3 grid((unsigned)((cols + kBlock - 1) / kBlock), (unsigned)((rows + kColRows - 1) / kColRows));
+        const dim3 grid((unsigned)((rows + kColRows - 1) / kColRows), (unsigned)((cols + kBlock - 1) / kBlock));
         hipLaunchKernelGGL((k_quant_col_scalar<F>), grid, dim3(kBlock), 0, st, x, rows, cols, ldx, margin, qt, ldqt,
                            scale_inv, col_amax);
     }
+    return hipGetLastError();
+}
+
+// Chunks of 16 bytes per lane that hold a whole row of `cols` bf16 values in
+// registers (1, 2, 4, .., 32), or 0 if the row is longer than that.
+int reg_chunks(int64_t cols) {
+    const int64_t per_lane = (cols / 8 + 63) / 64;
+    for (int c = 1; c <= 32; c *= 2)
+        if (per_lane <= c) return c;
+    return 0;
+}
+
+// Workgroups for the grid-stride tensor kernels: enough wavefronts to keep
+// every CU's memory pipeline full, few enough that the per-workgroup atomic
+// stays rare.
+int tensor_grid(int64_t rows) {
+    const int64_t cap = (int64_t)current_device_props().cus * 2;
+    const int64_t need = (rows + kWaves - 1) / kWaves;
+    return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+template <int F, bool DELAYED>
+hipError_t quant_tensor_reg(int chunks, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int margin,
+                            const float* scale, uint8_t* q, int64_t ldq, float* scale_inv, float* amax,
+                            hipStream_t st) {
+    const dim3 grid(tensor_grid(rows)), block(kBlock);
+#define FP8_TENSOR_CASE(C)                                                                                          \
+    case C:                                                                                                         \
+        hipLaunchKernelGGL((k_quant_tensor_reg<F, C, DELAYED>), grid, block, 0, st, x, rows, cols, ldx, margin,     \
+                           scale, q, ldq, scale_inv, amax);                                                         \
+        break;
+    switch (chunks) {
+        FP8_TENSOR_CASE(1)
+        FP8_TENSOR_CASE(2)
+        FP8_TENSOR_CASE(4)
+        FP8_TENSOR_CASE(8)
+        FP8_TENSOR_CASE(16)
+        default:
+            FP8_TENSOR_CASE(32)
+    }
+#undef FP8_TENSOR_CASE
     return hipGetLastError();
 }
 
@@ -560,7 +918,14 @@ hipError_t quant_tensor_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64
                             const float* scale, uint8_t* q, int64_t ldq, float* scale_inv, float* amax,
                             hipStream_t st) {
     const bool vec = is_aligned(x, 16) && is_aligned(q, 8) && ldx % 8 == 0 && ldq % 8 == 0 && cols % 8 == 0;
+    const int chunks = vec && rows > 0 && cols > 0 ? reg_chunks(cols) : 0;
     const dim3 grid(strided_grid(rows)), block(kBlock);
+    if (chunks) {
+        if (scale) return quant_tensor_reg<F, true>(chunks, x, rows, cols, ldx, margin, scale, q, ldq, scale_inv, amax, st);
+        hipError_t e = launch_amax(x, rows, cols, ldx, 0, amax, st);
+        if (e != hipSuccess) return e;
+        return quant_tensor_reg<F, false>(chunks, x, rows, cols, ldx, margin, scale, q, ldq, scale_inv, amax, st);
+    }
     if (scale) {
         if (vec)
             hipLaunchKernelGGL((k_quant_tensor<F, true, true>), grid, block, 0, st, x, rows, cols, ldx, margin, scale,
@@ -584,6 +949,11 @@ hipError_t quant_tensor_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64
 template <int F>
 hipError_t delayed_fmt(float* cur_amax, float* history, int32_t* head, int64_t n, int L, int algo, int margin,
                        float* scale, float* scale_inv, hipStream_t st) {
+    if (n <= kDelayedFusedMax) {
+        hipLaunchKernelGGL((k_delayed_update_fused<F>), dim3(1), dim3(kBlock), 0, st, cur_amax, history, head, n, L,
+                           algo, margin, scale, scale_inv);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_delayed_update<F>), dim3(grid_for_rows(n)), dim3(kBlock), 0, st, cur_amax, history, head, n,
                        L, algo, margin, scale, scale_inv);
     hipError_t e = hipGetLastError();
@@ -609,6 +979,25 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
     const bool vec = is_aligned(x, 16) && ldx % 8 == 0 && cols % 8 == 0;
     if (axis == 1) {
         if (rows == 0) return hipSuccess;
+        const int chunks = vec && cols > 0 ? reg_chunks(cols) : 0;
+        if (chunks) {
+            const dim3 grid(grid_for_rows(rows)), block(kBlock);
+#define FP8_AMAX_ROWS_CASE(C)                                                                                    \
+    case C:                                                                                                      \
+        hipLaunchKernelGGL((k_amax_rows_reg<C>), grid, block, 0, st, x, rows, cols, ldx, out);                   \
+        break;
+            switch (chunks) {
+                FP8_AMAX_ROWS_CASE(1)
+                FP8_AMAX_ROWS_CASE(2)
+                FP8_AMAX_ROWS_CASE(4)
+                FP8_AMAX_ROWS_CASE(8)
+                FP8_AMAX_ROWS_CASE(16)
+                default:
+                    FP8_AMAX_ROWS_CASE(32)
+            }
+#undef FP8_AMAX_ROWS_CASE
+            return hipGetLastError();
+        }
         if (vec)
             hipLaunchKernelGGL((k_amax_rows<true>), dim3(grid_for_rows(rows)), dim3(kBlock), 0, st, x, rows, cols, ldx,
                                out);
@@ -621,6 +1010,25 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
     hipError_t e = launch_fill(out, nout, 0.0f, st);
     if (e != hipSuccess || rows == 0 || cols == 0) return e;
     if (axis == 0) {
+        const int chunks = vec ? reg_chunks(cols) : 0;     // (cols > 0 here)
+        if (chunks) {
+            const dim3 grid(tensor_grid(rows)), block(kBlock);
+#define FP8_AMAX_CASE(C)                                                                                         \
+    case C:                                                                                                      \
+        hipLaunchKernelGGL((k_amax_tensor_reg<C>), grid, block, 0, st, x, rows, cols, ldx, out);                 \
+        break;
+            switch (chunks) {
+                FP8_AMAX_CASE(1)
+                FP8_AMAX_CASE(2)
+                FP8_AMAX_CASE(4)
+                FP8_AMAX_CASE(8)
+                FP8_AMAX_CASE(16)
+                default:
+                    FP8_AMAX_CASE(32)
+            }
+#undef FP8_AMAX_CASE
+            return hipGetLastError();
+        }
         if (vec)
             hipLaunchKernelGGL((k_amax_tensor<true>), dim3(strided_grid(rows)), dim3(kBlock), 0, st, x, rows, cols, ldx,
                                out);
@@ -631,10 +1039,11 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
     }
     const unsigned gy = (unsigned)((rows + kColRows - 1) / kColRows);
     if (vec)
-        hipLaunchKernelGGL(k_amax_cols_vec, dim3((unsigned)((cols + 511) / 512), gy), dim3(kBlock), 0, st, x, rows,
-                           cols, ldx, out);
+        hipLaunchKernelGGL(k_amax_cols_vec, dim3((unsigned)((rows + kColAmaxRows - 1) / kColAmaxRows),
+                                                 (unsigned)((cols + 511) / 512)),
+                           dim3(kBlock), 0, st, x, rows, cols, ldx, out);
     else
-        hipLaunchKernelGGL(k_amax_cols_scalar, dim3((unsigned)((cols + kBlock - 1) / kBlock), gy), dim3(kBlock), 0, st,
+        hipLaunchKernelGGL(k_amax_cols_scalar, dim3(gy, (unsigned)((cols + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                            x, rows, cols, ldx, out);
     return hipGetLastError();
 }
@@ -680,6 +1089,47 @@ hipError_t launch_quant_tensor(const uint16_t* x, int64_t rows, int64_t cols, in
         default: return CALL(kE5M2Fnuz);
     }
 #undef CALL
+}
+
+hipError_t launch_grouped_quant_col(const uint16_t* x, int64_t total_m, int64_t cols, int64_t ldx, int fmt,
+                                    int margin, const int64_t* offsets, int g, uint8_t* qt, int64_t ldqt,
+                                    float* scale_inv, float* col_amax, int col_amax_ready, hipStream_t st) {
+    if (cols == 0) return hipSuccess;
+    hipError_t e = hipSuccess;
+    if (!col_amax_ready) {
+        e = launch_fill(col_amax, (int64_t)g * cols, 0.0f, st);
+        if (e != hipSuccess) return e;
+        if (total_m > 0) {
+            hipLaunchKernelGGL(k_grouped_amax_cols,
+                               dim3((unsigned)((total_m + kColAmaxRows - 1) / kColAmaxRows), (unsigned)((cols + 511) / 512)),
+                               dim3(kBlock), 0, st, x, total_m, cols, ldx, offsets, g, col_amax);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    const int64_t n = (int64_t)g * cols;
+    const unsigned sblocks = (unsigned)((n + kBlock - 1) / kBlock < 1024 ? (n + kBlock - 1) / kBlock : 1024);
+    // every group's padded tile count is at most m_g / 128 + 2
+    const dim3 grid((unsigned)((total_m + kColTileR - 1) / kColTileR + 2 * (int64_t)g),
+                    (unsigned)((cols + kColTileC - 1) / kColTileC));
+#define CALL(F)                                                                                                  \
+    do {                                                                                                         \
+        hipLaunchKernelGGL((k_scale_inv_from_amax<F>), dim3(sblocks), dim3(kBlock), 0, st, col_amax, n, margin,  \
+                           scale_inv);                                                                           \
+        e = hipGetLastError();                                                                                   \
+        if (e != hipSuccess) return e;                                                                           \
+        if (total_m > 0)                                                                                         \
+            hipLaunchKernelGGL((k_grouped_quant_col_tiled<F>), grid, dim3(kBlock), 0, st, x, total_m, cols, ldx, \
+                               margin, offsets, g, qt, ldqt, col_amax, 1);                                       \
+    } while (0)
+    switch (fmt) {
+        case kE4M3: CALL(kE4M3); break;
+        case kE5M2: CALL(kE5M2); break;
+        case kE4M3Fnuz: CALL(kE4M3Fnuz); break;
+        default: CALL(kE5M2Fnuz); break;
+    }
+#undef CALL
+    return hipGetLastError();
 }
 
 hipError_t launch_delayed_update(float* cur_amax, float* history, int32_t* head, int64_t n, int32_t L, int algo,

@@ -193,12 +193,68 @@ fp8_status_t fp8_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t lda, con
  * offsets[g] = total_m (the library cannot read it without a host sync, so
  * it is not checked; rows outside [0, total_m) are never touched). Empty groups
  * produce nothing. a: [total_m x k]; a_scale_inv [total_m]; b_scale_inv [g x n];
- * d [total_m x n]. Formats and alignment as fp8_gemm_scaled; g: 1..4096. */
+ * d [total_m x n]. b_group_stride >= 0, a multiple of 16; the groups' weights may
+ * interleave (e.g. b_group_stride = k with ldb = g * k: the experts' columns of
+ * one grouped transposed matrix, see below). Formats and alignment as
+ * fp8_gemm_scaled; g: 1..4096. */
 fp8_status_t fp8_grouped_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b,
                                      fp8_format_t fb, int64_t ldb, int64_t b_group_stride,
                                      const int64_t* group_offsets, int32_t g, int64_t total_m, int64_t n, int64_t k,
                                      const float* a_scale_inv, const float* b_scale_inv, void* d, fp8_out_t d_type,
                                      int64_t ldd, void* stream);
+
+/* ------------------------------------------------------------ MoE backward --
+ * The backward of an MoE layer ([Titan]: FP8 grouped GEMM for MoE, the colwise
+ * scales of the MoE layer, the MoE model's backward-pass speedup). For expert g
+ * with tokens offsets[g] .. offsets[g+1]-1 (m_g rows), forward y_g = x_g w_g^T:
+ *   dgrad dx_g = dy_g w_g: fp8_quantize_row(dy) times w_g quantized per column
+ *     over its rows (fp8_grouped_quantize_col on the stacked weights, groups of
+ *     n rows), with fp8_grouped_gemm_scaled;
+ *   wgrad dw_g = dy_g^T x_g: a contraction over the group's own tokens, so dy
+ *     and x are quantized per column over each group's tokens
+ *     (fp8_grouped_quantize_col) and multiplied by fp8_grouped_gemm_ragged_k.
+ * Grouped transposed layout (a reading: the pages name no layout): the codes
+ * of group g sit at columns P_g .. P_g + m_g - 1 of one matrix, where
+ * P_g = sum over h < g of roundup(m_h, FP8_GROUP_K_ALIGN), and columns
+ * P_g + m_g .. P_{g+1} - 1 hold zero codes. P_G <= total_m + g * (FP8_GROUP_K_ALIGN - 1). */
+#define FP8_GROUP_K_ALIGN 256
+
+/* Grouped colwise quantization. x: bf16 [total_m x cols] (ldx), rows sorted by
+ * group per group_offsets (DEVICE int64 [g+1], non-decreasing, offsets[0] = 0,
+ * offsets[g] = total_m; not checked, rows outside [0, total_m) are never
+ * touched). Per group g and column j: s_{g,j} from the amax of column j over
+ * the group's rows only, and
+ *   qt[j * ldqt + P_g + (i - offsets[g])] = cast(x[i * ldx + j] * s_{g,j}),
+ * zero codes in the group's padding. qt: [cols x ldqt]; columns >= ldqt are
+ * never written, so ldqt >= P_G is needed for the whole result
+ * (total_m + g * (FP8_GROUP_K_ALIGN - 1) always suffices; ldqt >= total_m is
+ * checked). col_amax [g x cols]: overwritten when col_amax_ready == 0, read as
+ * already holding the per-group column amax when 1. scale_inv_out [g x cols]
+ * (required). An empty group has amax 0 and scale 1. Requirements: x 16-byte
+ * aligned, ldx and cols multiples of 8; qt 16-byte aligned, ldqt % 16 == 0;
+ * g: 1..4096; margin: 0..32. */
+fp8_status_t fp8_grouped_quantize_col(const uint16_t* x, int64_t total_m, int64_t cols, int64_t ldx,
+                                      fp8_format_t fmt, int32_t margin, const int64_t* group_offsets, int32_t g,
+                                      uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* col_amax,
+                                      int32_t col_amax_ready, void* stream);
+
+/* Grouped GEMM over ragged contraction ranges (the MoE weight gradient):
+ *   d_g[i, j] = out( fp32acc( sum_{t < m_g} dec(a[i * lda + P_g + t]) * dec(b[j * ldb + P_g + t]) )
+ *                    * a_scale_inv[g * m + i] * b_scale_inv[g * n + j] )
+ * for g = 0..G-1, m_g and P_g from group_offsets as above (offsets[g] =
+ * total_m). a: codes [m x lda] and b: codes [n x ldb] in the grouped
+ * transposed layout, whose zero padding lets the contraction run over
+ * roundup(m_g, FP8_GROUP_K_ALIGN) columns (the padding must hold zero codes,
+ * as fp8_grouped_quantize_col writes it). d_g = d + g * d_group_stride
+ * (elements), [m x n] with row stride ldd; d_group_stride >= m * ldd. An
+ * empty group writes 0 * sa * sb. Columns at or past min(lda, ldb) are never
+ * read (lda, ldb >= P_G is needed for the whole result; >= total_m is
+ * checked). Formats and alignment as fp8_gemm_scaled; g: 1..4096. */
+fp8_status_t fp8_grouped_gemm_ragged_k(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b,
+                                       fp8_format_t fb, int64_t ldb, const int64_t* group_offsets, int32_t g,
+                                       int64_t total_m, int64_t m, int64_t n, const float* a_scale_inv,
+                                       const float* b_scale_inv, void* d, fp8_out_t d_type, int64_t ldd,
+                                       int64_t d_group_stride, void* stream);
 
 #ifdef __cplusplus
 }

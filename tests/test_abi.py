@@ -97,10 +97,67 @@ def test_grouped_gemm_rejects_bad_arguments(fp8):
     bad[7] = None                   # no offsets
     assert _call(fp8, g, *bad)[0] == 1
     bad = list(ok_args)
-    bad[6] = 8                      # group stride smaller than one weight
+    bad[6] = -16                    # negative group stride (smaller ones may interleave, by design)
     assert _call(fp8, g, *bad)[0] == 1
     bad = list(ok_args)
+    bad[6] = 8                      # group stride off the 16-byte grid
+    assert _call(fp8, g, *bad)[0] == 2
+    bad = list(ok_args)
     bad[7] = ctypes.c_void_p(0x10004)
+    assert _call(fp8, g, *bad)[0] == 2
+
+
+def test_grouped_quantize_col_rejects_bad_arguments(fp8):
+    g = "fp8_grouped_quantize_col"
+    # x [64 x 32] bf16, 4 groups, qt [32 x 1088]
+    ok_args = [FAKE, 64, 32, 32, 0, 0, FAKE, 4, FAKE, 1088, FAKE, FAKE, 0, None]
+    bad = list(ok_args)
+    bad[7] = 0                      # no groups
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[7] = 5000                   # too many groups
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[6] = None                   # no offsets
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[9] = 48                     # ldqt < total_m
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[9] = 1096                   # ldqt off the 16-byte grid
+    assert _call(fp8, g, *bad)[0] == 2
+    bad = list(ok_args)
+    bad[2], bad[3] = 36, 36         # cols not a multiple of 8
+    assert _call(fp8, g, *bad)[0] == 2
+    bad = list(ok_args)
+    bad[10] = None                  # no scale output
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[12] = 2                     # col_amax_ready not 0 / 1
+    assert _call(fp8, g, *bad)[0] == 1
+
+
+def test_grouped_gemm_ragged_k_rejects_bad_arguments(fp8):
+    g = "fp8_grouped_gemm_ragged_k"
+    # a [64 x 1088], b [96 x 1088], 4 groups over 64 tokens, d [4 x 64 x 96]
+    ok_args = [FAKE, 1, 1088, FAKE, 0, 1088, FAKE, 4, 64, 64, 96, FAKE, FAKE, FAKE, 0, 96, 64 * 96, None]
+    bad = list(ok_args)
+    bad[1] = 2                      # fnuz operand
+    assert _call(fp8, g, *bad)[0] == 3
+    bad = list(ok_args)
+    bad[7] = 0                      # no groups
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[2] = 32                     # lda < total_m
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[16] = 64 * 96 - 1           # output groups overlap
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[6] = None                   # no offsets
+    assert _call(fp8, g, *bad)[0] == 1
+    bad = list(ok_args)
+    bad[0] = ctypes.c_void_p(0x10008)
     assert _call(fp8, g, *bad)[0] == 2
 
 

@@ -242,6 +242,52 @@ def test_quantize_tensor_current(fp8, orc, fmt, shape):
     assert_f32_bits_equal(am.cpu().numpy(), [oam], "amax")
 
 
+@pytest.mark.parametrize("shape", [(1, 8), (7, 1024), (64, 16384), (3, 24000), (4096, 1032)])
+def test_quantize_tensor_current_row_lengths(fp8, orc, shape):
+    """Every register-resident row length (1 .. 32 chunks of 8 per lane), rows
+    longer than that (strided fallback) and a tensor of many workgroups, whose
+    amax is combined across workgroups; the largest magnitude sits in the last row."""
+    xb = rand_bf16(*shape, seed=41)
+    xb[-1, shape[1] // 2] = workloads.bf16_bits(np.float32([-7e4]))[0]
+    x = dev_bf16(xb)
+    say("tensor current row lengths", shape)
+    q = torch.empty(shape, dtype=torch.uint8, device="cuda:0")
+    si = torch.empty(1, device="cuda:0")
+    am = torch.full((1,), 123.0, device="cuda:0")
+    fp8.fp8_quantize_tensor(x, 0, 0, None, q, si, am)
+    torch.cuda.synchronize()
+    oq, osi, oam = orc.quantize_tensor_current(xb, 0, 0)
+    assert_codes_equal(q.cpu().numpy(), oq, "codes")
+    assert_f32_bits_equal(si.cpu().numpy(), [osi], "scale_inv")
+    assert_f32_bits_equal(am.cpu().numpy(), [oam], "amax")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("shape", [(300, 4104), (2048, 512), (3, 24000), (37, 200)])
+def test_quantize_tensor_delayed_parity(fp8, orc, fmt, shape):
+    """Delayed (given-scale) cast of tensors with a NaN row and an Inf: codes,
+    scale_inv and the amax folded into the running value, twice in a row (the
+    second call folds into the first call's amax)."""
+    xb = rand_bf16(*shape, seed=43)
+    xb[1, 3] = 0x7FC1                                   # NaN (positive, payload)
+    xb[-1, 0] = 0xFF80                                  # -Inf
+    x = dev_bf16(xb)
+    scale = np.float32(0.75)
+    q = torch.empty(shape, dtype=torch.uint8, device="cuda:0")
+    si = torch.empty(1, device="cuda:0")
+    am = dev_f32([0.5])
+    prev = np.float32(0.5)
+    for call in range(2):
+        say("tensor delayed", NAMES[fmt], shape, "call", call)
+        fp8.fp8_quantize_tensor(x, fmt, 0, dev_f32([scale]), q, si, am)
+        torch.cuda.synchronize()
+        oq, osi, oam = orc.quantize_tensor_scaled(xb, fmt, scale, amax_in=prev)
+        prev = oam
+        assert_codes_equal(q.cpu().numpy(), oq, "codes")
+        assert_f32_bits_equal(si.cpu().numpy(), [osi], "scale_inv")
+        assert_f32_bits_equal(am.cpu().numpy(), [oam], "amax")
+
+
 def test_quantize_tensor_delayed_folds_amax(fp8, orc):
     xb = rand_bf16(64, 96, seed=29)
     x = dev_bf16(xb)
@@ -293,6 +339,17 @@ def test_delayed_update_wraps_at_1024(fp8, orc):
     amaxes[5] = [900.0, 1e-3, 0.0]
     say("delayed 1024 wrap")
     run_delayed(fp8, orc, amaxes, 3, 1024, 1, 0, 0)
+
+
+def test_delayed_update_more_tensors_than_one_workgroup(fp8, orc):
+    """Above 64 tensors the update runs one wavefront per tensor and a second
+    launch advances the head."""
+    rng = np.random.default_rng(4)
+    amaxes = np.exp2(rng.uniform(-6, 6, (12, 130))).astype(np.float32)
+    amaxes[3, 7] = 0.0
+    say("delayed 130 tensors")
+    run_delayed(fp8, orc, amaxes, 130, 8, 1, 0, 0)
+    run_delayed(fp8, orc, amaxes, 130, 8, 0, 1, 1)
 
 
 def test_delayed_update_many_tensors(fp8, orc):

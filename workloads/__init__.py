@@ -112,6 +112,19 @@ def c4(tokens=16384, experts=32, n=2048, k=7168, seed=0, forced_empty=3):
     return {"x": x, "w": w, "counts": counts, "offsets": offsets}
 
 
+def c4b(tokens=16384, experts=32, n=2048, k=7168, seed=0, forced_empty=3):
+    """Backward of c4's expert layer: c4's draws, then the output gradient
+    dY [tokens x n] ~ 1e-3 N(0,1) (same scale as c5's)."""
+    rng = np.random.default_rng(seed)
+    counts = zipf_counts(rng, tokens, experts, forced_empty=forced_empty)
+    offsets = np.zeros(experts + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    x = bf16_bits(_normal(rng, (tokens, k)))
+    w = bf16_bits(_normal(rng, (experts, n, k), 0.006))
+    dy = bf16_bits(_normal(rng, (tokens, n), 1e-3))
+    return {"x": x, "w": w, "dy": dy, "counts": counts, "offsets": offsets}
+
+
 def c5(m=8192, n=14336, k=4096, seed=0):
     """Backward of c2: X [m x k], W [n x k] as in c2, then dY [m x n]."""
     rng = np.random.default_rng(seed)
