@@ -333,6 +333,8 @@ fp8_status_t fp8_grouped_gemm_ragged_k(const uint8_t* a, fp8_format_t fa, int64_
     // (checked as k = total_m rounded down to 16, the operand width requirement)
     FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, m, n, total_m / 16 * 16, d, (int)d_type, ldd));
     if (lda < total_m || ldb < total_m) return fail(FP8_ERR_INVALID_ARG, "%s: lda, ldb must be >= total_m", fn);
+    if (lda >= (1 << 24) || ldb >= (1 << 24))
+        return fail(FP8_ERR_UNSUPPORTED, "%s: lda, ldb must be < 2^24 (256-row tiles use 32-bit offsets)", fn);
     if (m > 0 && n > 0 && (!a || !b)) return fail(FP8_ERR_INVALID_ARG, "%s: a or b is NULL", fn);
     if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0)
         return fail(FP8_ERR_ALIGNMENT, "%s: a, b must be 16-byte aligned with lda, ldb multiples of 16", fn);

@@ -279,15 +279,19 @@ __device__ __forceinline__ int big_slot(int row, int chunk) { return chunk ^ ((r
 // 16g .. 16g+15 with g = w*4 + i (1 KB: 16 bytes per lane, lane l at 16 l);
 // lane l fills row 16g + l/4, slot l%4, so it fetches the K chunk that belongs
 // in that slot. Rows past the last valid one are clamped to it (never stored).
+// 32-bit arithmetic: the large-tile kernels run only with ld < 2^24 (so that
+// 256 * ld fits in 32 bits).
 __device__ __forceinline__ void big_lane_offsets(uint32_t (&off)[4], int64_t ld, int64_t valid_rows) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const uint32_t ld32 = (uint32_t)ld;
+    const int last = (int)(valid_rows < 256 ? valid_rows : 256) - 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = (wave * 4 + i) * 16 + (lane >> 2);
         const int chunk = big_slot(row, lane & 3);      // the slot map is an involution
-        int64_t r = row < valid_rows ? row : valid_rows - 1;
-        off[i] = (uint32_t)(r * ld + chunk * 16);
+        const uint32_t r = (uint32_t)(row < last ? row : last);
+        off[i] = r * ld32 + (uint32_t)(chunk * 16);
     }
 }
 
@@ -769,7 +773,7 @@ hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t l
     const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     if (tiles == 0) return hipSuccess;
     const int64_t big_tiles = ((m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
-    if (k > 0 && k % (4 * big::BK) == 0 && big_tiles >= 128) {
+    if (k > 0 && k % (4 * big::BK) == 0 && big_tiles >= 128 && lda < (1 << 24) && ldb < (1 << 24)) {
         const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
         hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT_F32>), dim3((unsigned)big_tiles), dim3(256), 0, st, a, lda, b, ldb,
                            m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out);
@@ -787,7 +791,8 @@ hipError_t grouped_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_
     const int64_t tiles = ((total_m + BM - 1) / BM + g) * ((n + BN - 1) / BN);
     if (total_m == 0 || n == 0) return hipSuccess;
     const int64_t big_est = ((total_m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
-    if (k > 0 && k % (4 * big::BK) == 0 && big_est >= 128 && g <= kMaxGroupsBig) {
+    if (k > 0 && k % (4 * big::BK) == 0 && big_est >= 128 && g <= kMaxGroupsBig && lda < (1 << 24) &&
+        ldb < (1 << 24)) {
         const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
         const int64_t grid = ((total_m + big::BM - 1) / big::BM + g) * ((n + big::BN - 1) / big::BN);
         hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32>), dim3((unsigned)grid), dim3(256), 0, st, a, lda, b,

@@ -249,7 +249,8 @@ fp8_status_t fp8_grouped_quantize_col(const uint16_t* x, int64_t total_m, int64_
  * (elements), [m x n] with row stride ldd; d_group_stride >= m * ldd. An
  * empty group writes 0 * sa * sb. Columns at or past min(lda, ldb) are never
  * read (lda, ldb >= P_G is needed for the whole result; >= total_m is
- * checked). Formats and alignment as fp8_gemm_scaled; g: 1..4096. */
+ * checked; lda, ldb < 2^24, else FP8_ERR_UNSUPPORTED). Formats and alignment
+ * as fp8_gemm_scaled; g: 1..4096. */
 fp8_status_t fp8_grouped_gemm_ragged_k(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b,
                                        fp8_format_t fb, int64_t ldb, const int64_t* group_offsets, int32_t g,
                                        int64_t total_m, int64_t m, int64_t n, const float* a_scale_inv,
