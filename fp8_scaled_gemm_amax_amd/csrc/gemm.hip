@@ -233,28 +233,17 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm(const uint8_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile kernel: 256 x 256 output tile per workgroup, one 128 x 128
+// Large-tile kernels: 256 x 256 output tile per workgroup, one 128 x 128
 // quadrant per wavefront (4 x 4 blocks of 32x32x64, 256 fp32 accumulators per
-// lane). K advances in steps of 64 through four LDS stages of 32 KB (A: 256
-// rows x 64 B, then B), filled by direct global->LDS loads issued three steps
-// ahead of use. Step t:
-//   wait until stage t+1's loads have landed; barrier
-//   issue the loads of stage t+4 into the buffer stage t used (its fragments
-//   were read during step t-1)
-//   read step t+1's B fragments
-//   4 x (4 MFMAs on A block mi, then read step t+1's A block mi into its registers)
-// The direct loads are issued from inline assembly: the compiler cannot see
-// that they write LDS, so it does not make later LDS reads wait for them; the
-// explicit vmcnt waits below do that at the right depth instead. Requires
-// k % 256 == 0 (whole four-step iterations); rows past m / n are clamped to
-// the last valid row on load and never stored.
+// lane in AGPRs). The K loop (k128_mainloop below) streams the operands through
+// LDS with direct global->LDS loads issued from inline assembly: the compiler
+// cannot see that they write LDS, so it adds no waits of its own; explicit
+// vmcnt waits at the right points do. Rows past m / n are clamped to the last
+// valid row on load and never stored. Requires k % 256 == 0.
 namespace big {
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kStages = 4;
-constexpr int kStage = (BM + BN) * BK;              // 32 KB: A tile then B tile
-constexpr int kLoadsPerStage = 8;                   // direct loads per thread per stage (4 A + 4 B)
+constexpr int BM = 256, BN = 256;
 constexpr int kEpiWave = 32 * 1024;                 // one wavefront's staged 128 x 128 bf16 block
-constexpr int kMain = 4 * kEpiWave > kStages * kStage ? 4 * kEpiWave : kStages * kStage;
+constexpr int kMain = 4 * kEpiWave;                 // 128 KB: two K stages, or the staged output
 constexpr int kScaleOff = kMain;                    // 256 row scales, then 256 column scales (fp32)
 constexpr int kSmem = kMain + 2 * 256 * 4;
 }  // namespace big
@@ -265,34 +254,6 @@ template <int N, int L = 15>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64 && L >= 0 && L < 16, "counter range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | (L << 8));
-}
-
-// LDS layout of a stage: 64-byte rows of four 16-byte K chunks; chunk c of row r
-// sits in slot c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1). A fragment read touches one
-// chunk of each of 16 consecutive rows per 16 lanes; with this map those land
-// in 16 distinct 16-byte bank groups (and 8 consecutive rows in 8 distinct
-// groups of a 128-byte bank window).
-__device__ __forceinline__ int big_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 3) ^ ((row >> 3) & 1); }
-
-// Per-lane byte offsets of this thread's four A (or B) rows within a tile,
-// relative to the tile's first row: wavefront w, load i fills LDS rows
-// 16g .. 16g+15 with g = w*4 + i (1 KB: 16 bytes per lane, lane l at 16 l);
-// lane l fills row 16g + l/4, slot l%4, so it fetches the K chunk that belongs
-// in that slot. Rows past the last valid one are clamped to it (never stored).
-// 32-bit arithmetic: the large-tile kernels run only with ld < 2^24 (so that
-// 256 * ld fits in 32 bits).
-__device__ __forceinline__ void big_lane_offsets(uint32_t (&off)[4], int64_t ld, int64_t valid_rows) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const uint32_t ld32 = (uint32_t)ld;
-    const int last = (int)(valid_rows < 256 ? valid_rows : 256) - 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (wave * 4 + i) * 16 + (lane >> 2);
-        const int chunk = big_slot(row, lane & 3);      // the slot map is an involution
-        const uint32_t r = (uint32_t)(row < last ? row : last);
-        off[i] = r * ld32 + (uint32_t)(chunk * 16);
-    }
 }
 
 // One direct global->LDS load of 16 bytes per lane: lane l's bytes land at
@@ -320,25 +281,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Issue the 8 loads of one stage (K slice at k0) into the buffer at `stage`.
-__device__ __forceinline__ void big_issue_stage(const uint8_t* stage, const uint8_t* a, const uint32_t (&aoff)[4],
-                                                const uint8_t* b, const uint32_t (&boff)[4], int64_t k0) {
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage)) + wave * 4096;
-    const uint8_t* ak = a + k0;
-    const uint8_t* bk = b + k0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(base + i * 1024, ak + aoff[i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(base + big::BM * big::BK + i * 1024, bk + boff[i]);
-}
-
-// Fragment of the 32x32x64 instruction: row `row` of a stage, lanes 0-31 hold
-// K bytes 0-31, lanes 32-63 K bytes 32-63 (two 16-byte halves).
-__device__ __forceinline__ u32x4 big_half(const uint8_t* tile, int row, int h) {
-    const int c = ((threadIdx.x & 63) >> 5) * 2 + h;
-    return *reinterpret_cast<const u32x4*>(tile + row * 64 + (big_slot(row, c) << 4));
-}
 __device__ __forceinline__ int big_row(int j) {   // j < 4: A block j; j >= 4: B block j-4 (row in its tile)
     const int w = threadIdx.x >> 6;
     return (j < 4 ? (w >> 1) * 128 + j * 32 : (w & 1) * 128 + (j - 4) * 32) + (threadIdx.x & 31);
@@ -368,6 +310,71 @@ __device__ __forceinline__ void big_tile_coords(int64_t bid, int64_t tiles_m, in
     *pn = (t % (gm * tiles_n)) / gsize;
 }
 
+// K64 main loop (kept for the grouped product at long K): K advances in steps
+// of 64 through four LDS stages of 32 KB (A: 256 rows x 64 B, then B), filled
+// by direct loads issued three steps ahead of use, so the loads have three
+// steps to land (HBM-streamed expert weights need that lookahead; the K128
+// loop has one). Step t:
+//   wait until stage t+1's loads have landed; barrier
+//   issue the loads of stage t+4 into the buffer stage t used (its fragments
+//   were read during step t-1)
+//   16 MFMAs on step t's fragments, each followed by one 16-byte fragment read
+//   for step t+1 and every other one by one direct load.
+namespace k64 {
+constexpr int BK = 64;
+constexpr int kStages = 4;
+constexpr int kStage = (big::BM + big::BN) * BK;    // 32 KB: A tile then B tile
+constexpr int kLoadsPerStage = 8;                   // direct loads per thread per stage (4 A + 4 B)
+static_assert(kStages * kStage == big::kMain, "four stages below the scale area");
+}  // namespace k64
+
+// LDS layout of a stage: 64-byte rows of four 16-byte K chunks; chunk c of row r
+// sits in slot c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1). A fragment read touches one
+// chunk of each of 16 consecutive rows per 16 lanes; with this map those land
+// in 16 distinct 16-byte bank groups (and 8 consecutive rows in 8 distinct
+// groups of a 128-byte bank window).
+__device__ __forceinline__ int big_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+// Per-lane byte offsets of this thread's four A (or B) rows within a tile,
+// relative to the tile's first row: wavefront w, load i fills LDS rows
+// 16g .. 16g+15 with g = w*4 + i (1 KB: 16 bytes per lane, lane l at 16 l);
+// lane l fills row 16g + l/4, slot l%4, so it fetches the K chunk that belongs
+// in that slot. Rows past the last valid one are clamped to it (never stored).
+// 32-bit arithmetic: the large-tile kernels run only with ld < 2^24 (so that
+// 256 * ld fits in 32 bits).
+__device__ __forceinline__ void big_lane_offsets(uint32_t (&off)[4], int64_t ld, int64_t valid_rows) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint32_t ld32 = (uint32_t)ld;
+    const int last = (int)(valid_rows < 256 ? valid_rows : 256) - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = (wave * 4 + i) * 16 + (lane >> 2);
+        const int chunk = big_slot(row, lane & 3);      // the slot map is an involution
+        const uint32_t r = (uint32_t)(row < last ? row : last);
+        off[i] = r * ld32 + (uint32_t)(chunk * 16);
+    }
+}
+
+// Issue the 8 loads of one stage (K slice at k0) into the buffer at `stage`.
+__device__ __forceinline__ void big_issue_stage(const uint8_t* stage, const uint8_t* a, const uint32_t (&aoff)[4],
+                                                const uint8_t* b, const uint32_t (&boff)[4], int64_t k0) {
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage)) + wave * 4096;
+    const uint8_t* ak = a + k0;
+    const uint8_t* bk = b + k0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(base + i * 1024, ak + aoff[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(base + big::BM * k64::BK + i * 1024, bk + boff[i]);
+}
+
+// Fragment of the 32x32x64 instruction: row `row` of a stage, lanes 0-31 hold
+// K bytes 0-31, lanes 32-63 K bytes 32-63 (two 16-byte halves).
+__device__ __forceinline__ u32x4 big_half(const uint8_t* tile, int row, int h) {
+    const int c = ((threadIdx.x & 63) >> 5) * 2 + h;
+    return *reinterpret_cast<const u32x4*>(tile + row * 64 + (big_slot(row, c) << 4));
+}
 // Step t with t % 4 = S (compile-time): 16 matrix instructions on fc (step
 // t's fragments: A blocks 0-3, B blocks 4-7, read during step t-1). After each
 // one the wavefront issues one 16-byte half of step t+1's fragments into fn
@@ -377,18 +384,18 @@ __device__ __forceinline__ void big_tile_coords(int64_t bid, int64_t tiles_m, in
 // last stage they re-read the last K slice into buffers that are not read
 // again. sched_barrier(0) pins this order.
 template <int FA, int FB, int S>
-__device__ __forceinline__ void big_step(uint8_t* smem, v16f (&acc)[4][4], const v8i (&fc)[8], v8i (&fn)[8],
+__device__ __forceinline__ void k64_step(uint8_t* smem, v16f (&acc)[4][4], const v8i (&fc)[8], v8i (&fn)[8],
                                          const uint8_t* a, const uint32_t (&aoff)[4], const uint8_t* b,
                                          const uint32_t (&boff)[4], int64_t k4) {
-    const uint8_t* nxt = smem + ((S + 1) & 3) * big::kStage;
-    const uint8_t* nxt_b = nxt + big::BM * big::BK;
+    const uint8_t* nxt = smem + ((S + 1) & 3) * k64::kStage;
+    const uint8_t* nxt_b = nxt + big::BM * k64::BK;
     // stage t+1 landed (t+2, t+3 may be in flight) and this wavefront's LDS
     // reads are done: after the barrier other wavefronts load into the buffer
     // this one read during step t-1
-    wait_vmcnt<2 * big::kLoadsPerStage, 0>();
+    wait_vmcnt<2 * k64::kLoadsPerStage, 0>();
     __syncthreads();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(smem + S * big::kStage)) + wave * 4096;
+    const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(smem + S * k64::kStage)) + wave * 4096;
     u32x4 half[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -403,7 +410,7 @@ __device__ __forceinline__ void big_step(uint8_t* smem, v16f (&acc)[4][4], const
             if (l < 4)
                 lds_dma16(dma_base + l * 1024, a + k4 + aoff[l]);
             else
-                lds_dma16(dma_base + big::BM * big::BK + (l - 4) * 1024, b + k4 + boff[l - 4]);
+                lds_dma16(dma_base + big::BM * k64::BK + (l - 4) * 1024, b + k4 + boff[l - 4]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -418,7 +425,7 @@ __device__ __forceinline__ void big_step(uint8_t* smem, v16f (&acc)[4][4], const
 // tile column t). They are loaded straight into the scale area of LDS with the
 // first loads of the tile, so no register holds them across the main loop.
 template <int FA, int FB>
-__device__ __forceinline__ void big_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
+__device__ __forceinline__ void k64_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
                                              const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k,
                                              const float* sa_lane, const float* sb_lane, v16f (&acc)[4][4]) {
 #pragma unroll
@@ -430,7 +437,7 @@ __device__ __forceinline__ void big_mainloop(uint8_t* smem, const uint8_t* a, in
     uint32_t aoff[4], boff[4];
     big_lane_offsets(aoff, lda, a_rows);
     big_lane_offsets(boff, ldb, b_rows);
-    constexpr int64_t BK = big::BK;
+    constexpr int64_t BK = k64::BK;
     const int64_t nk = k / BK;
     const int64_t last = (nk - 1) * BK;
     auto kof = [&](int64_t s) { return s < nk ? s * BK : last; };
@@ -443,26 +450,161 @@ __device__ __forceinline__ void big_mainloop(uint8_t* smem, const uint8_t* a, in
         lds_dma4(sbase + 1024, sb_lane);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) big_issue_stage(smem + s * big::kStage, a, aoff, b, boff, kof(s));
-    wait_vmcnt<3 * big::kLoadsPerStage>();
+    for (int s = 0; s < 4; ++s) big_issue_stage(smem + s * k64::kStage, a, aoff, b, boff, kof(s));
+    wait_vmcnt<3 * k64::kLoadsPerStage>();
     __syncthreads();
     v8i f0[8], f1[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const uint8_t* t0 = j < 4 ? smem : smem + big::BM * big::BK;
+        const uint8_t* t0 = j < 4 ? smem : smem + big::BM * k64::BK;
         f0[j] = big_join(big_half(t0, big_row(j), 0), big_half(t0, big_row(j), 1));
     }
     // four steps per iteration: the stage index (t % 4) and the fragment set
     // (t % 2) stay compile-time
     for (int64_t t = 0; t < nk; t += 4) {
-        big_step<FA, FB, 0>(smem, acc, f0, f1, a, aoff, b, boff, kof(t + 4));
-        big_step<FA, FB, 1>(smem, acc, f1, f0, a, aoff, b, boff, kof(t + 5));
-        big_step<FA, FB, 2>(smem, acc, f0, f1, a, aoff, b, boff, kof(t + 6));
-        big_step<FA, FB, 3>(smem, acc, f1, f0, a, aoff, b, boff, kof(t + 7));
+        k64_step<FA, FB, 0>(smem, acc, f0, f1, a, aoff, b, boff, kof(t + 4));
+        k64_step<FA, FB, 1>(smem, acc, f1, f0, a, aoff, b, boff, kof(t + 5));
+        k64_step<FA, FB, 2>(smem, acc, f0, f1, a, aoff, b, boff, kof(t + 6));
+        k64_step<FA, FB, 3>(smem, acc, f1, f0, a, aoff, b, boff, kof(t + 7));
     }
     // (k % 256 == 0: whole iterations only; a remainder's join costs
     // accumulator spills at the epilogue)
     wait_vmcnt<0>();                                     // no load may still land in LDS after this
+}
+
+// ---------------------------------------------------------------------------
+// K128 main loop: the same 256 x 256 tile and MFMA blocking, but K advances 128
+// bytes per step through two 64 KB LDS stages (A: 256 rows x 128 B, then B).
+// Each direct load brings whole 128-byte row segments (8 lanes per row), so
+// the L1 sends full-line requests to L2: on gfx950 the load path's throughput
+// goes with the number of requests (64-byte row segments cost ~13% of the
+// GEMM's time at these shapes). With two stages the loads of step p+1 are
+// issued during the first half of step p and waited for at the start of step
+// p+1; step p's first-half fragments are read at its start (the barrier orders
+// them after the stage has landed), its second-half fragments during its first
+// 16 MFMAs. 128-byte rows: chunk c of row r sits in slot c ^ ((r >> 1) & 7),
+// so 16 consecutive rows reading one chunk hit 16 distinct 16-byte bank groups.
+namespace k128 {
+constexpr int BK = 128;
+constexpr int kOpBytes = 256 * BK;                   // one operand of a stage: 32 KB
+constexpr int kStage = 2 * kOpBytes;                 // 64 KB
+static_assert(2 * kStage == big::kScaleOff, "two stages below the scale area");
+}  // namespace k128
+
+__device__ __forceinline__ int k128_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// Per-lane byte offsets of this thread's 8 loads of one operand: load i of
+// wavefront w fills rows w*64 + 8i .. w*64 + 8i + 7 (1 KB, 16 bytes per lane):
+// lane l takes row + l / 8, slot l % 8, i.e. the chunk stored in that slot.
+// 32-bit arithmetic (ld < 2^24); rows past the last valid one are clamped.
+__device__ __forceinline__ void k128_lane_offsets(uint32_t (&off)[8], int64_t ld, int64_t valid_rows) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint32_t ld32 = (uint32_t)ld;
+    const int last = (int)(valid_rows < 256 ? valid_rows : 256) - 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = wave * 64 + i * 8 + (lane >> 3);
+        const int chunk = k128_slot(row, lane & 7);     // the slot map is an involution
+        const uint32_t r = (uint32_t)(row < last ? row : last);
+        off[i] = r * ld32 + (uint32_t)(chunk * 16);
+    }
+}
+
+// Fragment half of the 32x32x64 instruction for K half h (bytes 64h ..
+// 64h + 63 of the 128-byte row): lanes 0-31 take its bytes 0-31, lanes 32-63
+// bytes 32-63, in two 16-byte halves hh.
+__device__ __forceinline__ u32x4 k128_half(const uint8_t* tile, int row, int h, int hh) {
+    const int c = h * 4 + ((threadIdx.x & 63) >> 5) * 2 + hh;
+    return *reinterpret_cast<const u32x4*>(tile + row * 128 + (k128_slot(row, c) << 4));
+}
+
+// Fragment order of a step: A0, B0, B1, B2, B3, A1, A2, A3 (the order the MFMA
+// sweep (mi, ni) = (0,0), (0,1), .. first needs them). j < 4: A block j, else B.
+__device__ __forceinline__ int k128_frag(int f) { return f == 0 ? 0 : (f <= 4 ? 4 + (f - 1) : f - 4); }
+
+// Step p with stage CUR = p % 2 (compile-time). LOADS: the 16 loads of step
+// p+1 (K offset knext) go to the other stage during this step's first 16 MFMAs.
+template <int FA, int FB, int CUR, bool LOADS>
+__device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], const uint8_t* a,
+                                          const uint32_t (&aoff)[8], const uint8_t* b, const uint32_t (&boff)[8],
+                                          int64_t knext) {
+    wait_vmcnt<0, 0>();                                  // this stage has landed; this wavefront's reads are done
+    __syncthreads();                                     // (the other stage is now free for step p+1's loads)
+    const uint8_t* ta = smem + CUR * k128::kStage;
+    const uint8_t* tb = ta + k128::kOpBytes;
+    u32x4 h0[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int j = k128_frag(i >> 1);
+        h0[i] = k128_half(j < 4 ? ta : tb, big_row(j), 0, i & 1);
+    }
+    v8i f0[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) f0[k128_frag(f)] = big_join(h0[2 * f], h0[2 * f + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(smem + (CUR ^ 1) * k128::kStage)) + wave * 8192;
+    u32x4 h1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int mi = i >> 2, ni = i & 3;
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0[mi], f0[4 + ni], acc[mi][ni], MfmaFmt<FA>::v,
+                                                                      MfmaFmt<FB>::v, 0, 0, 0, 0);
+        const int j = k128_frag(i >> 1);
+        h1[i] = k128_half(j < 4 ? ta : tb, big_row(j), 1, i & 1);
+        if (LOADS) {
+            if (i < 8)
+                lds_dma16(dma_base + i * 1024, a + knext + aoff[i]);
+            else
+                lds_dma16(dma_base + k128::kOpBytes + (i - 8) * 1024, b + knext + boff[i - 8]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    v8i f1[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) f1[k128_frag(f)] = big_join(h1[2 * f], h1[2 * f + 1]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int mi = i >> 2, ni = i & 3;
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1[mi], f1[4 + ni], acc[mi][ni], MfmaFmt<FA>::v,
+                                                                      MfmaFmt<FB>::v, 0, 0, 0, 0);
+    }
+}
+
+// The K loop of the large-tile kernels; k % 256 == 0, k > 0.
+template <int FA, int FB>
+__device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
+                                              const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k,
+                                              const float* sa_lane, const float* sb_lane, v16f (&acc)[4][4]) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+    uint32_t aoff[8], boff[8];
+    k128_lane_offsets(aoff, lda, a_rows);
+    k128_lane_offsets(boff, ldb, b_rows);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    {
+        const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kScaleOff)) + wave * 256;
+        lds_dma4(sbase, sa_lane);
+        lds_dma4(sbase + 1024, sb_lane);
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem)) + wave * 8192;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma16(base + i * 1024, a + aoff[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma16(base + k128::kOpBytes + i * 1024, b + boff[i]);
+    }
+    const int64_t nk = k / k128::BK;                     // even, >= 2
+    for (int64_t p = 0; p + 2 < nk; p += 2) {
+        k128_step<FA, FB, 0, true>(smem, acc, a, aoff, b, boff, (p + 1) * k128::BK);
+        k128_step<FA, FB, 1, true>(smem, acc, a, aoff, b, boff, (p + 2) * k128::BK);
+    }
+    k128_step<FA, FB, 0, true>(smem, acc, a, aoff, b, boff, (nk - 1) * k128::BK);
+    k128_step<FA, FB, 1, false>(smem, acc, a, aoff, b, boff, 0);
+    wait_vmcnt<0>();                                     // (nothing is outstanding: the last step loads nothing)
 }
 
 // Staged bf16 block of the epilogue: group g of 4 rows, column c -> 8 bytes
@@ -482,8 +624,12 @@ template <bool OUT_F32>
 __device__ __forceinline__ void big_epilogue(uint8_t* smem, v16f (&acc)[4][4], void* __restrict__ d,
                                              int64_t ldd, int64_t row0, int64_t rows_total, int64_t col0,
                                              int64_t cols_total, int vec_out) {
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
+    // The thread index is made opaque here, so the epilogue's lane arithmetic
+    // is not hoisted above the main loop (where it would stay live and spill).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t wrow0 = row0 + wm * 128, wcol0 = col0 + wn * 128;
     const int64_t rows_valid = rows_total - wm * 128, cols_valid = cols_total - wn * 128;
@@ -594,8 +740,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
     const float* sa_lane = sa + (sa_vec ? (row0 + t < m ? row0 + t : m - 1) : 0);
     const float* sb_lane = sb + (sb_vec ? (col0 + t < n ? col0 + t : n - 1) : 0);
     v16f acc[4][4];
-    big_mainloop<FA, FB>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, sa_lane, sb_lane,
-                         acc);
+    k128_mainloop<FA, FB>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, sa_lane, sb_lane,
+                          acc);
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, m - row0, col0, n - col0, vec_out);
 }
 
@@ -612,9 +758,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
 // XCD covers neighbouring tiles of one group: shared b panels and a rows in
 // that XCD's L2) and find their group by binary search in the prefix sums.
 constexpr int kMaxGroupsBig = 4096;
-static_assert((kMaxGroupsBig + 1) * 8 <= big::kStages * big::kStage, "group prefix sums fit in the stage buffers");
+static_assert((kMaxGroupsBig + 1) * 8 <= big::kMain, "group prefix sums fit in the stage buffers");
 
-template <int FA, int FB, bool OUT_F32>
+template <int FA, int FB, bool OUT_F32, bool K64>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb, int64_t b_group_stride,
     const int64_t* __restrict__ offsets, int g, int64_t total_m, int64_t n, int64_t k, const float* __restrict__ sa,
@@ -689,8 +835,12 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
     const uint8_t* bg = b + (int64_t)grp * b_group_stride;
     v16f acc[4][4];
-    big_mainloop<FA, FB>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, sa_lane, sb_lane,
-                         acc);
+    if (K64)
+        k64_mainloop<FA, FB>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, sa_lane,
+                             sb_lane, acc);
+    else
+        k128_mainloop<FA, FB>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, sa_lane,
+                              sb_lane, acc);
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, hi - row0, col0, n - col0, vec_out);
 }
 
@@ -749,7 +899,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
     const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
     v16f acc[4][4];
     if (K > 0) {
-        big_mainloop<FA, FB>(smem, a + row0 * lda + P, lda, m - row0, b + col0 * ldb + P, ldb, n - col0, K, sa_lane,
+        k128_mainloop<FA, FB>(smem, a + row0 * lda + P, lda, m - row0, b + col0 * ldb + P, ldb, n - col0, K, sa_lane,
                              sb_lane, acc);
     } else {                                             // empty group: 0 * sa * sb
 #pragma unroll
@@ -773,7 +923,7 @@ hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t l
     const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     if (tiles == 0) return hipSuccess;
     const int64_t big_tiles = ((m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
-    if (k > 0 && k % (4 * big::BK) == 0 && big_tiles >= 128 && lda < (1 << 24) && ldb < (1 << 24)) {
+    if (k > 0 && k % 256 == 0 && big_tiles >= 128 && lda < (1 << 24) && ldb < (1 << 24)) {
         const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
         hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT_F32>), dim3((unsigned)big_tiles), dim3(256), 0, st, a, lda, b, ldb,
                            m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out);
@@ -791,12 +941,19 @@ hipError_t grouped_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_
     const int64_t tiles = ((total_m + BM - 1) / BM + g) * ((n + BN - 1) / BN);
     if (total_m == 0 || n == 0) return hipSuccess;
     const int64_t big_est = ((total_m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
-    if (k > 0 && k % (4 * big::BK) == 0 && big_est >= 128 && g <= kMaxGroupsBig && lda < (1 << 24) &&
+    if (k > 0 && k % 256 == 0 && big_est >= 128 && g <= kMaxGroupsBig && lda < (1 << 24) &&
         ldb < (1 << 24)) {
         const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
         const int64_t grid = ((total_m + big::BM - 1) / big::BM + g) * ((n + big::BN - 1) / big::BN);
-        hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32>), dim3((unsigned)grid), dim3(256), 0, st, a, lda, b,
-                           ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out);
+        // long K (each expert's weights streamed from HBM): the K64 loop's deeper
+        // lookahead wins (c4, k = 7168: 1495 vs 1392 TFLOP/s); short K: K128
+        // (k = 2048: 1327 vs 1211)
+        if (k >= 4096)
+            hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, true>), dim3((unsigned)grid), dim3(256), 0, st, a,
+                               lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out);
+        else
+            hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false>), dim3((unsigned)grid), dim3(256), 0, st,
+                               a, lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((k_grouped_gemm<FA, FB, OUT_F32>), dim3((unsigned)tiles), dim3(kThreads), 0, st, a, lda, b, ldb,

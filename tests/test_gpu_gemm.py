@@ -210,15 +210,18 @@ def many_groups(g=300, seed=11):
 GROUPED_LARGE = [([0, 1000, 1, 255, 257, 0, 2583], 2048, 512, 0, 0, False),
                  (many_groups(), 2048, 256, 1, 0, False),
                  ([4096], 2048, 256, 0, 1, True),
-                 ([3000, 0, 1100], 2200, 768, 1, 1, False)]
+                 ([3000, 0, 1100], 2200, 768, 1, 1, False),
+                 ([600, 0, 3500, 100], 2048, 4096, 0, 0, False)]
 
 
-@pytest.mark.parametrize("sizes,n,k,fa,fb,out_f32", GROUPED_LARGE, ids=["ragged", "g300", "one", "ragged_n"])
+@pytest.mark.parametrize("sizes,n,k,fa,fb,out_f32", GROUPED_LARGE,
+                         ids=["ragged", "g300", "one", "ragged_n", "long_k"])
 def test_grouped_gemm_parity_large_tiles(fp8, orc, sizes, n, k, fa, fb, out_f32):
     """Shapes that take the 256 x 256 grouped kernel (k % 256 == 0, at least 128
     tiles of 256 x 256 estimated from the total row count): empty groups, a
     one-row group, groups spanning several m-tiles, more groups than threads of
-    a workgroup (the per-group tile counts are summed in parallel), ragged n."""
+    a workgroup (the per-group tile counts are summed in parallel), ragged n,
+    and k >= 4096 (the 64-deep K loop; shorter k runs the 128-deep one)."""
     g = len(sizes)
     offsets = np.zeros(g + 1, np.int64)
     offsets[1:] = np.cumsum(sizes)
