@@ -113,10 +113,12 @@ __global__ __launch_bounds__(kBlock) void k_amax_rows_reg(const uint16_t* __rest
     if (lane == 0) out[row] = amax_from_bits16(mx);
 }
 
-// Column amax: a workgroup covers 512 columns (64 lanes x 8) of a band of
-// kColAmaxRows rows; wavefront w takes rows w, w + 4, .., sixteen 16-byte
-// loads per lane in flight at a time. Partial maxima meet in LDS and each
-// column is folded into out[] (cleared beforehand) by one atomic max per
+// Column amax: a workgroup covers 512 columns (64 lanes x 8) and strides over
+// bands of kColAmaxRows rows (band blockIdx.x, blockIdx.x + gridDim.x, ..; the
+// grid holds about two workgroups per CU in all, so every CU gets the same
+// share); wavefront w takes rows w, w + 4, .. of a band, sixteen 16-byte loads
+// per lane in flight at a time. Partial maxima meet in LDS once at the end and
+// each column is folded into out[] (cleared beforehand) by one atomic max per
 // workgroup.
 constexpr int kColRows = 256;       // row band of the scalar kernels
 constexpr int kColAmaxRows = 256;   // row band of the vector column-amax kernel
@@ -129,26 +131,27 @@ __global__ __launch_bounds__(kBlock) void k_amax_cols_vec(const uint16_t* __rest
     const int wave = threadIdx.x >> 6;
     const int64_t ch = (int64_t)blockIdx.y * 64 + lane;        // 8-column chunk index
     const int64_t nch = cols >> 3;
-    const int64_t r0 = (int64_t)blockIdx.x * kColAmaxRows;
-    const int64_t r1 = r0 + kColAmaxRows < rows ? r0 + kColAmaxRows : rows;
     uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
     if (ch < nch) {
         const uint16_t* base = x + ch * 8;
-        for (int64_t rb = r0 + wave; rb < r1; rb += kColAmaxUnroll * kWaves) {
-            uint4 v[kColAmaxUnroll];
+        for (int64_t r0 = (int64_t)blockIdx.x * kColAmaxRows; r0 < rows; r0 += (int64_t)gridDim.x * kColAmaxRows) {
+            const int64_t r1 = r0 + kColAmaxRows < rows ? r0 + kColAmaxRows : rows;
+            for (int64_t rb = r0 + wave; rb < r1; rb += kColAmaxUnroll * kWaves) {
+                uint4 v[kColAmaxUnroll];
 #pragma unroll
-            for (int u = 0; u < kColAmaxUnroll; ++u) {
-                const int64_t r = rb + u * kWaves;
-                // rows past the band re-read its last row (a max ignores duplicates); the
-                // loads stay unconditional, so all of them are in flight together
-                v[u] = *reinterpret_cast<const uint4*>(base + (r < r1 ? r : r1 - 1) * ldx);
-            }
+                for (int u = 0; u < kColAmaxUnroll; ++u) {
+                    const int64_t r = rb + u * kWaves;
+                    // rows past the band re-read its last row (a max ignores duplicates); the
+                    // loads stay unconditional, so all of them are in flight together
+                    v[u] = *reinterpret_cast<const uint4*>(base + (r < r1 ? r : r1 - 1) * ldx);
+                }
 #pragma unroll
-            for (int u = 0; u < kColAmaxUnroll; ++u) {
-                m0 = pk_absmax(m0, v[u].x);
-                m1 = pk_absmax(m1, v[u].y);
-                m2 = pk_absmax(m2, v[u].z);
-                m3 = pk_absmax(m3, v[u].w);
+                for (int u = 0; u < kColAmaxUnroll; ++u) {
+                    m0 = pk_absmax(m0, v[u].x);
+                    m1 = pk_absmax(m1, v[u].y);
+                    m2 = pk_absmax(m2, v[u].z);
+                    m3 = pk_absmax(m3, v[u].w);
+                }
             }
         }
     }
@@ -1038,13 +1041,17 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
         return hipGetLastError();
     }
     const unsigned gy = (unsigned)((rows + kColRows - 1) / kColRows);
-    if (vec)
-        hipLaunchKernelGGL(k_amax_cols_vec, dim3((unsigned)((rows + kColAmaxRows - 1) / kColAmaxRows),
-                                                 (unsigned)((cols + 511) / 512)),
-                           dim3(kBlock), 0, st, x, rows, cols, ldx, out);
-    else
+    if (vec) {
+        // about two workgroups per CU in all, each striding over row bands
+        const int64_t bands = (rows + kColAmaxRows - 1) / kColAmaxRows, chunks = (cols + 511) / 512;
+        int64_t workers = (int64_t)current_device_props().cus * 2 / chunks;
+        workers = workers < 1 ? 1 : (workers > bands ? bands : workers);
+        hipLaunchKernelGGL(k_amax_cols_vec, dim3((unsigned)workers, (unsigned)chunks), dim3(kBlock), 0, st, x, rows,
+                           cols, ldx, out);
+    } else {
         hipLaunchKernelGGL(k_amax_cols_scalar, dim3(gy, (unsigned)((cols + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                            x, rows, cols, ldx, out);
+    }
     return hipGetLastError();
 }
 
