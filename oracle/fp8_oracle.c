@@ -18,6 +18,9 @@
  *    "FP8 Training on AMD GPUs with TorchTitan and TorchAO" (rowwise FP8, the
  *    colwise-scales kernel) and "FP8 training for Flux models" (tensorwise/delayed).
  *  - The scaled FP8 GEMM, dense and grouped over MoE experts: the same two pages.
+ *  - MX (block-32, power-of-two scaled) quantization and product: the MXFP8
+ *    grouped GEMM the TorchTitan/TorchAO page names as next; the format is a
+ *    reading, stated at the MX block section below.
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes of the repository):
@@ -394,5 +397,79 @@ void orc_grouped_gemm_entries(const uint8_t* a, int fa, int64_t lda, const uint8
         double sa = a_scale[i], sb = b_scale[(int64_t)grp * n + j];
         y[e] = s * sa * sb;
         if (bound) bound[e] = fabs(sa * sb) * t;
+    }
+}
+
+/* --------------------------------------------------------------- MX blocks -- */
+/* MXFP8: the pages name an MXFP8 grouped GEMM for MI355X as the next step of
+ * the MoE work ("FP8 Training on AMD GPUs with TorchTitan and TorchAO",
+ * summary) without defining the block format. Reading used here, the plainest
+ * microscaling one: each row is cut into blocks of 32 consecutive elements
+ * along K; a block shares a power-of-two scale X = 2^e stored as the biased
+ * exponent e + 127 (E8M0, 0xFF = NaN) with e = floor(log2(amax)) - emax, emax
+ * the exponent of the element format's largest normal (8 for e4m3, 15 for
+ * e5m2), clamped to [-127, 127]; an all-zero block gets e = -127; a block with
+ * a NaN or Inf gets 0xFF and its elements are cast with scale 1. An element is
+ * the saturating RNE cast of x * 2^-e (exact in fp32): values of the top binade
+ * above fmax saturate. Dequantised value: dec(code) * X. OCP encodings only. */
+#define ORC_MX_BLOCK 32
+
+static int mx_emax(int fmt) { return fmt == ORC_E4M3 ? 8 : 15; }
+
+/* Biased scale exponent of a block whose amax (max |x|, NaN dominating) is a. */
+uint8_t orc_mx_scale(int fmt, float amax) {
+    if (!isfinite(amax)) return 0xFF;
+    if (!(amax > 0.0f)) return 0;
+    int e = ilogbf(amax) - mx_emax(fmt);                  /* floor(log2(amax)) - emax */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return (uint8_t)(e + 127);
+}
+
+double orc_mx_scale_value(uint8_t s) { return s == 0xFF ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* Rowwise MX quantization: x [rows x cols] (cols % 32 == 0) -> codes q
+ * [rows x cols] and scales [rows x cols/32] (row stride lds). */
+void orc_mx_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                         int64_t ldq, uint8_t* scale, int64_t lds) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b0 = 0; b0 < cols; b0 += ORC_MX_BLOCK) {
+            float amax = 0.0f;
+            for (int64_t c = b0; c < b0 + ORC_MX_BLOCK; ++c) amax = amax_combine(amax, bf16_value(x[r * ldx + c]));
+            uint8_t s = orc_mx_scale(fmt, amax);
+            scale[r * lds + b0 / ORC_MX_BLOCK] = s;
+            double mul = (s == 0xFF) ? 1.0 : ldexp(1.0, 127 - (int)s);
+            for (int64_t c = b0; c < b0 + ORC_MX_BLOCK; ++c)
+                q[r * ldq + c] = orc_encode(fmt, (float)((double)bf16_value(x[r * ldx + c]) * mul));
+        }
+    }
+}
+
+/* MX product Y = A * B^T in fp64: Y[i, j] = sum over blocks b of X_a[i, b] *
+ * X_b[j, b] * sum_{k in b} dec(A[i, k]) * dec(B[j, k]); bound (if not NULL)
+ * gets the same with |.| of every term. A [m x k] with scales sa [m x k/32]
+ * (row stride ldsa), B [n x k] with sb [n x k/32]. ad/bd: caller scratch of
+ * m*k and n*k doubles. */
+void orc_mx_gemm(const uint8_t* a, int fa, int64_t lda, const uint8_t* sa, int64_t ldsa, const uint8_t* b, int fb,
+                 int64_t ldb, const uint8_t* sb, int64_t ldsb, int64_t m, int64_t n, int64_t k, double* ad,
+                 double* bd, double* y, int64_t ldy, double* bound) {
+    decode_rows(a, m, k, lda, fa, ad);
+    decode_rows(b, n, k, ldb, fb, bd);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double s = 0.0, t = 0.0;
+            for (int64_t b0 = 0; b0 < k; b0 += ORC_MX_BLOCK) {
+                double x = orc_mx_scale_value(sa[i * ldsa + b0 / ORC_MX_BLOCK]) *
+                           orc_mx_scale_value(sb[j * ldsb + b0 / ORC_MX_BLOCK]);
+                double bt;
+                double bs = dot_row(ad + i * k + b0, bd + j * k + b0, ORC_MX_BLOCK, &bt);
+                s += x * bs;
+                t += fabs(x) * bt;
+            }
+            y[i * ldy + j] = s;
+            if (bound) bound[i * ldy + j] = t;
+        }
     }
 }

@@ -58,6 +58,10 @@ def _load():
         "orc_gemm_entries": (None, [P, I, I64, P, I, I64, I64, P, I, P, I, P, P, I64, P, P]),
         "orc_grouped_gemm_entries": (None, [P, I, I64, P, I, I64, I64, P, I, I64, I64, P, P,
                                             P, P, I64, P, P]),
+        "orc_mx_scale": (ctypes.c_uint8, [I, F]),
+        "orc_mx_scale_value": (ctypes.c_double, [ctypes.c_uint8]),
+        "orc_mx_quantize_row": (None, [P, I64, I64, I64, I, P, I64, P, I64]),
+        "orc_mx_gemm": (None, [P, I, I64, P, I64, P, I, I64, P, I64, I64, I64, I64, P, P, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -263,6 +267,64 @@ def grouped_gemm(a, fa, b, fb, offsets, a_scale, b_scale):
         lo, hi = int(offsets[gg]), int(offsets[gg + 1])
         if hi > lo:
             y[lo:hi], bound[lo:hi] = gemm(a[lo:hi], fa, b[gg], fb, a_scale[lo:hi], b_scale[gg])
+    return y, bound
+
+
+# ------------------------------------------------------------------ MX blocks --
+# MXFP8 (block-32 scales along K, E8M0 power-of-two): see the MX block section
+# of fp8_oracle.c for the reading of the format.
+MX_BLOCK = 32
+
+
+def mx_scale(fmt, amax):
+    """Biased E8M0 exponent of a block with the given amax (0xFF: NaN)."""
+    return int(_load().orc_mx_scale(fmt, float(amax)))
+
+
+def mx_scale_value(s):
+    return _load().orc_mx_scale_value(int(s))
+
+
+def mx_quantize_row(x_bf16, fmt):
+    """Rowwise MX quantization: returns (codes [rows x cols], scales uint8 [rows x cols/32])."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    assert cols % MX_BLOCK == 0
+    q = np.empty((rows, cols), np.uint8)
+    sc = np.empty((rows, cols // MX_BLOCK), np.uint8)
+    _load().orc_mx_quantize_row(_p(x), rows, cols, cols, fmt, _p(q), cols, _p(sc), cols // MX_BLOCK)
+    return q, sc
+
+
+def mx_gemm(a, fa, sa, b, fb, sb):
+    """Y = A B^T with per-block E8M0 scales, fp64: a [m x k], sa [m x k/32], b [n x k],
+    sb [n x k/32]. Returns (y, bound)."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    sa = _c(sa, np.uint8)
+    sb = _c(sb, np.uint8)
+    m, k = a.shape
+    n = b.shape[0]
+    ad = np.empty(max(m * k, 1), np.float64)
+    bd = np.empty(max(n * k, 1), np.float64)
+    y = np.empty((m, n), np.float64)
+    bound = np.empty((m, n), np.float64)
+    _load().orc_mx_gemm(_p(a), fa, k, _p(sa), k // MX_BLOCK, _p(b), fb, k, _p(sb), k // MX_BLOCK, m, n, k, _p(ad),
+                        _p(bd), _p(y), n, _p(bound))
+    return y, bound
+
+
+def mx_grouped_gemm(a, fa, sa, b, fb, sb, offsets):
+    """Grouped MX product: rows offsets[g] .. offsets[g+1] of a (scales sa) times
+    b[g]^T (scales sb[g]); returns (y [total_m x n], bound)."""
+    a = _c(a, np.uint8)
+    g, n, k = b.shape
+    y = np.full((a.shape[0], n), np.nan)
+    bound = np.full((a.shape[0], n), np.nan)
+    for gg in range(g):
+        lo, hi = int(offsets[gg]), int(offsets[gg + 1])
+        if hi > lo:
+            y[lo:hi], bound[lo:hi] = mx_gemm(a[lo:hi], fa, sa[lo:hi], b[gg], fb, sb[gg])
     return y, bound
 
 
