@@ -19,7 +19,9 @@ __all__ = [
     "AMAX_MOST_RECENT", "AMAX_MAX", "SCALE_TENSOR", "SCALE_VECTOR", "OUT_BF16", "OUT_F32",
     "Fp8Error", "LIB_PATH", "lib", "fp8_query_device", "fp8_status_string", "fp8_amax",
     "fp8_quantize_tensor", "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update",
-    "fp8_gemm_scaled", "fp8_grouped_gemm_scaled", "EXPORTED_SYMBOLS",
+    "fp8_gemm_scaled", "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
+    "grouped_layout_width", "GROUP_K_ALIGN", "MX_BLOCK", "fp8_mx_quantize_row", "fp8_gemm_mx",
+    "fp8_grouped_gemm_mx", "EXPORTED_SYMBOLS",
 ]
 
 E4M3, E5M2, E4M3_FNUZ, E5M2_FNUZ = 0, 1, 2, 3
@@ -32,9 +34,11 @@ EXPORTED_SYMBOLS = (
     "fp8_query_device", "fp8_status_string", "fp8_last_error", "fp8_amax", "fp8_quantize_tensor",
     "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update", "fp8_gemm_scaled",
     "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
+    "fp8_mx_quantize_row", "fp8_gemm_mx", "fp8_grouped_gemm_mx",
 )
 
 GROUP_K_ALIGN = 256     # FP8_GROUP_K_ALIGN of the C header
+MX_BLOCK = 32           # FP8_MX_BLOCK of the C header
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8amax.so")
 
@@ -68,6 +72,9 @@ def _load():
         "fp8_grouped_gemm_scaled": [P, I, I64, P, I, I64, I64, P, I32, I64, I64, I64, P, P, P, I, I64, P],
         "fp8_grouped_quantize_col": [P, I64, I64, I64, I, I32, P, I32, P, I64, P, P, I32, P],
         "fp8_grouped_gemm_ragged_k": [P, I, I64, P, I, I64, P, I32, I64, I64, I64, P, P, P, I, I64, I64, P],
+        "fp8_mx_quantize_row": [P, I64, I64, I64, I, P, I64, P, I64, P],
+        "fp8_gemm_mx": [P, I, I64, P, I64, P, I, I64, P, I64, I64, I64, I64, P, I, I64, P],
+        "fp8_grouped_gemm_mx": [P, I, I64, P, I64, P, I, I64, I64, P, I64, I64, P, I32, I64, I64, I64, P, I, I64, P],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -233,3 +240,49 @@ def fp8_grouped_gemm_ragged_k(a, fa, b, fb, group_offsets, total_m, a_scale_inv,
     _check(lib.fp8_grouped_gemm_ragged_k(_ptr(a), fa, lda, _ptr(b), fb, ldb, _ptr(group_offsets), g, total_m, m, n,
                                          _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(d), d_type, ldd, d.stride(0),
                                          _stream(a)))
+
+
+def fp8_mx_quantize_row(x, fmt, q, scale_e8m0):
+    """x bf16 [rows x cols] (cols % 32 == 0); q codes [rows x cols]; scale_e8m0
+    uint8 [rows x cols/32]."""
+    rows, cols, ldx = _bf16(x)
+    _, _, ldq = _mat(q, "q", 1)
+    _, _, lds = _mat(scale_e8m0, "scale_e8m0", 1)
+    _check(lib.fp8_mx_quantize_row(_ptr(x), rows, cols, ldx, fmt, _ptr(q), ldq, _ptr(scale_e8m0), lds, _stream(x)))
+
+
+def fp8_gemm_mx(a, fa, a_scale, b, fb, b_scale, d):
+    """d [m x n] = block-scaled (a [m x k] codes, a_scale uint8 [m x k/32]) times
+    (b [n x k] codes, b_scale uint8 [n x k/32])^T; d bf16 or float32."""
+    m, k, lda = _mat(a, "a", 1)
+    n, kb, ldb = _mat(b, "b", 1)
+    if kb != k:
+        raise ValueError(f"a has k = {k} but b has k = {kb}")
+    _, _, ldas = _mat(a_scale, "a_scale", 1)
+    _, _, ldbs = _mat(b_scale, "b_scale", 1)
+    _, _, ldd = _mat(d, "d")
+    d_type = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[d.dtype]
+    _check(lib.fp8_gemm_mx(_ptr(a), fa, lda, _ptr(a_scale), ldas, _ptr(b), fb, ldb, _ptr(b_scale), ldbs, m, n, k,
+                           _ptr(d), d_type, ldd, _stream(a)))
+
+
+def fp8_grouped_gemm_mx(a, fa, a_scale, b, fb, b_scale, group_offsets, d):
+    """a [total_m x k] codes sorted by group with a_scale uint8 [total_m x k/32];
+    b [g x n x k] codes with b_scale uint8 [g x n x k/32] (unit last strides);
+    group_offsets int64 [g+1] on the device; d [total_m x n]."""
+    total_m, k, lda = _mat(a, "a", 1)
+    _, _, ldas = _mat(a_scale, "a_scale", 1)
+    for t, name in ((b, "b"), (b_scale, "b_scale")):
+        if t.dim() != 3 or t.element_size() != 1 or (t.numel() > 0 and t.shape[2] > 1 and t.stride(2) != 1):
+            raise ValueError(f"{name} must be a [g x n x *] 1-byte tensor with unit last stride")
+    g, n, kb = b.shape
+    if kb != k or tuple(b_scale.shape[:2]) != (g, n):
+        raise ValueError(f"b {tuple(b.shape)} / b_scale {tuple(b_scale.shape)} do not match a's k = {k}")
+    _, _, ldd = _mat(d, "d")
+    d_type = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[d.dtype]
+    if group_offsets.dtype != torch.int64 or group_offsets.numel() != g + 1:
+        raise ValueError("group_offsets must be int64 with g + 1 entries")
+    _check(lib.fp8_grouped_gemm_mx(_ptr(a), fa, lda, _ptr(a_scale), ldas, _ptr(b), fb, max(b.stride(1), k),
+                                   b.stride(0), _ptr(b_scale), max(b_scale.stride(1), b_scale.shape[2]),
+                                   b_scale.stride(0), _ptr(group_offsets), g, total_m, n, k, _ptr(d), d_type, ldd,
+                                   _stream(a)))

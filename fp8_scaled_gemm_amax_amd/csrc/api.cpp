@@ -120,6 +120,22 @@ fp8_status_t check_gemm_operands(const char* fn, const uint8_t* a, int fa, int64
     return FP8_OK;
 }
 
+// Shared checks of the MX products: k % 256, the E8M0 scale matrices (one byte
+// per 32-element block, rows dword-aligned), and the 32-bit tile offsets.
+fp8_status_t check_mx(const char* fn, int64_t rows_a, int64_t rows_b, int64_t k, int64_t lda, int64_t ldb,
+                      const uint8_t* xa, int64_t ld_xa, const uint8_t* xb, int64_t ld_xb) {
+    if (k % 256 != 0) return fail(FP8_ERR_UNSUPPORTED, "%s: k = %lld is not a multiple of 256", fn, (long long)k);
+    FP8_TRY(check_matrix(fn, "a_scale", k > 0 ? xa : nullptr, rows_a, k / FP8_MX_BLOCK, ld_xa));
+    FP8_TRY(check_matrix(fn, "b_scale", k > 0 ? xb : nullptr, rows_b, k / FP8_MX_BLOCK, ld_xb));
+    if (k > 0 && rows_a > 0 && rows_b > 0 && (!xa || !xb)) return fail(FP8_ERR_INVALID_ARG, "%s: scale is NULL", fn);
+    if (k > 0 && (!aligned(xa, 4) || !aligned(xb, 4) || ld_xa % 4 != 0 || ld_xb % 4 != 0))
+        return fail(FP8_ERR_ALIGNMENT, "%s: scale matrices must be 4-byte aligned with leading dimensions multiples "
+                    "of 4", fn);
+    if (lda >= (1 << 24) || ldb >= (1 << 24))
+        return fail(FP8_ERR_UNSUPPORTED, "%s: lda, ldb must be < 2^24 (256-row tiles use 32-bit offsets)", fn);
+    return FP8_OK;
+}
+
 }  // namespace
 
 const DeviceProps& current_device_props() {
@@ -351,6 +367,64 @@ fp8_status_t fp8_grouped_gemm_ragged_k(const uint8_t* a, fp8_format_t fa, int64_
     return launched(launch_grouped_gemm_ragged_k(a, (int)fa, lda, b, (int)fb, ldb, group_offsets, g, total_m, m, n,
                                                  a_scale_inv, b_scale_inv, d, d_type == FP8_OUT_F32, ldd,
                                                  d_group_stride, (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_mx_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                                 uint8_t* q, int64_t ldq, uint8_t* scale_e8m0, int64_t ld_scale, void* stream) {
+    const char* fn = "fp8_mx_quantize_row";
+    FP8_TRY(check_common_quant(fn, x, rows, cols, ldx, (int)fmt, 0));
+    if (!ocp_fmt((int)fmt)) return fail(FP8_ERR_INVALID_ARG, "%s: MX elements are OCP e4m3 or e5m2 (format %d)", fn, (int)fmt);
+    if (cols % FP8_MX_BLOCK != 0) return fail(FP8_ERR_INVALID_ARG, "%s: cols = %lld is not a multiple of %d", fn,
+                                              (long long)cols, FP8_MX_BLOCK);
+    FP8_TRY(check_matrix(fn, "q", q, rows, cols, ldq));
+    FP8_TRY(check_matrix(fn, "scale_e8m0", scale_e8m0, rows, cols / FP8_MX_BLOCK, ld_scale));
+    if (!aligned(x, 16) || ldx % 8 != 0 || !aligned(q, 8) || ldq % 8 != 0)
+        return fail(FP8_ERR_ALIGNMENT, "%s: x must be 16-byte aligned with ldx a multiple of 8, q 8-byte aligned with "
+                    "ldq a multiple of 8", fn);
+    if (rows >= ((int64_t)1 << 26)) return fail(FP8_ERR_UNSUPPORTED, "%s: 2^26 rows or more", fn);
+    FP8_TRY(check_device());
+    return launched(launch_mx_quant_row(x, rows, cols, ldx, (int)fmt, q, ldq, scale_e8m0, ld_scale,
+                                        (hipStream_t)stream),
+                    fn);
+}
+
+
+fp8_status_t fp8_gemm_mx(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* a_scale, int64_t ld_as,
+                         const uint8_t* b, fp8_format_t fb, int64_t ldb, const uint8_t* b_scale, int64_t ld_bs,
+                         int64_t m, int64_t n, int64_t k, void* d, fp8_out_t d_type, int64_t ldd, void* stream) {
+    const char* fn = "fp8_gemm_mx";
+    FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, m, n, k, d, (int)d_type, ldd));
+    FP8_TRY(check_mx(fn, m, n, k, lda, ldb, a_scale, ld_as, b_scale, ld_bs));
+    if (((m + 255) / 256) * ((n + 255) / 256) >= ((int64_t)1 << 24))
+        return fail(FP8_ERR_UNSUPPORTED, "%s: 2^24 or more tiles of 256 x 256", fn);
+    FP8_TRY(check_device());
+    return launched(launch_gemm_mx(a, (int)fa, lda, a_scale, ld_as, b, (int)fb, ldb, b_scale, ld_bs, m, n, k, d,
+                                   d_type == FP8_OUT_F32, ldd, (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_grouped_gemm_mx(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* a_scale,
+                                 int64_t ld_as, const uint8_t* b, fp8_format_t fb, int64_t ldb, int64_t b_group_stride,
+                                 const uint8_t* b_scale, int64_t ld_bs, int64_t b_scale_group_stride,
+                                 const int64_t* group_offsets, int32_t g, int64_t total_m, int64_t n, int64_t k,
+                                 void* d, fp8_out_t d_type, int64_t ldd, void* stream) {
+    const char* fn = "fp8_grouped_gemm_mx";
+    FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, total_m, n, k, d, (int)d_type, ldd));
+    FP8_TRY(check_mx(fn, total_m, n, k, lda, ldb, a_scale, ld_as, b_scale, ld_bs));
+    if (g < 1 || g > 4096) return fail(FP8_ERR_INVALID_ARG, "%s: group count %d outside 1..4096", fn, g);
+    if (!group_offsets) return fail(FP8_ERR_INVALID_ARG, "%s: group_offsets is NULL", fn);
+    if (!aligned(group_offsets, 8)) return fail(FP8_ERR_ALIGNMENT, "%s: group_offsets must be 8-byte aligned", fn);
+    if (b_group_stride < 0 || b_scale_group_stride < 0)
+        return fail(FP8_ERR_INVALID_ARG, "%s: negative group stride", fn);
+    if (b_group_stride % 16 != 0 || b_scale_group_stride % 4 != 0)
+        return fail(FP8_ERR_ALIGNMENT, "%s: b_group_stride must be a multiple of 16, b_scale_group_stride of 4", fn);
+    if (((total_m + 255) / 256 + g) * ((n + 255) / 256) >= ((int64_t)1 << 24))
+        return fail(FP8_ERR_UNSUPPORTED, "%s: 2^24 or more tiles of 256 x 256", fn);
+    FP8_TRY(check_device());
+    return launched(launch_grouped_gemm_mx(a, (int)fa, lda, a_scale, ld_as, b, (int)fb, ldb, b_group_stride, b_scale,
+                                           ld_bs, b_scale_group_stride, group_offsets, g, total_m, n, k, d,
+                                           d_type == FP8_OUT_F32, ldd, (hipStream_t)stream),
                     fn);
 }
 

@@ -246,6 +246,11 @@ constexpr int kEpiWave = 32 * 1024;                 // one wavefront's staged 12
 constexpr int kMain = 4 * kEpiWave;                 // 128 KB: two K stages, or the staged output
 constexpr int kScaleOff = kMain;                    // 256 row scales, then 256 column scales (fp32)
 constexpr int kSmem = kMain + 2 * 256 * 4;
+// MX operands: per K step, each of the 256 A rows and 256 B rows brings one
+// dword of E8M0 block scales (its four 32-element blocks), in two stages
+constexpr int kMxStage = 2 * 256 * 4;
+constexpr int kMxOff = kSmem;
+constexpr int kSmemMx = kSmem + 2 * kMxStage;       // 134 KB
 }  // namespace big
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
@@ -512,10 +517,17 @@ __device__ __forceinline__ void k128_lane_offsets(uint32_t (&off)[8], int64_t ld
 }
 
 // Fragment half of the 32x32x64 instruction for K half h (bytes 64h ..
-// 64h + 63 of the 128-byte row): lanes 0-31 take its bytes 0-31, lanes 32-63
-// bytes 32-63, in two 16-byte halves hh.
+// 64h + 63 of the 128-byte row), in two 16-byte pieces hh. The instruction's
+// own K order: lane half s = lane / 32 holds K 16s .. 16s + 15 in its bytes
+// 0-15 and K 32 + 16s .. 32 + 16s + 15 in bytes 16-31, and with block scales
+// the scale of lane half s covers K 32s .. 32s + 31, i.e. bytes 0-15 of both
+// lane halves form the first 32-element block (measured on gfx950). That
+// order is taken with MX. Without block scales any order common to A and B
+// gives the same sums, and lane half s takes bytes 32s .. 32s + 31.
+template <bool MX>
 __device__ __forceinline__ u32x4 k128_half(const uint8_t* tile, int row, int h, int hh) {
-    const int c = h * 4 + ((threadIdx.x & 63) >> 5) * 2 + hh;
+    const int s = (threadIdx.x & 63) >> 5;
+    const int c = MX ? h * 4 + s + 2 * hh : h * 4 + s * 2 + hh;
     return *reinterpret_cast<const u32x4*>(tile + row * 128 + (k128_slot(row, c) << 4));
 }
 
@@ -523,21 +535,61 @@ __device__ __forceinline__ u32x4 k128_half(const uint8_t* tile, int row, int h, 
 // sweep (mi, ni) = (0,0), (0,1), .. first needs them). j < 4: A block j, else B.
 __device__ __forceinline__ int k128_frag(int f) { return f == 0 ? 0 : (f <= 4 ? 4 + (f - 1) : f - 4); }
 
+// MX block scales of a step in LDS: row r of the tile (A, then B at +1 KB) at
+// dword (r / 128) * 128 + (r % 32) * 4 + (r / 32) % 4, so the four rows
+// wm*128 + 32 mi + l (mi = 0..3) that lane l needs are one 16-byte read. The
+// thread that fills dword i (a wavefront's direct load fills 64 consecutive
+// dwords) loads row mx_row(i).
+__device__ __forceinline__ int mx_row(int i) { return (i >> 7) * 128 + (i & 3) * 32 + ((i & 127) >> 2); }
+
+// The four scale dwords of lane l's rows, shifted by the lane half s = l / 32:
+// lane half s supplies the scale of block s of each 64-deep half, so byte 0 is
+// then block s of the step's first half and byte 2 block s of its second.
+__device__ __forceinline__ u32x4 mx_scales(const uint8_t* stage, int half_sel) {
+    const int lane = threadIdx.x & 63;
+    const int w = (threadIdx.x >> 6);
+    const int base = half_sel == 0 ? (w >> 1) * 128 : 256 + (w & 1) * 128;
+    u32x4 v = *reinterpret_cast<const u32x4*>(stage + 4 * (base + (lane & 31) * 4));
+    const int sh = 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] >>= sh;
+    return v;
+}
+
+// MFMA of one 64-deep half: with MX the E8M0 scale bytes OPSEL of the lane's
+// A and B scale dwords, else unscaled.
+template <int FA, int FB, bool MX, int OPSEL>
+__device__ __forceinline__ v16f k128_mfma(const v8i& fa, const v8i& fb, const v16f& c, uint32_t xa, uint32_t xb) {
+    if constexpr (MX)
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, c, MfmaFmt<FA>::v, MfmaFmt<FB>::v, OPSEL,
+                                                               (int)xa, OPSEL, (int)xb);
+    else
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, c, MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 0, 0, 0);
+}
+
 // Step p with stage CUR = p % 2 (compile-time). LOADS: the 16 loads of step
-// p+1 (K offset knext) go to the other stage during this step's first 16 MFMAs.
-template <int FA, int FB, int CUR, bool LOADS>
+// p+1 (K offset knext) go to the other stage during this step's first 16 MFMAs
+// (with MX also the step's two scale dwords per thread, from the row
+// pointers xa / xb at byte knext / 32).
+template <int FA, int FB, int CUR, bool LOADS, bool MX>
 __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], const uint8_t* a,
                                           const uint32_t (&aoff)[8], const uint8_t* b, const uint32_t (&boff)[8],
-                                          int64_t knext) {
+                                          int64_t knext, const uint8_t* xa, const uint8_t* xb) {
     wait_vmcnt<0, 0>();                                  // this stage has landed; this wavefront's reads are done
     __syncthreads();                                     // (the other stage is now free for step p+1's loads)
     const uint8_t* ta = smem + CUR * k128::kStage;
     const uint8_t* tb = ta + k128::kOpBytes;
+    u32x4 sxa = {0u, 0u, 0u, 0u}, sxb = {0u, 0u, 0u, 0u};
+    if constexpr (MX) {
+        const uint8_t* xs = smem + big::kMxOff + CUR * big::kMxStage;
+        sxa = mx_scales(xs, 0);
+        sxb = mx_scales(xs, 1);
+    }
     u32x4 h0[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int j = k128_frag(i >> 1);
-        h0[i] = k128_half(j < 4 ? ta : tb, big_row(j), 0, i & 1);
+        h0[i] = k128_half<MX>(j < 4 ? ta : tb, big_row(j), 0, i & 1);
     }
     v8i f0[8];
 #pragma unroll
@@ -549,15 +601,22 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], cons
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0[mi], f0[4 + ni], acc[mi][ni], MfmaFmt<FA>::v,
-                                                                      MfmaFmt<FB>::v, 0, 0, 0, 0);
+        acc[mi][ni] = k128_mfma<FA, FB, MX, 0>(f0[mi], f0[4 + ni], acc[mi][ni], sxa[mi], sxb[ni]);
         const int j = k128_frag(i >> 1);
-        h1[i] = k128_half(j < 4 ? ta : tb, big_row(j), 1, i & 1);
+        h1[i] = k128_half<MX>(j < 4 ? ta : tb, big_row(j), 1, i & 1);
         if (LOADS) {
             if (i < 8)
                 lds_dma16(dma_base + i * 1024, a + knext + aoff[i]);
             else
                 lds_dma16(dma_base + k128::kOpBytes + (i - 8) * 1024, b + knext + boff[i - 8]);
+            if constexpr (MX) {
+                if (i == 3 || i == 11) {
+                    const uint32_t xbase = __builtin_amdgcn_readfirstlane(
+                                               lds_addr(smem + big::kMxOff + (CUR ^ 1) * big::kMxStage)) +
+                                           wave * 256 + (i == 3 ? 0 : 1024);
+                    lds_dma4(xbase, (i == 3 ? xa : xb) + knext / 32);
+                }
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -567,16 +626,20 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], cons
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1[mi], f1[4 + ni], acc[mi][ni], MfmaFmt<FA>::v,
-                                                                      MfmaFmt<FB>::v, 0, 0, 0, 0);
+        acc[mi][ni] = k128_mfma<FA, FB, MX, 2>(f1[mi], f1[4 + ni], acc[mi][ni], sxa[mi], sxb[ni]);
     }
 }
 
-// The K loop of the large-tile kernels; k % 256 == 0, k > 0.
-template <int FA, int FB>
+// The K loop of the large-tile kernels; k % 256 == 0 (k = 0: zero sums). The
+// epilogue's row and column scales go to the scale area: sa_lane / sb_lane
+// (thread t's row / column scale) or, with MX, 1 (the block scales are applied
+// inside the MFMAs, and xa / xb are thread t's scale row pointers, of A row
+// mx_row(t) and B row mx_row(t) of the tile).
+template <int FA, int FB, bool MX>
 __device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
                                               const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k,
-                                              const float* sa_lane, const float* sb_lane, v16f (&acc)[4][4]) {
+                                              const float* sa_lane, const float* sb_lane, const uint8_t* xa,
+                                              const uint8_t* xb, v16f (&acc)[4][4]) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -587,23 +650,35 @@ __device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, i
     k128_lane_offsets(aoff, lda, a_rows);
     k128_lane_offsets(boff, ldb, b_rows);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nk = k / k128::BK;
     {
-        const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kScaleOff)) + wave * 256;
-        lds_dma4(sbase, sa_lane);
-        lds_dma4(sbase + 1024, sb_lane);
+        if constexpr (MX) {
+            float* s = reinterpret_cast<float*>(smem + big::kScaleOff);
+            s[threadIdx.x] = 1.0f;
+            s[256 + threadIdx.x] = 1.0f;
+        } else {
+            const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kScaleOff)) + wave * 256;
+            lds_dma4(sbase, sa_lane);
+            lds_dma4(sbase + 1024, sb_lane);
+        }
+        if (MX && nk == 0) return;                       // (the epilogue's barrier orders the scale area)
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem)) + wave * 8192;
 #pragma unroll
         for (int i = 0; i < 8; ++i) lds_dma16(base + i * 1024, a + aoff[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) lds_dma16(base + k128::kOpBytes + i * 1024, b + boff[i]);
+        if constexpr (MX) {
+            const uint32_t xbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kMxOff)) + wave * 256;
+            lds_dma4(xbase, xa);
+            lds_dma4(xbase + 1024, xb);
+        }
     }
-    const int64_t nk = k / k128::BK;                     // even, >= 2
     for (int64_t p = 0; p + 2 < nk; p += 2) {
-        k128_step<FA, FB, 0, true>(smem, acc, a, aoff, b, boff, (p + 1) * k128::BK);
-        k128_step<FA, FB, 1, true>(smem, acc, a, aoff, b, boff, (p + 2) * k128::BK);
+        k128_step<FA, FB, 0, true, MX>(smem, acc, a, aoff, b, boff, (p + 1) * k128::BK, xa, xb);
+        k128_step<FA, FB, 1, true, MX>(smem, acc, a, aoff, b, boff, (p + 2) * k128::BK, xa, xb);
     }
-    k128_step<FA, FB, 0, true>(smem, acc, a, aoff, b, boff, (nk - 1) * k128::BK);
-    k128_step<FA, FB, 1, false>(smem, acc, a, aoff, b, boff, 0);
+    k128_step<FA, FB, 0, true, MX>(smem, acc, a, aoff, b, boff, (nk - 1) * k128::BK, xa, xb);
+    k128_step<FA, FB, 1, false, MX>(smem, acc, a, aoff, b, boff, 0, xa, xb);
     wait_vmcnt<0>();                                     // (nothing is outstanding: the last step loads nothing)
 }
 
@@ -740,8 +815,31 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
     const float* sa_lane = sa + (sa_vec ? (row0 + t < m ? row0 + t : m - 1) : 0);
     const float* sb_lane = sb + (sb_vec ? (col0 + t < n ? col0 + t : n - 1) : 0);
     v16f acc[4][4];
-    k128_mainloop<FA, FB>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, sa_lane, sb_lane,
-                          acc);
+    k128_mainloop<FA, FB, false>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, sa_lane,
+                                 sb_lane, nullptr, nullptr, acc);
+    big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, m - row0, col0, n - col0, vec_out);
+}
+
+// MX product: d = sum over 32-deep K blocks of the blocks' dot products times
+// 2^(xa - 127) * 2^(xb - 127), the E8M0 scales of row i's and column j's block
+// (xa row r at xa + r * ld_xa, one byte per block).
+template <int FA, int FB, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ a, int64_t lda,
+                                                    const uint8_t* __restrict__ xa, int64_t ld_xa,
+                                                    const uint8_t* __restrict__ b, int64_t ldb,
+                                                    const uint8_t* __restrict__ xb, int64_t ld_xb, int64_t m, int64_t n,
+                                                    int64_t k, void* __restrict__ d, int64_t ldd, int vec_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[big::kSmemMx];
+    const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
+    int64_t pm, pn;
+    big_tile_coords(blockIdx.x, tiles_m, tiles_n, &pm, &pn);
+    const int64_t row0 = pm * big::BM, col0 = pn * big::BN;
+    const int rt = mx_row(threadIdx.x);
+    const uint8_t* xa_lane = xa + (row0 + rt < m ? row0 + rt : m - 1) * ld_xa;
+    const uint8_t* xb_lane = xb + (col0 + rt < n ? col0 + rt : n - 1) * ld_xb;
+    v16f acc[4][4];
+    k128_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, nullptr,
+                                nullptr, xa_lane, xb_lane, acc);
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, m - row0, col0, n - col0, vec_out);
 }
 
@@ -760,12 +858,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
 constexpr int kMaxGroupsBig = 4096;
 static_assert((kMaxGroupsBig + 1) * 8 <= big::kMain, "group prefix sums fit in the stage buffers");
 
-template <int FA, int FB, bool OUT_F32, bool K64>
+// With MX the operands carry E8M0 block scales instead of sa / sb: xa (row r
+// of a at xa + r * ld_xa) and, for group e, xb + e * xb_group_stride.
+template <int FA, int FB, bool OUT_F32, bool K64, bool MX>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb, int64_t b_group_stride,
     const int64_t* __restrict__ offsets, int g, int64_t total_m, int64_t n, int64_t k, const float* __restrict__ sa,
-    const float* __restrict__ sb, void* __restrict__ d, int64_t ldd, int vec_out) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[big::kSmem];
+    const float* __restrict__ sb, void* __restrict__ d, int64_t ldd, int vec_out, const uint8_t* __restrict__ xa,
+    int64_t ld_xa, const uint8_t* __restrict__ xb, int64_t ld_xb, int64_t xb_group_stride) {
+    static_assert(!(MX && K64), "the MX block scales ride on the K128 loop");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? big::kSmemMx : big::kSmem];
     const int64_t tiles_n = (n + big::BN - 1) / big::BN;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
@@ -831,16 +933,24 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     const int64_t pm = first_m + (lt % (gm * tiles_n)) % gsize;
     const int64_t pn = (lt % (gm * tiles_n)) / gsize;
     const int64_t row0 = lo + pm * big::BM, col0 = pn * big::BN;
-    const float* sa_lane = sa + (row0 + t < hi ? row0 + t : hi - 1);
-    const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
     const uint8_t* bg = b + (int64_t)grp * b_group_stride;
     v16f acc[4][4];
-    if (K64)
-        k64_mainloop<FA, FB>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, sa_lane,
-                             sb_lane, acc);
-    else
-        k128_mainloop<FA, FB>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, sa_lane,
-                              sb_lane, acc);
+    if constexpr (MX) {
+        const int rt = mx_row(t);
+        const uint8_t* xa_lane = xa + (row0 + rt < hi ? row0 + rt : hi - 1) * ld_xa;
+        const uint8_t* xb_lane = xb + (int64_t)grp * xb_group_stride + (col0 + rt < n ? col0 + rt : n - 1) * ld_xb;
+        k128_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, nullptr,
+                                    nullptr, xa_lane, xb_lane, acc);
+    } else {
+        const float* sa_lane = sa + (row0 + t < hi ? row0 + t : hi - 1);
+        const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
+        if (K64)
+            k64_mainloop<FA, FB>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, sa_lane,
+                                 sb_lane, acc);
+        else
+            k128_mainloop<FA, FB, false>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
+                                         sa_lane, sb_lane, nullptr, nullptr, acc);
+    }
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, hi - row0, col0, n - col0, vec_out);
 }
 
@@ -899,8 +1009,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
     const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
     v16f acc[4][4];
     if (K > 0) {
-        k128_mainloop<FA, FB>(smem, a + row0 * lda + P, lda, m - row0, b + col0 * ldb + P, ldb, n - col0, K, sa_lane,
-                             sb_lane, acc);
+        k128_mainloop<FA, FB, false>(smem, a + row0 * lda + P, lda, m - row0, b + col0 * ldb + P, ldb, n - col0, K,
+                                     sa_lane, sb_lane, nullptr, nullptr, acc);
     } else {                                             // empty group: 0 * sa * sb
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
@@ -948,16 +1058,49 @@ hipError_t grouped_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_
         // long K (each expert's weights streamed from HBM): the K64 loop's deeper
         // lookahead wins (c4, k = 7168: 1495 vs 1392 TFLOP/s); short K: K128
         // (k = 2048: 1327 vs 1211)
+        const uint8_t* none = nullptr;
         if (k >= 4096)
-            hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, true>), dim3((unsigned)grid), dim3(256), 0, st, a,
-                               lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out);
+            hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, true, false>), dim3((unsigned)grid), dim3(256), 0,
+                               st, a, lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out, none,
+                               (int64_t)0, none, (int64_t)0, (int64_t)0);
         else
-            hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false>), dim3((unsigned)grid), dim3(256), 0, st,
-                               a, lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out);
+            hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false, false>), dim3((unsigned)grid), dim3(256), 0,
+                               st, a, lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out, none,
+                               (int64_t)0, none, (int64_t)0, (int64_t)0);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((k_grouped_gemm<FA, FB, OUT_F32>), dim3((unsigned)tiles), dim3(kThreads), 0, st, a, lda, b, ldb,
                        stride, offsets, g, total_m, n, k, sa, sb, d, ldd);
+    return hipGetLastError();
+}
+
+// The MX products always take the large-tile kernels (rows and columns past
+// the operands are clamped; k % 256 == 0 and lda, ldb < 2^24 are checked by
+// the caller).
+template <int FA, int FB, bool OUT_F32>
+hipError_t gemm_mx_typed(const uint8_t* a, int64_t lda, const uint8_t* xa, int64_t ld_xa, const uint8_t* b,
+                         int64_t ldb, const uint8_t* xb, int64_t ld_xb, int64_t m, int64_t n, int64_t k, void* d,
+                         int64_t ldd, hipStream_t st) {
+    const int64_t tiles = ((m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
+    if (tiles == 0) return hipSuccess;
+    const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
+    hipLaunchKernelGGL((k_gemm_mx<FA, FB, OUT_F32>), dim3((unsigned)tiles), dim3(256), 0, st, a, lda, xa, ld_xa, b,
+                       ldb, xb, ld_xb, m, n, k, d, ldd, vec_out);
+    return hipGetLastError();
+}
+
+template <int FA, int FB, bool OUT_F32>
+hipError_t grouped_mx_typed(const uint8_t* a, int64_t lda, const uint8_t* xa, int64_t ld_xa, const uint8_t* b,
+                            int64_t ldb, int64_t stride, const uint8_t* xb, int64_t ld_xb, int64_t xstride,
+                            const int64_t* offsets, int g, int64_t total_m, int64_t n, int64_t k, void* d, int64_t ldd,
+                            hipStream_t st) {
+    if (total_m == 0 || n == 0) return hipSuccess;
+    const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
+    const int64_t grid = ((total_m + big::BM - 1) / big::BM + g) * ((n + big::BN - 1) / big::BN);
+    const float* none = nullptr;
+    hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false, true>), dim3((unsigned)grid), dim3(256), 0, st, a,
+                       lda, b, ldb, stride, offsets, g, total_m, n, k, none, none, d, ldd, vec_out, xa, ld_xa, xb,
+                       ld_xb, xstride);
     return hipGetLastError();
 }
 
@@ -982,6 +1125,36 @@ hipError_t launch_grouped_gemm_ragged_k(const uint8_t* a, int fa, int64_t lda, c
                                         int64_t d_group_stride, hipStream_t st) {
 #define CALL(FA, FB, OF) \
     ragged_typed<FA, FB, OF>(a, lda, b, ldb, offsets, g, total_m, m, n, sa, sb, d, ldd, d_group_stride, st)
+#define BY_OUT(FA, FB) return out_f32 ? CALL(FA, FB, true) : CALL(FA, FB, false)
+    if (fa == kE4M3 && fb == kE4M3) BY_OUT(kE4M3, kE4M3);
+    if (fa == kE4M3 && fb == kE5M2) BY_OUT(kE4M3, kE5M2);
+    if (fa == kE5M2 && fb == kE4M3) BY_OUT(kE5M2, kE4M3);
+    BY_OUT(kE5M2, kE5M2);
+#undef BY_OUT
+#undef CALL
+}
+
+hipError_t launch_gemm_mx(const uint8_t* a, int fa, int64_t lda, const uint8_t* xa, int64_t ld_xa, const uint8_t* b,
+                          int fb, int64_t ldb, const uint8_t* xb, int64_t ld_xb, int64_t m, int64_t n, int64_t k,
+                          void* d, int out_f32, int64_t ldd, hipStream_t st) {
+#define CALL(FA, FB, OF) gemm_mx_typed<FA, FB, OF>(a, lda, xa, ld_xa, b, ldb, xb, ld_xb, m, n, k, d, ldd, st)
+#define BY_OUT(FA, FB) return out_f32 ? CALL(FA, FB, true) : CALL(FA, FB, false)
+    if (fa == kE4M3 && fb == kE4M3) BY_OUT(kE4M3, kE4M3);
+    if (fa == kE4M3 && fb == kE5M2) BY_OUT(kE4M3, kE5M2);
+    if (fa == kE5M2 && fb == kE4M3) BY_OUT(kE5M2, kE4M3);
+    BY_OUT(kE5M2, kE5M2);
+#undef BY_OUT
+#undef CALL
+}
+
+hipError_t launch_grouped_gemm_mx(const uint8_t* a, int fa, int64_t lda, const uint8_t* xa, int64_t ld_xa,
+                                  const uint8_t* b, int fb, int64_t ldb, int64_t b_group_stride, const uint8_t* xb,
+                                  int64_t ld_xb, int64_t xb_group_stride, const int64_t* offsets, int g,
+                                  int64_t total_m, int64_t n, int64_t k, void* d, int out_f32, int64_t ldd,
+                                  hipStream_t st) {
+#define CALL(FA, FB, OF)                                                                                        \
+    grouped_mx_typed<FA, FB, OF>(a, lda, xa, ld_xa, b, ldb, b_group_stride, xb, ld_xb, xb_group_stride, offsets, g, \
+                                 total_m, n, k, d, ldd, st)
 #define BY_OUT(FA, FB) return out_f32 ? CALL(FA, FB, true) : CALL(FA, FB, false)
     if (fa == kE4M3 && fb == kE4M3) BY_OUT(kE4M3, kE4M3);
     if (fa == kE4M3 && fb == kE5M2) BY_OUT(kE4M3, kE5M2);

@@ -53,4 +53,19 @@ hipError_t launch_grouped_gemm_ragged_k(const uint8_t* a, int fa, int64_t lda, c
                                         const float* sa, const float* sb, void* d, int out_f32, int64_t ldd,
                                         int64_t d_group_stride, hipStream_t st);
 
+// MXFP8: rowwise block-32 quantization with E8M0 scales, and the products
+// whose operands carry such scales along K (dense, and grouped over rows).
+hipError_t launch_mx_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                               int64_t ldq, uint8_t* scale, int64_t ld_scale, hipStream_t st);
+
+hipError_t launch_gemm_mx(const uint8_t* a, int fa, int64_t lda, const uint8_t* xa, int64_t ld_xa, const uint8_t* b,
+                          int fb, int64_t ldb, const uint8_t* xb, int64_t ld_xb, int64_t m, int64_t n, int64_t k,
+                          void* d, int out_f32, int64_t ldd, hipStream_t st);
+
+hipError_t launch_grouped_gemm_mx(const uint8_t* a, int fa, int64_t lda, const uint8_t* xa, int64_t ld_xa,
+                                  const uint8_t* b, int fb, int64_t ldb, int64_t b_group_stride, const uint8_t* xb,
+                                  int64_t ld_xb, int64_t xb_group_stride, const int64_t* offsets, int g,
+                                  int64_t total_m, int64_t n, int64_t k, void* d, int out_f32, int64_t ldd,
+                                  hipStream_t st);
+
 }  // namespace fp8amax

@@ -436,6 +436,74 @@ __global__ __launch_bounds__(kBlock) void k_quant_tensor_reg(const uint16_t* __r
     }
 }
 
+// --------------------------------------------------------------- MX quantizer --
+// MXFP8 rowwise: blocks of 32 consecutive elements of a row share a
+// power-of-two scale 2^e stored as e + 127 (E8M0; 0xFF for a block holding a
+// NaN or Inf, whose elements are then cast with scale 1), e = floor(log2 amax)
+// - emax (8 for e4m3, 15 for e5m2) clamped to [-127, 127], e = -127 for a zero
+// block; elements are the saturating RNE cast of x * 2^-e (a reading of the
+// MXFP8 the TorchTitan/TorchAO page names; the pages define no format). One
+// wavefront per row slice of up to kMxSlice columns (grid y), held in
+// registers; a block is 4 lanes' 16-byte chunks, reduced with two lane
+// exchanges; the lane holding a block's first chunk stores its scale byte.
+template <int F>
+__device__ __forceinline__ constexpr int mx_emax() { return F == kE4M3 ? 8 : 15; }
+
+constexpr int64_t kMxSlice = 32 * 64 * 8;               // 16384 columns: 32 chunks per lane
+
+template <int F, int MAXC>
+__global__ __launch_bounds__(kBlock) void k_mx_quant_row(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                         int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                         uint8_t* __restrict__ sc, int64_t ldsc) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int64_t c0 = (int64_t)blockIdx.y * kMxSlice;
+    x += c0;
+    q += c0;
+    sc += c0 / 32;
+    const int nch = (int)((cols - c0 < kMxSlice ? cols - c0 : kMxSlice) >> 3);
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
+    uint4 v[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk, never stored
+    }
+    uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        uint32_t mx = pk_fold(word_absmax(0u, v[c]));
+        uint32_t o = __shfl_xor(mx, 1);
+        mx = o > mx ? o : mx;
+        o = __shfl_xor(mx, 2);
+        mx = o > mx ? o : mx;                            // the block's amax (16-bit magnitude bits)
+        uint32_t e8;
+        float mul;
+        if (mx >= 0x7f80u) {                             // Inf or NaN in the block
+            e8 = 0xFFu;
+            mul = 1.0f;
+        } else if (mx == 0u) {
+            e8 = 0u;
+            mul = 1.0f;                                  // (zeros cast to zero at any scale)
+        } else {
+            // floor(log2 amax) from the bf16 magnitude bits: the exponent field,
+            // or for a subnormal (field 0) the position of the top mantissa bit
+            const int fld = (int)(mx >> 7);
+            const int lg = fld > 0 ? fld - 127 : (31 - __builtin_clz(mx)) - 133;
+            int e = lg - mx_emax<F>();
+            e = e < -127 ? -127 : (e > 127 ? 127 : e);
+            e8 = (uint32_t)(e + 127);
+            mul = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, a normal float for every e reachable here
+        }
+        if (ch < nch) {
+            qr[ch] = e8 != 0xFFu ? encode8<F, true>(v[c], mul) : encode8<F, false>(v[c], mul);
+            if ((lane & 3) == 0) sc[row * ldsc + (ch >> 2)] = (uint8_t)e8;
+        }
+    }
+}
+
 // ---------------------------------------------------------- colwise quantizer --
 
 // Scales of the workgroup's 64 columns, computed once into LDS.
@@ -1096,6 +1164,36 @@ hipError_t launch_quant_tensor(const uint16_t* x, int64_t rows, int64_t cols, in
         default: return CALL(kE5M2Fnuz);
     }
 #undef CALL
+}
+
+hipError_t launch_mx_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                               int64_t ldq, uint8_t* scale, int64_t ld_scale, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int chunks = reg_chunks(cols < kMxSlice ? cols : kMxSlice);
+    const dim3 grid(grid_for_rows(rows), (unsigned)((cols + kMxSlice - 1) / kMxSlice)), block(kBlock);
+#define FP8_MX_CASE(F, C)                                                                                        \
+    case C:                                                                                                      \
+        hipLaunchKernelGGL((k_mx_quant_row<F, C>), grid, block, 0, st, x, rows, cols, ldx, q, ldq, scale,        \
+                           ld_scale);                                                                            \
+        break;
+#define FP8_MX_FMT(F)                                                                                            \
+    switch (chunks) {                                                                                            \
+        FP8_MX_CASE(F, 1)                                                                                        \
+        FP8_MX_CASE(F, 2)                                                                                        \
+        FP8_MX_CASE(F, 4)                                                                                        \
+        FP8_MX_CASE(F, 8)                                                                                        \
+        FP8_MX_CASE(F, 16)                                                                                       \
+        default:                                                                                                 \
+            FP8_MX_CASE(F, 32)                                                                                   \
+    }
+    if (fmt == kE4M3) {
+        FP8_MX_FMT(kE4M3)
+    } else {
+        FP8_MX_FMT(kE5M2)
+    }
+#undef FP8_MX_FMT
+#undef FP8_MX_CASE
+    return hipGetLastError();
 }
 
 hipError_t launch_grouped_quant_col(const uint16_t* x, int64_t total_m, int64_t cols, int64_t ldx, int fmt,

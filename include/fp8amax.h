@@ -257,6 +257,58 @@ fp8_status_t fp8_grouped_gemm_ragged_k(const uint8_t* a, fp8_format_t fa, int64_
                                        const float* b_scale_inv, void* d, fp8_out_t d_type, int64_t ldd,
                                        int64_t d_group_stride, void* stream);
 
+/* ------------------------------------------------------------------- MXFP8 --
+ * Block-scaled FP8 ([Flux] section "Configuration": mxfp8 among the recipes;
+ * [Titan] summary and next steps: MXFP8 grouped GEMM for MI355X). The pages
+ * name the recipe without defining it; this follows the OCP microscaling
+ * (MX) format, a reading: along K (the row of x, a and b), every block of
+ * FP8_MX_BLOCK consecutive elements shares one scale X = 2^e stored as the
+ * E8M0 byte e + 127 (255 = NaN). For a block with amax = max |x| over its
+ * elements:
+ *   e = floor(log2 amax) - emax (emax 8 for e4m3, 15 for e5m2), clamped to
+ *       -127..127; a zero block has e = -127;
+ *   element code = cast(x * 2^-e) with the saturating RNE cast above;
+ *   a block holding a NaN or an Inf gets the byte 255 and its elements are
+ *   cast with scale 1.
+ * Only the OCP encodings (e4m3, e5m2) carry MX data. */
+#define FP8_MX_BLOCK 32
+
+/* MX rowwise quantization. x: bf16 [rows x cols] (ldx); q: codes [rows x cols]
+ * (ldq); scale_e8m0: bytes [rows x cols/32] (ld_scale), block b of row i at
+ * scale_e8m0[i * ld_scale + b]. Requirements: cols % 32 == 0; x 16-byte
+ * aligned, ldx % 8 == 0; q 8-byte aligned, ldq % 8 == 0; rows < 2^26 (else
+ * FP8_ERR_UNSUPPORTED); fmt e4m3 or e5m2. */
+fp8_status_t fp8_mx_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                                 uint8_t* q, int64_t ldq, uint8_t* scale_e8m0, int64_t ld_scale, void* stream);
+
+/* MX GEMM:
+ *   d[i, j] = out( sum over blocks c < k/32 of
+ *                  2^(a_scale[i * ld_as + c] - 127) * 2^(b_scale[j * ld_bs + c] - 127)
+ *                  * sum_{t in block c} dec(a[i * lda + t]) * dec(b[j * ldb + t]) )
+ * accumulated in fp32 (a NaN scale byte makes the sums it enters NaN). a:
+ * codes [m x k], b: codes [n x k] (K-contiguous rows, b is W as stored),
+ * a_scale [m x k/32], b_scale [n x k/32] (as fp8_mx_quantize_row writes them).
+ * Requirements: k % 256 == 0 (else FP8_ERR_UNSUPPORTED); the scale matrices
+ * 4-byte aligned with ld_as, ld_bs multiples of 4; lda, ldb < 2^24 (else
+ * FP8_ERR_UNSUPPORTED); fewer than 2^24 tiles of 256 x 256; output type,
+ * formats (OCP only) and operand alignment as fp8_gemm_scaled. */
+fp8_status_t fp8_gemm_mx(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* a_scale, int64_t ld_as,
+                         const uint8_t* b, fp8_format_t fb, int64_t ldb, const uint8_t* b_scale, int64_t ld_bs,
+                         int64_t m, int64_t n, int64_t k, void* d, fp8_out_t d_type, int64_t ldd, void* stream);
+
+/* Grouped MX GEMM (MoE experts): rows offsets[g] .. offsets[g+1]-1 of a,
+ * a_scale and d belong to group g, whose weights are the codes
+ * b + g * b_group_stride [n x k] (ldb) with scales b_scale +
+ * g * b_scale_group_stride [n x k/32] (ld_bs); each group's rows as
+ * fp8_gemm_mx. group_offsets as fp8_grouped_gemm_scaled (device int64 [g+1],
+ * clamped to [0, total_m]). b_group_stride % 16 == 0, b_scale_group_stride %
+ * 4 == 0, g: 1..4096; otherwise as fp8_gemm_mx. */
+fp8_status_t fp8_grouped_gemm_mx(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* a_scale,
+                                 int64_t ld_as, const uint8_t* b, fp8_format_t fb, int64_t ldb, int64_t b_group_stride,
+                                 const uint8_t* b_scale, int64_t ld_bs, int64_t b_scale_group_stride,
+                                 const int64_t* group_offsets, int32_t g, int64_t total_m, int64_t n, int64_t k,
+                                 void* d, fp8_out_t d_type, int64_t ldd, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
