@@ -21,7 +21,7 @@ __all__ = [
     "fp8_quantize_tensor", "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update",
     "fp8_gemm_scaled", "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "grouped_layout_width", "GROUP_K_ALIGN", "MX_BLOCK", "fp8_mx_quantize_row", "fp8_gemm_mx",
-    "fp8_grouped_gemm_mx", "EXPORTED_SYMBOLS",
+    "fp8_grouped_gemm_mx", "mx_scale_records", "EXPORTED_SYMBOLS",
 ]
 
 E4M3, E5M2, E4M3_FNUZ, E5M2_FNUZ = 0, 1, 2, 3
@@ -242,24 +242,44 @@ def fp8_grouped_gemm_ragged_k(a, fa, b, fb, group_offsets, total_m, a_scale_inv,
                                          _stream(a)))
 
 
+def mx_scale_records(rows, cols, device="cuda:0"):
+    """An empty uint8 [ceil(cols/128) x rows x 4] tensor: the MX scale records
+    of a [rows x cols] matrix (record (j, r) holds the scales of blocks
+    4j .. 4j+3 of row r)."""
+    return torch.empty(((cols + 127) // 128, rows, 4), dtype=torch.uint8, device=device)
+
+
+def _records(t, name):
+    """(record rows J, rows, ld) of a uint8 [J x rows x 4] record tensor."""
+    if t.dim() != 3 or t.element_size() != 1 or t.shape[2] != 4:
+        raise ValueError(f"{name} must be a 1-byte [J x rows x 4] tensor, got {tuple(t.shape)} {t.dtype}")
+    if t.numel() > 0 and (t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != 4) or
+                          (t.shape[0] > 1 and t.stride(0) % 4 != 0)):
+        raise ValueError(f"{name} must hold contiguous 4-byte records, rows contiguous")
+    ld = t.stride(0) // 4 if t.shape[0] > 1 else t.shape[1]
+    return t.shape[0], t.shape[1], max(ld, t.shape[1], 1)
+
+
 def fp8_mx_quantize_row(x, fmt, q, scale_e8m0):
     """x bf16 [rows x cols] (cols % 32 == 0); q codes [rows x cols]; scale_e8m0
-    uint8 [rows x cols/32]."""
+    uint8 records [ceil(cols/128) x rows x 4] (mx_scale_records)."""
     rows, cols, ldx = _bf16(x)
     _, _, ldq = _mat(q, "q", 1)
-    _, _, lds = _mat(scale_e8m0, "scale_e8m0", 1)
+    J, r, lds = _records(scale_e8m0, "scale_e8m0")
+    if r != rows or J != (cols + 127) // 128:
+        raise ValueError(f"scale_e8m0 must be [{(cols + 127) // 128} x {rows} x 4], got {tuple(scale_e8m0.shape)}")
     _check(lib.fp8_mx_quantize_row(_ptr(x), rows, cols, ldx, fmt, _ptr(q), ldq, _ptr(scale_e8m0), lds, _stream(x)))
 
 
 def fp8_gemm_mx(a, fa, a_scale, b, fb, b_scale, d):
-    """d [m x n] = block-scaled (a [m x k] codes, a_scale uint8 [m x k/32]) times
-    (b [n x k] codes, b_scale uint8 [n x k/32])^T; d bf16 or float32."""
+    """d [m x n] = block-scaled (a [m x k] codes, a_scale records [k/128 x m x 4])
+    times (b [n x k] codes, b_scale records [k/128 x n x 4])^T; d bf16 or float32."""
     m, k, lda = _mat(a, "a", 1)
     n, kb, ldb = _mat(b, "b", 1)
     if kb != k:
         raise ValueError(f"a has k = {k} but b has k = {kb}")
-    _, _, ldas = _mat(a_scale, "a_scale", 1)
-    _, _, ldbs = _mat(b_scale, "b_scale", 1)
+    _, _, ldas = _records(a_scale, "a_scale")
+    _, _, ldbs = _records(b_scale, "b_scale")
     _, _, ldd = _mat(d, "d")
     d_type = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[d.dtype]
     _check(lib.fp8_gemm_mx(_ptr(a), fa, lda, _ptr(a_scale), ldas, _ptr(b), fb, ldb, _ptr(b_scale), ldbs, m, n, k,
@@ -267,22 +287,23 @@ def fp8_gemm_mx(a, fa, a_scale, b, fb, b_scale, d):
 
 
 def fp8_grouped_gemm_mx(a, fa, a_scale, b, fb, b_scale, group_offsets, d):
-    """a [total_m x k] codes sorted by group with a_scale uint8 [total_m x k/32];
-    b [g x n x k] codes with b_scale uint8 [g x n x k/32] (unit last strides);
+    """a [total_m x k] codes sorted by group with a_scale records [k/128 x total_m x 4];
+    b [g x n x k] codes (unit last stride) with b_scale records [g x k/128 x n x 4];
     group_offsets int64 [g+1] on the device; d [total_m x n]."""
     total_m, k, lda = _mat(a, "a", 1)
-    _, _, ldas = _mat(a_scale, "a_scale", 1)
-    for t, name in ((b, "b"), (b_scale, "b_scale")):
-        if t.dim() != 3 or t.element_size() != 1 or (t.numel() > 0 and t.shape[2] > 1 and t.stride(2) != 1):
-            raise ValueError(f"{name} must be a [g x n x *] 1-byte tensor with unit last stride")
+    _, _, ldas = _records(a_scale, "a_scale")
+    if b.dim() != 3 or b.element_size() != 1 or (b.numel() > 0 and b.shape[2] > 1 and b.stride(2) != 1):
+        raise ValueError("b must be a [g x n x k] 1-byte tensor with unit last stride")
     g, n, kb = b.shape
-    if kb != k or tuple(b_scale.shape[:2]) != (g, n):
+    if b_scale.dim() != 4 or b_scale.shape[0] != g:
+        raise ValueError(f"b_scale must be [{g} x k/128 x {n} x 4], got {tuple(b_scale.shape)}")
+    _, nb, ldbs = _records(b_scale[0], "b_scale[g]")
+    if kb != k or nb != n:
         raise ValueError(f"b {tuple(b.shape)} / b_scale {tuple(b_scale.shape)} do not match a's k = {k}")
     _, _, ldd = _mat(d, "d")
     d_type = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[d.dtype]
     if group_offsets.dtype != torch.int64 or group_offsets.numel() != g + 1:
         raise ValueError("group_offsets must be int64 with g + 1 entries")
     _check(lib.fp8_grouped_gemm_mx(_ptr(a), fa, lda, _ptr(a_scale), ldas, _ptr(b), fb, max(b.stride(1), k),
-                                   b.stride(0), _ptr(b_scale), max(b_scale.stride(1), b_scale.shape[2]),
-                                   b_scale.stride(0), _ptr(group_offsets), g, total_m, n, k, _ptr(d), d_type, ldd,
-                                   _stream(a)))
+                                   b.stride(0), _ptr(b_scale), ldbs, b_scale.stride(0), _ptr(group_offsets), g,
+                                   total_m, n, k, _ptr(d), d_type, ldd, _stream(a)))

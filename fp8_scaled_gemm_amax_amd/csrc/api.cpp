@@ -120,17 +120,18 @@ fp8_status_t check_gemm_operands(const char* fn, const uint8_t* a, int fa, int64
     return FP8_OK;
 }
 
-// Shared checks of the MX products: k % 256, the E8M0 scale matrices (one byte
-// per 32-element block, rows dword-aligned), and the 32-bit tile offsets.
+// Shared checks of the MX products: k % 256, the E8M0 scale records (one
+// dword per row and 128-deep K step, ld records apart per step), and the
+// 32-bit tile offsets.
 fp8_status_t check_mx(const char* fn, int64_t rows_a, int64_t rows_b, int64_t k, int64_t lda, int64_t ldb,
                       const uint8_t* xa, int64_t ld_xa, const uint8_t* xb, int64_t ld_xb) {
     if (k % 256 != 0) return fail(FP8_ERR_UNSUPPORTED, "%s: k = %lld is not a multiple of 256", fn, (long long)k);
-    FP8_TRY(check_matrix(fn, "a_scale", k > 0 ? xa : nullptr, rows_a, k / FP8_MX_BLOCK, ld_xa));
-    FP8_TRY(check_matrix(fn, "b_scale", k > 0 ? xb : nullptr, rows_b, k / FP8_MX_BLOCK, ld_xb));
-    if (k > 0 && rows_a > 0 && rows_b > 0 && (!xa || !xb)) return fail(FP8_ERR_INVALID_ARG, "%s: scale is NULL", fn);
-    if (k > 0 && (!aligned(xa, 4) || !aligned(xb, 4) || ld_xa % 4 != 0 || ld_xb % 4 != 0))
-        return fail(FP8_ERR_ALIGNMENT, "%s: scale matrices must be 4-byte aligned with leading dimensions multiples "
-                    "of 4", fn);
+    if (k > 0) {
+        if (rows_a > 0 && rows_b > 0 && (!xa || !xb)) return fail(FP8_ERR_INVALID_ARG, "%s: scale is NULL", fn);
+        if (ld_xa < rows_a || ld_xb < rows_b || ld_xa < 1 || ld_xb < 1)
+            return fail(FP8_ERR_INVALID_ARG, "%s: scale record stride smaller than the row count", fn);
+        if (!aligned(xa, 4) || !aligned(xb, 4)) return fail(FP8_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
+    }
     if (lda >= (1 << 24) || ldb >= (1 << 24))
         return fail(FP8_ERR_UNSUPPORTED, "%s: lda, ldb must be < 2^24 (256-row tiles use 32-bit offsets)", fn);
     return FP8_OK;
@@ -378,10 +379,12 @@ fp8_status_t fp8_mx_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, 
     if (cols % FP8_MX_BLOCK != 0) return fail(FP8_ERR_INVALID_ARG, "%s: cols = %lld is not a multiple of %d", fn,
                                               (long long)cols, FP8_MX_BLOCK);
     FP8_TRY(check_matrix(fn, "q", q, rows, cols, ldq));
-    FP8_TRY(check_matrix(fn, "scale_e8m0", scale_e8m0, rows, cols / FP8_MX_BLOCK, ld_scale));
-    if (!aligned(x, 16) || ldx % 8 != 0 || !aligned(q, 8) || ldq % 8 != 0)
+    if (rows > 0 && cols > 0 && !scale_e8m0) return fail(FP8_ERR_INVALID_ARG, "%s: scale_e8m0 is NULL", fn);
+    if (ld_scale < rows || ld_scale < 1)
+        return fail(FP8_ERR_INVALID_ARG, "%s: scale record stride %lld < rows", fn, (long long)ld_scale);
+    if (!aligned(x, 16) || ldx % 8 != 0 || !aligned(q, 8) || ldq % 8 != 0 || !aligned(scale_e8m0, 4))
         return fail(FP8_ERR_ALIGNMENT, "%s: x must be 16-byte aligned with ldx a multiple of 8, q 8-byte aligned with "
-                    "ldq a multiple of 8", fn);
+                    "ldq a multiple of 8, scale_e8m0 4-byte aligned", fn);
     if (rows >= ((int64_t)1 << 26)) return fail(FP8_ERR_UNSUPPORTED, "%s: 2^26 rows or more", fn);
     FP8_TRY(check_device());
     return launched(launch_mx_quant_row(x, rows, cols, ldx, (int)fmt, q, ldq, scale_e8m0, ld_scale,

@@ -569,12 +569,13 @@ __device__ __forceinline__ v16f k128_mfma(const v8i& fa, const v8i& fb, const v1
 
 // Step p with stage CUR = p % 2 (compile-time). LOADS: the 16 loads of step
 // p+1 (K offset knext) go to the other stage during this step's first 16 MFMAs
-// (with MX also the step's two scale dwords per thread, from the row
-// pointers xa / xb at byte knext / 32).
+// (with MX also step p+1's two scale dwords per thread: the records xa / xb
+// of K step 0 advanced by knext / 128 steps of xsa / xsb bytes).
 template <int FA, int FB, int CUR, bool LOADS, bool MX>
 __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], const uint8_t* a,
                                           const uint32_t (&aoff)[8], const uint8_t* b, const uint32_t (&boff)[8],
-                                          int64_t knext, const uint8_t* xa, const uint8_t* xb) {
+                                          int64_t knext, const uint8_t* xa, const uint8_t* xb, int64_t xsa,
+                                          int64_t xsb) {
     wait_vmcnt<0, 0>();                                  // this stage has landed; this wavefront's reads are done
     __syncthreads();                                     // (the other stage is now free for step p+1's loads)
     const uint8_t* ta = smem + CUR * k128::kStage;
@@ -614,7 +615,7 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], cons
                     const uint32_t xbase = __builtin_amdgcn_readfirstlane(
                                                lds_addr(smem + big::kMxOff + (CUR ^ 1) * big::kMxStage)) +
                                            wave * 256 + (i == 3 ? 0 : 1024);
-                    lds_dma4(xbase, (i == 3 ? xa : xb) + knext / 32);
+                    lds_dma4(xbase, i == 3 ? xa + (knext / k128::BK) * xsa : xb + (knext / k128::BK) * xsb);
                 }
             }
         }
@@ -633,13 +634,14 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], cons
 // The K loop of the large-tile kernels; k % 256 == 0 (k = 0: zero sums). The
 // epilogue's row and column scales go to the scale area: sa_lane / sb_lane
 // (thread t's row / column scale) or, with MX, 1 (the block scales are applied
-// inside the MFMAs, and xa / xb are thread t's scale row pointers, of A row
-// mx_row(t) and B row mx_row(t) of the tile).
+// inside the MFMAs; xa / xb are the K-step-0 scale records of A row mx_row(t)
+// and B row mx_row(t) of the tile, and a K step advances them by xsa / xsb
+// bytes).
 template <int FA, int FB, bool MX>
 __device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
                                               const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k,
                                               const float* sa_lane, const float* sb_lane, const uint8_t* xa,
-                                              const uint8_t* xb, v16f (&acc)[4][4]) {
+                                              const uint8_t* xb, int64_t xsa, int64_t xsb, v16f (&acc)[4][4]) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -674,11 +676,11 @@ __device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, i
         }
     }
     for (int64_t p = 0; p + 2 < nk; p += 2) {
-        k128_step<FA, FB, 0, true, MX>(smem, acc, a, aoff, b, boff, (p + 1) * k128::BK, xa, xb);
-        k128_step<FA, FB, 1, true, MX>(smem, acc, a, aoff, b, boff, (p + 2) * k128::BK, xa, xb);
+        k128_step<FA, FB, 0, true, MX>(smem, acc, a, aoff, b, boff, (p + 1) * k128::BK, xa, xb, xsa, xsb);
+        k128_step<FA, FB, 1, true, MX>(smem, acc, a, aoff, b, boff, (p + 2) * k128::BK, xa, xb, xsa, xsb);
     }
-    k128_step<FA, FB, 0, true, MX>(smem, acc, a, aoff, b, boff, (nk - 1) * k128::BK, xa, xb);
-    k128_step<FA, FB, 1, false, MX>(smem, acc, a, aoff, b, boff, 0, xa, xb);
+    k128_step<FA, FB, 0, true, MX>(smem, acc, a, aoff, b, boff, (nk - 1) * k128::BK, xa, xb, xsa, xsb);
+    k128_step<FA, FB, 1, false, MX>(smem, acc, a, aoff, b, boff, 0, xa, xb, xsa, xsb);
     wait_vmcnt<0>();                                     // (nothing is outstanding: the last step loads nothing)
 }
 
@@ -816,13 +818,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
     const float* sb_lane = sb + (sb_vec ? (col0 + t < n ? col0 + t : n - 1) : 0);
     v16f acc[4][4];
     k128_mainloop<FA, FB, false>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, sa_lane,
-                                 sb_lane, nullptr, nullptr, acc);
+                                 sb_lane, nullptr, nullptr, 0, 0, acc);
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, m - row0, col0, n - col0, vec_out);
 }
 
 // MX product: d = sum over 32-deep K blocks of the blocks' dot products times
 // 2^(xa - 127) * 2^(xb - 127), the E8M0 scales of row i's and column j's block
-// (xa row r at xa + r * ld_xa, one byte per block).
+// (K-step-major records: the scales of blocks 4j .. 4j+3 of row r are the
+// 4 bytes at xa + 4 (j ld_xa + r)).
 template <int FA, int FB, bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ a, int64_t lda,
                                                     const uint8_t* __restrict__ xa, int64_t ld_xa,
@@ -835,11 +838,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ 
     big_tile_coords(blockIdx.x, tiles_m, tiles_n, &pm, &pn);
     const int64_t row0 = pm * big::BM, col0 = pn * big::BN;
     const int rt = mx_row(threadIdx.x);
-    const uint8_t* xa_lane = xa + (row0 + rt < m ? row0 + rt : m - 1) * ld_xa;
-    const uint8_t* xb_lane = xb + (col0 + rt < n ? col0 + rt : n - 1) * ld_xb;
+    const uint8_t* xa_lane = xa + 4 * (row0 + rt < m ? row0 + rt : m - 1);
+    const uint8_t* xb_lane = xb + 4 * (col0 + rt < n ? col0 + rt : n - 1);
     v16f acc[4][4];
     k128_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, nullptr,
-                                nullptr, xa_lane, xb_lane, acc);
+                                nullptr, xa_lane, xb_lane, 4 * ld_xa, 4 * ld_xb, acc);
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, m - row0, col0, n - col0, vec_out);
 }
 
@@ -859,7 +862,8 @@ constexpr int kMaxGroupsBig = 4096;
 static_assert((kMaxGroupsBig + 1) * 8 <= big::kMain, "group prefix sums fit in the stage buffers");
 
 // With MX the operands carry E8M0 block scales instead of sa / sb: xa (row r
-// of a at xa + r * ld_xa) and, for group e, xb + e * xb_group_stride.
+// of a in the records of xa with ld_xa) and, for group e, xb + e *
+// xb_group_stride (bytes) with ld_xb.
 template <int FA, int FB, bool OUT_F32, bool K64, bool MX>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb, int64_t b_group_stride,
@@ -937,10 +941,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     v16f acc[4][4];
     if constexpr (MX) {
         const int rt = mx_row(t);
-        const uint8_t* xa_lane = xa + (row0 + rt < hi ? row0 + rt : hi - 1) * ld_xa;
-        const uint8_t* xb_lane = xb + (int64_t)grp * xb_group_stride + (col0 + rt < n ? col0 + rt : n - 1) * ld_xb;
+        const uint8_t* xa_lane = xa + 4 * (row0 + rt < hi ? row0 + rt : hi - 1);
+        const uint8_t* xb_lane = xb + (int64_t)grp * xb_group_stride + 4 * (col0 + rt < n ? col0 + rt : n - 1);
         k128_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, nullptr,
-                                    nullptr, xa_lane, xb_lane, acc);
+                                    nullptr, xa_lane, xb_lane, 4 * ld_xa, 4 * ld_xb, acc);
     } else {
         const float* sa_lane = sa + (row0 + t < hi ? row0 + t : hi - 1);
         const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
@@ -949,7 +953,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
                                  sb_lane, acc);
         else
             k128_mainloop<FA, FB, false>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
-                                         sa_lane, sb_lane, nullptr, nullptr, acc);
+                                         sa_lane, sb_lane, nullptr, nullptr, 0, 0, acc);
     }
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, hi - row0, col0, n - col0, vec_out);
 }
@@ -1010,7 +1014,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
     v16f acc[4][4];
     if (K > 0) {
         k128_mainloop<FA, FB, false>(smem, a + row0 * lda + P, lda, m - row0, b + col0 * ldb + P, ldb, n - col0, K,
-                                     sa_lane, sb_lane, nullptr, nullptr, acc);
+                                     sa_lane, sb_lane, nullptr, nullptr, 0, 0, acc);
     } else {                                             // empty group: 0 * sa * sb
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)

@@ -445,7 +445,11 @@ __global__ __launch_bounds__(kBlock) void k_quant_tensor_reg(const uint16_t* __r
 // MXFP8 the TorchTitan/TorchAO page names; the pages define no format). One
 // wavefront per row slice of up to kMxSlice columns (grid y), held in
 // registers; a block is 4 lanes' 16-byte chunks, reduced with two lane
-// exchanges; the lane holding a block's first chunk stores its scale byte.
+// exchanges. Scale layout, K-step major: the scales of blocks 4j .. 4j+3 of
+// row r are the 4 bytes at sc + 4 (j ldsc + r) (so the rows of one 128-deep K
+// step are contiguous for the GEMM); the lane holding the first chunk of
+// blocks 4j .. 4j+3 gathers their bytes and stores the dword, with zero bytes
+// for blocks past the row.
 template <int F>
 __device__ __forceinline__ constexpr int mx_emax() { return F == kE4M3 ? 8 : 15; }
 
@@ -461,7 +465,7 @@ __global__ __launch_bounds__(kBlock) void k_mx_quant_row(const uint16_t* __restr
     const int64_t c0 = (int64_t)blockIdx.y * kMxSlice;
     x += c0;
     q += c0;
-    sc += c0 / 32;
+    sc += (c0 / 128) * ldsc * 4;
     const int nch = (int)((cols - c0 < kMxSlice ? cols - c0 : kMxSlice) >> 3);
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
     uint4 v[MAXC];
@@ -497,10 +501,13 @@ __global__ __launch_bounds__(kBlock) void k_mx_quant_row(const uint16_t* __restr
             e8 = (uint32_t)(e + 127);
             mul = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, a normal float for every e reachable here
         }
-        if (ch < nch) {
-            qr[ch] = e8 != 0xFFu ? encode8<F, true>(v[c], mul) : encode8<F, false>(v[c], mul);
-            if ((lane & 3) == 0) sc[row * ldsc + (ch >> 2)] = (uint8_t)e8;
-        }
+        if (ch < nch) qr[ch] = e8 != 0xFFu ? encode8<F, true>(v[c], mul) : encode8<F, false>(v[c], mul);
+        // lanes 16i, 16i+4, 16i+8, 16i+12 hold the first chunks of blocks 4j .. 4j+3
+        const uint32_t mine = ch < nch ? e8 : 0u;
+        const uint32_t b1 = __shfl_down(mine, 4), b2 = __shfl_down(mine, 8), b3 = __shfl_down(mine, 12);
+        if ((lane & 15) == 0 && ch < nch)
+            *reinterpret_cast<uint32_t*>(sc + 4 * ((int64_t)(ch >> 4) * ldsc + row)) =
+                mine | (b1 << 8) | (b2 << 16) | (b3 << 24);
     }
 }
 

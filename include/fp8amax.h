@@ -273,36 +273,46 @@ fp8_status_t fp8_grouped_gemm_ragged_k(const uint8_t* a, fp8_format_t fa, int64_
  * Only the OCP encodings (e4m3, e5m2) carry MX data. */
 #define FP8_MX_BLOCK 32
 
+/* Scale layout of the MX entry points (K-step major, a layout of this
+ * library): the scales of blocks 4j .. 4j+3 of row r (elements 128j ..
+ * 128j + 127) are the four bytes, in block order, of the 4-byte record at
+ * scale + 4 * (j * ld_scale + r); ld_scale >= rows counts records. A matrix
+ * with cols columns has ceil(cols / 128) record rows, (ceil(cols / 128) - 1)
+ * * ld_scale + rows records in all. The 256 rows of a GEMM tile then bring
+ * one K step's scales in as one contiguous 1 KB run per operand. */
+
 /* MX rowwise quantization. x: bf16 [rows x cols] (ldx); q: codes [rows x cols]
- * (ldq); scale_e8m0: bytes [rows x cols/32] (ld_scale), block b of row i at
- * scale_e8m0[i * ld_scale + b]. Requirements: cols % 32 == 0; x 16-byte
- * aligned, ldx % 8 == 0; q 8-byte aligned, ldq % 8 == 0; rows < 2^26 (else
- * FP8_ERR_UNSUPPORTED); fmt e4m3 or e5m2. */
+ * (ldq); scale_e8m0: the rows' block scales as records (above; bytes of
+ * blocks past cols / 32 in the last record are written as 0). Requirements:
+ * cols % 32 == 0; x 16-byte aligned, ldx % 8 == 0; q 8-byte aligned,
+ * ldq % 8 == 0; scale_e8m0 4-byte aligned, ld_scale >= rows; rows < 2^26
+ * (else FP8_ERR_UNSUPPORTED); fmt e4m3 or e5m2. */
 fp8_status_t fp8_mx_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
                                  uint8_t* q, int64_t ldq, uint8_t* scale_e8m0, int64_t ld_scale, void* stream);
 
 /* MX GEMM:
  *   d[i, j] = out( sum over blocks c < k/32 of
- *                  2^(a_scale[i * ld_as + c] - 127) * 2^(b_scale[j * ld_bs + c] - 127)
+ *                  2^(sa(i, c) - 127) * 2^(sb(j, c) - 127)
  *                  * sum_{t in block c} dec(a[i * lda + t]) * dec(b[j * ldb + t]) )
- * accumulated in fp32 (a NaN scale byte makes the sums it enters NaN). a:
- * codes [m x k], b: codes [n x k] (K-contiguous rows, b is W as stored),
- * a_scale [m x k/32], b_scale [n x k/32] (as fp8_mx_quantize_row writes them).
- * Requirements: k % 256 == 0 (else FP8_ERR_UNSUPPORTED); the scale matrices
- * 4-byte aligned with ld_as, ld_bs multiples of 4; lda, ldb < 2^24 (else
- * FP8_ERR_UNSUPPORTED); fewer than 2^24 tiles of 256 x 256; output type,
- * formats (OCP only) and operand alignment as fp8_gemm_scaled. */
+ * accumulated in fp32 (a NaN scale byte makes the sums it enters NaN), where
+ * sa(i, c) is block c's scale of row i of a in the records of a_scale (record
+ * stride ld_as >= m), sb(j, c) likewise in b_scale (ld_bs >= n). a: codes
+ * [m x k], b: codes [n x k] (K-contiguous rows, b is W as stored).
+ * Requirements: k % 256 == 0 (else FP8_ERR_UNSUPPORTED); the scales 4-byte
+ * aligned; lda, ldb < 2^24 (else FP8_ERR_UNSUPPORTED); fewer than 2^24 tiles
+ * of 256 x 256; output type, formats (OCP only) and operand alignment as
+ * fp8_gemm_scaled. */
 fp8_status_t fp8_gemm_mx(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* a_scale, int64_t ld_as,
                          const uint8_t* b, fp8_format_t fb, int64_t ldb, const uint8_t* b_scale, int64_t ld_bs,
                          int64_t m, int64_t n, int64_t k, void* d, fp8_out_t d_type, int64_t ldd, void* stream);
 
-/* Grouped MX GEMM (MoE experts): rows offsets[g] .. offsets[g+1]-1 of a,
- * a_scale and d belong to group g, whose weights are the codes
- * b + g * b_group_stride [n x k] (ldb) with scales b_scale +
- * g * b_scale_group_stride [n x k/32] (ld_bs); each group's rows as
- * fp8_gemm_mx. group_offsets as fp8_grouped_gemm_scaled (device int64 [g+1],
- * clamped to [0, total_m]). b_group_stride % 16 == 0, b_scale_group_stride %
- * 4 == 0, g: 1..4096; otherwise as fp8_gemm_mx. */
+/* Grouped MX GEMM (MoE experts): rows offsets[g] .. offsets[g+1]-1 of a
+ * (scale records of a_scale, ld_as >= total_m) and of d belong to group g,
+ * whose weights are the codes b + g * b_group_stride [n x k] (ldb) with the
+ * scale records at b_scale + g * b_scale_group_stride (bytes; ld_bs >= n);
+ * each group's rows as fp8_gemm_mx. group_offsets as fp8_grouped_gemm_scaled
+ * (device int64 [g+1], clamped to [0, total_m]). b_group_stride % 16 == 0,
+ * b_scale_group_stride % 4 == 0, g: 1..4096; otherwise as fp8_gemm_mx. */
 fp8_status_t fp8_grouped_gemm_mx(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* a_scale,
                                  int64_t ld_as, const uint8_t* b, fp8_format_t fb, int64_t ldb, int64_t b_group_stride,
                                  const uint8_t* b_scale, int64_t ld_bs, int64_t b_scale_group_stride,

@@ -195,8 +195,8 @@ def test_query_device_rejects_null(fp8):
 
 def test_mx_entry_points_reject_bad_arguments(fp8):
     q = "fp8_mx_quantize_row"
-    # x [4 x 64] bf16, q [4 x 64], scales [4 x 2]
-    ok_q = [FAKE, 4, 64, 64, 0, FAKE, 64, FAKE, 2, None]
+    # x [4 x 64] bf16, q [4 x 64], one K step of 4 scale records
+    ok_q = [FAKE, 4, 64, 64, 0, FAKE, 64, FAKE, 4, None]
     bad = list(ok_q)
     bad[2], bad[3], bad[6] = 48, 64, 64      # cols not a multiple of 32
     assert _call(fp8, q, *bad)[0] == 1
@@ -204,26 +204,29 @@ def test_mx_entry_points_reject_bad_arguments(fp8):
     bad[4] = 2                               # fnuz elements
     assert _call(fp8, q, *bad)[0] == 1
     bad = list(ok_q)
-    bad[8] = 1                               # scale row shorter than cols / 32
+    bad[8] = 3                               # record stride < rows
     assert _call(fp8, q, *bad)[0] == 1
+    bad = list(ok_q)
+    bad[7] = ctypes.c_void_p(0x10002)        # scale records off the dword grid
+    assert _call(fp8, q, *bad)[0] == 2
     bad = list(ok_q)
     bad[5] = ctypes.c_void_p(0x10004)        # q off the 8-byte grid
     assert _call(fp8, q, *bad)[0] == 2
     bad = list(ok_q)
-    bad[1] = 1 << 26                         # too many rows
+    bad[1] = bad[8] = 1 << 26                # too many rows
     assert _call(fp8, q, *bad)[0] == 3
     g = "fp8_gemm_mx"
-    # a [64 x 512], b [32 x 512], scales [* x 16], d [64 x 32]
-    ok_g = [FAKE, 0, 512, FAKE, 16, FAKE, 0, 512, FAKE, 16, 64, 32, 512, FAKE, 0, 32, None]
+    # a [64 x 512], b [32 x 512], scale records with ld = rows, d [64 x 32]
+    ok_g = [FAKE, 0, 512, FAKE, 64, FAKE, 0, 512, FAKE, 32, 64, 32, 512, FAKE, 0, 32, None]
     bad = list(ok_g)
     bad[12], bad[2], bad[7] = 384, 384, 384  # k not a multiple of 256
     st, msg = _call(fp8, g, *bad)
     assert st == 3 and "256" in msg
     bad = list(ok_g)
-    bad[4] = 8                               # scale row shorter than k / 32
+    bad[4] = 63                              # record stride < m
     assert _call(fp8, g, *bad)[0] == 1
     bad = list(ok_g)
-    bad[9] = 18                              # scale row stride off the dword grid
+    bad[8] = ctypes.c_void_p(0x10006)        # scale records off the dword grid
     assert _call(fp8, g, *bad)[0] == 2
     bad = list(ok_g)
     bad[3] = None                            # no scales
@@ -232,8 +235,8 @@ def test_mx_entry_points_reject_bad_arguments(fp8):
     bad[6] = 3                               # fnuz operand
     assert _call(fp8, g, *bad)[0] == 3
     gg = "fp8_grouped_gemm_mx"
-    # a [64 x 512], 4 groups of b [32 x 512], scales [* x 16]
-    ok_gg = [FAKE, 0, 512, FAKE, 16, FAKE, 1, 512, 32 * 512, FAKE, 16, 32 * 16, FAKE, 4, 64, 32, 512, FAKE, 0, 32,
+    # a [64 x 512], 4 groups of b [32 x 512], scale records with ld = rows
+    ok_gg = [FAKE, 0, 512, FAKE, 64, FAKE, 1, 512, 32 * 512, FAKE, 32, 4 * 32 * 4, FAKE, 4, 64, 32, 512, FAKE, 0, 32,
              None]
     bad = list(ok_gg)
     bad[13] = 0                              # no groups

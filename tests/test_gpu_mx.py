@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import workloads
-from helpers import assert_codes_equal, check_guard, dev_bf16, dev_u8, guarded, say
+from helpers import SENTINEL, assert_codes_equal, check_guard, dev_bf16, dev_u8, guarded, say
 
 pytestmark = pytest.mark.gpu
 
@@ -30,10 +30,25 @@ def block_scaled_bf16(rows, cols, seed, spread=20):
     return workloads.bf16_bits(x)
 
 
-def gpu_mx_quantize(fp8, xb, fmt, ldx=None, ldq=None, lds=None):
-    """Quantize on the GPU into guarded outputs; returns (codes, scale bytes)."""
+def to_records(s):
+    """Scale bytes [rows x nb] (the oracle's row-major blocks) -> the library's
+    K-step-major records [ceil(nb/4) x rows x 4], zero bytes past nb."""
+    rows, nb = s.shape
+    J = (nb + 3) // 4
+    pad = np.zeros((rows, 4 * J), np.uint8)
+    pad[:, :nb] = s
+    return np.ascontiguousarray(pad.reshape(rows, J, 4).transpose(1, 0, 2))
+
+
+def dev_records(s):
+    return dev_u8(to_records(s))
+
+
+def gpu_mx_quantize(fp8, xb, fmt, ldx=None, ldq=None, lds_extra=3):
+    """Quantize on the GPU into guarded outputs (the scale records with
+    lds_extra spare records per K step); returns (codes, scale records)."""
     rows, cols = xb.shape
-    nb = cols // BLOCK
+    J = (cols + 127) // 128
     if ldx is not None:
         xbuf = torch.zeros((rows, ldx), dtype=torch.bfloat16, device="cuda:0")
         xbuf[:, :cols] = dev_bf16(xb)
@@ -41,11 +56,16 @@ def gpu_mx_quantize(fp8, xb, fmt, ldx=None, ldq=None, lds=None):
     else:
         x = dev_bf16(xb)
     q, qbuf, qo = guarded(rows, cols, torch.uint8, ld=ldq)
-    s, sbuf, so = guarded(rows, nb, torch.uint8, ld=lds)
+    ld = rows + lds_extra
+    sbuf = torch.full((J + 2, ld * 4), SENTINEL, dtype=torch.uint8, device="cuda:0")
+    s = sbuf[1:1 + J].view(J, ld, 4)[:, :rows, :]
     fp8.fp8_mx_quantize_row(x, fmt, q, s)
     torch.cuda.synchronize()
     check_guard(qbuf, qo, rows, cols)
-    check_guard(sbuf, so, rows, nb)
+    host = sbuf.cpu().numpy()
+    outside = np.ones(host.shape, bool)
+    outside[1:1 + J, :rows * 4] = False
+    assert np.all(host[outside] == SENTINEL), "write outside the scale records"
     return q.cpu().numpy(), s.cpu().numpy()
 
 
@@ -61,7 +81,7 @@ def test_mx_quantize_row_parity(fp8, orc, fmt, rows, cols):
     say("mx quantize", rows, cols, fmt)
     q, s = gpu_mx_quantize(fp8, xb, fmt)
     oq, osc = orc.mx_quantize_row(xb, fmt)
-    assert_codes_equal(s, osc, "scale bytes")
+    assert_codes_equal(s, to_records(osc), "scale records")
     assert_codes_equal(q, oq, "codes")
 
 
@@ -76,7 +96,7 @@ def test_mx_quantize_every_bf16_value(fp8, orc, fmt):
         say("mx every bf16", name, fmt)
         q, s = gpu_mx_quantize(fp8, xb, fmt)
         oq, osc = orc.mx_quantize_row(xb, fmt)
-        assert_codes_equal(s, osc, f"scale bytes ({name})")
+        assert_codes_equal(s, to_records(osc), f"scale records ({name})")
         assert_codes_equal(q, oq, f"codes ({name})")
 
 
@@ -98,7 +118,7 @@ def test_mx_quantize_special_blocks(fp8, orc):
         say("mx special", fmt)
         q, s = gpu_mx_quantize(fp8, xb, fmt)
         oq, osc = orc.mx_quantize_row(xb, fmt)
-        assert_codes_equal(s, osc, "scale bytes")
+        assert_codes_equal(s, to_records(osc), "scale records")
         assert_codes_equal(q, oq, "codes")
 
 
@@ -106,9 +126,9 @@ def test_mx_quantize_strided(fp8, orc):
     """Leading dimensions past the row: x, q and the scales as strided views."""
     xb = block_scaled_bf16(37, 1024, seed=11)
     say("mx strided")
-    q, s = gpu_mx_quantize(fp8, xb, 0, ldx=1024 + 72, ldq=1024 + 40, lds=32 + 5)
+    q, s = gpu_mx_quantize(fp8, xb, 0, ldx=1024 + 72, ldq=1024 + 40, lds_extra=61)
     oq, osc = orc.mx_quantize_row(xb, 0)
-    assert_codes_equal(s, osc, "scale bytes")
+    assert_codes_equal(s, to_records(osc), "scale records")
     assert_codes_equal(q, oq, "codes")
 
 
@@ -128,7 +148,7 @@ def mx_operands(orc, rows, k, fmt, seed, spread=6):
 def gpu_gemm_mx(fp8, a, fa, sa, b, fb, sb, out_f32=False):
     m, n = a.shape[0], b.shape[0]
     d, dbuf, do = guarded(m, n, torch.float32 if out_f32 else torch.bfloat16, ld=n + 8)
-    fp8.fp8_gemm_mx(dev_u8(a), fa, dev_u8(sa), dev_u8(b), fb, dev_u8(sb), d)
+    fp8.fp8_gemm_mx(dev_u8(a), fa, dev_records(sa), dev_u8(b), fb, dev_records(sb), d)
     torch.cuda.synchronize()
     check_guard(dbuf, do, m, n)
     return d.float().cpu().numpy().astype(np.float64)
@@ -183,8 +203,9 @@ def test_gemm_mx_nan_scale_and_empty_k(fp8, orc):
     say("gemm mx k = 0")
     d = torch.full((m, n), float("nan"), device="cuda:0")
     e = torch.empty((m, 0), dtype=torch.uint8, device="cuda:0")
-    fp8.fp8_gemm_mx(e, 0, e, torch.empty((n, 0), dtype=torch.uint8, device="cuda:0"), 0,
-                    torch.empty((n, 0), dtype=torch.uint8, device="cuda:0"), d)
+    fp8.fp8_gemm_mx(e, 0, torch.empty((0, m, 4), dtype=torch.uint8, device="cuda:0"),
+                    torch.empty((n, 0), dtype=torch.uint8, device="cuda:0"), 0,
+                    torch.empty((0, n, 4), dtype=torch.uint8, device="cuda:0"), d)
     torch.cuda.synchronize()
     assert (d == 0).all().item()
 
@@ -212,7 +233,8 @@ def test_grouped_gemm_mx_parity(fp8, orc, sizes, n, k, fa, fb, out_f32):
     say("grouped gemm mx", sizes, n, k, fa, fb, out_f32)
     dt = torch.float32 if out_f32 else torch.bfloat16
     d, dbuf, do = guarded(T, n, dt, ld=n + 8)
-    fp8.fp8_grouped_gemm_mx(dev_u8(a), fa, dev_u8(sa), dev_u8(b), fb, dev_u8(sb),
+    sb_rec = np.stack([to_records(sb[e]) for e in range(g)])
+    fp8.fp8_grouped_gemm_mx(dev_u8(a), fa, dev_records(sa), dev_u8(b), fb, dev_u8(sb_rec),
                             torch.from_numpy(offsets).to("cuda:0"), d)
     torch.cuda.synchronize()
     check_guard(dbuf, do, T, n)
@@ -230,9 +252,9 @@ def test_mx_layer_forward_composed(fp8, orc):
     say("mx layer forward")
     dev = "cuda:0"
     xq = torch.empty((m, k), dtype=torch.uint8, device=dev)
-    xs = torch.empty((m, k // BLOCK), dtype=torch.uint8, device=dev)
+    xs = fp8.mx_scale_records(m, k)
     wq = torch.empty((n, k), dtype=torch.uint8, device=dev)
-    ws = torch.empty((n, k // BLOCK), dtype=torch.uint8, device=dev)
+    ws = fp8.mx_scale_records(n, k)
     fp8.fp8_mx_quantize_row(dev_bf16(xb), 0, xq, xs)
     fp8.fp8_mx_quantize_row(dev_bf16(wb), 0, wq, ws)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -241,6 +263,6 @@ def test_mx_layer_forward_composed(fp8, orc):
     oxq, oxs = orc.mx_quantize_row(xb, 0)
     owq, ows = orc.mx_quantize_row(wb, 0)
     assert_codes_equal(xq.cpu().numpy(), oxq, "x codes")
-    assert_codes_equal(ws.cpu().numpy(), ows, "w scales")
+    assert_codes_equal(ws.cpu().numpy(), to_records(ows), "w scales")
     oy, ob = orc.mx_gemm(oxq, 0, oxs, owq, 0, ows)
     assert_within(orc, y.float().cpu().numpy().astype(np.float64), oy, ob, True, "mx forward")
