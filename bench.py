@@ -14,9 +14,10 @@ algorithmic GB/s (2 B read + 1 B written per element + 4 B per scale) against
 8 TB/s; `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload on this host's cores.
 
-Other workloads (--workload c1|c3|c4|c4b|c5) print the same line for the
+Other workloads (--workload c1|c3|c4|c4b|c4mx|c5) print the same line for the
 other shapes (c3 tensorwise delayed, c4 MoE grouped GEMM, c4b the MoE expert
-layer's backward, c5 hybrid backward).
+layer's backward, c4mx c4 with MXFP8 block-32 E8M0 scales, c5 hybrid
+backward).
 """
 import argparse
 import json
@@ -39,7 +40,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c4b", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c4b", "c4mx", "c5"])
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -120,6 +121,26 @@ class Step:
             self.desc = ("DeepSeek-V3 MoE grouped GEMM, one GPU's share: 32 experts Zipf(1.1) counts (3 empty), "
                          "tokens bf16 [16384x7168] N(0,1), W_e bf16 [2048x7168] N(0,0.006^2); e4m3 rowwise; bf16 out")
             self.scales = {"recipe": "rowwise", "format": "e4m3"}
+        elif name == "c4mx":
+            w = workloads.c4()
+            g, n, k = w["w"].shape
+            self.x = bf16_dev(w["x"])
+            self.w = bf16_dev(w["w"].reshape(g * n, k))
+            self.offsets = torch.from_numpy(w["offsets"]).to(dev)
+            self.cpu_sample = (w["x"], 0, w["w"][0], 0)
+            self.cpu_kind = "mx"
+            m = self.x.shape[0]
+            self.g, self.n, self.k = g, n, k
+            self.qx, self.qw = E((m, k), dtype=torch.uint8, device=dev), E((g * n, k), dtype=torch.uint8, device=dev)
+            self.sx, self.sw = fp8.mx_scale_records(m, k), fp8.mx_scale_records(g * n, k)
+            self.d = E((m, n), dtype=torch.bfloat16, device=dev)
+            self.mnk = [(m, n, k)]
+            # (4-byte scale records: k / 128 per row)
+            self.calls = [("mx_quantize_row tokens", m * k, m * k // 512),
+                          ("mx_quantize_row expert W", g * n * k, g * n * k // 512), ("grouped_gemm_mx", None, 0)]
+            self.desc = ("DeepSeek-V3 MoE grouped GEMM, one GPU's share, MXFP8: c4's experts and tokens; e4m3 "
+                         "elements with E8M0 scales per 32 elements along K (tokens and expert weights); bf16 out")
+            self.scales = {"recipe": "mxfp8", "format": "e4m3"}
         elif name == "c4b":
             w = workloads.c4b()
             g, n, k = w["w"].shape
@@ -203,6 +224,16 @@ class Step:
             f.fp8_grouped_gemm_scaled(self.qx, f.E4M3, self.qw.view(self.g, self.n, self.k), f.E4M3, self.offsets,
                                       self.sx, self.sw.view(self.g, self.n), self.d)
             ev[3].record()
+        elif self.name == "c4mx":
+            g, n, k = self.g, self.n, self.k
+            f.fp8_mx_quantize_row(self.x, f.E4M3, self.qx, self.sx)
+            ev[1].record()
+            f.fp8_mx_quantize_row(self.w, f.E4M3, self.qw, self.sw)
+            ev[2].record()
+            # expert e's weight records: rows e*n .. e*n+n-1 of the stacked records
+            sw = self.torch.as_strided(self.sw, (g, k // 128, n, 4), (4 * n, 4 * g * n, 4, 1))
+            f.fp8_grouped_gemm_mx(self.qx, f.E4M3, self.sx, self.qw.view(g, n, k), f.E4M3, sw, self.offsets, self.d)
+            ev[3].record()
         elif self.name == "c4b":
             g, n, k = self.g, self.n, self.k
             f.fp8_quantize_row(self.dy, f.E5M2, 0, self.dyq, self.dys)
@@ -277,11 +308,12 @@ def copy_calibration(args):
                       "steps": args.steps}), flush=True)
 
 
-def cpu_baseline(sample, target_s):
+def cpu_baseline(sample, target_s, kind="rowwise"):
     """The CPU oracle on a bounded sample of the workload's own tensors: the
     first ms rows of the activation and the first ns rows of the weight
-    (K-contiguous) quantized rowwise, then the oracle's fp64
-    dequantize-and-matmul of the sample. Reported as 2*ms*ns*K / time in TFLOP/s."""
+    (K-contiguous) quantized rowwise (kind "mx": MX block-32), then the
+    oracle's fp64 dequantize-and-matmul of the sample. Reported as
+    2*ms*ns*K / time in TFLOP/s."""
     from oracle import oracle as orc
     act, fa, wgt, fw = sample
     k = act.shape[1]
@@ -289,9 +321,14 @@ def cpu_baseline(sample, target_s):
 
     def run(ms, ns):
         t0 = time.perf_counter()
-        qx, sx, _ = orc.quantize_row(act[:ms], fa)
-        qw, sw, _ = orc.quantize_row(wgt[:ns], fw)
-        orc.gemm(qx, fa, qw, fw, sx, sw, with_bound=False)
+        if kind == "mx":
+            qx, sx = orc.mx_quantize_row(act[:ms], fa)
+            qw, sw = orc.mx_quantize_row(wgt[:ns], fw)
+            orc.mx_gemm(qx, fa, sx, qw, fw, sw)
+        else:
+            qx, sx, _ = orc.quantize_row(act[:ms], fa)
+            qw, sw, _ = orc.quantize_row(wgt[:ns], fw)
+            orc.gemm(qx, fa, qw, fw, sx, sw, with_bound=False)
         return time.perf_counter() - t0
 
     ms, ns = min(act.shape[0], 1024), min(wgt.shape[0], 512)
@@ -303,8 +340,9 @@ def cpu_baseline(sample, target_s):
         t = run(ms, ns)
     return {"value": round(2.0 * ms * ns * k / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{ms} activation rows x {ns} weight rows x K={k} of the workload's tensors: rowwise "
-                      f"quantize of both (oracle) + fp64 dequantize-and-matmul, {t:.1f} s on {threads} threads"}
+            "sample": f"{ms} activation rows x {ns} weight rows x K={k} of the workload's tensors: "
+                      f"{'MX block-32' if kind == 'mx' else 'rowwise'} quantize of both (oracle) + fp64 "
+                      f"dequantize-and-matmul, {t:.1f} s on {threads} threads"}
 
 
 def main():
@@ -338,7 +376,7 @@ def main():
     g = gemm_idx[0]
     gemm_flops = 2.0 * np.prod(step.mnk[0])
     gemm_tflops = gemm_flops / (per_call_ms[g] * 1e-3) / 1e12
-    kernel_key = "grouped_gemm" if args.workload in ("c4", "c4b") else "gemm"
+    kernel_key = {"c4": "grouped_gemm", "c4b": "grouped_gemm", "c4mx": "grouped_gemm_mx"}.get(args.workload, "gemm")
     traffic = measured_traffic(f"{kernel_key}:{args.workload}")
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
@@ -367,7 +405,8 @@ def main():
         "config": {"workload": step.desc, "m": m, "n": n, "k": k, **step.scales, "out": "bf16",
                    "flops_per_step": step.flops},
         "roofline": roofline, "quantizers": quant, "other_kernels": other,
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(step.cpu_sample, args.cpu_seconds),
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(step.cpu_sample, args.cpu_seconds,
+                                                                       getattr(step, "cpu_kind", "rowwise")),
     }
     print(json.dumps(out), flush=True)
 

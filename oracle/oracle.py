@@ -328,6 +328,43 @@ def mx_grouped_gemm(a, fa, sa, b, fb, sb, offsets):
     return y, bound
 
 
+def mx_scale_values(s):
+    """E8M0 bytes -> 2^(s - 127) in fp64; 255 -> NaN."""
+    s = np.asarray(s)
+    return np.where(s == 255, np.nan, np.exp2(s.astype(np.float64) - 127.0))
+
+
+def mx_gemm_entries(a, fa, sa, b, fb, sb, ii, jj, chunk=1024):
+    """Selected outputs Y[ii[e], jj[e]] of the MX product, from its definition:
+    per 32-element block the dot product of the decoded codes times both block
+    scales, summed over the blocks (fp64). Returns (y, bound)."""
+    a = np.asarray(a, np.uint8)
+    b = np.asarray(b, np.uint8)
+    ii = np.asarray(ii, np.int64)
+    jj = np.asarray(jj, np.int64)
+    k = a.shape[1]
+    nb = k // MX_BLOCK
+    y = np.empty(ii.size, np.float64)
+    bound = np.empty(ii.size, np.float64)
+    for lo in range(0, ii.size, chunk):
+        i, j = ii[lo:lo + chunk], jj[lo:lo + chunk]
+        p = decode(fa, a[i]).reshape(-1, nb, MX_BLOCK) * decode(fb, b[j]).reshape(-1, nb, MX_BLOCK)
+        x = mx_scale_values(np.asarray(sa)[i]) * mx_scale_values(np.asarray(sb)[j])
+        y[lo:lo + chunk] = (x * p.sum(axis=2)).sum(axis=1)
+        bound[lo:lo + chunk] = (x * np.abs(p).sum(axis=2)).sum(axis=1)
+    return y, bound
+
+
+def mx_grouped_gemm_entries(a, fa, sa, b, fb, sb, offsets, ii, jj):
+    """Selected outputs of the grouped MX product: row i belongs to the group g
+    with offsets[g] <= i < offsets[g+1], whose weights are b[g] (scales sb[g])."""
+    g, n, k = b.shape
+    grp = np.searchsorted(np.asarray(offsets, np.int64), np.asarray(ii, np.int64), side="right") - 1
+    rows_b = grp * n + np.asarray(jj, np.int64)
+    return mx_gemm_entries(a, fa, sa, np.asarray(b).reshape(g * n, k), fb,
+                           np.asarray(sb).reshape(g * n, k // MX_BLOCK), ii, rows_b)
+
+
 # ---------------------------------------------------------------- MoE backward --
 # The MoE backward ("FP8 Training on AMD GPUs with TorchTitan and TorchAO": the
 # backward-pass speedup of the MoE model, colwise scales, grouped GEMM) needs the

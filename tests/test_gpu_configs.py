@@ -1,4 +1,4 @@
-"""Full-size parity on the five workloads, in the launch configuration the
+"""Full-size parity on the workloads, in the launch configuration the
 benchmark times: every quantizer output compared bit for bit with the oracle on
 the whole tensor, every GEMM output compared on sampled entries (at least one
 per 128 x 128 output tile, plus the last row and column) within the bound
@@ -226,3 +226,47 @@ def test_c5_hybrid_backward(fp8, orc):
     say("c5 gemm check")
     check_sampled(orc, dx, oqdy, 1, oqwt, 0, osdy, oswt, seed=6, what="dgrad")
     check_sampled(orc, dw, oqdyt, 1, oqxt, 0, osdyt, osxt, seed=7, what="wgrad")
+
+
+def test_c4mx_moe_grouped_mx(fp8, orc):
+    """The c4 tensors with MXFP8: tokens and expert weights through the MX
+    quantizer (codes and scale records bit-exact on the whole tensors), the
+    grouped MX product on sampled outputs incl. the first and last row of
+    every non-empty expert, in the bench's launch configuration (expert
+    weight records as a strided view of the stacked records)."""
+    say("c4mx generate")
+    w = workloads.c4()
+    offsets = w["offsets"]
+    g, n, k = w["w"].shape
+    T = int(offsets[-1])
+    wflat = w["w"].reshape(g * n, k)
+    say("c4mx quantize")
+    qx = torch.empty((T, k), dtype=torch.uint8, device="cuda:0")
+    sx = fp8.mx_scale_records(T, k)
+    qw = torch.empty((g * n, k), dtype=torch.uint8, device="cuda:0")
+    sw = fp8.mx_scale_records(g * n, k)
+    fp8.fp8_mx_quantize_row(dev_bf16(w["x"]), 0, qx, sx)
+    fp8.fp8_mx_quantize_row(dev_bf16(wflat), 0, qw, sw)
+    d = torch.empty((T, n), dtype=torch.bfloat16, device="cuda:0")
+    swv = torch.as_strided(sw, (g, k // 128, n, 4), (4 * n, 4 * g * n, 4, 1))
+    fp8.fp8_grouped_gemm_mx(qx, 0, sx, qw.view(g, n, k), 0, swv, torch.from_numpy(offsets).to("cuda:0"), d)
+    torch.cuda.synchronize()
+    oqx, osx = orc.mx_quantize_row(w["x"], 0)
+    assert_codes_equal(qx.cpu().numpy(), oqx, "token codes")
+    rec = lambda s: np.ascontiguousarray(s.reshape(s.shape[0], -1, 4).transpose(1, 0, 2))
+    assert_codes_equal(sx.cpu().numpy(), rec(osx), "token scale records")
+    oqw, osw = orc.mx_quantize_row(wflat, 0)
+    assert_codes_equal(qw.cpu().numpy(), oqw, "expert weight codes")
+    assert_codes_equal(sw.cpu().numpy(), rec(osw), "expert weight scale records")
+    say("c4mx grouped gemm check")
+    ii, jj = sample_entries(T, n, seed=14)
+    rng = np.random.default_rng(15)
+    for e in range(g):
+        if offsets[e + 1] > offsets[e]:
+            ii = np.concatenate([ii, [offsets[e], offsets[e + 1] - 1]])
+            jj = np.concatenate([jj, rng.integers(0, n, 2)])
+    y, bound = orc.mx_grouped_gemm_entries(oqx, 0, osx, oqw.reshape(g, n, k), 0, osw.reshape(g, n, k // 32),
+                                           offsets, ii, jj)
+    got = d[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()].float().cpu().numpy().astype(np.float64)
+    ok = orc.gemm_within_bound(got, y, bound)
+    assert ok.all(), f"{int((~ok).sum())} sampled grouped MX outputs outside the bound"

@@ -108,3 +108,29 @@ def test_mx_gemm_exact_integers(orc):
                 want += x * float(np.dot(ia[i, sl], ib[j, sl]))
                 mag += x * float(np.abs(ia[i, sl] * ib[j, sl]).sum())
             assert y[i, j] == want and bound[i, j] == mag
+
+
+def test_mx_entries_match_the_whole_product(orc):
+    """The sampled-entry form (used on full-size outputs) against the whole
+    product on random codes and scales, dense and grouped (a NaN scale byte
+    included); the two sum in different orders, so to fp64 rounding."""
+    rng = np.random.default_rng(7)
+    m, n, k = 20, 12, 256
+    a = rng.integers(0, 0x7E, (m, k)).astype(np.uint8)
+    b = rng.integers(0x80, 0xFB, (n, k)).astype(np.uint8)
+    sa = rng.integers(110, 140, (m, k // 32)).astype(np.uint8)
+    sb = rng.integers(110, 140, (n, k // 32)).astype(np.uint8)
+    sa[3, 2] = 0xFF
+    y, bound = orc.mx_gemm(a, 0, sa, b, 1, sb)
+    ii, jj = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+    ye, be = orc.mx_gemm_entries(a, 0, sa, b, 1, sb, ii.ravel(), jj.ravel())
+    assert np.allclose(ye.reshape(m, n), y, rtol=1e-12, atol=0, equal_nan=True)
+    assert np.allclose(be.reshape(m, n), bound, rtol=1e-12, atol=0, equal_nan=True)
+    assert np.isnan(ye.reshape(m, n)[3]).all()
+    offsets = np.array([0, 5, 5, 20], np.int64)
+    bg = rng.integers(0, 0x7E, (3, n, k)).astype(np.uint8)
+    sbg = rng.integers(110, 140, (3, n, k // 32)).astype(np.uint8)
+    yg, bg_bound = orc.mx_grouped_gemm(a, 0, sa, bg, 0, sbg, offsets)
+    ye, be = orc.mx_grouped_gemm_entries(a, 0, sa, bg, 0, sbg, offsets, ii.ravel(), jj.ravel())
+    assert np.allclose(ye.reshape(m, n), yg, rtol=1e-12, atol=0, equal_nan=True)
+    assert np.allclose(be.reshape(m, n), bg_bound, rtol=1e-12, atol=0, equal_nan=True)
