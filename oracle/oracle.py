@@ -438,3 +438,114 @@ def gemm_within_bound(gpu, y, bound, out_bf16=True):
     both_nan = np.isnan(gpu) & np.isnan(y)
     same_inf = np.isinf(gpu) & np.isinf(y) & (np.sign(gpu) == np.sign(y))
     return ok | both_nan | same_inf
+
+
+# ------------------------------------------------------------- MoE layer forward --
+# The per-layer MoE path ("How PyTorch FP8 Optimizations on AMD GPUs Reduce LLM
+# Cost ...": What Happened, the per-MoE-layer latency; "FP8 Training on AMD GPUs
+# with TorchTitan and TorchAO": fused quantization kernels, FP8 grouped GEMM for
+# MoE). The pages give no layer definition; the reading used here is the
+# plainest MoE feed-forward layer: each token goes to its top-k experts, every
+# expert applies a SwiGLU FFN, and the k results are summed with the router's
+# weights. Steps: route (expert-sorted order), permute + rowwise quantize,
+# grouped GEMM with the stacked gate|up weights, SwiGLU + rowwise quantize,
+# grouped GEMM with the down weights, unpermute + weighted combine.
+
+def moe_route(expert_idx, num_experts):
+    """expert_idx int [T x k] -> (offsets int64 [E+1], dest int32 [T x k]):
+    a counting sort of the T*k (token, slot) entries by expert, stable in
+    (token, slot) order. dest[t, j] is the row of entry (t, j) in the
+    expert-sorted order; expert e owns rows offsets[e] .. offsets[e+1]-1."""
+    idx = np.asarray(expert_idx, np.int64)
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    counts = np.zeros(num_experts, np.int64)
+    for e in flat:                                      # histogram
+        counts[e] += 1
+    offsets = np.zeros(num_experts + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    nxt = offsets[:-1].copy()                           # next free row of each expert
+    dest = np.empty(flat.size, np.int64)
+    for i, e in enumerate(flat):                        # entries in (token, slot) order
+        dest[i] = nxt[e]
+        nxt[e] += 1
+    return offsets, dest.reshape(T, k).astype(np.int32)
+
+
+def moe_permute_quantize_row(x_bf16, dest, fmt, margin=0):
+    """Rowwise quantization of every token, its codes and scale placed at each
+    of its k destination rows: returns (q [T*k x H], scale_inv [T*k])."""
+    q_tok, si_tok, _ = quantize_row(x_bf16, fmt, margin)
+    dest = np.asarray(dest, np.int64)
+    T, k = dest.shape
+    q = np.empty((T * k, q_tok.shape[1]), np.uint8)
+    si = np.empty(T * k, np.float32)
+    for t in range(T):
+        for j in range(k):
+            q[dest[t, j]] = q_tok[t]
+            si[dest[t, j]] = si_tok[t]
+    return q, si
+
+
+def silu(x):
+    """x * sigmoid(x) in fp64."""
+    x = np.asarray(x, np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def swiglu_quantize_row(h_bf16, fmt, margin=0):
+    """h [rows x 2I] bf16 holding gate (columns 0 .. I-1) | up (I .. 2I-1):
+    a = silu(gate) * up in fp64, rounded once to fp32; then rowwise current
+    scaling of the fp32 rows (amax, s = scale rule, code = cast(fl32(a * s))).
+    Returns (q [rows x I], scale_inv [rows], a32 [rows x I])."""
+    h = bf16_to_f64(h_bf16)
+    inter = h.shape[1] // 2
+    a32 = (silu(h[:, :inter]) * h[:, inter:]).astype(np.float32)
+    rows = a32.shape[0]
+    q = np.empty((rows, inter), np.uint8)
+    si = np.empty(rows, np.float32)
+    for r in range(rows):
+        row = a32[r]
+        am = np.float32(np.nan) if np.isnan(row).any() else np.abs(row).max(initial=np.float32(0))
+        s = scale_current(fmt, am, margin)
+        q[r] = encode(fmt, row * s)                      # fp32 product, then the saturating RNE cast
+        si[r] = reciprocal(s)
+    return q, si, a32
+
+
+def moe_unpermute_combine(y_bf16, dest, weights):
+    """out[t] = sum over slots j of weights[t, j] * y[dest[t, j]] in fp64
+    (returned unrounded, with the sum of magnitudes as the bound's base)."""
+    y = bf16_to_f64(y_bf16)
+    dest = np.asarray(dest, np.int64)
+    w = np.asarray(weights, np.float64)
+    T, k = dest.shape
+    out = np.zeros((T, y.shape[1]))
+    mag = np.zeros((T, y.shape[1]))
+    for j in range(k):
+        out += w[:, j:j + 1] * y[dest[:, j]]
+        mag += np.abs(w[:, j:j + 1] * y[dest[:, j]])
+    return out, mag
+
+
+def bf16_to_f64(bits):
+    """bf16 bit patterns -> fp64 values (exact)."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_round(x):
+    """fp64 -> bf16 bit patterns, round to nearest even. Goes through fp32
+    rounded to odd (truncate toward zero, then set the last bit if anything
+    was dropped), which keeps the bf16 decision that of the fp64 value."""
+    x = np.asarray(x, np.float64)
+    f = x.astype(np.float32)
+    over = np.abs(f.astype(np.float64)) > np.abs(x)
+    f = np.where(over, np.nextafter(f, np.float32(0)), f).astype(np.float32)
+    u = f.view(np.uint32).copy()
+    inexact = (f.astype(np.float64) != x) & np.isfinite(x)
+    u[inexact] |= 1
+    u64 = u.astype(np.uint64)
+    r = ((u64 + 0x7FFF + ((u64 >> 16) & 1)) >> 16).astype(np.uint16)
+    r[np.isnan(x)] = 0x7FC0
+    return r
