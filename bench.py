@@ -17,7 +17,8 @@ workload on this host's cores.
 Other workloads (--workload c1|c3|c4|c4b|c4mx|c5) print the same line for the
 other shapes (c3 tensorwise delayed, c4 MoE grouped GEMM, c4b the MoE expert
 layer's backward, c4mx c4 with MXFP8 block-32 E8M0 scales, c5 hybrid
-backward).
+backward, c6 the DeepSeek-V3 MoE layer forward: route, permute + cast,
+gate|up grouped GEMM, SwiGLU + cast, down grouped GEMM, weighted combine).
 """
 import argparse
 import json
@@ -40,7 +41,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c4b", "c4mx", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c4b", "c4mx", "c5", "c6"])
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -141,6 +142,44 @@ class Step:
             self.desc = ("DeepSeek-V3 MoE grouped GEMM, one GPU's share, MXFP8: c4's experts and tokens; e4m3 "
                          "elements with E8M0 scales per 32 elements along K (tokens and expert weights); bf16 out")
             self.scales = {"recipe": "mxfp8", "format": "e4m3"}
+        elif name == "c6":
+            w = workloads.c6()
+            T, H = w["x"].shape
+            nexp, I2, _ = w["w1"].shape
+            k = w["idx"].shape[1]
+            P, inter = T * k, I2 // 2
+            self.T, self.H, self.E, self.I2, self.k, self.P, self.inter = T, H, nexp, I2, k, P, inter
+            self.x = bf16_dev(w["x"])
+            self.idx = torch.from_numpy(w["idx"]).to(dev)
+            self.wts = torch.from_numpy(w["weights"]).to(dev)
+            self.w1 = bf16_dev(w["w1"].reshape(nexp * I2, H))
+            self.w2 = bf16_dev(w["w2"].reshape(nexp * H, inter))
+            self.cpu_sample = w
+            self.cpu_kind = "moe_layer"
+            self.off = E(nexp + 1, dtype=torch.int64, device=dev)
+            self.dest = E((T, k), dtype=torch.int32, device=dev)
+            self.xq, self.xs = E((P, H), dtype=torch.uint8, device=dev), E(P, device=dev)
+            self.w1q, self.w1s = E((nexp * I2, H), dtype=torch.uint8, device=dev), E(nexp * I2, device=dev)
+            self.h = E((P, I2), dtype=torch.bfloat16, device=dev)
+            self.aq, self.asi = E((P, inter), dtype=torch.uint8, device=dev), E(P, device=dev)
+            self.w2q, self.w2s = E((nexp * H, inter), dtype=torch.uint8, device=dev), E(nexp * H, device=dev)
+            self.y = E((P, H), dtype=torch.bfloat16, device=dev)
+            self.out = E((T, H), dtype=torch.bfloat16, device=dev)
+            self.mnk = [(P, I2, H), (P, H, inter)]
+            # (name, elements, scales[, algorithmic bytes])
+            self.calls = [("moe_route", 0, 0, 8 * T * k + 8 * (nexp + 1)),
+                          ("moe_permute_quantize tokens", T * H, P, 2 * T * H + P * H + 4 * P),
+                          ("quantize_row W1 (gate|up)", nexp * I2 * H, nexp * I2),
+                          ("grouped_gemm gate|up", None, 0),
+                          ("swiglu_quantize", P * inter, P, 4 * P * inter + P * inter + 4 * P),
+                          ("quantize_row W2 (down)", nexp * H * inter, nexp * H),
+                          ("grouped_gemm down", None, 0),
+                          ("moe_unpermute_combine", 0, 0, 2 * P * H + 2 * T * H + 8 * T * k)]
+            self.desc = ("DeepSeek-V3 MoE layer forward, one GPU's share: 2048 tokens [2048x7168] N(0,1), top-8 of "
+                         "32 experts (Zipf(1.1) popularity, softmax weights), SwiGLU experts gate|up W1 "
+                         "[32x4096x7168], down W2 [32x7168x2048] N(0,0.006^2); e4m3 rowwise, weights quantized "
+                         "every step; bf16 out")
+            self.scales = {"recipe": "rowwise", "format": "e4m3"}
         elif name == "c4b":
             w = workloads.c4b()
             g, n, k = w["w"].shape
@@ -234,6 +273,26 @@ class Step:
             sw = self.torch.as_strided(self.sw, (g, k // 128, n, 4), (4 * n, 4 * g * n, 4, 1))
             f.fp8_grouped_gemm_mx(self.qx, f.E4M3, self.sx, self.qw.view(g, n, k), f.E4M3, sw, self.offsets, self.d)
             ev[3].record()
+        elif self.name == "c6":
+            E, I2, H, inter = self.E, self.I2, self.H, self.inter
+            f.fp8_moe_route(self.idx, E, self.off, self.dest)
+            ev[1].record()
+            f.fp8_moe_permute_quantize_row(self.x, self.dest, f.E4M3, 0, self.xq, self.xs)
+            ev[2].record()
+            f.fp8_quantize_row(self.w1, f.E4M3, 0, self.w1q, self.w1s)
+            ev[3].record()
+            f.fp8_grouped_gemm_scaled(self.xq, f.E4M3, self.w1q.view(E, I2, H), f.E4M3, self.off, self.xs,
+                                      self.w1s.view(E, I2), self.h)
+            ev[4].record()
+            f.fp8_swiglu_quantize_row(self.h, f.E4M3, 0, self.aq, self.asi)
+            ev[5].record()
+            f.fp8_quantize_row(self.w2, f.E4M3, 0, self.w2q, self.w2s)
+            ev[6].record()
+            f.fp8_grouped_gemm_scaled(self.aq, f.E4M3, self.w2q.view(E, H, inter), f.E4M3, self.off, self.asi,
+                                      self.w2s.view(E, H), self.y)
+            ev[7].record()
+            f.fp8_moe_unpermute_combine(self.y, self.dest, self.wts, self.out)
+            ev[8].record()
         elif self.name == "c4b":
             g, n, k = self.g, self.n, self.k
             f.fp8_quantize_row(self.dy, f.E5M2, 0, self.dyq, self.dys)
@@ -345,6 +404,41 @@ def cpu_baseline(sample, target_s, kind="rowwise"):
                       f"dequantize-and-matmul, {t:.1f} s on {threads} threads"}
 
 
+def cpu_baseline_moe(w, target_s):
+    """The oracle's MoE layer forward on the workload's first ts tokens (all
+    their entries, every expert's weights quantized): route, permute + cast,
+    gate|up grouped product, SwiGLU + cast, down grouped product, combine.
+    Reported as 6 * (ts * topk) * hidden * inter / time in TFLOP/s."""
+    from oracle import oracle as orc
+    x, idx, wts, w1, w2 = w["x"], w["idx"], w["weights"], w["w1"], w["w2"]
+    nexp, I2, H = w1.shape
+    inter = I2 // 2
+    k = idx.shape[1]
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+
+    def run(ts):
+        t0 = time.perf_counter()
+        off, dest = orc.moe_route(idx[:ts], nexp)
+        xq, xs = orc.moe_permute_quantize_row(x[:ts], dest, 0)
+        w1q, w1s, _ = orc.quantize_row(w1.reshape(nexp * I2, H), 0)
+        h, _ = orc.grouped_gemm(xq, 0, w1q.reshape(nexp, I2, H), 0, off, xs, w1s.reshape(nexp, I2))
+        aq, asi, _ = orc.swiglu_quantize_row(orc.bf16_round(h), 0)
+        w2q, w2s, _ = orc.quantize_row(w2.reshape(nexp * H, inter), 0)
+        y, _ = orc.grouped_gemm(aq, 0, w2q.reshape(nexp, H, inter), 0, off, asi, w2s.reshape(nexp, H))
+        orc.moe_unpermute_combine(orc.bf16_round(y), dest, wts[:ts])
+        return time.perf_counter() - t0
+
+    ts = 16
+    t = run(ts)
+    if t < 0.5 * target_s:
+        ts = int(min(x.shape[0], ts * target_s / t))
+        t = run(ts)
+    return {"value": round(6.0 * ts * k * H * inter / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the layer forward on the first {ts} tokens (x{k} expert entries) with all {nexp} experts' "
+                      f"weights quantized, oracle steps incl. fp64 grouped products, {t:.1f} s on {threads} threads"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -372,30 +466,32 @@ def main():
     ms_step = elapsed / args.steps * 1e3
     value = step.flops / (ms_step * 1e-3) / 1e12
 
-    gemm_idx = [i for i, (nm, _, _) in enumerate(step.calls) if "gemm" in nm]
+    gemm_idx = [i for i, call in enumerate(step.calls) if "gemm" in call[0]]
     g = gemm_idx[0]
     gemm_flops = 2.0 * np.prod(step.mnk[0])
     gemm_tflops = gemm_flops / (per_call_ms[g] * 1e-3) / 1e12
-    kernel_key = {"c4": "grouped_gemm", "c4b": "grouped_gemm", "c4mx": "grouped_gemm_mx"}.get(args.workload, "gemm")
+    kernel_key = {"c4": "grouped_gemm", "c4b": "grouped_gemm", "c4mx": "grouped_gemm_mx",
+                  "c6": "grouped_gemm"}.get(args.workload, "gemm")
     traffic = measured_traffic(f"{kernel_key}:{args.workload}")
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                 "kernel": step.calls[g][0], "avg_ms": round(per_call_ms[g], 5),
                 "flops_per_launch": gemm_flops}
-    quant = []
-    for i, (nm, elems, nscales) in enumerate(step.calls):
-        if elems:
-            nbytes = 3.0 * elems + 4.0 * nscales
+    quant, other = [], []
+    for i, call in enumerate(step.calls):
+        nm, elems, nscales = call[:3]
+        nbytes = float(call[3]) if len(call) > 3 else (3.0 * elems + 4.0 * nscales if elems else 0.0)
+        if nbytes:
             gbps = nbytes / (per_call_ms[i] * 1e-3) / 1e9
-            quant.append({"kernel": nm, "avg_ms": round(per_call_ms[i], 5), "algorithmic_bytes": nbytes,
-                          "gbps": round(gbps, 1), "frac_of_hbm": round(gbps / PEAK_HBM_GBPS, 4)})
-    other = [{"kernel": nm, "avg_ms": round(per_call_ms[i], 5)} for i, (nm, e, _) in enumerate(step.calls)
-             if e == 0 or ("gemm" in nm and i != g)]
-    for o in other:
-        if "gemm" in o["kernel"]:
-            j = [i for i, (nm, _, _) in enumerate(step.calls) if nm == o["kernel"]][0]
+            rec = {"kernel": nm, "avg_ms": round(per_call_ms[i], 5), "algorithmic_bytes": nbytes,
+                   "gbps": round(gbps, 1), "frac_of_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+            (quant if "quant" in nm else other).append(rec)
+        elif "gemm" in nm and i != g:
             m, n, k = step.mnk[1]
-            o["tflops"] = round(2.0 * m * n * k / (per_call_ms[j] * 1e-3) / 1e12, 2)
+            other.append({"kernel": nm, "avg_ms": round(per_call_ms[i], 5),
+                          "tflops": round(2.0 * m * n * k / (per_call_ms[i] * 1e-3) / 1e12, 2)})
+        elif i != g:
+            other.append({"kernel": nm, "avg_ms": round(per_call_ms[i], 5)})
     m, n, k = step.mnk[0]
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -405,8 +501,9 @@ def main():
         "config": {"workload": step.desc, "m": m, "n": n, "k": k, **step.scales, "out": "bf16",
                    "flops_per_step": step.flops},
         "roofline": roofline, "quantizers": quant, "other_kernels": other,
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(step.cpu_sample, args.cpu_seconds,
-                                                                       getattr(step, "cpu_kind", "rowwise")),
+        "cpu_baseline": None if args.no_cpu_baseline else (
+            cpu_baseline_moe(step.cpu_sample, args.cpu_seconds) if getattr(step, "cpu_kind", "") == "moe_layer"
+            else cpu_baseline(step.cpu_sample, args.cpu_seconds, getattr(step, "cpu_kind", "rowwise"))),
     }
     print(json.dumps(out), flush=True)
 

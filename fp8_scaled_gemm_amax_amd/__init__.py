@@ -21,7 +21,8 @@ __all__ = [
     "fp8_quantize_tensor", "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update",
     "fp8_gemm_scaled", "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "grouped_layout_width", "GROUP_K_ALIGN", "MX_BLOCK", "fp8_mx_quantize_row", "fp8_gemm_mx",
-    "fp8_grouped_gemm_mx", "mx_scale_records", "EXPORTED_SYMBOLS",
+    "fp8_grouped_gemm_mx", "mx_scale_records", "fp8_moe_route", "fp8_moe_permute_quantize_row",
+    "fp8_swiglu_quantize_row", "fp8_moe_unpermute_combine", "EXPORTED_SYMBOLS",
 ]
 
 E4M3, E5M2, E4M3_FNUZ, E5M2_FNUZ = 0, 1, 2, 3
@@ -34,7 +35,8 @@ EXPORTED_SYMBOLS = (
     "fp8_query_device", "fp8_status_string", "fp8_last_error", "fp8_amax", "fp8_quantize_tensor",
     "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update", "fp8_gemm_scaled",
     "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
-    "fp8_mx_quantize_row", "fp8_gemm_mx", "fp8_grouped_gemm_mx",
+    "fp8_mx_quantize_row", "fp8_gemm_mx", "fp8_grouped_gemm_mx", "fp8_moe_route", "fp8_moe_permute_quantize_row",
+    "fp8_swiglu_quantize_row", "fp8_moe_unpermute_combine",
 )
 
 GROUP_K_ALIGN = 256     # FP8_GROUP_K_ALIGN of the C header
@@ -75,6 +77,10 @@ def _load():
         "fp8_mx_quantize_row": [P, I64, I64, I64, I, P, I64, P, I64, P],
         "fp8_gemm_mx": [P, I, I64, P, I64, P, I, I64, P, I64, I64, I64, I64, P, I, I64, P],
         "fp8_grouped_gemm_mx": [P, I, I64, P, I64, P, I, I64, I64, P, I64, I64, P, I32, I64, I64, I64, P, I, I64, P],
+        "fp8_moe_route": [P, I64, I32, I32, P, P, P],
+        "fp8_moe_permute_quantize_row": [P, I64, I64, I64, P, I32, I64, I, I32, P, I64, P, P],
+        "fp8_swiglu_quantize_row": [P, I64, I64, I64, I, I32, P, I64, P, P],
+        "fp8_moe_unpermute_combine": [P, I64, I64, I64, P, P, I64, I32, P, I64, P],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -307,3 +313,58 @@ def fp8_grouped_gemm_mx(a, fa, a_scale, b, fb, b_scale, group_offsets, d):
     _check(lib.fp8_grouped_gemm_mx(_ptr(a), fa, lda, _ptr(a_scale), ldas, _ptr(b), fb, max(b.stride(1), k),
                                    b.stride(0), _ptr(b_scale), ldbs, b_scale.stride(0), _ptr(group_offsets), g,
                                    total_m, n, k, _ptr(d), d_type, ldd, _stream(a)))
+
+
+def _i32_2d(t, name):
+    if t.dim() != 2 or t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 [tokens x topk] tensor")
+    return t.shape[0], t.shape[1]
+
+
+def fp8_moe_route(expert_idx, num_experts, offsets_out, dest_out):
+    """expert_idx int32 [T x k] -> offsets_out int64 [E+1], dest_out int32 [T x k]."""
+    T, k = _i32_2d(expert_idx, "expert_idx")
+    if tuple(dest_out.shape) != (T, k) or dest_out.dtype != torch.int32 or not dest_out.is_contiguous():
+        raise ValueError(f"dest_out must be a contiguous int32 [{T} x {k}] tensor")
+    if offsets_out.dtype != torch.int64 or offsets_out.numel() != num_experts + 1:
+        raise ValueError(f"offsets_out must be int64 with {num_experts + 1} entries")
+    _check(lib.fp8_moe_route(_ptr(expert_idx), T, k, num_experts, _ptr(offsets_out), _ptr(dest_out),
+                             _stream(expert_idx)))
+
+
+def fp8_moe_permute_quantize_row(x, dest, fmt, margin, q, scale_inv_out):
+    """x bf16 [T x H]; dest int32 [T x k] (fp8_moe_route); q codes [rows_out x H];
+    scale_inv_out fp32 [rows_out]."""
+    T, H, ldx = _bf16(x)
+    Td, k = _i32_2d(dest, "dest")
+    if Td != T:
+        raise ValueError(f"dest has {Td} rows, x has {T}")
+    rows_out, qc, ldq = _mat(q, "q", 1)
+    if qc != H:
+        raise ValueError(f"q must have {H} columns")
+    _check(lib.fp8_moe_permute_quantize_row(_ptr(x), T, H, ldx, _ptr(dest), k, rows_out, fmt, margin, _ptr(q), ldq,
+                                            _ptr(scale_inv_out), _stream(x)))
+
+
+def fp8_swiglu_quantize_row(h, fmt, margin, q, scale_inv_out):
+    """h bf16 [rows x 2I] (gate | up); q codes [rows x I]; scale_inv_out fp32 [rows]."""
+    rows, two_i, ldh = _bf16(h, "h")
+    if two_i % 2:
+        raise ValueError("h must have an even number of columns (gate | up)")
+    _, _, ldq = _mat(q, "q", 1)
+    _check(lib.fp8_swiglu_quantize_row(_ptr(h), rows, two_i // 2, ldh, fmt, margin, _ptr(q), ldq,
+                                       _ptr(scale_inv_out), _stream(h)))
+
+
+def fp8_moe_unpermute_combine(y, dest, weights, out):
+    """y bf16 [rows x H] in expert order; dest int32 [T x k]; weights fp32 [T x k];
+    out bf16 [T x H]."""
+    rows, H, ldy = _bf16(y, "y")
+    T, k = _i32_2d(dest, "dest")
+    if tuple(weights.shape) != (T, k) or weights.dtype != torch.float32 or not weights.is_contiguous():
+        raise ValueError(f"weights must be a contiguous float32 [{T} x {k}] tensor")
+    To, Ho, ldo = _bf16(out, "out")
+    if (To, Ho) != (T, H):
+        raise ValueError(f"out must be [{T} x {H}]")
+    _check(lib.fp8_moe_unpermute_combine(_ptr(y), rows, H, ldy, _ptr(dest), _ptr(weights), T, k, _ptr(out), ldo,
+                                         _stream(y)))

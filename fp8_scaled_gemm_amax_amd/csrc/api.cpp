@@ -431,4 +431,81 @@ fp8_status_t fp8_grouped_gemm_mx(const uint8_t* a, fp8_format_t fa, int64_t lda,
                     fn);
 }
 
+fp8_status_t fp8_moe_route(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t num_experts,
+                           int64_t* offsets_out, int32_t* dest_out, void* stream) {
+    const char* fn = "fp8_moe_route";
+    if (tokens < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative token count", fn);
+    if (topk < 1 || topk > kMoeMaxTopk) return fail(FP8_ERR_INVALID_ARG, "%s: topk %d outside 1..%d", fn, topk, kMoeMaxTopk);
+    if (num_experts < 1 || num_experts > kMoeMaxExperts)
+        return fail(FP8_ERR_INVALID_ARG, "%s: expert count %d outside 1..%d", fn, num_experts, kMoeMaxExperts);
+    if (tokens * topk >= ((int64_t)1 << 31)) return fail(FP8_ERR_UNSUPPORTED, "%s: 2^31 or more entries", fn);
+    if (!offsets_out || (tokens > 0 && (!expert_idx || !dest_out)))
+        return fail(FP8_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(expert_idx, 4) || !aligned(dest_out, 4) || !aligned(offsets_out, 8))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned pointer", fn);
+    FP8_TRY(check_device());
+    return launched(launch_moe_route(expert_idx, tokens, topk, num_experts, offsets_out, dest_out,
+                                     (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_moe_permute_quantize_row(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ldx,
+                                          const int32_t* dest, int32_t topk, int64_t rows_out, fp8_format_t fmt,
+                                          int32_t margin, uint8_t* q, int64_t ldq, float* scale_inv_out,
+                                          void* stream) {
+    const char* fn = "fp8_moe_permute_quantize_row";
+    FP8_TRY(check_common_quant(fn, x, tokens, cols, ldx, (int)fmt, margin));
+    FP8_TRY(check_matrix(fn, "q", q, rows_out, cols, ldq));
+    if (topk < 1 || topk > kMoeMaxTopk) return fail(FP8_ERR_INVALID_ARG, "%s: topk %d outside 1..%d", fn, topk, kMoeMaxTopk);
+    if (tokens > 0 && cols > 0 && (!dest || !scale_inv_out)) return fail(FP8_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(x, 16) || ldx % 8 != 0 || cols % 8 != 0 || !aligned(q, 8) || ldq % 8 != 0 || !aligned(dest, 4) ||
+        !aligned(scale_inv_out, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: x must be 16-byte aligned with ldx, cols multiples of 8; q 8-byte "
+                    "aligned with ldq a multiple of 8", fn);
+    if (cols > 16384) return fail(FP8_ERR_UNSUPPORTED, "%s: rows longer than 16384 columns", fn);
+    if (tokens >= ((int64_t)1 << 31)) return fail(FP8_ERR_UNSUPPORTED, "%s: 2^31 or more tokens", fn);
+    FP8_TRY(check_device());
+    return launched(launch_moe_permute_quant_row(x, tokens, cols, ldx, dest, topk, rows_out, (int)fmt, margin, q, ldq,
+                                                 scale_inv_out, (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_swiglu_quantize_row(const uint16_t* h, int64_t rows, int64_t inter, int64_t ldh, fp8_format_t fmt,
+                                     int32_t margin, uint8_t* q, int64_t ldq, float* scale_inv_out, void* stream) {
+    const char* fn = "fp8_swiglu_quantize_row";
+    FP8_TRY(check_common_quant(fn, h, rows, 2 * inter, ldh, (int)fmt, margin));
+    FP8_TRY(check_matrix(fn, "q", q, rows, inter, ldq));
+    if (rows > 0 && inter > 0 && !scale_inv_out) return fail(FP8_ERR_INVALID_ARG, "%s: scale_inv_out is NULL", fn);
+    if (!aligned(h, 16) || ldh % 8 != 0 || inter % 8 != 0 || !aligned(q, 8) || ldq % 8 != 0 ||
+        !aligned(scale_inv_out, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: h must be 16-byte aligned with ldh, inter multiples of 8; q 8-byte "
+                    "aligned with ldq a multiple of 8", fn);
+    if (inter > kSwigluMaxChunks * 512)
+        return fail(FP8_ERR_UNSUPPORTED, "%s: intermediate size above %d", fn, kSwigluMaxChunks * 512);
+    if (rows >= ((int64_t)1 << 31)) return fail(FP8_ERR_UNSUPPORTED, "%s: 2^31 or more rows", fn);
+    FP8_TRY(check_device());
+    return launched(launch_swiglu_quant_row(h, rows, inter, ldh, (int)fmt, margin, q, ldq, scale_inv_out,
+                                            (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_moe_unpermute_combine(const uint16_t* y, int64_t rows, int64_t cols, int64_t ldy,
+                                       const int32_t* dest, const float* weights, int64_t tokens, int32_t topk,
+                                       uint16_t* out, int64_t ldo, void* stream) {
+    const char* fn = "fp8_moe_unpermute_combine";
+    FP8_TRY(check_matrix(fn, "y", y, rows, cols, ldy));
+    FP8_TRY(check_matrix(fn, "out", out, tokens, cols, ldo));
+    if (topk < 1 || topk > kMoeMaxTopk) return fail(FP8_ERR_INVALID_ARG, "%s: topk %d outside 1..%d", fn, topk, kMoeMaxTopk);
+    if (tokens > 0 && cols > 0 && (!dest || !weights)) return fail(FP8_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(y, 16) || ldy % 8 != 0 || cols % 8 != 0 || !aligned(out, 16) || ldo % 8 != 0 ||
+        !aligned(dest, 4) || !aligned(weights, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: y and out must be 16-byte aligned with ldy, ldo, cols multiples of 8",
+                    fn);
+    if (tokens >= ((int64_t)1 << 31)) return fail(FP8_ERR_UNSUPPORTED, "%s: 2^31 or more tokens", fn);
+    FP8_TRY(check_device());
+    return launched(launch_moe_unpermute_combine(y, rows, cols, ldy, dest, weights, tokens, topk, out, ldo,
+                                                 (hipStream_t)stream),
+                    fn);
+}
+
 }  // extern "C"

@@ -146,6 +146,14 @@ __device__ __forceinline__ uint32_t pk_fold(uint32_t acc) {
     return lo > hi ? lo : hi;
 }
 
+// Running packed max of the 8 bf16 magnitudes of one 16-byte chunk.
+__device__ __forceinline__ uint32_t word_absmax(uint32_t acc, uint4 v) {
+    acc = pk_absmax(acc, v.x);
+    acc = pk_absmax(acc, v.y);
+    acc = pk_absmax(acc, v.z);
+    return pk_absmax(acc, v.w);
+}
+
 // Wavefront (64 lanes) maximum of an unsigned value; every lane gets the result.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -170,6 +178,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     uint32_t u = __float_as_uint(f);
     uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
     return __builtin_isnan(f) ? ((u >> 16) | 0x40u) : r;
+}
+
+// Eight bf16 values (one 16-byte chunk) times s -> eight codes.
+template <int F, bool NAN_FREE>
+__device__ __forceinline__ uint2 encode8(uint4 v, float s) {
+    uint2 o;
+    o.x = encode4<F, NAN_FREE>(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+    o.y = encode4<F, NAN_FREE>(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
+    return o;
 }
 
 }  // namespace fp8amax

@@ -68,4 +68,24 @@ hipError_t launch_grouped_gemm_mx(const uint8_t* a, int fa, int64_t lda, const u
                                   int64_t total_m, int64_t n, int64_t k, void* d, int out_f32, int64_t ldd,
                                   hipStream_t st);
 
+// MoE layer forward: routing, permutation fused with the rowwise cast, SwiGLU
+// fused with the rowwise cast, weighted combine.
+constexpr int kMoeMaxExperts = 1024;
+constexpr int kMoeMaxTopk = 64;
+constexpr int kSwigluMaxChunks = 8;                  // 16-byte chunks per lane: intermediate size <= 4096
+
+hipError_t launch_moe_route(const int32_t* idx, int64_t tokens, int topk, int num_experts, int64_t* offsets,
+                            int32_t* dest, hipStream_t st);
+
+hipError_t launch_moe_permute_quant_row(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ldx,
+                                        const int32_t* dest, int topk, int64_t rows_out, int fmt, int margin,
+                                        uint8_t* q, int64_t ldq, float* scale_inv, hipStream_t st);
+
+hipError_t launch_swiglu_quant_row(const uint16_t* h, int64_t rows, int64_t inter, int64_t ldh, int fmt, int margin,
+                                   uint8_t* q, int64_t ldq, float* scale_inv, hipStream_t st);
+
+hipError_t launch_moe_unpermute_combine(const uint16_t* y, int64_t rows, int64_t cols, int64_t ldy,
+                                        const int32_t* dest, const float* wts, int64_t tokens, int topk,
+                                        uint16_t* out, int64_t ldo, hipStream_t st);
+
 }  // namespace fp8amax

@@ -28,22 +28,6 @@ __device__ __forceinline__ uint32_t encode1(float v) {
     return encode_sw<F>(v);
 }
 
-__device__ __forceinline__ uint32_t word_absmax(uint32_t acc, uint4 v) {
-    acc = pk_absmax(acc, v.x);
-    acc = pk_absmax(acc, v.y);
-    acc = pk_absmax(acc, v.z);
-    return pk_absmax(acc, v.w);
-}
-
-// Eight bf16 values (one 16-byte chunk) times s -> eight codes.
-template <int F, bool NAN_FREE>
-__device__ __forceinline__ uint2 encode8(uint4 v, float s) {
-    uint2 o;
-    o.x = encode4<F, NAN_FREE>(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
-    o.y = encode4<F, NAN_FREE>(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
-    return o;
-}
-
 // Block-wide max of per-lane magnitude bits (32-bit); result valid in all threads.
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* lds) {
     v = wave_max_u32(v);

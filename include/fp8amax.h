@@ -17,6 +17,9 @@
  *           (rowwise FP8, fused quantization kernels, colwise scales, grouped
  *           GEMM for MoE) and its answers on the wrong-max corruption and on
  *           the non-coalesced colwise-scale writes.
+ *   [Kimbodo] "How PyTorch FP8 Optimizations on AMD GPUs Reduce LLM Cost and
+ *           Scale Training Past 1,000 GPUs": What Happened (per-MoE-layer
+ *           latency).
  *
  * Conventions common to every entry point
  *  - Pointers named x, q, qt, amax*, scale*, history, head, a, b, d and
@@ -318,6 +321,65 @@ fp8_status_t fp8_grouped_gemm_mx(const uint8_t* a, fp8_format_t fa, int64_t lda,
                                  const uint8_t* b_scale, int64_t ld_bs, int64_t b_scale_group_stride,
                                  const int64_t* group_offsets, int32_t g, int64_t total_m, int64_t n, int64_t k,
                                  void* d, fp8_out_t d_type, int64_t ldd, void* stream);
+
+/* -------------------------------------------------------- MoE layer forward --
+ * The MoE layer around its two grouped GEMMs ([Kimbodo] What Happened: the
+ * per-MoE-layer latency; [Titan] fused quantization kernels, FP8 grouped GEMM
+ * for MoE). The pages do not define the layer; the reading is the plain top-k
+ * MoE feed-forward layer: token t goes to the experts expert_idx[t, 0..k-1];
+ * expert e applies y = down( silu(x gate_e^T) * (x up_e^T) ); the k results are
+ * summed with the router's weights. The forward, all on the device:
+ *   fp8_moe_route                  -> expert offsets and each entry's row
+ *   fp8_moe_permute_quantize_row   -> tokens cast rowwise into expert order
+ *   fp8_grouped_gemm_scaled        -> h = [gate | up] per expert (bf16)
+ *   fp8_swiglu_quantize_row        -> silu(gate) * up cast rowwise
+ *   fp8_grouped_gemm_scaled        -> expert outputs in expert order (bf16)
+ *   fp8_moe_unpermute_combine      -> weighted sum back in token order
+ * An "entry" is a (token, slot) pair, numbered t * topk + j. */
+
+/* Routing: expert_idx int32 [tokens x topk] (device). A stable counting sort of
+ * the entries by expert: offsets_out int64 [num_experts + 1] (expert e owns
+ * rows offsets[e] .. offsets[e+1]-1), dest_out int32 [tokens x topk] = the row
+ * of each entry, entries of one expert in entry order (deterministic). An
+ * index outside [0, num_experts) drops its entry: dest = -1, not counted.
+ * Limits: topk 1..64, num_experts 1..1024, tokens * topk < 2^31. One
+ * workgroup: meant for the per-GPU token counts of a layer (tens of thousands
+ * of entries). */
+fp8_status_t fp8_moe_route(const int32_t* expert_idx, int64_t tokens, int32_t topk, int32_t num_experts,
+                           int64_t* offsets_out, int32_t* dest_out, void* stream);
+
+/* Permutation fused with the rowwise cast: token t of x bf16 [tokens x cols]
+ * (ldx) is quantized once (as fp8_quantize_row) and its codes and scale_inv
+ * written to rows dest[t * topk + j] (j < topk) of q [rows_out x cols] (ldq)
+ * and scale_inv_out [rows_out]. Destinations outside [0, rows_out) are
+ * skipped. Requirements: x 16-byte aligned, ldx and cols multiples of 8,
+ * cols <= 16384 (else FP8_ERR_UNSUPPORTED); q 8-byte aligned, ldq % 8 == 0;
+ * margin 0..32. */
+fp8_status_t fp8_moe_permute_quantize_row(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ldx,
+                                          const int32_t* dest, int32_t topk, int64_t rows_out, fp8_format_t fmt,
+                                          int32_t margin, uint8_t* q, int64_t ldq, float* scale_inv_out,
+                                          void* stream);
+
+/* SwiGLU fused with the rowwise cast: row r of h bf16 [rows x 2 inter] (ldh)
+ * holds gate (columns 0 .. inter-1) and up (inter .. 2 inter-1);
+ * a = silu(gate) * up = gate / (1 + exp(-gate)) * up in fp32, then per row
+ * s from max |a| (the current-scaling rule), q[r] = cast(a * s),
+ * scale_inv_out[r] = 1 / s. q: codes [rows x inter] (ldq). Requirements: h
+ * 16-byte aligned, ldh and inter multiples of 8, inter <= 4096 (else
+ * FP8_ERR_UNSUPPORTED); q 8-byte aligned, ldq % 8 == 0. */
+fp8_status_t fp8_swiglu_quantize_row(const uint16_t* h, int64_t rows, int64_t inter, int64_t ldh, fp8_format_t fmt,
+                                     int32_t margin, uint8_t* q, int64_t ldq, float* scale_inv_out, void* stream);
+
+/* Weighted combine back to token order:
+ *   out[t] = bf16( sum over j = 0 .. topk-1, in that order, of
+ *                  weights[t * topk + j] * y[dest[t * topk + j]] )
+ * with fp32 accumulation; y bf16 [rows x cols] (ldy) in expert order, out bf16
+ * [tokens x cols] (ldo); slots whose destination is outside [0, rows) add
+ * nothing. Requirements: y and out 16-byte aligned, ldy, ldo and cols
+ * multiples of 8. */
+fp8_status_t fp8_moe_unpermute_combine(const uint16_t* y, int64_t rows, int64_t cols, int64_t ldy,
+                                       const int32_t* dest, const float* weights, int64_t tokens, int32_t topk,
+                                       uint16_t* out, int64_t ldo, void* stream);
 
 #ifdef __cplusplus
 }

@@ -455,20 +455,23 @@ def moe_route(expert_idx, num_experts):
     """expert_idx int [T x k] -> (offsets int64 [E+1], dest int32 [T x k]):
     a counting sort of the T*k (token, slot) entries by expert, stable in
     (token, slot) order. dest[t, j] is the row of entry (t, j) in the
-    expert-sorted order; expert e owns rows offsets[e] .. offsets[e+1]-1."""
+    expert-sorted order; expert e owns rows offsets[e] .. offsets[e+1]-1. An
+    index outside [0, E) drops its entry (dest -1, not counted)."""
     idx = np.asarray(expert_idx, np.int64)
     T, k = idx.shape
     flat = idx.reshape(-1)
     counts = np.zeros(num_experts, np.int64)
     for e in flat:                                      # histogram
-        counts[e] += 1
+        if 0 <= e < num_experts:
+            counts[e] += 1
     offsets = np.zeros(num_experts + 1, np.int64)
     offsets[1:] = np.cumsum(counts)
     nxt = offsets[:-1].copy()                           # next free row of each expert
-    dest = np.empty(flat.size, np.int64)
+    dest = np.full(flat.size, -1, np.int64)
     for i, e in enumerate(flat):                        # entries in (token, slot) order
-        dest[i] = nxt[e]
-        nxt[e] += 1
+        if 0 <= e < num_experts:
+            dest[i] = nxt[e]
+            nxt[e] += 1
     return offsets, dest.reshape(T, k).astype(np.int32)
 
 
@@ -482,8 +485,9 @@ def moe_permute_quantize_row(x_bf16, dest, fmt, margin=0):
     si = np.empty(T * k, np.float32)
     for t in range(T):
         for j in range(k):
-            q[dest[t, j]] = q_tok[t]
-            si[dest[t, j]] = si_tok[t]
+            if dest[t, j] >= 0:
+                q[dest[t, j]] = q_tok[t]
+                si[dest[t, j]] = si_tok[t]
     return q, si
 
 
@@ -515,7 +519,8 @@ def swiglu_quantize_row(h_bf16, fmt, margin=0):
 
 def moe_unpermute_combine(y_bf16, dest, weights):
     """out[t] = sum over slots j of weights[t, j] * y[dest[t, j]] in fp64
-    (returned unrounded, with the sum of magnitudes as the bound's base)."""
+    (returned unrounded, with the sum of magnitudes as the bound's base);
+    slots whose destination is outside y's rows add nothing."""
     y = bf16_to_f64(y_bf16)
     dest = np.asarray(dest, np.int64)
     w = np.asarray(weights, np.float64)
@@ -523,8 +528,10 @@ def moe_unpermute_combine(y_bf16, dest, weights):
     out = np.zeros((T, y.shape[1]))
     mag = np.zeros((T, y.shape[1]))
     for j in range(k):
-        out += w[:, j:j + 1] * y[dest[:, j]]
-        mag += np.abs(w[:, j:j + 1] * y[dest[:, j]])
+        ok = (dest[:, j] >= 0) & (dest[:, j] < y.shape[0])
+        term = np.where(ok[:, None], w[:, j:j + 1] * y[np.where(ok, dest[:, j], 0)], 0.0)
+        out += term
+        mag += np.abs(term)
     return out, mag
 
 

@@ -250,3 +250,45 @@ def test_mx_entry_points_reject_bad_arguments(fp8):
     bad = list(ok_gg)
     bad[12] = None                           # no offsets
     assert _call(fp8, gg, *bad)[0] == 1
+
+
+def test_moe_layer_entry_points_reject_bad_arguments(fp8):
+    r = "fp8_moe_route"
+    ok_r = [FAKE, 100, 8, 32, FAKE, FAKE, None]
+    for i, v, st in ((2, 0, 1), (2, 65, 1), (3, 0, 1), (3, 1025, 1), (1, -1, 1), (4, None, 1),
+                     (4, ctypes.c_void_p(0x10004), 2), (5, ctypes.c_void_p(0x10002), 2)):
+        bad = list(ok_r)
+        bad[i] = v
+        assert _call(fp8, r, *bad)[0] == st, (i, v)
+    bad = list(ok_r)
+    bad[1], bad[2] = 1 << 30, 2               # 2^31 entries
+    assert _call(fp8, r, *bad)[0] == 3
+    p = "fp8_moe_permute_quantize_row"
+    # x [100 x 64], dest [100 x 8], q [800 x 64]
+    ok_p = [FAKE, 100, 64, 64, FAKE, 8, 800, 0, 0, FAKE, 64, FAKE, None]
+    for i, v, st in ((5, 0, 1), (8, 33, 1), (7, 9, 1), (10, 32, 1), (4, None, 1), (11, None, 1),
+                     (9, ctypes.c_void_p(0x10004), 2), (0, ctypes.c_void_p(0x10008), 2)):
+        bad = list(ok_p)
+        bad[i] = v
+        assert _call(fp8, p, *bad)[0] == st, (i, v)
+    bad = list(ok_p)
+    bad[2], bad[3], bad[10] = 16392, 16392, 16392          # rows longer than 16384
+    assert _call(fp8, p, *bad)[0] == 3
+    s = "fp8_swiglu_quantize_row"
+    # h [64 x 2*256], q [64 x 256]
+    ok_s = [FAKE, 64, 256, 512, 0, 0, FAKE, 256, FAKE, None]
+    for i, v, st in ((3, 256, 1), (8, None, 1), (2, 252, 2), (6, ctypes.c_void_p(0x10004), 2), (4, 7, 1)):
+        bad = list(ok_s)
+        bad[i] = v
+        assert _call(fp8, s, *bad)[0] == st, (i, v)
+    bad = list(ok_s)
+    bad[2], bad[3], bad[7] = 4104, 8208, 4104              # intermediate size above 4096
+    assert _call(fp8, s, *bad)[0] == 3
+    c = "fp8_moe_unpermute_combine"
+    # y [800 x 64], dest / weights [100 x 8], out [100 x 64]
+    ok_c = [FAKE, 800, 64, 64, FAKE, FAKE, 100, 8, FAKE, 64, None]
+    for i, v, st in ((7, 0, 1), (4, None, 1), (5, None, 1), (9, 32, 1), (8, ctypes.c_void_p(0x10008), 2),
+                     (2, 60, 2)):
+        bad = list(ok_c)
+        bad[i] = v
+        assert _call(fp8, c, *bad)[0] == st, (i, v)

@@ -15,7 +15,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-Xc
          "-Xclang", "-packed-fp32-ops", "--cuda-device-only", "-S", "-o", "-"]
 
 
-@pytest.fixture(scope="module", params=["gemm.hip", "quant.hip"])
+@pytest.fixture(scope="module", params=["gemm.hip", "quant.hip", "moe.hip"])
 def asm(request):
     out = subprocess.run(["/opt/rocm/bin/hipcc", *FLAGS, os.path.join(CSRC, request.param)], capture_output=True,
                          text=True)

@@ -16,6 +16,13 @@ def test_route_hand_example(orc):
     assert dest.tolist() == [[1, 4], [2, 0], [5, 3]]
 
 
+def test_route_drops_out_of_range_indices(orc):
+    """Indices -1 and E drop their entries: dest -1, the rest as if absent."""
+    offsets, dest = orc.moe_route(np.array([[1, -1], [4, 0], [1, 1]]), 4)
+    assert list(offsets) == [0, 1, 4, 4, 4]
+    assert dest.tolist() == [[1, -1], [-1, 0], [2, 3]]
+
+
 def test_route_matches_a_stable_sort(orc):
     rng = np.random.default_rng(3)
     T, k, E = 300, 6, 20

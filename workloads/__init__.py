@@ -20,6 +20,11 @@ Workloads (full sizes; every function accepts smaller shapes for tests):
       tokens [16384 x 7168] ~ N(0,1) sorted by expert,
       W_e [32 x 2048 x 7168] ~ N(0, 0.006^2)
   c5  backward of c2: c2's X and W, then dY [8192 x 14336] ~ N(0, 1e-3^2)
+  c6  DeepSeek-V3 MoE layer forward, one GPU's share: 2048 tokens
+      [2048 x 7168] ~ N(0,1), each routed to 8 of 32 experts (Zipf(1.1)
+      popularity, drawn without replacement), router weights a softmax of
+      N(0,1) logits over the 8; per expert gate|up W1 [4096 x 7168] and down
+      W2 [7168 x 2048], both ~ N(0, 0.006^2)
 """
 import numpy as np
 
@@ -131,3 +136,30 @@ def c5(m=8192, n=14336, k=4096, seed=0):
     d = _c2_draw(rng, m, n, k)
     d["dy"] = bf16_bits(_normal(rng, (m, n), 1e-3))
     return d
+
+
+def topk_routing(rng, tokens, experts, topk, exponent=1.1):
+    """Expert choices per token, distinct, drawn without replacement with
+    Zipf(exponent) popularity (a random rank per expert; Gumbel top-k over
+    log-probabilities), and router weights: a softmax over topk N(0,1) logits.
+    Returns (idx int32 [tokens x topk], weights float32 [tokens x topk])."""
+    ranks = rng.permutation(experts)
+    logp = -exponent * np.log(ranks + 1.0)
+    keys = logp[None, :] + rng.gumbel(size=(tokens, experts))
+    idx = np.argsort(-keys, axis=1, kind="stable")[:, :topk].astype(np.int32)
+    logits = rng.standard_normal((tokens, topk))
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    return idx, w.astype(np.float32)
+
+
+def c6(tokens=2048, experts=32, topk=8, hidden=7168, inter=2048, seed=0):
+    """MoE layer forward. Returns dict(x [tokens x hidden], idx, weights
+    [tokens x topk], w1 [experts x 2 inter x hidden] (gate rows, then up rows),
+    w2 [experts x hidden x inter])."""
+    rng = np.random.default_rng(seed)
+    idx, weights = topk_routing(rng, tokens, experts, topk)
+    x = bf16_bits(_normal(rng, (tokens, hidden)))
+    w1 = bf16_bits(_normal(rng, (experts, 2 * inter, hidden), 0.006))
+    w2 = bf16_bits(_normal(rng, (experts, hidden, inter), 0.006))
+    return {"x": x, "idx": idx, "weights": weights, "w1": w1, "w2": w2}
