@@ -25,63 +25,88 @@ constexpr int kWaves = kBlock / 64;
 // ---------------------------------------------------------------- routing --
 // One workgroup of 16 wavefronts walks the T*k entries in chunks of 1024, in
 // (token, slot) order. Within a wavefront, entries of one expert get their
-// rank by ballots (one round per distinct expert present); a wavefront's
-// per-expert counts go to LDS, and an entry's row within its expert is the
-// running count of earlier chunks + the counts of earlier wavefronts + its
-// rank: the stable counting sort, deterministic. The expert offsets are the
-// exclusive scan of the totals; a second pass adds them. Entries whose expert
-// index is outside [0, E) get dest = -1 and are not counted.
+// rank by ballots (one round per distinct expert present) and the leader
+// writes the wavefront's count of that expert to LDS; then one thread per
+// expert turns the 16 wavefronts' counts into running offsets (earlier chunks
+// + earlier wavefronts), so an entry's row within its expert is one LDS read
+// + its rank: the stable counting sort, deterministic. The counts are double
+// buffered (the expert threads clear the other buffer), so a chunk costs two
+// barriers. The expert offsets are the exclusive scan of the totals. Entries
+// are read in batches of 16 chunks held in registers (all loads of a batch in
+// flight at once); when everything fits one batch, the rows are completed in
+// registers and written once, else each batch writes its rows within the
+// expert and a last pass adds the offsets. Entries whose expert index is
+// outside [0, E) get dest = -1, not counted.
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteBatch = 16;                             // chunks per batch
+constexpr int64_t kRouteBatchEntries = (int64_t)kRouteThreads * kRouteBatch;
 
 __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t* __restrict__ idx, int64_t n, int E,
                                                                int64_t* __restrict__ offsets,
                                                                int32_t* __restrict__ dest) {
-    __shared__ int32_t run[kMoeMaxExperts];                 // entries of each expert in earlier chunks
-    __shared__ int32_t wcnt[kRouteWaves][kMoeMaxExperts];   // this chunk's count per wavefront and expert
+    __shared__ int32_t run[kMoeMaxExperts];                      // entries of each expert in earlier chunks
+    __shared__ int32_t wcnt[2][kRouteWaves][kMoeMaxExperts];     // per wavefront: count, then running offset
     __shared__ int32_t wsum[kRouteWaves];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     for (int e = tid; e < E; e += kRouteThreads) {
         run[e] = 0;
 #pragma unroll
-        for (int v = 0; v < kRouteWaves; ++v) wcnt[v][e] = 0;
+        for (int v = 0; v < kRouteWaves; ++v) wcnt[0][v][e] = wcnt[1][v][e] = 0;
     }
     __syncthreads();
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int64_t c0 = 0; c0 < n; c0 += kRouteThreads) {
-        const int64_t i = c0 + tid;
-        int e = i < n ? idx[i] : -1;
-        if (e < 0 || e >= E) e = -1;
-        uint64_t pending = __ballot(e >= 0);
-        int rank = 0;
-        while (pending) {                                   // uniform over the wavefront
-            const int leader = __ffsll((unsigned long long)pending) - 1;
-            const int e0 = __shfl(e, leader);
-            const uint64_t m = __ballot(e == e0);
-            if (e == e0) rank = __popcll(m & below);
-            if (lane == leader) wcnt[w][e0] = __popcll(m);
-            pending &= ~m;
-        }
-        __syncthreads();
-        if (e >= 0) {
-            int before = run[e];
-            for (int v = 0; v < w; ++v) before += wcnt[v][e];
-            dest[i] = before + rank;                        // row within the expert; offsets added below
-        } else if (i < n) {
-            dest[i] = -1;
-        }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += kRouteThreads) {
-            int s = 0;
+    const bool one_batch = n <= kRouteBatchEntries;
+    int ev[kRouteBatch], pos[kRouteBatch];
+    int buf = 0;
+    for (int64_t b0 = 0; b0 < n; b0 += kRouteBatchEntries) {
 #pragma unroll
-            for (int v = 0; v < kRouteWaves; ++v) {
-                s += wcnt[v][ee];
-                wcnt[v][ee] = 0;
-            }
-            run[ee] += s;
+        for (int c = 0; c < kRouteBatch; ++c) {
+            const int64_t i = b0 + (int64_t)c * kRouteThreads + tid;
+            const int e = i < n ? idx[i] : -1;
+            ev[c] = (e >= 0 && e < E) ? e : -1;
         }
-        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < kRouteBatch; ++c) {
+            int32_t(*cnt)[kMoeMaxExperts] = wcnt[buf];
+            const int e = ev[c];
+            uint64_t pending = __ballot(e >= 0);
+            int rank = 0;
+            while (pending) {                                    // uniform over the wavefront
+                const int leader = __ffsll((unsigned long long)pending) - 1;
+                const int e0 = __builtin_amdgcn_readlane(e, leader);
+                const uint64_t m = __ballot(e == e0);
+                if (e == e0) rank = __popcll(m & below);
+                if (lane == leader) cnt[w][e0] = __popcll(m);
+                pending &= ~m;
+            }
+            __syncthreads();
+            for (int ee = tid; ee < E; ee += kRouteThreads) {   // counts -> running offsets
+                int c16[kRouteWaves];
+#pragma unroll
+                for (int v = 0; v < kRouteWaves; ++v) c16[v] = cnt[v][ee];
+                int acc = run[ee];
+#pragma unroll
+                for (int v = 0; v < kRouteWaves; ++v) {
+                    cnt[v][ee] = acc;
+                    acc += c16[v];
+                    wcnt[buf ^ 1][v][ee] = 0;
+                }
+                run[ee] = acc;
+            }
+            __syncthreads();
+            pos[c] = e >= 0 ? cnt[w][e] + rank : -1;             // row within the expert
+            buf ^= 1;
+        }
+        if (!one_batch) {
+#pragma unroll
+            for (int c = 0; c < kRouteBatch; ++c) {
+                const int64_t i = b0 + (int64_t)c * kRouteThreads + tid;
+                if (i < n) dest[i] = pos[c];
+            }
+        }
     }
+    __syncthreads();                                             // (every pos read done before pre reuses LDS)
     // exclusive scan of run[0 .. E) (E <= 1024: one expert per thread)
     const int mine = tid < E ? run[tid] : 0;
     int incl = mine;
@@ -94,16 +119,21 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t* __re
     __syncthreads();
     int excl = incl - mine;
     for (int v = 0; v < w; ++v) excl += wsum[v];
-    int32_t* pre = &wcnt[0][0];                             // (the counts are dead)
+    int32_t* pre = &wcnt[0][0][0];                          // (the counts are dead)
     if (tid < E) {
         pre[tid] = excl;
         offsets[tid] = excl;
     }
     if (tid == E - 1) offsets[E] = excl + mine;
     __syncthreads();
-    for (int64_t c0 = 0; c0 < n; c0 += kRouteThreads) {
-        const int64_t i = c0 + tid;
-        if (i < n) {
+    if (one_batch) {
+#pragma unroll
+        for (int c = 0; c < kRouteBatch; ++c) {
+            const int64_t i = (int64_t)c * kRouteThreads + tid;
+            if (i < n) dest[i] = ev[c] >= 0 ? pre[ev[c]] + pos[c] : -1;
+        }
+    } else {
+        for (int64_t i = tid; i < n; i += kRouteThreads) {
             const int e = idx[i];
             if (e >= 0 && e < E) dest[i] += pre[e];
         }

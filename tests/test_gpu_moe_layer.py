@@ -32,14 +32,14 @@ def gpu_route(fp8, idx, E):
     return off.cpu().numpy(), dest.cpu().numpy()
 
 
-ROUTES = [(2048, 8, 32, 0), (1, 1, 1, 1), (3000, 4, 1024, 2), (5000, 2, 3, 3), (700, 6, 64, 4)]
+ROUTES = [(2048, 8, 32, 0), (1, 1, 1, 1), (3000, 4, 1024, 2), (5000, 2, 3, 3), (700, 6, 64, 4), (9000, 4, 16, 5)]
 
 
 @pytest.mark.parametrize("T,k,E,seed", ROUTES)
 def test_route_parity(fp8, orc, T, k, E, seed):
     """Zipf top-k routing (distinct experts per token), one expert, 1024
-    experts, more entries than one chunk per expert, and -1 / E indices that
-    drop their entries."""
+    experts, more entries than one chunk per expert, -1 / E indices that drop
+    their entries, and more entries than one register batch (36000)."""
     rng = np.random.default_rng(seed)
     if k <= E:
         idx, _ = workloads.topk_routing(rng, T, E, k)
