@@ -556,3 +556,88 @@ def bf16_round(x):
     r = ((u64 + 0x7FFF + ((u64 >> 16) & 1)) >> 16).astype(np.uint16)
     r[np.isnan(x)] = 0x7FC0
     return r
+
+
+# ------------------------------------------------------------------- blockwise --
+# The blockwise recipe ("FP8 training for Flux models", Configuration: blockwise
+# among the recipes; no block shapes or scale rule on the pages). Reading used
+# here: tiles of 1 x 128 along K for activations and gradients and 128 x 128 for
+# weights share one scale; the scale is the current-scaling rule's fmax / amax
+# (with its zero / non-finite / overflow conventions, no margin) rounded down
+# to a power of two, so that no element saturates and the block scale is exact
+# as a power of two. Stored as the E8M0 byte of the dequantization factor
+# 1 / s (= 127 - log2 s, within 0 .. 247); codes are cast(x * s).
+BLOCK = 128
+
+
+def pow2_scale(fmt, amax):
+    """The block scale: the current-scaling scale rounded down to a power of two."""
+    s = float(scale_current(fmt, amax, 0))
+    return 2.0 ** np.floor(np.log2(s))
+
+
+def _block_codes(xv_bits, fmt, s):
+    """Cast of a block of bf16 values at scale s (fp32 product, then the
+    saturating RNE cast)."""
+    vals = (np.asarray(xv_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return encode(fmt, vals * np.float32(s))
+
+
+def blockwise_quantize_act(x_bf16, fmt):
+    """1 x 128 blocks: returns (q [rows x K], e8 bytes [rows x K/128])."""
+    x = np.asarray(x_bf16, np.uint16)
+    rows, K = x.shape
+    assert K % BLOCK == 0
+    q = np.empty((rows, K), np.uint8)
+    e8 = np.empty((rows, K // BLOCK), np.uint8)
+    for r in range(rows):
+        for b in range(K // BLOCK):
+            blk = x[r, b * BLOCK:(b + 1) * BLOCK]
+            am = amax(blk[None, :], AXIS_TENSOR)[0]
+            s = pow2_scale(fmt, am)
+            q[r, b * BLOCK:(b + 1) * BLOCK] = _block_codes(blk, fmt, s)
+            e8[r, b] = 127 - int(np.log2(s))
+    return q, e8
+
+
+def blockwise_quantize_weight(w_bf16, fmt):
+    """128 x 128 tiles (the last row tile may be shorter): returns
+    (q [n x K], e8 bytes [ceil(n/128) x K/128])."""
+    w = np.asarray(w_bf16, np.uint16)
+    n, K = w.shape
+    assert K % BLOCK == 0
+    nt = (n + BLOCK - 1) // BLOCK
+    q = np.empty((n, K), np.uint8)
+    e8 = np.empty((nt, K // BLOCK), np.uint8)
+    for t in range(nt):
+        r0, r1 = t * BLOCK, min(n, (t + 1) * BLOCK)
+        for b in range(K // BLOCK):
+            tile = np.ascontiguousarray(w[r0:r1, b * BLOCK:(b + 1) * BLOCK])
+            am = amax(tile.reshape(1, -1), AXIS_TENSOR)[0]
+            s = pow2_scale(fmt, am)
+            q[r0:r1, b * BLOCK:(b + 1) * BLOCK] = _block_codes(tile, fmt, s)
+            e8[t, b] = 127 - int(np.log2(s))
+    return q, e8
+
+
+def blockwise_gemm(a, fa, ea, b, fb, eb_tiles):
+    """Y = sum over 128-deep K blocks kb of 2^(ea[i,kb]-127) 2^(eb[j//128,kb]-127)
+    * sum_{k in kb} dec(a_ik) dec(b_jk), fp64. Returns (y, bound)."""
+    a = np.asarray(a, np.uint8)
+    b = np.asarray(b, np.uint8)
+    m, K = a.shape
+    n = b.shape[0]
+    nb = K // BLOCK
+    ad = decode(fa, a).reshape(m, nb, BLOCK)
+    bd = decode(fb, b).reshape(n, nb, BLOCK)
+    xa = np.exp2(np.asarray(ea, np.float64) - 127.0)                       # [m x nb]
+    xb = np.exp2(np.asarray(eb_tiles, np.float64) - 127.0)[np.arange(n) // BLOCK]   # [n x nb]
+    y = np.zeros((m, n))
+    bound = np.zeros((m, n))
+    for kb in range(nb):
+        p = ad[:, kb, :] @ bd[:, kb, :].T
+        pm = np.abs(ad[:, kb, :]) @ np.abs(bd[:, kb, :]).T
+        x = xa[:, kb:kb + 1] * xb[None, :, kb]
+        y += x * p
+        bound += x * pm
+    return y, bound
