@@ -18,7 +18,9 @@ Other workloads (--workload c1|c3|c4|c4b|c4mx|c5) print the same line for the
 other shapes (c3 tensorwise delayed, c4 MoE grouped GEMM, c4b the MoE expert
 layer's backward, c4mx c4 with MXFP8 block-32 E8M0 scales, c5 hybrid
 backward, c6 the DeepSeek-V3 MoE layer forward: route, permute + cast,
-gate|up grouped GEMM, SwiGLU + cast, down grouped GEMM, weighted combine).
+gate|up grouped GEMM, SwiGLU + cast, down grouped GEMM, weighted combine;
+c2bw c2's tensors with the blockwise recipe: 1 x 128 activation blocks,
+128 x 128 weight tiles, power-of-two scales, the product on the MX kernel).
 """
 import argparse
 import json
@@ -41,7 +43,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c4b", "c4mx", "c5", "c6"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2bw", "c3", "c4", "c4b", "c4mx", "c5", "c6"])
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -82,6 +84,23 @@ class Step:
                          "c2": "Llama3-8B FFN up-proj rowwise FP8: X bf16 [8192x4096] Student-t(4)/sqrt(2), "
                                "W bf16 [14336x4096] N(0,0.02^2); e4m3 row/col scales; bf16 out"}[name]
             self.scales = {"recipe": "rowwise", "format": "e4m3"}
+        elif name == "c2bw":
+            w = workloads.c2()
+            self.x, self.w = bf16_dev(w["x"]), bf16_dev(w["w"])
+            self.cpu_sample = (w["x"], 0, w["w"], 0)
+            self.cpu_kind = "blockwise"
+            m, k = self.x.shape
+            n = self.w.shape[0]
+            self.qx, self.qw = E((m, k), dtype=torch.uint8, device=dev), E((n, k), dtype=torch.uint8, device=dev)
+            self.sx, self.sw = fp8.mx_scale_records(m, k), fp8.mx_scale_records(n, k)
+            self.d = E((m, n), dtype=torch.bfloat16, device=dev)
+            self.mnk = [(m, n, k)]
+            # (4-byte scale records: one per row per 128 columns)
+            self.calls = [("blockwise_quantize_act X", m * k, m * k // 128),
+                          ("blockwise_quantize_weight W", n * k, n * k // 128), ("gemm_mx", None, 0)]
+            self.desc = ("Llama3-8B FFN up-proj, blockwise FP8: c2's X bf16 [8192x4096] and W bf16 [14336x4096]; "
+                         "e4m3, 1x128 activation blocks, 128x128 weight tiles, power-of-two scales; bf16 out")
+            self.scales = {"recipe": "blockwise", "format": "e4m3"}
         elif name == "c3":
             w = workloads.c3()
             self.w = bf16_dev(w["w"])
@@ -244,6 +263,13 @@ class Step:
             f.fp8_gemm_scaled(self.qx, f.E4M3, self.qw, f.E4M3, self.sx, f.SCALE_VECTOR, self.sw, f.SCALE_VECTOR,
                               self.d)
             ev[3].record()
+        elif self.name == "c2bw":
+            f.fp8_blockwise_quantize_act(self.x, f.E4M3, self.qx, self.sx)
+            ev[1].record()
+            f.fp8_blockwise_quantize_weight(self.w, f.E4M3, self.qw, self.sw)
+            ev[2].record()
+            f.fp8_gemm_mx(self.qx, f.E4M3, self.sx, self.qw, f.E4M3, self.sw, self.d)
+            ev[3].record()
         elif self.name == "c3":
             f.fp8_quantize_tensor(self.x, f.E4M3, 0, self.scale[0:1], self.qx, self.six, self.cur[0:1])
             ev[1].record()
@@ -384,6 +410,10 @@ def cpu_baseline(sample, target_s, kind="rowwise"):
             qx, sx = orc.mx_quantize_row(act[:ms], fa)
             qw, sw = orc.mx_quantize_row(wgt[:ns], fw)
             orc.mx_gemm(qx, fa, sx, qw, fw, sw)
+        elif kind == "blockwise":
+            qx, ex = orc.blockwise_quantize_act(act[:ms], fa)
+            qw, ew = orc.blockwise_quantize_weight(wgt[:ns], fw)
+            orc.blockwise_gemm(qx, fa, ex, qw, fw, ew)
         else:
             qx, sx, _ = orc.quantize_row(act[:ms], fa)
             qw, sw, _ = orc.quantize_row(wgt[:ns], fw)
@@ -397,10 +427,14 @@ def cpu_baseline(sample, target_s, kind="rowwise"):
         ns = int(min(wgt.shape[0], max(ns, pairs / ms)))
         ms = int(min(act.shape[0], max(ms, pairs / ns)))
         t = run(ms, ns)
+    if t < 0.5 * target_s and ms < act.shape[0]:     # (per-row costs dominate: grow the activation rows)
+        ms = int(min(act.shape[0], ms * target_s / t))
+        t = run(ms, ns)
     return {"value": round(2.0 * ms * ns * k / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{ms} activation rows x {ns} weight rows x K={k} of the workload's tensors: "
-                      f"{'MX block-32' if kind == 'mx' else 'rowwise'} quantize of both (oracle) + fp64 "
+                      f"{ {'mx': 'MX block-32', 'blockwise': 'blockwise'}.get(kind, 'rowwise') } quantize of both "
+                      f"(oracle) + fp64 "
                       f"dequantize-and-matmul, {t:.1f} s on {threads} threads"}
 
 
@@ -471,7 +505,7 @@ def main():
     gemm_flops = 2.0 * np.prod(step.mnk[0])
     gemm_tflops = gemm_flops / (per_call_ms[g] * 1e-3) / 1e12
     kernel_key = {"c4": "grouped_gemm", "c4b": "grouped_gemm", "c4mx": "grouped_gemm_mx",
-                  "c6": "grouped_gemm"}.get(args.workload, "gemm")
+                  "c6": "grouped_gemm", "c2bw": "gemm_mx"}.get(args.workload, "gemm")
     traffic = measured_traffic(f"{kernel_key}:{args.workload}")
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,

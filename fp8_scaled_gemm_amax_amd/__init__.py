@@ -22,7 +22,8 @@ __all__ = [
     "fp8_gemm_scaled", "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "grouped_layout_width", "GROUP_K_ALIGN", "MX_BLOCK", "fp8_mx_quantize_row", "fp8_gemm_mx",
     "fp8_grouped_gemm_mx", "mx_scale_records", "fp8_moe_route", "fp8_moe_permute_quantize_row",
-    "fp8_swiglu_quantize_row", "fp8_moe_unpermute_combine", "EXPORTED_SYMBOLS",
+    "fp8_swiglu_quantize_row", "fp8_moe_unpermute_combine", "fp8_blockwise_quantize_act",
+    "fp8_blockwise_quantize_weight", "EXPORTED_SYMBOLS",
 ]
 
 E4M3, E5M2, E4M3_FNUZ, E5M2_FNUZ = 0, 1, 2, 3
@@ -36,7 +37,8 @@ EXPORTED_SYMBOLS = (
     "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update", "fp8_gemm_scaled",
     "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "fp8_mx_quantize_row", "fp8_gemm_mx", "fp8_grouped_gemm_mx", "fp8_moe_route", "fp8_moe_permute_quantize_row",
-    "fp8_swiglu_quantize_row", "fp8_moe_unpermute_combine",
+    "fp8_swiglu_quantize_row", "fp8_moe_unpermute_combine", "fp8_blockwise_quantize_act",
+    "fp8_blockwise_quantize_weight",
 )
 
 GROUP_K_ALIGN = 256     # FP8_GROUP_K_ALIGN of the C header
@@ -78,6 +80,8 @@ def _load():
         "fp8_gemm_mx": [P, I, I64, P, I64, P, I, I64, P, I64, I64, I64, I64, P, I, I64, P],
         "fp8_grouped_gemm_mx": [P, I, I64, P, I64, P, I, I64, I64, P, I64, I64, P, I32, I64, I64, I64, P, I, I64, P],
         "fp8_moe_route": [P, I64, I32, I32, P, P, P],
+        "fp8_blockwise_quantize_act": [P, I64, I64, I64, I, P, I64, P, I64, P],
+        "fp8_blockwise_quantize_weight": [P, I64, I64, I64, I, P, I64, P, I64, P],
         "fp8_moe_permute_quantize_row": [P, I64, I64, I64, P, I32, I64, I, I32, P, I64, P, P],
         "fp8_swiglu_quantize_row": [P, I64, I64, I64, I, I32, P, I64, P, P],
         "fp8_moe_unpermute_combine": [P, I64, I64, I64, P, P, I64, I32, P, I64, P],
@@ -368,3 +372,23 @@ def fp8_moe_unpermute_combine(y, dest, weights, out):
         raise ValueError(f"out must be [{T} x {H}]")
     _check(lib.fp8_moe_unpermute_combine(_ptr(y), rows, H, ldy, _ptr(dest), _ptr(weights), T, k, _ptr(out), ldo,
                                          _stream(y)))
+
+
+def _blockwise(fn, x, fmt, q, scale_records):
+    rows, cols, ldx = _bf16(x)
+    _, _, ldq = _mat(q, "q", 1)
+    J, r, lds = _records(scale_records, "scale_records")
+    if r != rows or J != (cols + 127) // 128:
+        raise ValueError(f"scale_records must be [{(cols + 127) // 128} x {rows} x 4]")
+    _check(fn(_ptr(x), rows, cols, ldx, fmt, _ptr(q), ldq, _ptr(scale_records), lds, _stream(x)))
+
+
+def fp8_blockwise_quantize_act(x, fmt, q, scale_records):
+    """1 x 128 blocks: x bf16 [rows x cols] (cols % 128 == 0); q codes; scale
+    records uint8 [cols/128 x rows x 4] (mx_scale_records), for fp8_gemm_mx."""
+    _blockwise(lib.fp8_blockwise_quantize_act, x, fmt, q, scale_records)
+
+
+def fp8_blockwise_quantize_weight(w, fmt, q, scale_records):
+    """128 x 128 tiles: as fp8_blockwise_quantize_act, one scale per tile."""
+    _blockwise(lib.fp8_blockwise_quantize_weight, w, fmt, q, scale_records)

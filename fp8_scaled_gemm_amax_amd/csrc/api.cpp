@@ -120,6 +120,22 @@ fp8_status_t check_gemm_operands(const char* fn, const uint8_t* a, int fa, int64
     return FP8_OK;
 }
 
+fp8_status_t check_blockwise(const char* fn, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                             const uint8_t* q, int64_t ldq, const uint8_t* scale, int64_t ld_scale) {
+    FP8_TRY(check_common_quant(fn, x, rows, cols, ldx, fmt, 0));
+    if (!ocp_fmt(fmt)) return fail(FP8_ERR_INVALID_ARG, "%s: blockwise codes are OCP e4m3 or e5m2 (format %d)", fn, fmt);
+    if (cols % 128 != 0) return fail(FP8_ERR_INVALID_ARG, "%s: cols = %lld is not a multiple of 128", fn, (long long)cols);
+    FP8_TRY(check_matrix(fn, "q", q, rows, cols, ldq));
+    if (rows > 0 && cols > 0 && !scale) return fail(FP8_ERR_INVALID_ARG, "%s: scale records are NULL", fn);
+    if (ld_scale < rows || ld_scale < 1)
+        return fail(FP8_ERR_INVALID_ARG, "%s: scale record stride %lld < rows", fn, (long long)ld_scale);
+    if (!aligned(x, 16) || ldx % 8 != 0 || !aligned(q, 8) || ldq % 8 != 0 || !aligned(scale, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: x must be 16-byte aligned with ldx a multiple of 8, q 8-byte aligned with "
+                    "ldq a multiple of 8, the scale records 4-byte aligned", fn);
+    if (rows >= ((int64_t)1 << 26)) return fail(FP8_ERR_UNSUPPORTED, "%s: 2^26 rows or more", fn);
+    return FP8_OK;
+}
+
 // Shared checks of the MX products: k % 256, the E8M0 scale records (one
 // dword per row and 128-deep K step, ld records apart per step), and the
 // 32-bit tile offsets.
@@ -505,6 +521,29 @@ fp8_status_t fp8_moe_unpermute_combine(const uint16_t* y, int64_t rows, int64_t 
     FP8_TRY(check_device());
     return launched(launch_moe_unpermute_combine(y, rows, cols, ldy, dest, weights, tokens, topk, out, ldo,
                                                  (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_blockwise_quantize_act(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                        fp8_format_t fmt, uint8_t* q, int64_t ldq, uint8_t* scale_records,
+                                        int64_t ld_scale, void* stream) {
+    const char* fn = "fp8_blockwise_quantize_act";
+    FP8_TRY(check_blockwise(fn, x, rows, cols, ldx, (int)fmt, q, ldq, scale_records, ld_scale));
+    FP8_TRY(check_device());
+    return launched(launch_blockwise_quant(x, rows, cols, ldx, (int)fmt, 0, q, ldq, scale_records, ld_scale,
+                                           (hipStream_t)stream),
+                    fn);
+}
+
+fp8_status_t fp8_blockwise_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw,
+                                           fp8_format_t fmt, uint8_t* q, int64_t ldq, uint8_t* scale_records,
+                                           int64_t ld_scale, void* stream) {
+    const char* fn = "fp8_blockwise_quantize_weight";
+    FP8_TRY(check_blockwise(fn, w, rows, cols, ldw, (int)fmt, q, ldq, scale_records, ld_scale));
+    if (cols / 128 > 65535) return fail(FP8_ERR_UNSUPPORTED, "%s: more than 65535 K blocks", fn);
+    FP8_TRY(check_device());
+    return launched(launch_blockwise_quant(w, rows, cols, ldw, (int)fmt, 1, q, ldq, scale_records, ld_scale,
+                                           (hipStream_t)stream),
                     fn);
 }
 

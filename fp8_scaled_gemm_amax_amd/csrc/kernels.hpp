@@ -58,6 +58,11 @@ hipError_t launch_grouped_gemm_ragged_k(const uint8_t* a, int fa, int64_t lda, c
 hipError_t launch_mx_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
                                int64_t ldq, uint8_t* scale, int64_t ld_scale, hipStream_t st);
 
+// Blockwise casts (1 x 128 activation blocks, or 128 x 128 weight tiles when
+// weight != 0) with power-of-two scales, into MX scale records.
+hipError_t launch_blockwise_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int weight,
+                                  uint8_t* q, int64_t ldq, uint8_t* scale, int64_t ld_scale, hipStream_t st);
+
 hipError_t launch_gemm_mx(const uint8_t* a, int fa, int64_t lda, const uint8_t* xa, int64_t ld_xa, const uint8_t* b,
                           int fb, int64_t ldb, const uint8_t* xb, int64_t ld_xb, int64_t m, int64_t n, int64_t k,
                           void* d, int out_f32, int64_t ldd, hipStream_t st);

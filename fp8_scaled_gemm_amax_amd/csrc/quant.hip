@@ -495,6 +495,104 @@ __global__ __launch_bounds__(kBlock) void k_mx_quant_row(const uint16_t* __restr
     }
 }
 
+// ---------------------------------------------------------- blockwise casts --
+// Blockwise recipe: 1 x 128 blocks along K for activations, 128 x 128 tiles for
+// weights, one scale per block: the current-scaling scale fmax / amax (1 for a
+// zero or non-finite amax, FLT_MAX at most) rounded down to a power of two (its
+// mantissa bits cleared), so no element saturates (a reading of the blockwise
+// recipe the Flux page lists; the pages give no shapes or rule). The scale is
+// stored as the E8M0 byte of 1 / s, 254 - (exponent field of s), in the K-step
+// major records of the MX entry points (all four bytes of a record equal: a
+// 128-deep K step is one block), so the products run as MX products.
+__device__ __forceinline__ float pow2_floor(float s) { return __uint_as_float(__float_as_uint(s) & 0xff800000u); }
+__device__ __forceinline__ uint32_t e8m0_of_inverse(float s_pow2) { return 254u - (__float_as_uint(s_pow2) >> 23); }
+
+// One wavefront per row slice of up to kMxSlice columns (grid y), in registers;
+// a 128-block is 16 lanes' chunks, reduced with four lane exchanges; the lane
+// holding a block's first chunk stores its record.
+template <int F, int MAXC>
+__global__ __launch_bounds__(kBlock) void k_blockwise_quant_act(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int64_t cols, int64_t ldx, uint8_t* __restrict__ q,
+                                                                int64_t ldq, uint8_t* __restrict__ sc,
+                                                                int64_t ldsc) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int64_t c0 = (int64_t)blockIdx.y * kMxSlice;
+    x += c0;
+    q += c0;
+    sc += (c0 / 128) * ldsc * 4;
+    const int nch = (int)((cols - c0 < kMxSlice ? cols - c0 : kMxSlice) >> 3);
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
+    uint4 v[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk, never stored
+    }
+    uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        uint32_t mx = pk_fold(word_absmax(0u, v[c]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const uint32_t y = __shfl_xor(mx, o);
+            mx = y > mx ? y : mx;
+        }
+        const float amax = amax_from_bits16(mx);
+        const float s = pow2_floor(scale_from_amax<F>(amax, 0));
+        if (ch < nch) {
+            qr[ch] = !__builtin_isnan(amax) ? encode8<F, true>(v[c], s) : encode8<F, false>(v[c], s);
+            if ((lane & 15) == 0)
+                *reinterpret_cast<uint32_t*>(sc + 4 * ((int64_t)(ch >> 4) * ldsc + row)) =
+                    e8m0_of_inverse(s) * 0x01010101u;
+        }
+    }
+}
+
+// One workgroup per 128 x 128 tile (grid x: row tiles, y: K blocks). Thread
+// (wave w, lane l) holds chunk l % 16 of rows 16p + 4w + l / 16, p = 0..7 (rows
+// past the matrix clamped to its last row); tile amax over the workgroup
+// through LDS; threads holding chunk 0 store their rows' records.
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_blockwise_quant_weight(const uint16_t* __restrict__ w, int64_t rows,
+                                                                   int64_t ldw, uint8_t* __restrict__ q,
+                                                                   int64_t ldq, uint8_t* __restrict__ sc,
+                                                                   int64_t ldsc) {
+    __shared__ uint32_t red[kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cc = lane & 15;
+    const int64_t r0 = (int64_t)blockIdx.x * 128;
+    const int64_t k0 = (int64_t)blockIdx.y * 128;
+    uint4 v[8];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int64_t r = r0 + 16 * p + 4 * wave + (lane >> 4);
+        const int64_t rc = r < rows ? r : rows - 1;
+        v[p] = *reinterpret_cast<const uint4*>(w + rc * ldw + k0 + 8 * cc);
+        mx = word_absmax(mx, v[p]);
+    }
+    mx = wave_max_u32(pk_fold(mx));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) mx = red[i] > mx ? red[i] : mx;
+    const float amax = amax_from_bits16(mx);
+    const float s = pow2_floor(scale_from_amax<F>(amax, 0));
+    const uint32_t rec = e8m0_of_inverse(s) * 0x01010101u;
+    const bool nan_free = !__builtin_isnan(amax);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int64_t r = r0 + 16 * p + 4 * wave + (lane >> 4);
+        if (r >= rows) continue;
+        *reinterpret_cast<uint2*>(q + r * ldq + k0 + 8 * cc) = nan_free ? encode8<F, true>(v[p], s)
+                                                                        : encode8<F, false>(v[p], s);
+        if (cc == 0) *reinterpret_cast<uint32_t*>(sc + 4 * (blockIdx.y * ldsc + r)) = rec;
+    }
+}
+
 // ---------------------------------------------------------- colwise quantizer --
 
 // Scales of the workgroup's 64 columns, computed once into LDS.
@@ -1184,6 +1282,46 @@ hipError_t launch_mx_quant_row(const uint16_t* x, int64_t rows, int64_t cols, in
     }
 #undef FP8_MX_FMT
 #undef FP8_MX_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_blockwise_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int weight,
+                                  uint8_t* q, int64_t ldq, uint8_t* scale, int64_t ld_scale, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (weight) {
+        const dim3 grid((unsigned)((rows + 127) / 128), (unsigned)(cols / 128)), block(kBlock);
+        if (fmt == kE4M3)
+            hipLaunchKernelGGL((k_blockwise_quant_weight<kE4M3>), grid, block, 0, st, x, rows, ldx, q, ldq, scale,
+                               ld_scale);
+        else
+            hipLaunchKernelGGL((k_blockwise_quant_weight<kE5M2>), grid, block, 0, st, x, rows, ldx, q, ldq, scale,
+                               ld_scale);
+        return hipGetLastError();
+    }
+    const int chunks = reg_chunks(cols < kMxSlice ? cols : kMxSlice);
+    const dim3 grid(grid_for_rows(rows), (unsigned)((cols + kMxSlice - 1) / kMxSlice)), block(kBlock);
+#define FP8_BW_CASE(F, C)                                                                                        \
+    case C:                                                                                                      \
+        hipLaunchKernelGGL((k_blockwise_quant_act<F, C>), grid, block, 0, st, x, rows, cols, ldx, q, ldq, scale, \
+                           ld_scale);                                                                            \
+        break;
+#define FP8_BW_FMT(F)                                                                                            \
+    switch (chunks) {                                                                                            \
+        FP8_BW_CASE(F, 1)                                                                                        \
+        FP8_BW_CASE(F, 2)                                                                                        \
+        FP8_BW_CASE(F, 4)                                                                                        \
+        FP8_BW_CASE(F, 8)                                                                                        \
+        FP8_BW_CASE(F, 16)                                                                                       \
+        default:                                                                                                 \
+            FP8_BW_CASE(F, 32)                                                                                   \
+    }
+    if (fmt == kE4M3) {
+        FP8_BW_FMT(kE4M3)
+    } else {
+        FP8_BW_FMT(kE5M2)
+    }
+#undef FP8_BW_FMT
+#undef FP8_BW_CASE
     return hipGetLastError();
 }
 

@@ -322,6 +322,31 @@ fp8_status_t fp8_grouped_gemm_mx(const uint8_t* a, fp8_format_t fa, int64_t lda,
                                  const int64_t* group_offsets, int32_t g, int64_t total_m, int64_t n, int64_t k,
                                  void* d, fp8_out_t d_type, int64_t ldd, void* stream);
 
+/* ---------------------------------------------------------------- blockwise --
+ * Blockwise recipe ([Flux] section "Configuration": blockwise among the
+ * recipes; no block shapes or scale rule on the pages). Reading: activations
+ * and gradients take one scale per 1 x 128 block along K (per row), weights
+ * one per 128 x 128 tile; the scale s is the current-scaling scale fmax / amax
+ * of the block (1 for a zero or non-finite amax, FLT_MAX at most) rounded down
+ * to a power of two, so no element saturates; codes are cast(x * s). s is
+ * stored as the E8M0 byte of 1 / s in the MX scale records (above), all four
+ * bytes of a record equal (a 128-deep K step is one block), so blockwise
+ * operands multiply with fp8_gemm_mx / fp8_grouped_gemm_mx. Requirements of
+ * both: cols % 128 == 0; x 16-byte aligned, ldx % 8 == 0; q 8-byte aligned,
+ * ldq % 8 == 0; records 4-byte aligned, ld_scale >= rows; rows < 2^26 (else
+ * FP8_ERR_UNSUPPORTED); fmt e4m3 or e5m2. */
+
+/* 1 x 128 blocks of x bf16 [rows x cols] (ldx). */
+fp8_status_t fp8_blockwise_quantize_act(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                        fp8_format_t fmt, uint8_t* q, int64_t ldq, uint8_t* scale_records,
+                                        int64_t ld_scale, void* stream);
+
+/* 128 x 128 tiles of w bf16 [rows x cols] (ldw; the last row tile may be
+ * shorter); every row of a tile gets the tile's record. */
+fp8_status_t fp8_blockwise_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw,
+                                           fp8_format_t fmt, uint8_t* q, int64_t ldq, uint8_t* scale_records,
+                                           int64_t ld_scale, void* stream);
+
 /* -------------------------------------------------------- MoE layer forward --
  * The MoE layer around its two grouped GEMMs ([Kimbodo] What Happened: the
  * per-MoE-layer latency; [Titan] fused quantization kernels, FP8 grouped GEMM

@@ -641,3 +641,22 @@ def blockwise_gemm(a, fa, ea, b, fb, eb_tiles):
         y += x * p
         bound += x * pm
     return y, bound
+
+
+def blockwise_gemm_entries(a, fa, ea, b, fb, eb_tiles, ii, jj, chunk=1024):
+    """Selected outputs Y[ii[e], jj[e]] of blockwise_gemm, from the same
+    definition evaluated per entry. Returns (y, bound)."""
+    a = np.asarray(a, np.uint8)
+    b = np.asarray(b, np.uint8)
+    ii = np.asarray(ii, np.int64)
+    jj = np.asarray(jj, np.int64)
+    nb = a.shape[1] // BLOCK
+    y = np.empty(ii.size)
+    bound = np.empty(ii.size)
+    for lo in range(0, ii.size, chunk):
+        i, j = ii[lo:lo + chunk], jj[lo:lo + chunk]
+        p = decode(fa, a[i]).reshape(-1, nb, BLOCK) * decode(fb, b[j]).reshape(-1, nb, BLOCK)
+        x = np.exp2(np.asarray(ea, np.float64)[i] - 127.0) * np.exp2(np.asarray(eb_tiles, np.float64)[j // BLOCK] - 127.0)
+        y[lo:lo + chunk] = (x * p.sum(axis=2)).sum(axis=1)
+        bound[lo:lo + chunk] = (x * np.abs(p).sum(axis=2)).sum(axis=1)
+    return y, bound

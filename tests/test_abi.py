@@ -292,3 +292,15 @@ def test_moe_layer_entry_points_reject_bad_arguments(fp8):
         bad = list(ok_c)
         bad[i] = v
         assert _call(fp8, c, *bad)[0] == st, (i, v)
+
+
+def test_blockwise_entry_points_reject_bad_arguments(fp8):
+    for f in ("fp8_blockwise_quantize_act", "fp8_blockwise_quantize_weight"):
+        ok = [FAKE, 4, 256, 256, 0, FAKE, 256, FAKE, 4, None]
+        for i, v, st in ((2, 192, 1), (4, 2, 1), (8, 3, 1), (7, None, 1), (7, ctypes.c_void_p(0x10002), 2),
+                         (5, ctypes.c_void_p(0x10004), 2), (3, 260, 2)):
+            bad = list(ok)
+            bad[i] = v
+            if i == 2:
+                bad[3], bad[6] = 192, 192
+            assert _call(fp8, f, *bad)[0] == st, (f, i, v)

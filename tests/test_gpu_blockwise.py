@@ -1,0 +1,207 @@
+"""GPU parity of the blockwise recipe against the CPU oracle, through the C
+ABI: the 1 x 128 activation cast and the 128 x 128 weight-tile cast bit-exact
+(codes and scale records, special blocks, ragged row tiles, long rows, strided
+views with guard bands), and blockwise operands multiplied by the MX product
+entry points, dense and grouped, within the GEMM bound; the Llama3-8B
+up-projection at full size on sampled outputs."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from helpers import SENTINEL, assert_codes_equal, check_guard, dev_bf16, dev_u8, guarded, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    import fp8_scaled_gemm_amax_amd as m
+    return m
+
+
+def act_records(e8):
+    """Oracle bytes [rows x K/128] -> records [K/128 x rows x 4]."""
+    return np.ascontiguousarray(np.repeat(e8.T[:, :, None], 4, axis=2))
+
+
+def weight_records(e8_tiles, rows):
+    """Oracle tile bytes [ceil(rows/128) x K/128] -> records [K/128 x rows x 4]."""
+    per_row = e8_tiles[np.arange(rows) // 128]                # [rows x K/128]
+    return act_records(per_row)
+
+
+def blocky_bf16(rows, cols, seed, spread=20):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(-spread, spread + 1, (rows, cols // 128))).repeat(128, axis=1).astype(np.float32)
+    return workloads.bf16_bits(x)
+
+
+def gpu_blockwise(fp8, xb, fmt, weight, ldx=None, ldq=None, lds_extra=3):
+    rows, cols = xb.shape
+    J = cols // 128
+    if ldx is not None:
+        xbuf = torch.zeros((rows, ldx), dtype=torch.bfloat16, device=DEV)
+        xbuf[:, :cols] = dev_bf16(xb)
+        x = xbuf[:, :cols]
+    else:
+        x = dev_bf16(xb)
+    q, qbuf, qo = guarded(rows, cols, torch.uint8, ld=ldq)
+    ld = rows + lds_extra
+    sbuf = torch.full((J + 2, ld * 4), SENTINEL, dtype=torch.uint8, device=DEV)
+    s = sbuf[1:1 + J].view(J, ld, 4)[:, :rows, :]
+    (fp8.fp8_blockwise_quantize_weight if weight else fp8.fp8_blockwise_quantize_act)(x, fmt, q, s)
+    torch.cuda.synchronize()
+    check_guard(qbuf, qo, rows, cols)
+    host = sbuf.cpu().numpy()
+    outside = np.ones(host.shape, bool)
+    outside[1:1 + J, :rows * 4] = False
+    assert np.all(host[outside] == SENTINEL), "write outside the scale records"
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (7, 384), (33, 4096), (3, 16384 + 384)])
+def test_act_parity(fp8, orc, fmt, rows, cols):
+    xb = blocky_bf16(rows, cols, seed=rows + cols + fmt)
+    say("blockwise act", rows, cols, fmt)
+    q, rec = gpu_blockwise(fp8, xb, fmt, weight=False)
+    oq, oe = orc.blockwise_quantize_act(xb, fmt)
+    assert_codes_equal(rec, act_records(oe), "records")
+    assert_codes_equal(q, oq, "codes")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (130, 256), (300, 384), (256, 1024)])
+def test_weight_parity(fp8, orc, fmt, rows, cols):
+    rng = np.random.default_rng(rows * cols + fmt)
+    wf = rng.standard_normal((rows, cols)).astype(np.float32) * np.float32(0.02)
+    wf[rng.integers(0, rows), rng.integers(0, cols)] = 7.5           # one tile with a large element
+    xb = workloads.bf16_bits(wf)
+    say("blockwise weight", rows, cols, fmt)
+    q, rec = gpu_blockwise(fp8, xb, fmt, weight=True)
+    oq, oe = orc.blockwise_quantize_weight(xb, fmt)
+    assert_codes_equal(rec, weight_records(oe, rows), "records")
+    assert_codes_equal(q, oq, "codes")
+
+
+def test_special_blocks_and_strides(fp8, orc):
+    """Zero, NaN, Inf and tiny blocks in both casts; strided x, q and records."""
+    xf = np.random.default_rng(4).standard_normal((6, 640)).astype(np.float32)
+    xf[0, :128] = 0
+    xf[1, 130] = np.inf
+    xf[3, 300] = 2.0 ** -133
+    xf[3, 256:300] = 0
+    xf[3, 301:384] = 0
+    xb = workloads.bf16_bits(xf)
+    xb[2, 5] = 0x7FC0
+    for weight in (False, True):
+        say("blockwise special", weight)
+        q, rec = gpu_blockwise(fp8, xb, 0, weight, ldx=640 + 24, ldq=640 + 16, lds_extra=9)
+        if weight:
+            oq, oe = orc.blockwise_quantize_weight(xb, 0)
+            want = weight_records(oe, 6)
+        else:
+            oq, oe = orc.blockwise_quantize_act(xb, 0)
+            want = act_records(oe)
+        assert_codes_equal(rec, want, "records")
+        assert_codes_equal(q, oq, "codes")
+
+
+def assert_within(orc, got, y, bound, out_bf16, what):
+    ok = orc.gemm_within_bound(got, y, bound, out_bf16=out_bf16)
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} outside the bound; first {i}: "
+                             f"gpu {got[i]!r} oracle {y[i]!r} bound {bound[i]!r}")
+
+
+@pytest.mark.parametrize("m,n,k,fa,fb,out_f32", [(300, 520, 512, 0, 0, False), (1, 7, 256, 1, 0, True),
+                                                 (513, 1000, 768, 0, 1, True)])
+def test_blockwise_gemm_parity(fp8, orc, m, n, k, fa, fb, out_f32):
+    """Activations cast 1 x 128 and weights 128 x 128 by the oracle; the GPU
+    product of those operands (through the MX entry point) against the
+    oracle's blockwise product."""
+    xa = blocky_bf16(m, k, seed=m + k, spread=6)
+    wb = workloads.bf16_bits((np.random.default_rng(n).standard_normal((n, k)) * 0.02).astype(np.float32))
+    a, ea = orc.blockwise_quantize_act(xa, fa)
+    b, eb = orc.blockwise_quantize_weight(wb, fb)
+    say("blockwise gemm", m, n, k)
+    d, dbuf, do = guarded(m, n, torch.float32 if out_f32 else torch.bfloat16, ld=n + 8)
+    fp8.fp8_gemm_mx(dev_u8(a), fa, dev_u8(act_records(ea)), dev_u8(b), fb, dev_u8(weight_records(eb, n)), d)
+    torch.cuda.synchronize()
+    check_guard(dbuf, do, m, n)
+    y, bound = orc.blockwise_gemm(a, fa, ea, b, fb, eb)
+    assert_within(orc, d.float().cpu().numpy().astype(np.float64), y, bound, not out_f32, "blockwise gemm")
+
+
+def test_blockwise_grouped_gemm(fp8, orc):
+    """Tokens cast 1 x 128 on the GPU, each expert's weights cast 128 x 128 on
+    the GPU (experts of 256 rows: tiles never straddle two experts), the
+    grouped MX product, against the oracle per group."""
+    sizes = [0, 1, 255, 256, 257, 0, 600]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    T, g, n, k = int(off[-1]), len(sizes), 256, 512
+    xb = blocky_bf16(T, k, seed=31, spread=6)
+    wb = workloads.bf16_bits((np.random.default_rng(32).standard_normal((g * n, k)) * 0.02).astype(np.float32))
+    say("blockwise grouped gemm")
+    xq = torch.empty((T, k), dtype=torch.uint8, device=DEV)
+    xs = fp8.mx_scale_records(T, k)
+    wq = torch.empty((g * n, k), dtype=torch.uint8, device=DEV)
+    ws = fp8.mx_scale_records(g * n, k)
+    fp8.fp8_blockwise_quantize_act(dev_bf16(xb), 0, xq, xs)
+    fp8.fp8_blockwise_quantize_weight(dev_bf16(wb), 0, wq, ws)
+    d = torch.empty((T, n), dtype=torch.bfloat16, device=DEV)
+    wsv = torch.as_strided(ws, (g, k // 128, n, 4), (4 * n, 4 * g * n, 4, 1))
+    fp8.fp8_grouped_gemm_mx(xq, 0, xs, wq.view(g, n, k), 0, wsv, torch.from_numpy(off).to(DEV), d)
+    torch.cuda.synchronize()
+    oa, oea = orc.blockwise_quantize_act(xb, 0)
+    ob, oeb = orc.blockwise_quantize_weight(wb, 0)
+    assert_codes_equal(xq.cpu().numpy(), oa, "token codes")
+    assert_codes_equal(wq.cpu().numpy(), ob, "weight codes")
+    got = d.float().cpu().numpy().astype(np.float64)
+    for e in range(g):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        y, bound = orc.blockwise_gemm(oa[lo:hi], 0, oea[lo:hi], ob[e * n:(e + 1) * n], 0,
+                                      oeb[2 * e:2 * e + 2])
+        assert_within(orc, got[lo:hi], y, bound, True, f"expert {e}")
+
+
+def test_c2_blockwise_full(fp8, orc):
+    """The Llama3-8B up-projection tensors (X [8192 x 4096], W [14336 x 4096])
+    with the blockwise recipe, in the bench's launch configuration: codes and
+    records bit-exact on the whole tensors, the product on sampled outputs
+    (one per 128 x 128 output tile plus 4096 more)."""
+    say("c2 blockwise generate")
+    w = workloads.c2()
+    m, k = w["x"].shape
+    n = w["w"].shape[0]
+    xq = torch.empty((m, k), dtype=torch.uint8, device=DEV)
+    xs = fp8.mx_scale_records(m, k)
+    wq = torch.empty((n, k), dtype=torch.uint8, device=DEV)
+    ws = fp8.mx_scale_records(n, k)
+    say("c2 blockwise cast + gemm")
+    fp8.fp8_blockwise_quantize_act(dev_bf16(w["x"]), 0, xq, xs)
+    fp8.fp8_blockwise_quantize_weight(dev_bf16(w["w"]), 0, wq, ws)
+    d = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    fp8.fp8_gemm_mx(xq, 0, xs, wq, 0, ws, d)
+    torch.cuda.synchronize()
+    oa, oea = orc.blockwise_quantize_act(w["x"], 0)
+    ob, oeb = orc.blockwise_quantize_weight(w["w"], 0)
+    assert_codes_equal(xq.cpu().numpy(), oa, "X codes")
+    assert_codes_equal(xs.cpu().numpy(), act_records(oea), "X records")
+    assert_codes_equal(wq.cpu().numpy(), ob, "W codes")
+    assert_codes_equal(ws.cpu().numpy(), weight_records(oeb, n), "W records")
+    rng = np.random.default_rng(41)
+    ti, tj = np.meshgrid(np.arange(m // 128), np.arange(n // 128), indexing="ij")
+    ii = np.concatenate([ti.ravel() * 128 + rng.integers(0, 128, ti.size), rng.integers(0, m, 4096), [m - 1]])
+    jj = np.concatenate([tj.ravel() * 128 + rng.integers(0, 128, tj.size), rng.integers(0, n, 4096), [n - 1]])
+    y, bound = orc.blockwise_gemm_entries(oa, 0, oea, ob, 0, oeb, ii, jj)
+    got = d[torch.from_numpy(ii).to(DEV), torch.from_numpy(jj).to(DEV)].float().cpu().numpy().astype(np.float64)
+    ok = orc.gemm_within_bound(got, y, bound)
+    assert ok.all(), f"{int((~ok).sum())} sampled outputs outside the bound"

@@ -102,3 +102,18 @@ def test_blockwise_gemm_exact_integers(orc):
                 want += x * float(np.dot(ia[i, sl], ib[j, sl]))
                 mag += x * float(np.abs(ia[i, sl] * ib[j, sl]).sum())
             assert y[i, j] == want and bound[i, j] == mag
+
+
+def test_blockwise_entries_match_the_whole_product(orc):
+    """The sampled-entry form against the whole product (to fp64 rounding)."""
+    rng = np.random.default_rng(13)
+    m, n, K = 9, 300, 384
+    a = rng.integers(0, 0x7E, (m, K)).astype(np.uint8)
+    b = rng.integers(0x80, 0xFB, (n, K)).astype(np.uint8)
+    ea = rng.integers(110, 140, (m, 3)).astype(np.uint8)
+    eb = rng.integers(110, 140, (3, 3)).astype(np.uint8)
+    y, bound = orc.blockwise_gemm(a, 0, ea, b, 1, eb)
+    ii, jj = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+    ye, be = orc.blockwise_gemm_entries(a, 0, ea, b, 1, eb, ii.ravel(), jj.ravel())
+    assert np.allclose(ye.reshape(m, n), y, rtol=1e-12, atol=0)
+    assert np.allclose(be.reshape(m, n), bound, rtol=1e-12, atol=0)
