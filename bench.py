@@ -42,7 +42,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=100,
+                   help="untimed steps first: the clock settles over the first few tens of ms of load")
     p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2bw", "c3", "c4", "c4b", "c4mx", "c5", "c6"])
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")

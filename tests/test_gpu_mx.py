@@ -155,13 +155,15 @@ def gpu_gemm_mx(fp8, a, fa, sa, b, fb, sb, out_f32=False):
 
 
 GEMMS = [(300, 520, 512, 0, 0, False), (256, 256, 256, 0, 1, False), (1, 7, 256, 1, 0, True),
-         (513, 1000, 768, 0, 0, True), (1030, 260, 1536, 1, 1, False)]
+         (513, 1000, 768, 0, 0, True), (1030, 260, 1536, 1, 1, False), (512, 768, 1024, 1, 0, True),
+         (768, 512, 512, 0, 0, False)]
 
 
 @pytest.mark.parametrize("m,n,k,fa,fb,out_f32", GEMMS)
 def test_gemm_mx_parity(fp8, orc, m, n, k, fa, fb, out_f32):
-    """Operands from the oracle's MX quantizer; tiles of 256 with ragged edges,
-    one to six 256-deep passes of the K loop, every format pair."""
+    """Operands from the oracle's MX quantizer; tiles of 256 with ragged edges
+    and whole tiles only, one to six 256-deep passes of the K loop, every
+    format pair."""
     a, sa = mx_operands(orc, m, k, fa, seed=m + k)
     b, sb = mx_operands(orc, n, k, fb, seed=n + 2 * k)
     say("gemm mx", m, n, k, fa, fb, out_f32)
