@@ -6,9 +6,10 @@ tooling: nothing on the compute path imports it).
       from the *kernel_stats.csv that `rocprofv3 --kernel-trace --stats
       --output-format csv -d DIR` writes.
 
-  python -m fp8_scaled_gemm_amax_amd.profiling trace DIR --skip N
+  python -m fp8_scaled_gemm_amax_amd.profiling trace DIR [--skip N | --skip-frac F]
       per-kernel average duration over the calls after each kernel's first N
-      (the warmup calls of a bench run) from DIR's *kernel_trace.csv.
+      (or first fraction F: warmup / (warmup + steps) of a bench run, whatever
+      the kernel's calls per step) from DIR's *kernel_trace.csv.
 
   python -m fp8_scaled_gemm_amax_amd.profiling counters DIR
       per-kernel average per dispatch of every counter in DIR's
@@ -67,16 +68,17 @@ def kernel_stats(dirname):
              "total_us": float(r["TotalDurationNs"]) / 1e3, "pct": float(r["Percentage"])} for r in rows]
 
 
-def trace(dirname, skip):
+def trace(dirname, skip, skip_frac=0.0):
     """{kernel name: (calls kept, average us, min us, max us)} over the calls
-    after each kernel's first `skip`."""
+    after each kernel's first `skip` (or its first `skip_frac` of calls)."""
     per = collections.defaultdict(list)
     rows = sorted(csv.DictReader(open(_one(dirname, "kernel_trace.csv"))), key=lambda r: int(r["Start_Timestamp"]))
     for r in rows:
         per[short_name(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     out = {}
     for k, d in per.items():
-        d = d[skip:] if len(d) > skip else d
+        s = int(round(skip_frac * len(d))) if skip_frac else skip
+        d = d[s:] if len(d) > s else d
         out[k] = (len(d), sum(d) / len(d), min(d), max(d))
     return out
 
@@ -108,9 +110,10 @@ def cmd_stats(a):
 
 
 def cmd_trace(a):
-    print(f"{'kernel':70s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}   (first {a.skip} calls of "
+    what = f"first {a.skip_frac:g} of" if a.skip_frac else f"first {a.skip}"
+    print(f"{'kernel':70s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}   ({what} calls of "
           f"each kernel skipped)")
-    for k, (n, avg, lo, hi) in trace(a.dir, a.skip).items():
+    for k, (n, avg, lo, hi) in trace(a.dir, a.skip, a.skip_frac).items():
         print(f"{k[:70]:70s} {n:6d} {avg:10.2f} {lo:10.2f} {hi:10.2f}")
 
 
@@ -152,6 +155,7 @@ def main(argv=None):
     tr = sub.add_parser("trace")
     tr.add_argument("dir")
     tr.add_argument("--skip", type=int, default=0)
+    tr.add_argument("--skip-frac", type=float, default=0.0)
     tr.set_defaults(fn=cmd_trace)
     c = sub.add_parser("counters")
     c.add_argument("dir")
