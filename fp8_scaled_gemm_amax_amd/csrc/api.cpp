@@ -241,7 +241,8 @@ fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int
         return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer", fn);
     FP8_TRY(check_device());
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_quant_row(x, rows, cols, ldx, (int)fmt, margin, q, ldq, scale_inv_out, amax_out, st);
+    hipError_t e = launch_quant_row(x, rows, cols, ldx, (int)fmt, margin, q, ldq, scale_inv_out, amax_out,
+                                    col_amax_out != nullptr, st);
     if (e == hipSuccess && col_amax_out) e = launch_amax(x, rows, cols, ldx, FP8_AXIS_COL, col_amax_out, st);
     return launched(e, fn);
 }

@@ -18,8 +18,10 @@ hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int axis, float* out,
                        hipStream_t st);
 
+// reread: x is read again right after (the column amax pass), so it is loaded
+// through the caches; otherwise as streamed input (nontemporal loads).
 hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
-                            uint8_t* q, int64_t ldq, float* scale_inv, float* amax_out, hipStream_t st);
+                            uint8_t* q, int64_t ldq, float* scale_inv, float* amax_out, bool reread, hipStream_t st);
 
 hipError_t launch_quant_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
                             uint8_t* qt, int64_t ldqt, float* scale_inv, const float* col_amax, hipStream_t st);

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_permute_quant_row(const uint16_t
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         const int ch = lane + c * 64;
-        v[c] = xr[ch < nch ? ch : nch - 1];                 // past the row: a duplicate chunk, never stored
+        v[c] = load_stream(xr + (ch < nch ? ch : nch - 1));  // past the row: a duplicate chunk, never stored
     }
     uint32_t mx = 0;
 #pragma unroll
@@ -211,8 +211,8 @@ __global__ __launch_bounds__(kBlock) void k_swiglu_quant_row(const uint16_t* __r
     for (int c = 0; c < MAXC; ++c) {
         const int ch = lane + c * 64;
         const int cc = ch < nch ? ch : nch - 1;             // past the row: a duplicate chunk, never stored
-        gv[c] = gr[cc];
-        uv[c] = ur[cc];
+        gv[c] = load_stream(gr + cc);
+        uv[c] = load_stream(ur + cc);
     }
     float a[MAXC][8];
     uint32_t mxb = 0;
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_unpermute_combine(const uint16_t
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int ch = lane + c * 64;
-            v[c] = yr[ch < nch ? ch : nch - 1];
+            v[c] = load_stream(yr + (ch < nch ? ch : nch - 1));
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void k_amax_rows_reg(const uint16_t* __rest
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         const int ch = lane + c * 64;
-        v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk (a max ignores it)
+        v[c] = load_stream(xr + (ch < nch ? ch : nch - 1));     // past the row: a duplicate chunk (a max ignores it)
     }
     uint32_t mx = 0;
 #pragma unroll
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kBlock) void k_amax_tensor_reg(const uint16_t* __re
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = lane + c * 64;
-            v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk, never stored
+            v[c] = load_stream(xr + (ch < nch ? ch : nch - 1));     // past the row: a duplicate chunk, never stored
         }
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) mx = word_absmax(mx, v[c]);
@@ -224,8 +224,9 @@ __global__ __launch_bounds__(kBlock) void k_amax_tensor_reg(const uint16_t* __re
 // ---------------------------------------------------------- rowwise quantizer --
 
 // One wavefront per row, the whole row held in registers (MAXC 16-byte chunks
-// per lane): read once, amax, scale, cast, write once.
-template <int F, int MAXC>
+// per lane): read once, amax, scale, cast, write once. NT: nontemporal loads
+// (x streamed), unless another pass reads x right after.
+template <int F, int MAXC, bool NT>
 __global__ __launch_bounds__(kBlock) void k_quant_row_reg(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                           int64_t ldx, int margin, uint8_t* __restrict__ q,
                                                           int64_t ldq, float* __restrict__ scale_inv,
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(kBlock) void k_quant_row_reg(const uint16_t* __rest
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         const int ch = lane + c * 64;
-        v[c] = xr[ch < nch ? ch : nch - 1];         // past the row: a duplicate chunk, never stored
+        v[c] = NT ? load_stream(xr + (ch < nch ? ch : nch - 1)) : xr[ch < nch ? ch : nch - 1];         // past the row: a duplicate chunk, never stored
     }
     uint32_t mx = 0;
 #pragma unroll
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(kBlock) void k_quant_tensor_reg(const uint16_t* __r
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = lane + c * 64;
-            v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk, never stored
+            v[c] = load_stream(xr + (ch < nch ? ch : nch - 1));     // past the row: a duplicate chunk, never stored
         }
         bool nan_row = tensor_nan;
         if (DELAYED) {
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(kBlock) void k_mx_quant_row(const uint16_t* __restr
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         const int ch = lane + c * 64;
-        v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk, never stored
+        v[c] = load_stream(xr + (ch < nch ? ch : nch - 1));     // past the row: a duplicate chunk, never stored
     }
     uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
 #pragma unroll
@@ -528,7 +529,7 @@ __global__ __launch_bounds__(kBlock) void k_blockwise_quant_act(const uint16_t* 
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         const int ch = lane + c * 64;
-        v[c] = xr[ch < nch ? ch : nch - 1];     // past the row: a duplicate chunk, never stored
+        v[c] = load_stream(xr + (ch < nch ? ch : nch - 1));     // past the row: a duplicate chunk, never stored
     }
     uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
 #pragma unroll
@@ -571,7 +572,7 @@ __global__ __launch_bounds__(kBlock) void k_blockwise_quant_weight(const uint16_
     for (int p = 0; p < 8; ++p) {
         const int64_t r = r0 + 16 * p + 4 * wave + (lane >> 4);
         const int64_t rc = r < rows ? r : rows - 1;
-        v[p] = *reinterpret_cast<const uint4*>(w + rc * ldw + k0 + 8 * cc);
+        v[p] = load_stream(reinterpret_cast<const uint4*>(w + rc * ldw + k0 + 8 * cc));
         mx = word_absmax(mx, v[p]);
     }
     mx = wave_max_u32(pk_fold(mx));
@@ -986,7 +987,7 @@ bool is_aligned(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>
 
 template <int F>
 hipError_t quant_row_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int margin, uint8_t* q,
-                         int64_t ldq, float* scale_inv, float* amax_out, hipStream_t st) {
+                         int64_t ldq, float* scale_inv, float* amax_out, bool reread, hipStream_t st) {
     const dim3 grid(grid_for_rows(rows)), block(kBlock);
     // (cols > 0: the register kernels read at least one chunk per row)
     const bool vec =
@@ -999,8 +1000,12 @@ hipError_t quant_row_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
     const int64_t per_lane = (cols / 8 + 63) / 64;
 #define FP8_ROW_CASE(C)                                                                                        \
     if (per_lane <= C) {                                                                                       \
-        hipLaunchKernelGGL((k_quant_row_reg<F, C>), grid, block, 0, st, x, rows, cols, ldx, margin, q, ldq,    \
-                           scale_inv, amax_out);                                                               \
+        if (reread)                                                                                            \
+            hipLaunchKernelGGL((k_quant_row_reg<F, C, false>), grid, block, 0, st, x, rows, cols, ldx, margin, \
+                               q, ldq, scale_inv, amax_out);                                                   \
+        else                                                                                                   \
+            hipLaunchKernelGGL((k_quant_row_reg<F, C, true>), grid, block, 0, st, x, rows, cols, ldx, margin,  \
+                               q, ldq, scale_inv, amax_out);                                                   \
         return hipGetLastError();                                                                              \
     }
     FP8_ROW_CASE(1)
@@ -1213,9 +1218,9 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
 }
 
 hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
-                            uint8_t* q, int64_t ldq, float* scale_inv, float* amax_out, hipStream_t st) {
+                            uint8_t* q, int64_t ldq, float* scale_inv, float* amax_out, bool reread, hipStream_t st) {
     if (rows == 0) return hipSuccess;
-#define CALL(F) quant_row_fmt<F>(x, rows, cols, ldx, margin, q, ldq, scale_inv, amax_out, st)
+#define CALL(F) quant_row_fmt<F>(x, rows, cols, ldx, margin, q, ldq, scale_inv, amax_out, reread, st)
     switch (fmt) {
         case kE4M3: return CALL(kE4M3);
         case kE5M2: return CALL(kE5M2);
