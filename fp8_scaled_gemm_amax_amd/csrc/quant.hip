@@ -727,6 +727,11 @@ __global__ __launch_bounds__(kBlock) void k_quant_col_tiled(const uint16_t* __re
 
 // ------------------------------------------------- grouped colwise (MoE) --
 
+// Groups of at most kSmallGroupRows rows take the one-pass kernel
+// (k_grouped_quant_col_small, 32-column strips); larger ones the two passes.
+constexpr int kSmallGroupRows = 2048;
+constexpr int kSmallStrip = 32;
+
 // Row range of group g: offsets clamped to [0, total], hi >= lo.
 __device__ __forceinline__ void group_rows(const int64_t* __restrict__ off, int g, int64_t total, int64_t* lo,
                                            int64_t* hi) {
@@ -745,7 +750,7 @@ __device__ __forceinline__ void group_rows(const int64_t* __restrict__ off, int 
 __global__ __launch_bounds__(kBlock) void k_grouped_amax_cols(const uint16_t* __restrict__ x, int64_t total,
                                                               int64_t cols, int64_t ldx,
                                                               const int64_t* __restrict__ off, int G,
-                                                              float* __restrict__ out) {
+                                                              float* __restrict__ out, int skip_small) {
     __shared__ uint32_t part[kWaves][256];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -769,6 +774,10 @@ __global__ __launch_bounds__(kBlock) void k_grouped_amax_cols(const uint16_t* __
         group_rows(off, g, total, &lo, &hi);
         const int64_t a = r0 > lo ? r0 : lo, b = r1 < hi ? r1 : hi;
         if (b <= a) continue;                            // (uniform: the whole workgroup skips)
+        if (skip_small && hi - lo <= kSmallGroupRows) {  // (done by the one-pass kernel)
+            r0 = b;
+            continue;
+        }
         uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
         if (ch < nch) {
             const uint16_t* base = x + ch * 8;
@@ -829,7 +838,7 @@ __global__ __launch_bounds__(kBlock) void k_grouped_quant_col_tiled(const uint16
                                                                     const int64_t* __restrict__ off, int G,
                                                                     uint8_t* __restrict__ qt, int64_t ldqt,
                                                                     const float* __restrict__ col_amax,
-                                                                    int vec_store) {
+                                                                    int vec_store, int skip_small) {
     __shared__ float s_lds[kColTileC];
     __shared__ int nan_lds[kColTileC];
     __shared__ __attribute__((aligned(16))) uint32_t tile[kColTileC * kColTileR / 4];
@@ -876,10 +885,151 @@ __global__ __launch_bounds__(kBlock) void k_grouped_quant_col_tiled(const uint16
     const int64_t tt = y - pre[g];
     int64_t lo, hi;
     group_rows(off, g, total, &lo, &hi);
+    if (skip_small && hi - lo <= kSmallGroupRows) return;   // (done by the one-pass kernel; uniform)
     const int64_t c0 = (int64_t)blockIdx.y * kColTileC;
     col_scales_to_lds<F>(col_amax + (int64_t)g * cols, c0, cols, margin, nullptr, s_lds, nan_lds);
     const int64_t d0 = (int64_t)pre[g] * kColTileR + tt * kColTileR;
     col_tile<F>(x, ldx, lo + tt * kColTileR, hi, true, c0, cols, s_lds, nan_lds, tile, qt, ldqt, d0, ldqt, vec_store);
+}
+
+// Groups of at most kSmallGroupRows rows in one pass: a workgroup holds a
+// group's whole 32-column strip in registers (thread t: chunk t % 4 of 8
+// columns, rows 4 (t / 4 + 64 i) + j, i < 8, j < 4), reduces the column amax
+// (lanes, then the four wavefronts through LDS), casts, transposes 4 x 4 byte
+// blocks into an LDS tile [32 columns][2048 rows] and stores each column's
+// padded range P_g .. P_g + roundup(m_g, 256) as 16-byte chunks (zero codes
+// past m_g). It writes the group's column amax and scale_inv; workgroups of
+// larger groups exit (the two-pass kernels take them). P_g is summed over the
+// earlier groups by the workgroup's threads.
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_grouped_quant_col_small(const uint16_t* __restrict__ x, int64_t total,
+                                                                    int64_t cols, int64_t ldx, int margin,
+                                                                    const int64_t* __restrict__ off, int G,
+                                                                    uint8_t* __restrict__ qt, int64_t ldqt,
+                                                                    float* __restrict__ scale_inv,
+                                                                    float* __restrict__ col_amax) {
+    __shared__ uint32_t tile[kSmallStrip][kSmallGroupRows / 4 + 1];   // (+1: rows of a column apart in banks)
+    __shared__ uint32_t red[kWaves][4][4];
+    __shared__ int64_t psum[kWaves];
+    const int g = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int64_t lo, hi;
+    group_rows(off, g, total, &lo, &hi);
+    const int64_t m = hi - lo;
+    if (m > kSmallGroupRows) return;                     // uniform over the workgroup
+    // P_g: the padded sizes of the earlier groups
+    int64_t part = 0;
+    for (int h = t; h < g; h += kBlock) {
+        int64_t a, b;
+        group_rows(off, h, total, &a, &b);
+        part += (b - a + 255) / 256 * 256;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    if (lane == 0) psum[wave] = part;
+    const int cq = t & 3, rq = t >> 2;
+    const int64_t c0 = (int64_t)blockIdx.y * kSmallStrip;
+    const int64_t nch = cols >> 3;                       // chunks of 8 columns in a row
+    const int64_t ch = c0 / 8 + cq;
+    const int64_t chc = ch < nch ? ch : nch - 1;         // past the last column: a duplicate chunk, never stored
+    const uint16_t* base = x + lo * ldx + chc * 8;
+    uint4 v[8][4];
+    const int64_t mlast = m > 0 ? m - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t r = 4 * (rq + 64 * i) + j;
+            v[i][j] = m > 0 ? load_stream(reinterpret_cast<const uint4*>(base + (r < m ? r : mlast) * ldx))
+                            : make_uint4(0u, 0u, 0u, 0u);
+        }
+    uint32_t mx[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {                    // (duplicated rows past m do not change a max)
+            mx[0] = pk_absmax(mx[0], v[i][j].x);
+            mx[1] = pk_absmax(mx[1], v[i][j].y);
+            mx[2] = pk_absmax(mx[2], v[i][j].z);
+            mx[3] = pk_absmax(mx[3], v[i][j].w);
+        }
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t y = __shfl_xor(mx[q], o);
+            mx[q] = pk_absmax(mx[q], y & 0x7fff7fffu);
+        }
+    if (lane < 4)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[wave][lane][q] = mx[q];
+    __syncthreads();
+    const int64_t P = psum[0] + psum[1] + psum[2] + psum[3];
+    float s[8];
+    bool nan_free = true;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t w = red[0][cq][q];
+#pragma unroll
+        for (int k = 1; k < kWaves; ++k) w = pk_absmax(w, red[k][cq][q]);
+        const float a0 = amax_from_bits16(w & 0xffffu), a1 = amax_from_bits16(w >> 16);
+        s[2 * q] = scale_from_amax<F>(a0, margin);
+        s[2 * q + 1] = scale_from_amax<F>(a1, margin);
+        nan_free = nan_free && !__builtin_isnan(a0) && !__builtin_isnan(a1);
+        if (rq == 0 && ch < nch) {                       // the four threads of row group 0 publish
+            const int64_t c = ch * 8 + 2 * q;
+            col_amax[(int64_t)g * cols + c] = a0;
+            col_amax[(int64_t)g * cols + c + 1] = a1;
+            scale_inv[(int64_t)g * cols + c] = 1.0f / s[2 * q];
+            scale_inv[(int64_t)g * cols + c + 1] = 1.0f / s[2 * q + 1];
+        }
+    }
+    // cast (zero codes past m), 4 x 4 byte transposes, LDS tile [column][row word]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t w[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t r = 4 * (rq + 64 * i) + j;
+            const uint4 u = r < m ? v[i][j] : make_uint4(0u, 0u, 0u, 0u);
+            if (nan_free) {
+                w[j][0] = encode4<F, true>(bf16_lo(u.x) * s[0], bf16_hi(u.x) * s[1], bf16_lo(u.y) * s[2],
+                                           bf16_hi(u.y) * s[3]);
+                w[j][1] = encode4<F, true>(bf16_lo(u.z) * s[4], bf16_hi(u.z) * s[5], bf16_lo(u.w) * s[6],
+                                           bf16_hi(u.w) * s[7]);
+            } else {
+                w[j][0] = encode4<F, false>(bf16_lo(u.x) * s[0], bf16_hi(u.x) * s[1], bf16_lo(u.y) * s[2],
+                                            bf16_hi(u.y) * s[3]);
+                w[j][1] = encode4<F, false>(bf16_lo(u.z) * s[4], bf16_hi(u.z) * s[5], bf16_lo(u.w) * s[6],
+                                            bf16_hi(u.w) * s[7]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t a_lo = __builtin_amdgcn_perm(w[1][h], w[0][h], 0x05010400u);
+            const uint32_t a_hi = __builtin_amdgcn_perm(w[1][h], w[0][h], 0x07030602u);
+            const uint32_t b_lo = __builtin_amdgcn_perm(w[3][h], w[2][h], 0x05010400u);
+            const uint32_t b_hi = __builtin_amdgcn_perm(w[3][h], w[2][h], 0x07030602u);
+            const uint32_t tcol[4] = {__builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u),
+                                      __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u),
+                                      __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u),
+                                      __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u)};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) tile[cq * 8 + h * 4 + c][rq + 64 * i] = tcol[c];
+        }
+    }
+    __syncthreads();
+    // each column's padded range: roundup(m, 256) bytes as 16-byte chunks
+    const int64_t padded = (m + 255) / 256 * 256;
+    const int nck = (int)(padded / 16);                  // chunks per column
+    for (int p = t; p < kSmallStrip * nck; p += kBlock) {
+        const int lc = p / nck, k = p - lc * nck;
+        const int64_t col = c0 + lc;
+        if (col >= cols || P + 16 * k >= ldqt) continue;    // (columns of qt at or past ldqt are never written)
+        const uint32_t* src = &tile[lc][4 * k];
+        const uint4 val = make_uint4(src[0], src[1], src[2], src[3]);
+        *reinterpret_cast<uint4*>(qt + col * ldqt + P + 16 * k) = val;
+    }
 }
 
 // Any layout: one thread per column of a band of rows (reads coalesce across
@@ -1335,13 +1485,44 @@ hipError_t launch_grouped_quant_col(const uint16_t* x, int64_t total_m, int64_t 
                                     float* scale_inv, float* col_amax, int col_amax_ready, hipStream_t st) {
     if (cols == 0) return hipSuccess;
     hipError_t e = hipSuccess;
+    // Groups of at most kSmallGroupRows rows in one pass, when the tensor is
+    // larger than the 256 MB last-level cache (the two-pass path's second read
+    // then comes from HBM: c4b's expert weights, 940 MB, 483 -> 402 us); a
+    // tensor that fits is read the second time from that cache, and the
+    // two-pass path is faster (c4b's token tensors, 67 and 235 MB: 52 / 167 us
+    // against 115 / 307 us one-pass). Not with a supplied amax.
+    const int small = !col_amax_ready && (cols + kSmallStrip - 1) / kSmallStrip <= 65535 &&
+                      total_m * cols * 2 > ((int64_t)256 << 20);
     if (!col_amax_ready) {
         e = launch_fill(col_amax, (int64_t)g * cols, 0.0f, st);
         if (e != hipSuccess) return e;
+        if (small) {
+            const dim3 sgrid((unsigned)g, (unsigned)((cols + kSmallStrip - 1) / kSmallStrip));
+            switch (fmt) {
+                case kE4M3:
+                    hipLaunchKernelGGL((k_grouped_quant_col_small<kE4M3>), sgrid, dim3(kBlock), 0, st, x, total_m,
+                                       cols, ldx, margin, offsets, g, qt, ldqt, scale_inv, col_amax);
+                    break;
+                case kE5M2:
+                    hipLaunchKernelGGL((k_grouped_quant_col_small<kE5M2>), sgrid, dim3(kBlock), 0, st, x, total_m,
+                                       cols, ldx, margin, offsets, g, qt, ldqt, scale_inv, col_amax);
+                    break;
+                case kE4M3Fnuz:
+                    hipLaunchKernelGGL((k_grouped_quant_col_small<kE4M3Fnuz>), sgrid, dim3(kBlock), 0, st, x,
+                                       total_m, cols, ldx, margin, offsets, g, qt, ldqt, scale_inv, col_amax);
+                    break;
+                default:
+                    hipLaunchKernelGGL((k_grouped_quant_col_small<kE5M2Fnuz>), sgrid, dim3(kBlock), 0, st, x,
+                                       total_m, cols, ldx, margin, offsets, g, qt, ldqt, scale_inv, col_amax);
+                    break;
+            }
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         if (total_m > 0) {
             hipLaunchKernelGGL(k_grouped_amax_cols,
                                dim3((unsigned)((total_m + kColAmaxRows - 1) / kColAmaxRows), (unsigned)((cols + 511) / 512)),
-                               dim3(kBlock), 0, st, x, total_m, cols, ldx, offsets, g, col_amax);
+                               dim3(kBlock), 0, st, x, total_m, cols, ldx, offsets, g, col_amax, small);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1359,7 +1540,7 @@ hipError_t launch_grouped_quant_col(const uint16_t* x, int64_t total_m, int64_t 
         if (e != hipSuccess) return e;                                                                           \
         if (total_m > 0)                                                                                         \
             hipLaunchKernelGGL((k_grouped_quant_col_tiled<F>), grid, dim3(kBlock), 0, st, x, total_m, cols, ldx, \
-                               margin, offsets, g, qt, ldqt, col_amax, 1);                                       \
+                               margin, offsets, g, qt, ldqt, col_amax, 1, small);                                \
     } while (0)
     switch (fmt) {
         case kE4M3: CALL(kE4M3); break;

@@ -59,14 +59,16 @@ def padded(offsets):
     return out
 
 
-GROUPS = [[0, 1, 255, 256, 257, 0, 600], [300], [0, 0, 5], [512] * 4, [17] * 30]
+GROUPS = [[0, 1, 255, 256, 257, 0, 600], [300], [0, 0, 5], [512] * 4, [17] * 30,
+          [3000, 5, 2100, 0, 2048, 2049], [2048] * 3 + [1]]
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2])
 @pytest.mark.parametrize("sizes", GROUPS)
 def test_grouped_quantize_col_parity(fp8, orc, fmt, sizes):
     offsets = offsets_of(sizes)
-    cols = 72                                              # one full and one ragged 64-column tile
+    cols = 72                                              # 64-column tiles (two-pass) and 32-column strips
+                                                           # (one pass, groups of <= 2048 rows), both ragged
     xb = rand_bf16(int(offsets[-1]), cols, seed=len(sizes) + fmt)
     say("grouped col", sizes, fmt)
     qt, si, am = gpu_grouped_col(fp8, xb, fmt, offsets)
@@ -76,15 +78,35 @@ def test_grouped_quantize_col_parity(fp8, orc, fmt, sizes):
     assert_f32_bits_equal(am, oam, "amax")
 
 
+def test_grouped_quantize_col_one_pass(fp8, orc):
+    """A tensor past 256 MB (70,000 rows x 2048 columns) takes the one-pass
+    kernel for its groups of at most 2048 rows (32-column strips) and the two
+    passes for the rest: 30 groups of 2048 rows, then 3000, 1, 0, 2500, 1003
+    and 2049 rows, a NaN in a one-pass group; all codes, scales and amax
+    bit-exact."""
+    sizes = [2048] * 30 + [3000, 1, 0, 2500, 1003, 2049]
+    offsets = offsets_of(sizes)
+    xb = rand_bf16(int(offsets[-1]), 2048, seed=77)
+    xb[5000, 100] = 0x7FC0                                 # group 2
+    say("grouped col one pass", int(offsets[-1]))
+    qt, si, am = gpu_grouped_col(fp8, xb, 0, offsets)
+    oq, osi, oam = orc.grouped_quantize_col(xb, 0, offsets, ALIGN)
+    assert_codes_equal(qt, oq, "codes")
+    assert_f32_bits_equal(si, osi, "scale_inv")
+    assert_f32_bits_equal(am, oam, "amax")
+
+
 def test_grouped_quantize_col_nan_and_ready_amax(fp8, orc):
     """A NaN in one group's column (its codes take the bit-level encoder, the
-    other groups' codes of that column are unaffected), and col_amax_ready = 1
-    with the per-group amax supplied."""
-    sizes = [40, 0, 300, 3]
+    other groups' codes of that column are unaffected), in a small group and
+    in one past 2048 rows, and col_amax_ready = 1 with the per-group amax
+    supplied."""
+    sizes = [40, 0, 300, 3, 2500]
     offsets = offsets_of(sizes)
     xb = rand_bf16(int(offsets[-1]), 64, seed=9)
     xb[50, 7] = 0xFFC0                                     # -NaN in group 2, column 7
     xb[5, 9] = 0x7F80                                      # +Inf in group 0
+    xb[400, 11] = 0x7FC0                                   # NaN in group 4 (2500 rows)
     say("grouped col nan")
     qt, si, am = gpu_grouped_col(fp8, xb, 1, offsets)
     oq, osi, oam = orc.grouped_quantize_col(xb, 1, offsets, ALIGN)
