@@ -315,22 +315,62 @@ __device__ __forceinline__ void big_tile_coords(int64_t bid, int64_t tiles_m, in
     *pn = (t % (gm * tiles_n)) / gsize;
 }
 
-// K64 main loop (kept for the grouped product at long K): K advances in steps
-// of 64 through four LDS stages of 32 KB (A: 256 rows x 64 B, then B), filled
-// by direct loads issued three steps ahead of use, so the loads have three
-// steps to land (HBM-streamed expert weights need that lookahead; the K128
-// loop has one). Step t:
+// MX block scales of a step in LDS: row r of the tile (A, then B at +1 KB) at
+// dword (r / 128) * 128 + (r % 32) * 4 + (r / 32) % 4, so the four rows
+// wm*128 + 32 mi + l (mi = 0..3) that lane l needs are one 16-byte read. The
+// thread that fills dword i (a wavefront's direct load fills 64 consecutive
+// dwords) loads row mx_row(i).
+__device__ __forceinline__ int mx_row(int i) { return (i >> 7) * 128 + (i & 3) * 32 + ((i & 127) >> 2); }
+
+// The four scale dwords of lane l's rows, shifted by the lane half s = l / 32:
+// lane half s supplies the scale of block s of each 64-deep half, so byte 0 is
+// then block s of the step's first half and byte 2 block s of its second.
+__device__ __forceinline__ u32x4 mx_scales(const uint8_t* stage, int half_sel) {
+    const int lane = threadIdx.x & 63;
+    const int w = (threadIdx.x >> 6);
+    const int base = half_sel == 0 ? (w >> 1) * 128 : 256 + (w & 1) * 128;
+    u32x4 v = *reinterpret_cast<const u32x4*>(stage + 4 * (base + (lane & 31) * 4));
+    const int sh = 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] >>= sh;
+    return v;
+}
+
+// MFMA of one 64-deep half: with MX the E8M0 scale bytes OPSEL of the lane's
+// A and B scale dwords, else unscaled.
+template <int FA, int FB, bool MX, int OPSEL>
+__device__ __forceinline__ v16f mfma64(const v8i& fa, const v8i& fb, const v16f& c, uint32_t xa, uint32_t xb) {
+    if constexpr (MX)
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, c, MfmaFmt<FA>::v, MfmaFmt<FB>::v, OPSEL,
+                                                               (int)xa, OPSEL, (int)xb);
+    else
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, c, MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 0, 0, 0);
+}
+
+// K64 main loop (the grouped product at long K): K advances in steps of 64
+// through four LDS stages of 32 KB (A: 256 rows x 64 B, then B), filled by
+// direct loads issued three steps ahead of use, so the loads have three steps
+// to land (HBM-streamed expert weights need that lookahead; the K128 loop has
+// one). Step t:
 //   wait until stage t+1's loads have landed; barrier
 //   issue the loads of stage t+4 into the buffer stage t used (its fragments
 //   were read during step t-1)
 //   16 MFMAs on step t's fragments, each followed by one 16-byte fragment read
 //   for step t+1 and every other one by one direct load.
+// With MX each stage also has a 2 KB scale slot: the record dwords of the
+// stage's K128 step (one per A row and B row, in the layout mx_scales reads)
+// come with the stage's loads (two more per thread; the two K64 steps of a
+// K128 step each load it), and step t+1's scales are read during step t with
+// its fragments.
 namespace k64 {
 constexpr int BK = 64;
 constexpr int kStages = 4;
 constexpr int kStage = (big::BM + big::BN) * BK;    // 32 KB: A tile then B tile
-constexpr int kLoadsPerStage = 8;                   // direct loads per thread per stage (4 A + 4 B)
 static_assert(kStages * kStage == big::kMain, "four stages below the scale area");
+// direct loads per thread per stage: 4 A + 4 B (+ the A and B scale dwords)
+template <bool MX>
+constexpr int loads_per_stage() { return MX ? 10 : 8; }
+constexpr int kSmemMx = big::kSmem + kStages * big::kMxStage;    // 138 KB
 }  // namespace k64
 
 // LDS layout of a stage: 64-byte rows of four 16-byte K chunks; chunk c of row r
@@ -361,9 +401,33 @@ __device__ __forceinline__ void big_lane_offsets(uint32_t (&off)[4], int64_t ld,
     }
 }
 
-// Issue the 8 loads of one stage (K slice at k0) into the buffer at `stage`.
+// MX scale records of the K64 loop: xa / xb are this thread's A and B record
+// dwords of K step 0 (rows mx_row(t) of the tiles); K128 step j is j * xsa /
+// j * xsb bytes further.
+struct K64Scales {
+    const uint8_t* xa;
+    const uint8_t* xb;
+    int64_t xsa, xsb;
+};
+
+// Scale slot of stage s.
+__device__ __forceinline__ uint8_t* k64_xslot(uint8_t* smem, int s) { return smem + big::kMxOff + s * big::kMxStage; }
+
+// The two scale-dword loads of the stage at K offset k0 into slot `xslot`.
+__device__ __forceinline__ void k64_issue_scales(uint8_t* xslot, const K64Scales& x, int64_t k0) {
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(xslot)) + wave * 256;
+    const int64_t j = k0 / 128;
+    lds_dma4(base, x.xa + j * x.xsa);
+    lds_dma4(base + 1024, x.xb + j * x.xsb);
+}
+
+// Issue the loads of one stage (K slice at k0) into the buffer at `stage`
+// (with MX, and the scale dwords into `xslot`).
+template <bool MX>
 __device__ __forceinline__ void big_issue_stage(const uint8_t* stage, const uint8_t* a, const uint32_t (&aoff)[4],
-                                                const uint8_t* b, const uint32_t (&boff)[4], int64_t k0) {
+                                                const uint8_t* b, const uint32_t (&boff)[4], int64_t k0,
+                                                uint8_t* xslot, const K64Scales& x) {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage)) + wave * 4096;
     const uint8_t* ak = a + k0;
@@ -372,32 +436,43 @@ __device__ __forceinline__ void big_issue_stage(const uint8_t* stage, const uint
     for (int i = 0; i < 4; ++i) lds_dma16(base + i * 1024, ak + aoff[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) lds_dma16(base + big::BM * k64::BK + i * 1024, bk + boff[i]);
+    if constexpr (MX) k64_issue_scales(xslot, x, k0);
 }
 
-// Fragment of the 32x32x64 instruction: row `row` of a stage, lanes 0-31 hold
-// K bytes 0-31, lanes 32-63 K bytes 32-63 (two 16-byte halves).
+// Fragment of the 32x32x64 instruction from row `row` of a stage, in two
+// 16-byte halves h. With MX the instruction's own K order (lane half s holds
+// K 16s .. 16s + 15 and 32 + 16s .. 32 + 16s + 15; block s is K 32s .. 32s +
+// 31, scaled by lane half s's byte): half h is chunk s + 2h. Without block
+// scales lanes 0-31 take K bytes 0-31 and lanes 32-63 K bytes 32-63 (any order
+// common to A and B gives the same sums).
+template <bool MX>
 __device__ __forceinline__ u32x4 big_half(const uint8_t* tile, int row, int h) {
-    const int c = ((threadIdx.x & 63) >> 5) * 2 + h;
+    const int s = (threadIdx.x & 63) >> 5;
+    const int c = MX ? s + 2 * h : s * 2 + h;
     return *reinterpret_cast<const u32x4*>(tile + row * 64 + (big_slot(row, c) << 4));
 }
 // Step t with t % 4 = S (compile-time): 16 matrix instructions on fc (step
-// t's fragments: A blocks 0-3, B blocks 4-7, read during step t-1). After each
-// one the wavefront issues one 16-byte half of step t+1's fragments into fn
-// and, every other slot, one of the 8 direct loads of stage t+4: the LDS
-// queue never backs up in front of a matrix instruction (issue is in order).
-// The loads are unconditional so that the vmcnt depth stays fixed: past the
-// last stage they re-read the last K slice into buffers that are not read
-// again. sched_barrier(0) pins this order.
-template <int FA, int FB, int S>
+// t's fragments: A blocks 0-3, B blocks 4-7, read during step t-1; with MX sc
+// holds step t's A and B scale dwords, the K128 step's bytes 2 (t % 2) + s
+// selected by opsel). After each one the wavefront issues one 16-byte half of
+// step t+1's fragments into fn and, every other slot, one of the 8 direct loads
+// of stage t+4 (with MX, slots 1 and 9 issue the stage's scale loads and the
+// first two read step t+1's scales into sn): the LDS queue never backs up in
+// front of a matrix instruction (issue is in order). The loads are
+// unconditional so that the vmcnt depth stays fixed: past the last stage they
+// re-read the last K slice into buffers that are not read again.
+// sched_barrier(0) pins this order.
+template <int FA, int FB, int S, bool MX>
 __device__ __forceinline__ void k64_step(uint8_t* smem, v16f (&acc)[4][4], const v8i (&fc)[8], v8i (&fn)[8],
-                                         const uint8_t* a, const uint32_t (&aoff)[4], const uint8_t* b,
-                                         const uint32_t (&boff)[4], int64_t k4) {
+                                         const u32x4 (&sc)[2], u32x4 (&sn)[2], const uint8_t* a,
+                                         const uint32_t (&aoff)[4], const uint8_t* b, const uint32_t (&boff)[4],
+                                         int64_t k4, const K64Scales& x) {
     const uint8_t* nxt = smem + ((S + 1) & 3) * k64::kStage;
     const uint8_t* nxt_b = nxt + big::BM * k64::BK;
     // stage t+1 landed (t+2, t+3 may be in flight) and this wavefront's LDS
     // reads are done: after the barrier other wavefronts load into the buffer
     // this one read during step t-1
-    wait_vmcnt<2 * k64::kLoadsPerStage, 0>();
+    wait_vmcnt<2 * k64::loads_per_stage<MX>(), 0>();
     __syncthreads();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(smem + S * k64::kStage)) + wave * 4096;
@@ -405,17 +480,23 @@ __device__ __forceinline__ void k64_step(uint8_t* smem, v16f (&acc)[4][4], const
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc[mi], fc[4 + ni], acc[mi][ni], MfmaFmt<FA>::v,
-                                                                      MfmaFmt<FB>::v, 0, 0, 0, 0);
+        acc[mi][ni] = mfma64<FA, FB, MX, 2 * (S & 1)>(fc[mi], fc[4 + ni], acc[mi][ni], sc[0][mi], sc[1][ni]);
         // half i of fragment j = i / 2 (B fragments first: the B tile is needed by every A block)
         const int j = (i >> 1) < 4 ? 4 + (i >> 1) : (i >> 1) - 4;
-        half[i] = big_half(j < 4 ? nxt : nxt_b, big_row(j), i & 1);
+        half[i] = big_half<MX>(j < 4 ? nxt : nxt_b, big_row(j), i & 1);
+        if constexpr (MX) {
+            if (i < 2) sn[i] = mx_scales(k64_xslot(smem, (S + 1) & 3), i);
+        }
         if ((i & 1) == 0) {
             const int l = i >> 1;                        // load l: A rows for l < 4, B rows for l >= 4
             if (l < 4)
                 lds_dma16(dma_base + l * 1024, a + k4 + aoff[l]);
             else
                 lds_dma16(dma_base + big::BM * k64::BK + (l - 4) * 1024, b + k4 + boff[l - 4]);
+        } else if (MX && (i == 1 || i == 9)) {
+            const uint32_t xbase =
+                __builtin_amdgcn_readfirstlane(lds_addr(k64_xslot(smem, S))) + wave * 256 + (i == 1 ? 0 : 1024);
+            lds_dma4(xbase, i == 1 ? x.xa + (k4 / 128) * x.xsa : x.xb + (k4 / 128) * x.xsb);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -429,10 +510,13 @@ __device__ __forceinline__ void k64_step(uint8_t* smem, v16f (&acc)[4][4], const
 // sa_lane / sb_lane: this thread's row / column scale (thread t: tile row t,
 // tile column t). They are loaded straight into the scale area of LDS with the
 // first loads of the tile, so no register holds them across the main loop.
-template <int FA, int FB>
+// With MX the scale area holds 1 and x carries the block-scale records.
+// k % 256 == 0, k > 0.
+template <int FA, int FB, bool MX>
 __device__ __forceinline__ void k64_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
                                              const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k,
-                                             const float* sa_lane, const float* sb_lane, v16f (&acc)[4][4]) {
+                                             const float* sa_lane, const float* sb_lane, const K64Scales& x,
+                                             v16f (&acc)[4][4]) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -443,34 +527,45 @@ __device__ __forceinline__ void k64_mainloop(uint8_t* smem, const uint8_t* a, in
     big_lane_offsets(aoff, lda, a_rows);
     big_lane_offsets(boff, ldb, b_rows);
     constexpr int64_t BK = k64::BK;
+    constexpr int L = k64::loads_per_stage<MX>();
     const int64_t nk = k / BK;
     const int64_t last = (nk - 1) * BK;
     auto kof = [&](int64_t s) { return s < nk ? s * BK : last; };
     // prologue: the scales, then stages 0..3 in flight; wait for the scales and
     // stage 0 (loads complete in order) and read step 0's fragments
-    {
+    if constexpr (MX) {
+        float* s = reinterpret_cast<float*>(smem + big::kScaleOff);
+        s[threadIdx.x] = 1.0f;
+        s[256 + threadIdx.x] = 1.0f;
+    } else {
         const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kScaleOff)) + wave * 256;
         lds_dma4(sbase, sa_lane);
         lds_dma4(sbase + 1024, sb_lane);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) big_issue_stage(smem + s * k64::kStage, a, aoff, b, boff, kof(s));
-    wait_vmcnt<3 * k64::kLoadsPerStage>();
+    for (int s = 0; s < 4; ++s)
+        big_issue_stage<MX>(smem + s * k64::kStage, a, aoff, b, boff, kof(s), k64_xslot(smem, s), x);
+    wait_vmcnt<3 * L>();
     __syncthreads();
     v8i f0[8], f1[8];
+    u32x4 s0[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}}, s1[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint8_t* t0 = j < 4 ? smem : smem + big::BM * k64::BK;
-        f0[j] = big_join(big_half(t0, big_row(j), 0), big_half(t0, big_row(j), 1));
+        f0[j] = big_join(big_half<MX>(t0, big_row(j), 0), big_half<MX>(t0, big_row(j), 1));
+    }
+    if constexpr (MX) {
+        s0[0] = mx_scales(k64_xslot(smem, 0), 0);
+        s0[1] = mx_scales(k64_xslot(smem, 0), 1);
     }
     // four steps per iteration: the stage index (t % 4) and the fragment set
     // (t % 2) stay compile-time
     for (int64_t t = 0; t < nk; t += 4) {
-        k64_step<FA, FB, 0>(smem, acc, f0, f1, a, aoff, b, boff, kof(t + 4));
-        k64_step<FA, FB, 1>(smem, acc, f1, f0, a, aoff, b, boff, kof(t + 5));
-        k64_step<FA, FB, 2>(smem, acc, f0, f1, a, aoff, b, boff, kof(t + 6));
-        k64_step<FA, FB, 3>(smem, acc, f1, f0, a, aoff, b, boff, kof(t + 7));
+        k64_step<FA, FB, 0, MX>(smem, acc, f0, f1, s0, s1, a, aoff, b, boff, kof(t + 4), x);
+        k64_step<FA, FB, 1, MX>(smem, acc, f1, f0, s1, s0, a, aoff, b, boff, kof(t + 5), x);
+        k64_step<FA, FB, 2, MX>(smem, acc, f0, f1, s0, s1, a, aoff, b, boff, kof(t + 6), x);
+        k64_step<FA, FB, 3, MX>(smem, acc, f1, f0, s1, s0, a, aoff, b, boff, kof(t + 7), x);
     }
     // (k % 256 == 0: whole iterations only; a remainder's join costs
     // accumulator spills at the epilogue)
@@ -535,38 +630,6 @@ __device__ __forceinline__ u32x4 k128_half(const uint8_t* tile, int row, int h, 
 // sweep (mi, ni) = (0,0), (0,1), .. first needs them). j < 4: A block j, else B.
 __device__ __forceinline__ int k128_frag(int f) { return f == 0 ? 0 : (f <= 4 ? 4 + (f - 1) : f - 4); }
 
-// MX block scales of a step in LDS: row r of the tile (A, then B at +1 KB) at
-// dword (r / 128) * 128 + (r % 32) * 4 + (r / 32) % 4, so the four rows
-// wm*128 + 32 mi + l (mi = 0..3) that lane l needs are one 16-byte read. The
-// thread that fills dword i (a wavefront's direct load fills 64 consecutive
-// dwords) loads row mx_row(i).
-__device__ __forceinline__ int mx_row(int i) { return (i >> 7) * 128 + (i & 3) * 32 + ((i & 127) >> 2); }
-
-// The four scale dwords of lane l's rows, shifted by the lane half s = l / 32:
-// lane half s supplies the scale of block s of each 64-deep half, so byte 0 is
-// then block s of the step's first half and byte 2 block s of its second.
-__device__ __forceinline__ u32x4 mx_scales(const uint8_t* stage, int half_sel) {
-    const int lane = threadIdx.x & 63;
-    const int w = (threadIdx.x >> 6);
-    const int base = half_sel == 0 ? (w >> 1) * 128 : 256 + (w & 1) * 128;
-    u32x4 v = *reinterpret_cast<const u32x4*>(stage + 4 * (base + (lane & 31) * 4));
-    const int sh = 8 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] >>= sh;
-    return v;
-}
-
-// MFMA of one 64-deep half: with MX the E8M0 scale bytes OPSEL of the lane's
-// A and B scale dwords, else unscaled.
-template <int FA, int FB, bool MX, int OPSEL>
-__device__ __forceinline__ v16f k128_mfma(const v8i& fa, const v8i& fb, const v16f& c, uint32_t xa, uint32_t xb) {
-    if constexpr (MX)
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, c, MfmaFmt<FA>::v, MfmaFmt<FB>::v, OPSEL,
-                                                               (int)xa, OPSEL, (int)xb);
-    else
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, c, MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 0, 0, 0);
-}
-
 // Step p with stage CUR = p % 2 (compile-time). LOADS: the 16 loads of step
 // p+1 (K offset knext) go to the other stage during this step's first 16 MFMAs
 // (with MX also step p+1's two scale dwords per thread: the records xa / xb
@@ -602,7 +665,7 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], cons
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = k128_mfma<FA, FB, MX, 0>(f0[mi], f0[4 + ni], acc[mi][ni], sxa[mi], sxb[ni]);
+        acc[mi][ni] = mfma64<FA, FB, MX, 0>(f0[mi], f0[4 + ni], acc[mi][ni], sxa[mi], sxb[ni]);
         const int j = k128_frag(i >> 1);
         h1[i] = k128_half<MX>(j < 4 ? ta : tb, big_row(j), 1, i & 1);
         if (LOADS) {
@@ -627,7 +690,7 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], cons
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = k128_mfma<FA, FB, MX, 2>(f1[mi], f1[4 + ni], acc[mi][ni], sxa[mi], sxb[ni]);
+        acc[mi][ni] = mfma64<FA, FB, MX, 2>(f1[mi], f1[4 + ni], acc[mi][ni], sxa[mi], sxb[ni]);
     }
 }
 
@@ -870,8 +933,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     const int64_t* __restrict__ offsets, int g, int64_t total_m, int64_t n, int64_t k, const float* __restrict__ sa,
     const float* __restrict__ sb, void* __restrict__ d, int64_t ldd, int vec_out, const uint8_t* __restrict__ xa,
     int64_t ld_xa, const uint8_t* __restrict__ xb, int64_t ld_xb, int64_t xb_group_stride) {
-    static_assert(!(MX && K64), "the MX block scales ride on the K128 loop");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? big::kSmemMx : big::kSmem];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? (K64 ? k64::kSmemMx : big::kSmemMx) : big::kSmem];
     const int64_t tiles_n = (n + big::BN - 1) / big::BN;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
@@ -943,14 +1005,18 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
         const int rt = mx_row(t);
         const uint8_t* xa_lane = xa + 4 * (row0 + rt < hi ? row0 + rt : hi - 1);
         const uint8_t* xb_lane = xb + (int64_t)grp * xb_group_stride + 4 * (col0 + rt < n ? col0 + rt : n - 1);
-        k128_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, nullptr,
-                                    nullptr, xa_lane, xb_lane, 4 * ld_xa, 4 * ld_xb, acc);
+        if constexpr (K64)
+            k64_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
+                                       nullptr, nullptr, K64Scales{xa_lane, xb_lane, 4 * ld_xa, 4 * ld_xb}, acc);
+        else
+            k128_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
+                                        nullptr, nullptr, xa_lane, xb_lane, 4 * ld_xa, 4 * ld_xb, acc);
     } else {
         const float* sa_lane = sa + (row0 + t < hi ? row0 + t : hi - 1);
         const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
         if (K64)
-            k64_mainloop<FA, FB>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, sa_lane,
-                                 sb_lane, acc);
+            k64_mainloop<FA, FB, false>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
+                                        sa_lane, sb_lane, K64Scales{nullptr, nullptr, 0, 0}, acc);
         else
             k128_mainloop<FA, FB, false>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
                                          sa_lane, sb_lane, nullptr, nullptr, 0, 0, acc);
@@ -1102,9 +1168,15 @@ hipError_t grouped_mx_typed(const uint8_t* a, int64_t lda, const uint8_t* xa, in
     const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
     const int64_t grid = ((total_m + big::BM - 1) / big::BM + g) * ((n + big::BN - 1) / big::BN);
     const float* none = nullptr;
-    hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false, true>), dim3((unsigned)grid), dim3(256), 0, st, a,
-                       lda, b, ldb, stride, offsets, g, total_m, n, k, none, none, d, ldd, vec_out, xa, ld_xa, xb,
-                       ld_xb, xstride);
+    // long K: the K64 loop's deeper lookahead, as for the rowwise-scaled product
+    if (k >= 4096)
+        hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, true, true>), dim3((unsigned)grid), dim3(256), 0, st,
+                           a, lda, b, ldb, stride, offsets, g, total_m, n, k, none, none, d, ldd, vec_out, xa, ld_xa,
+                           xb, ld_xb, xstride);
+    else
+        hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false, true>), dim3((unsigned)grid), dim3(256), 0, st,
+                           a, lda, b, ldb, stride, offsets, g, total_m, n, k, none, none, d, ldd, vec_out, xa, ld_xa,
+                           xb, ld_xb, xstride);
     return hipGetLastError();
 }
 

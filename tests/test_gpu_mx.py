@@ -219,10 +219,12 @@ def offsets_of(sizes):
 
 
 GROUPED = [([0, 1, 255, 256, 257, 0, 600], 520, 512, 0, 0, False), ([300], 256, 256, 1, 0, True),
-           ([17] * 30, 96, 768, 0, 1, False), ([1000, 20, 700, 3], 1024, 2048, 0, 0, False)]
+           ([17] * 30, 96, 768, 0, 1, False), ([1000, 20, 700, 3], 1024, 2048, 0, 0, False),
+           ([0, 300, 1, 257, 0, 520], 300, 4096, 1, 0, True), ([513, 2, 256], 520, 4352, 0, 1, False)]
 
 
-@pytest.mark.parametrize("sizes,n,k,fa,fb,out_f32", GROUPED, ids=["ragged", "one", "many", "large"])
+@pytest.mark.parametrize("sizes,n,k,fa,fb,out_f32", GROUPED,
+                         ids=["ragged", "one", "many", "large", "long_k", "long_k_ragged"])
 def test_grouped_gemm_mx_parity(fp8, orc, sizes, n, k, fa, fb, out_f32):
     """Groups with empty, one-row and tile-straddling row counts; weights and
     their scales as strided [g x n x k] and [g x n x k/32] stacks."""
@@ -243,6 +245,32 @@ def test_grouped_gemm_mx_parity(fp8, orc, sizes, n, k, fa, fb, out_f32):
     got = d.float().cpu().numpy().astype(np.float64)
     y, bound = orc.mx_grouped_gemm(a, fa, sa, b, fb, sb, offsets)
     assert_within(orc, got, y, bound, not out_f32, f"grouped mx {sizes}")
+
+
+def test_grouped_gemm_mx_long_k_random_scales(fp8, orc):
+    """The long-K grouped product (k >= 4096 takes the K64 loop, whose two
+    64-deep steps share one record dword) with codes drawn uniformly and scale
+    bytes drawn independently per block: a scale byte taken from the wrong
+    step, block or stage shows at once."""
+    rng = np.random.default_rng(23)
+    sizes, n, k = [260, 0, 1, 300], 270, 4096
+    offsets = offsets_of(sizes)
+    T, g = int(offsets[-1]), len(sizes)
+    a = rng.integers(0, 256, (T, k)).astype(np.uint8)
+    b = rng.integers(0, 256, (g, n, k)).astype(np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x10                           # no NaN codes (e4m3)
+    b[(b & 0x7F) == 0x7F] = 0x10
+    sa = rng.integers(117, 138, (T, k // BLOCK)).astype(np.uint8)
+    sb = rng.integers(117, 138, (g, n, k // BLOCK)).astype(np.uint8)
+    say("grouped gemm mx long k random scales")
+    d, dbuf, do = guarded(T, n, torch.float32, ld=n + 4)
+    sb_rec = np.stack([to_records(sb[e]) for e in range(g)])
+    fp8.fp8_grouped_gemm_mx(dev_u8(a), 0, dev_records(sa), dev_u8(b), 0, dev_u8(sb_rec),
+                            torch.from_numpy(offsets).to("cuda:0"), d)
+    torch.cuda.synchronize()
+    check_guard(dbuf, do, T, n)
+    y, bound = orc.mx_grouped_gemm(a, 0, sa, b, 0, sb, offsets)
+    assert_within(orc, d.cpu().numpy().astype(np.float64), y, bound, False, "grouped mx long k random scales")
 
 
 def test_mx_layer_forward_composed(fp8, orc):
