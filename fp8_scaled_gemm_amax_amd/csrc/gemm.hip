@@ -578,11 +578,11 @@ __device__ __forceinline__ void k64_mainloop(uint8_t* smem, const uint8_t* a, in
 // Each direct load brings whole 128-byte row segments (8 lanes per row), so
 // the L1 sends full-line requests to L2: on gfx950 the load path's throughput
 // goes with the number of requests (64-byte row segments cost ~13% of the
-// GEMM's time at these shapes). With two stages the loads of step p+1 are
-// issued during the first half of step p and waited for at the start of step
-// p+1; step p's first-half fragments are read at its start (the barrier orders
-// them after the stage has landed), its second-half fragments during its first
-// 16 MFMAs. 128-byte rows: chunk c of row r sits in slot c ^ ((r >> 1) & 7),
+// GEMM's time at these shapes). With two stages the loads of step p+2 are
+// issued during the second half of step p and waited for in the middle of
+// step p+1 (a barrier between the two halves of each step); step p's
+// second-half fragments are read during its first 16 MFMAs and step p+1's
+// first-half fragments during its last 16. 128-byte rows: chunk c of row r sits in slot c ^ ((r >> 1) & 7),
 // so 16 consecutive rows reading one chunk hit 16 distinct 16-byte bank groups.
 namespace k128 {
 constexpr int BK = 128;
@@ -630,44 +630,61 @@ __device__ __forceinline__ u32x4 k128_half(const uint8_t* tile, int row, int h, 
 // sweep (mi, ni) = (0,0), (0,1), .. first needs them). j < 4: A block j, else B.
 __device__ __forceinline__ int k128_frag(int f) { return f == 0 ? 0 : (f <= 4 ? 4 + (f - 1) : f - 4); }
 
-// Step p with stage CUR = p % 2 (compile-time). LOADS: the 16 loads of step
-// p+1 (K offset knext) go to the other stage during this step's first 16 MFMAs
-// (with MX also step p+1's two scale dwords per thread: the records xa / xb
-// of K step 0 advanced by knext / 128 steps of xsa / xsb bytes).
-template <int FA, int FB, int CUR, bool LOADS, bool MX>
-__device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], const uint8_t* a,
-                                          const uint32_t (&aoff)[8], const uint8_t* b, const uint32_t (&boff)[8],
-                                          int64_t knext, const uint8_t* xa, const uint8_t* xb, int64_t xsa,
-                                          int64_t xsb) {
-    wait_vmcnt<0, 0>();                                  // this stage has landed; this wavefront's reads are done
-    __syncthreads();                                     // (the other stage is now free for step p+1's loads)
+// Step p with stage CUR = p % 2 (compile-time). On entry f0 holds step p's
+// first-half fragments and sx its A and B scale dwords (MX), both read during
+// step p-1 (or the prologue). The step:
+//   16 MFMAs on f0, each followed by one read of step p's second-half
+//   fragments from stage CUR
+//   wait until this thread's loads have landed (those of step p+1, issued
+//   during step p-1); barrier: stage CUR^1 is complete and every wavefront
+//   has read stage CUR for the last time
+//   16 MFMAs on f1, each followed (NEXT) by one read of step p+1's first-half
+//   fragments from stage CUR^1 and (LOADS) by one of the 16 loads of step p+2
+//   (K offset knext) into stage CUR; with MX also step p+2's two scale dwords
+//   per thread (the records xa / xb of K step 0 advanced by knext / 128 steps
+//   of xsa / xsb bytes), and step p+1's scales read into sx.
+// A step's MFMAs thus never wait for LDS reads issued after the barrier, and
+// the loads have a full step to land.
+template <int FA, int FB, int CUR, bool NEXT, bool LOADS, bool MX>
+__device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], v8i (&f0)[8], u32x4 (&sx)[2],
+                                          const uint8_t* a, const uint32_t (&aoff)[8], const uint8_t* b,
+                                          const uint32_t (&boff)[8], int64_t knext, const uint8_t* xa,
+                                          const uint8_t* xb, int64_t xsa, int64_t xsb) {
     const uint8_t* ta = smem + CUR * k128::kStage;
     const uint8_t* tb = ta + k128::kOpBytes;
-    u32x4 sxa = {0u, 0u, 0u, 0u}, sxb = {0u, 0u, 0u, 0u};
-    if constexpr (MX) {
-        const uint8_t* xs = smem + big::kMxOff + CUR * big::kMxStage;
-        sxa = mx_scales(xs, 0);
-        sxb = mx_scales(xs, 1);
-    }
-    u32x4 h0[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int j = k128_frag(i >> 1);
-        h0[i] = k128_half<MX>(j < 4 ? ta : tb, big_row(j), 0, i & 1);
-    }
-    v8i f0[8];
-#pragma unroll
-    for (int f = 0; f < 8; ++f) f0[k128_frag(f)] = big_join(h0[2 * f], h0[2 * f + 1]);
-    __builtin_amdgcn_sched_barrier(0);
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(smem + (CUR ^ 1) * k128::kStage)) + wave * 8192;
+    const uint8_t* na = smem + (CUR ^ 1) * k128::kStage;
+    const uint8_t* nb = na + k128::kOpBytes;
     u32x4 h1[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = mfma64<FA, FB, MX, 0>(f0[mi], f0[4 + ni], acc[mi][ni], sxa[mi], sxb[ni]);
+        acc[mi][ni] = mfma64<FA, FB, MX, 0>(f0[mi], f0[4 + ni], acc[mi][ni], sx[0][mi], sx[1][ni]);
         const int j = k128_frag(i >> 1);
         h1[i] = k128_half<MX>(j < 4 ? ta : tb, big_row(j), 1, i & 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    v8i f1[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) f1[k128_frag(f)] = big_join(h1[2 * f], h1[2 * f + 1]);
+    wait_vmcnt<0, 0>();
+    __syncthreads();
+    const u32x4 sxc[2] = {sx[0], sx[1]};
+    if constexpr (MX && NEXT) {
+        const uint8_t* xs = smem + big::kMxOff + (CUR ^ 1) * big::kMxStage;
+        sx[0] = mx_scales(xs, 0);
+        sx[1] = mx_scales(xs, 1);
+    }
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(smem + CUR * k128::kStage)) + wave * 8192;
+    u32x4 h0[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int mi = i >> 2, ni = i & 3;
+        acc[mi][ni] = mfma64<FA, FB, MX, 2>(f1[mi], f1[4 + ni], acc[mi][ni], sxc[0][mi], sxc[1][ni]);
+        if (NEXT) {
+            const int j = k128_frag(i >> 1);
+            h0[i] = k128_half<MX>(j < 4 ? na : nb, big_row(j), 0, i & 1);
+        }
         if (LOADS) {
             if (i < 8)
                 lds_dma16(dma_base + i * 1024, a + knext + aoff[i]);
@@ -676,7 +693,7 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], cons
             if constexpr (MX) {
                 if (i == 3 || i == 11) {
                     const uint32_t xbase = __builtin_amdgcn_readfirstlane(
-                                               lds_addr(smem + big::kMxOff + (CUR ^ 1) * big::kMxStage)) +
+                                               lds_addr(smem + big::kMxOff + CUR * big::kMxStage)) +
                                            wave * 256 + (i == 3 ? 0 : 1024);
                     lds_dma4(xbase, i == 3 ? xa + (knext / k128::BK) * xsa : xb + (knext / k128::BK) * xsb);
                 }
@@ -684,13 +701,9 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], cons
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    v8i f1[8];
+    if (NEXT) {
 #pragma unroll
-    for (int f = 0; f < 8; ++f) f1[k128_frag(f)] = big_join(h1[2 * f], h1[2 * f + 1]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = mfma64<FA, FB, MX, 2>(f1[mi], f1[4 + ni], acc[mi][ni], sxa[mi], sxb[ni]);
+        for (int f = 0; f < 8; ++f) f0[k128_frag(f)] = big_join(h0[2 * f], h0[2 * f + 1]);
     }
 }
 
@@ -699,7 +712,8 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], cons
 // (thread t's row / column scale) or, with MX, 1 (the block scales are applied
 // inside the MFMAs; xa / xb are the K-step-0 scale records of A row mx_row(t)
 // and B row mx_row(t) of the tile, and a K step advances them by xsa / xsb
-// bytes).
+// bytes). Prologue: steps 0 and 1 in flight, wait for step 0, read its
+// first-half fragments.
 template <int FA, int FB, bool MX>
 __device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
                                               const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k,
@@ -716,6 +730,9 @@ __device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, i
     k128_lane_offsets(boff, ldb, b_rows);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nk = k / k128::BK;
+    constexpr int L = MX ? 18 : 16;                      // loads per thread per step
+    v8i f0[8];
+    u32x4 sx[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     {
         if constexpr (MX) {
             float* s = reinterpret_cast<float*>(smem + big::kScaleOff);
@@ -727,24 +744,43 @@ __device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, i
             lds_dma4(sbase + 1024, sb_lane);
         }
         if (MX && nk == 0) return;                       // (the epilogue's barrier orders the scale area)
-        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem)) + wave * 8192;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lds_dma16(base + i * 1024, a + aoff[i]);
+        for (int s = 0; s < 2; ++s) {
+            const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem + s * k128::kStage)) + wave * 8192;
+            const int64_t k0 = s * k128::BK;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lds_dma16(base + k128::kOpBytes + i * 1024, b + boff[i]);
+            for (int i = 0; i < 8; ++i) lds_dma16(base + i * 1024, a + k0 + aoff[i]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) lds_dma16(base + k128::kOpBytes + i * 1024, b + k0 + boff[i]);
+            if constexpr (MX) {
+                const uint32_t xbase =
+                    __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kMxOff + s * big::kMxStage)) + wave * 256;
+                lds_dma4(xbase, xa + s * xsa);
+                lds_dma4(xbase + 1024, xb + s * xsb);
+            }
+        }
+        wait_vmcnt<L>();                                 // step 0 (and the scales) landed
+        __syncthreads();
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            const int j = k128_frag(f);
+            f0[j] = big_join(k128_half<MX>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 0),
+                             k128_half<MX>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 1));
+        }
         if constexpr (MX) {
-            const uint32_t xbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kMxOff)) + wave * 256;
-            lds_dma4(xbase, xa);
-            lds_dma4(xbase + 1024, xb);
+            sx[0] = mx_scales(smem + big::kMxOff, 0);
+            sx[1] = mx_scales(smem + big::kMxOff, 1);
         }
     }
     for (int64_t p = 0; p + 2 < nk; p += 2) {
-        k128_step<FA, FB, 0, true, MX>(smem, acc, a, aoff, b, boff, (p + 1) * k128::BK, xa, xb, xsa, xsb);
-        k128_step<FA, FB, 1, true, MX>(smem, acc, a, aoff, b, boff, (p + 2) * k128::BK, xa, xb, xsa, xsb);
+        k128_step<FA, FB, 0, true, true, MX>(smem, acc, f0, sx, a, aoff, b, boff, (p + 2) * k128::BK, xa, xb, xsa,
+                                             xsb);
+        k128_step<FA, FB, 1, true, true, MX>(smem, acc, f0, sx, a, aoff, b, boff, (p + 3) * k128::BK, xa, xb, xsa,
+                                             xsb);
     }
-    k128_step<FA, FB, 0, true, MX>(smem, acc, a, aoff, b, boff, (nk - 1) * k128::BK, xa, xb, xsa, xsb);
-    k128_step<FA, FB, 1, false, MX>(smem, acc, a, aoff, b, boff, 0, xa, xb, xsa, xsb);
-    wait_vmcnt<0>();                                     // (nothing is outstanding: the last step loads nothing)
+    k128_step<FA, FB, 0, true, false, MX>(smem, acc, f0, sx, a, aoff, b, boff, 0, xa, xb, xsa, xsb);
+    k128_step<FA, FB, 1, false, false, MX>(smem, acc, f0, sx, a, aoff, b, boff, 0, xa, xb, xsa, xsb);
+    wait_vmcnt<0>();                                     // (nothing is outstanding: the last steps load nothing)
 }
 
 // Staged bf16 block of the epilogue: group g of 4 rows, column c -> 8 bytes
