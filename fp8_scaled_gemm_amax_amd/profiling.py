@@ -15,6 +15,14 @@ tooling: nothing on the compute path imports it).
       per-kernel average per dispatch of every counter in DIR's
       *counter_collection.csv (`rocprofv3 --pmc ...`).
 
+  python -m fp8_scaled_gemm_amax_amd.profiling mfma DIR [--dispatch-mod M --dispatch-rem R]
+      per-kernel matrix-core use from a `rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+      SQ_INSTS_VALU_MFMA_MOPS_F8 GRBM_GUI_ACTIVE` run: MFMA busy cycles over
+      (active cycles per XCC x SIMDs), the average shader clock (active cycles
+      per XCC over the dispatch's duration) and the FP8 rate the MOPS count
+      gives. --dispatch-mod/--dispatch-rem keep a kernel's dispatches whose
+      index (in launch order) is R modulo M, for kernels launched on two shapes.
+
   python -m fp8_scaled_gemm_amax_amd.profiling traffic --key KEY --kernel SUBSTR
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR
         --copy-kernel SUBSTR --copy-bytes N --sources FILE [FILE ...]
@@ -83,16 +91,64 @@ def trace(dirname, skip, skip_frac=0.0):
     return out
 
 
-def counters(dirname):
+def _counter_rows(dirname, mod=None, rem=None):
+    """Rows of DIR's *counter_collection.csv, optionally only each kernel's
+    dispatches whose index in launch order is rem modulo mod."""
+    rows = list(csv.DictReader(open(_one(dirname, "counter_collection.csv"))))
+    if not mod:
+        return rows
+    order = collections.defaultdict(list)
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        k = short_name(r["Kernel_Name"])
+        if r["Dispatch_Id"] not in order[k]:
+            order[k].append(r["Dispatch_Id"])
+    keep = {d for k, ids in order.items() for i, d in enumerate(ids) if i % mod == rem}
+    return [r for r in rows if r["Dispatch_Id"] in keep]
+
+
+def counters(dirname, mod=None, rem=None):
     """{kernel name: {counter: average value per dispatch}} (a counter's values
     over the instances of one dispatch are summed first)."""
     per = collections.defaultdict(lambda: collections.defaultdict(float))
     disp = collections.defaultdict(set)
-    for r in csv.DictReader(open(_one(dirname, "counter_collection.csv"))):
+    for r in _counter_rows(dirname, mod, rem):
         k = short_name(r["Kernel_Name"])
         per[k][r["Counter_Name"]] += float(r["Counter_Value"])
         disp[k].add(r["Dispatch_Id"])
     return {k: {c: v / len(disp[k]) for c, v in d.items()} for k, d in per.items()}
+
+
+def agent_info(dirname):
+    """The GPU agent's row of DIR's *agent_info.csv."""
+    for r in csv.DictReader(open(_one(dirname, "agent_info.csv"))):
+        if r["Agent_Type"] == "GPU":
+            return r
+    raise SystemExit(f"no GPU agent in {dirname}")
+
+
+def mfma(dirname, mod=None, rem=None):
+    """{kernel: (dispatches, avg us, GHz, MFMA busy %, FP8 TFLOP/s)} for the
+    kernels that issue FP8 MFMAs. GRBM_GUI_ACTIVE arrives summed over the XCCs
+    (each counts the same active cycles), so it is divided by their number."""
+    info = agent_info(dirname)
+    xcc, simds = int(info["Num_Xcc"]), int(info["Simd_Count"])
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    dur = collections.defaultdict(dict)
+    for r in _counter_rows(dirname, mod, rem):
+        k = short_name(r["Kernel_Name"])
+        acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        dur[k][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    out = {}
+    for k, c in acc.items():
+        n = len(dur[k])
+        t = sum(dur[k].values()) / n
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) / n
+        if mops <= 0 or "GRBM_GUI_ACTIVE" not in c:
+            continue
+        cycles = c["GRBM_GUI_ACTIVE"] / n / xcc
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / n
+        out[k] = (n, t * 1e6, cycles / t / 1e9, 100.0 * busy / (cycles * simds), mops * 512 / t / 1e12)
+    return out
 
 
 def _pick(table, substr):
@@ -124,9 +180,15 @@ def cmd_counters(a):
             print(f"    {c:32s} {v:16.1f}")
 
 
+def cmd_mfma(a):
+    print(f"{'kernel':60s} {'disp':>5s} {'avg us':>9s} {'GHz':>6s} {'MFMA busy %':>12s} {'FP8 TFLOP/s':>12s}")
+    for k, (n, t, ghz, util, tf) in mfma(a.dir, a.dispatch_mod, a.dispatch_rem).items():
+        print(f"{k[:60]:60s} {n:5d} {t:9.2f} {ghz:6.3f} {util:12.1f} {tf:12.1f}")
+
+
 def cmd_traffic(a):
-    fetch, kname = _pick(counters(a.fetch), a.kernel)
-    write, _ = _pick(counters(a.write), a.kernel)
+    fetch, kname = _pick(counters(a.fetch, a.dispatch_mod, a.dispatch_rem), a.kernel)
+    write, _ = _pick(counters(a.write, a.dispatch_mod, a.dispatch_rem), a.kernel)
     cfetch, cname = _pick(counters(a.copy_fetch), a.copy_kernel)
     cwrite, _ = _pick(counters(a.copy_write), a.copy_kernel)
     f_read = a.copy_bytes / (cfetch["FETCH_SIZE"] * 1024.0)
@@ -160,11 +222,17 @@ def main(argv=None):
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.set_defaults(fn=cmd_counters)
+    mf = sub.add_parser("mfma")
+    mf.add_argument("dir")
     t = sub.add_parser("traffic")
     for opt in ("--key", "--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write", "--copy-kernel"):
         t.add_argument(opt, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--sources", nargs="+", required=True)
+    for q in (mf, t):
+        q.add_argument("--dispatch-mod", type=int, default=None)
+        q.add_argument("--dispatch-rem", type=int, default=0)
+    mf.set_defaults(fn=cmd_mfma)
     t.set_defaults(fn=cmd_traffic)
     a = p.parse_args(argv)
     a.fn(a)
