@@ -347,238 +347,12 @@ __device__ __forceinline__ v16f mfma64(const v8i& fa, const v8i& fb, const v16f&
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, c, MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 0, 0, 0);
 }
 
-// K64 main loop (the grouped product at long K): K advances in steps of 64
-// through four LDS stages of 32 KB (A: 256 rows x 64 B, then B), filled by
-// direct loads issued three steps ahead of use, so the loads have three steps
-// to land (HBM-streamed expert weights need that lookahead; the K128 loop has
-// one). Step t:
-//   wait until stage t+1's loads have landed; barrier
-//   issue the loads of stage t+4 into the buffer stage t used (its fragments
-//   were read during step t-1)
-//   16 MFMAs on step t's fragments, each followed by one 16-byte fragment read
-//   for step t+1 and every other one by one direct load.
-// With MX each stage also has a 2 KB scale slot: the record dwords of the
-// stage's K128 step (one per A row and B row, in the layout mx_scales reads)
-// come with the stage's loads (two more per thread; the two K64 steps of a
-// K128 step each load it), and step t+1's scales are read during step t with
-// its fragments.
-namespace k64 {
-constexpr int BK = 64;
-constexpr int kStages = 4;
-constexpr int kStage = (big::BM + big::BN) * BK;    // 32 KB: A tile then B tile
-static_assert(kStages * kStage == big::kMain, "four stages below the scale area");
-// direct loads per thread per stage: 4 A + 4 B (+ the A and B scale dwords)
-template <bool MX>
-constexpr int loads_per_stage() { return MX ? 10 : 8; }
-constexpr int kSmemMx = big::kSmem + kStages * big::kMxStage;    // 138 KB
-}  // namespace k64
-
-// LDS layout of a stage: 64-byte rows of four 16-byte K chunks; chunk c of row r
-// sits in slot c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1). A fragment read touches one
-// chunk of each of 16 consecutive rows per 16 lanes; with this map those land
-// in 16 distinct 16-byte bank groups (and 8 consecutive rows in 8 distinct
-// groups of a 128-byte bank window).
-__device__ __forceinline__ int big_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 3) ^ ((row >> 3) & 1); }
-
-// Per-lane byte offsets of this thread's four A (or B) rows within a tile,
-// relative to the tile's first row: wavefront w, load i fills LDS rows
-// 16g .. 16g+15 with g = w*4 + i (1 KB: 16 bytes per lane, lane l at 16 l);
-// lane l fills row 16g + l/4, slot l%4, so it fetches the K chunk that belongs
-// in that slot. Rows past the last valid one are clamped to it (never stored).
-// 32-bit arithmetic: the large-tile kernels run only with ld < 2^24 (so that
-// 256 * ld fits in 32 bits).
-__device__ __forceinline__ void big_lane_offsets(uint32_t (&off)[4], int64_t ld, int64_t valid_rows) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const uint32_t ld32 = (uint32_t)ld;
-    const int last = (int)(valid_rows < 256 ? valid_rows : 256) - 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (wave * 4 + i) * 16 + (lane >> 2);
-        const int chunk = big_slot(row, lane & 3);      // the slot map is an involution
-        const uint32_t r = (uint32_t)(row < last ? row : last);
-        off[i] = r * ld32 + (uint32_t)(chunk * 16);
-    }
-}
-
-// MX scale records of the K64 loop: xa / xb are this thread's A and B record
-// dwords of K step 0 (rows mx_row(t) of the tiles); K128 step j is j * xsa /
-// j * xsb bytes further.
-struct K64Scales {
-    const uint8_t* xa;
-    const uint8_t* xb;
-    int64_t xsa, xsb;
-};
-
-// Scale slot of stage s.
-__device__ __forceinline__ uint8_t* k64_xslot(uint8_t* smem, int s) { return smem + big::kMxOff + s * big::kMxStage; }
-
-// The two scale-dword loads of the stage at K offset k0 into slot `xslot`.
-__device__ __forceinline__ void k64_issue_scales(uint8_t* xslot, const K64Scales& x, int64_t k0) {
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(xslot)) + wave * 256;
-    const int64_t j = k0 / 128;
-    lds_dma4(base, x.xa + j * x.xsa);
-    lds_dma4(base + 1024, x.xb + j * x.xsb);
-}
-
-// Issue the loads of one stage (K slice at k0) into the buffer at `stage`
-// (with MX, and the scale dwords into `xslot`).
-template <bool MX>
-__device__ __forceinline__ void big_issue_stage(const uint8_t* stage, const uint8_t* a, const uint32_t (&aoff)[4],
-                                                const uint8_t* b, const uint32_t (&boff)[4], int64_t k0,
-                                                uint8_t* xslot, const K64Scales& x) {
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage)) + wave * 4096;
-    const uint8_t* ak = a + k0;
-    const uint8_t* bk = b + k0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(base + i * 1024, ak + aoff[i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(base + big::BM * k64::BK + i * 1024, bk + boff[i]);
-    if constexpr (MX) k64_issue_scales(xslot, x, k0);
-}
-
-// Fragment of the 32x32x64 instruction from row `row` of a stage, in two
-// 16-byte halves h. With MX the instruction's own K order (lane half s holds
-// K 16s .. 16s + 15 and 32 + 16s .. 32 + 16s + 15; block s is K 32s .. 32s +
-// 31, scaled by lane half s's byte): half h is chunk s + 2h. Without block
-// scales lanes 0-31 take K bytes 0-31 and lanes 32-63 K bytes 32-63 (any order
-// common to A and B gives the same sums).
-template <bool MX>
-__device__ __forceinline__ u32x4 big_half(const uint8_t* tile, int row, int h) {
-    const int s = (threadIdx.x & 63) >> 5;
-    const int c = MX ? s + 2 * h : s * 2 + h;
-    return *reinterpret_cast<const u32x4*>(tile + row * 64 + (big_slot(row, c) << 4));
-}
-// Step t with t % 4 = S (compile-time): 16 matrix instructions on fc (step
-// t's fragments: A blocks 0-3, B blocks 4-7, read during step t-1; with MX sc
-// holds step t's A and B scale dwords, the K128 step's bytes 2 (t % 2) + s
-// selected by opsel). After each one the wavefront issues one 16-byte half of
-// step t+1's fragments into fn and, every other slot, one of the 8 direct loads
-// of stage t+4 (with MX, slots 1 and 9 issue the stage's scale loads and the
-// first two read step t+1's scales into sn): the LDS queue never backs up in
-// front of a matrix instruction (issue is in order). The loads are
-// unconditional so that the vmcnt depth stays fixed: past the last stage they
-// re-read the last K slice into buffers that are not read again.
-// sched_barrier(0) pins this order.
-template <int FA, int FB, int S, bool MX>
-__device__ __forceinline__ void k64_step(uint8_t* smem, v16f (&acc)[4][4], const v8i (&fc)[8], v8i (&fn)[8],
-                                         const u32x4 (&sc)[2], u32x4 (&sn)[2], const uint8_t* a,
-                                         const uint32_t (&aoff)[4], const uint8_t* b, const uint32_t (&boff)[4],
-                                         int64_t k4, const K64Scales& x) {
-    const uint8_t* nxt = smem + ((S + 1) & 3) * k64::kStage;
-    const uint8_t* nxt_b = nxt + big::BM * k64::BK;
-    // stage t+1 landed (t+2, t+3 may be in flight) and this wavefront's LDS
-    // reads are done: after the barrier other wavefronts load into the buffer
-    // this one read during step t-1
-    wait_vmcnt<2 * k64::loads_per_stage<MX>(), 0>();
-    __syncthreads();
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(smem + S * k64::kStage)) + wave * 4096;
-    u32x4 half[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = mfma64<FA, FB, MX, 2 * (S & 1)>(fc[mi], fc[4 + ni], acc[mi][ni], sc[0][mi], sc[1][ni]);
-        // half i of fragment j = i / 2 (B fragments first: the B tile is needed by every A block)
-        const int j = (i >> 1) < 4 ? 4 + (i >> 1) : (i >> 1) - 4;
-        half[i] = big_half<MX>(j < 4 ? nxt : nxt_b, big_row(j), i & 1);
-        if constexpr (MX) {
-            if (i < 2) sn[i] = mx_scales(k64_xslot(smem, (S + 1) & 3), i);
-        }
-        if ((i & 1) == 0) {
-            const int l = i >> 1;                        // load l: A rows for l < 4, B rows for l >= 4
-            if (l < 4)
-                lds_dma16(dma_base + l * 1024, a + k4 + aoff[l]);
-            else
-                lds_dma16(dma_base + big::BM * k64::BK + (l - 4) * 1024, b + k4 + boff[l - 4]);
-        } else if (MX && (i == 1 || i == 9)) {
-            const uint32_t xbase =
-                __builtin_amdgcn_readfirstlane(lds_addr(k64_xslot(smem, S))) + wave * 256 + (i == 1 ? 0 : 1024);
-            lds_dma4(xbase, i == 1 ? x.xa + (k4 / 128) * x.xsa : x.xb + (k4 / 128) * x.xsb);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-        const int j = f < 4 ? 4 + f : f - 4;            // fragment f was read in halves 2f, 2f+1
-        fn[j] = big_join(half[2 * f], half[2 * f + 1]);
-    }
-}
-
-// sa_lane / sb_lane: this thread's row / column scale (thread t: tile row t,
-// tile column t). They are loaded straight into the scale area of LDS with the
-// first loads of the tile, so no register holds them across the main loop.
-// With MX the scale area holds 1 and x carries the block-scale records.
-// k % 256 == 0, k > 0.
-template <int FA, int FB, bool MX>
-__device__ __forceinline__ void k64_mainloop(uint8_t* smem, const uint8_t* a, int64_t lda, int64_t a_rows,
-                                             const uint8_t* b, int64_t ldb, int64_t b_rows, int64_t k,
-                                             const float* sa_lane, const float* sb_lane, const K64Scales& x,
-                                             v16f (&acc)[4][4]) {
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-    uint32_t aoff[4], boff[4];
-    big_lane_offsets(aoff, lda, a_rows);
-    big_lane_offsets(boff, ldb, b_rows);
-    constexpr int64_t BK = k64::BK;
-    constexpr int L = k64::loads_per_stage<MX>();
-    const int64_t nk = k / BK;
-    const int64_t last = (nk - 1) * BK;
-    auto kof = [&](int64_t s) { return s < nk ? s * BK : last; };
-    // prologue: the scales, then stages 0..3 in flight; wait for the scales and
-    // stage 0 (loads complete in order) and read step 0's fragments
-    if constexpr (MX) {
-        float* s = reinterpret_cast<float*>(smem + big::kScaleOff);
-        s[threadIdx.x] = 1.0f;
-        s[256 + threadIdx.x] = 1.0f;
-    } else {
-        const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kScaleOff)) + wave * 256;
-        lds_dma4(sbase, sa_lane);
-        lds_dma4(sbase + 1024, sb_lane);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        big_issue_stage<MX>(smem + s * k64::kStage, a, aoff, b, boff, kof(s), k64_xslot(smem, s), x);
-    wait_vmcnt<3 * L>();
-    __syncthreads();
-    v8i f0[8], f1[8];
-    u32x4 s0[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}}, s1[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint8_t* t0 = j < 4 ? smem : smem + big::BM * k64::BK;
-        f0[j] = big_join(big_half<MX>(t0, big_row(j), 0), big_half<MX>(t0, big_row(j), 1));
-    }
-    if constexpr (MX) {
-        s0[0] = mx_scales(k64_xslot(smem, 0), 0);
-        s0[1] = mx_scales(k64_xslot(smem, 0), 1);
-    }
-    // four steps per iteration: the stage index (t % 4) and the fragment set
-    // (t % 2) stay compile-time
-    for (int64_t t = 0; t < nk; t += 4) {
-        k64_step<FA, FB, 0, MX>(smem, acc, f0, f1, s0, s1, a, aoff, b, boff, kof(t + 4), x);
-        k64_step<FA, FB, 1, MX>(smem, acc, f1, f0, s1, s0, a, aoff, b, boff, kof(t + 5), x);
-        k64_step<FA, FB, 2, MX>(smem, acc, f0, f1, s0, s1, a, aoff, b, boff, kof(t + 6), x);
-        k64_step<FA, FB, 3, MX>(smem, acc, f1, f0, s1, s0, a, aoff, b, boff, kof(t + 7), x);
-    }
-    // (k % 256 == 0: whole iterations only; a remainder's join costs
-    // accumulator spills at the epilogue)
-    wait_vmcnt<0>();                                     // no load may still land in LDS after this
-}
-
-// ---------------------------------------------------------------------------
-// K128 main loop: the same 256 x 256 tile and MFMA blocking, but K advances 128
-// bytes per step through two 64 KB LDS stages (A: 256 rows x 128 B, then B).
-// Each direct load brings whole 128-byte row segments (8 lanes per row), so
-// the L1 sends full-line requests to L2: on gfx950 the load path's throughput
-// goes with the number of requests (64-byte row segments cost ~13% of the
-// GEMM's time at these shapes). With two stages the loads of step p+2 are
+// K128 main loop of the large-tile kernels: K advances 128 bytes per step
+// through two 64 KB LDS stages (A: 256 rows x 128 B, then B). Each direct load
+// brings whole 128-byte row segments (8 lanes per row), so the L1 sends
+// full-line requests to L2: on gfx950 the load path's throughput goes with the
+// number of requests (a loop of 64-deep steps, whose loads move 64-byte row
+// segments, was ~13% slower at these shapes). With two stages the loads of step p+2 are
 // issued during the second half of step p and waited for in the middle of
 // step p+1 (a barrier between the two halves of each step); step p's
 // second-half fragments are read during its first 16 MFMAs and step p+1's
@@ -963,13 +737,13 @@ static_assert((kMaxGroupsBig + 1) * 8 <= big::kMain, "group prefix sums fit in t
 // With MX the operands carry E8M0 block scales instead of sa / sb: xa (row r
 // of a in the records of xa with ld_xa) and, for group e, xb + e *
 // xb_group_stride (bytes) with ld_xb.
-template <int FA, int FB, bool OUT_F32, bool K64, bool MX>
+template <int FA, int FB, bool OUT_F32, bool MX>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb, int64_t b_group_stride,
     const int64_t* __restrict__ offsets, int g, int64_t total_m, int64_t n, int64_t k, const float* __restrict__ sa,
     const float* __restrict__ sb, void* __restrict__ d, int64_t ldd, int vec_out, const uint8_t* __restrict__ xa,
     int64_t ld_xa, const uint8_t* __restrict__ xb, int64_t ld_xb, int64_t xb_group_stride) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? (K64 ? k64::kSmemMx : big::kSmemMx) : big::kSmem];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? big::kSmemMx : big::kSmem];
     const int64_t tiles_n = (n + big::BN - 1) / big::BN;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
@@ -1041,21 +815,13 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
         const int rt = mx_row(t);
         const uint8_t* xa_lane = xa + 4 * (row0 + rt < hi ? row0 + rt : hi - 1);
         const uint8_t* xb_lane = xb + (int64_t)grp * xb_group_stride + 4 * (col0 + rt < n ? col0 + rt : n - 1);
-        if constexpr (K64)
-            k64_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
-                                       nullptr, nullptr, K64Scales{xa_lane, xb_lane, 4 * ld_xa, 4 * ld_xb}, acc);
-        else
-            k128_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
-                                        nullptr, nullptr, xa_lane, xb_lane, 4 * ld_xa, 4 * ld_xb, acc);
+        k128_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, nullptr,
+                                    nullptr, xa_lane, xb_lane, 4 * ld_xa, 4 * ld_xb, acc);
     } else {
         const float* sa_lane = sa + (row0 + t < hi ? row0 + t : hi - 1);
         const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
-        if (K64)
-            k64_mainloop<FA, FB, false>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
-                                        sa_lane, sb_lane, K64Scales{nullptr, nullptr, 0, 0}, acc);
-        else
-            k128_mainloop<FA, FB, false>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k,
-                                         sa_lane, sb_lane, nullptr, nullptr, 0, 0, acc);
+        k128_mainloop<FA, FB, false>(smem, a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, sa_lane,
+                                     sb_lane, nullptr, nullptr, 0, 0, acc);
     }
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, hi - row0, col0, n - col0, vec_out);
 }
@@ -1161,18 +927,10 @@ hipError_t grouped_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_
         ldb < (1 << 24)) {
         const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
         const int64_t grid = ((total_m + big::BM - 1) / big::BM + g) * ((n + big::BN - 1) / big::BN);
-        // long K (each expert's weights streamed from HBM): the K64 loop's deeper
-        // lookahead wins (c4, k = 7168: 1495 vs 1392 TFLOP/s); short K: K128
-        // (k = 2048: 1327 vs 1211)
         const uint8_t* none = nullptr;
-        if (k >= 4096)
-            hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, true, false>), dim3((unsigned)grid), dim3(256), 0,
-                               st, a, lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out, none,
-                               (int64_t)0, none, (int64_t)0, (int64_t)0);
-        else
-            hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false, false>), dim3((unsigned)grid), dim3(256), 0,
-                               st, a, lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out, none,
-                               (int64_t)0, none, (int64_t)0, (int64_t)0);
+        hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false>), dim3((unsigned)grid), dim3(256), 0, st, a,
+                           lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out, none, (int64_t)0,
+                           none, (int64_t)0, (int64_t)0);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((k_grouped_gemm<FA, FB, OUT_F32>), dim3((unsigned)tiles), dim3(kThreads), 0, st, a, lda, b, ldb,
@@ -1204,15 +962,9 @@ hipError_t grouped_mx_typed(const uint8_t* a, int64_t lda, const uint8_t* xa, in
     const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
     const int64_t grid = ((total_m + big::BM - 1) / big::BM + g) * ((n + big::BN - 1) / big::BN);
     const float* none = nullptr;
-    // long K: the K64 loop's deeper lookahead, as for the rowwise-scaled product
-    if (k >= 4096)
-        hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, true, true>), dim3((unsigned)grid), dim3(256), 0, st,
-                           a, lda, b, ldb, stride, offsets, g, total_m, n, k, none, none, d, ldd, vec_out, xa, ld_xa,
-                           xb, ld_xb, xstride);
-    else
-        hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false, true>), dim3((unsigned)grid), dim3(256), 0, st,
-                           a, lda, b, ldb, stride, offsets, g, total_m, n, k, none, none, d, ldd, vec_out, xa, ld_xa,
-                           xb, ld_xb, xstride);
+    hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, true>), dim3((unsigned)grid), dim3(256), 0, st, a, lda, b,
+                       ldb, stride, offsets, g, total_m, n, k, none, none, d, ldd, vec_out, xa, ld_xa, xb, ld_xb,
+                       xstride);
     return hipGetLastError();
 }
 

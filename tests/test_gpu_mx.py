@@ -248,10 +248,9 @@ def test_grouped_gemm_mx_parity(fp8, orc, sizes, n, k, fa, fb, out_f32):
 
 
 def test_grouped_gemm_mx_long_k_random_scales(fp8, orc):
-    """The long-K grouped product (k >= 4096 takes the K64 loop, whose two
-    64-deep steps share one record dword) with codes drawn uniformly and scale
-    bytes drawn independently per block: a scale byte taken from the wrong
-    step, block or stage shows at once."""
+    """The long-K grouped product (32 K steps through the two LDS stages) with
+    codes drawn uniformly and scale bytes drawn independently per block: a
+    scale byte taken from the wrong step, block or stage shows at once."""
     rng = np.random.default_rng(23)
     sizes, n, k = [260, 0, 1, 300], 270, 4096
     offsets = offsets_of(sizes)
