@@ -2,7 +2,8 @@
 
 A step is one pass of the layer over one batch of synthetic input, inputs
 resident in HBM: quantize the activation and the weight (amax -> scale ->
-saturating cast) and run the scaled FP8 GEMM. The default workload is the
+saturating cast; rowwise, both tensors in one launch since they share K) and
+run the scaled FP8 GEMM. The default workload is the
 Llama3-8B FFN up-projection, rowwise e4m3: X bf16 [8192 x 4096] (Student-t,
 unit variance), W bf16 [14336 x 4096] ~ N(0, 0.02^2), bf16 output.
 
@@ -79,7 +80,8 @@ class Step:
             self.sx, self.sw = E(m, device=dev), E(n, device=dev)
             self.d = E((m, n), dtype=torch.bfloat16, device=dev)
             self.mnk = [(m, n, k)]
-            self.calls = [("quantize_row X", m * k, m), ("quantize_row W", n * k, n), ("gemm", None, 0)]
+            # X and W share K: one rowwise-cast launch for both
+            self.calls = [("quantize_row X+W (one launch)", m * k + n * k, m + n), ("gemm", None, 0)]
             self.desc = {"c1": "rowwise FP8 linear Y = X W^T, X bf16 [256x512] N(0,1) with 2 rows x50, "
                                "W bf16 [512x512] N(0,0.02^2); e4m3 rowwise both operands; bf16 out",
                          "c2": "Llama3-8B FFN up-proj rowwise FP8: X bf16 [8192x4096] Student-t(4)/sqrt(2), "
@@ -137,7 +139,8 @@ class Step:
             self.sx, self.sw = E(m, device=dev), E(g * n, device=dev)
             self.d = E((m, n), dtype=torch.bfloat16, device=dev)
             self.mnk = [(m, n, k)]
-            self.calls = [("quantize_row tokens", m * k, m), ("quantize_row expert W", g * n * k, g * n),
+            # tokens and expert weights share K: one rowwise-cast launch for both
+            self.calls = [("quantize_row tokens+expert W (one launch)", m * k + g * n * k, m + g * n),
                           ("grouped_gemm", None, 0)]
             self.desc = ("DeepSeek-V3 MoE grouped GEMM, one GPU's share: 32 experts Zipf(1.1) counts (3 empty), "
                          "tokens bf16 [16384x7168] N(0,1), W_e bf16 [2048x7168] N(0,0.006^2); e4m3 rowwise; bf16 out")
@@ -257,13 +260,11 @@ class Step:
         f = self.fp8
         ev[0].record()
         if self.name in ("c1", "c2"):
-            f.fp8_quantize_row(self.x, f.E4M3, 0, self.qx, self.sx)
+            f.fp8_quantize_row_batch([self.x, self.w], f.E4M3, 0, [self.qx, self.qw], [self.sx, self.sw])
             ev[1].record()
-            f.fp8_quantize_row(self.w, f.E4M3, 0, self.qw, self.sw)
-            ev[2].record()
             f.fp8_gemm_scaled(self.qx, f.E4M3, self.qw, f.E4M3, self.sx, f.SCALE_VECTOR, self.sw, f.SCALE_VECTOR,
                               self.d)
-            ev[3].record()
+            ev[2].record()
         elif self.name == "c2bw":
             f.fp8_blockwise_quantize_act(self.x, f.E4M3, self.qx, self.sx)
             ev[1].record()
@@ -283,13 +284,11 @@ class Step:
                                        self.scale_inv)
             ev[4].record()
         elif self.name == "c4":
-            f.fp8_quantize_row(self.x, f.E4M3, 0, self.qx, self.sx)
+            f.fp8_quantize_row_batch([self.x, self.w], f.E4M3, 0, [self.qx, self.qw], [self.sx, self.sw])
             ev[1].record()
-            f.fp8_quantize_row(self.w, f.E4M3, 0, self.qw, self.sw)
-            ev[2].record()
             f.fp8_grouped_gemm_scaled(self.qx, f.E4M3, self.qw.view(self.g, self.n, self.k), f.E4M3, self.offsets,
                                       self.sx, self.sw.view(self.g, self.n), self.d)
-            ev[3].record()
+            ev[2].record()
         elif self.name == "c4mx":
             g, n, k = self.g, self.n, self.k
             f.fp8_mx_quantize_row(self.x, f.E4M3, self.qx, self.sx)

@@ -18,7 +18,7 @@ __all__ = [
     "E4M3", "E5M2", "E4M3_FNUZ", "E5M2_FNUZ", "AXIS_TENSOR", "AXIS_ROW", "AXIS_COL",
     "AMAX_MOST_RECENT", "AMAX_MAX", "SCALE_TENSOR", "SCALE_VECTOR", "OUT_BF16", "OUT_F32",
     "Fp8Error", "LIB_PATH", "lib", "fp8_query_device", "fp8_status_string", "fp8_amax",
-    "fp8_quantize_tensor", "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update",
+    "fp8_quantize_tensor", "fp8_quantize_row", "fp8_quantize_row_batch", "fp8_quantize_col", "fp8_delayed_scale_update",
     "fp8_gemm_scaled", "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "grouped_layout_width", "GROUP_K_ALIGN", "MX_BLOCK", "fp8_mx_quantize_row", "fp8_gemm_mx",
     "fp8_grouped_gemm_mx", "mx_scale_records", "fp8_moe_route", "fp8_moe_permute_quantize_row",
@@ -34,7 +34,7 @@ OUT_BF16, OUT_F32 = 0, 1
 
 EXPORTED_SYMBOLS = (
     "fp8_query_device", "fp8_status_string", "fp8_last_error", "fp8_amax", "fp8_quantize_tensor",
-    "fp8_quantize_row", "fp8_quantize_col", "fp8_delayed_scale_update", "fp8_gemm_scaled",
+    "fp8_quantize_row", "fp8_quantize_row_batch", "fp8_quantize_col", "fp8_delayed_scale_update", "fp8_gemm_scaled",
     "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "fp8_mx_quantize_row", "fp8_gemm_mx", "fp8_grouped_gemm_mx", "fp8_moe_route", "fp8_moe_permute_quantize_row",
     "fp8_swiglu_quantize_row", "fp8_moe_unpermute_combine", "fp8_blockwise_quantize_act",
@@ -42,6 +42,7 @@ EXPORTED_SYMBOLS = (
 )
 
 GROUP_K_ALIGN = 256     # FP8_GROUP_K_ALIGN of the C header
+MAX_ROW_BATCH = 8       # FP8_MAX_ROW_BATCH of the C header
 MX_BLOCK = 32           # FP8_MX_BLOCK of the C header
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8amax.so")
@@ -70,6 +71,7 @@ def _load():
         "fp8_amax": [P, I64, I64, I64, I, P, P],
         "fp8_quantize_tensor": [P, I64, I64, I64, I, I32, P, P, I64, P, P, P],
         "fp8_quantize_row": [P, I64, I64, I64, I, I32, P, I64, P, P, P, P],
+        "fp8_quantize_row_batch": [I32, P, P, I64, P, I, I32, P, P, P, P, P],
         "fp8_quantize_col": [P, I64, I64, I64, I, I32, P, I64, P, P, I32, P],
         "fp8_delayed_scale_update": [P, P, P, I64, I32, I, I32, I, P, P, P],
         "fp8_gemm_scaled": [P, I, I64, P, I, I64, I64, I64, I64, P, I, P, I, P, I, I64, P],
@@ -165,6 +167,28 @@ def fp8_quantize_row(x, fmt, margin, q, scale_inv_out, amax_out=None, col_amax_o
     _, _, ldq = _mat(q, "q", 1)
     _check(lib.fp8_quantize_row(_ptr(x), rows, cols, ldx, fmt, margin, _ptr(q), ldq, _ptr(scale_inv_out),
                                 _ptr(amax_out), _ptr(col_amax_out), _stream(x)))
+
+
+def fp8_quantize_row_batch(xs, fmt, margin, qs, scale_inv_outs, amax_outs=None):
+    """Rowwise casts of the bf16 tensors xs (same number of columns) in one launch."""
+    count = len(xs)
+    if not (len(qs) == len(scale_inv_outs) == count) or (amax_outs is not None and len(amax_outs) != count):
+        raise ValueError("xs, qs, scale_inv_outs (and amax_outs) must have the same length")
+    if count == 0:
+        raise ValueError("no tensors")
+    shapes = [_bf16(x) for x in xs]
+    cols = shapes[0][1]
+    if any(c != cols for _, c, _ in shapes):
+        raise ValueError("the tensors of one batch share their number of columns")
+    P64, PP = ctypes.c_int64 * count, ctypes.c_void_p * count
+    xp = PP(*[_ptr(x) for x in xs])
+    rows = P64(*[r for r, _, _ in shapes])
+    ldx = P64(*[ld for _, _, ld in shapes])
+    qp = PP(*[_ptr(q) for q in qs])
+    ldq = P64(*[_mat(q, "q", 1)[2] for q in qs])
+    sp = PP(*[_ptr(s) for s in scale_inv_outs])
+    ap = PP(*[_ptr(a) for a in amax_outs]) if amax_outs is not None else None
+    _check(lib.fp8_quantize_row_batch(count, xp, rows, cols, ldx, fmt, margin, qp, ldq, sp, ap, _stream(xs[0])))
 
 
 def fp8_quantize_col(x, fmt, margin, qt, scale_inv_out, col_amax, col_amax_ready=False):

@@ -227,13 +227,10 @@ __global__ __launch_bounds__(kBlock) void k_amax_tensor_reg(const uint16_t* __re
 // per lane): read once, amax, scale, cast, write once. NT: nontemporal loads
 // (x streamed), unless another pass reads x right after.
 template <int F, int MAXC, bool NT>
-__global__ __launch_bounds__(kBlock) void k_quant_row_reg(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
-                                                          int64_t ldx, int margin, uint8_t* __restrict__ q,
-                                                          int64_t ldq, float* __restrict__ scale_inv,
-                                                          float* __restrict__ amax_out) {
+__device__ __forceinline__ void quant_row_one(const uint16_t* __restrict__ x, int64_t row, int64_t cols, int64_t ldx,
+                                              int margin, uint8_t* __restrict__ q, int64_t ldq,
+                                              float* __restrict__ scale_inv, float* __restrict__ amax_out) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (row >= rows) return;
     const int nch = (int)(cols >> 3);
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
     uint4 v[MAXC];
@@ -265,6 +262,63 @@ __global__ __launch_bounds__(kBlock) void k_quant_row_reg(const uint16_t* __rest
             if (ch < nch) qr[ch] = encode8<F, false>(v[c], s);
         }
     }
+}
+
+template <int F, int MAXC, bool NT>
+__global__ __launch_bounds__(kBlock) void k_quant_row_reg(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                          int64_t ldx, int margin, uint8_t* __restrict__ q,
+                                                          int64_t ldq, float* __restrict__ scale_inv,
+                                                          float* __restrict__ amax_out) {
+    const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    quant_row_one<F, MAXC, NT>(x, row, cols, ldx, margin, q, ldq, scale_inv, amax_out);
+}
+
+// Rowwise casts of up to kMaxRowBatch tensors with the same number of columns
+// (a linear layer's activation and weight share K) in one launch: tensor j
+// owns workgroups first[j] .. first[j+1]-1, one wavefront per row as above.
+// One launch instead of one per tensor saves a launch gap and one ramp-up and
+// drain of the memory pipeline. The arrays are indexed through compare-select
+// chains on the wave-uniform tensor index (no private-memory copy).
+constexpr int kMaxRowBatch = 8;
+struct RowBatch {
+    const uint16_t* x[kMaxRowBatch];
+    uint8_t* q[kMaxRowBatch];
+    float* scale_inv[kMaxRowBatch];
+    float* amax[kMaxRowBatch];
+    int64_t rows[kMaxRowBatch];
+    int64_t ldx[kMaxRowBatch];
+    int64_t ldq[kMaxRowBatch];
+    int64_t first[kMaxRowBatch + 1];
+    int count;
+};
+
+template <typename T>
+__device__ __forceinline__ T batch_pick(const T (&a)[kMaxRowBatch], int j) {
+    T r = a[0];
+#pragma unroll
+    for (int i = 1; i < kMaxRowBatch; ++i)
+        if (i == j) r = a[i];
+    return r;
+}
+
+template <int F, int MAXC>
+__global__ __launch_bounds__(kBlock) void k_quant_row_batch(RowBatch b, int64_t cols, int margin) {
+    const int64_t bid = blockIdx.x;
+    // the last tensor whose first workgroup is at or before this one (an empty
+    // tensor shares its start with the next, which then wins)
+    int j = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxRowBatch; ++i)
+        if (i < b.count && bid >= b.first[i]) j = i;
+    int64_t first = b.first[0];
+#pragma unroll
+    for (int i = 1; i < kMaxRowBatch; ++i)
+        if (i == j) first = b.first[i];
+    const int64_t row = (bid - first) * kWaves + (threadIdx.x >> 6);
+    if (row >= batch_pick(b.rows, j)) return;
+    quant_row_one<F, MAXC, true>(batch_pick(b.x, j), row, cols, batch_pick(b.ldx, j), margin, batch_pick(b.q, j),
+                                 batch_pick(b.ldq, j), batch_pick(b.scale_inv, j), batch_pick(b.amax, j));
 }
 
 // Rows too long for registers, or unaligned layouts: two passes over the row
@@ -1378,6 +1432,64 @@ hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64
         default: return CALL(kE5M2Fnuz);
     }
 #undef CALL
+}
+
+template <int F>
+hipError_t quant_row_batch_fmt(const RowBatch& b, int64_t blocks, int64_t cols, int margin, hipStream_t st) {
+    const int64_t per_lane = (cols / 8 + 63) / 64;
+#define FP8_ROW_BATCH_CASE(C)                                                                                      \
+    if (per_lane <= C) {                                                                                           \
+        hipLaunchKernelGGL((k_quant_row_batch<F, C>), dim3((unsigned)blocks), dim3(kBlock), 0, st, b, cols, margin); \
+        return hipGetLastError();                                                                                  \
+    }
+    FP8_ROW_BATCH_CASE(1)
+    FP8_ROW_BATCH_CASE(2)
+    FP8_ROW_BATCH_CASE(4)
+    FP8_ROW_BATCH_CASE(8)
+    FP8_ROW_BATCH_CASE(16)
+    FP8_ROW_BATCH_CASE(32)
+#undef FP8_ROW_BATCH_CASE
+    return hipErrorInvalidValue;   // (the caller checked per_lane <= 32)
+}
+
+hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
+                                  const int64_t* ldx, int fmt, int margin, uint8_t* const* q, const int64_t* ldq,
+                                  float* const* scale_inv, float* const* amax_out, hipStream_t st) {
+    // one launch when every tensor takes the register kernel (vector layout,
+    // rows of at most 32 chunks per lane); otherwise one launch per tensor
+    bool one = count <= kMaxRowBatch && cols > 0 && cols % 8 == 0 && (cols / 8 + 63) / 64 <= 32;
+    for (int j = 0; j < count && one; ++j)
+        one = is_aligned(x[j], 16) && is_aligned(q[j], 8) && ldx[j] % 8 == 0 && ldq[j] % 8 == 0;
+    if (!one) {
+        for (int j = 0; j < count; ++j) {
+            const hipError_t e = launch_quant_row(x[j], rows[j], cols, ldx[j], fmt, margin, q[j], ldq[j],
+                                                  scale_inv[j], amax_out ? amax_out[j] : nullptr, false, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    RowBatch b{};
+    b.count = count;
+    int64_t blocks = 0;
+    for (int j = 0; j < count; ++j) {
+        b.x[j] = x[j];
+        b.q[j] = q[j];
+        b.scale_inv[j] = scale_inv[j];
+        b.amax[j] = amax_out ? amax_out[j] : nullptr;
+        b.rows[j] = rows[j];
+        b.ldx[j] = ldx[j];
+        b.ldq[j] = ldq[j];
+        b.first[j] = blocks;
+        blocks += (rows[j] + kWaves - 1) / kWaves;
+    }
+    for (int j = count; j <= kMaxRowBatch; ++j) b.first[j] = blocks;
+    if (blocks == 0) return hipSuccess;
+    switch (fmt) {
+        case kE4M3: return quant_row_batch_fmt<kE4M3>(b, blocks, cols, margin, st);
+        case kE5M2: return quant_row_batch_fmt<kE5M2>(b, blocks, cols, margin, st);
+        case kE4M3Fnuz: return quant_row_batch_fmt<kE4M3Fnuz>(b, blocks, cols, margin, st);
+        default: return quant_row_batch_fmt<kE5M2Fnuz>(b, blocks, cols, margin, st);
+    }
 }
 
 hipError_t launch_quant_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,

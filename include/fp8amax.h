@@ -139,6 +139,26 @@ fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int
                               int32_t margin, uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out,
                               float* col_amax_out, void* stream);
 
+/* Rowwise quantization of several tensors that share cols in one launch
+ * ([Titan]: fused quantization kernels cut the launches and HBM round trips
+ * of the FP8 path; a linear layer's activation [m x k] and weight [n x k]
+ * share k). Tensor j (j < count) is x[j] (bf16 [rows[j] x cols], ldx[j]) with
+ * codes q[j] (ldq[j]), scale_inv_out[j] [rows[j]] (required when rows[j] > 0)
+ * and amax_out[j] [rows[j]] (amax_out itself, or any entry, may be NULL);
+ * every result equals what fp8_quantize_row gives for that tensor alone (no
+ * column-amax side output here). x, rows, ldx, q, ldq, scale_inv_out, amax_out
+ * are HOST arrays of count entries (read during the call); the pointers in them
+ * are device memory. count: 1..FP8_MAX_ROW_BATCH. All tensors share fmt and
+ * margin. One launch when every tensor has the vector layout (x 16-byte and q
+ * 8-byte aligned, ldx, ldq, cols multiples of 8) and cols <= 16384; otherwise
+ * one launch per tensor. Errors: any tensor's argument error (as
+ * fp8_quantize_row) fails the whole call before anything is enqueued. */
+#define FP8_MAX_ROW_BATCH 8
+fp8_status_t fp8_quantize_row_batch(int32_t count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
+                                    const int64_t* ldx, fp8_format_t fmt, int32_t margin, uint8_t* const* q,
+                                    const int64_t* ldq, float* const* scale_inv_out, float* const* amax_out,
+                                    void* stream);
+
 /* Colwise quantization with transposed output ([Titan] colwise scales, whose
  * non-coalesced writes the post singles out). One scale per column of x
  * (reduction over the rows, e.g. over tokens), and the codes are written

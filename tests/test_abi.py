@@ -181,6 +181,28 @@ def test_quantizers_reject_bad_arguments(fp8):
     assert _call(fp8, "fp8_amax", FAKE, 4, 16, 16, 3, FAKE, None)[0] == 1
 
 
+def test_quantize_row_batch_rejects_bad_arguments(fp8):
+    f = "fp8_quantize_row_batch"
+    PP, P64 = ctypes.c_void_p * 2, ctypes.c_int64 * 2
+    x, q, s = PP(FAKE, FAKE), PP(FAKE, FAKE), PP(FAKE, FAKE)
+    rows, ld = P64(4, 8), P64(16, 16)
+
+    def call(count=2, x=x, rows=rows, cols=16, ldx=ld, fmt=0, margin=0, q=q, ldq=ld, s=s, a=None):
+        return _call(fp8, f, count, x, rows, cols, ldx, fmt, margin, q, ldq, s, a, None)
+
+    st, msg = call(count=0)
+    assert st == 1 and "count" in msg
+    assert call(count=fp8.MAX_ROW_BATCH + 1)[0] == 1
+    assert call(x=None)[0] == 1                                   # a host array is missing
+    assert call(margin=33)[0] == 1
+    assert call(fmt=9)[0] == 1
+    st, msg = call(ldx=P64(16, 8))                                # tensor 1: ld smaller than the row
+    assert st == 1 and "leading dimension" in msg
+    assert call(s=PP(FAKE, None))[0] == 1                         # tensor 1 has rows but no scale output
+    assert call(x=PP(FAKE, ctypes.c_void_p(0x10001)))[0] == 2     # tensor 1 misaligned for bf16
+    assert call(a=PP(None, ctypes.c_void_p(0x10002)))[0] == 2     # misaligned amax output
+
+
 def test_delayed_update_rejects_bad_arguments(fp8):
     f = "fp8_delayed_scale_update"
     assert _call(fp8, f, FAKE, FAKE, FAKE, 2, 0, 1, 0, 0, FAKE, FAKE, None)[0] == 1        # L = 0

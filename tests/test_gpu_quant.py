@@ -372,3 +372,106 @@ def test_quantizers_deterministic(fp8):
     d = gpu_col(fp8, xb, 1)
     for u, v in zip(c, d):
         assert np.array_equal(u, v)
+
+
+# ------------------------------------------------------------ batched rowwise --
+
+def gpu_row_batch(fp8, xbs, fmt, margin=0, ld_pad=0, amax_mask=None):
+    """fp8_quantize_row_batch over the tensors xbs (numpy bf16 bits, same cols);
+    ld_pad > 0 pads the code rows (a layout that takes one launch per tensor)."""
+    cols = xbs[0].shape[1]
+    xs = [dev_bf16(xb) for xb in xbs]
+    views, bufs = [], []
+    for xb in xbs:
+        v, buf, org = guarded(xb.shape[0], cols, torch.uint8, ld=cols + ld_pad if ld_pad else cols)
+        views.append(v)
+        bufs.append((buf, org, xb.shape[0]))
+    sis = [torch.full((max(xb.shape[0], 1),), -1.0, device="cuda:0") for xb in xbs]
+    ams = [torch.full((max(xb.shape[0], 1),), -1.0, device="cuda:0") for xb in xbs]
+    amax_outs = [a if (amax_mask is None or amax_mask[j]) else None for j, a in enumerate(ams)]
+    fp8.fp8_quantize_row_batch(xs, fmt, margin, views, sis, amax_outs)
+    torch.cuda.synchronize()
+    for buf, org, rows in bufs:
+        check_guard(buf, org, rows, cols)
+    return ([v.cpu().numpy() for v in views], [s.cpu().numpy()[:xb.shape[0]] for s, xb in zip(sis, xbs)],
+            [a.cpu().numpy()[:xb.shape[0]] for a, xb in zip(ams, xbs)])
+
+
+def check_row_batch(orc, xbs, fmt, margin, got, amax_mask=None):
+    qs, sis, ams = got
+    for j, xb in enumerate(xbs):
+        oq, osi, oam = orc.quantize_row(xb, fmt, margin)
+        assert_codes_equal(qs[j], oq, f"codes of tensor {j} {xb.shape}")
+        assert_f32_bits_equal(sis[j], osi, f"scale_inv of tensor {j}")
+        if amax_mask is None or amax_mask[j]:
+            assert_f32_bits_equal(ams[j], oam, f"amax of tensor {j}")
+        else:
+            assert np.all(ams[j] == -1.0), f"amax of tensor {j} was written although not requested"
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_quantize_row_batch_parity(fp8, orc, fmt):
+    """Eight tensors in one launch: ragged row counts (not multiples of the four
+    rows of a workgroup), empty tensors in the middle and at the end, one row."""
+    cols = 136
+    sizes = [5, 0, 64, 1, 130, 3, 0, 257]
+    xbs = [rand_bf16(r, cols, seed=100 + j) for j, r in enumerate(sizes)]
+    mask = [True, True, False, True, True, False, True, True]
+    say("row batch", NAMES[fmt], sizes, cols)
+    got = gpu_row_batch(fp8, xbs, fmt, 1, amax_mask=mask)
+    check_row_batch(orc, xbs, fmt, 1, got, mask)
+
+
+@pytest.mark.parametrize("cols", [8, 4096, 14336, 16384])
+def test_quantize_row_batch_linear_pair(fp8, orc, cols):
+    """A linear layer's activation and weight (same K) at row lengths from one
+    chunk per lane to the longest row held in registers."""
+    m, n = (1030, 2050) if cols <= 4096 else (70, 133)
+    xbs = [rand_bf16(m, cols, seed=7), rand_bf16(n, cols, seed=8)]
+    say("row batch pair", (m, n, cols))
+    got = gpu_row_batch(fp8, xbs, 0, 0)
+    check_row_batch(orc, xbs, 0, 0, got)
+
+
+@pytest.mark.parametrize("fmt", [0, 3])
+def test_quantize_row_batch_per_tensor_layouts(fp8, orc, fmt):
+    """Padded code rows (ldq not a multiple of 8), rows longer than the register
+    kernels hold, and special values: one launch per tensor, same results."""
+    say("row batch fallback", NAMES[fmt])
+    xbs = [rand_bf16(9, 40, seed=1), np.ascontiguousarray(np.pad(special_rows(), ((0, 0), (0, 24))))]
+    got = gpu_row_batch(fp8, xbs, fmt, 2, ld_pad=3)
+    check_row_batch(orc, xbs, fmt, 2, got)
+    long = [rand_bf16(3, 16392, seed=2), rand_bf16(5, 16392, seed=3)]
+    got = gpu_row_batch(fp8, long, fmt, 0)
+    check_row_batch(orc, long, fmt, 0, got)
+
+
+def test_quantize_row_batch_special_values(fp8, orc):
+    xbs = [special_rows(), special_rows()[::-1].copy()]
+    for fmt in FORMATS:
+        say("row batch specials", NAMES[fmt])
+        got = gpu_row_batch(fp8, xbs, fmt, 0)
+        check_row_batch(orc, xbs, fmt, 0, got)
+
+
+def test_quantize_row_batch_matches_single_calls_at_llama3_8b(fp8):
+    """X [8192 x 4096] and W [14336 x 4096] of the Llama3-8B up-projection:
+    the batched launch gives the bytes of two fp8_quantize_row calls."""
+    w = workloads.c2()
+    say("row batch c2 full size")
+    x, wt = dev_bf16(w["x"]), dev_bf16(w["w"])
+    outs = []
+    for batched in (True, False):
+        qx = torch.empty(x.shape, dtype=torch.uint8, device="cuda:0")
+        qw = torch.empty(wt.shape, dtype=torch.uint8, device="cuda:0")
+        sx = torch.empty(x.shape[0], device="cuda:0")
+        sw = torch.empty(wt.shape[0], device="cuda:0")
+        if batched:
+            fp8.fp8_quantize_row_batch([x, wt], 0, 0, [qx, qw], [sx, sw])
+        else:
+            fp8.fp8_quantize_row(x, 0, 0, qx, sx)
+            fp8.fp8_quantize_row(wt, 0, 0, qw, sw)
+        torch.cuda.synchronize()
+        outs.append((qx, qw, sx, sw))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
