@@ -18,7 +18,8 @@ __all__ = [
     "E4M3", "E5M2", "E4M3_FNUZ", "E5M2_FNUZ", "AXIS_TENSOR", "AXIS_ROW", "AXIS_COL",
     "AMAX_MOST_RECENT", "AMAX_MAX", "SCALE_TENSOR", "SCALE_VECTOR", "OUT_BF16", "OUT_F32",
     "Fp8Error", "LIB_PATH", "lib", "fp8_query_device", "fp8_status_string", "fp8_amax",
-    "fp8_quantize_tensor", "fp8_quantize_row", "fp8_quantize_row_batch", "fp8_quantize_col", "fp8_delayed_scale_update",
+    "fp8_quantize_tensor", "fp8_quantize_tensor_batch", "fp8_quantize_row", "fp8_quantize_row_batch",
+    "fp8_quantize_col", "fp8_delayed_scale_update",
     "fp8_gemm_scaled", "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "grouped_layout_width", "GROUP_K_ALIGN", "MX_BLOCK", "fp8_mx_quantize_row", "fp8_gemm_mx",
     "fp8_grouped_gemm_mx", "mx_scale_records", "fp8_moe_route", "fp8_moe_permute_quantize_row",
@@ -34,7 +35,8 @@ OUT_BF16, OUT_F32 = 0, 1
 
 EXPORTED_SYMBOLS = (
     "fp8_query_device", "fp8_status_string", "fp8_last_error", "fp8_amax", "fp8_quantize_tensor",
-    "fp8_quantize_row", "fp8_quantize_row_batch", "fp8_quantize_col", "fp8_delayed_scale_update", "fp8_gemm_scaled",
+    "fp8_quantize_row", "fp8_quantize_row_batch", "fp8_quantize_tensor_batch", "fp8_quantize_col",
+    "fp8_delayed_scale_update", "fp8_gemm_scaled",
     "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "fp8_mx_quantize_row", "fp8_gemm_mx", "fp8_grouped_gemm_mx", "fp8_moe_route", "fp8_moe_permute_quantize_row",
     "fp8_swiglu_quantize_row", "fp8_moe_unpermute_combine", "fp8_blockwise_quantize_act",
@@ -72,6 +74,7 @@ def _load():
         "fp8_quantize_tensor": [P, I64, I64, I64, I, I32, P, P, I64, P, P, P],
         "fp8_quantize_row": [P, I64, I64, I64, I, I32, P, I64, P, P, P, P],
         "fp8_quantize_row_batch": [I32, P, P, I64, P, I, I32, P, P, P, P, P],
+        "fp8_quantize_tensor_batch": [I32, P, P, I64, P, I, P, P, P, P, P, P],
         "fp8_quantize_col": [P, I64, I64, I64, I, I32, P, I64, P, P, I32, P],
         "fp8_delayed_scale_update": [P, P, P, I64, I32, I, I32, I, P, P, P],
         "fp8_gemm_scaled": [P, I, I64, P, I, I64, I64, I64, I64, P, I, P, I, P, I, I64, P],
@@ -189,6 +192,23 @@ def fp8_quantize_row_batch(xs, fmt, margin, qs, scale_inv_outs, amax_outs=None):
     sp = PP(*[_ptr(s) for s in scale_inv_outs])
     ap = PP(*[_ptr(a) for a in amax_outs]) if amax_outs is not None else None
     _check(lib.fp8_quantize_row_batch(count, xp, rows, cols, ldx, fmt, margin, qp, ldq, sp, ap, _stream(xs[0])))
+
+
+def fp8_quantize_tensor_batch(xs, fmt, scales, qs, scale_inv_outs, amax_outs):
+    """Delayed tensorwise casts of the bf16 tensors xs (same number of columns)
+    in one launch; scales[j] (device fp32 [1]) is tensor j's delayed scale."""
+    count = len(xs)
+    if count == 0 or not (len(scales) == len(qs) == len(scale_inv_outs) == len(amax_outs) == count):
+        raise ValueError("xs, scales, qs, scale_inv_outs and amax_outs must have the same, nonzero length")
+    shapes = [_bf16(x) for x in xs]
+    cols = shapes[0][1]
+    if any(c != cols for _, c, _ in shapes):
+        raise ValueError("the tensors of one batch share their number of columns")
+    P64, PP = ctypes.c_int64 * count, ctypes.c_void_p * count
+    _check(lib.fp8_quantize_tensor_batch(
+        count, PP(*[_ptr(x) for x in xs]), P64(*[r for r, _, _ in shapes]), cols, P64(*[ld for _, _, ld in shapes]),
+        fmt, PP(*[_ptr(t) for t in scales]), PP(*[_ptr(q) for q in qs]), P64(*[_mat(q, "q", 1)[2] for q in qs]),
+        PP(*[_ptr(t) for t in scale_inv_outs]), PP(*[_ptr(t) for t in amax_outs]), _stream(xs[0])))
 
 
 def fp8_quantize_col(x, fmt, margin, qt, scale_inv_out, col_amax, col_amax_ready=False):

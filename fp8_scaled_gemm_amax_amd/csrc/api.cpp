@@ -269,6 +269,29 @@ fp8_status_t fp8_quantize_row_batch(int32_t count, const uint16_t* const* x, con
                     fn);
 }
 
+fp8_status_t fp8_quantize_tensor_batch(int32_t count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
+                                       const int64_t* ldx, fp8_format_t fmt, const float* const* scale,
+                                       uint8_t* const* q, const int64_t* ldq, float* const* scale_inv_out,
+                                       float* const* amax_out, void* stream) {
+    const char* fn = "fp8_quantize_tensor_batch";
+    if (count < 1 || count > FP8_MAX_ROW_BATCH)
+        return fail(FP8_ERR_INVALID_ARG, "%s: count %d outside 1..%d", fn, (int)count, FP8_MAX_ROW_BATCH);
+    if (!x || !rows || !ldx || !scale || !q || !ldq || !scale_inv_out || !amax_out)
+        return fail(FP8_ERR_INVALID_ARG, "%s: a host array is NULL", fn);
+    for (int j = 0; j < count; ++j) {
+        FP8_TRY(check_common_quant(fn, x[j], rows[j], cols, ldx[j], (int)fmt, 0));
+        FP8_TRY(check_matrix(fn, "q", q[j], rows[j], cols, ldq[j]));
+        if (!scale[j] || !scale_inv_out[j] || !amax_out[j])
+            return fail(FP8_ERR_INVALID_ARG, "%s: scale, scale_inv_out and amax_out of tensor %d are required", fn, j);
+        if (!aligned(scale[j], 4) || !aligned(scale_inv_out[j], 4) || !aligned(amax_out[j], 4))
+            return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer (tensor %d)", fn, j);
+    }
+    FP8_TRY(check_device());
+    return launched(launch_quant_tensor_batch(count, x, rows, cols, ldx, (int)fmt, scale, q, ldq, scale_inv_out,
+                                              amax_out, (hipStream_t)stream),
+                    fn);
+}
+
 fp8_status_t fp8_quantize_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
                               int32_t margin, uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* col_amax,
                               int32_t col_amax_ready, void* stream) {

@@ -36,6 +36,13 @@ hipError_t launch_quant_tensor(const uint16_t* x, int64_t rows, int64_t cols, in
                                const float* scale, uint8_t* q, int64_t ldq, float* scale_inv, float* amax,
                                hipStream_t st);
 
+// Delayed tensorwise casts of count tensors sharing cols (host arrays of
+// count entries, every scale[j] set): one launch when all take the register kernel.
+hipError_t launch_quant_tensor_batch(int count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
+                                     const int64_t* ldx, int fmt, const float* const* scale, uint8_t* const* q,
+                                     const int64_t* ldq, float* const* scale_inv, float* const* amax,
+                                     hipStream_t st);
+
 hipError_t launch_delayed_update(float* cur_amax, float* history, int32_t* head, int64_t n, int32_t L, int algo,
                                  int margin, int fmt, float* scale, float* scale_inv, hipStream_t st);
 

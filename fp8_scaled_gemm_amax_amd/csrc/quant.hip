@@ -423,21 +423,22 @@ __global__ __launch_bounds__(kBlock) void k_quant_tensor(const uint16_t* __restr
 // a row holding a NaN takes the bit-level one); otherwise the scale comes from
 // amax_io, which the amax pass filled, and a NaN amax sends every row to the
 // bit-level encoder.
+// The rows of one tensor taken by workgroup `wg` of the `nwg` that share it
+// (red: kWaves words of LDS for the workgroup's amax).
 template <int F, int MAXC, bool DELAYED>
-__global__ __launch_bounds__(kBlock) void k_quant_tensor_reg(const uint16_t* __restrict__ x, int64_t rows,
-                                                             int64_t cols, int64_t ldx, int margin,
-                                                             const float* __restrict__ scale, uint8_t* __restrict__ q,
-                                                             int64_t ldq, float* __restrict__ scale_inv,
-                                                             float* __restrict__ amax_io) {
-    __shared__ uint32_t red[kWaves];
+__device__ __forceinline__ void quant_tensor_rows(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                  int64_t ldx, int margin, const float* __restrict__ scale,
+                                                  uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale_inv,
+                                                  float* __restrict__ amax_io, int64_t wg, int64_t nwg,
+                                                  uint32_t* red) {
     const int lane = threadIdx.x & 63;
-    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int64_t nwaves = nwg * kWaves;
     const float s = DELAYED ? *scale : scale_from_amax<F>(*amax_io, margin);
     const bool tensor_nan = DELAYED ? false : __builtin_isnan(*amax_io);
-    if (blockIdx.x == 0 && threadIdx.x == 0) scale_inv[0] = 1.0f / s;
+    if (wg == 0 && threadIdx.x == 0) scale_inv[0] = 1.0f / s;
     const int nch = (int)(cols >> 3);
     uint32_t mx = 0;
-    for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < rows; row += nwaves) {
+    for (int64_t row = wg * kWaves + (threadIdx.x >> 6); row < rows; row += nwaves) {
         const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
         uint4 v[MAXC];
 #pragma unroll
@@ -473,6 +474,55 @@ __global__ __launch_bounds__(kBlock) void k_quant_tensor_reg(const uint16_t* __r
         mx = block_max_u32(mx, red);
         if (threadIdx.x == 0) atomic_max_bits(amax_io, mx << 16);
     }
+}
+
+template <int F, int MAXC, bool DELAYED>
+__global__ __launch_bounds__(kBlock) void k_quant_tensor_reg(const uint16_t* __restrict__ x, int64_t rows,
+                                                             int64_t cols, int64_t ldx, int margin,
+                                                             const float* __restrict__ scale, uint8_t* __restrict__ q,
+                                                             int64_t ldq, float* __restrict__ scale_inv,
+                                                             float* __restrict__ amax_io) {
+    __shared__ uint32_t red[kWaves];
+    quant_tensor_rows<F, MAXC, DELAYED>(x, rows, cols, ldx, margin, scale, q, ldq, scale_inv, amax_io, blockIdx.x,
+                                        gridDim.x, red);
+}
+
+// Delayed tensorwise casts of up to kMaxRowBatch tensors with the same number
+// of columns in one launch (a linear layer's X and W, each with its own
+// delayed scale and amax): tensor j owns workgroups first[j] .. first[j+1]-1
+// (at least one), which stride over its rows as above.
+struct TensorBatch {
+    const uint16_t* x[kMaxRowBatch];
+    uint8_t* q[kMaxRowBatch];
+    const float* scale[kMaxRowBatch];
+    float* scale_inv[kMaxRowBatch];
+    float* amax[kMaxRowBatch];
+    int64_t rows[kMaxRowBatch];
+    int64_t ldx[kMaxRowBatch];
+    int64_t ldq[kMaxRowBatch];
+    int64_t first[kMaxRowBatch + 1];
+    int count;
+};
+
+template <int F, int MAXC>
+__global__ __launch_bounds__(kBlock) void k_quant_tensor_batch(TensorBatch b, int64_t cols) {
+    __shared__ uint32_t red[kWaves];
+    const int64_t bid = blockIdx.x;
+    int j = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxRowBatch; ++i)
+        if (i < b.count && bid >= b.first[i]) j = i;
+    int64_t first = b.first[0], next = b.first[1];
+#pragma unroll
+    for (int i = 1; i < kMaxRowBatch; ++i)
+        if (i == j) {
+            first = b.first[i];
+            next = b.first[i + 1];
+        }
+    const int64_t nwg = next - first;
+    quant_tensor_rows<F, MAXC, true>(batch_pick(b.x, j), batch_pick(b.rows, j), cols, batch_pick(b.ldx, j), 0,
+                                     batch_pick(b.scale, j), batch_pick(b.q, j), batch_pick(b.ldq, j),
+                                     batch_pick(b.scale_inv, j), batch_pick(b.amax, j), bid - first, nwg, red);
 }
 
 // --------------------------------------------------------------- MX quantizer --
@@ -1520,6 +1570,65 @@ hipError_t launch_quant_tensor(const uint16_t* x, int64_t rows, int64_t cols, in
         default: return CALL(kE5M2Fnuz);
     }
 #undef CALL
+}
+
+template <int F>
+hipError_t quant_tensor_batch_fmt(const TensorBatch& b, int64_t blocks, int64_t cols, hipStream_t st) {
+    switch (reg_chunks(cols)) {
+#define FP8_TENSOR_BATCH_CASE(C)                                                                                   \
+    case C:                                                                                                        \
+        hipLaunchKernelGGL((k_quant_tensor_batch<F, C>), dim3((unsigned)blocks), dim3(kBlock), 0, st, b, cols);    \
+        break;
+        FP8_TENSOR_BATCH_CASE(1)
+        FP8_TENSOR_BATCH_CASE(2)
+        FP8_TENSOR_BATCH_CASE(4)
+        FP8_TENSOR_BATCH_CASE(8)
+        FP8_TENSOR_BATCH_CASE(16)
+        default:
+            FP8_TENSOR_BATCH_CASE(32)
+#undef FP8_TENSOR_BATCH_CASE
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor_batch(int count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
+                                     const int64_t* ldx, int fmt, const float* const* scale, uint8_t* const* q,
+                                     const int64_t* ldq, float* const* scale_inv, float* const* amax,
+                                     hipStream_t st) {
+    // one launch when every tensor takes the register kernel; otherwise one per tensor
+    bool one = count <= kMaxRowBatch && cols > 0 && cols % 8 == 0 && reg_chunks(cols) > 0;
+    for (int j = 0; j < count && one; ++j)
+        one = rows[j] > 0 && is_aligned(x[j], 16) && is_aligned(q[j], 8) && ldx[j] % 8 == 0 && ldq[j] % 8 == 0;
+    if (!one) {
+        for (int j = 0; j < count; ++j) {
+            const hipError_t e = launch_quant_tensor(x[j], rows[j], cols, ldx[j], fmt, 0, scale[j], q[j], ldq[j],
+                                                     scale_inv[j], amax[j], st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    TensorBatch b{};
+    b.count = count;
+    int64_t blocks = 0;
+    for (int j = 0; j < count; ++j) {
+        b.x[j] = x[j];
+        b.q[j] = q[j];
+        b.scale[j] = scale[j];
+        b.scale_inv[j] = scale_inv[j];
+        b.amax[j] = amax[j];
+        b.rows[j] = rows[j];
+        b.ldx[j] = ldx[j];
+        b.ldq[j] = ldq[j];
+        b.first[j] = blocks;
+        blocks += tensor_grid(rows[j]);
+    }
+    for (int j = count; j <= kMaxRowBatch; ++j) b.first[j] = blocks;
+    switch (fmt) {
+        case kE4M3: return quant_tensor_batch_fmt<kE4M3>(b, blocks, cols, st);
+        case kE5M2: return quant_tensor_batch_fmt<kE5M2>(b, blocks, cols, st);
+        case kE4M3Fnuz: return quant_tensor_batch_fmt<kE4M3Fnuz>(b, blocks, cols, st);
+        default: return quant_tensor_batch_fmt<kE5M2Fnuz>(b, blocks, cols, st);
+    }
 }
 
 hipError_t launch_mx_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,

@@ -159,6 +159,23 @@ fp8_status_t fp8_quantize_row_batch(int32_t count, const uint16_t* const* x, con
                                     const int64_t* ldq, float* const* scale_inv_out, float* const* amax_out,
                                     void* stream);
 
+/* Delayed tensorwise quantization of several tensors that share cols in one
+ * launch ([Flux] delayed recipe; a linear layer's X and W, each with its own
+ * delayed state). Tensor j is cast exactly as fp8_quantize_tensor with
+ * scale = scale[j] (device fp32, required) would: scale_inv_out[j][0] =
+ * fl32(1 / *scale[j]) and the tensor's amax is folded into amax_out[j][0] (the
+ * state's cur_amax, cleared by fp8_delayed_scale_update). x, rows, ldx, scale,
+ * q, ldq, scale_inv_out, amax_out are HOST arrays of count entries (all
+ * required); the pointers in them are device memory. count: 1..FP8_MAX_ROW_BATCH.
+ * One launch when every tensor has rows > 0 and the vector layout (x 16-byte,
+ * q 8-byte aligned; ldx, ldq, cols multiples of 8) and cols <= 16384; otherwise
+ * one launch per tensor. Errors as fp8_quantize_tensor, for any tensor, before
+ * anything is enqueued. */
+fp8_status_t fp8_quantize_tensor_batch(int32_t count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
+                                       const int64_t* ldx, fp8_format_t fmt, const float* const* scale,
+                                       uint8_t* const* q, const int64_t* ldq, float* const* scale_inv_out,
+                                       float* const* amax_out, void* stream);
+
 /* Colwise quantization with transposed output ([Titan] colwise scales, whose
  * non-coalesced writes the post singles out). One scale per column of x
  * (reduction over the rows, e.g. over tokens), and the codes are written

@@ -203,6 +203,26 @@ def test_quantize_row_batch_rejects_bad_arguments(fp8):
     assert call(a=PP(None, ctypes.c_void_p(0x10002)))[0] == 2     # misaligned amax output
 
 
+def test_quantize_tensor_batch_rejects_bad_arguments(fp8):
+    f = "fp8_quantize_tensor_batch"
+    PP, P64 = ctypes.c_void_p * 2, ctypes.c_int64 * 2
+    two = PP(FAKE, FAKE)
+    rows, ld = P64(4, 8), P64(16, 16)
+
+    def call(count=2, x=two, rows=rows, ldx=ld, fmt=0, sc=two, ldq=ld, si=two, am=two):
+        return _call(fp8, f, count, x, rows, 16, ldx, fmt, sc, two, ldq, si, am, None)
+
+    st, msg = call(count=9)
+    assert st == 1 and "count" in msg
+    assert call(sc=None)[0] == 1                                   # the scale array is required
+    st, msg = call(sc=PP(FAKE, None))                              # tensor 1 without its delayed scale
+    assert st == 1 and "required" in msg
+    assert call(am=PP(FAKE, None))[0] == 1
+    assert call(fmt=7)[0] == 1
+    assert call(ldq=P64(16, 4))[0] == 1
+    assert call(si=PP(FAKE, ctypes.c_void_p(0x10002)))[0] == 2
+
+
 def test_delayed_update_rejects_bad_arguments(fp8):
     f = "fp8_delayed_scale_update"
     assert _call(fp8, f, FAKE, FAKE, FAKE, 2, 0, 1, 0, 0, FAKE, FAKE, None)[0] == 1        # L = 0

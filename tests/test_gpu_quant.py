@@ -475,3 +475,64 @@ def test_quantize_row_batch_matches_single_calls_at_llama3_8b(fp8):
         outs.append((qx, qw, sx, sw))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------- batched delayed tensorwise --
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_quantize_tensor_batch_delayed_parity(fp8, orc, fmt):
+    """Three tensors with their own delayed scales in one launch (ragged row
+    counts, one tensor of one row): codes, scale_inv and the folded amax as
+    fp8_quantize_tensor gives them, and as the oracle computes them."""
+    cols = 264
+    sizes = [37, 1, 600]
+    xbs = [rand_bf16(r, cols, seed=40 + j, spread=3) for j, r in enumerate(sizes)]
+    scales = [np.float32(v) for v in (3.5, 0.75, 1.0 / 24.0)]
+    start = [np.float32(v) for v in (0.0, 1e6, 0.5)]      # a folded amax keeps a larger value already there
+    say("tensor batch delayed", NAMES[fmt], sizes)
+    xs = [dev_bf16(xb) for xb in xbs]
+    outs = {}
+    for batched in (True, False):
+        qs = [torch.empty((r, cols), dtype=torch.uint8, device="cuda:0") for r in sizes]
+        sc = [torch.tensor([v], device="cuda:0") for v in scales]
+        si = [torch.full((1,), -1.0, device="cuda:0") for _ in sizes]
+        am = [torch.tensor([v], device="cuda:0") for v in start]
+        if batched:
+            fp8.fp8_quantize_tensor_batch(xs, fmt, sc, qs, si, am)
+        else:
+            for j in range(len(sizes)):
+                fp8.fp8_quantize_tensor(xs[j], fmt, 0, sc[j], qs[j], si[j], am[j])
+        torch.cuda.synchronize()
+        outs[batched] = ([q.cpu().numpy() for q in qs], [t.cpu().numpy() for t in si], [t.cpu().numpy() for t in am])
+    for j, xb in enumerate(xbs):
+        for part in range(3):
+            assert np.array_equal(outs[True][part][j].view(np.uint8), outs[False][part][j].view(np.uint8)), (j, part)
+        oq, osi, oam = orc.quantize_tensor_scaled(xb, fmt, scales[j], amax_in=start[j])
+        assert_codes_equal(outs[True][0][j], oq, f"codes of tensor {j}")
+        assert_f32_bits_equal(outs[True][1][j], [osi], f"scale_inv of tensor {j}")
+        assert_f32_bits_equal(outs[True][2][j], [oam], f"amax of tensor {j}")
+
+
+def test_quantize_tensor_batch_flux_mlp(fp8):
+    """The Flux-12B MLP's X [4608 x 3072] and W [12288 x 3072] with their delayed
+    scales: the batched launch gives the bytes of two fp8_quantize_tensor calls."""
+    w = workloads.c3()
+    _, xb = next(w["x_steps"]())
+    say("tensor batch c3 full size")
+    x, wt = dev_bf16(xb), dev_bf16(w["w"])
+    res = []
+    for batched in (True, False):
+        qx = torch.empty(x.shape, dtype=torch.uint8, device="cuda:0")
+        qw = torch.empty(wt.shape, dtype=torch.uint8, device="cuda:0")
+        sc = [torch.tensor([112.0], device="cuda:0"), torch.tensor([3584.0], device="cuda:0")]
+        si = [torch.empty(1, device="cuda:0") for _ in range(2)]
+        am = [torch.zeros(1, device="cuda:0") for _ in range(2)]
+        if batched:
+            fp8.fp8_quantize_tensor_batch([x, wt], 0, sc, [qx, qw], si, am)
+        else:
+            fp8.fp8_quantize_tensor(x, 0, 0, sc[0], qx, si[0], am[0])
+            fp8.fp8_quantize_tensor(wt, 0, 0, sc[1], qw, si[1], am[1])
+        torch.cuda.synchronize()
+        res.append([qx, qw] + si + am)
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
