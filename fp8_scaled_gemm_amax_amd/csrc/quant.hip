@@ -931,9 +931,11 @@ __global__ void k_scale_inv_from_amax(const float* __restrict__ amax, int64_t n,
 // row tiles of 128; tile t of group g covers its rows t*128 .. t*128+127
 // (zeros past m_g: the padding) and lands at qt columns P_g + t*128 .., where
 // P_g = 128 * (rt_0 + .. + rt_{g-1}). Every workgroup forms those prefix sums
-// in LDS (256 threads, then a block scan), exits if blockIdx.x is past the last
-// tile (the grid is a host-side upper bound), and finds its group by binary
-// search.
+// in LDS once (256 threads, then a block scan), then strides over the row
+// tiles (the grid's x extent is at most the host-side upper bound of the tile
+// count, capped near eight workgroups per CU over the column tiles) and finds
+// each tile's group by binary search. (One workgroup per tile slot spent ~20 us
+// of c4b's expert-weight cast on slots that only exit.)
 constexpr int kMaxGroups = 4096;
 
 template <int F>
@@ -975,25 +977,28 @@ __global__ __launch_bounds__(kBlock) void k_grouped_quant_col_tiled(const uint16
     }
     if (t == kBlock - 1) pre[G] = run;
     __syncthreads();
-    const int32_t y = (int32_t)blockIdx.x;
-    if (y >= pre[G]) return;                             // uniform over the workgroup
-    int glo = 0, ghi = G;                                // pre[glo] <= y < pre[ghi]
-    while (ghi - glo > 1) {
-        const int mid = (glo + ghi) >> 1;
-        if (pre[mid] <= y)
-            glo = mid;
-        else
-            ghi = mid;
+    // row tiles y = blockIdx.x, blockIdx.x + gridDim.x, .. (uniform over the workgroup)
+    for (int32_t y = (int32_t)blockIdx.x; y < pre[G]; y += (int32_t)gridDim.x) {
+        int glo = 0, ghi = G;                            // pre[glo] <= y < pre[ghi]
+        while (ghi - glo > 1) {
+            const int mid = (glo + ghi) >> 1;
+            if (pre[mid] <= y)
+                glo = mid;
+            else
+                ghi = mid;
+        }
+        const int g = glo;
+        const int64_t tt = y - pre[g];
+        int64_t lo, hi;
+        group_rows(off, g, total, &lo, &hi);
+        if (skip_small && hi - lo <= kSmallGroupRows) continue;   // (done by the one-pass kernel)
+        __syncthreads();                                 // the previous tile's LDS reads are done
+        const int64_t c0 = (int64_t)blockIdx.y * kColTileC;
+        col_scales_to_lds<F>(col_amax + (int64_t)g * cols, c0, cols, margin, nullptr, s_lds, nan_lds);
+        const int64_t d0 = (int64_t)pre[g] * kColTileR + tt * kColTileR;
+        col_tile<F>(x, ldx, lo + tt * kColTileR, hi, true, c0, cols, s_lds, nan_lds, tile, qt, ldqt, d0, ldqt,
+                    vec_store);
     }
-    const int g = glo;
-    const int64_t tt = y - pre[g];
-    int64_t lo, hi;
-    group_rows(off, g, total, &lo, &hi);
-    if (skip_small && hi - lo <= kSmallGroupRows) return;   // (done by the one-pass kernel; uniform)
-    const int64_t c0 = (int64_t)blockIdx.y * kColTileC;
-    col_scales_to_lds<F>(col_amax + (int64_t)g * cols, c0, cols, margin, nullptr, s_lds, nan_lds);
-    const int64_t d0 = (int64_t)pre[g] * kColTileR + tt * kColTileR;
-    col_tile<F>(x, ldx, lo + tt * kColTileR, hi, true, c0, cols, s_lds, nan_lds, tile, qt, ldqt, d0, ldqt, vec_store);
 }
 
 // Groups of at most kSmallGroupRows rows in one pass: a workgroup holds a
@@ -1751,8 +1756,13 @@ hipError_t launch_grouped_quant_col(const uint16_t* x, int64_t total_m, int64_t 
     const int64_t n = (int64_t)g * cols;
     const unsigned sblocks = (unsigned)((n + kBlock - 1) / kBlock < 1024 ? (n + kBlock - 1) / kBlock : 1024);
     // every group's padded tile count is at most m_g / 128 + 2
-    const dim3 grid((unsigned)((total_m + kColTileR - 1) / kColTileR + 2 * (int64_t)g),
-                    (unsigned)((cols + kColTileC - 1) / kColTileC));
+    // row-tile slots: the tile count's upper bound, at most about eight
+    // workgroups per CU over the column tiles (each workgroup forms the group
+    // prefix sums once and strides over row tiles)
+    const int64_t ctiles = (cols + kColTileC - 1) / kColTileC;
+    const int64_t rt_bound = (total_m + kColTileR - 1) / kColTileR + 2 * (int64_t)g;
+    const int64_t rt_cap = ((int64_t)current_device_props().cus * 8 + ctiles - 1) / ctiles;
+    const dim3 grid((unsigned)(rt_bound < rt_cap ? rt_bound : rt_cap), (unsigned)ctiles);
 #define CALL(F)                                                                                                  \
     do {                                                                                                         \
         hipLaunchKernelGGL((k_scale_inv_from_amax<F>), dim3(sblocks), dim3(kBlock), 0, st, col_amax, n, margin,  \
