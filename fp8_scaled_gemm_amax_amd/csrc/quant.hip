@@ -1513,8 +1513,12 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
     // one launch when every tensor takes the register kernel (vector layout,
     // rows of at most 32 chunks per lane); otherwise one launch per tensor
     bool one = count <= kMaxRowBatch && cols > 0 && cols % 8 == 0 && (cols / 8 + 63) / 64 <= 32;
-    for (int j = 0; j < count && one; ++j)
+    int64_t total_rows = 0;
+    for (int j = 0; j < count && one; ++j) {
         one = is_aligned(x[j], 16) && is_aligned(q[j], 8) && ldx[j] % 8 == 0 && ldq[j] % 8 == 0;
+        total_rows += rows[j];
+    }
+    one = one && total_rows / kWaves < ((int64_t)1 << 31) - kMaxRowBatch;    // the grid's x extent
     if (!one) {
         for (int j = 0; j < count; ++j) {
             const hipError_t e = launch_quant_row(x[j], rows[j], cols, ldx[j], fmt, margin, q[j], ldq[j],
