@@ -536,3 +536,41 @@ def test_quantize_tensor_batch_flux_mlp(fp8):
         res.append([qx, qw] + si + am)
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+def test_quantize_row_batch_single_and_empty(fp8, orc):
+    """count = 1 (the batch entry point as a plain rowwise cast), and batches
+    whose only rows sit in one tensor."""
+    xb = rand_bf16(77, 520, seed=61)
+    say("row batch count 1")
+    check_row_batch(orc, [xb], 1, 0, gpu_row_batch(fp8, [xb], 1, 0))
+    xbs = [rand_bf16(0, 520, seed=62), rand_bf16(0, 520, seed=63), xb]
+    say("row batch empty leaders")
+    check_row_batch(orc, xbs, 2, 1, gpu_row_batch(fp8, xbs, 2, 1))
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_quantize_tensor_batch_per_tensor_paths(fp8, orc, fmt):
+    """An empty tensor and a misaligned row stride send the batch to one launch
+    per tensor: results as fp8_quantize_tensor's, the empty tensor still writes
+    its scale_inv and leaves its amax target as it was."""
+    cols = 40
+    xbs = [rand_bf16(13, cols, seed=71, spread=2), rand_bf16(0, cols, seed=72)]
+    scales = [np.float32(2.5), np.float32(0.125)]
+    start = [np.float32(0.0), np.float32(7.0)]
+    say("tensor batch fallback", NAMES[fmt])
+    xs = [dev_bf16(xb) for xb in xbs]
+    qbuf = torch.full((13, cols + 3), 0x5A, dtype=torch.uint8, device="cuda:0")
+    qs = [qbuf[:, :cols], torch.empty((0, cols), dtype=torch.uint8, device="cuda:0")]
+    sc = [torch.tensor([v], device="cuda:0") for v in scales]
+    si = [torch.full((1,), -1.0, device="cuda:0") for _ in xbs]
+    am = [torch.tensor([v], device="cuda:0") for v in start]
+    fp8.fp8_quantize_tensor_batch(xs, fmt, sc, qs, si, am)
+    torch.cuda.synchronize()
+    oq, osi, oam = orc.quantize_tensor_scaled(xbs[0], fmt, scales[0], amax_in=start[0])
+    assert_codes_equal(qs[0].cpu().numpy(), oq, "codes")
+    assert np.all(qbuf[:, cols:].cpu().numpy() == 0x5A), "padding written"
+    assert_f32_bits_equal(si[0].cpu().numpy(), [osi], "scale_inv")
+    assert_f32_bits_equal(am[0].cpu().numpy(), [oam], "amax")
+    assert_f32_bits_equal(si[1].cpu().numpy(), [np.float32(1.0) / scales[1]], "scale_inv of the empty tensor")
+    assert_f32_bits_equal(am[1].cpu().numpy(), [start[1]], "amax of the empty tensor")
