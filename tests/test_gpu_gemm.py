@@ -173,7 +173,12 @@ def test_grouped_gemm_parity(fp8, orc, sizes, fa, fb):
 
 LARGE = [((2100, 4100, 256), 0, 0, False, 4104), ((4096, 2048, 512), 1, 0, False, 2048),
          ((1024, 8192, 768), 0, 1, True, 8200), ((2304, 3100, 256), 1, 1, False, 3107),
-         ((2304, 3100, 256), 0, 0, False, 3104), ((4096, 2048, 384), 1, 0, False, 2048)]
+         ((2304, 3100, 256), 0, 0, False, 3104), ((4096, 2048, 384), 1, 0, False, 2048),
+         # more tiles than CUs (bf16 out: persistent workgroups with several tiles each):
+         # edge tiles shifted back (n - 256 off the 8-column grid), m below one tile
+         # (clamped rows), an output stride off the 8-element grid
+         ((4100, 4500, 256), 0, 0, False, 4504), ((200, 65800, 256), 1, 0, False, 65800),
+         ((2600, 7000, 512), 0, 0, False, 7003)]
 
 
 @pytest.mark.parametrize("shape,fa,fb,out_f32,ldd", LARGE)
