@@ -935,7 +935,8 @@ __global__ void k_scale_inv_from_amax(const float* __restrict__ amax, int64_t n,
 // tiles (the grid's x extent is at most the host-side upper bound of the tile
 // count, capped near eight workgroups per CU over the column tiles) and finds
 // each tile's group by binary search. (One workgroup per tile slot spent ~20 us
-// of c4b's expert-weight cast on slots that only exit.)
+// of the MoE backward's expert-weight cast, 32 x 2048 x 7168, on slots that
+// only exit.)
 constexpr int kMaxGroups = 4096;
 
 template <int F>
@@ -1717,9 +1718,9 @@ hipError_t launch_grouped_quant_col(const uint16_t* x, int64_t total_m, int64_t 
     hipError_t e = hipSuccess;
     // Groups of at most kSmallGroupRows rows in one pass, when the tensor is
     // larger than the 256 MB last-level cache (the two-pass path's second read
-    // then comes from HBM: c4b's expert weights, 940 MB, 483 -> 402 us); a
+    // then comes from HBM: the MoE backward's expert weights, 940 MB, 483 -> 402 us); a
     // tensor that fits is read the second time from that cache, and the
-    // two-pass path is faster (c4b's token tensors, 67 and 235 MB: 52 / 167 us
+    // two-pass path is faster (its token-side tensors, 67 and 235 MB: 52 / 167 us
     // against 115 / 307 us one-pass). Not with a supplied amax.
     const int small = !col_amax_ready && (cols + kSmallStrip - 1) / kSmallStrip <= 65535 &&
                       total_m * cols * 2 > ((int64_t)256 << 20);
