@@ -574,3 +574,78 @@ def test_quantize_tensor_batch_per_tensor_paths(fp8, orc, fmt):
     assert_f32_bits_equal(am[0].cpu().numpy(), [oam], "amax")
     assert_f32_bits_equal(si[1].cpu().numpy(), [np.float32(1.0) / scales[1]], "scale_inv of the empty tensor")
     assert_f32_bits_equal(am[1].cpu().numpy(), [start[1]], "amax of the empty tensor")
+
+
+# ------------------------------------------------ delayed state checkpointing --
+
+def test_delayed_state_checkpoint_resume_bitwise(fp8):
+    """The delayed-scaling state is plain caller-owned device memory (history,
+    head, scale, scale_inv, cur_amax): 16 steps straight give the same bytes as
+    8 steps, a copy of the state to the host, fresh device buffers filled from
+    that copy, and 8 more steps, at every step (codes, scale_inv, state)."""
+    rng = np.random.default_rng(17)
+    n_t, L, rows, cols = 2, 1024, 96, 264
+    drift = np.cumprod(np.concatenate([[1.0], rng.uniform(0.5, 2.0, 15)])).astype(np.float32)
+    xs = [workloads.bf16_bits(rng.standard_normal((2, rows, cols)).astype(np.float32) * d) for d in drift]
+
+    def fresh(state=None):
+        if state is None:
+            return [torch.zeros((n_t, L), device="cuda:0"), torch.zeros(1, dtype=torch.int32, device="cuda:0"),
+                    torch.ones(n_t, device="cuda:0"), torch.ones(n_t, device="cuda:0"),
+                    torch.zeros(n_t, device="cuda:0")]
+        return [torch.from_numpy(a.copy()).to("cuda:0") for a in state]
+
+    def steps(st, t0, t1, log):
+        hist, head, scale, scale_inv, cur = st
+        for t in range(t0, t1):
+            qs = [torch.empty((rows, cols), dtype=torch.uint8, device="cuda:0") for _ in range(n_t)]
+            si = [torch.empty(1, device="cuda:0") for _ in range(n_t)]
+            fp8.fp8_quantize_tensor_batch([dev_bf16(xs[t][j]) for j in range(n_t)], fp8.E4M3,
+                                          [scale[j:j + 1] for j in range(n_t)], qs, si,
+                                          [cur[j:j + 1] for j in range(n_t)])
+            fp8.fp8_delayed_scale_update(cur, hist, head, fp8.AMAX_MAX, 0, fp8.E4M3, scale, scale_inv)
+            torch.cuda.synchronize()
+            log.append([q.cpu().numpy() for q in qs] + [s.cpu().numpy() for s in si] +
+                       [a.cpu().numpy().copy() for a in (hist, head, scale, scale_inv, cur)])
+
+    say("delayed checkpoint / resume, 16 steps")
+    straight, resumed = [], []
+    steps(fresh(), 0, 16, straight)
+    first = fresh()
+    steps(first, 0, 8, resumed)
+    host = [a.cpu().numpy().copy() for a in first]      # the checkpoint
+    del first
+    steps(fresh(host), 8, 16, resumed)
+    assert len(straight) == len(resumed) == 16
+    for t, (a, b) in enumerate(zip(straight, resumed)):
+        for i, (u, v) in enumerate(zip(a, b)):
+            assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), f"step {t}, output {i}"
+    # the drift moves the scales: the sequence is not trivially constant
+    assert len({float(x[-3][0]) for x in straight}) > 2
+
+
+def test_wrong_max_is_not_used_by_the_library(fp8, orc):
+    """The silent corruption of a scale computed against the wrong format max
+    (448 for e4m3fnuz, whose largest value is 240) does not happen on the
+    library path: x = 400 cast rowwise in e4m3fnuz gives the top code 0x7F with
+    scale_inv = 400 / 240, so the dequantised value stays 400; in OCP e4m3 the
+    top code is 0x7E (448). The fnuz and OCP bytes differ, and each decodes
+    only in its own format."""
+    xb = workloads.bf16_bits(np.array([[400.0, -400.0, 100.0, 0.0] * 4], np.float32))
+    x = dev_bf16(xb)
+    out = {}
+    for fmt in (0, 2):
+        q = torch.empty((1, 16), dtype=torch.uint8, device="cuda:0")
+        si = torch.empty(1, device="cuda:0")
+        say("wrong-max check", NAMES[fmt])
+        fp8.fp8_quantize_row(x, fmt, 0, q, si)
+        torch.cuda.synchronize()
+        out[fmt] = (q.cpu().numpy()[0], si.cpu().numpy()[0])
+    qf, sf = out[2]
+    assert qf[0] == 0x7F and qf[1] == 0xFF                # +-240, fnuz's top codes
+    assert abs(orc.decode(2, qf[:1])[0] * float(sf) - 400.0) < 1e-3
+    assert abs(float(sf) - 400.0 / 240.0) < 1e-6          # not 400 / 448
+    qo, so = out[0]
+    assert qo[0] == 0x7E and qo[1] == 0xFE                # +-448, OCP e4m3's top codes
+    assert abs(orc.decode(0, qo[:1])[0] * float(so) - 400.0) < 1e-3
+    assert abs(orc.decode(2, qo[:1])[0] * float(so) - 400.0) > 100.0   # read as fnuz: wrong by half
