@@ -110,6 +110,7 @@ class Step:
             _, xb = next(w["x_steps"]())
             self.x = bf16_dev(xb)
             self.cpu_sample = (xb, 0, w["w"], 0)
+            self.cpu_kind = "tensor"
             m, k = self.x.shape
             n = self.w.shape[0]
             self.qx, self.qw = E((m, k), dtype=torch.uint8, device=dev), E((n, k), dtype=torch.uint8, device=dev)
@@ -396,9 +397,11 @@ def copy_calibration(args):
 def cpu_baseline(sample, target_s, kind="rowwise"):
     """The CPU oracle on a bounded sample of the workload's own tensors: the
     first ms rows of the activation and the first ns rows of the weight
-    (K-contiguous) quantized rowwise (kind "mx": MX block-32), then the
-    oracle's fp64 dequantize-and-matmul of the sample. Reported as
-    2*ms*ns*K / time in TFLOP/s."""
+    (K-contiguous) quantized rowwise (kind "mx": MX block-32; "blockwise";
+    "tensor": one scale per tensor, the delayed recipe's cast given the scale
+    its state holds, here the tensor's current one), then the oracle's fp64
+    dequantize-and-matmul of the sample. Reported as 2*ms*ns*K / time in
+    TFLOP/s."""
     from oracle import oracle as orc
     act, fa, wgt, fw = sample
     k = act.shape[1]
@@ -414,6 +417,10 @@ def cpu_baseline(sample, target_s, kind="rowwise"):
             qx, ex = orc.blockwise_quantize_act(act[:ms], fa)
             qw, ew = orc.blockwise_quantize_weight(wgt[:ns], fw)
             orc.blockwise_gemm(qx, fa, ex, qw, fw, ew)
+        elif kind == "tensor":
+            qx, sx, _ = orc.quantize_tensor_current(act[:ms], fa)
+            qw, sw, _ = orc.quantize_tensor_current(wgt[:ns], fw)
+            orc.gemm(qx, fa, qw, fw, sx, sw, with_bound=False)
         else:
             qx, sx, _ = orc.quantize_row(act[:ms], fa)
             qw, sw, _ = orc.quantize_row(wgt[:ns], fw)
@@ -433,7 +440,7 @@ def cpu_baseline(sample, target_s, kind="rowwise"):
     return {"value": round(2.0 * ms * ns * k / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{ms} activation rows x {ns} weight rows x K={k} of the workload's tensors: "
-                      f"{ {'mx': 'MX block-32', 'blockwise': 'blockwise'}.get(kind, 'rowwise') } quantize of both "
+                      f"{ {'mx': 'MX block-32', 'blockwise': 'blockwise', 'tensor': 'tensorwise'}.get(kind, 'rowwise') } quantize of both "
                       f"(oracle) + fp64 "
                       f"dequantize-and-matmul, {t:.1f} s on {threads} threads"}
 
