@@ -544,18 +544,36 @@ __device__ __forceinline__ constexpr int mx_emax() { return F == kE4M3 ? 8 : 15;
 
 constexpr int64_t kMxSlice = 32 * 64 * 8;               // 16384 columns: 32 chunks per lane
 
-template <int F, int MAXC>
-__global__ __launch_bounds__(kBlock) void k_mx_quant_row(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+// The scale records of a workgroup's W rows are gathered in LDS and stored one
+// K step at a time (the step's W records are contiguous in the K-step-major
+// layout): one W * 4-byte store per step instead of W scattered 4-byte stores.
+constexpr int kRecSteps = (int)(kMxSlice / 128);       // records per row of one slice
+
+template <int W>
+__device__ __forceinline__ void store_records(const uint32_t* rec, int nrec, uint8_t* __restrict__ sc, int64_t ldsc,
+                                              int64_t row0, int64_t rows) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < nrec * W; i += W * 64) {
+        const int j = i / W, r = i % W;
+        if (row0 + r < rows) *reinterpret_cast<uint32_t*>(sc + 4 * ((int64_t)j * ldsc + row0 + r)) = rec[i];
+    }
+}
+
+template <int F, int MAXC, int W>
+__global__ __launch_bounds__(W * 64) void k_mx_quant_row(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                          int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
                                                          uint8_t* __restrict__ sc, int64_t ldsc) {
+    __shared__ uint32_t rec[kRecSteps * W];
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    const int rl = threadIdx.x >> 6;
+    const int64_t row0 = (int64_t)blockIdx.x * W;
+    const int64_t row = row0 + rl;
     const int64_t c0 = (int64_t)blockIdx.y * kMxSlice;
     x += c0;
     q += c0;
     sc += (c0 / 128) * ldsc * 4;
     const int nch = (int)((cols - c0 < kMxSlice ? cols - c0 : kMxSlice) >> 3);
+    if (row < rows) {                                    // (uniform over the wavefront)
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
     uint4 v[MAXC];
 #pragma unroll
@@ -594,10 +612,10 @@ __global__ __launch_bounds__(kBlock) void k_mx_quant_row(const uint16_t* __restr
         // lanes 16i, 16i+4, 16i+8, 16i+12 hold the first chunks of blocks 4j .. 4j+3
         const uint32_t mine = ch < nch ? e8 : 0u;
         const uint32_t b1 = __shfl_down(mine, 4), b2 = __shfl_down(mine, 8), b3 = __shfl_down(mine, 12);
-        if ((lane & 15) == 0 && ch < nch)
-            *reinterpret_cast<uint32_t*>(sc + 4 * ((int64_t)(ch >> 4) * ldsc + row)) =
-                mine | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        if ((lane & 15) == 0 && ch < nch) rec[(ch >> 4) * W + rl] = mine | (b1 << 8) | (b2 << 16) | (b3 << 24);
     }
+    }
+    store_records<W>(rec, (nch + 15) / 16, sc, ldsc, row0, rows);
 }
 
 // ---------------------------------------------------------- blockwise casts --
@@ -615,19 +633,22 @@ __device__ __forceinline__ uint32_t e8m0_of_inverse(float s_pow2) { return 254u 
 // One wavefront per row slice of up to kMxSlice columns (grid y), in registers;
 // a 128-block is 16 lanes' chunks, reduced with four lane exchanges; the lane
 // holding a block's first chunk stores its record.
-template <int F, int MAXC>
-__global__ __launch_bounds__(kBlock) void k_blockwise_quant_act(const uint16_t* __restrict__ x, int64_t rows,
+template <int F, int MAXC, int W>
+__global__ __launch_bounds__(W * 64) void k_blockwise_quant_act(const uint16_t* __restrict__ x, int64_t rows,
                                                                 int64_t cols, int64_t ldx, uint8_t* __restrict__ q,
                                                                 int64_t ldq, uint8_t* __restrict__ sc,
                                                                 int64_t ldsc) {
+    __shared__ uint32_t rec[kRecSteps * W];
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    const int rl = threadIdx.x >> 6;
+    const int64_t row0 = (int64_t)blockIdx.x * W;
+    const int64_t row = row0 + rl;
     const int64_t c0 = (int64_t)blockIdx.y * kMxSlice;
     x += c0;
     q += c0;
     sc += (c0 / 128) * ldsc * 4;
     const int nch = (int)((cols - c0 < kMxSlice ? cols - c0 : kMxSlice) >> 3);
+    if (row < rows) {                                    // (uniform over the wavefront)
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
     uint4 v[MAXC];
 #pragma unroll
@@ -649,11 +670,11 @@ __global__ __launch_bounds__(kBlock) void k_blockwise_quant_act(const uint16_t* 
         const float s = pow2_floor(scale_from_amax<F>(amax, 0));
         if (ch < nch) {
             qr[ch] = !__builtin_isnan(amax) ? encode8<F, true>(v[c], s) : encode8<F, false>(v[c], s);
-            if ((lane & 15) == 0)
-                *reinterpret_cast<uint32_t*>(sc + 4 * ((int64_t)(ch >> 4) * ldsc + row)) =
-                    e8m0_of_inverse(s) * 0x01010101u;
+            if ((lane & 15) == 0) rec[(ch >> 4) * W + rl] = e8m0_of_inverse(s) * 0x01010101u;
         }
     }
+    }
+    store_records<W>(rec, (nch + 15) / 16, sc, ldsc, row0, rows);
 }
 
 // One workgroup per 128 x 128 tile (grid x: row tiles, y: K blocks). Thread
@@ -1645,12 +1666,17 @@ hipError_t launch_mx_quant_row(const uint16_t* x, int64_t rows, int64_t cols, in
                                int64_t ldq, uint8_t* scale, int64_t ld_scale, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
     const int chunks = reg_chunks(cols < kMxSlice ? cols : kMxSlice);
-    const dim3 grid(grid_for_rows(rows), (unsigned)((cols + kMxSlice - 1) / kMxSlice)), block(kBlock);
+    const unsigned slices = (unsigned)((cols + kMxSlice - 1) / kMxSlice);
+    // rows of up to 8 chunks per lane: 16 rows (wavefronts) per workgroup, two
+    // workgroups per CU; longer rows: 4 (16 wavefronts of 16-chunk rows would
+    // leave one workgroup per CU: slower)
 #define FP8_MX_CASE(F, C)                                                                                        \
-    case C:                                                                                                      \
-        hipLaunchKernelGGL((k_mx_quant_row<F, C>), grid, block, 0, st, x, rows, cols, ldx, q, ldq, scale,        \
-                           ld_scale);                                                                            \
-        break;
+    case C: {                                                                                                    \
+        constexpr int W = C <= 8 ? 16 : 4;                                                                       \
+        hipLaunchKernelGGL((k_mx_quant_row<F, C, W>), dim3((unsigned)((rows + W - 1) / W), slices), dim3(W * 64), \
+                           0, st, x, rows, cols, ldx, q, ldq, scale, ld_scale);                                  \
+        break;                                                                                                   \
+    }
 #define FP8_MX_FMT(F)                                                                                            \
     switch (chunks) {                                                                                            \
         FP8_MX_CASE(F, 1)                                                                                        \
@@ -1685,12 +1711,14 @@ hipError_t launch_blockwise_quant(const uint16_t* x, int64_t rows, int64_t cols,
         return hipGetLastError();
     }
     const int chunks = reg_chunks(cols < kMxSlice ? cols : kMxSlice);
-    const dim3 grid(grid_for_rows(rows), (unsigned)((cols + kMxSlice - 1) / kMxSlice)), block(kBlock);
+    const unsigned slices = (unsigned)((cols + kMxSlice - 1) / kMxSlice);
 #define FP8_BW_CASE(F, C)                                                                                        \
-    case C:                                                                                                      \
-        hipLaunchKernelGGL((k_blockwise_quant_act<F, C>), grid, block, 0, st, x, rows, cols, ldx, q, ldq, scale, \
-                           ld_scale);                                                                            \
-        break;
+    case C: {                                                                                                    \
+        constexpr int W = C <= 8 ? 16 : 4;                                                                       \
+        hipLaunchKernelGGL((k_blockwise_quant_act<F, C, W>), dim3((unsigned)((rows + W - 1) / W), slices),       \
+                           dim3(W * 64), 0, st, x, rows, cols, ldx, q, ldq, scale, ld_scale);                    \
+        break;                                                                                                   \
+    }
 #define FP8_BW_FMT(F)                                                                                            \
     switch (chunks) {                                                                                            \
         FP8_BW_CASE(F, 1)                                                                                        \
