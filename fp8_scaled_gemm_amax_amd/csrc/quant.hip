@@ -677,20 +677,24 @@ __global__ __launch_bounds__(W * 64) void k_blockwise_quant_act(const uint16_t* 
     store_records<W>(rec, (nch + 15) / 16, sc, ldsc, row0, rows);
 }
 
-// One workgroup per 128 x 128 tile (grid x: row tiles, y: K blocks). Thread
-// (wave w, lane l) holds chunk l % 16 of rows 16p + 4w + l / 16, p = 0..7 (rows
-// past the matrix clamped to its last row); tile amax over the workgroup
-// through LDS; threads holding chunk 0 store their rows' records.
+// One workgroup per 128 x 128 tile (kfast: grid x the K blocks and y the row
+// tiles, so that consecutive workgroups read neighbouring 256-byte segments of
+// the same rows, ~6% faster; otherwise x the row tiles and y the K blocks, for
+// more than 65535 row tiles). Thread (wave w, lane l) holds chunk l % 16 of
+// rows 16p + 4w + l / 16, p = 0..7 (rows past the matrix clamped to its last
+// row); tile amax over the workgroup through LDS; threads holding chunk 0 store
+// their rows' records.
 template <int F>
 __global__ __launch_bounds__(kBlock) void k_blockwise_quant_weight(const uint16_t* __restrict__ w, int64_t rows,
                                                                    int64_t ldw, uint8_t* __restrict__ q,
                                                                    int64_t ldq, uint8_t* __restrict__ sc,
-                                                                   int64_t ldsc) {
+                                                                   int64_t ldsc, int kfast) {
     __shared__ uint32_t red[kWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cc = lane & 15;
-    const int64_t r0 = (int64_t)blockIdx.x * 128;
-    const int64_t k0 = (int64_t)blockIdx.y * 128;
+    const int64_t kb = kfast ? blockIdx.x : blockIdx.y;         // K block
+    const int64_t r0 = (int64_t)(kfast ? blockIdx.y : blockIdx.x) * 128;
+    const int64_t k0 = kb * 128;
     uint4 v[8];
     uint32_t mx = 0;
 #pragma unroll
@@ -715,7 +719,7 @@ __global__ __launch_bounds__(kBlock) void k_blockwise_quant_weight(const uint16_
         if (r >= rows) continue;
         *reinterpret_cast<uint2*>(q + r * ldq + k0 + 8 * cc) = nan_free ? encode8<F, true>(v[p], s)
                                                                         : encode8<F, false>(v[p], s);
-        if (cc == 0) *reinterpret_cast<uint32_t*>(sc + 4 * (blockIdx.y * ldsc + r)) = rec;
+        if (cc == 0) *reinterpret_cast<uint32_t*>(sc + 4 * (kb * ldsc + r)) = rec;
     }
 }
 
@@ -1701,13 +1705,15 @@ hipError_t launch_blockwise_quant(const uint16_t* x, int64_t rows, int64_t cols,
                                   uint8_t* q, int64_t ldq, uint8_t* scale, int64_t ld_scale, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
     if (weight) {
-        const dim3 grid((unsigned)((rows + 127) / 128), (unsigned)(cols / 128)), block(kBlock);
+        const int64_t rt = (rows + 127) / 128, kbs = cols / 128;
+        const int kfast = rt <= 65535;
+        const dim3 grid(kfast ? (unsigned)kbs : (unsigned)rt, kfast ? (unsigned)rt : (unsigned)kbs), block(kBlock);
         if (fmt == kE4M3)
             hipLaunchKernelGGL((k_blockwise_quant_weight<kE4M3>), grid, block, 0, st, x, rows, ldx, q, ldq, scale,
-                               ld_scale);
+                               ld_scale, kfast);
         else
             hipLaunchKernelGGL((k_blockwise_quant_weight<kE5M2>), grid, block, 0, st, x, rows, ldx, q, ldq, scale,
-                               ld_scale);
+                               ld_scale, kfast);
         return hipGetLastError();
     }
     const int chunks = reg_chunks(cols < kMxSlice ? cols : kMxSlice);
