@@ -13,7 +13,9 @@ stream the kernels run on; `roofline` is for the GEMM (the dominant kernel)
 against MI355X's dense FP8 peak; `quantizers` gives each quantizer's
 algorithmic GB/s (2 B read + 1 B written per element + 4 B per scale) against
 8 TB/s; `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload on this host's cores.
+workload on this host's cores; `cold` repeats the step after evicting the
+caches (a 1 GiB read before each step, outside the step's events) and gives
+the median and minimum of every call.
 
 Other workloads (--workload c1|c3|c4|c4b|c4mx|c5) print the same line for the
 other shapes (c3 tensorwise delayed, c4 MoE grouped GEMM, c4b the MoE expert
@@ -37,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "FP8 scaled-GEMM TFLOP/s incl. quantize; quantizer GB/s; % of MI355X peak"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 matrix throughput (no sparsity)
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+EVICT_BYTES = 1 << 30         # > 8 x 4 MB of L2 and the 256 MB last-level cache
 
 
 def parse():
@@ -48,6 +51,8 @@ def parse():
     p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2bw", "c3", "c4", "c4b", "c4mx", "c5", "c6"])
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cold-steps", type=int, default=10,
+                   help="steps timed after evicting the caches (0: skip the cold-cache leg)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="time a plain 1 GiB copy kernel instead (for scaling rocprofv3 byte counters)")
     return p.parse_args()
@@ -480,6 +485,36 @@ def cpu_baseline_moe(w, target_s):
                       f"weights quantized, oracle steps incl. fp64 grouped products, {t:.1f} s on {threads} threads"}
 
 
+def cold_leg(step, steps, wev):
+    """Steps timed one at a time after a read of EVICT_BYTES, which pushes the
+    inputs out of the 4 MB L2s and the 256 MB last-level cache: each step then
+    starts from HBM as the first use of freshly loaded tensors would. A read
+    leaves clean lines behind (a write of the same size leaves dirty ones,
+    whose write-back the step's kernels would then pay for). The read is
+    enqueued before the step's first event, so no kernel of the step is
+    charged for it. Reports the median and minimum of each call and of the
+    whole step over these steps."""
+    import torch
+    buf = torch.ones(EVICT_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    ncalls = len(step.calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(steps)]
+    for _ in range(3):                                   # code objects loaded, clocks up
+        step.run(wev)
+    for i in range(steps):
+        buf.sum()
+        step.run(ev[i])
+    torch.cuda.synchronize()
+    call_ms = np.array([[ev[i][c].elapsed_time(ev[i][c + 1]) for c in range(ncalls)] for i in range(steps)])
+    step_ms = np.array([ev[i][0].elapsed_time(ev[i][ncalls]) for i in range(steps)])
+    del buf
+    return {"steps": steps, "evict_bytes": EVICT_BYTES,
+            "ms_per_step_median": round(float(np.median(step_ms)), 5),
+            "ms_per_step_min": round(float(step_ms.min()), 5),
+            "value_median": round(step.flops / (float(np.median(step_ms)) * 1e-3) / 1e12, 2),
+            "calls": [{"kernel": step.calls[c][0], "median_ms": round(float(np.median(call_ms[:, c])), 5),
+                       "min_ms": round(float(call_ms[:, c].min()), 5)} for c in range(ncalls)]}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -494,6 +529,9 @@ def main():
     ncalls = len(step.calls)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(args.steps)]
     wev = [torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)]
+    # the cold-cache leg runs first, so the warm timed steps are the last calls
+    # of every kernel in a trace of this process
+    cold = cold_leg(step, args.cold_steps, wev) if args.cold_steps > 0 else None
     for _ in range(args.warmup):
         step.run(wev)
     torch.cuda.synchronize()
@@ -541,7 +579,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": step.desc, "m": m, "n": n, "k": k, **step.scales, "out": "bf16",
                    "flops_per_step": step.flops},
-        "roofline": roofline, "quantizers": quant, "other_kernels": other,
+        "roofline": roofline, "quantizers": quant, "other_kernels": other, "cold": cold,
         "cpu_baseline": None if args.no_cpu_baseline else (
             cpu_baseline_moe(step.cpu_sample, args.cpu_seconds) if getattr(step, "cpu_kind", "") == "moe_layer"
             else cpu_baseline(step.cpu_sample, args.cpu_seconds, getattr(step, "cpu_kind", "rowwise"))),
