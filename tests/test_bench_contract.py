@@ -38,7 +38,8 @@ def test_traffic_records_name_their_sources():
     assert table
     for key, rec in table.items():
         assert rec["sources"] and rec["source_digest"], key
-        assert rec["bytes_per_launch"] == rec["read_bytes"] + rec["write_bytes"], key
+        # (each of the three is rounded to whole bytes on its own)
+        assert abs(rec["bytes_per_launch"] - rec["read_bytes"] - rec["write_bytes"]) <= 1, key
         for n in rec["sources"]:
             assert os.path.exists(os.path.join(ROOT, "fp8_scaled_gemm_amax_amd", "csrc", n)), (key, n)
 
