@@ -226,10 +226,19 @@ __global__ __launch_bounds__(kBlock) void k_amax_tensor_reg(const uint16_t* __re
 // One wavefront per row, the whole row held in registers (MAXC 16-byte chunks
 // per lane): read once, amax, scale, cast, write once. NT: nontemporal loads
 // (x streamed), unless another pass reads x right after.
+// Codes are stored nontemporally when one launch writes more of them than the
+// 256 MB last-level cache holds: kept there, they would leave it full of dirty
+// lines that the consuming GEMM then has to write back while it streams its
+// operands (DeepSeek-V3 expert layer: 587 MB of codes, grouped GEMM 318 ->
+// 284 us). Smaller outputs stay cached for the GEMM that reads them next
+// (Llama3-8B up-projection: 92 MB, where streaming them costs the GEMM 5%).
+constexpr int64_t kStreamCodesAbove = (int64_t)256 << 20;
+inline int streamed_codes(int64_t code_bytes) { return code_bytes > kStreamCodesAbove ? 1 : 0; }
+
 template <int F, int MAXC, bool NT>
 __device__ __forceinline__ void quant_row_one(const uint16_t* __restrict__ x, int64_t row, int64_t cols, int64_t ldx,
                                               int margin, uint8_t* __restrict__ q, int64_t ldq,
-                                              float* __restrict__ scale_inv, float* __restrict__ amax_out) {
+                                              float* __restrict__ scale_inv, float* __restrict__ amax_out, int nt_store) {
     const int lane = threadIdx.x & 63;
     const int nch = (int)(cols >> 3);
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
@@ -253,7 +262,13 @@ __device__ __forceinline__ void quant_row_one(const uint16_t* __restrict__ x, in
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = lane + c * 64;
-            if (ch < nch) qr[ch] = encode8<F, true>(v[c], s);
+            if (ch >= nch) continue;
+            const uint2 code = encode8<F, true>(v[c], s);
+            if (nt_store)
+                __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, code),
+                                            reinterpret_cast<unsigned long long*>(&qr[ch]));
+            else
+                qr[ch] = code;
         }
     } else {   // a NaN in the row (then s = 1): the bit-level encoder keeps NaN signs
 #pragma unroll
@@ -268,10 +283,10 @@ template <int F, int MAXC, bool NT>
 __global__ __launch_bounds__(kBlock) void k_quant_row_reg(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                           int64_t ldx, int margin, uint8_t* __restrict__ q,
                                                           int64_t ldq, float* __restrict__ scale_inv,
-                                                          float* __restrict__ amax_out) {
+                                                          float* __restrict__ amax_out, int nt_store) {
     const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (row >= rows) return;
-    quant_row_one<F, MAXC, NT>(x, row, cols, ldx, margin, q, ldq, scale_inv, amax_out);
+    quant_row_one<F, MAXC, NT>(x, row, cols, ldx, margin, q, ldq, scale_inv, amax_out, nt_store);
 }
 
 // Rowwise casts of up to kMaxRowBatch tensors with the same number of columns
@@ -291,6 +306,7 @@ struct RowBatch {
     int64_t ldq[kMaxRowBatch];
     int64_t first[kMaxRowBatch + 1];
     int count;
+    int nt_store;   // codes written nontemporally (see streamed_codes)
 };
 
 template <typename T>
@@ -318,7 +334,7 @@ __global__ __launch_bounds__(kBlock) void k_quant_row_batch(RowBatch b, int64_t 
     const int64_t row = (bid - first) * kWaves + (threadIdx.x >> 6);
     if (row >= batch_pick(b.rows, j)) return;
     quant_row_one<F, MAXC, true>(batch_pick(b.x, j), row, cols, batch_pick(b.ldx, j), margin, batch_pick(b.q, j),
-                                 batch_pick(b.ldq, j), batch_pick(b.scale_inv, j), batch_pick(b.amax, j));
+                                 batch_pick(b.ldq, j), batch_pick(b.scale_inv, j), batch_pick(b.amax, j), b.nt_store);
 }
 
 // Rows too long for registers, or unaligned layouts: two passes over the row
@@ -1283,14 +1299,15 @@ hipError_t quant_row_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
         return hipGetLastError();
     }
     const int64_t per_lane = (cols / 8 + 63) / 64;
+    const int nts = streamed_codes(rows * cols);
 #define FP8_ROW_CASE(C)                                                                                        \
     if (per_lane <= C) {                                                                                       \
         if (reread)                                                                                            \
             hipLaunchKernelGGL((k_quant_row_reg<F, C, false>), grid, block, 0, st, x, rows, cols, ldx, margin, \
-                               q, ldq, scale_inv, amax_out);                                                   \
+                               q, ldq, scale_inv, amax_out, nts);                                              \
         else                                                                                                   \
             hipLaunchKernelGGL((k_quant_row_reg<F, C, true>), grid, block, 0, st, x, rows, cols, ldx, margin,  \
-                               q, ldq, scale_inv, amax_out);                                                   \
+                               q, ldq, scale_inv, amax_out, nts);                                              \
         return hipGetLastError();                                                                              \
     }
     FP8_ROW_CASE(1)
@@ -1555,6 +1572,7 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
     }
     RowBatch b{};
     b.count = count;
+    b.nt_store = streamed_codes(total_rows * cols);
     int64_t blocks = 0;
     for (int j = 0; j < count; ++j) {
         b.x[j] = x[j];
