@@ -660,3 +660,77 @@ def blockwise_gemm_entries(a, fa, ea, b, fb, eb_tiles, ii, jj, chunk=1024):
         y[lo:lo + chunk] = (x * p.sum(axis=2)).sum(axis=1)
         bound[lo:lo + chunk] = (x * np.abs(p).sum(axis=2)).sum(axis=1)
     return y, bound
+
+
+# ------------------------------------------------------ whole products by rows --
+# The products above evaluated on every output of a full-size workload, in
+# blocks of rows so that the fp64 results of a block fit in memory. Same
+# definition ("FP8 Training on AMD GPUs with TorchTitan and TorchAO": rowwise /
+# colwise scaled FP8 linear layers and grouped GEMM; the MX and blockwise
+# readings above): the decoded codes form fp64 matrices and numpy's fp64 matrix
+# product is the library step that sums over k. Every product of two decoded
+# codes is exact in fp64, so only the summation order differs from the loops
+# of fp8_oracle.c (a relative error of at most k * 2^-53 of the bound term).
+# For the block-scaled forms, each decoded code is first multiplied by its
+# block's power-of-two factor (exact in fp64: the factors lie in 2^-127 ..
+# 2^127 and the codes' magnitudes in 2^-17 .. 2^16), which turns the sum over
+# blocks of scaled block sums into one plain sum over k.
+
+def _scaled_rows(codes, fmt, e8, block):
+    """Decoded codes [r x k] times 2^(e8 - 127) of their K block (e8 [r x k/block]; 255 -> NaN)."""
+    dec = decode(fmt, codes)
+    x = mx_scale_values(np.asarray(e8))
+    return dec * np.repeat(x, block, axis=1)
+
+
+def _product(ad, bd, bd_abs, sa, sb):
+    """(y, bound) of decoded operand rows ad [r x k], bd [n x k] (bd_abs = |bd|)
+    with the dequantisation factors sa [r] / sb [n] (or single values):
+    y = (ad bd^T) * sa * sb, bound = |sa * sb| * (|ad| |bd|^T)."""
+    sa = np.asarray(sa, np.float64).reshape(-1, 1) if np.size(sa) > 1 else np.float64(np.asarray(sa).reshape(-1)[0])
+    sb = np.asarray(sb, np.float64).reshape(1, -1) if np.size(sb) > 1 else np.float64(np.asarray(sb).reshape(-1)[0])
+    s = ad @ bd.T
+    t = np.abs(ad) @ bd_abs.T
+    return s * sa * sb, np.abs(sa * sb) * t
+
+
+def gemm_by_rows(a, fa, b, fb, a_scale, b_scale, chunk=1024):
+    """Every output of Y = (A B^T) * sa * sb (the oracle's gemm), yielded as
+    (r0, r1, y [r1-r0 x n], bound) over blocks of `chunk` rows of A."""
+    a = np.asarray(a, np.uint8)
+    m = a.shape[0]
+    sa = np.asarray(np.atleast_1d(a_scale), np.float32)
+    sb = np.asarray(np.atleast_1d(b_scale), np.float32)
+    bd = decode(fb, b)
+    bd_abs = np.abs(bd)
+    for r0 in range(0, m, chunk):
+        r1 = min(m, r0 + chunk)
+        y, bound = _product(decode(fa, a[r0:r1]), bd, bd_abs, sa[r0:r1] if sa.size > 1 else sa, sb)
+        yield r0, r1, y, bound
+
+
+def mx_gemm_by_rows(a, fa, sa, b, fb, sb, chunk=1024):
+    """Every output of the MX product (mx_gemm): a [m x k] with E8M0 block
+    scales sa [m x k/32], b [n x k] with sb [n x k/32]; yields (r0, r1, y, bound)."""
+    a = np.asarray(a, np.uint8)
+    bd = _scaled_rows(b, fb, sb, MX_BLOCK)
+    bd_abs = np.abs(bd)
+    for r0 in range(0, a.shape[0], chunk):
+        r1 = min(a.shape[0], r0 + chunk)
+        y, bound = _product(_scaled_rows(a[r0:r1], fa, np.asarray(sa)[r0:r1], MX_BLOCK), bd, bd_abs, 1.0, 1.0)
+        yield r0, r1, y, bound
+
+
+def blockwise_gemm_by_rows(a, fa, ea, b, fb, eb_tiles, chunk=1024):
+    """Every output of the blockwise product (blockwise_gemm): ea [m x k/128]
+    per activation row, eb_tiles [ceil(n/128) x k/128] per weight tile;
+    yields (r0, r1, y, bound)."""
+    a = np.asarray(a, np.uint8)
+    n = np.asarray(b).shape[0]
+    eb_rows = np.asarray(eb_tiles)[np.arange(n) // BLOCK]
+    bd = _scaled_rows(b, fb, eb_rows, BLOCK)
+    bd_abs = np.abs(bd)
+    for r0 in range(0, a.shape[0], chunk):
+        r1 = min(a.shape[0], r0 + chunk)
+        y, bound = _product(_scaled_rows(a[r0:r1], fa, np.asarray(ea)[r0:r1], BLOCK), bd, bd_abs, 1.0, 1.0)
+        yield r0, r1, y, bound

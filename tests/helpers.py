@@ -88,3 +88,27 @@ def assert_f32_bits_equal(got, want, what):
     if bad.size:
         i = tuple(bad[0])
         raise AssertionError(f"{what}: {len(bad)} mismatches, first at {i}: gpu {g[i]!r} oracle {w[i]!r}")
+
+
+def check_full(orc, d, blocks, what, row_offset=0, out_bf16=True):
+    """Every output of d (a torch tensor [rows x n], or its values already on
+    the host as a numpy array) against the oracle's row blocks (r0, r1, y,
+    bound), r0/r1 counted from row_offset of d. Reports the largest
+    |gpu - oracle| as a fraction of the allowed error."""
+    host = d if isinstance(d, np.ndarray) else d.float().cpu().numpy()
+    worst, rows = 0.0, 0
+    for r0, r1, y, bound in blocks:
+        got = host[row_offset + r0:row_offset + r1].astype(np.float64)
+        ok = orc.gemm_within_bound(got, y, bound, out_bf16=out_bf16)
+        if not ok.all():
+            i, j = np.argwhere(~ok)[0]
+            raise AssertionError(f"{what}: {int((~ok).sum())} outputs outside the bound in rows {r0}..{r1}; first "
+                                 f"({row_offset + r0 + i}, {j}): gpu {got[i, j]!r} oracle {y[i, j]!r} "
+                                 f"bound {bound[i, j]!r}")
+        tol = 1e-3 * bound + (2.0 ** -8 * np.abs(y) if out_bf16 else 0.0)
+        fin = np.isfinite(y) & (tol > 0)
+        if fin.any():
+            worst = max(worst, float((np.abs(got - y)[fin] / tol[fin]).max()))
+        rows += r1 - r0
+    say(what, "every output of", rows, "rows within the bound; max |err| / allowed =", round(worst, 4))
+    return rows

@@ -79,6 +79,38 @@ def test_cast_every_bf16_value_times_scales(fp8, orc, fmt):
         assert_f32_bits_equal(am.cpu().numpy(), [oam], "amax")
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_cast_products_next_to_every_tie(fp8, orc, fmt):
+    """The hardware-convert path at the rounding boundaries: every FP8 tie
+    (the midpoint of two neighbouring codes, in every binade and between
+    subnormals) is a bf16 value, so with s = 1 + j 2^-23 and s = 1 - j 2^-24
+    (j = 1..8) the fp32 products x s of all 65536 bf16 values x fall 1 to 16
+    fp32 ulps above and below each tie, and with s = 1 exactly on it. Also the
+    product-rounding witness s = 0x3F86F21C, for which fl32(1.0078125 s) is the
+    tie 1.0625 exactly while the exact product lies above it (e4m3: 0x38, the
+    even neighbour, only if the product is rounded to fp32 first)."""
+    xb = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    x = dev_bf16(xb)
+    scales = [np.float32(1.0)]
+    for j in range(1, 9):
+        scales += [np.float32(1.0 + j * 2.0 ** -23), np.float32(1.0 - j * 2.0 ** -24)]
+    witness = np.array([0x3F86F21C], np.uint32).view(np.float32)[0]
+    scales.append(witness)
+    for s32 in scales:
+        say("cast near ties", NAMES[fmt], "scale bits", hex(int(np.float32(s32).view(np.uint32))))
+        q = torch.empty((256, 256), dtype=torch.uint8, device="cuda:0")
+        si = torch.empty(1, device="cuda:0")
+        am = torch.zeros(1, device="cuda:0")
+        fp8.fp8_quantize_tensor(x, fmt, 0, dev_f32([s32]), q, si, am)
+        torch.cuda.synchronize()
+        oq, osi, _ = orc.quantize_tensor_scaled(xb, fmt, s32)
+        got = q.cpu().numpy()
+        assert_codes_equal(got, oq, f"{NAMES[fmt]} s=0x{int(np.float32(s32).view(np.uint32)):08X}")
+        assert_f32_bits_equal(si.cpu().numpy(), [osi], "scale_inv")
+    if fmt == 0:
+        assert got[0x3F81 >> 8, 0x3F81 & 0xFF] == 0x38
+
+
 # ----------------------------------------------------------------------- rows --
 
 ROW_SHAPES = [(1, 16), (3, 48), (37, 200), (256, 512), (300, 4104), (64, 14336), (9, 16392), (5, 0)]
