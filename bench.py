@@ -15,7 +15,9 @@ algorithmic GB/s (2 B read + 1 B written per element + 4 B per scale) against
 8 TB/s; `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload on this host's cores; `cold` repeats the step after evicting the
 caches (a 1 GiB read before each step, outside the step's events) and gives
-the median and minimum of every call.
+the median and minimum of every call. Before the W warmup steps, untimed
+steps run for --settle-seconds (reported as `settle`), so that the timed
+steps see the clock the device holds under sustained load.
 
 Other workloads (--workload c1|c3|c4|c4b|c4mx|c5) print the same line for the
 other shapes (c3 tensorwise delayed, c4 MoE grouped GEMM, c4b the MoE expert
@@ -51,6 +53,9 @@ def parse():
     p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2bw", "c3", "c4", "c4b", "c4mx", "c5", "c6"])
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target length of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--settle-seconds", type=float, default=1.0,
+                   help="untimed steps for this long before the warmup steps (the clock ramps up over the first "
+                        "tens of ms of load on a fresh device)")
     p.add_argument("--cold-steps", type=int, default=10,
                    help="steps timed after evicting the caches (0: skip the cold-cache leg)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -253,14 +258,59 @@ class Step:
             self.qxt, self.sxt, self.cax = E((k, m), dtype=torch.uint8, device=dev), E(k, device=dev), E(k, device=dev)
             self.dx = E((m, k), dtype=torch.bfloat16, device=dev)
             self.dw = E((n, k), dtype=torch.bfloat16, device=dev)
+            # the forward's rowwise cast of X and W left their column amax as side
+            # outputs (fp8_quantize_row_batch with col_amax_out): the backward's
+            # colwise casts of X^T and W^T take them as ready
+            qx, qw = E((m, k), dtype=torch.uint8, device=dev), E((n, k), dtype=torch.uint8, device=dev)
+            fp8.fp8_quantize_row_batch([self.x, self.w], fp8.E4M3, 0, [qx, qw], [E(m, device=dev), E(n, device=dev)],
+                                       None, [self.cax, self.caw])
+            torch.cuda.synchronize()
+            del qx, qw
             self.mnk = [(m, k, n), (n, k, m)]
-            self.calls = [("quantize_row dY e5m2 (+col amax)", m * n, m), ("quantize_col dY^T e5m2", m * n, n),
-                          ("quantize_col W^T e4m3", n * k, k), ("quantize_col X^T e4m3", m * k, k),
-                          ("gemm dgrad", None, 0), ("gemm wgrad", None, 0)]
+            # each product right after the casts it reads, so that their codes are
+            # still in the last-level cache (and no other cast's dirty codes are)
+            self.calls = [("quantize_row dY e5m2 (+col amax, one pass)", m * n, m),
+                          ("quantize_col W^T e4m3 (col amax from the forward)", n * k, k),
+                          ("gemm dgrad", None, 0),
+                          ("quantize_col dY^T e5m2 (col amax ready)", m * n, n),
+                          ("quantize_col X^T e4m3 (col amax from the forward)", m * k, k),
+                          ("gemm wgrad", None, 0)]
             self.desc = ("hybrid backward of the Llama3-8B up-proj: dY bf16 [8192x14336] N(0,1e-3^2) e5m2; "
-                         "dgrad dX = dY W, wgrad dW = dY^T X with colwise token scales; bf16 out")
+                         "dgrad dX = dY W, wgrad dW = dY^T X with colwise token scales (X and W column amax "
+                         "from the forward cast's side outputs); bf16 out")
             self.scales = {"recipe": "rowwise+colwise", "format": "e5m2 x e4m3"}
         self.flops = sum(2.0 * m * n * k for m, n, k in self.mnk)
+
+    def extra(self, reps=50):
+        """Measurements beside the step. Llama3-8B up-projection: the forward
+        cast of X and W with their column amax as side outputs (what a training
+        step's forward does so that the backward's colwise casts of X^T and W^T
+        need no amax pass), algorithmic bytes 2 + 1 per element, 4 per row scale
+        and 4 per column amax."""
+        if self.name != "c2":
+            return {}
+        torch, f = self.torch, self.fp8
+        m, k = self.x.shape
+        n = self.w.shape[0]
+        cx, cw = torch.empty(k, device="cuda:0"), torch.empty(k, device="cuda:0")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def cast():
+            f.fp8_quantize_row_batch([self.x, self.w], f.E4M3, 0, [self.qx, self.qw], [self.sx, self.sw], None,
+                                     [cx, cw])
+        for _ in range(10):
+            cast()
+        e0.record()
+        for _ in range(reps):
+            cast()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = 3.0 * (m + n) * k + 4.0 * (m + n) + 8.0 * k
+        return {"forward_cast_with_col_amax": {
+            "kernel": "quantize_row X+W with column amax side outputs (clear + one pass)", "avg_ms": round(ms, 5),
+            "algorithmic_bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "reps": reps}}
 
     def run(self, ev):
         """Enqueue one step; ev[i] is recorded after call i (ev[0] before the first)."""
@@ -344,14 +394,14 @@ class Step:
         else:
             f.fp8_quantize_row(self.dy, f.E5M2, 0, self.qdy, self.sdy, None, self.cady)
             ev[1].record()
-            f.fp8_quantize_col(self.dy, f.E5M2, 0, self.qdyt, self.sdyt, self.cady, col_amax_ready=True)
+            f.fp8_quantize_col(self.w, f.E4M3, 0, self.qwt, self.swt, self.caw, col_amax_ready=True)
             ev[2].record()
-            f.fp8_quantize_col(self.w, f.E4M3, 0, self.qwt, self.swt, self.caw)
-            ev[3].record()
-            f.fp8_quantize_col(self.x, f.E4M3, 0, self.qxt, self.sxt, self.cax)
-            ev[4].record()
             f.fp8_gemm_scaled(self.qdy, f.E5M2, self.qwt, f.E4M3, self.sdy, f.SCALE_VECTOR, self.swt, f.SCALE_VECTOR,
                               self.dx)
+            ev[3].record()
+            f.fp8_quantize_col(self.dy, f.E5M2, 0, self.qdyt, self.sdyt, self.cady, col_amax_ready=True)
+            ev[4].record()
+            f.fp8_quantize_col(self.x, f.E4M3, 0, self.qxt, self.sxt, self.cax, col_amax_ready=True)
             ev[5].record()
             f.fp8_gemm_scaled(self.qdyt, f.E5M2, self.qxt, f.E4M3, self.sdyt, f.SCALE_VECTOR, self.sxt,
                               f.SCALE_VECTOR, self.dw)
@@ -532,6 +582,13 @@ def main():
     # the cold-cache leg runs first, so the warm timed steps are the last calls
     # of every kernel in a trace of this process
     cold = cold_leg(step, args.cold_steps, wev) if args.cold_steps > 0 else None
+    settle_steps, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for _ in range(10):
+            step.run(wev)
+        torch.cuda.synchronize()
+        settle_steps += 10
+    settle_s = time.perf_counter() - t_settle
     for _ in range(args.warmup):
         step.run(wev)
     torch.cuda.synchronize()
@@ -580,6 +637,8 @@ def main():
         "config": {"workload": step.desc, "m": m, "n": n, "k": k, **step.scales, "out": "bf16",
                    "flops_per_step": step.flops},
         "roofline": roofline, "quantizers": quant, "other_kernels": other, "cold": cold,
+        "settle": {"seconds": round(settle_s, 3), "steps": settle_steps},
+        **step.extra(),
         "cpu_baseline": None if args.no_cpu_baseline else (
             cpu_baseline_moe(step.cpu_sample, args.cpu_seconds) if getattr(step, "cpu_kind", "") == "moe_layer"
             else cpu_baseline(step.cpu_sample, args.cpu_seconds, getattr(step, "cpu_kind", "rowwise"))),

@@ -73,7 +73,7 @@ def _load():
         "fp8_amax": [P, I64, I64, I64, I, P, P],
         "fp8_quantize_tensor": [P, I64, I64, I64, I, I32, P, P, I64, P, P, P],
         "fp8_quantize_row": [P, I64, I64, I64, I, I32, P, I64, P, P, P, P],
-        "fp8_quantize_row_batch": [I32, P, P, I64, P, I, I32, P, P, P, P, P],
+        "fp8_quantize_row_batch": [I32, P, P, I64, P, I, I32, P, P, P, P, P, P],
         "fp8_quantize_tensor_batch": [I32, P, P, I64, P, I, P, P, P, P, P, P],
         "fp8_quantize_col": [P, I64, I64, I64, I, I32, P, I64, P, P, I32, P],
         "fp8_delayed_scale_update": [P, P, P, I64, I32, I, I32, I, P, P, P],
@@ -172,11 +172,13 @@ def fp8_quantize_row(x, fmt, margin, q, scale_inv_out, amax_out=None, col_amax_o
                                 _ptr(amax_out), _ptr(col_amax_out), _stream(x)))
 
 
-def fp8_quantize_row_batch(xs, fmt, margin, qs, scale_inv_outs, amax_outs=None):
-    """Rowwise casts of the bf16 tensors xs (same number of columns) in one launch."""
+def fp8_quantize_row_batch(xs, fmt, margin, qs, scale_inv_outs, amax_outs=None, col_amax_outs=None):
+    """Rowwise casts of the bf16 tensors xs (same number of columns) in one
+    launch; col_amax_outs[j] (fp32 [cols] or None) receives tensor j's column amax."""
     count = len(xs)
-    if not (len(qs) == len(scale_inv_outs) == count) or (amax_outs is not None and len(amax_outs) != count):
-        raise ValueError("xs, qs, scale_inv_outs (and amax_outs) must have the same length")
+    if not (len(qs) == len(scale_inv_outs) == count) or (amax_outs is not None and len(amax_outs) != count) or (
+            col_amax_outs is not None and len(col_amax_outs) != count):
+        raise ValueError("xs, qs, scale_inv_outs (and amax_outs, col_amax_outs) must have the same length")
     if count == 0:
         raise ValueError("no tensors")
     shapes = [_bf16(x) for x in xs]
@@ -191,7 +193,9 @@ def fp8_quantize_row_batch(xs, fmt, margin, qs, scale_inv_outs, amax_outs=None):
     ldq = P64(*[_mat(q, "q", 1)[2] for q in qs])
     sp = PP(*[_ptr(s) for s in scale_inv_outs])
     ap = PP(*[_ptr(a) for a in amax_outs]) if amax_outs is not None else None
-    _check(lib.fp8_quantize_row_batch(count, xp, rows, cols, ldx, fmt, margin, qp, ldq, sp, ap, _stream(xs[0])))
+    cp = PP(*[_ptr(c) for c in col_amax_outs]) if col_amax_outs is not None else None
+    _check(lib.fp8_quantize_row_batch(count, xp, rows, cols, ldx, fmt, margin, qp, ldq, sp, ap, cp,
+                                      _stream(xs[0])))
 
 
 def fp8_quantize_tensor_batch(xs, fmt, scales, qs, scale_inv_outs, amax_outs):

@@ -241,16 +241,18 @@ fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int
         return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer", fn);
     FP8_TRY(check_device());
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_quant_row(x, rows, cols, ldx, (int)fmt, margin, q, ldq, scale_inv_out, amax_out,
-                                    col_amax_out != nullptr, st);
-    if (e == hipSuccess && col_amax_out) e = launch_amax(x, rows, cols, ldx, FP8_AXIS_COL, col_amax_out, st);
-    return launched(e, fn);
+    if (col_amax_out)       // the column amax as a side output of the same pass (a batch of one)
+        return launched(launch_quant_row_batch(1, &x, &rows, cols, &ldx, (int)fmt, margin, &q, &ldq, &scale_inv_out,
+                                               &amax_out, &col_amax_out, st),
+                        fn);
+    return launched(launch_quant_row(x, rows, cols, ldx, (int)fmt, margin, q, ldq, scale_inv_out, amax_out, false, st),
+                    fn);
 }
 
 fp8_status_t fp8_quantize_row_batch(int32_t count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
                                     const int64_t* ldx, fp8_format_t fmt, int32_t margin, uint8_t* const* q,
                                     const int64_t* ldq, float* const* scale_inv_out, float* const* amax_out,
-                                    void* stream) {
+                                    float* const* col_amax_out, void* stream) {
     const char* fn = "fp8_quantize_row_batch";
     if (count < 1 || count > FP8_MAX_ROW_BATCH)
         return fail(FP8_ERR_INVALID_ARG, "%s: count %d outside 1..%d", fn, (int)count, FP8_MAX_ROW_BATCH);
@@ -260,12 +262,13 @@ fp8_status_t fp8_quantize_row_batch(int32_t count, const uint16_t* const* x, con
         FP8_TRY(check_common_quant(fn, x[j], rows[j], cols, ldx[j], (int)fmt, margin));
         FP8_TRY(check_matrix(fn, "q", q[j], rows[j], cols, ldq[j]));
         if (rows[j] > 0 && !scale_inv_out[j]) return fail(FP8_ERR_INVALID_ARG, "%s: scale_inv_out[%d] is NULL", fn, j);
-        if (!aligned(scale_inv_out[j], 4) || (amax_out && !aligned(amax_out[j], 4)))
+        if (!aligned(scale_inv_out[j], 4) || (amax_out && !aligned(amax_out[j], 4)) ||
+            (col_amax_out && !aligned(col_amax_out[j], 4)))
             return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer (tensor %d)", fn, j);
     }
     FP8_TRY(check_device());
     return launched(launch_quant_row_batch(count, x, rows, cols, ldx, (int)fmt, margin, q, ldq, scale_inv_out,
-                                           amax_out, (hipStream_t)stream),
+                                           amax_out, col_amax_out, (hipStream_t)stream),
                     fn);
 }
 

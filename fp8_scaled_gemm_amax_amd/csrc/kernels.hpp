@@ -24,10 +24,13 @@ hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64
                             uint8_t* q, int64_t ldq, float* scale_inv, float* amax_out, bool reread, hipStream_t st);
 
 // Rowwise casts of count tensors sharing cols (host arrays of count entries;
-// amax_out may be NULL): one launch when all take the register kernel.
+// amax_out and col_amax, or any of their entries, may be NULL): one launch
+// when all take the register kernel (after a clearing launch when a column
+// amax is asked for: it is then a side output of the same pass).
 hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
                                   const int64_t* ldx, int fmt, int margin, uint8_t* const* q, const int64_t* ldq,
-                                  float* const* scale_inv, float* const* amax_out, hipStream_t st);
+                                  float* const* scale_inv, float* const* amax_out, float* const* col_amax,
+                                  hipStream_t st);
 
 hipError_t launch_quant_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
                             uint8_t* qt, int64_t ldqt, float* scale_inv, const float* col_amax, hipStream_t st);

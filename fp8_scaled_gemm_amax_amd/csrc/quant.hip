@@ -301,6 +301,7 @@ struct RowBatch {
     uint8_t* q[kMaxRowBatch];
     float* scale_inv[kMaxRowBatch];
     float* amax[kMaxRowBatch];
+    float* col_amax[kMaxRowBatch];   // column-amax side outputs (k_quant_row_colmax only; may be NULL)
     int64_t rows[kMaxRowBatch];
     int64_t ldx[kMaxRowBatch];
     int64_t ldq[kMaxRowBatch];
@@ -335,6 +336,178 @@ __global__ __launch_bounds__(kBlock) void k_quant_row_batch(RowBatch b, int64_t 
     if (row >= batch_pick(b.rows, j)) return;
     quant_row_one<F, MAXC, true>(batch_pick(b.x, j), row, cols, batch_pick(b.ldx, j), margin, batch_pick(b.q, j),
                                  batch_pick(b.ldq, j), batch_pick(b.scale_inv, j), batch_pick(b.amax, j), b.nt_store);
+}
+
+// Rowwise casts with the per-column amax of each tensor as a side output (for
+// a later colwise quantization of the same tensor: "FP8 Training on AMD GPUs
+// with TorchTitan and TorchAO", colwise scales), in the same single pass over
+// x. Tensor j owns workgroups first[j] .. first[j+1]-1 (about one per CU in
+// all), which stride over its rows, a wavefront per row at a time. The
+// workgroup's column maxima meet in LDS as fp32 bit patterns (relaxed LDS max)
+// at index (col % 8) * 64 MAXC + col / 8, so the 64 lanes of one LDS max touch
+// 64 consecutive words. REG: each wavefront keeps the running packed magnitude
+// max of its chunks in registers and folds it into LDS once at the end (rows
+// of up to 8 chunks per lane); otherwise it folds every row into LDS right
+// after casting it (longer rows leave no registers for a running max). PREF:
+// each wavefront loads its next row before casting the current one (two rows
+// in registers). At the end
+// each column is folded into col_amax[j] (cleared beforehand) by one relaxed
+// atomic max per workgroup, skipped where the workgroup saw only zeros: with
+// one workgroup per CU the atomics stay few (one per column per CU).
+template <int MAXC>
+__device__ __forceinline__ void load_row_chunks(uint4 (&v)[MAXC], const uint16_t* __restrict__ x, int64_t row,
+                                                int64_t ldx, int nch) {
+    const int lane = threadIdx.x & 63;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int ch = lane + c * 64;
+        v[c] = load_stream(xr + (ch < nch ? ch : nch - 1));   // past the row: a duplicate chunk, never used
+    }
+}
+
+template <int F, int MAXC>
+__device__ __forceinline__ void cast_row_chunks(const uint4 (&v)[MAXC], int64_t row, int nch, int margin,
+                                                uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale_inv,
+                                                float* __restrict__ amax_out, int nt_store) {
+    const int lane = threadIdx.x & 63;
+    uint32_t mx = 0;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) mx = word_absmax(mx, v[c]);
+    const float amax = amax_from_bits16(wave_max_u32(pk_fold(mx)));
+    const float s = scale_from_amax<F>(amax, margin);
+    if (lane == 0) {
+        scale_inv[row] = 1.0f / s;
+        if (amax_out) amax_out[row] = amax;
+    }
+    uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+    if (!__builtin_isnan(amax)) {
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = lane + c * 64;
+            if (ch >= nch) continue;
+            const uint2 code = encode8<F, true>(v[c], s);
+            if (nt_store)
+                __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, code),
+                                            reinterpret_cast<unsigned long long*>(&qr[ch]));
+            else
+                qr[ch] = code;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = lane + c * 64;
+            if (ch < nch) qr[ch] = encode8<F, false>(v[c], s);
+        }
+    }
+}
+
+// Folds packed magnitude words (chunk layout) into the LDS column maxima:
+// column col at word (col % 8) * MAXC * 64 + col / 8 (so every address is the
+// lane's word plus a compile-time offset).
+template <int MAXC>
+__device__ __forceinline__ void fold_chunks_lds(const uint4 (&w)[MAXC], uint32_t* red, int nch) {
+    constexpr int kSeg = MAXC * 64;
+    const int lane = threadIdx.x & 63;
+    uint32_t* base = red + lane;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        if (lane + c * 64 >= nch) continue;
+        const uint32_t a[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __hip_atomic_fetch_max(base + (2 * k) * kSeg + c * 64, (a[k] & 0xffffu) << 16, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_max(base + (2 * k + 1) * kSeg + c * 64, a[k] & 0xffff0000u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+}
+
+template <int F, int MAXC, int WAVES, bool REG, bool PREF>
+__global__ __launch_bounds__(WAVES * 64) void k_quant_row_colmax(RowBatch b, int64_t cols, int margin) {
+    constexpr int kCols = MAXC * 64 * 8;                 // columns a row of MAXC chunks per lane can hold
+    __shared__ uint32_t red[kCols];
+    const int64_t bid = blockIdx.x;
+    int j = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxRowBatch; ++i)
+        if (i < b.count && bid >= b.first[i]) j = i;
+    int64_t first = b.first[0], next = b.first[1];
+#pragma unroll
+    for (int i = 1; i < kMaxRowBatch; ++i)
+        if (i == j) {
+            first = b.first[i];
+            next = b.first[i + 1];
+        }
+    const int wave = threadIdx.x >> 6;
+    const int nch = (int)(cols >> 3);
+    const int64_t rows = batch_pick(b.rows, j);
+    float* cam = batch_pick(b.col_amax, j);
+    for (int i = threadIdx.x; i < kCols; i += WAVES * 64) red[i] = 0u;
+    __syncthreads();
+    const uint16_t* x = batch_pick(b.x, j);
+    uint8_t* q = batch_pick(b.q, j);
+    float* si = batch_pick(b.scale_inv, j);
+    float* am = batch_pick(b.amax, j);
+    const int64_t ldx = batch_pick(b.ldx, j), ldq = batch_pick(b.ldq, j);
+    const int64_t stride = (next - first) * WAVES;
+    uint4 cm[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) cm[c] = make_uint4(0u, 0u, 0u, 0u);
+    int64_t row = (bid - first) * WAVES + wave;
+    uint4 v[MAXC];
+    if (PREF && row < rows) load_row_chunks<MAXC>(v, x, row, ldx, nch);
+    while (row < rows) {
+        uint4 cur[MAXC];
+        const int64_t nrow = row + stride;
+        if constexpr (PREF) {
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) cur[c] = v[c];
+            if (nrow < rows) load_row_chunks<MAXC>(v, x, nrow, ldx, nch);     // the next row is in flight meanwhile
+        } else {
+            load_row_chunks<MAXC>(cur, x, row, ldx, nch);
+        }
+        cast_row_chunks<F, MAXC>(cur, row, nch, margin, q, ldq, si, am, b.nt_store);
+        if (cam) {
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) {
+                cur[c].x &= 0x7fff7fffu;
+                cur[c].y &= 0x7fff7fffu;
+                cur[c].z &= 0x7fff7fffu;
+                cur[c].w &= 0x7fff7fffu;
+            }
+            if constexpr (REG) {
+#pragma unroll
+                for (int c = 0; c < MAXC; ++c) {
+                    cm[c].x = pk_absmax(cm[c].x, cur[c].x);
+                    cm[c].y = pk_absmax(cm[c].y, cur[c].y);
+                    cm[c].z = pk_absmax(cm[c].z, cur[c].z);
+                    cm[c].w = pk_absmax(cm[c].w, cur[c].w);
+                }
+            } else {
+                fold_chunks_lds<MAXC>(cur, red, nch);
+            }
+        }
+        row = nrow;
+    }
+    if (cam == nullptr) return;                          // (uniform over the workgroup)
+    if constexpr (REG) fold_chunks_lds<MAXC>(cm, red, nch);
+    __syncthreads();
+    for (int i = threadIdx.x; i < cols; i += WAVES * 64) {
+        const uint32_t v32 = red[(i & 7) * (MAXC * 64) + (i >> 3)];
+        if (v32 != 0u) atomic_max_bits(cam + i, v32);
+    }
+}
+
+// Clears the column-amax outputs of a batch (count x cols floats) in one launch.
+__global__ void k_fill_col_amax(RowBatch b, int64_t cols) {
+    const int64_t n = (int64_t)b.count * cols;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int j = (int)(i / cols);
+        float* cam = batch_pick(b.col_amax, j);
+        if (cam) cam[i - (int64_t)j * cols] = 0.0f;
+    }
 }
 
 // Rows too long for registers, or unaligned layouts: two passes over the row
@@ -513,6 +686,7 @@ struct TensorBatch {
     const float* scale[kMaxRowBatch];
     float* scale_inv[kMaxRowBatch];
     float* amax[kMaxRowBatch];
+    float* col_amax[kMaxRowBatch];   // column-amax side outputs (k_quant_row_colmax only; may be NULL)
     int64_t rows[kMaxRowBatch];
     int64_t ldx[kMaxRowBatch];
     int64_t ldq[kMaxRowBatch];
@@ -768,18 +942,33 @@ __device__ __forceinline__ void col_scales_to_lds(const float* __restrict__ col_
 // (= input column) as 128 contiguous bytes.
 constexpr int kColTileR = 128, kColTileC = 64;
 
-// One 128 x 64 tile: source rows r0 .. r0+127 (rows at or past src_end read as
-// row src_end-1, or as zeros when zero_past_end), columns c0 .. c0+63 scaled by
-// s_lds / nan_lds; written transposed to qt rows c0 .. (one per column) at
-// columns d0 .. d0+127, none at or past d_end.
-template <int F>
-__device__ __forceinline__ void col_tile(const uint16_t* __restrict__ x, int64_t ldx, int64_t r0, int64_t src_end,
-                                         bool zero_past_end, int64_t c0, int64_t cols, const float* s_lds,
-                                         const int* nan_lds, uint32_t* tile, uint8_t* __restrict__ qt, int64_t ldqt,
-                                         int64_t d0, int64_t d_end, int vec_store) {
+// Loads of one 128 x 64 tile: source rows r0 .. r0+127 (rows at or past
+// src_end read as row src_end-1, or as zeros when zero_past_end), columns
+// c0 .. c0+63; thread (cc = t % 8, rg = t / 8) takes rows 4rg .. 4rg+3 of
+// columns 8cc .. 8cc+7. Rows / columns past the end re-read the last row /
+// chunk, so the loads stay unconditional (all four in flight together); those
+// codes are never stored, or become zeros when zero_past_end.
+__device__ __forceinline__ void col_tile_load(uint4 (&v)[4], const uint16_t* __restrict__ x, int64_t ldx, int64_t r0,
+                                              int64_t src_end, bool zero_past_end, int64_t c0, int64_t cols) {
     const int t = threadIdx.x;
     const int cc = t & 7, rg = t >> 3;
     const int64_t col = c0 + cc * 8;
+    const int64_t lcol = col < cols ? col : cols - 8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t row = r0 + rg * 4 + r;
+        v[r] = *reinterpret_cast<const uint4*>(x + (row < src_end ? row : src_end - 1) * ldx + lcol);
+        if (zero_past_end && row >= src_end) v[r] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// Casts the loaded rows with the column scales s_lds / nan_lds and writes them
+// transposed into the LDS tile (no barrier).
+template <int F>
+__device__ __forceinline__ void col_tile_encode(const uint4 (&v)[4], const float* s_lds, const int* nan_lds,
+                                               uint32_t* tile) {
+    const int t = threadIdx.x;
+    const int cc = t & 7, rg = t >> 3;
     uint32_t w[4][2];
     float s[8];
     int any_nan = 0;
@@ -787,17 +976,6 @@ __device__ __forceinline__ void col_tile(const uint16_t* __restrict__ x, int64_t
     for (int j = 0; j < 8; ++j) {
         s[j] = s_lds[cc * 8 + j];
         any_nan |= nan_lds[cc * 8 + j];
-    }
-    // rows / columns past the end re-read the last row / chunk, so the loads stay
-    // unconditional (all four in flight together); those codes are never stored,
-    // or become zeros when zero_past_end
-    uint4 v[4];
-    const int64_t lcol = col < cols ? col : cols - 8;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t row = r0 + rg * 4 + r;
-        v[r] = *reinterpret_cast<const uint4*>(x + (row < src_end ? row : src_end - 1) * ldx + lcol);
-        if (zero_past_end && row >= src_end) v[r] = make_uint4(0u, 0u, 0u, 0u);
     }
     if (!any_nan) {
 #pragma unroll
@@ -834,7 +1012,14 @@ __device__ __forceinline__ void col_tile(const uint16_t* __restrict__ x, int64_t
             tile[lc * (kColTileR / 4) + chunk * 4 + (rg & 3)] = tcol[c];
         }
     }
-    __syncthreads();
+}
+
+// Writes the LDS tile transposed to qt rows c0 .. (one per column) at columns
+// d0 .. d0+127, none at or past d_end (after a barrier).
+__device__ __forceinline__ void col_tile_store(const uint32_t* tile, int64_t c0, int64_t cols,
+                                               uint8_t* __restrict__ qt, int64_t ldqt, int64_t d0, int64_t d_end,
+                                               int vec_store) {
+    const int t = threadIdx.x;
     // 64 columns x 8 chunks of 16 bytes; two per thread
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -853,6 +1038,20 @@ __device__ __forceinline__ void col_tile(const uint16_t* __restrict__ x, int64_t
             for (int b = 0; b < 16 && orow + b < d_end; ++b) dst[b] = (uint8_t)(wv[b >> 2] >> (8 * (b & 3)));
         }
     }
+}
+
+// One 128 x 64 tile (load, cast, transpose through LDS, store): source rows
+// r0 .. r0+127 of columns c0 .. c0+63 to qt rows c0 .. at columns d0 ...
+template <int F>
+__device__ __forceinline__ void col_tile(const uint16_t* __restrict__ x, int64_t ldx, int64_t r0, int64_t src_end,
+                                         bool zero_past_end, int64_t c0, int64_t cols, const float* s_lds,
+                                         const int* nan_lds, uint32_t* tile, uint8_t* __restrict__ qt, int64_t ldqt,
+                                         int64_t d0, int64_t d_end, int vec_store) {
+    uint4 v[4];
+    col_tile_load(v, x, ldx, r0, src_end, zero_past_end, c0, cols);
+    col_tile_encode<F>(v, s_lds, nan_lds, tile);
+    __syncthreads();
+    col_tile_store(tile, c0, cols, qt, ldqt, d0, d_end, vec_store);
 }
 
 template <int F>
@@ -1550,11 +1749,50 @@ hipError_t quant_row_batch_fmt(const RowBatch& b, int64_t blocks, int64_t cols, 
     return hipErrorInvalidValue;   // (the caller checked per_lane <= 32)
 }
 
+// Launch shape of the column-amax rowwise kernel by row length (16-byte
+// chunks per lane): wavefronts per workgroup, workgroups per CU, running max
+// in registers (REG) or folded into LDS per row, next row prefetched (PREF).
+struct ColmaxShape {
+    int waves, wg_per_cu;
+};
+ColmaxShape colmax_shape(int64_t per_lane) {
+    if (per_lane > 8) return {4, 1};        // 16, 32 chunks: the row and its running max fill a SIMD's registers
+    return {4, 4};
+}
+template <int F>
+hipError_t quant_row_colmax_fmt(const RowBatch& b, int64_t blocks, int64_t cols, int margin, hipStream_t st) {
+    const int64_t per_lane = (cols / 8 + 63) / 64;
+    // clear every requested column amax (one launch), then the single pass
+    hipLaunchKernelGGL(k_fill_col_amax, dim3((unsigned)((b.count * cols + kBlock - 1) / kBlock < 1024
+                                                            ? (b.count * cols + kBlock - 1) / kBlock : 1024)),
+                       dim3(kBlock), 0, st, b, cols);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+#define FP8_ROW_COLMAX_CASE(C, W, REG, PREF)                                                                       \
+    if (per_lane <= C) {                                                                                           \
+        hipLaunchKernelGGL((k_quant_row_colmax<F, C, W, REG, PREF>), dim3((unsigned)blocks), dim3(W * 64), 0, st, b,  \
+                           cols, margin);                                                                          \
+        return hipGetLastError();                                                                                  \
+    }
+    FP8_ROW_COLMAX_CASE(1, 4, true, false)
+    FP8_ROW_COLMAX_CASE(2, 4, true, false)
+    FP8_ROW_COLMAX_CASE(4, 4, true, false)
+    FP8_ROW_COLMAX_CASE(8, 4, true, false)
+    FP8_ROW_COLMAX_CASE(16, 4, true, false)
+    FP8_ROW_COLMAX_CASE(32, 4, true, false)
+#undef FP8_ROW_COLMAX_CASE
+    return hipErrorInvalidValue;   // (the caller checked per_lane <= 32)
+}
+
 hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
                                   const int64_t* ldx, int fmt, int margin, uint8_t* const* q, const int64_t* ldq,
-                                  float* const* scale_inv, float* const* amax_out, hipStream_t st) {
+                                  float* const* scale_inv, float* const* amax_out, float* const* col_amax,
+                                  hipStream_t st) {
+    bool any_col = false;
+    for (int j = 0; j < count && col_amax; ++j) any_col = any_col || col_amax[j] != nullptr;
     // one launch when every tensor takes the register kernel (vector layout,
     // rows of at most 32 chunks per lane); otherwise one launch per tensor
+    // (and a separate column-amax pass per tensor that asks for it)
     bool one = count <= kMaxRowBatch && cols > 0 && cols % 8 == 0 && (cols / 8 + 63) / 64 <= 32;
     int64_t total_rows = 0;
     for (int j = 0; j < count && one; ++j) {
@@ -1564,8 +1802,10 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
     one = one && total_rows / kWaves < ((int64_t)1 << 31) - kMaxRowBatch;    // the grid's x extent
     if (!one) {
         for (int j = 0; j < count; ++j) {
-            const hipError_t e = launch_quant_row(x[j], rows[j], cols, ldx[j], fmt, margin, q[j], ldq[j],
-                                                  scale_inv[j], amax_out ? amax_out[j] : nullptr, false, st);
+            float* ca = any_col ? col_amax[j] : nullptr;
+            hipError_t e = launch_quant_row(x[j], rows[j], cols, ldx[j], fmt, margin, q[j], ldq[j], scale_inv[j],
+                                            amax_out ? amax_out[j] : nullptr, ca != nullptr, st);
+            if (e == hipSuccess && ca) e = launch_amax(x[j], rows[j], cols, ldx[j], 2, ca, st);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -1573,19 +1813,40 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
     RowBatch b{};
     b.count = count;
     b.nt_store = streamed_codes(total_rows * cols);
+    // with column amax: a few workgroups per CU in all (colmax_shape), dealt to
+    // the tensors in proportion to their rows (each striding over its rows)
+    const ColmaxShape shape = colmax_shape((cols / 8 + 63) / 64);
+    const int64_t waves = shape.waves;
+    const int64_t target = (int64_t)current_device_props().cus * shape.wg_per_cu;
     int64_t blocks = 0;
     for (int j = 0; j < count; ++j) {
         b.x[j] = x[j];
         b.q[j] = q[j];
         b.scale_inv[j] = scale_inv[j];
         b.amax[j] = amax_out ? amax_out[j] : nullptr;
+        b.col_amax[j] = any_col ? col_amax[j] : nullptr;
         b.rows[j] = rows[j];
         b.ldx[j] = ldx[j];
         b.ldq[j] = ldq[j];
         b.first[j] = blocks;
-        blocks += (rows[j] + kWaves - 1) / kWaves;
+        const int64_t need = (rows[j] + (any_col ? waves : kWaves) - 1) / (any_col ? waves : kWaves);
+        if (any_col) {
+            int64_t share = total_rows > 0 ? (target * rows[j] + total_rows - 1) / total_rows : 0;
+            share = share < 1 ? 1 : share;
+            blocks += need < share ? need : share;
+        } else {
+            blocks += need;
+        }
     }
     for (int j = count; j <= kMaxRowBatch; ++j) b.first[j] = blocks;
+    if (any_col) {
+        switch (fmt) {
+            case kE4M3: return quant_row_colmax_fmt<kE4M3>(b, blocks, cols, margin, st);
+            case kE5M2: return quant_row_colmax_fmt<kE5M2>(b, blocks, cols, margin, st);
+            case kE4M3Fnuz: return quant_row_colmax_fmt<kE4M3Fnuz>(b, blocks, cols, margin, st);
+            default: return quant_row_colmax_fmt<kE5M2Fnuz>(b, blocks, cols, margin, st);
+        }
+    }
     if (blocks == 0) return hipSuccess;
     switch (fmt) {
         case kE4M3: return quant_row_batch_fmt<kE4M3>(b, blocks, cols, margin, st);

@@ -132,7 +132,10 @@ fp8_status_t fp8_quantize_tensor(const uint16_t* x, int64_t rows, int64_t cols, 
  * scale_inv_out[rows] (required); amax_out[rows] (optional, NULL to skip);
  * col_amax_out[cols] (optional): if given, it is overwritten with the
  * per-column amax of x, a side output for a later colwise quantization of the
- * same tensor (fp8_quantize_col with col_amax_ready = 1).
+ * same tensor (fp8_quantize_col with col_amax_ready = 1). On the vector path
+ * with cols <= 16384 the column amax comes from the same single pass over x
+ * (after a launch that clears col_amax_out); longer rows or other layouts
+ * take a second pass over x for it.
  * margin: 0..32. Vector path when x, q are 16/8-byte aligned and ldx, ldq,
  * cols are multiples of 8; any other layout takes a scalar path. */
 fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
@@ -144,20 +147,25 @@ fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int
  * of the FP8 path; a linear layer's activation [m x k] and weight [n x k]
  * share k). Tensor j (j < count) is x[j] (bf16 [rows[j] x cols], ldx[j]) with
  * codes q[j] (ldq[j]), scale_inv_out[j] [rows[j]] (required when rows[j] > 0)
- * and amax_out[j] [rows[j]] (amax_out itself, or any entry, may be NULL);
- * every result equals what fp8_quantize_row gives for that tensor alone (no
- * column-amax side output here). x, rows, ldx, q, ldq, scale_inv_out, amax_out
- * are HOST arrays of count entries (read during the call); the pointers in them
- * are device memory. count: 1..FP8_MAX_ROW_BATCH. All tensors share fmt and
- * margin. One launch when every tensor has the vector layout (x 16-byte and q
- * 8-byte aligned, ldx, ldq, cols multiples of 8) and cols <= 16384; otherwise
- * one launch per tensor. Errors: any tensor's argument error (as
- * fp8_quantize_row) fails the whole call before anything is enqueued. */
+ * amax_out[j] [rows[j]] and col_amax_out[j] [cols] (amax_out and col_amax_out
+ * themselves, or any of their entries, may be NULL); every result equals what
+ * fp8_quantize_row gives for that tensor alone, the column amax of a tensor
+ * included (e.g. a linear layer's X and W, whose column amax the backward's
+ * colwise casts of X^T and W^T then take as ready). x, rows, ldx, q, ldq,
+ * scale_inv_out, amax_out, col_amax_out are HOST arrays of count entries (read
+ * during the call); the pointers in them are device memory. count:
+ * 1..FP8_MAX_ROW_BATCH. All tensors share fmt and margin. One launch (two
+ * with column amax: the outputs are cleared first) when every tensor has the
+ * vector layout (x 16-byte and q 8-byte aligned, ldx, ldq, cols multiples of
+ * 8) and cols <= 16384; otherwise one launch per tensor, and a second pass
+ * over each tensor whose column amax is asked for. Errors: any tensor's
+ * argument error (as fp8_quantize_row) fails the whole call before anything
+ * is enqueued. */
 #define FP8_MAX_ROW_BATCH 8
 fp8_status_t fp8_quantize_row_batch(int32_t count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
                                     const int64_t* ldx, fp8_format_t fmt, int32_t margin, uint8_t* const* q,
                                     const int64_t* ldq, float* const* scale_inv_out, float* const* amax_out,
-                                    void* stream);
+                                    float* const* col_amax_out, void* stream);
 
 /* Delayed tensorwise quantization of several tensors that share cols in one
  * launch ([Flux] delayed recipe; a linear layer's X and W, each with its own

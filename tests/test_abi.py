@@ -187,8 +187,8 @@ def test_quantize_row_batch_rejects_bad_arguments(fp8):
     x, q, s = PP(FAKE, FAKE), PP(FAKE, FAKE), PP(FAKE, FAKE)
     rows, ld = P64(4, 8), P64(16, 16)
 
-    def call(count=2, x=x, rows=rows, cols=16, ldx=ld, fmt=0, margin=0, q=q, ldq=ld, s=s, a=None):
-        return _call(fp8, f, count, x, rows, cols, ldx, fmt, margin, q, ldq, s, a, None)
+    def call(count=2, x=x, rows=rows, cols=16, ldx=ld, fmt=0, margin=0, q=q, ldq=ld, s=s, a=None, ca=None):
+        return _call(fp8, f, count, x, rows, cols, ldx, fmt, margin, q, ldq, s, a, ca, None)
 
     st, msg = call(count=0)
     assert st == 1 and "count" in msg
@@ -201,6 +201,7 @@ def test_quantize_row_batch_rejects_bad_arguments(fp8):
     assert call(s=PP(FAKE, None))[0] == 1                         # tensor 1 has rows but no scale output
     assert call(x=PP(FAKE, ctypes.c_void_p(0x10001)))[0] == 2     # tensor 1 misaligned for bf16
     assert call(a=PP(None, ctypes.c_void_p(0x10002)))[0] == 2     # misaligned amax output
+    assert call(ca=PP(ctypes.c_void_p(0x10002), None))[0] == 2    # misaligned column-amax output
 
 
 def test_quantize_tensor_batch_rejects_bad_arguments(fp8):

@@ -408,9 +408,10 @@ def test_quantizers_deterministic(fp8):
 
 # ------------------------------------------------------------ batched rowwise --
 
-def gpu_row_batch(fp8, xbs, fmt, margin=0, ld_pad=0, amax_mask=None):
+def gpu_row_batch(fp8, xbs, fmt, margin=0, ld_pad=0, amax_mask=None, col_mask=None):
     """fp8_quantize_row_batch over the tensors xbs (numpy bf16 bits, same cols);
-    ld_pad > 0 pads the code rows (a layout that takes one launch per tensor)."""
+    ld_pad > 0 pads the code rows (a layout that takes one launch per tensor);
+    col_mask[j] asks for tensor j's column amax (then returned as a 4th list)."""
     cols = xbs[0].shape[1]
     xs = [dev_bf16(xb) for xb in xbs]
     views, bufs = [], []
@@ -421,16 +422,31 @@ def gpu_row_batch(fp8, xbs, fmt, margin=0, ld_pad=0, amax_mask=None):
     sis = [torch.full((max(xb.shape[0], 1),), -1.0, device="cuda:0") for xb in xbs]
     ams = [torch.full((max(xb.shape[0], 1),), -1.0, device="cuda:0") for xb in xbs]
     amax_outs = [a if (amax_mask is None or amax_mask[j]) else None for j, a in enumerate(ams)]
-    fp8.fp8_quantize_row_batch(xs, fmt, margin, views, sis, amax_outs)
+    cas = None
+    if col_mask is not None:
+        # one guard float after each column-amax output
+        cabufs = [torch.full((cols + 1,), -1.0, device="cuda:0") for _ in xbs]
+        cas = [b[:cols] if col_mask[j] else None for j, b in enumerate(cabufs)]
+    fp8.fp8_quantize_row_batch(xs, fmt, margin, views, sis, amax_outs, cas)
     torch.cuda.synchronize()
     for buf, org, rows in bufs:
         check_guard(buf, org, rows, cols)
-    return ([v.cpu().numpy() for v in views], [s.cpu().numpy()[:xb.shape[0]] for s, xb in zip(sis, xbs)],
-            [a.cpu().numpy()[:xb.shape[0]] for a, xb in zip(ams, xbs)])
+    out = ([v.cpu().numpy() for v in views], [s.cpu().numpy()[:xb.shape[0]] for s, xb in zip(sis, xbs)],
+           [a.cpu().numpy()[:xb.shape[0]] for a, xb in zip(ams, xbs)])
+    if col_mask is None:
+        return out
+    for b in cabufs:
+        assert b[cols].item() == -1.0, "write past the column-amax output"
+    return out + ([b.cpu().numpy()[:cols] for b in cabufs],)
 
 
-def check_row_batch(orc, xbs, fmt, margin, got, amax_mask=None):
-    qs, sis, ams = got
+def check_row_batch(orc, xbs, fmt, margin, got, amax_mask=None, col_mask=None):
+    qs, sis, ams = got[:3]
+    for j, xb in enumerate(xbs):
+        if col_mask is not None and col_mask[j]:
+            assert_f32_bits_equal(got[3][j], orc.amax(xb, orc.AXIS_COL), f"column amax of tensor {j} {xb.shape}")
+        elif col_mask is not None:
+            assert np.all(got[3][j] == -1.0), f"column amax of tensor {j} was written although not requested"
     for j, xb in enumerate(xbs):
         oq, osi, oam = orc.quantize_row(xb, fmt, margin)
         assert_codes_equal(qs[j], oq, f"codes of tensor {j} {xb.shape}")
@@ -465,6 +481,39 @@ def test_quantize_row_batch_linear_pair(fp8, orc, cols):
     check_row_batch(orc, xbs, 0, 0, got)
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_quantize_row_batch_col_amax_parity(fp8, orc, fmt):
+    """The column-amax side output in the same pass: ragged row counts, empty
+    tensors, a tensor that does not ask for it, special values (NaN and Inf
+    columns); codes, scales and row amax unchanged."""
+    cols = 136
+    sizes = [5, 0, 64, 1, 130, 3, 0, 257]
+    xbs = [rand_bf16(r, cols, seed=200 + j) for j, r in enumerate(sizes)]
+    xbs[4][7:11] = np.pad(special_rows(), ((0, 0), (0, cols - 16)))[:4]    # NaN in column 1, Inf in 0
+    xbs[4][20, 100] = 0x7FC1                             # a NaN in column 100
+    cmask = [True, True, True, False, True, True, True, True]
+    say("row batch col amax", NAMES[fmt], sizes, cols)
+    got = gpu_row_batch(fp8, xbs, fmt, 1, col_mask=cmask)
+    check_row_batch(orc, xbs, fmt, 1, got, col_mask=cmask)
+    assert np.isnan(got[3][4][1]) and np.isnan(got[3][4][100]) and np.isinf(got[3][4][0])
+
+
+@pytest.mark.parametrize("shape", [(3000, 8), (2500, 520), (5000, 4096), (2100, 8200), (2300, 14336),
+                                   (900, 16384)])
+def test_quantize_row_col_amax_row_lengths(fp8, orc, shape):
+    """Single tensors from one chunk per lane to the longest row held in
+    registers, with more rows than the grid's wavefronts (each wavefront
+    folds several rows into its running column max)."""
+    rows, cols = shape
+    xb = rand_bf16(rows, cols, seed=rows + cols)
+    say("row + col amax", shape)
+    q, si, am, ca = gpu_row(fp8, xb, 1, 0, col_amax=True)
+    oq, osi, oam = orc.quantize_row(xb, 1, 0)
+    assert_codes_equal(q, oq, "codes")
+    assert_f32_bits_equal(si, osi, "scale_inv")
+    assert_f32_bits_equal(ca, orc.amax(xb, orc.AXIS_COL), "col amax")
+
+
 @pytest.mark.parametrize("fmt", [0, 3])
 def test_quantize_row_batch_per_tensor_layouts(fp8, orc, fmt):
     """Padded code rows (ldq not a multiple of 8), rows longer than the register
@@ -476,6 +525,11 @@ def test_quantize_row_batch_per_tensor_layouts(fp8, orc, fmt):
     long = [rand_bf16(3, 16392, seed=2), rand_bf16(5, 16392, seed=3)]
     got = gpu_row_batch(fp8, long, fmt, 0)
     check_row_batch(orc, long, fmt, 0, got)
+    say("row batch fallback with col amax", NAMES[fmt])
+    got = gpu_row_batch(fp8, long, fmt, 0, col_mask=[True, False])
+    check_row_batch(orc, long, fmt, 0, got, col_mask=[True, False])
+    got = gpu_row_batch(fp8, xbs, fmt, 2, ld_pad=3, col_mask=[True, True])
+    check_row_batch(orc, xbs, fmt, 2, got, col_mask=[True, True])
 
 
 def test_quantize_row_batch_special_values(fp8, orc):
@@ -486,27 +540,34 @@ def test_quantize_row_batch_special_values(fp8, orc):
         check_row_batch(orc, xbs, fmt, 0, got)
 
 
-def test_quantize_row_batch_matches_single_calls_at_llama3_8b(fp8):
+def test_quantize_row_batch_matches_single_calls_at_llama3_8b(fp8, orc):
     """X [8192 x 4096] and W [14336 x 4096] of the Llama3-8B up-projection:
-    the batched launch gives the bytes of two fp8_quantize_row calls."""
+    the batched launch gives the bytes of two fp8_quantize_row calls, with and
+    without the column-amax side outputs (compared with the oracle's column
+    amax of both whole tensors)."""
     w = workloads.c2()
     say("row batch c2 full size")
     x, wt = dev_bf16(w["x"]), dev_bf16(w["w"])
     outs = []
-    for batched in (True, False):
+    for batched, colmax in ((True, False), (False, False), (True, True)):
         qx = torch.empty(x.shape, dtype=torch.uint8, device="cuda:0")
         qw = torch.empty(wt.shape, dtype=torch.uint8, device="cuda:0")
         sx = torch.empty(x.shape[0], device="cuda:0")
         sw = torch.empty(wt.shape[0], device="cuda:0")
+        cx = torch.full((x.shape[1],), -1.0, device="cuda:0")
+        cw = torch.full((wt.shape[1],), -1.0, device="cuda:0")
         if batched:
-            fp8.fp8_quantize_row_batch([x, wt], 0, 0, [qx, qw], [sx, sw])
+            fp8.fp8_quantize_row_batch([x, wt], 0, 0, [qx, qw], [sx, sw], None, [cx, cw] if colmax else None)
         else:
             fp8.fp8_quantize_row(x, 0, 0, qx, sx)
             fp8.fp8_quantize_row(wt, 0, 0, qw, sw)
         torch.cuda.synchronize()
         outs.append((qx, qw, sx, sw))
-    for a, b in zip(*outs):
-        assert torch.equal(a, b)
+    for ref in outs[1:]:
+        for a, b in zip(outs[0], ref):
+            assert torch.equal(a, b)
+    assert_f32_bits_equal(cx.cpu().numpy(), orc.amax(w["x"], orc.AXIS_COL), "X column amax")
+    assert_f32_bits_equal(cw.cpu().numpy(), orc.amax(w["w"], orc.AXIS_COL), "W column amax")
 
 
 # ---------------------------------------------------- batched delayed tensorwise --
