@@ -273,6 +273,24 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const uint8_t* gptr
                  : "s"(lds_base), "v"(gptr)
                  : "memory", "m0");
 }
+// The same load with the address split into a wave-uniform 64-bit base
+// (SGPRs) and the lane's 32-bit byte offset (the instruction's SGPR-base
+// form: one VGPR per lane instead of two). The base's halves go through
+// v_readfirstlane, whose result is a signed int: each half is zero-extended
+// before the two are joined (a sign-extended low half would set every bit of
+// the high half for an address whose bit 31 is set). The s_nop gives the five
+// wait states that a VMEM instruction reading an SGPR needs after a VALU
+// instruction (such as v_readfirstlane) wrote it; the compiler does not
+// account for the SGPR reads of an asm statement.
+__device__ __forceinline__ void lds_dma16_s(uint32_t lds_base, const uint8_t* base, uint32_t voff) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t hi = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint64_t lo = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"((hi << 32) | lo)
+                 : "memory", "m0");
+}
 // Same with 4 bytes per lane: lane l's dword lands at lds_base + 4 l.
 __device__ __forceinline__ void lds_dma4(uint32_t lds_base, const void* gptr) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
@@ -419,7 +437,7 @@ __device__ __forceinline__ int k128_frag(int f) { return f == 0 ? 0 : (f <= 4 ? 
 //   of xsa / xsb bytes), and step p+1's scales read into sx.
 // A step's MFMAs thus never wait for LDS reads issued after the barrier, and
 // the loads have a full step to land.
-template <int FA, int FB, int CUR, bool NEXT, bool LOADS, bool MX>
+template <int FA, int FB, int CUR, bool NEXT, bool LOADS, bool MX, bool SADDR = false>
 __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], v8i (&f0)[8], u32x4 (&sx)[2],
                                           const uint8_t* a, const uint32_t (&aoff)[8], const uint8_t* b,
                                           const uint32_t (&boff)[8], int64_t knext, const uint8_t* xa,
@@ -460,10 +478,17 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], v8i 
             h0[i] = k128_half<MX>(j < 4 ? na : nb, big_row(j), 0, i & 1);
         }
         if (LOADS) {
-            if (i < 8)
-                lds_dma16(dma_base + i * 1024, a + knext + aoff[i]);
-            else
-                lds_dma16(dma_base + k128::kOpBytes + (i - 8) * 1024, b + knext + boff[i - 8]);
+            if constexpr (SADDR) {
+                if (i < 8)
+                    lds_dma16_s(dma_base + i * 1024, a + knext, aoff[i]);
+                else
+                    lds_dma16_s(dma_base + k128::kOpBytes + (i - 8) * 1024, b + knext, boff[i - 8]);
+            } else {
+                if (i < 8)
+                    lds_dma16(dma_base + i * 1024, a + knext + aoff[i]);
+                else
+                    lds_dma16(dma_base + k128::kOpBytes + (i - 8) * 1024, b + knext + boff[i - 8]);
+            }
             if constexpr (MX) {
                 if (i == 3 || i == 11) {
                     const uint32_t xbase = __builtin_amdgcn_readfirstlane(
@@ -900,6 +925,241 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
     big_epilogue<OUT_F32>(smem, acc, dg, ldd, row0, m - row0, col0, n - col0, vec_out);
 }
 
+// Persistent dense kernel: at most one workgroup per CU; workgroup w computes
+// the tiles w, w + G, w + 2G, .. (G = gridDim.x, a multiple of 8 whenever a
+// workgroup has more than one tile, so each keeps its XCD in the XCD-aware
+// order). During a tile's last two K steps the stages are loaded with the next
+// tile's first two steps; the epilogue then stages its bf16 block through an
+// LDS area of its own (16 rows x 128 columns per wavefront at a time), so those
+// loads land while it runs and the next tile starts without a load's latency.
+// Every tile loads 256 whole rows of each operand: a tile at the bottom or
+// right edge is shifted back to end at row m (column n) and stores only the
+// rows and columns past the previous tile (with 16-byte stores only where its
+// first column keeps them aligned); with m (n) < 256 there is one tile row
+// (column) and its loads are clamped. The per-lane load offsets are then the
+// same for every tile.
+namespace persist {
+constexpr int kChunk = 4 * 1024;                     // one wavefront's 16 staged rows
+constexpr int kEpiOff = big::kSmem;                  // after the stages and the scale area
+constexpr int kSmem = big::kSmem + 4 * kChunk;       // 146 KB
+}  // namespace persist
+
+// Epilogue of the tile whose loaded rows start at row0 and columns at col0:
+// stores rows row0 + [row_lo, row_hi) and columns col0 + [col_lo, col_hi),
+// d = acc * sa_row * sb_col with the tile's 256 row and 256 column scales in
+// the scale area; the stages are untouched.
+template <bool OUT_F32>
+__device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4], void* __restrict__ d, int64_t ldd,
+                                               int64_t row0, int row_lo, int row_hi, int64_t col0, int col_lo,
+                                               int col_hi, int vec_out) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t wrow0 = row0 + wm * 128, wcol0 = col0 + wn * 128;
+    const int rlo = row_lo - wm * 128, rhi = row_hi - wm * 128;      // this wavefront's rows [rlo, rhi)
+    const int clo = col_lo - wn * 128, chi = col_hi - wn * 128;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
+    const float* s_rows = reinterpret_cast<const float*>(smem + big::kScaleOff);
+    const float* s_cols = s_rows + 256;
+    float sbj[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) sbj[ni] = s_cols[wn * 128 + ni * 32 + (lane & 31)];
+    if (OUT_F32) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (lr < rlo || lr >= rhi) continue;
+                const float sai = s_rows[wm * 128 + lr];
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int lc = ni * 32 + (lane & 31);
+                    if (lc < clo || lc >= chi) continue;
+                    reinterpret_cast<float*>(d)[(wrow0 + lr) * ldd + wcol0 + lc] = acc[mi][ni][r] * sai * sbj[ni];
+                }
+            }
+        return;
+    }
+    uint8_t* ep = smem + persist::kEpiOff + wave * persist::kChunk;
+    const int cc = lane & 15;
+    const bool full_cols = vec_out && 8 * cc >= clo && 8 * cc + 8 <= chi;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // row groups 8 mi + 4 h .. + 3 (16 rows): groups 2 qq + lane / 32 of the chunk
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const int q = 2 * h + qq;
+                const int g = 8 * mi + 2 * q + (lane >> 5);
+                const u32x4 s4 = *reinterpret_cast<const u32x4*>(&s_rows[wm * 128 + 4 * g]);
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int r = 4 * q;
+                    v2f v01 = {acc[mi][ni][r] * __uint_as_float(s4[0]) * sbj[ni],
+                               acc[mi][ni][r + 1] * __uint_as_float(s4[1]) * sbj[ni]};
+                    v2f v23 = {acc[mi][ni][r + 2] * __uint_as_float(s4[2]) * sbj[ni],
+                               acc[mi][ni][r + 3] * __uint_as_float(s4[3]) * sbj[ni]};
+                    uint2 w;
+                    w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, v2bf));
+                    w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, v2bf));
+                    *reinterpret_cast<uint2*>(ep + epi_off(2 * qq + (lane >> 5), 32 * ni + (lane & 31))) = w;
+                }
+            }
+            wait_vmcnt<63, 0>();                         // this wavefront's chunk writes are done
+            __builtin_amdgcn_wave_barrier();
+            const int gl = lane >> 4;
+            const int g = 8 * mi + 4 * h + gl;
+            u32x4 un[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) un[k] = *reinterpret_cast<const u32x4*>(ep + epi_off(gl, 8 * cc + 2 * k));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int lr = 4 * g + r;
+                if (lr < rlo || lr >= rhi) continue;
+                const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
+                const int wlo = (r >> 1), whi = 2 + (r >> 1);
+                u32x4 row;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) row[k] = __builtin_amdgcn_perm(un[k][whi], un[k][wlo], sel);
+                uint16_t* dst = reinterpret_cast<uint16_t*>(d) + (wrow0 + lr) * ldd + wcol0 + 8 * cc;
+                if (full_cols) {
+                    __builtin_nontemporal_store(row, reinterpret_cast<u32x4*>(dst));
+                } else {
+                    for (int e = 0; e < 8; ++e)
+                        if (8 * cc + e >= clo && 8 * cc + e < chi) dst[e] = (uint16_t)(row[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
+}
+
+// big_tile_coords in 32-bit arithmetic (tile counts below 2^31), its divisors
+// made opaque at each call so that the divisions' setup is not kept live
+// across the K loop.
+__device__ __forceinline__ void tile_coords32(uint32_t bid, uint32_t tiles_m, uint32_t tiles_n, int64_t* pm,
+                                              int64_t* pn) {
+    asm volatile("" : "+s"(tiles_m), "+s"(tiles_n));
+    const uint32_t nt = tiles_m * tiles_n;
+    const uint32_t q = nt / 8, rem = nt % 8;
+    const uint32_t xcd = bid % 8, idx = bid / 8;
+    const uint32_t t = xcd * q + (xcd < rem ? xcd : rem) + idx;
+    constexpr uint32_t gm = 4;
+    const uint32_t span = gm * tiles_n;
+    const uint32_t first_m = t / span * gm;
+    const uint32_t gsize = tiles_m - first_m < gm ? tiles_m - first_m : gm;
+    const uint32_t u = t % span;
+    *pm = first_m + u % gsize;
+    *pn = u / gsize;
+}
+
+template <int FA, int FB, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restrict__ a, int64_t lda,
+                                                         const uint8_t* __restrict__ b, int64_t ldb, int64_t m,
+                                                         int64_t n, int64_t k, const float* __restrict__ sa,
+                                                         int sa_vec, const float* __restrict__ sb, int sb_vec,
+                                                         void* __restrict__ d, int64_t ldd, int vec_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[persist::kSmem];
+    const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
+    const int64_t nt = tiles_m * tiles_n, G = gridDim.x;
+    const int t = threadIdx.x;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nk = k / k128::BK;                     // even, >= 2
+    // tile (pm, pn): rows loaded from lrow(pm), columns from lcol(pn)
+    auto lrow = [&](int64_t pm) {
+        const int64_t r = pm * big::BM;
+        return (r + big::BM > m && m >= big::BM) ? m - big::BM : r;
+    };
+    auto lcol = [&](int64_t pn) {
+        const int64_t c = pn * big::BN;
+        return (c + big::BN > n && n >= big::BN) ? n - big::BN : c;
+    };
+    uint32_t aoff[8], boff[8];
+    k128_lane_offsets(aoff, lda, m);
+    k128_lane_offsets(boff, ldb, n);
+    int64_t id = blockIdx.x;                             // < nt (grid <= nt)
+    int64_t pm, pn;
+    tile_coords32((uint32_t)id, (uint32_t)tiles_m, (uint32_t)tiles_n, &pm, &pn);
+    int64_t row0 = lrow(pm), col0 = lcol(pn);
+    int row_lo = (int)(pm * big::BM - row0), col_lo = (int)(pn * big::BN - col0);
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kScaleOff)) + wave * 256;
+    auto issue_scales = [&](int64_t r0, int64_t c0) {
+        lds_dma4(sbase, sa + (sa_vec ? (r0 + t < m ? r0 + t : m - 1) : 0));
+        lds_dma4(sbase + 1024, sb + (sb_vec ? (c0 + t < n ? c0 + t : n - 1) : 0));
+    };
+    const uint8_t* at = a + row0 * lda;
+    const uint8_t* bt = b + col0 * ldb;
+    issue_scales(row0, col0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem + s * k128::kStage)) + wave * 8192;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma16_s(base + i * 1024, at + s * k128::BK, aoff[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma16_s(base + k128::kOpBytes + i * 1024, bt + s * k128::BK, boff[i]);
+    }
+    wait_vmcnt<16>();                                    // the scales and step 0 landed
+    v16f acc[4][4];
+    v8i f0[8];
+    u32x4 sx[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    __syncthreads();                                     // step 0 (all threads' loads) is in LDS
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        const int j = k128_frag(f);
+        f0[j] = big_join(k128_half<false>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 0),
+                         k128_half<false>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 1));
+    }
+    for (;;) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+        const int64_t nid = id + G;
+        const int64_t crow0 = row0, ccol0 = col0;
+        const int crow_lo = row_lo, ccol_lo = col_lo;
+        const uint8_t* nat = at;                         // with no next tile: this tile's own first
+        const uint8_t* nbt = bt;                         // steps (valid addresses, never used)
+        if (nid < nt) {
+            tile_coords32((uint32_t)nid, (uint32_t)tiles_m, (uint32_t)tiles_n, &pm, &pn);
+            row0 = lrow(pm);
+            col0 = lcol(pn);
+            row_lo = (int)(pm * big::BM - row0);
+            col_lo = (int)(pn * big::BN - col0);
+            nat = a + row0 * lda;
+            nbt = b + col0 * ldb;
+        }
+        // steps p, p+1 load steps p+2, p+3; the last pair loads the next tile's
+        // steps 0 and 1, and its second step reads the next tile's first fragments
+        for (int64_t p = 0; p < nk; p += 2) {
+            const bool last = p + 2 >= nk;
+            const uint8_t* la = last ? nat : at;
+            const uint8_t* lb = last ? nbt : bt;
+            const int64_t kl = last ? 0 : (p + 2) * k128::BK;
+            k128_step<FA, FB, 0, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl, nullptr, nullptr, 0,
+                                                          0);
+            k128_step<FA, FB, 1, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl + k128::BK, nullptr,
+                                                    nullptr, 0, 0);
+        }
+        at = nat;
+        bt = nbt;
+        const int64_t rhi = m - crow0, chi = n - ccol0;
+        chunk_epilogue<OUT_F32>(smem, acc, d, ldd, crow0, crow_lo, (int)(rhi < 256 ? rhi : 256), ccol0, ccol_lo,
+                                (int)(chi < 256 ? chi : 256), vec_out && ccol0 % 8 == 0);
+        if (nid >= nt) break;
+        id = nid;
+        __syncthreads();                                 // every wavefront is done with the scale area
+        issue_scales(row0, col0);                        // (landed by the next tile's first mid-step wait)
+    }
+    wait_vmcnt<0>();
+}
+
 template <int FA, int FB, bool OUT_F32>
 hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m, int64_t n, int64_t k,
                       const float* sa, int sa_vec, const float* sb, int sb_vec, void* d, int64_t ldd,
@@ -909,6 +1169,16 @@ hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t l
     const int64_t big_tiles = ((m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
     if (k > 0 && k % 256 == 0 && big_tiles >= 128 && lda < (1 << 24) && ldb < (1 << 24)) {
         const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
+        const int64_t cus = current_device_props().cus;
+        // more tiles than CUs, bf16 output: the persistent kernel (its fp32
+        // epilogue would spill, and with one tile per workgroup it gains nothing)
+        if constexpr (!OUT_F32) {
+            if (big_tiles > cus && cus >= 8 && big_tiles < ((int64_t)1 << 31)) {
+                hipLaunchKernelGGL((k_gemm_persist<FA, FB, false>), dim3((unsigned)(cus / 8 * 8)), dim3(256), 0, st, a,
+                                   lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out);
+                return hipGetLastError();
+            }
+        }
         hipLaunchKernelGGL((k_gemm_big<FA, FB, OUT_F32>), dim3((unsigned)big_tiles), dim3(256), 0, st, a, lda, b, ldb,
                            m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out);
         return hipGetLastError();

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import workloads
-from helpers import check_guard, dev_f32, dev_u8, guarded, say
+from helpers import check_full, check_guard, dev_f32, dev_u8, guarded, say
 
 pytestmark = pytest.mark.gpu
 
@@ -174,9 +174,11 @@ def test_grouped_gemm_parity(fp8, orc, sizes, fa, fb):
 LARGE = [((2100, 4100, 256), 0, 0, False, 4104), ((4096, 2048, 512), 1, 0, False, 2048),
          ((1024, 8192, 768), 0, 1, True, 8200), ((2304, 3100, 256), 1, 1, False, 3107),
          ((2304, 3100, 256), 0, 0, False, 3104), ((4096, 2048, 384), 1, 0, False, 2048),
-         # more tiles than CUs (bf16 out: persistent workgroups with several tiles each):
-         # edge tiles shifted back (n - 256 off the 8-column grid), m below one tile
-         # (clamped rows), an output stride off the 8-element grid
+         # more tiles than CUs with bf16 output (the persistent kernel: a workgroup
+         # per CU walks several tiles, loading the next tile's first K steps during
+         # the current tile's last ones): edge tiles shifted back to end at m / n
+         # (n - 256 off the 8-column grid), m below one tile (clamped rows), an
+         # output stride off the 8-element grid
          ((4100, 4500, 256), 0, 0, False, 4504), ((200, 65800, 256), 1, 0, False, 65800),
          ((2600, 7000, 512), 0, 0, False, 7003)]
 
@@ -194,6 +196,21 @@ def test_gemm_parity_large_tiles(fp8, orc, shape, fa, fb, out_f32, ldd):
     y, bound = orc.gemm(a, fa, b, fb, sa, sb)
     got = gpu_gemm(fp8, a, fa, b, fb, sa, sb, 1, 1, out_f32=out_f32, ldd=ldd)
     assert_within(orc, got, y, bound, not out_f32, f"large {shape}")
+
+
+@pytest.mark.parametrize("fa,fb", [(1, 0), (0, 0)])
+def test_gemm_full_output_long_k(fp8, orc, fa, fb):
+    """K = 14336 (the Llama3-8B backward's dgrad contraction) on 17 x 16 tiles of
+    256 x 256 (the persistent kernel, ragged last row of tiles): every output
+    against the oracle's whole product, with per-row scales spread over 2^-4 .. 2^4."""
+    m, n, k = 4300, 4096, 14336
+    a, sa = operands(orc, m, k, fa, seed=31)
+    b, sb = operands(orc, n, k, fb, seed=32)
+    say("gemm long k", (m, n, k), fa, fb)
+    d = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+    fp8.fp8_gemm_scaled(dev_u8(a), fa, dev_u8(b), fb, dev_f32(sa), 1, dev_f32(sb), 1, d)
+    torch.cuda.synchronize()
+    check_full(orc, d, orc.gemm_by_rows(a, fa, b, fb, sa, sb), f"long k {(m, n, k)}")
 
 
 def random_codes(rng, shape, fmt):
@@ -226,7 +243,7 @@ def test_grouped_gemm_parity_large_tiles(fp8, orc, sizes, n, k, fa, fb, out_f32)
     tiles of 256 x 256 estimated from the total row count): empty groups, a
     one-row group, groups spanning several m-tiles, more groups than threads of
     a workgroup (the per-group tile counts are summed in parallel), ragged n,
-    and k >= 4096 (the 64-deep K loop; shorter k runs the 128-deep one)."""
+    and a long contraction (k = 4096)."""
     g = len(sizes)
     offsets = np.zeros(g + 1, np.int64)
     offsets[1:] = np.cumsum(sizes)
