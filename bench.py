@@ -449,6 +449,18 @@ def copy_calibration(args):
                       "steps": args.steps}), flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(sample, target_s, kind="rowwise"):
     """The CPU oracle on a bounded sample of the workload's own tensors: the
     first ms rows of the activation and the first ns rows of the weight
@@ -493,7 +505,7 @@ def cpu_baseline(sample, target_s, kind="rowwise"):
         ms = int(min(act.shape[0], ms * target_s / t))
         t = run(ms, ns)
     return {"value": round(2.0 * ms * ns * k / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{ms} activation rows x {ns} weight rows x K={k} of the workload's tensors: "
                       f"{ {'mx': 'MX block-32', 'blockwise': 'blockwise', 'tensor': 'tensorwise'}.get(kind, 'rowwise') } quantize of both "
                       f"(oracle) + fp64 "
@@ -530,7 +542,7 @@ def cpu_baseline_moe(w, target_s):
         ts = int(min(x.shape[0], ts * target_s / t))
         t = run(ts)
     return {"value": round(6.0 * ts * k * H * inter / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"the layer forward on the first {ts} tokens (x{k} expert entries) with all {nexp} experts' "
                       f"weights quantized, oracle steps incl. fp64 grouped products, {t:.1f} s on {threads} threads"}
 

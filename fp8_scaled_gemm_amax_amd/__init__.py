@@ -75,7 +75,7 @@ def _load():
         "fp8_quantize_row": [P, I64, I64, I64, I, I32, P, I64, P, P, P, P],
         "fp8_quantize_row_batch": [I32, P, P, I64, P, I, I32, P, P, P, P, P, P],
         "fp8_quantize_tensor_batch": [I32, P, P, I64, P, I, P, P, P, P, P, P],
-        "fp8_quantize_col": [P, I64, I64, I64, I, I32, P, I64, P, P, I32, P],
+        "fp8_quantize_col": [P, I64, I64, I64, I, I32, I32, P, I64, P, P, I32, P],
         "fp8_delayed_scale_update": [P, P, P, I64, I32, I, I32, I, P, P, P],
         "fp8_gemm_scaled": [P, I, I64, P, I, I64, I64, I64, I64, P, I, P, I, P, I, I64, P],
         "fp8_grouped_gemm_scaled": [P, I, I64, P, I, I64, I64, P, I32, I64, I64, I64, P, P, P, I, I64, P],
@@ -215,11 +215,12 @@ def fp8_quantize_tensor_batch(xs, fmt, scales, qs, scale_inv_outs, amax_outs):
         PP(*[_ptr(t) for t in scale_inv_outs]), PP(*[_ptr(t) for t in amax_outs]), _stream(xs[0])))
 
 
-def fp8_quantize_col(x, fmt, margin, qt, scale_inv_out, col_amax, col_amax_ready=False):
+def fp8_quantize_col(x, fmt, margin, q, scale_inv_out, col_amax, col_amax_ready=False, transpose_out=True):
+    """Colwise scales; q is [cols x rows] (transpose_out) or [rows x cols]."""
     rows, cols, ldx = _bf16(x)
-    _, _, ldqt = _mat(qt, "qt", 1)
-    _check(lib.fp8_quantize_col(_ptr(x), rows, cols, ldx, fmt, margin, _ptr(qt), ldqt, _ptr(scale_inv_out),
-                                _ptr(col_amax), int(bool(col_amax_ready)), _stream(x)))
+    _, _, ldq = _mat(q, "q", 1)
+    _check(lib.fp8_quantize_col(_ptr(x), rows, cols, ldx, fmt, margin, int(bool(transpose_out)), _ptr(q), ldq,
+                                _ptr(scale_inv_out), _ptr(col_amax), int(bool(col_amax_ready)), _stream(x)))
 
 
 def fp8_delayed_scale_update(cur_amax, history, head, algo, margin, fmt, scale, scale_inv):

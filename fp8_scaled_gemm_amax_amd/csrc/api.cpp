@@ -296,11 +296,16 @@ fp8_status_t fp8_quantize_tensor_batch(int32_t count, const uint16_t* const* x, 
 }
 
 fp8_status_t fp8_quantize_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
-                              int32_t margin, uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* col_amax,
-                              int32_t col_amax_ready, void* stream) {
+                              int32_t margin, int32_t transpose_out, uint8_t* q, int64_t ldq, float* scale_inv_out,
+                              float* col_amax, int32_t col_amax_ready, void* stream) {
     const char* fn = "fp8_quantize_col";
     FP8_TRY(check_common_quant(fn, x, rows, cols, ldx, (int)fmt, margin));
-    FP8_TRY(check_matrix(fn, "qt", qt, cols, rows, ldqt));
+    if (transpose_out != 0 && transpose_out != 1)
+        return fail(FP8_ERR_INVALID_ARG, "%s: transpose_out must be 0 or 1", fn);
+    if (transpose_out)
+        FP8_TRY(check_matrix(fn, "q", q, cols, rows, ldq));
+    else
+        FP8_TRY(check_matrix(fn, "q", q, rows, cols, ldq));
     if (cols > 0 && (!scale_inv_out || !col_amax))
         return fail(FP8_ERR_INVALID_ARG, "%s: scale_inv_out and col_amax are required", fn);
     if (col_amax_ready != 0 && col_amax_ready != 1)
@@ -311,7 +316,8 @@ fp8_status_t fp8_quantize_col(const uint16_t* x, int64_t rows, int64_t cols, int
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     if (!col_amax_ready) e = launch_amax(x, rows, cols, ldx, FP8_AXIS_COL, col_amax, st);
-    if (e == hipSuccess) e = launch_quant_col(x, rows, cols, ldx, (int)fmt, margin, qt, ldqt, scale_inv_out, col_amax, st);
+    if (e == hipSuccess)
+        e = launch_quant_col(x, rows, cols, ldx, (int)fmt, margin, transpose_out, q, ldq, scale_inv_out, col_amax, st);
     return launched(e, fn);
 }
 

@@ -861,7 +861,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
 // dealt evenly to the 8 XCDs (slot w goes to XCD w % 8), contiguous within an
 // XCD, so groups of very different K_g keep the XCDs balanced; slots past a
 // group's tile count exit. Contraction columns at or past min(lda, ldb) are
-// never read.
+// never read: a group whose padded range reaches them writes NaN.
 template <int FA, int FB, bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
     const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb,
@@ -899,10 +899,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
     const int64_t P = wsum[0] + wsum[1] + wsum[2] + wsum[3];
     int64_t K = kpad(grp);
     const int64_t lim = lda < ldb ? lda : ldb;
-    if (P >= lim)
-        K = 0;
-    else if (P + K > lim)
-        K = (lim - P) / 256 * 256;
+    // a group whose padded range runs past the operands' width would lose real
+    // contraction columns: its outputs are made NaN instead of a short sum
+    const bool cut = K > 0 && P + K > lim;
+    if (cut) K = 0;
     const int64_t row0 = pm * big::BM, col0 = pn * big::BN;
     const float* sa_lane = sa + (int64_t)grp * m + (row0 + t < m ? row0 + t : m - 1);
     const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
@@ -910,13 +910,14 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
     if (K > 0) {
         k128_mainloop<FA, FB, false>(smem, a + row0 * lda + P, lda, m - row0, b + col0 * ldb + P, ldb, n - col0, K,
                                      sa_lane, sb_lane, nullptr, nullptr, 0, 0, acc);
-    } else {                                             // empty group: 0 * sa * sb
+    } else {                                             // empty group: 0 * sa * sb (cut: NaN)
+        const float fill = cut ? __builtin_nanf("") : 0.0f;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = fill;
         float* s_rows = reinterpret_cast<float*>(smem + big::kScaleOff);
         s_rows[t] = *sa_lane;
         s_rows[256 + t] = *sb_lane;

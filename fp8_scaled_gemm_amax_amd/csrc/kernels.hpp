@@ -32,8 +32,10 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
                                   float* const* scale_inv, float* const* amax_out, float* const* col_amax,
                                   hipStream_t st);
 
+// transpose: codes written transposed (qt [cols x rows]) or in x's layout (q [rows x cols]).
 hipError_t launch_quant_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
-                            uint8_t* qt, int64_t ldqt, float* scale_inv, const float* col_amax, hipStream_t st);
+                            int transpose, uint8_t* qt, int64_t ldqt, float* scale_inv, const float* col_amax,
+                            hipStream_t st);
 
 hipError_t launch_quant_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
                                const float* scale, uint8_t* q, int64_t ldq, float* scale_inv, float* amax,

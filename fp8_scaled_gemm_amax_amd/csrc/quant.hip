@@ -1389,14 +1389,52 @@ __global__ __launch_bounds__(kBlock) void k_quant_col_scalar(const uint16_t* __r
                                                              int64_t cols, int64_t ldx, int margin,
                                                              uint8_t* __restrict__ qt, int64_t ldqt,
                                                              float* __restrict__ scale_inv,
-                                                             const float* __restrict__ col_amax) {
+                                                             const float* __restrict__ col_amax, int transpose) {
     const int64_t col = (int64_t)blockIdx.y * kBlock + threadIdx.x;
     if (col >= cols) return;
     const float s = scale_from_amax<F>(col_amax[col], margin);
     if (blockIdx.x == 0) scale_inv[col] = 1.0f / s;
     const int64_t r0 = (int64_t)blockIdx.x * kColRows;
     const int64_t r1 = r0 + kColRows < rows ? r0 + kColRows : rows;
-    for (int64_t r = r0; r < r1; ++r) qt[col * ldqt + r] = (uint8_t)encode1<F>(bf16_lo(x[r * ldx + col]) * s);
+    for (int64_t r = r0; r < r1; ++r)
+        qt[transpose ? col * ldqt + r : r * ldqt + col] = (uint8_t)encode1<F>(bf16_lo(x[r * ldx + col]) * s);
+}
+
+// Colwise scales with the codes in x's own layout (q [rows x cols], no
+// transpose): lane l of a workgroup takes columns 8l .. 8l+7 of its 512-column
+// chunk (grid y), their scales formed once in registers, and wavefront w the
+// rows w, w + 4, .. of its 256-row band (grid x): 16-byte loads, 8-byte stores.
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_quant_col_rows(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                           int64_t ldx, int margin, uint8_t* __restrict__ q,
+                                                           int64_t ldq, float* __restrict__ scale_inv,
+                                                           const float* __restrict__ col_amax) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.y * 512 + lane * 8;
+    if (c0 >= cols) return;                              // (cols % 8 == 0: a lane's chunk is whole or absent)
+    float s[8];
+    int any_nan = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float a = col_amax[c0 + j];
+        s[j] = scale_from_amax<F>(a, margin);
+        any_nan |= __builtin_isnan(a) ? 1 : 0;
+        if (blockIdx.x == 0 && wave == 0) scale_inv[c0 + j] = 1.0f / s[j];
+    }
+    const int64_t r0 = (int64_t)blockIdx.x * kColRows;
+    const int64_t r1 = r0 + kColRows < rows ? r0 + kColRows : rows;
+    for (int64_t r = r0 + wave; r < r1; r += kWaves) {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + r * ldx + c0);
+        uint2 o;
+        if (!any_nan) {
+            o.x = encode4<F, true>(bf16_lo(v.x) * s[0], bf16_hi(v.x) * s[1], bf16_lo(v.y) * s[2], bf16_hi(v.y) * s[3]);
+            o.y = encode4<F, true>(bf16_lo(v.z) * s[4], bf16_hi(v.z) * s[5], bf16_lo(v.w) * s[6], bf16_hi(v.w) * s[7]);
+        } else {
+            o.x = encode4<F, false>(bf16_lo(v.x) * s[0], bf16_hi(v.x) * s[1], bf16_lo(v.y) * s[2], bf16_hi(v.y) * s[3]);
+            o.y = encode4<F, false>(bf16_lo(v.z) * s[4], bf16_hi(v.z) * s[5], bf16_lo(v.w) * s[6], bf16_hi(v.w) * s[7]);
+        }
+        *reinterpret_cast<uint2*>(q + r * ldq + c0) = o;
+    }
 }
 
 // ------------------------------------------------------ delayed scale update --
@@ -1522,9 +1560,21 @@ hipError_t quant_row_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
 }
 
 template <int F>
-hipError_t quant_col_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int margin, uint8_t* qt,
-                         int64_t ldqt, float* scale_inv, const float* col_amax, hipStream_t st) {
+hipError_t quant_col_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int margin, int transpose,
+                         uint8_t* qt, int64_t ldqt, float* scale_inv, const float* col_amax, hipStream_t st) {
     const bool vec_in = is_aligned(x, 16) && ldx % 8 == 0 && cols % 8 == 0;
+    if (!transpose) {
+        if (vec_in && is_aligned(qt, 8) && ldqt % 8 == 0) {
+            const dim3 grid((unsigned)((rows + kColRows - 1) / kColRows), (unsigned)((cols + 511) / 512));
+            hipLaunchKernelGGL((k_quant_col_rows<F>), grid, dim3(kBlock), 0, st, x, rows, cols, ldx, margin, qt, ldqt,
+                               scale_inv, col_amax);
+        } else {
+            const dim3 grid((unsigned)((rows + kColRows - 1) / kColRows), (unsigned)((cols + kBlock - 1) / kBlock));
+            hipLaunchKernelGGL((k_quant_col_scalar<F>), grid, dim3(kBlock), 0, st, x, rows, cols, ldx, margin, qt,
+                               ldqt, scale_inv, col_amax, 0);
+        }
+        return hipGetLastError();
+    }
     if (vec_in) {
         const int vec_store = is_aligned(qt, 16) && ldqt % 16 == 0;
         const dim3 grid((unsigned)((rows + kColTileR - 1) / kColTileR), (unsigned)((cols + kColTileC - 1) / kColTileC));
@@ -1533,7 +1583,7 @@ hipError_t quant_col_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
     } else {
         const dim3 grid((unsigned)((rows + kColRows - 1) / kColRows), (unsigned)((cols + kBlock - 1) / kBlock));
         hipLaunchKernelGGL((k_quant_col_scalar<F>), grid, dim3(kBlock), 0, st, x, rows, cols, ldx, margin, qt, ldqt,
-                           scale_inv, col_amax);
+                           scale_inv, col_amax, 1);
     }
     return hipGetLastError();
 }
@@ -1857,13 +1907,14 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
 }
 
 hipError_t launch_quant_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
-                            uint8_t* qt, int64_t ldqt, float* scale_inv, const float* col_amax, hipStream_t st) {
+                            int transpose, uint8_t* qt, int64_t ldqt, float* scale_inv, const float* col_amax,
+                            hipStream_t st) {
     if (cols == 0) return hipSuccess;
     if (rows == 0) {
         // no rows: every column has amax 0 (already in col_amax) -> scale 1
         return launch_fill(scale_inv, cols, 1.0f, st);
     }
-#define CALL(F) quant_col_fmt<F>(x, rows, cols, ldx, margin, qt, ldqt, scale_inv, col_amax, st)
+#define CALL(F) quant_col_fmt<F>(x, rows, cols, ldx, margin, transpose, qt, ldqt, scale_inv, col_amax, st)
     switch (fmt) {
         case kE4M3: return CALL(kE4M3);
         case kE5M2: return CALL(kE5M2);

@@ -184,18 +184,23 @@ fp8_status_t fp8_quantize_tensor_batch(int32_t count, const uint16_t* const* x, 
                                        uint8_t* const* q, const int64_t* ldq, float* const* scale_inv_out,
                                        float* const* amax_out, void* stream);
 
-/* Colwise quantization with transposed output ([Titan] colwise scales, whose
- * non-coalesced writes the post singles out). One scale per column of x
- * (reduction over the rows, e.g. over tokens), and the codes are written
- * transposed so that the next GEMM's contraction dimension is contiguous:
- * qt[j * ldqt + i] = cast(x[i * ldx + j] * s_j), qt is [cols x rows], ldqt >= rows.
+/* Colwise quantization ([Titan] colwise scales, whose non-coalesced writes
+ * the post singles out). One scale per column of x (reduction over the rows,
+ * e.g. over tokens).
+ *  - transpose_out = 1: the codes are written transposed so that the next
+ *    GEMM's contraction dimension is contiguous: q[j * ldq + i] =
+ *    cast(x[i * ldx + j] * s_j), q is [cols x rows], ldq >= rows (the layout
+ *    every GEMM operand of this library takes). The transpose goes through
+ *    LDS in tiles, so reads and writes are both coalesced.
+ *  - transpose_out = 0: the codes keep x's layout, q[i * ldq + j] =
+ *    cast(x[i * ldx + j] * s_j), q is [rows x cols], ldq >= cols.
  * col_amax[cols]: if col_amax_ready == 0 it is overwritten with the column
  * amax (computed by a first pass over x); if 1 it is read as already holding
  * it (from fp8_amax(FP8_AXIS_COL) or fp8_quantize_row's side output).
- * scale_inv_out[cols] (required). margin: 0..32. */
+ * scale_inv_out[cols] (required). margin: 0..32; transpose_out: 0 or 1. */
 fp8_status_t fp8_quantize_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
-                              int32_t margin, uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* col_amax,
-                              int32_t col_amax_ready, void* stream);
+                              int32_t margin, int32_t transpose_out, uint8_t* q, int64_t ldq, float* scale_inv_out,
+                              float* col_amax, int32_t col_amax_ready, void* stream);
 
 /* Fused end-of-step update of n delayed-scaling states ([Flux] "Configuration":
  * fp8_amax_history_len, fp8_amax_compute_algo, fp8_margin; [Flux] "Testing":
@@ -296,9 +301,13 @@ fp8_status_t fp8_grouped_quantize_col(const uint16_t* x, int64_t total_m, int64_
  * as fp8_grouped_quantize_col writes it). d_g = d + g * d_group_stride
  * (elements), [m x n] with row stride ldd; d_group_stride >= m * ldd. An
  * empty group writes 0 * sa * sb. Columns at or past min(lda, ldb) are never
- * read (lda, ldb >= P_G is needed for the whole result; >= total_m is
- * checked; lda, ldb < 2^24, else FP8_ERR_UNSUPPORTED). Formats and alignment
- * as fp8_gemm_scaled; g: 1..4096. */
+ * read: lda, ldb >= P_G is needed (total_m + g * (FP8_GROUP_K_ALIGN - 1)
+ * always suffices), and since P_G depends on the device offsets it is not
+ * checked on the host; a group whose padded range P_g + roundup(m_g,
+ * FP8_GROUP_K_ALIGN) runs past min(lda, ldb) writes NaN to its whole output
+ * instead of a sum that silently misses columns. Checked: lda, ldb >= total_m;
+ * lda, ldb < 2^24 (else FP8_ERR_UNSUPPORTED). Formats and alignment as
+ * fp8_gemm_scaled; g: 1..4096. */
 fp8_status_t fp8_grouped_gemm_ragged_k(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b,
                                        fp8_format_t fb, int64_t ldb, const int64_t* group_offsets, int32_t g,
                                        int64_t total_m, int64_t m, int64_t n, const float* a_scale_inv,

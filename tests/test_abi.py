@@ -174,9 +174,14 @@ def test_quantizers_reject_bad_arguments(fp8):
                  None)[0] == 2
     # tensorwise needs scale_inv_out and amax_out
     assert _call(fp8, "fp8_quantize_tensor", FAKE, 4, 16, 16, 0, 0, None, FAKE, 16, None, FAKE, None)[0] == 1
-    # colwise: transposed output needs ldqt >= rows; col_amax_ready must be 0/1
-    assert _call(fp8, "fp8_quantize_col", FAKE, 64, 16, 16, 0, 0, FAKE, 32, FAKE, FAKE, 0, None)[0] == 1
-    assert _call(fp8, "fp8_quantize_col", FAKE, 64, 16, 16, 0, 0, FAKE, 64, FAKE, FAKE, 2, None)[0] == 1
+    # colwise: transposed output needs ldq >= rows, untransposed ldq >= cols;
+    # col_amax_ready and transpose_out must be 0/1
+    assert _call(fp8, "fp8_quantize_col", FAKE, 64, 16, 16, 0, 0, 1, FAKE, 32, FAKE, FAKE, 0, None)[0] == 1
+    assert _call(fp8, "fp8_quantize_col", FAKE, 64, 16, 16, 0, 0, 1, FAKE, 64, FAKE, FAKE, 2, None)[0] == 1
+    st, msg = _call(fp8, "fp8_quantize_col", FAKE, 64, 16, 16, 0, 0, 0, FAKE, 8, FAKE, FAKE, 0, None)
+    assert st == 1 and "leading dimension" in msg
+    st, msg = _call(fp8, "fp8_quantize_col", FAKE, 64, 16, 16, 0, 0, 2, FAKE, 64, FAKE, FAKE, 0, None)
+    assert st == 1 and "transpose_out" in msg
     # amax: unknown axis
     assert _call(fp8, "fp8_amax", FAKE, 4, 16, 16, 3, FAKE, None)[0] == 1
 

@@ -172,6 +172,25 @@ def test_grouped_gemm_ragged_k_parity(fp8, orc, sizes, m, n, fa, fb, out_f32):
             assert not got[g].any(), f"empty group {g} is not zero"
 
 
+def test_grouped_gemm_ragged_k_short_operands_give_nan(fp8, orc):
+    """Operands narrower than the grouped layout (lda = ldb below P_G, still >=
+    total_m): the groups whose padded range fits are exact within the bound,
+    the group that would lose contraction columns writes NaN everywhere
+    instead of a short sum."""
+    sizes = [300, 10, 300]
+    offsets = offsets_of(sizes)                            # P = 0, 512, 768; P_G = 1280
+    m, n = 256, 264
+    a_t, sa, _ = orc.grouped_quantize_col(rand_bf16(610, m, 5), 1, offsets, ALIGN)
+    b_t, sb, _ = orc.grouped_quantize_col(rand_bf16(610, n, 6), 0, offsets, ALIGN)
+    assert a_t.shape[1] == 1280
+    y, bound = orc.grouped_gemm_ragged_k(a_t, 1, b_t, 0, offsets, ALIGN, sa, sb)
+    say("ragged k short operands")
+    got = gpu_ragged(fp8, np.ascontiguousarray(a_t[:, :1024]), 1, np.ascontiguousarray(b_t[:, :1024]), 0, offsets,
+                     sa, sb)
+    assert_within(orc, got[:2], y[:2], bound[:2], True, "groups that fit")
+    assert np.isnan(got[2]).all(), "the cut group is not NaN"
+
+
 def test_moe_layer_backward_composed(fp8, orc):
     """An expert layer's backward from bf16 tensors through the library only:
     dgrad dX_g = dY_g W_g (dY rowwise e5m2, W_g colwise over its rows by the

@@ -41,15 +41,16 @@ def gpu_row(fp8, xb, fmt, margin=0, ldq=None, col_amax=False):
     return q.cpu().numpy(), si.cpu().numpy(), am.cpu().numpy(), (ca.cpu().numpy() if col_amax else None)
 
 
-def gpu_col(fp8, xb, fmt, margin=0, ldqt=None, ready=None):
+def gpu_col(fp8, xb, fmt, margin=0, ldqt=None, ready=None, transpose=True):
     x = dev_bf16(xb)
     rows, cols = xb.shape
-    qt, qbuf, org = guarded(cols, rows, torch.uint8, ld=ldqt)
+    qr, qc = (cols, rows) if transpose else (rows, cols)
+    qt, qbuf, org = guarded(qr, qc, torch.uint8, ld=ldqt)
     si = torch.full((cols,), -1.0, device="cuda:0")
     ca = dev_f32(ready) if ready is not None else torch.full((cols,), -1.0, device="cuda:0")
-    fp8.fp8_quantize_col(x, fmt, margin, qt, si, ca, col_amax_ready=ready is not None)
+    fp8.fp8_quantize_col(x, fmt, margin, qt, si, ca, col_amax_ready=ready is not None, transpose_out=transpose)
     torch.cuda.synchronize()
-    check_guard(qbuf, org, cols, rows)
+    check_guard(qbuf, org, qr, qc)
     return qt.cpu().numpy(), si.cpu().numpy(), ca.cpu().numpy()
 
 
@@ -188,6 +189,26 @@ def test_quantize_row_col_amax_side_output(fp8, orc, shape):
 # -------------------------------------------------------------------- columns --
 
 COL_SHAPES = [(1, 8), (128, 64), (130, 72), (257, 136), (1000, 520), (64, 4104), (3, 48)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("shape", [(1, 8), (300, 520), (257, 1032), (70, 37), (5, 3)])
+def test_quantize_col_untransposed_parity(fp8, orc, fmt, shape):
+    """transpose_out = 0: column scales with the codes in x's own layout (the
+    oracle's transposed codes, transposed back), vector and scalar layouts,
+    a padded output stride, a NaN column and an all-zero column."""
+    rows, cols = shape
+    xb = rand_bf16(rows, cols, seed=rows * 3 + cols)
+    if rows > 2 and cols > 2:
+        xb[rows // 2, 1] = 0x7FC0
+        xb[:, 2] = 0
+    for ready in (False, True):
+        say("col untransposed", NAMES[fmt], shape, "ready", ready)
+        oqt, osi, oam = orc.quantize_col(xb, fmt, 1)
+        q, si, ca = gpu_col(fp8, xb, fmt, margin=1, ldqt=cols + 24, ready=oam if ready else None, transpose=False)
+        assert_codes_equal(q, np.ascontiguousarray(oqt.T), f"codes {shape}")
+        assert_f32_bits_equal(si, osi, "scale_inv")
+        assert_f32_bits_equal(ca, oam, "col amax")
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
