@@ -98,8 +98,11 @@ fp8_status_t check_common_quant(const char* fn, const uint16_t* x, int64_t rows,
     return FP8_OK;
 }
 
+// fnuz_ok: the product has the bf16 compatibility path for fnuz operands
+// (dense and grouped scaled GEMMs); the MX and ragged-K products take OCP only.
 fp8_status_t check_gemm_operands(const char* fn, const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb,
-                                 int64_t ldb, int64_t m, int64_t n, int64_t k, const void* d, int d_type, int64_t ldd) {
+                                 int64_t ldb, int64_t m, int64_t n, int64_t k, const void* d, int d_type, int64_t ldd,
+                                 bool fnuz_ok = false) {
     if (m < 0 || n < 0 || k < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative size m=%lld n=%lld k=%lld", fn,
                                              (long long)m, (long long)n, (long long)k);
     if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8_ERR_INVALID_ARG, "%s: unknown format (%d, %d)", fn, fa, fb);
@@ -114,9 +117,9 @@ fp8_status_t check_gemm_operands(const char* fn, const uint8_t* a, int fa, int64
     if (k > 0 && (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0))
         return fail(FP8_ERR_ALIGNMENT, "%s: a, b must be 16-byte aligned with lda, ldb multiples of 16", fn);
     if (!aligned(d, 4)) return fail(FP8_ERR_ALIGNMENT, "%s: d must be 4-byte aligned", fn);
-    if (!ocp_fmt(fa) || !ocp_fmt(fb))
+    if (!fnuz_ok && (!ocp_fmt(fa) || !ocp_fmt(fb)))
         return fail(FP8_ERR_UNSUPPORTED,
-                    "%s: fnuz operands (%d, %d): gfx950 matrix cores consume the OCP e4m3/e5m2 encodings", fn, fa, fb);
+                    "%s: fnuz operands (%d, %d): this product takes the OCP e4m3/e5m2 encodings only", fn, fa, fb);
     return FP8_OK;
 }
 
@@ -348,7 +351,7 @@ fp8_status_t fp8_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t lda, con
                              fp8_scale_mode_t a_mode, const float* b_scale_inv, fp8_scale_mode_t b_mode, void* d,
                              fp8_out_t d_type, int64_t ldd, void* stream) {
     const char* fn = "fp8_gemm_scaled";
-    FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, m, n, k, d, (int)d_type, ldd));
+    FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, m, n, k, d, (int)d_type, ldd, true));
     if ((a_mode != FP8_SCALE_TENSOR && a_mode != FP8_SCALE_VECTOR) ||
         (b_mode != FP8_SCALE_TENSOR && b_mode != FP8_SCALE_VECTOR))
         return fail(FP8_ERR_INVALID_ARG, "%s: unknown scale mode", fn);
@@ -356,6 +359,11 @@ fp8_status_t fp8_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t lda, con
     if (!aligned(a_scale_inv, 4) || !aligned(b_scale_inv, 4))
         return fail(FP8_ERR_ALIGNMENT, "%s: misaligned scale pointer", fn);
     FP8_TRY(check_device());
+    if (!ocp_fmt((int)fa) || !ocp_fmt((int)fb))
+        return launched(launch_gemm_compat(a, (int)fa, lda, b, (int)fb, ldb, m, n, k, a_scale_inv,
+                                           a_mode == FP8_SCALE_VECTOR, b_scale_inv, b_mode == FP8_SCALE_VECTOR, d,
+                                           d_type == FP8_OUT_F32, ldd, (hipStream_t)stream),
+                        fn);
     return launched(launch_gemm(a, (int)fa, lda, b, (int)fb, ldb, m, n, k, a_scale_inv, a_mode == FP8_SCALE_VECTOR,
                                 b_scale_inv, b_mode == FP8_SCALE_VECTOR, d, d_type == FP8_OUT_F32, ldd,
                                 (hipStream_t)stream),
@@ -368,7 +376,7 @@ fp8_status_t fp8_grouped_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t 
                                      const float* a_scale_inv, const float* b_scale_inv, void* d, fp8_out_t d_type,
                                      int64_t ldd, void* stream) {
     const char* fn = "fp8_grouped_gemm_scaled";
-    FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, total_m, n, k, d, (int)d_type, ldd));
+    FP8_TRY(check_gemm_operands(fn, a, (int)fa, lda, b, (int)fb, ldb, total_m, n, k, d, (int)d_type, ldd, true));
     if (g < 1 || g > 4096) return fail(FP8_ERR_INVALID_ARG, "%s: group count %d outside 1..4096", fn, g);
     if (!group_offsets) return fail(FP8_ERR_INVALID_ARG, "%s: group_offsets is NULL", fn);
     if (!aligned(group_offsets, 8)) return fail(FP8_ERR_ALIGNMENT, "%s: group_offsets must be 8-byte aligned", fn);
@@ -379,6 +387,11 @@ fp8_status_t fp8_grouped_gemm_scaled(const uint8_t* a, fp8_format_t fa, int64_t 
     if (!aligned(a_scale_inv, 4) || !aligned(b_scale_inv, 4))
         return fail(FP8_ERR_ALIGNMENT, "%s: misaligned scale pointer", fn);
     FP8_TRY(check_device());
+    if (!ocp_fmt((int)fa) || !ocp_fmt((int)fb))
+        return launched(launch_grouped_gemm_compat(a, (int)fa, lda, b, (int)fb, ldb, b_group_stride, group_offsets, g,
+                                                   total_m, n, k, a_scale_inv, b_scale_inv, d, d_type == FP8_OUT_F32,
+                                                   ldd, (hipStream_t)stream),
+                        fn);
     return launched(launch_grouped_gemm(a, (int)fa, lda, b, (int)fb, ldb, b_group_stride, group_offsets, g, total_m,
                                         n, k, a_scale_inv, b_scale_inv, d, d_type == FP8_OUT_F32, ldd,
                                         (hipStream_t)stream),

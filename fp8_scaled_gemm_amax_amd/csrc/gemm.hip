@@ -233,6 +233,164 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm(const uint8_t* __rest
 }
 
 // ---------------------------------------------------------------------------
+// Compatibility path for fnuz operands ("FP8 Training on MI300X": the fnuz
+// encodings e4m3fnuz / e5m2fnuz that MI300-generation parts consume; gfx950's
+// matrix cores take only the OCP encodings, and no fixed re-encoding maps
+// either fnuz format onto an OCP one: e4m3fnuz holds 2^-10 and, read as OCP
+// bits, 240 is a NaN code). Every FP8 value of any of the four encodings is
+// exactly a bf16 value (at most 4 significant bits, exponents within bf16's
+// normal range), so the operands are decoded to bf16 through a 256-entry table
+// in LDS and multiplied on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16):
+// each product of two decoded values is exact in fp32 and the sum is an fp32
+// accumulation, the arithmetic of the FP8 path. 128 x 128 tiles, 32-deep K
+// steps staged as bf16 in LDS; a correctness path, not tuned.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// bf16 bit pattern of FP8 code c in encoding F (NaN codes -> quiet NaN, OCP
+// e5m2 Inf -> Inf).
+template <int F>
+__device__ __forceinline__ uint32_t fp8_to_bf16_bits(uint32_t c) {
+    using T = FmtTraits<F>;
+    constexpr int mb = T::mbits, eb = 7 - mb;
+    const uint32_t sign = (c & 0x80u) << 8;
+    const uint32_t e = (c >> mb) & ((1u << eb) - 1u), m = c & ((1u << mb) - 1u);
+    if (T::fnuz) {
+        if (c == 0x80u) return 0x7fc0u;
+    } else if (F == kE4M3) {
+        if ((c & 0x7fu) == 0x7fu) return sign | 0x7fc0u;
+    } else {
+        if (e == 31u) return m == 0u ? (sign | 0x7f80u) : (sign | 0x7fc0u);
+    }
+    if (e == 0u) {
+        if (m == 0u) return sign;                        // zero (OCP keeps the sign)
+        const int p = 31 - __builtin_clz(m);             // leading one of the subnormal mantissa
+        const uint32_t exp = (uint32_t)(p + 1 - T::bias - mb + 127);
+        return sign | (exp << 7) | ((m - (1u << p)) << (7 - p));
+    }
+    return sign | ((e - (uint32_t)T::bias + 127u) << 7) | (m << (7 - mb));
+}
+
+template <int F>
+__device__ __forceinline__ void fill_bf16_table(uint16_t* lut) {
+    lut[threadIdx.x] = (uint16_t)fp8_to_bf16_bits<F>(threadIdx.x);    // (256 threads: one code each)
+}
+
+namespace compat {
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int kPitch = BK + 8;                           // bf16 per LDS row (80 bytes: spreads the fragment reads)
+}  // namespace compat
+
+// Loads 16 codes (row t / 2, K half t % 2 of the 32-deep step) of a 128-row
+// operand tile, decodes them through lut and stores them as bf16 in LDS.
+__device__ __forceinline__ void compat_stage(const uint8_t* base, int64_t ld, int64_t valid_rows, int64_t k0, int64_t k,
+                                             const uint16_t* lut, uint16_t* lds) {
+    const int t = threadIdx.x;
+    const int row = t >> 1, kh = (t & 1) * 16;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < valid_rows && k0 + kh < k)                 // (k % 16 == 0: a 16-code chunk is whole or absent)
+        v = *reinterpret_cast<const uint4*>(base + (int64_t)row * ld + k0 + kh);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t word = w[i >> 1] >> (16 * (i & 1));
+        o[i] = (uint32_t)lut[word & 0xffu] | ((uint32_t)lut[(word >> 8) & 0xffu] << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(lds + row * compat::kPitch + kh);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// One 128 x 128 tile of d = a * b^T with bf16-decoded operands: wavefront w owns
+// the 64 x 64 quarter (w / 2, w % 2) as 2 x 2 blocks of 32 x 32.
+template <int FA, int FB>
+__device__ __forceinline__ void compat_tile(const uint8_t* a, int64_t lda, int64_t a_rows, const uint8_t* b,
+                                            int64_t ldb, int64_t b_rows, int64_t k, v16f (&acc)[2][2]) {
+    __shared__ uint16_t lut_a[256], lut_b[256];
+    __shared__ __attribute__((aligned(16))) uint16_t As[compat::BM * compat::kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[compat::BN * compat::kPitch];
+    fill_bf16_table<FA>(lut_a);
+    fill_bf16_table<FB>(lut_b);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+    for (int64_t k0 = 0; k0 < k; k0 += compat::BK) {
+        __syncthreads();                                 // the tables are written; the previous step's reads are done
+        compat_stage(a, lda, a_rows, k0, k, lut_a, As);
+        compat_stage(b, ldb, b_rows, k0, k, lut_b, Bs);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            // lane l: row l % 32 of its block, 8 consecutive K of the 16-deep slice kk
+            // (the same map for a and b, so equal K indices are paired)
+            const int kc = kk * 16 + (lane >> 5) * 8;
+            v8bf fa[2], fb[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                fa[mi] = *reinterpret_cast<const v8bf*>(As + (wm * 64 + mi * 32 + (lane & 31)) * compat::kPitch + kc);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                fb[ni] = *reinterpret_cast<const v8bf*>(Bs + (wn * 64 + ni * 32 + (lane & 31)) * compat::kPitch + kc);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+        }
+    }
+}
+
+template <int FA, int FB, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void k_gemm_compat(const uint8_t* __restrict__ a, int64_t lda,
+                                                          const uint8_t* __restrict__ b, int64_t ldb, int64_t m,
+                                                          int64_t n, int64_t k, const float* __restrict__ sa,
+                                                          int sa_vec, const float* __restrict__ sb, int sb_vec,
+                                                          void* __restrict__ d, int64_t ldd) {
+    const int64_t tiles_n = (n + compat::BN - 1) / compat::BN;
+    const int64_t row0 = (int64_t)(blockIdx.x / tiles_n) * compat::BM, col0 = (int64_t)(blockIdx.x % tiles_n) * compat::BN;
+    v16f acc[2][2];
+    compat_tile<FA, FB>(a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, acc);
+    store_tile_out<OUT_F32>(acc, d, ldd, row0, m - row0, col0, n - col0, sa, sa_vec, sb, sb_vec);
+}
+
+// Grouped form: the linear workgroup index enumerates each group's (m-tile,
+// n-tile) pairs group after group (as k_grouped_gemm).
+template <int FA, int FB, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void k_grouped_gemm_compat(
+    const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb, int64_t b_group_stride,
+    const int64_t* __restrict__ offsets, int g, int64_t total_m, int64_t n, int64_t k, const float* __restrict__ sa,
+    const float* __restrict__ sb, void* __restrict__ d, int64_t ldd) {
+    const int64_t tiles_n = (n + compat::BN - 1) / compat::BN;
+    int64_t pid = blockIdx.x;
+    int grp = -1;
+    int64_t lo = 0, hi = 0;
+    for (int e = 0; e < g; ++e) {
+        int64_t s0 = offsets[e], s1 = offsets[e + 1];
+        s0 = s0 < 0 ? 0 : (s0 > total_m ? total_m : s0);
+        s1 = s1 < s0 ? s0 : (s1 > total_m ? total_m : s1);
+        const int64_t tiles = ((s1 - s0 + compat::BM - 1) / compat::BM) * tiles_n;
+        if (pid < tiles) {
+            grp = e;
+            lo = s0;
+            hi = s1;
+            break;
+        }
+        pid -= tiles;
+    }
+    if (grp < 0) return;
+    const int64_t row0 = lo + (pid / tiles_n) * compat::BM, col0 = (pid % tiles_n) * compat::BN;
+    const uint8_t* bg = b + (int64_t)grp * b_group_stride;
+    v16f acc[2][2];
+    compat_tile<FA, FB>(a + row0 * lda, lda, hi - row0, bg + col0 * ldb, ldb, n - col0, k, acc);
+    store_tile_out<OUT_F32>(acc, d, ldd, row0, hi - row0, col0, n - col0, sa, 1, sb + (int64_t)grp * n, 1);
+}
+
+// ---------------------------------------------------------------------------
 // Large-tile kernels: 256 x 256 output tile per workgroup, one 128 x 128
 // quadrant per wavefront (4 x 4 blocks of 32x32x64, 256 fp32 accumulators per
 // lane in AGPRs). The K loop (k128_mainloop below) streams the operands through
@@ -1300,6 +1458,74 @@ hipError_t launch_grouped_gemm_mx(const uint8_t* a, int fa, int64_t lda, const u
 #undef BY_OUT
 #undef CALL
 }
+
+// fnuz operands (any pair with at least one fnuz format): the bf16 compatibility kernels.
+template <int FA, int FB, bool OUT_F32>
+hipError_t compat_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                        const float* sa, int sa_vec, const float* sb, int sb_vec, void* d, int64_t ldd,
+                        hipStream_t st) {
+    const int64_t tiles = ((m + compat::BM - 1) / compat::BM) * ((n + compat::BN - 1) / compat::BN);
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_gemm_compat<FA, FB, OUT_F32>), dim3((unsigned)tiles), dim3(kThreads), 0, st, a, lda, b, ldb,
+                       m, n, k, sa, sa_vec, sb, sb_vec, d, ldd);
+    return hipGetLastError();
+}
+
+template <int FA, int FB, bool OUT_F32>
+hipError_t grouped_compat_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t stride,
+                                const int64_t* offsets, int g, int64_t total_m, int64_t n, int64_t k, const float* sa,
+                                const float* sb, void* d, int64_t ldd, hipStream_t st) {
+    if (total_m == 0 || n == 0) return hipSuccess;
+    const int64_t tiles = ((total_m + compat::BM - 1) / compat::BM + g) * ((n + compat::BN - 1) / compat::BN);
+    hipLaunchKernelGGL((k_grouped_gemm_compat<FA, FB, OUT_F32>), dim3((unsigned)tiles), dim3(kThreads), 0, st, a, lda,
+                       b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd);
+    return hipGetLastError();
+}
+
+// Dispatch over the 16 format pairs of the compatibility kernels.
+#define FP8_COMPAT_PAIRS(CALL)                                  \
+    switch (fa * 4 + fb) {                                      \
+        case 0: return CALL(kE4M3, kE4M3);                      \
+        case 1: return CALL(kE4M3, kE5M2);                      \
+        case 2: return CALL(kE4M3, kE4M3Fnuz);                  \
+        case 3: return CALL(kE4M3, kE5M2Fnuz);                  \
+        case 4: return CALL(kE5M2, kE4M3);                      \
+        case 5: return CALL(kE5M2, kE5M2);                      \
+        case 6: return CALL(kE5M2, kE4M3Fnuz);                  \
+        case 7: return CALL(kE5M2, kE5M2Fnuz);                  \
+        case 8: return CALL(kE4M3Fnuz, kE4M3);                  \
+        case 9: return CALL(kE4M3Fnuz, kE5M2);                  \
+        case 10: return CALL(kE4M3Fnuz, kE4M3Fnuz);             \
+        case 11: return CALL(kE4M3Fnuz, kE5M2Fnuz);             \
+        case 12: return CALL(kE5M2Fnuz, kE4M3);                 \
+        case 13: return CALL(kE5M2Fnuz, kE5M2);                 \
+        case 14: return CALL(kE5M2Fnuz, kE4M3Fnuz);             \
+        default: return CALL(kE5M2Fnuz, kE5M2Fnuz);             \
+    }
+
+hipError_t launch_gemm_compat(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb, int64_t m,
+                              int64_t n, int64_t k, const float* sa, int sa_vec, const float* sb, int sb_vec, void* d,
+                              int out_f32, int64_t ldd, hipStream_t st) {
+#define CALL(FA, FB)                                                                                            \
+    (out_f32 ? compat_typed<FA, FB, true>(a, lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, st)         \
+             : compat_typed<FA, FB, false>(a, lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, st))
+    FP8_COMPAT_PAIRS(CALL)
+#undef CALL
+}
+
+hipError_t launch_grouped_gemm_compat(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb,
+                                      int64_t b_group_stride, const int64_t* offsets, int g, int64_t total_m,
+                                      int64_t n, int64_t k, const float* sa, const float* sb, void* d, int out_f32,
+                                      int64_t ldd, hipStream_t st) {
+#define CALL(FA, FB)                                                                                               \
+    (out_f32 ? grouped_compat_typed<FA, FB, true>(a, lda, b, ldb, b_group_stride, offsets, g, total_m, n, k, sa, sb, \
+                                                  d, ldd, st)                                                      \
+             : grouped_compat_typed<FA, FB, false>(a, lda, b, ldb, b_group_stride, offsets, g, total_m, n, k, sa, sb, \
+                                                   d, ldd, st))
+    FP8_COMPAT_PAIRS(CALL)
+#undef CALL
+}
+#undef FP8_COMPAT_PAIRS
 
 hipError_t launch_gemm(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb, int64_t m,
                        int64_t n, int64_t k, const float* sa, int sa_vec, const float* sb, int sb_vec, void* d,

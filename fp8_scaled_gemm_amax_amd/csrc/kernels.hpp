@@ -60,6 +60,17 @@ hipError_t launch_grouped_gemm(const uint8_t* a, int fa, int64_t lda, const uint
                                int64_t k, const float* sa, const float* sb, void* d, int out_f32, int64_t ldd,
                                hipStream_t st);
 
+// Products with fnuz operands (any of the four encodings on either side): the
+// operands decoded to bf16 in registers and multiplied on the bf16 matrix cores.
+hipError_t launch_gemm_compat(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb, int64_t m,
+                              int64_t n, int64_t k, const float* sa, int sa_vec, const float* sb, int sb_vec, void* d,
+                              int out_f32, int64_t ldd, hipStream_t st);
+
+hipError_t launch_grouped_gemm_compat(const uint8_t* a, int fa, int64_t lda, const uint8_t* b, int fb, int64_t ldb,
+                                      int64_t b_group_stride, const int64_t* offsets, int g, int64_t total_m,
+                                      int64_t n, int64_t k, const float* sa, const float* sb, void* d, int out_f32,
+                                      int64_t ldd, hipStream_t st);
+
 // MoE backward: per-group colwise quantization into the grouped transposed
 // layout, and the grouped product over ragged contraction ranges.
 constexpr int64_t kGroupKAlign = 256;

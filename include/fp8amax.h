@@ -77,7 +77,7 @@ typedef enum {
     FP8_OK = 0,
     FP8_ERR_INVALID_ARG = 1,  /* null pointer, negative size, ld < width, bad enum, margin out of range */
     FP8_ERR_ALIGNMENT = 2,    /* a pointer or leading dimension breaks a stated alignment */
-    FP8_ERR_UNSUPPORTED = 3,  /* valid request this build does not run (device not gfx950, fnuz GEMM operands) */
+    FP8_ERR_UNSUPPORTED = 3,  /* valid request this build does not run (device not gfx950, fnuz MX / ragged-K operands) */
     FP8_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
 } fp8_status_t;
 
@@ -226,9 +226,13 @@ fp8_status_t fp8_delayed_scale_update(float* cur_amax, float* history, int32_t* 
  * a_scale_inv[0] (TENSOR); likewise sb_j with b_scale_inv ([n]). The scales
  * are the quantizers' scale_inv outputs (device fp32). out: bf16
  * (round-to-nearest-even) or fp32, d [m x n] with row stride ldd >= n.
- * Formats: fa, fb in {FP8_E4M3, FP8_E5M2}, mixed allowed ([Flux] "hybrid":
- * e4m3 activations and weights, e5m2 gradients). fnuz operands return
- * FP8_ERR_UNSUPPORTED (gfx950's matrix cores consume OCP encodings).
+ * Formats: fa, fb any of the four encodings, mixed allowed ([Flux] "hybrid":
+ * e4m3 activations and weights, e5m2 gradients). OCP pairs run on the FP8
+ * matrix cores. A pair with a fnuz operand ([MI300]: the encodings of MI300
+ * parts, which gfx950's FP8 matrix cores do not consume and no fixed
+ * re-encoding maps onto OCP) takes a compatibility path: both operands are
+ * decoded to bf16 (exact for every FP8 value) and multiplied on the bf16
+ * matrix cores with fp32 accumulation, the same arithmetic at a lower rate.
  * Requirements: k % 16 == 0; a, b 16-byte aligned; lda, ldb multiples of 16;
  * d 4-byte aligned. m, n >= 0 arbitrary (ragged tiles are masked); k == 0
  * writes zeros times the scales. */
@@ -306,8 +310,8 @@ fp8_status_t fp8_grouped_quantize_col(const uint16_t* x, int64_t total_m, int64_
  * checked on the host; a group whose padded range P_g + roundup(m_g,
  * FP8_GROUP_K_ALIGN) runs past min(lda, ldb) writes NaN to its whole output
  * instead of a sum that silently misses columns. Checked: lda, ldb >= total_m;
- * lda, ldb < 2^24 (else FP8_ERR_UNSUPPORTED). Formats and alignment as
- * fp8_gemm_scaled; g: 1..4096. */
+ * lda, ldb < 2^24 (else FP8_ERR_UNSUPPORTED). Alignment as fp8_gemm_scaled;
+ * formats OCP e4m3 / e5m2 only (fnuz: FP8_ERR_UNSUPPORTED); g: 1..4096. */
 fp8_status_t fp8_grouped_gemm_ragged_k(const uint8_t* a, fp8_format_t fa, int64_t lda, const uint8_t* b,
                                        fp8_format_t fb, int64_t ldb, const int64_t* group_offsets, int32_t g,
                                        int64_t total_m, int64_t m, int64_t n, const float* a_scale_inv,

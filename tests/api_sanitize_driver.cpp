@@ -75,6 +75,10 @@ STUB(launch_gemm, const uint8_t*, int, int64_t, const uint8_t*, int, int64_t, in
      int, const float*, int, void*, int, int64_t, hipStream_t)
 STUB(launch_grouped_gemm, const uint8_t*, int, int64_t, const uint8_t*, int, int64_t, int64_t, const int64_t*, int,
      int64_t, int64_t, int64_t, const float*, const float*, void*, int, int64_t, hipStream_t)
+STUB(launch_gemm_compat, const uint8_t*, int, int64_t, const uint8_t*, int, int64_t, int64_t, int64_t, int64_t,
+     const float*, int, const float*, int, void*, int, int64_t, hipStream_t)
+STUB(launch_grouped_gemm_compat, const uint8_t*, int, int64_t, const uint8_t*, int, int64_t, int64_t, const int64_t*,
+     int, int64_t, int64_t, int64_t, const float*, const float*, void*, int, int64_t, hipStream_t)
 STUB(launch_grouped_quant_col, const uint16_t*, int64_t, int64_t, int64_t, int, int, const int64_t*, int, uint8_t*,
      int64_t, float*, float*, int, hipStream_t)
 STUB(launch_grouped_gemm_ragged_k, const uint8_t*, int, int64_t, const uint8_t*, int, int64_t, const int64_t*, int,
@@ -244,9 +248,12 @@ int main() {
     ERR(fp8_gemm_scaled(U8(1), FP8_E4M3, 4096, U8(2), FP8_E4M3, 4096, 512, 512, 4088, F32(3), FP8_SCALE_VECTOR, F32(4),
                         FP8_SCALE_VECTOR, dev(5), FP8_OUT_BF16, 512, nullptr),
         IA);
-    ERR(fp8_gemm_scaled(U8(1), FP8_E4M3_FNUZ, 4096, U8(2), FP8_E4M3, 4096, 512, 512, 4096, F32(3), FP8_SCALE_VECTOR,
-                        F32(4), FP8_SCALE_VECTOR, dev(5), FP8_OUT_BF16, 512, nullptr),
-        UN);
+    OK(fp8_gemm_scaled(U8(1), FP8_E4M3_FNUZ, 4096, U8(2), FP8_E4M3, 4096, 512, 512, 4096, F32(3), FP8_SCALE_VECTOR,
+                       F32(4), FP8_SCALE_VECTOR, dev(5), FP8_OUT_BF16, 512, nullptr),
+       "launch_gemm_compat");
+    OK(fp8_grouped_gemm_scaled(U8(1), FP8_E5M2_FNUZ, 7168, U8(2), FP8_E4M3_FNUZ, 7168, 2048 * 7168, I64(3), 32, 16384,
+                               2048, 7168, F32(4), F32(5), dev(6), FP8_OUT_F32, 2048, nullptr),
+       "launch_grouped_gemm_compat");
     ERR(fp8_gemm_scaled(U8(1), FP8_E4M3, 4100, U8(2), FP8_E4M3, 4096, 512, 512, 4096, F32(3), FP8_SCALE_VECTOR, F32(4),
                         FP8_SCALE_VECTOR, dev(5), FP8_OUT_BF16, 512, nullptr),
         AL);
@@ -273,6 +280,9 @@ int main() {
     ERR(fp8_grouped_gemm_ragged_k(U8(1), FP8_E5M2, 992, U8(2), FP8_E4M3, 2048, I64(3), 4, 1000, 256, 512, F32(4),
                                   F32(5), dev(6), FP8_OUT_BF16, 512, 256 * 512, nullptr),
         IA);
+    ERR(fp8_grouped_gemm_ragged_k(U8(1), FP8_E5M2_FNUZ, 2048, U8(2), FP8_E4M3, 2048, I64(3), 4, 1000, 256, 512,
+                                  F32(4), F32(5), dev(6), FP8_OUT_BF16, 512, 256 * 512, nullptr),
+        UN);
     ERR(fp8_grouped_gemm_ragged_k(U8(1), FP8_E5M2, 2048, U8(2), FP8_E4M3, 2048, I64(3), 4, 1000, 256, 512, F32(4),
                                   F32(5), dev(6), FP8_OUT_BF16, 512, 100, nullptr),
         IA);

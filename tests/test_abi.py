@@ -76,9 +76,10 @@ def test_gemm_rejects_bad_arguments(fp8):
     # lda not a multiple of 16
     st, _ = _call(fp8, g, FAKE, 0, 40, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 0, 8, None)
     assert st == 2
-    # fnuz operands: valid request, not run on gfx950 matrix cores
-    st, msg = _call(fp8, g, FAKE, 2, 32, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 0, 8, None)
-    assert st == 3 and "fnuz" in msg
+    # fnuz operands are accepted (the bf16 compatibility path) and validated like
+    # the others: here ldd < n
+    st, msg = _call(fp8, g, FAKE, 2, 32, FAKE, 3, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 0, 4, None)
+    assert st == 1 and "leading dimension" in msg
     # unknown format / output type / scale mode
     assert _call(fp8, g, FAKE, 7, 32, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 0, 8, None)[0] == 1
     assert _call(fp8, g, FAKE, 0, 32, FAKE, 0, 32, 8, 8, 32, FAKE, 1, FAKE, 1, FAKE, 5, 8, None)[0] == 1
