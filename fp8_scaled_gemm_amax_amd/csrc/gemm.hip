@@ -1058,9 +1058,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
     int64_t K = kpad(grp);
     const int64_t lim = lda < ldb ? lda : ldb;
     // a group whose padded range runs past the operands' width would lose real
-    // contraction columns: its outputs are made NaN instead of a short sum
-    const bool cut = K > 0 && P + K > lim;
-    if (cut) K = 0;
+    // contraction columns: its outputs are made NaN instead of a short sum (K = -1)
+    if (K > 0 && P + K > lim) K = -1;
     const int64_t row0 = pm * big::BM, col0 = pn * big::BN;
     const float* sa_lane = sa + (int64_t)grp * m + (row0 + t < m ? row0 + t : m - 1);
     const float* sb_lane = sb + (int64_t)grp * n + (col0 + t < n ? col0 + t : n - 1);
@@ -1068,16 +1067,15 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k(
     if (K > 0) {
         k128_mainloop<FA, FB, false>(smem, a + row0 * lda + P, lda, m - row0, b + col0 * ldb + P, ldb, n - col0, K,
                                      sa_lane, sb_lane, nullptr, nullptr, 0, 0, acc);
-    } else {                                             // empty group: 0 * sa * sb (cut: NaN)
-        const float fill = cut ? __builtin_nanf("") : 0.0f;
+    } else {                                             // empty group: 0 * sa * sb (cut: 0 * NaN)
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = fill;
+                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
         float* s_rows = reinterpret_cast<float*>(smem + big::kScaleOff);
-        s_rows[t] = *sa_lane;
+        s_rows[t] = K < 0 ? __builtin_nanf("") : *sa_lane;
         s_rows[256 + t] = *sb_lane;
     }
     uint8_t* dg = reinterpret_cast<uint8_t*>(d) + (int64_t)grp * d_group_stride * (OUT_F32 ? 4 : 2);
