@@ -19,7 +19,7 @@ __all__ = [
     "AMAX_MOST_RECENT", "AMAX_MAX", "SCALE_TENSOR", "SCALE_VECTOR", "OUT_BF16", "OUT_F32",
     "Fp8Error", "LIB_PATH", "lib", "fp8_query_device", "fp8_status_string", "fp8_amax",
     "fp8_quantize_tensor", "fp8_quantize_tensor_batch", "fp8_quantize_row", "fp8_quantize_row_batch",
-    "fp8_quantize_col", "fp8_delayed_scale_update",
+    "fp8_quantize_col", "fp8_quantize_rowcol", "fp8_delayed_scale_update",
     "fp8_gemm_scaled", "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "grouped_layout_width", "GROUP_K_ALIGN", "MX_BLOCK", "fp8_mx_quantize_row", "fp8_gemm_mx",
     "fp8_grouped_gemm_mx", "mx_scale_records", "fp8_moe_route", "fp8_moe_permute_quantize_row",
@@ -36,7 +36,7 @@ OUT_BF16, OUT_F32 = 0, 1
 EXPORTED_SYMBOLS = (
     "fp8_query_device", "fp8_status_string", "fp8_last_error", "fp8_amax", "fp8_quantize_tensor",
     "fp8_quantize_row", "fp8_quantize_row_batch", "fp8_quantize_tensor_batch", "fp8_quantize_col",
-    "fp8_delayed_scale_update", "fp8_gemm_scaled",
+    "fp8_quantize_rowcol", "fp8_delayed_scale_update", "fp8_gemm_scaled",
     "fp8_grouped_gemm_scaled", "fp8_grouped_quantize_col", "fp8_grouped_gemm_ragged_k",
     "fp8_mx_quantize_row", "fp8_gemm_mx", "fp8_grouped_gemm_mx", "fp8_moe_route", "fp8_moe_permute_quantize_row",
     "fp8_swiglu_quantize_row", "fp8_moe_unpermute_combine", "fp8_blockwise_quantize_act",
@@ -76,6 +76,7 @@ def _load():
         "fp8_quantize_row_batch": [I32, P, P, I64, P, I, I32, P, P, P, P, P, P],
         "fp8_quantize_tensor_batch": [I32, P, P, I64, P, I, P, P, P, P, P, P],
         "fp8_quantize_col": [P, I64, I64, I64, I, I32, I32, P, I64, P, P, I32, P],
+        "fp8_quantize_rowcol": [P, I64, I64, I64, I, I32, P, I64, P, P, P, I64, P, P, P],
         "fp8_delayed_scale_update": [P, P, P, I64, I32, I, I32, I, P, P, P],
         "fp8_gemm_scaled": [P, I, I64, P, I, I64, I64, I64, I64, P, I, P, I, P, I, I64, P],
         "fp8_grouped_gemm_scaled": [P, I, I64, P, I, I64, I64, P, I32, I64, I64, I64, P, P, P, I, I64, P],
@@ -221,6 +222,16 @@ def fp8_quantize_col(x, fmt, margin, q, scale_inv_out, col_amax, col_amax_ready=
     _, _, ldq = _mat(q, "q", 1)
     _check(lib.fp8_quantize_col(_ptr(x), rows, cols, ldx, fmt, margin, int(bool(transpose_out)), _ptr(q), ldq,
                                 _ptr(scale_inv_out), _ptr(col_amax), int(bool(col_amax_ready)), _stream(x)))
+
+
+def fp8_quantize_rowcol(x, fmt, margin, q, scale_inv_out, amax_out, qt, col_scale_inv_out, col_amax_out):
+    """Rowwise codes q [rows x cols] and colwise-transposed codes qt [cols x rows] of x in two passes."""
+    rows, cols, ldx = _bf16(x)
+    _, _, ldq = _mat(q, "q", 1)
+    _, _, ldqt = _mat(qt, "qt", 1)
+    _check(lib.fp8_quantize_rowcol(_ptr(x), rows, cols, ldx, fmt, margin, _ptr(q), ldq, _ptr(scale_inv_out),
+                                   _ptr(amax_out), _ptr(qt), ldqt, _ptr(col_scale_inv_out), _ptr(col_amax_out),
+                                   _stream(x)))
 
 
 def fp8_delayed_scale_update(cur_amax, history, head, algo, margin, fmt, scale, scale_inv):

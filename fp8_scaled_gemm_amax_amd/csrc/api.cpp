@@ -324,6 +324,28 @@ fp8_status_t fp8_quantize_col(const uint16_t* x, int64_t rows, int64_t cols, int
     return launched(e, fn);
 }
 
+fp8_status_t fp8_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                                 int32_t margin, uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out,
+                                 uint8_t* qt, int64_t ldqt, float* col_scale_inv_out, float* col_amax_out,
+                                 void* stream) {
+    const char* fn = "fp8_quantize_rowcol";
+    FP8_TRY(check_common_quant(fn, x, rows, cols, ldx, (int)fmt, margin));
+    FP8_TRY(check_matrix(fn, "q", q, rows, cols, ldq));
+    FP8_TRY(check_matrix(fn, "qt", qt, cols, rows, ldqt));
+    if ((rows > 0 && (!scale_inv_out || !amax_out)) || (cols > 0 && (!col_scale_inv_out || !col_amax_out)))
+        return fail(FP8_ERR_INVALID_ARG, "%s: scale and amax outputs are required", fn);
+    if (!aligned(scale_inv_out, 4) || !aligned(amax_out, 4) || !aligned(col_scale_inv_out, 4) ||
+        !aligned(col_amax_out, 4))
+        return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer", fn);
+    if (!aligned(x, 16) || ldx % 8 != 0 || cols % 8 != 0 || !aligned(q, 8) || ldq % 8 != 0)
+        return fail(FP8_ERR_ALIGNMENT, "%s: x must be 16-byte aligned with ldx, cols multiples of 8; q 8-byte "
+                    "aligned with ldq a multiple of 8", fn);
+    FP8_TRY(check_device());
+    return launched(launch_quant_rowcol(x, rows, cols, ldx, (int)fmt, margin, q, ldq, scale_inv_out, amax_out, qt,
+                                        ldqt, col_scale_inv_out, col_amax_out, (hipStream_t)stream),
+                    fn);
+}
+
 fp8_status_t fp8_delayed_scale_update(float* cur_amax, float* history, int32_t* head, int64_t n, int32_t L,
                                       fp8_amax_algo_t algo, int32_t margin, fp8_format_t fmt, float* scale,
                                       float* scale_inv, void* stream) {

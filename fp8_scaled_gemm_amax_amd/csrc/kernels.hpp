@@ -37,6 +37,13 @@ hipError_t launch_quant_col(const uint16_t* x, int64_t rows, int64_t cols, int64
                             int transpose, uint8_t* qt, int64_t ldqt, float* scale_inv, const float* col_amax,
                             hipStream_t st);
 
+// Dual cast (vector layout: x 16-byte aligned, ldx and cols multiples of 8; q
+// 8-byte aligned, ldq % 8 == 0): row amax and column amax in one pass, then
+// one pass writing the rowwise codes q and the colwise codes qt (transposed).
+hipError_t launch_quant_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
+                               uint8_t* q, int64_t ldq, float* row_scale_inv, float* row_amax, uint8_t* qt,
+                               int64_t ldqt, float* col_scale_inv, float* col_amax, hipStream_t st);
+
 hipError_t launch_quant_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
                                const float* scale, uint8_t* q, int64_t ldq, float* scale_inv, float* amax,
                                hipStream_t st);

@@ -154,6 +154,106 @@ __global__ __launch_bounds__(kBlock) void k_amax_cols_vec(const uint16_t* __rest
     if (col + 1 < cols) atomic_max_bits(out + col + 1, w & 0xffff0000u);
 }
 
+// Maxima of 16 rows across a wavefront at once: lane l holds its value of
+// row u in v[u]; each exchange step pairs lanes l and l ^ o and halves the
+// rows a lane carries (the lane with bit o clear keeps the lower half), so
+// after the steps o = 32, 16, 8, 4 (8 + 4 + 2 + 1 shuffles) lane l carries
+// row 8 b5 + 4 b4 + 2 b3 + b2 (b_i: bit i of l) over the 16 lanes that share
+// bits 2..5, and two more steps (o = 2, 1) complete it: 17 shuffles instead of
+// 16 full wavefront reductions. Returns that row's maximum (valid in every lane).
+__device__ __forceinline__ uint32_t wave_max_16rows(const uint32_t (&v)[16]) {
+    const int lane = threadIdx.x & 63;
+    uint32_t a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const bool hi = lane & 32;
+        const uint32_t keep = hi ? v[i + 8] : v[i], send = hi ? v[i] : v[i + 8];
+        const uint32_t o = (uint32_t)__shfl_xor((int)send, 32, 64);
+        a[i] = keep > o ? keep : o;
+    }
+    uint32_t b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool hi = lane & 16;
+        const uint32_t keep = hi ? a[i + 4] : a[i], send = hi ? a[i] : a[i + 4];
+        const uint32_t o = (uint32_t)__shfl_xor((int)send, 16, 64);
+        b[i] = keep > o ? keep : o;
+    }
+    uint32_t c[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const bool hi = lane & 8;
+        const uint32_t keep = hi ? b[i + 2] : b[i], send = hi ? b[i] : b[i + 2];
+        const uint32_t o = (uint32_t)__shfl_xor((int)send, 8, 64);
+        c[i] = keep > o ? keep : o;
+    }
+    const bool hi = lane & 4;
+    uint32_t d = hi ? c[1] : c[0];
+    uint32_t o = (uint32_t)__shfl_xor((int)(hi ? c[0] : c[1]), 4, 64);
+    d = d > o ? d : o;
+    o = (uint32_t)__shfl_xor((int)d, 2, 64);
+    d = d > o ? d : o;
+    o = (uint32_t)__shfl_xor((int)d, 1, 64);
+    return d > o ? d : o;
+}
+
+// Row and column amax in one pass (the first pass of the dual cast below):
+// k_amax_cols_vec's walk, and in addition each loaded row segment's maximum
+// (one wavefront covers the workgroup's 512 columns of a row) is reduced
+// across the wavefront, 16 rows at a time (wave_max_16rows), and folded into
+// row_out by one atomic max per row and 512-column chunk. Both outputs are
+// cleared beforehand.
+__global__ __launch_bounds__(kBlock) void k_amax_rows_cols_vec(const uint16_t* __restrict__ x, int64_t rows,
+                                                               int64_t cols, int64_t ldx, float* __restrict__ row_out,
+                                                               float* __restrict__ col_out) {
+    __shared__ uint32_t part[kWaves][256];   // packed u16 pairs: 512 columns
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t ch = (int64_t)blockIdx.y * 64 + lane;        // 8-column chunk index
+    const int64_t nch = cols >> 3;
+    const bool have = ch < nch;
+    const uint16_t* base = x + (have ? ch : nch - 1) * 8;      // (past the row: a duplicate chunk, not counted)
+    uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+    for (int64_t r0 = (int64_t)blockIdx.x * kColAmaxRows; r0 < rows; r0 += (int64_t)gridDim.x * kColAmaxRows) {
+        const int64_t r1 = r0 + kColAmaxRows < rows ? r0 + kColAmaxRows : rows;
+        for (int64_t rb = r0 + wave; rb < r1; rb += kColAmaxUnroll * kWaves) {
+            uint4 v[kColAmaxUnroll];
+#pragma unroll
+            for (int u = 0; u < kColAmaxUnroll; ++u) {
+                const int64_t r = rb + u * kWaves;
+                v[u] = *reinterpret_cast<const uint4*>(base + (r < r1 ? r : r1 - 1) * ldx);
+            }
+            static_assert(kColAmaxUnroll == 16, "wave_max_16rows reduces 16 rows");
+            uint32_t rmax[kColAmaxUnroll];
+#pragma unroll
+            for (int u = 0; u < kColAmaxUnroll; ++u) {
+                if (!have) v[u] = make_uint4(0u, 0u, 0u, 0u);
+                m0 = pk_absmax(m0, v[u].x);
+                m1 = pk_absmax(m1, v[u].y);
+                m2 = pk_absmax(m2, v[u].z);
+                m3 = pk_absmax(m3, v[u].w);
+                rmax[u] = pk_fold(word_absmax(0u, v[u]));
+            }
+            const uint32_t rm = wave_max_16rows(rmax);
+            const int u = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+            const int64_t r = rb + u * kWaves;
+            if ((lane & 3) == 0 && r < r1) atomic_max_bits(row_out + r, rm << 16);
+        }
+    }
+    part[wave][lane * 4 + 0] = m0;
+    part[wave][lane * 4 + 1] = m1;
+    part[wave][lane * 4 + 2] = m2;
+    part[wave][lane * 4 + 3] = m3;
+    __syncthreads();
+    const int t = threadIdx.x;
+    uint32_t w = part[0][t];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) w = pk_absmax(w, part[k][t]);
+    const int64_t col = (int64_t)blockIdx.y * 512 + 2 * t;
+    if (col < cols) atomic_max_bits(col_out + col, (w & 0xffffu) << 16);
+    if (col + 1 < cols) atomic_max_bits(col_out + col + 1, w & 0xffff0000u);
+}
+
 __global__ __launch_bounds__(kBlock) void k_amax_cols_scalar(const uint16_t* __restrict__ x, int64_t rows,
                                                              int64_t cols, int64_t ldx, float* __restrict__ out) {
     const int64_t col = (int64_t)blockIdx.y * kBlock + threadIdx.x;
@@ -1069,6 +1169,59 @@ __global__ __launch_bounds__(kBlock) void k_quant_col_tiled(const uint16_t* __re
     col_tile<F>(x, ldx, r0, rows, false, c0, cols, s_lds, nan_lds, tile, qt, ldqt, r0, rows, vec_store);
 }
 
+// Dual cast of one tensor (rowwise codes and colwise-transposed codes, e.g.
+// the gradient dY of a linear layer, which its dgrad takes rowwise and its
+// wgrad colwise: "FP8 training for Flux models", fp8 hybrid and fp8_wgrad;
+// "FP8 Training on AMD GPUs with TorchTitan and TorchAO", colwise scales),
+// second pass: with the row and column amax known, each 128 x 64 tile is read
+// once and cast twice. Row codes, with the scales of the tile's 128 rows (in
+// LDS), go straight out in x's layout (8 lanes per 64-byte row segment);
+// column codes go through the LDS transpose as in k_quant_col_tiled.
+template <int F>
+__global__ __launch_bounds__(kBlock) void k_quant_rowcol_tiled(const uint16_t* __restrict__ x, int64_t rows,
+                                                               int64_t cols, int64_t ldx, int margin,
+                                                               uint8_t* __restrict__ q, int64_t ldq,
+                                                               float* __restrict__ row_scale_inv,
+                                                               const float* __restrict__ row_amax,
+                                                               uint8_t* __restrict__ qt, int64_t ldqt,
+                                                               float* __restrict__ col_scale_inv,
+                                                               const float* __restrict__ col_amax, int vec_store) {
+    __shared__ float s_lds[kColTileC];
+    __shared__ int nan_lds[kColTileC];
+    __shared__ float rs_lds[kColTileR];
+    __shared__ int rnan_lds[kColTileR];
+    __shared__ __attribute__((aligned(16))) uint32_t tile[kColTileC * kColTileR / 4];
+    const int64_t c0 = (int64_t)blockIdx.y * kColTileC;
+    const int64_t r0 = (int64_t)blockIdx.x * kColTileR;
+    const int t = threadIdx.x;
+    if (t < kColTileR) {
+        const int64_t r = r0 + t;
+        const float a = r < rows ? row_amax[r] : 0.0f;
+        const float sr = scale_from_amax<F>(a, margin);
+        rs_lds[t] = sr;
+        rnan_lds[t] = __builtin_isnan(a) ? 1 : 0;
+        if (blockIdx.y == 0 && r < rows) row_scale_inv[r] = 1.0f / sr;
+    }
+    col_scales_to_lds<F>(col_amax, c0, cols, margin, blockIdx.x == 0 ? col_scale_inv : nullptr, s_lds, nan_lds);
+    uint4 v[4];
+    col_tile_load(v, x, ldx, r0, rows, false, c0, cols);
+    const int cc = t & 7, rg = t >> 3;
+    const int64_t col = c0 + cc * 8;
+    if (col < cols) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int lr = rg * 4 + r;
+            const int64_t row = r0 + lr;
+            if (row >= rows) continue;
+            const uint2 code = rnan_lds[lr] ? encode8<F, false>(v[r], rs_lds[lr]) : encode8<F, true>(v[r], rs_lds[lr]);
+            *reinterpret_cast<uint2*>(q + row * ldq + col) = code;
+        }
+    }
+    col_tile_encode<F>(v, s_lds, nan_lds, tile);
+    __syncthreads();
+    col_tile_store(tile, c0, cols, qt, ldqt, r0, rows, vec_store);
+}
+
 // ------------------------------------------------- grouped colwise (MoE) --
 
 // Groups of at most kSmallGroupRows rows take the one-pass kernel
@@ -1915,6 +2068,47 @@ hipError_t launch_quant_col(const uint16_t* x, int64_t rows, int64_t cols, int64
         return launch_fill(scale_inv, cols, 1.0f, st);
     }
 #define CALL(F) quant_col_fmt<F>(x, rows, cols, ldx, margin, transpose, qt, ldqt, scale_inv, col_amax, st)
+    switch (fmt) {
+        case kE4M3: return CALL(kE4M3);
+        case kE5M2: return CALL(kE5M2);
+        case kE4M3Fnuz: return CALL(kE4M3Fnuz);
+        default: return CALL(kE5M2Fnuz);
+    }
+#undef CALL
+}
+
+template <int F>
+hipError_t quant_rowcol_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int margin, uint8_t* q,
+                            int64_t ldq, float* row_scale_inv, float* row_amax, uint8_t* qt, int64_t ldqt,
+                            float* col_scale_inv, float* col_amax, hipStream_t st) {
+    const int vec_store = is_aligned(qt, 16) && ldqt % 16 == 0;
+    const dim3 grid((unsigned)((rows + kColTileR - 1) / kColTileR), (unsigned)((cols + kColTileC - 1) / kColTileC));
+    hipLaunchKernelGGL((k_quant_rowcol_tiled<F>), grid, dim3(kBlock), 0, st, x, rows, cols, ldx, margin, q, ldq,
+                       row_scale_inv, row_amax, qt, ldqt, col_scale_inv, col_amax, vec_store);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,
+                               uint8_t* q, int64_t ldq, float* row_scale_inv, float* row_amax, uint8_t* qt,
+                               int64_t ldqt, float* col_scale_inv, float* col_amax, hipStream_t st) {
+    if (rows == 0 || cols == 0) {
+        hipError_t e = launch_fill(col_amax, cols, 0.0f, st);
+        if (e == hipSuccess) e = launch_fill(col_scale_inv, cols, 1.0f, st);
+        return e;
+    }
+    // first pass: both amax (cleared first), then the dual cast
+    hipError_t e = launch_fill(row_amax, rows, 0.0f, st);
+    if (e == hipSuccess) e = launch_fill(col_amax, cols, 0.0f, st);
+    if (e != hipSuccess) return e;
+    const int64_t bands = (rows + kColAmaxRows - 1) / kColAmaxRows, chunks = (cols + 511) / 512;
+    int64_t workers = (int64_t)current_device_props().cus * 2 / chunks;
+    workers = workers < 1 ? 1 : (workers > bands ? bands : workers);
+    hipLaunchKernelGGL(k_amax_rows_cols_vec, dim3((unsigned)workers, (unsigned)chunks), dim3(kBlock), 0, st, x, rows,
+                       cols, ldx, row_amax, col_amax);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+#define CALL(F) quant_rowcol_fmt<F>(x, rows, cols, ldx, margin, q, ldq, row_scale_inv, row_amax, qt, ldqt, col_scale_inv, \
+                                    col_amax, st)
     switch (fmt) {
         case kE4M3: return CALL(kE4M3);
         case kE5M2: return CALL(kE5M2);

@@ -202,6 +202,24 @@ fp8_status_t fp8_quantize_col(const uint16_t* x, int64_t rows, int64_t cols, int
                               int32_t margin, int32_t transpose_out, uint8_t* q, int64_t ldq, float* scale_inv_out,
                               float* col_amax, int32_t col_amax_ready, void* stream);
 
+/* Dual cast of one tensor: rowwise codes and colwise-transposed codes ([Flux]
+ * "Configuration": fp8 hybrid and fp8_wgrad, where the output gradient dY
+ * feeds the dgrad rowwise and the wgrad colwise; [Titan] colwise scales and
+ * fused quantization kernels). Gives exactly what fp8_quantize_row (q,
+ * scale_inv_out, amax_out) and fp8_quantize_col with transpose_out = 1 (qt,
+ * col_scale_inv_out, col_amax_out) give, in two passes over x instead of
+ * three: the row and column amax together, then one pass writing both code
+ * tensors. x: bf16 [rows x cols] (ldx); q: codes [rows x cols] (ldq >= cols);
+ * qt: codes [cols x rows] (ldqt >= rows). scale_inv_out[rows], amax_out[rows],
+ * col_scale_inv_out[cols] and col_amax_out[cols] are all required (the amax
+ * outputs hold the first pass's results). Requirements: x 16-byte aligned,
+ * ldx and cols multiples of 8; q 8-byte aligned, ldq % 8 == 0 (else
+ * FP8_ERR_ALIGNMENT). margin: 0..32. */
+fp8_status_t fp8_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, fp8_format_t fmt,
+                                 int32_t margin, uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out,
+                                 uint8_t* qt, int64_t ldqt, float* col_scale_inv_out, float* col_amax_out,
+                                 void* stream);
+
 /* Fused end-of-step update of n delayed-scaling states ([Flux] "Configuration":
  * fp8_amax_history_len, fp8_amax_compute_algo, fp8_margin; [Flux] "Testing":
  * the fused delayed-scale update). State layout, all device memory:

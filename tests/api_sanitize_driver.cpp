@@ -68,6 +68,8 @@ STUB(launch_quant_col, const uint16_t*, int64_t, int64_t, int64_t, int, int, int
      const float*, hipStream_t)
 STUB(launch_quant_tensor, const uint16_t*, int64_t, int64_t, int64_t, int, int, const float*, uint8_t*, int64_t, float*,
      float*, hipStream_t)
+STUB(launch_quant_rowcol, const uint16_t*, int64_t, int64_t, int64_t, int, int, uint8_t*, int64_t, float*, float*,
+     uint8_t*, int64_t, float*, float*, hipStream_t)
 STUB(launch_quant_tensor_batch, int, const uint16_t* const*, const int64_t*, int64_t, const int64_t*, int,
      const float* const*, uint8_t* const*, const int64_t*, float* const*, float* const*, hipStream_t)
 STUB(launch_delayed_update, float*, float*, int32_t*, int64_t, int32_t, int, int, int, float*, float*, hipStream_t)
@@ -232,6 +234,23 @@ int main() {
     ERR(fp8_quantize_col(U16(1), 64, 128, 128, FP8_E4M3, 0, 0, U8(2), 64, F32(3), F32(4), 0, nullptr), IA);
     ERR(fp8_quantize_col(U16(1), 64, 128, 128, FP8_E4M3, 0, 2, U8(2), 64, F32(3), F32(4), 0, nullptr), IA);
     ERR(fp8_quantize_col(U16(1), 64, 128, 128, FP8_E4M3, 0, 1, U8(2), 64, F32(3), F32(4), 3, nullptr), IA);
+
+    // dual cast
+    OK(fp8_quantize_rowcol(U16(1), 64, 128, 128, FP8_E5M2, 0, U8(2), 128, F32(3), F32(4), U8(5), 64, F32(6), F32(7),
+                           nullptr),
+       "launch_quant_rowcol");
+    ERR(fp8_quantize_rowcol(U16(1), 64, 128, 128, FP8_E5M2, 0, U8(2), 128, F32(3), nullptr, U8(5), 64, F32(6), F32(7),
+                            nullptr),
+        IA);
+    ERR(fp8_quantize_rowcol(U16(1), 64, 128, 128, FP8_E5M2, 0, U8(2), 128, F32(3), F32(4), U8(5), 32, F32(6), F32(7),
+                            nullptr),
+        IA);
+    ERR(fp8_quantize_rowcol(U16(1), 64, 120, 120, FP8_E5M2, 0, nullptr, 128, F32(3), F32(4), U8(5), 64, F32(6),
+                            F32(7), nullptr),
+        IA);
+    ERR(fp8_quantize_rowcol(U16(1), 64, 124, 124, FP8_E5M2, 0, U8(2), 128, F32(3), F32(4), U8(5), 64, F32(6), F32(7),
+                            nullptr),
+        AL);
 
     // delayed update
     OK(fp8_delayed_scale_update(F32(1), F32(2), I32(3), 4, 1024, FP8_AMAX_MAX, 0, FP8_E4M3, F32(4), F32(5), nullptr),

@@ -204,17 +204,29 @@ def test_c4_moe_grouped(fp8, orc):
 
 
 def test_c5_hybrid_backward(fp8, orc):
-    """dY [8192 x 14336] cast to e5m2 rowwise (with the column-amax side output),
-    dY^T / W^T / X^T colwise-transposed (e5m2 / e4m3 / e4m3); dgrad
-    dX = dY W and wgrad dW = dY^T X as e5m2 x e4m3 GEMMs."""
+    """In the benchmark's launch configuration: dY [8192 x 14336] through the
+    dual cast (e5m2 rowwise codes and colwise-transposed codes in two passes),
+    X and W cast rowwise with their column-amax side outputs (the forward), then
+    W^T / X^T colwise-transposed with those amax (e4m3); dgrad dX = dY W and
+    wgrad dW = dY^T X as e5m2 x e4m3 GEMMs. Every code, scale and amax and every
+    GEMM output compared."""
     say("c5 generate")
     w = workloads.c5()
     xd, wd, dyd = dev_bf16(w["x"]), dev_bf16(w["w"]), dev_bf16(w["dy"])
+    m, k = w["x"].shape
+    n = w["w"].shape[0]
     say("c5 quantize")
-    qdy, sdy, _, ca_dy = row_quant(fp8, dyd, 1, col_amax=True)
-    qdyt, sdyt, _ = col_quant(fp8, dyd, 1, ready=ca_dy)
-    qwt, swt, _ = col_quant(fp8, wd, 0)
-    qxt, sxt, _ = col_quant(fp8, xd, 0)
+    qdy, sdy, ady = torch.empty((m, n), dtype=torch.uint8, device="cuda:0"), torch.empty(m, device="cuda:0"), \
+        torch.empty(m, device="cuda:0")
+    qdyt, sdyt, ca_dy = torch.empty((n, m), dtype=torch.uint8, device="cuda:0"), torch.empty(n, device="cuda:0"), \
+        torch.empty(n, device="cuda:0")
+    fp8.fp8_quantize_rowcol(dyd, 1, 0, qdy, sdy, ady, qdyt, sdyt, ca_dy)
+    cax, caw = torch.empty(k, device="cuda:0"), torch.empty(k, device="cuda:0")
+    fwd = [torch.empty((m, k), dtype=torch.uint8, device="cuda:0"), torch.empty((n, k), dtype=torch.uint8, device="cuda:0")]
+    fp8.fp8_quantize_row_batch([xd, wd], 0, 0, fwd, [torch.empty(m, device="cuda:0"), torch.empty(n, device="cuda:0")],
+                               None, [cax, caw])
+    qwt, swt, _ = col_quant(fp8, wd, 0, ready=caw)
+    qxt, sxt, _ = col_quant(fp8, xd, 0, ready=cax)
     dx = gemm(fp8, qdy, 1, qwt, 0, sdy, 1, swt, 1)       # [8192 x 4096]
     dw = gemm(fp8, qdyt, 1, qxt, 0, sdyt, 1, sxt, 1)     # [14336 x 4096]
     torch.cuda.synchronize()
@@ -223,13 +235,16 @@ def test_c5_hybrid_backward(fp8, orc):
     assert_codes_equal(qdy.cpu().numpy(), oqdy, "dY row codes")
     assert_f32_bits_equal(sdy.cpu().numpy(), osdy, "dY row scale_inv")
     oqdyt, osdyt, oady = orc.quantize_col(w["dy"], 1)
-    assert_f32_bits_equal(ca_dy.cpu().numpy(), oady, "dY col amax (side output)")
+    assert_f32_bits_equal(ca_dy.cpu().numpy(), oady, "dY col amax")
+    assert_f32_bits_equal(ady.cpu().numpy(), orc.amax(w["dy"], orc.AXIS_ROW), "dY row amax")
     assert_codes_equal(qdyt.cpu().numpy(), oqdyt, "dY^T codes")
     assert_f32_bits_equal(sdyt.cpu().numpy(), osdyt, "dY^T scale_inv")
-    oqwt, oswt, _ = orc.quantize_col(w["w"], 0)
+    oqwt, oswt, oaw = orc.quantize_col(w["w"], 0)
+    assert_f32_bits_equal(caw.cpu().numpy(), oaw, "W col amax (forward side output)")
     assert_codes_equal(qwt.cpu().numpy(), oqwt, "W^T codes")
     assert_f32_bits_equal(swt.cpu().numpy(), oswt, "W^T scale_inv")
-    oqxt, osxt, _ = orc.quantize_col(w["x"], 0)
+    oqxt, osxt, oax = orc.quantize_col(w["x"], 0)
+    assert_f32_bits_equal(cax.cpu().numpy(), oax, "X col amax (forward side output)")
     assert_codes_equal(qxt.cpu().numpy(), oqxt, "X^T codes")
     assert_f32_bits_equal(sxt.cpu().numpy(), osxt, "X^T scale_inv")
     say("c5 gemm check")

@@ -192,6 +192,40 @@ COL_SHAPES = [(1, 8), (128, 64), (130, 72), (257, 136), (1000, 520), (64, 4104),
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("shape", [(1, 8), (128, 64), (130, 72), (300, 1032), (1000, 520), (2100, 4104)])
+def test_quantize_rowcol_parity(fp8, orc, fmt, shape):
+    """Dual cast: rowwise codes and colwise-transposed codes of one tensor, as
+    fp8_quantize_row and fp8_quantize_col give them (oracle), with ragged
+    tiles, a NaN row and column, an Inf, an all-zero row and column, padded
+    output strides and guard bands around both outputs."""
+    rows, cols = shape
+    xb = rand_bf16(rows, cols, seed=rows + 5 * cols)
+    if rows > 3 and cols > 3:
+        xb[1, 2] = 0x7FC0                                # NaN: row 1 and column 2
+        xb[2, 3] = 0xFF80                                # -Inf: row 2 and column 3
+        xb[3, :] = 0
+        xb[:, 1] = 0x8000                                # a column of -0
+    x = dev_bf16(xb)
+    q, qbuf, qorg = guarded(rows, cols, torch.uint8, ld=cols + 8)
+    qt, tbuf, torg = guarded(cols, rows, torch.uint8, ld=rows + 16 - rows % 16)
+    si, am = torch.full((rows,), -1.0, device="cuda:0"), torch.full((rows,), -1.0, device="cuda:0")
+    sc, ca = torch.full((cols,), -1.0, device="cuda:0"), torch.full((cols,), -1.0, device="cuda:0")
+    say("rowcol", NAMES[fmt], shape)
+    fp8.fp8_quantize_rowcol(x, fmt, 1, q, si, am, qt, sc, ca)
+    torch.cuda.synchronize()
+    check_guard(qbuf, qorg, rows, cols)
+    check_guard(tbuf, torg, cols, rows)
+    oq, osi, oam = orc.quantize_row(xb, fmt, 1)
+    oqt, osc, oca = orc.quantize_col(xb, fmt, 1)
+    assert_codes_equal(q.cpu().numpy(), oq, "row codes")
+    assert_f32_bits_equal(si.cpu().numpy(), osi, "row scale_inv")
+    assert_f32_bits_equal(am.cpu().numpy(), oam, "row amax")
+    assert_codes_equal(qt.cpu().numpy(), oqt, "column codes")
+    assert_f32_bits_equal(sc.cpu().numpy(), osc, "column scale_inv")
+    assert_f32_bits_equal(ca.cpu().numpy(), oca, "column amax")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("shape", [(1, 8), (300, 520), (257, 1032), (70, 37), (5, 3)])
 def test_quantize_col_untransposed_parity(fp8, orc, fmt, shape):
     """transpose_out = 0: column scales with the codes in x's own layout (the
