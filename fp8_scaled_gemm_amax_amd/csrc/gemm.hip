@@ -1317,6 +1317,195 @@ __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restri
     wait_vmcnt<0>();
 }
 
+// Persistent ragged-K product (bf16 output, at most ragged::kMaxGroups
+// groups): the sums of k_grouped_gemm_ragged_k, with the persistent kernel's
+// overlap of one tile's epilogue and the next tile's first loads. Each
+// workgroup first builds the group table in LDS: padded K_g (-1 for a group
+// cut by the operands' width), its start P_g, and the groups ranked by
+// decreasing K_g (ties by index). Slot s = r * per8 + w then stands for tile w
+// of the group ranked r, w dealt to the XCDs as in k_grouped_gemm_ragged_k;
+// workgroup i takes slots i, i + G, i + 2G, .. (G = gridDim.x, a multiple of
+// 8, so a workgroup keeps to its XCD's share of every group). Dealing the
+// longest contractions first keeps the workgroups' total work even when the
+// group sizes are skewed. Edge tiles are shifted back as in k_gemm_persist.
+namespace ragged {
+constexpr int kMaxGroups = 256;
+}  // namespace ragged
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// One tile of the persistent ragged-K loop (every field wave-uniform).
+struct RaggedTile {
+    uint32_t slot;
+    int grp;
+    int32_t k;              // padded contraction length; 0: empty group, -1: cut
+    int64_t p;              // first contraction column
+    int64_t row0, col0;     // first loaded row / column
+    int row_lo, col_lo;     // first stored row / column, relative to row0 / col0
+};
+
+template <int FA, int FB>
+__global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k_persist(
+    const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb,
+    const int64_t* __restrict__ offsets, int G, int64_t total, int64_t m, int64_t n, const float* __restrict__ sa,
+    const float* __restrict__ sb, void* __restrict__ d, int64_t ldd, int64_t d_group_stride, int vec_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[persist::kSmem];
+    __shared__ int64_t g_start[ragged::kMaxGroups];
+    __shared__ int32_t g_k[ragged::kMaxGroups];
+    __shared__ int32_t g_by_rank[ragged::kMaxGroups];
+    const int t = threadIdx.x;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // group table (G <= 256 = the thread count)
+    int32_t kp = 0;
+    if (t < G) {
+        int64_t lo = offsets[t], hi = offsets[t + 1];
+        lo = lo < 0 ? 0 : (lo > total ? total : lo);
+        hi = hi < lo ? lo : (hi > total ? total : hi);
+        kp = (int32_t)((hi - lo + 255) / 256 * 256);
+    }
+    g_k[t] = kp;
+    __syncthreads();
+    int64_t pstart = 0;
+    for (int h = 0; h < t && h < G; ++h) pstart += g_k[h];
+    const int64_t lim = lda < ldb ? lda : ldb;
+    __syncthreads();                                     // every thread has read g_k
+    if (t < G) {
+        g_start[t] = pstart;
+        // a padded range past the operands' width would lose contraction columns
+        if (kp > 0 && pstart + kp > lim) g_k[t] = -1;
+    }
+    __syncthreads();
+    if (t < G) {
+        const int32_t kt = g_k[t];
+        int r = 0;
+        for (int h = 0; h < G; ++h) {
+            const int32_t kh = g_k[h];
+            r += (kh > kt) || (kh == kt && h < t);
+        }
+        g_by_rank[r] = t;
+    }
+    __syncthreads();
+
+    const uint32_t tiles_m = (uint32_t)((m + big::BM - 1) / big::BM), tiles_n = (uint32_t)((n + big::BN - 1) / big::BN);
+    const uint32_t per = tiles_m * tiles_n, per8 = (per + 7) / 8 * 8;
+    const uint32_t slots = (uint32_t)G * per8, gd = gridDim.x;
+    auto resolve = [&](uint32_t s, RaggedTile& tl) -> bool {
+        uint32_t tm = tiles_m, tn = tiles_n, p8 = per8;
+        asm volatile("" : "+s"(tm), "+s"(tn), "+s"(p8));
+        const uint32_t q = tm * tn / 8, rem = tm * tn % 8;
+        for (; s < slots; s += gd) {
+            const uint32_t r = s / p8, w = s % p8;
+            const uint32_t xcd = w % 8, idx = w / 8;
+            if (idx >= q + (xcd < rem ? 1u : 0u)) continue;
+            const uint32_t lt = xcd * q + (xcd < rem ? xcd : rem) + idx;
+            constexpr uint32_t gm = 4;
+            const uint32_t span = gm * tn;
+            const uint32_t first_m = lt / span * gm;
+            const uint32_t gsize = tm - first_m < gm ? tm - first_m : gm;
+            const uint32_t u = lt % span;
+            const int64_t pm = first_m + u % gsize, pn = u / gsize;
+            tl.slot = s;
+            tl.grp = __builtin_amdgcn_readfirstlane(g_by_rank[r]);
+            tl.k = __builtin_amdgcn_readfirstlane(g_k[tl.grp]);
+            tl.p = uniform64(g_start[tl.grp]);
+            const int64_t r0 = pm * big::BM, c0 = pn * big::BN;
+            tl.row0 = (r0 + big::BM > m && m >= big::BM) ? m - big::BM : r0;
+            tl.col0 = (c0 + big::BN > n && n >= big::BN) ? n - big::BN : c0;
+            tl.row_lo = (int)(r0 - tl.row0);
+            tl.col_lo = (int)(c0 - tl.col0);
+            return true;
+        }
+        return false;
+    };
+    RaggedTile cur;
+    if (!resolve(blockIdx.x, cur)) return;               // uniform over the workgroup
+    uint32_t aoff[8], boff[8];
+    k128_lane_offsets(aoff, lda, m);
+    k128_lane_offsets(boff, ldb, n);
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kScaleOff)) + wave * 256;
+    auto issue_scales = [&](const RaggedTile& tl) {
+        const int64_t r = tl.row0 + t, c = tl.col0 + t;
+        lds_dma4(sbase, sa + (int64_t)tl.grp * m + (r < m ? r : m - 1));
+        lds_dma4(sbase + 1024, sb + (int64_t)tl.grp * n + (c < n ? c : n - 1));
+    };
+    issue_scales(cur);
+    bool loaded = false;                                 // the stages hold cur's steps 0 and 1
+    v16f acc[4][4];
+    v8i f0[8];
+    u32x4 sx[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    for (;;) {
+        RaggedTile nxt;
+        const bool more = resolve(cur.slot + gd, nxt);
+        const uint8_t* at = a + cur.row0 * lda + cur.p;
+        const uint8_t* bt = b + cur.col0 * ldb + cur.p;
+        if (cur.k > 0 && !loaded) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem + s * k128::kStage)) + wave * 8192;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) lds_dma16_s(base + i * 1024, at + s * k128::BK, aoff[i]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) lds_dma16_s(base + k128::kOpBytes + i * 1024, bt + s * k128::BK, boff[i]);
+            }
+            wait_vmcnt<16>();                            // everything before step 1's loads landed
+            __syncthreads();
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                const int j = k128_frag(f);
+                f0[j] = big_join(k128_half<false>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 0),
+                                 k128_half<false>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 1));
+            }
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+        if (cur.k > 0) {
+            // steps p, p+1 load steps p+2, p+3; the last pair loads the next
+            // tile's steps 0 and 1 when it has a contraction (else this tile's
+            // own first steps again: valid addresses, never used)
+            const bool pre = more && nxt.k > 0;
+            const uint8_t* nat = pre ? a + nxt.row0 * lda + nxt.p : at;
+            const uint8_t* nbt = pre ? b + nxt.col0 * ldb + nxt.p : bt;
+            const int64_t nk = cur.k / k128::BK;         // even, >= 2
+            for (int64_t p = 0; p < nk; p += 2) {
+                const bool last = p + 2 >= nk;
+                const uint8_t* la = last ? nat : at;
+                const uint8_t* lb = last ? nbt : bt;
+                const int64_t kl = last ? 0 : (p + 2) * k128::BK;
+                k128_step<FA, FB, 0, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl, nullptr,
+                                                              nullptr, 0, 0);
+                k128_step<FA, FB, 1, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl + k128::BK,
+                                                              nullptr, nullptr, 0, 0);
+            }
+            loaded = pre;
+        } else {                                         // empty group: 0 * sa * sb (cut: NaN row scales)
+            wait_vmcnt<0>();
+            __syncthreads();                             // every thread's scale loads landed
+            if (cur.k < 0) {
+                reinterpret_cast<float*>(smem + big::kScaleOff)[t] = __builtin_nanf("");
+                __syncthreads();
+            }
+            loaded = false;
+        }
+        const int64_t rhi = m - cur.row0, chi = n - cur.col0;
+        uint8_t* dg = reinterpret_cast<uint8_t*>(d) + (int64_t)cur.grp * d_group_stride * 2;
+        chunk_epilogue<false>(smem, acc, dg, ldd, cur.row0, cur.row_lo, (int)(rhi < 256 ? rhi : 256), cur.col0,
+                              cur.col_lo, (int)(chi < 256 ? chi : 256), vec_out && cur.col0 % 8 == 0);
+        if (!more) break;
+        cur = nxt;
+        __syncthreads();                                 // every wavefront is done with the scale area
+        issue_scales(cur);                               // (landed by the next mid-step wait, or waited for above)
+    }
+    wait_vmcnt<0>();
+}
+
 template <int FA, int FB, bool OUT_F32>
 hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m, int64_t n, int64_t k,
                       const float* sa, int sa_vec, const float* sb, int sb_vec, void* d, int64_t ldd,
@@ -1405,6 +1594,16 @@ hipError_t ragged_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t
     const int64_t per = ((m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
     const int64_t grid = (int64_t)g * ((per + 7) / 8 * 8);
     const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0 && dgs % 8 == 0;
+    const int64_t cus = current_device_props().cus;
+    // bf16 output, at most 256 groups, more tiles than CUs: the persistent kernel
+    if constexpr (!OUT_F32) {
+        const int64_t slots = (int64_t)g * ((per + 7) / 8 * 8);
+        if (g <= ragged::kMaxGroups && cus >= 8 && slots > cus && slots < ((int64_t)1 << 31)) {
+            hipLaunchKernelGGL((k_grouped_gemm_ragged_k_persist<FA, FB>), dim3((unsigned)(cus / 8 * 8)), dim3(256), 0,
+                               st, a, lda, b, ldb, offsets, g, total, m, n, sa, sb, d, ldd, dgs, vec_out);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((k_grouped_gemm_ragged_k<FA, FB, OUT_F32>), dim3((unsigned)grid), dim3(256), 0, st, a, lda, b,
                        ldb, offsets, g, total, m, n, sa, sb, d, ldd, dgs, vec_out);
     return hipGetLastError();

@@ -203,6 +203,77 @@ def test_c4_moe_grouped(fp8, orc):
     assert rows == T
 
 
+def test_c4b_moe_backward(fp8, orc):
+    """The c4 expert layer's backward in the benchmark's launch configuration:
+    dY [16384 x 2048] rowwise e5m2; W^T, dY^T and X^T through the grouped
+    colwise cast (per-expert column scales, transposed into the 256-padded
+    grouped layout); dgrad dX_g = dY_g W_g as a grouped e5m2 x e4m3 product
+    over a strided view of W^T, wgrad dW_g = dY_g^T X_g as the ragged-K
+    product (the persistent kernel at this size). Every code and scale, every
+    output of both products."""
+    say("c4b generate")
+    w = workloads.c4b()
+    offsets = w["offsets"]
+    g, n, k = w["w"].shape
+    T = int(offsets[-1])
+    L = fp8.grouped_layout_width(T, g)
+    wflat = w["w"].reshape(g * n, k)
+    woff = np.arange(g + 1, dtype=np.int64) * n
+    off_d = torch.from_numpy(offsets).to("cuda:0")
+    say("c4b quantize")
+    dyq, dys, _, _ = row_quant(fp8, dev_bf16(w["dy"]), 1)
+    wt = torch.empty((k, g * n), dtype=torch.uint8, device="cuda:0")
+    wts, wta = torch.empty((g, k), device="cuda:0"), torch.empty((g, k), device="cuda:0")
+    fp8.fp8_grouped_quantize_col(dev_bf16(wflat), 0, 0, torch.from_numpy(woff).to("cuda:0"), wt, wts, wta)
+    dyt = torch.zeros((n, L), dtype=torch.uint8, device="cuda:0")
+    dyts, dyta = torch.empty((g, n), device="cuda:0"), torch.empty((g, n), device="cuda:0")
+    fp8.fp8_grouped_quantize_col(dev_bf16(w["dy"]), 1, 0, off_d, dyt, dyts, dyta)
+    xt = torch.zeros((k, L), dtype=torch.uint8, device="cuda:0")
+    xts, xta = torch.empty((g, k), device="cuda:0"), torch.empty((g, k), device="cuda:0")
+    fp8.fp8_grouped_quantize_col(dev_bf16(w["x"]), 0, 0, off_d, xt, xts, xta)
+    dx = torch.empty((T, k), dtype=torch.bfloat16, device="cuda:0")
+    fp8.fp8_grouped_gemm_scaled(dyq, 1, torch.as_strided(wt, (g, k, n), (n, g * n, 1)), 0, off_d, dys, wts, dx)
+    dw = torch.empty((g, n, k), dtype=torch.bfloat16, device="cuda:0")
+    fp8.fp8_grouped_gemm_ragged_k(dyt, 1, xt, 0, off_d, T, dyts, xts, dw)
+    torch.cuda.synchronize()
+    say("c4b oracle quantize")
+    oqdy, osdy, _ = orc.quantize_row(w["dy"], 1)
+    assert_codes_equal(dyq.cpu().numpy(), oqdy, "dY codes")
+    assert_f32_bits_equal(dys.cpu().numpy(), osdy, "dY scale_inv")
+    oqwt, oswt, oawt = orc.grouped_quantize_col(wflat, 0, woff, 256)
+    assert_codes_equal(wt.cpu().numpy(), oqwt, "W^T codes")
+    assert_f32_bits_equal(wts.cpu().numpy(), oswt, "W^T scale_inv")
+    assert_f32_bits_equal(wta.cpu().numpy(), oawt, "W^T amax")
+    oqdyt, osdyt, oadyt = orc.grouped_quantize_col(w["dy"], 1, offsets, 256)
+    assert oqdyt.shape[1] <= L
+    assert_codes_equal(dyt.cpu().numpy()[:, :oqdyt.shape[1]], oqdyt, "dY^T codes")
+    assert_f32_bits_equal(dyts.cpu().numpy(), osdyt, "dY^T scale_inv")
+    assert_f32_bits_equal(dyta.cpu().numpy(), oadyt, "dY^T amax")
+    oqxt, osxt, oaxt = orc.grouped_quantize_col(w["x"], 0, offsets, 256)
+    assert_codes_equal(xt.cpu().numpy()[:, :oqxt.shape[1]], oqxt, "X^T codes")
+    assert_f32_bits_equal(xts.cpu().numpy(), osxt, "X^T scale_inv")
+    assert_f32_bits_equal(xta.cpu().numpy(), oaxt, "X^T amax")
+    say("c4b dgrad check")
+    dxh = dx.float().cpu().numpy()
+    rows = 0
+    for e in range(g):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            bt = np.ascontiguousarray(oqwt[:, e * n:(e + 1) * n])          # W_e^T rows: [k x n]
+            rows += check_full(orc, dxh, orc.gemm_by_rows(oqdy[lo:hi], 1, bt, 0, osdy[lo:hi], oswt[e]),
+                               f"c4b dgrad expert {e}", row_offset=lo)
+    assert rows == T
+    say("c4b wgrad check")
+    P = np.concatenate([[0], np.cumsum((np.diff(offsets) + 255) // 256 * 256)])
+    for e in range(g):
+        if P[e + 1] > P[e]:
+            at = np.ascontiguousarray(oqdyt[:, P[e]:P[e + 1]])
+            bt = np.ascontiguousarray(oqxt[:, P[e]:P[e + 1]])
+            check_full(orc, dw[e], orc.gemm_by_rows(at, 1, bt, 0, osdyt[e], osxt[e]), f"c4b wgrad expert {e}")
+        else:
+            assert not dw[e].any().item(), f"empty expert {e}: dW is not zero"
+
+
 def test_c5_hybrid_backward(fp8, orc):
     """In the benchmark's launch configuration: dY [8192 x 14336] through the
     dual cast (e5m2 rowwise codes and colwise-transposed codes in two passes),

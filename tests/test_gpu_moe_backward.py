@@ -172,6 +172,45 @@ def test_grouped_gemm_ragged_k_parity(fp8, orc, sizes, m, n, fa, fb, out_f32):
             assert not got[g].any(), f"empty group {g} is not zero"
 
 
+PERSIST = [(40, 300, 520, 1, 0, 0, 11), (20, 100, 2100, 0, 0, 0, 12), (48, 512, 520, 1, 0, 1, 13)]
+
+
+@pytest.mark.parametrize("g,m,n,fa,fb,cut,seed", PERSIST, ids=["shifted_edges", "m_below_tile", "cut_groups"])
+def test_grouped_gemm_ragged_k_many_tiles_parity(fp8, orc, g, m, n, fa, fb, cut, seed):
+    """More tile slots than CUs (the persistent kernel, tiles dealt longest
+    contraction first): skewed group sizes with empty groups and sizes on and
+    off the 256 boundary; m, n off the 256 tile (edge tiles shifted back) or
+    m < 256 (loads clamped). With cut, the operands end 512 columns short of
+    the padded layout: the groups whose range fits are within the bound, the
+    ones that would lose columns are NaN. Every output of every group checked."""
+    rng = np.random.default_rng(seed)
+    sizes = rng.integers(0, 700, g)
+    sizes[::7] = 0
+    sizes[1], sizes[2], sizes[3], sizes[4] = 3000, 256, 257, 1
+    offsets = offsets_of(sizes)
+    T = int(offsets[-1])
+    a_t, sa, _ = orc.grouped_quantize_col(rand_bf16(T, m, seed), fa, offsets, ALIGN)
+    b_t, sb, _ = orc.grouped_quantize_col(rand_bf16(T, n, seed + 1), fb, offsets, ALIGN)
+    kp = (sizes + ALIGN - 1) // ALIGN * ALIGN
+    starts = np.concatenate([[0], np.cumsum(kp)[:-1]])
+    cut_groups = np.zeros(g, bool)
+    if cut:
+        width = max((T + 15) // 16 * 16, int(a_t.shape[1]) - 512)
+        a_t, b_t = np.ascontiguousarray(a_t[:, :width]), np.ascontiguousarray(b_t[:, :width])
+        cut_groups = (kp > 0) & (starts + kp > width)
+        assert cut_groups.any() and not cut_groups.all()
+    say("ragged k many tiles", g, m, n, fa, fb, "cut" if cut else "")
+    got = gpu_ragged(fp8, a_t, fa, b_t, fb, offsets, sa, sb)
+    full_a, _, _ = orc.grouped_quantize_col(rand_bf16(T, m, seed), fa, offsets, ALIGN)
+    full_b, _, _ = orc.grouped_quantize_col(rand_bf16(T, n, seed + 1), fb, offsets, ALIGN)
+    y, bound = orc.grouped_gemm_ragged_k(full_a, fa, full_b, fb, offsets, ALIGN, sa, sb)
+    keep = ~cut_groups
+    assert_within(orc, got[keep], y[keep], bound[keep], True, f"ragged many tiles {g} {m} {n}")
+    assert np.isnan(got[cut_groups]).all(), "a cut group is not NaN"
+    for e in np.flatnonzero(sizes == 0):
+        assert not got[e].any(), f"empty group {e} is not zero"
+
+
 def test_grouped_gemm_ragged_k_short_operands_give_nan(fp8, orc):
     """Operands narrower than the grouped layout (lda = ldb below P_G, still >=
     total_m): the groups whose padded range fits are exact within the bound,
