@@ -236,14 +236,33 @@ class Step:
             self.dyts, self.dyta = E((g, n), device=dev), E((g, n), device=dev)
             self.xts, self.xta = E((g, k), device=dev), E((g, k), device=dev)
             self.dw = E((g, n, k), dtype=torch.bfloat16, device=dev)
+            # the forward's rowwise cast of the tokens X and the expert weights W
+            # left their per-group column amax as side outputs (token groups,
+            # and each expert's n weight rows): the backward's grouped colwise
+            # casts of X^T and W^T take them as ready
+            qx, qw = E((t, k), dtype=torch.uint8, device=dev), E((g * n, k), dtype=torch.uint8, device=dev)
+            fp8.fp8_quantize_row_batch([self.x, self.w], fp8.E4M3, 0, [qx, qw], [E(t, device=dev), E(g * n, device=dev)],
+                                       None, [self.xta, self.wta], [self.offsets, self.woffsets])
+            torch.cuda.synchronize()
+            del qx, qw
             self.mnk = [(t, k, n), (n, k, t)]
-            self.calls = [("quantize_row dY e5m2", t * n, t), ("grouped_quantize_col W^T e4m3", g * n * k, g * k),
-                          ("grouped_quantize_col dY^T e5m2", t * n, g * n),
-                          ("grouped_quantize_col X^T e4m3", t * k, g * k),
-                          ("grouped_gemm dgrad", None, 0), ("grouped_gemm_ragged_k wgrad", None, 0)]
+            # dY^T right after dY's row cast (dY still in the last-level cache),
+            # each product right after the casts it reads
+            self.calls = [("quantize_row dY e5m2 with per-expert column amax (clear + one pass)", t * n, t,
+                           3.0 * t * n + 4.0 * t + 4.0 * g * n),
+                          ("grouped_quantize_col dY^T e5m2 (column amax from the row cast)", t * n, g * n,
+                           3.0 * t * n + 8.0 * g * n),
+                          ("grouped_quantize_col W^T e4m3 (column amax from the forward)", g * n * k, g * k,
+                           3.0 * g * n * k + 8.0 * g * k),
+                          ("grouped_gemm dgrad", None, 0),
+                          ("grouped_quantize_col X^T e4m3 (column amax from the forward)", t * k, g * k,
+                           3.0 * t * k + 8.0 * g * k),
+                          ("grouped_gemm_ragged_k wgrad", None, 0)]
             self.desc = ("DeepSeek-V3 MoE expert layer backward, one GPU's share: c4's experts and tokens, "
                          "dY bf16 [16384x2048] N(0,1e-3^2) e5m2; dgrad dX_g = dY_g W_g (grouped GEMM), "
-                         "wgrad dW_g = dY_g^T X_g over each expert's tokens (ragged-K grouped GEMM); bf16 out")
+                         "wgrad dW_g = dY_g^T X_g over each expert's tokens (ragged-K grouped GEMM); per-expert "
+                         "column amax of X and W from the forward cast's side outputs, of dY from its row cast; "
+                         "bf16 out")
             self.scales = {"recipe": "rowwise+grouped colwise", "format": "e5m2 x e4m3"}
         else:
             w = workloads.c5()
@@ -378,16 +397,19 @@ class Step:
             ev[8].record()
         elif self.name == "c4b":
             g, n, k = self.g, self.n, self.k
-            f.fp8_quantize_row(self.dy, f.E5M2, 0, self.dyq, self.dys)
+            f.fp8_quantize_row_batch([self.dy], f.E5M2, 0, [self.dyq], [self.dys], None, [self.dyta], [self.offsets])
             ev[1].record()
-            f.fp8_grouped_quantize_col(self.w, f.E4M3, 0, self.woffsets, self.wt, self.wts, self.wta)
+            f.fp8_grouped_quantize_col(self.dy, f.E5M2, 0, self.offsets, self.dyt, self.dyts, self.dyta,
+                                       col_amax_ready=True)
             ev[2].record()
-            f.fp8_grouped_quantize_col(self.dy, f.E5M2, 0, self.offsets, self.dyt, self.dyts, self.dyta)
+            f.fp8_grouped_quantize_col(self.w, f.E4M3, 0, self.woffsets, self.wt, self.wts, self.wta,
+                                       col_amax_ready=True)
             ev[3].record()
-            f.fp8_grouped_quantize_col(self.x, f.E4M3, 0, self.offsets, self.xt, self.xts, self.xta)
-            ev[4].record()
             b_view = self.torch.as_strided(self.wt, (g, k, n), (n, g * n, 1))   # expert g: columns g*n.. of W^T
             f.fp8_grouped_gemm_scaled(self.dyq, f.E5M2, b_view, f.E4M3, self.offsets, self.dys, self.wts, self.dx)
+            ev[4].record()
+            f.fp8_grouped_quantize_col(self.x, f.E4M3, 0, self.offsets, self.xt, self.xts, self.xta,
+                                       col_amax_ready=True)
             ev[5].record()
             f.fp8_grouped_gemm_ragged_k(self.dyt, f.E5M2, self.xt, f.E4M3, self.offsets, self.t, self.dyts, self.xts,
                                         self.dw)

@@ -73,7 +73,7 @@ def _load():
         "fp8_amax": [P, I64, I64, I64, I, P, P],
         "fp8_quantize_tensor": [P, I64, I64, I64, I, I32, P, P, I64, P, P, P],
         "fp8_quantize_row": [P, I64, I64, I64, I, I32, P, I64, P, P, P, P],
-        "fp8_quantize_row_batch": [I32, P, P, I64, P, I, I32, P, P, P, P, P, P],
+        "fp8_quantize_row_batch": [I32, P, P, I64, P, I, I32, P, P, P, P, P, P, P, P],
         "fp8_quantize_tensor_batch": [I32, P, P, I64, P, I, P, P, P, P, P, P],
         "fp8_quantize_col": [P, I64, I64, I64, I, I32, I32, P, I64, P, P, I32, P],
         "fp8_quantize_rowcol": [P, I64, I64, I64, I, I32, P, I64, P, P, P, I64, P, P, P],
@@ -173,13 +173,19 @@ def fp8_quantize_row(x, fmt, margin, q, scale_inv_out, amax_out=None, col_amax_o
                                 _ptr(amax_out), _ptr(col_amax_out), _stream(x)))
 
 
-def fp8_quantize_row_batch(xs, fmt, margin, qs, scale_inv_outs, amax_outs=None, col_amax_outs=None):
+def fp8_quantize_row_batch(xs, fmt, margin, qs, scale_inv_outs, amax_outs=None, col_amax_outs=None,
+                           col_group_offsets=None):
     """Rowwise casts of the bf16 tensors xs (same number of columns) in one
-    launch; col_amax_outs[j] (fp32 [cols] or None) receives tensor j's column amax."""
+    launch; col_amax_outs[j] (fp32 [cols] or None) receives tensor j's column
+    amax. With col_group_offsets[j] (a device int64 tensor [G + 1], or None),
+    col_amax_outs[j] is fp32 [G x cols] and receives the column amax of each
+    group of rows."""
     count = len(xs)
     if not (len(qs) == len(scale_inv_outs) == count) or (amax_outs is not None and len(amax_outs) != count) or (
-            col_amax_outs is not None and len(col_amax_outs) != count):
-        raise ValueError("xs, qs, scale_inv_outs (and amax_outs, col_amax_outs) must have the same length")
+            col_amax_outs is not None and len(col_amax_outs) != count) or (
+            col_group_offsets is not None and len(col_group_offsets) != count):
+        raise ValueError("xs, qs, scale_inv_outs (and amax_outs, col_amax_outs, col_group_offsets) must have the "
+                         "same length")
     if count == 0:
         raise ValueError("no tensors")
     shapes = [_bf16(x) for x in xs]
@@ -195,7 +201,14 @@ def fp8_quantize_row_batch(xs, fmt, margin, qs, scale_inv_outs, amax_outs=None, 
     sp = PP(*[_ptr(s) for s in scale_inv_outs])
     ap = PP(*[_ptr(a) for a in amax_outs]) if amax_outs is not None else None
     cp = PP(*[_ptr(c) for c in col_amax_outs]) if col_amax_outs is not None else None
-    _check(lib.fp8_quantize_row_batch(count, xp, rows, cols, ldx, fmt, margin, qp, ldq, sp, ap, cp,
+    gp, gn = None, None
+    if col_group_offsets is not None:
+        for o in col_group_offsets:
+            if o is not None and (o.dtype != torch.int64 or o.dim() != 1 or o.numel() < 2 or not o.is_contiguous()):
+                raise ValueError("col_group_offsets entries are contiguous int64 tensors [G + 1]")
+        gp = PP(*[_ptr(o) for o in col_group_offsets])
+        gn = (ctypes.c_int32 * count)(*[o.numel() - 1 if o is not None else 0 for o in col_group_offsets])
+    _check(lib.fp8_quantize_row_batch(count, xp, rows, cols, ldx, fmt, margin, qp, ldq, sp, ap, cp, gp, gn,
                                       _stream(xs[0])))
 
 

@@ -246,7 +246,7 @@ fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int
     hipStream_t st = (hipStream_t)stream;
     if (col_amax_out)       // the column amax as a side output of the same pass (a batch of one)
         return launched(launch_quant_row_batch(1, &x, &rows, cols, &ldx, (int)fmt, margin, &q, &ldq, &scale_inv_out,
-                                               &amax_out, &col_amax_out, st),
+                                               &amax_out, &col_amax_out, nullptr, nullptr, st),
                         fn);
     return launched(launch_quant_row(x, rows, cols, ldx, (int)fmt, margin, q, ldq, scale_inv_out, amax_out, false, st),
                     fn);
@@ -255,7 +255,8 @@ fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int
 fp8_status_t fp8_quantize_row_batch(int32_t count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
                                     const int64_t* ldx, fp8_format_t fmt, int32_t margin, uint8_t* const* q,
                                     const int64_t* ldq, float* const* scale_inv_out, float* const* amax_out,
-                                    float* const* col_amax_out, void* stream) {
+                                    float* const* col_amax_out, const int64_t* const* col_group_offsets,
+                                    const int32_t* col_groups, void* stream) {
     const char* fn = "fp8_quantize_row_batch";
     if (count < 1 || count > FP8_MAX_ROW_BATCH)
         return fail(FP8_ERR_INVALID_ARG, "%s: count %d outside 1..%d", fn, (int)count, FP8_MAX_ROW_BATCH);
@@ -269,9 +270,32 @@ fp8_status_t fp8_quantize_row_batch(int32_t count, const uint16_t* const* x, con
             (col_amax_out && !aligned(col_amax_out[j], 4)))
             return fail(FP8_ERR_ALIGNMENT, "%s: misaligned fp32 pointer (tensor %d)", fn, j);
     }
+    bool grouped = false;
+    for (int j = 0; j < count && col_groups; ++j) {
+        if (col_groups[j] < 0 || col_groups[j] > 4096)
+            return fail(FP8_ERR_INVALID_ARG, "%s: col_groups[%d] = %d outside 0..4096", fn, j, (int)col_groups[j]);
+        if (col_groups[j] == 0) continue;
+        grouped = true;
+        if (!col_amax_out || !col_amax_out[j])
+            return fail(FP8_ERR_INVALID_ARG, "%s: tensor %d has column groups but no col_amax_out", fn, j);
+        if (!col_group_offsets || !col_group_offsets[j])
+            return fail(FP8_ERR_INVALID_ARG, "%s: col_group_offsets[%d] is NULL", fn, j);
+        if (!aligned(col_group_offsets[j], 8))
+            return fail(FP8_ERR_ALIGNMENT, "%s: col_group_offsets[%d] must be 8-byte aligned", fn, j);
+    }
+    if (grouped) {      // the single-pass kernel only: every tensor in the vector layout, rows <= 16384 columns
+        if (cols > 16384)
+            return fail(FP8_ERR_UNSUPPORTED, "%s: grouped column amax needs cols <= 16384 (cols = %lld)", fn,
+                        (long long)cols);
+        for (int j = 0; j < count; ++j)
+            if (cols % 8 != 0 || ldx[j] % 8 != 0 || ldq[j] % 8 != 0 || !aligned(x[j], 16) || !aligned(q[j], 8))
+                return fail(FP8_ERR_ALIGNMENT, "%s: grouped column amax needs every tensor's x 16-byte and q 8-byte "
+                            "aligned, ldx, ldq, cols multiples of 8 (tensor %d)", fn, j);
+    }
     FP8_TRY(check_device());
     return launched(launch_quant_row_batch(count, x, rows, cols, ldx, (int)fmt, margin, q, ldq, scale_inv_out,
-                                           amax_out, col_amax_out, (hipStream_t)stream),
+                                           amax_out, col_amax_out, grouped ? col_group_offsets : nullptr,
+                                           grouped ? col_groups : nullptr, (hipStream_t)stream),
                     fn);
 }
 

@@ -30,7 +30,7 @@ hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64
 hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
                                   const int64_t* ldx, int fmt, int margin, uint8_t* const* q, const int64_t* ldq,
                                   float* const* scale_inv, float* const* amax_out, float* const* col_amax,
-                                  hipStream_t st);
+                                  const int64_t* const* col_groups, const int32_t* ngroups, hipStream_t st);
 
 // transpose: codes written transposed (qt [cols x rows]) or in x's layout (q [rows x cols]).
 hipError_t launch_quant_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, int margin,

@@ -402,6 +402,9 @@ struct RowBatch {
     float* scale_inv[kMaxRowBatch];
     float* amax[kMaxRowBatch];
     float* col_amax[kMaxRowBatch];   // column-amax side outputs (k_quant_row_colmax only; may be NULL)
+    const int64_t* groups[kMaxRowBatch];   // row groups of the column amax (device offsets [ngroups + 1])
+    int ngroups[kMaxRowBatch];             // 0: one column amax over all rows
+    int64_t cam_first[kMaxRowBatch + 1];   // prefix sums of the column-amax sizes (k_fill_col_amax)
     int64_t rows[kMaxRowBatch];
     int64_t ldx[kMaxRowBatch];
     int64_t ldq[kMaxRowBatch];
@@ -454,6 +457,13 @@ __global__ __launch_bounds__(kBlock) void k_quant_row_batch(RowBatch b, int64_t 
 // each column is folded into col_amax[j] (cleared beforehand) by one relaxed
 // atomic max per workgroup, skipped where the workgroup saw only zeros: with
 // one workgroup per CU the atomics stay few (one per column per CU).
+// Grouped column amax (ngroups[j] = G > 0: the per-group column amax that a
+// later grouped colwise cast of the same tensor takes as ready, e.g. MoE
+// tokens sorted by expert): each workgroup takes a contiguous band of rows
+// instead, cut where a group ends; after each piece its maxima go to
+// col_amax[j][g * cols + c] of that piece's group g and LDS is cleared for the
+// next. Rows of no group (before offsets[0] or past offsets[G]) are cast but
+// fold nowhere.
 template <int MAXC>
 __device__ __forceinline__ void load_row_chunks(uint4 (&v)[MAXC], const uint16_t* __restrict__ x, int64_t row,
                                                 int64_t ldx, int nch) {
@@ -524,7 +534,7 @@ __device__ __forceinline__ void fold_chunks_lds(const uint4 (&w)[MAXC], uint32_t
     }
 }
 
-template <int F, int MAXC, int WAVES, bool REG, bool PREF>
+template <int F, int MAXC, int WAVES, bool REG, bool PREF, bool GROUPED>
 __global__ __launch_bounds__(WAVES * 64) void k_quant_row_colmax(RowBatch b, int64_t cols, int margin) {
     constexpr int kCols = MAXC * 64 * 8;                 // columns a row of MAXC chunks per lane can hold
     __shared__ uint32_t red[kCols];
@@ -555,6 +565,82 @@ __global__ __launch_bounds__(WAVES * 64) void k_quant_row_colmax(RowBatch b, int
     uint4 cm[MAXC];
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) cm[c] = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (GROUPED) {
+        // every tensor of the batch by bands; an ungrouped column amax is one
+        // group of all rows, a tensor without column amax has no group
+        const int64_t* off = batch_pick(b.groups, j);
+        const int G = cam ? (batch_pick(b.ngroups, j) > 0 ? batch_pick(b.ngroups, j) : 1) : 0;
+        auto start = [&](int g) {                        // offsets[g] clamped to [0, rows]
+            if (off == nullptr) return g == 0 && G > 0 ? (int64_t)0 : rows;
+            const int64_t v = off[g];
+            return v < 0 ? 0 : (v > rows ? rows : v);
+        };
+        const int64_t band = (rows + (next - first) - 1) / (next - first);
+        const int64_t lo = (bid - first) * band;
+        const int64_t hi = lo + band < rows ? lo + band : rows;
+        for (int64_t s = lo; s < hi;) {
+            // the piece [s, e): rows of group g (the last whose start is <= s)
+            // up to its end, or rows of no group (g = -1) up to the next start
+            int glo = -1, ghi = G;
+            while (ghi - glo > 1) {
+                const int mid = (glo + ghi) >> 1;
+                if (start(mid) <= s)
+                    glo = mid;
+                else
+                    ghi = mid;
+            }
+            int g = glo;
+            int64_t e;
+            if (g >= 0 && start(g + 1) > s) {
+                e = start(g + 1) < hi ? start(g + 1) : hi;
+            } else {
+                const int64_t nx = start(g + 1);
+                e = nx > s && nx < hi ? nx : hi;
+                g = -1;
+            }
+            for (int64_t r = s + wave; r < e; r += WAVES) {
+                uint4 cur[MAXC];
+                load_row_chunks<MAXC>(cur, x, r, ldx, nch);
+                cast_row_chunks<F, MAXC>(cur, r, nch, margin, q, ldq, si, am, b.nt_store);
+#pragma unroll
+                for (int c = 0; c < MAXC; ++c) {
+                    cur[c].x &= 0x7fff7fffu;
+                    cur[c].y &= 0x7fff7fffu;
+                    cur[c].z &= 0x7fff7fffu;
+                    cur[c].w &= 0x7fff7fffu;
+                }
+                if constexpr (REG) {
+#pragma unroll
+                    for (int c = 0; c < MAXC; ++c) {
+                        cm[c].x = pk_absmax(cm[c].x, cur[c].x);
+                        cm[c].y = pk_absmax(cm[c].y, cur[c].y);
+                        cm[c].z = pk_absmax(cm[c].z, cur[c].z);
+                        cm[c].w = pk_absmax(cm[c].w, cur[c].w);
+                    }
+                } else if (g >= 0) {
+                    fold_chunks_lds<MAXC>(cur, red, nch);
+                }
+            }
+            if (g >= 0) {                                // (uniform)
+                if constexpr (REG) fold_chunks_lds<MAXC>(cm, red, nch);
+                __syncthreads();
+                float* cg = cam + (int64_t)g * cols;
+                for (int i = threadIdx.x; i < cols; i += WAVES * 64) {
+                    const int k = (i & 7) * (MAXC * 64) + (i >> 3);
+                    const uint32_t v32 = red[k];
+                    if (v32 != 0u) {
+                        atomic_max_bits(cg + i, v32);
+                        red[k] = 0u;
+                    }
+                }
+                __syncthreads();                         // LDS clear before the next piece folds
+            }
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) cm[c] = make_uint4(0u, 0u, 0u, 0u);
+            s = e;
+        }
+        return;
+    }
     int64_t row = (bid - first) * WAVES + wave;
     uint4 v[MAXC];
     if (PREF && row < rows) load_row_chunks<MAXC>(v, x, row, ldx, nch);
@@ -600,13 +686,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_quant_row_colmax(RowBatch b, int
     }
 }
 
-// Clears the column-amax outputs of a batch (count x cols floats) in one launch.
-__global__ void k_fill_col_amax(RowBatch b, int64_t cols) {
-    const int64_t n = (int64_t)b.count * cols;
+// Clears the column-amax outputs of a batch in one launch (tensor j's
+// cam_first[j + 1] - cam_first[j] floats: cols, or G * cols when grouped).
+__global__ void k_fill_col_amax(RowBatch b) {
+    const int64_t n = b.cam_first[b.count];
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const int j = (int)(i / cols);
+        int j = 0;
+#pragma unroll
+        for (int t = 1; t < kMaxRowBatch; ++t)
+            if (t < b.count && i >= b.cam_first[t]) j = t;
         float* cam = batch_pick(b.col_amax, j);
-        if (cam) cam[i - (int64_t)j * cols] = 0.0f;
+        int64_t f = b.cam_first[0];
+#pragma unroll
+        for (int t = 1; t < kMaxRowBatch; ++t)
+            if (t == j) f = b.cam_first[t];
+        if (cam) cam[i - f] = 0.0f;
     }
 }
 
@@ -786,7 +880,6 @@ struct TensorBatch {
     const float* scale[kMaxRowBatch];
     float* scale_inv[kMaxRowBatch];
     float* amax[kMaxRowBatch];
-    float* col_amax[kMaxRowBatch];   // column-amax side outputs (k_quant_row_colmax only; may be NULL)
     int64_t rows[kMaxRowBatch];
     int64_t ldx[kMaxRowBatch];
     int64_t ldq[kMaxRowBatch];
@@ -1338,7 +1431,8 @@ __global__ __launch_bounds__(kBlock) void k_grouped_quant_col_tiled(const uint16
                                                                     const int64_t* __restrict__ off, int G,
                                                                     uint8_t* __restrict__ qt, int64_t ldqt,
                                                                     const float* __restrict__ col_amax,
-                                                                    int vec_store, int skip_small) {
+                                                                    float* __restrict__ scale_inv, int vec_store,
+                                                                    int skip_small) {
     __shared__ float s_lds[kColTileC];
     __shared__ int nan_lds[kColTileC];
     __shared__ __attribute__((aligned(16))) uint32_t tile[kColTileC * kColTileR / 4];
@@ -1371,6 +1465,15 @@ __global__ __launch_bounds__(kBlock) void k_grouped_quant_col_tiled(const uint16
     }
     if (t == kBlock - 1) pre[G] = run;
     __syncthreads();
+    const int64_t c0 = (int64_t)blockIdx.y * kColTileC;
+    // scale_inv of the empty groups (no row tile visits them), by the first
+    // workgroup of each column tile; with skip_small the one-pass kernel wrote them
+    if (blockIdx.x == 0 && !skip_small) {
+        const int64_t c = c0 + (t & 63);
+        for (int g = t >> 6; g < G; g += kWaves)
+            if (pre[g + 1] == pre[g] && c < cols)
+                scale_inv[(int64_t)g * cols + c] = 1.0f / scale_from_amax<F>(col_amax[(int64_t)g * cols + c], margin);
+    }
     // row tiles y = blockIdx.x, blockIdx.x + gridDim.x, .. (uniform over the workgroup)
     for (int32_t y = (int32_t)blockIdx.x; y < pre[G]; y += (int32_t)gridDim.x) {
         int glo = 0, ghi = G;                            // pre[glo] <= y < pre[ghi]
@@ -1387,8 +1490,9 @@ __global__ __launch_bounds__(kBlock) void k_grouped_quant_col_tiled(const uint16
         group_rows(off, g, total, &lo, &hi);
         if (skip_small && hi - lo <= kSmallGroupRows) continue;   // (done by the one-pass kernel)
         __syncthreads();                                 // the previous tile's LDS reads are done
-        const int64_t c0 = (int64_t)blockIdx.y * kColTileC;
-        col_scales_to_lds<F>(col_amax + (int64_t)g * cols, c0, cols, margin, nullptr, s_lds, nan_lds);
+        // (the group's first row tile also writes its scale_inv)
+        col_scales_to_lds<F>(col_amax + (int64_t)g * cols, c0, cols, margin,
+                             tt == 0 ? scale_inv + (int64_t)g * cols : nullptr, s_lds, nan_lds);
         const int64_t d0 = (int64_t)pre[g] * kColTileR + tt * kColTileR;
         col_tile<F>(x, ldx, lo + tt * kColTileR, hi, true, c0, cols, s_lds, nan_lds, tile, qt, ldqt, d0, ldqt,
                     vec_store);
@@ -1958,31 +2062,45 @@ hipError_t quant_row_batch_fmt(const RowBatch& b, int64_t blocks, int64_t cols, 
 struct ColmaxShape {
     int waves, wg_per_cu;
 };
-ColmaxShape colmax_shape(int64_t per_lane) {
+ColmaxShape colmax_shape(int64_t per_lane, bool grouped) {
     if (per_lane > 8) return {4, 1};        // 16, 32 chunks: the row and its running max fill a SIMD's registers
+    // grouped: one workgroup of 16 wavefronts per CU (a quarter of the
+    // per-group flushes of four workgroups of 4; the MoE backward's dY,
+    // 16384 x 2048: 35 -> 30 us; two rows in flight per wavefront, or two
+    // workgroups of 8, were slower); rows of 8 chunks per lane would not fit
+    // 16 wavefronts' registers: two workgroups of 8
+    if (grouped) return per_lane > 4 ? ColmaxShape{8, 2} : ColmaxShape{16, 1};
     return {4, 4};
 }
 template <int F>
-hipError_t quant_row_colmax_fmt(const RowBatch& b, int64_t blocks, int64_t cols, int margin, hipStream_t st) {
+hipError_t quant_row_colmax_fmt(const RowBatch& b, int64_t blocks, int64_t cols, int margin, int waves,
+                                bool grouped, hipStream_t st) {
     const int64_t per_lane = (cols / 8 + 63) / 64;
     // clear every requested column amax (one launch), then the single pass
-    hipLaunchKernelGGL(k_fill_col_amax, dim3((unsigned)((b.count * cols + kBlock - 1) / kBlock < 1024
-                                                            ? (b.count * cols + kBlock - 1) / kBlock : 1024)),
-                       dim3(kBlock), 0, st, b, cols);
+    const int64_t nfill = b.cam_first[b.count];
+    hipLaunchKernelGGL(k_fill_col_amax, dim3((unsigned)((nfill + kBlock - 1) / kBlock < 1024
+                                                            ? (nfill + kBlock - 1) / kBlock : 1024)),
+                       dim3(kBlock), 0, st, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-#define FP8_ROW_COLMAX_CASE(C, W, REG, PREF)                                                                       \
-    if (per_lane <= C) {                                                                                           \
-        hipLaunchKernelGGL((k_quant_row_colmax<F, C, W, REG, PREF>), dim3((unsigned)blocks), dim3(W * 64), 0, st, b,  \
-                           cols, margin);                                                                          \
+#define FP8_ROW_COLMAX_CASE(C, W, REG, PREF, GR)                                                                   \
+    if (per_lane <= C && waves == W && grouped == GR) {                                                            \
+        hipLaunchKernelGGL((k_quant_row_colmax<F, C, W, REG, PREF, GR>), dim3((unsigned)blocks), dim3(W * 64), 0, st, \
+                           b, cols, margin);                                                                       \
         return hipGetLastError();                                                                                  \
     }
-    FP8_ROW_COLMAX_CASE(1, 4, true, false)
-    FP8_ROW_COLMAX_CASE(2, 4, true, false)
-    FP8_ROW_COLMAX_CASE(4, 4, true, false)
-    FP8_ROW_COLMAX_CASE(8, 4, true, false)
-    FP8_ROW_COLMAX_CASE(16, 4, true, false)
-    FP8_ROW_COLMAX_CASE(32, 4, true, false)
+    FP8_ROW_COLMAX_CASE(1, 4, true, false, false)
+    FP8_ROW_COLMAX_CASE(2, 4, true, false, false)
+    FP8_ROW_COLMAX_CASE(4, 4, true, false, false)
+    FP8_ROW_COLMAX_CASE(8, 4, true, false, false)
+    FP8_ROW_COLMAX_CASE(16, 4, true, false, false)
+    FP8_ROW_COLMAX_CASE(32, 4, true, false, false)
+    FP8_ROW_COLMAX_CASE(1, 16, true, false, true)
+    FP8_ROW_COLMAX_CASE(2, 16, true, false, true)
+    FP8_ROW_COLMAX_CASE(4, 16, true, false, true)
+    FP8_ROW_COLMAX_CASE(8, 8, true, false, true)
+    FP8_ROW_COLMAX_CASE(16, 4, true, false, true)
+    FP8_ROW_COLMAX_CASE(32, 4, false, false, true)     // (a running max of 32 chunks would not fit beside the row)
 #undef FP8_ROW_COLMAX_CASE
     return hipErrorInvalidValue;   // (the caller checked per_lane <= 32)
 }
@@ -1990,9 +2108,12 @@ hipError_t quant_row_colmax_fmt(const RowBatch& b, int64_t blocks, int64_t cols,
 hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
                                   const int64_t* ldx, int fmt, int margin, uint8_t* const* q, const int64_t* ldq,
                                   float* const* scale_inv, float* const* amax_out, float* const* col_amax,
-                                  hipStream_t st) {
-    bool any_col = false;
-    for (int j = 0; j < count && col_amax; ++j) any_col = any_col || col_amax[j] != nullptr;
+                                  const int64_t* const* col_groups, const int32_t* ngroups, hipStream_t st) {
+    bool any_col = false, any_grouped = false;
+    for (int j = 0; j < count && col_amax; ++j) {
+        any_col = any_col || col_amax[j] != nullptr;
+        any_grouped = any_grouped || (col_amax[j] && ngroups && ngroups[j] > 0);
+    }
     // one launch when every tensor takes the register kernel (vector layout,
     // rows of at most 32 chunks per lane); otherwise one launch per tensor
     // (and a separate column-amax pass per tensor that asks for it)
@@ -2003,6 +2124,7 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
         total_rows += rows[j];
     }
     one = one && total_rows / kWaves < ((int64_t)1 << 31) - kMaxRowBatch;    // the grid's x extent
+    if (!one && any_grouped) return hipErrorInvalidValue;   // (the caller checked the layouts)
     if (!one) {
         for (int j = 0; j < count; ++j) {
             float* ca = any_col ? col_amax[j] : nullptr;
@@ -2018,7 +2140,7 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
     b.nt_store = streamed_codes(total_rows * cols);
     // with column amax: a few workgroups per CU in all (colmax_shape), dealt to
     // the tensors in proportion to their rows (each striding over its rows)
-    const ColmaxShape shape = colmax_shape((cols / 8 + 63) / 64);
+    const ColmaxShape shape = colmax_shape((cols / 8 + 63) / 64, any_grouped);
     const int64_t waves = shape.waves;
     const int64_t target = (int64_t)current_device_props().cus * shape.wg_per_cu;
     int64_t blocks = 0;
@@ -2028,6 +2150,10 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
         b.scale_inv[j] = scale_inv[j];
         b.amax[j] = amax_out ? amax_out[j] : nullptr;
         b.col_amax[j] = any_col ? col_amax[j] : nullptr;
+        const int gj = any_col && ngroups ? ngroups[j] : 0;
+        b.groups[j] = gj > 0 ? col_groups[j] : nullptr;
+        b.ngroups[j] = gj > 0 ? gj : 0;
+        b.cam_first[j + 1] = b.cam_first[j] + cols * (gj > 0 ? gj : 1);
         b.rows[j] = rows[j];
         b.ldx[j] = ldx[j];
         b.ldq[j] = ldq[j];
@@ -2042,12 +2168,13 @@ hipError_t launch_quant_row_batch(int count, const uint16_t* const* x, const int
         }
     }
     for (int j = count; j <= kMaxRowBatch; ++j) b.first[j] = blocks;
+    for (int j = count + 1; j <= kMaxRowBatch; ++j) b.cam_first[j] = b.cam_first[count];
     if (any_col) {
         switch (fmt) {
-            case kE4M3: return quant_row_colmax_fmt<kE4M3>(b, blocks, cols, margin, st);
-            case kE5M2: return quant_row_colmax_fmt<kE5M2>(b, blocks, cols, margin, st);
-            case kE4M3Fnuz: return quant_row_colmax_fmt<kE4M3Fnuz>(b, blocks, cols, margin, st);
-            default: return quant_row_colmax_fmt<kE5M2Fnuz>(b, blocks, cols, margin, st);
+            case kE4M3: return quant_row_colmax_fmt<kE4M3>(b, blocks, cols, margin, (int)waves, any_grouped, st);
+            case kE5M2: return quant_row_colmax_fmt<kE5M2>(b, blocks, cols, margin, (int)waves, any_grouped, st);
+            case kE4M3Fnuz: return quant_row_colmax_fmt<kE4M3Fnuz>(b, blocks, cols, margin, (int)waves, any_grouped, st);
+            default: return quant_row_colmax_fmt<kE5M2Fnuz>(b, blocks, cols, margin, (int)waves, any_grouped, st);
         }
     }
     if (blocks == 0) return hipSuccess;
@@ -2326,15 +2453,16 @@ hipError_t launch_grouped_quant_col(const uint16_t* x, int64_t total_m, int64_t 
     const int64_t rt_bound = (total_m + kColTileR - 1) / kColTileR + 2 * (int64_t)g;
     const int64_t rt_cap = ((int64_t)current_device_props().cus * 8 + ctiles - 1) / ctiles;
     const dim3 grid((unsigned)(rt_bound < rt_cap ? rt_bound : rt_cap), (unsigned)ctiles);
+    // the cast also writes scale_inv (each group's first row tile; the empty
+    // groups by the first row-tile slot); with no rows only scale_inv is left
 #define CALL(F)                                                                                                  \
     do {                                                                                                         \
-        hipLaunchKernelGGL((k_scale_inv_from_amax<F>), dim3(sblocks), dim3(kBlock), 0, st, col_amax, n, margin,  \
-                           scale_inv);                                                                           \
-        e = hipGetLastError();                                                                                   \
-        if (e != hipSuccess) return e;                                                                           \
         if (total_m > 0)                                                                                         \
             hipLaunchKernelGGL((k_grouped_quant_col_tiled<F>), grid, dim3(kBlock), 0, st, x, total_m, cols, ldx, \
-                               margin, offsets, g, qt, ldqt, col_amax, 1, small);                                \
+                               margin, offsets, g, qt, ldqt, col_amax, scale_inv, 1, small);                     \
+        else                                                                                                     \
+            hipLaunchKernelGGL((k_scale_inv_from_amax<F>), dim3(sblocks), dim3(kBlock), 0, st, col_amax, n,      \
+                               margin, scale_inv);                                                               \
     } while (0)
     switch (fmt) {
         case kE4M3: CALL(kE4M3); break;

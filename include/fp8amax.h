@@ -158,14 +158,27 @@ fp8_status_t fp8_quantize_row(const uint16_t* x, int64_t rows, int64_t cols, int
  * with column amax: the outputs are cleared first) when every tensor has the
  * vector layout (x 16-byte and q 8-byte aligned, ldx, ldq, cols multiples of
  * 8) and cols <= 16384; otherwise one launch per tensor, and a second pass
- * over each tensor whose column amax is asked for. Errors: any tensor's
- * argument error (as fp8_quantize_row) fails the whole call before anything
- * is enqueued. */
+ * over each tensor whose column amax is asked for.
+ * Grouped column amax (the per-group amax that fp8_grouped_quantize_col then
+ * takes with col_amax_ready = 1, e.g. for the MoE backward's casts of X^T,
+ * W^T and dY^T, whose groups are an expert's tokens or its weight rows):
+ * col_groups (HOST int32 [count], or NULL for none) gives tensor j's group
+ * count G_j, 0..4096 (0: one amax per column over all rows, as above);
+ * with G_j > 0, col_group_offsets[j] (HOST array of count DEVICE pointers;
+ * entry j: int64 [G_j + 1], non-decreasing, as for fp8_grouped_quantize_col)
+ * is required and col_amax_out[j] [G_j x cols] receives, for each group g and
+ * column c, the amax of column c over rows offsets[g] .. offsets[g+1]-1
+ * (0 for an empty group; rows outside [offsets[0], offsets[G_j]) count in no
+ * group). Still one pass over x, needing for every tensor of the call the
+ * vector layout and cols <= 16384 (else FP8_ERR_ALIGNMENT /
+ * FP8_ERR_UNSUPPORTED). Errors: any tensor's argument error (as
+ * fp8_quantize_row) fails the whole call before anything is enqueued. */
 #define FP8_MAX_ROW_BATCH 8
 fp8_status_t fp8_quantize_row_batch(int32_t count, const uint16_t* const* x, const int64_t* rows, int64_t cols,
                                     const int64_t* ldx, fp8_format_t fmt, int32_t margin, uint8_t* const* q,
                                     const int64_t* ldq, float* const* scale_inv_out, float* const* amax_out,
-                                    float* const* col_amax_out, void* stream);
+                                    float* const* col_amax_out, const int64_t* const* col_group_offsets,
+                                    const int32_t* col_groups, void* stream);
 
 /* Delayed tensorwise quantization of several tensors that share cols in one
  * launch ([Flux] delayed recipe; a linear layer's X and W, each with its own

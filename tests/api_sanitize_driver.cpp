@@ -63,7 +63,8 @@ STUB(launch_amax, const uint16_t*, int64_t, int64_t, int64_t, int, float*, hipSt
 STUB(launch_quant_row, const uint16_t*, int64_t, int64_t, int64_t, int, int, uint8_t*, int64_t, float*, float*, bool,
      hipStream_t)
 STUB(launch_quant_row_batch, int, const uint16_t* const*, const int64_t*, int64_t, const int64_t*, int, int,
-     uint8_t* const*, const int64_t*, float* const*, float* const*, float* const*, hipStream_t)
+     uint8_t* const*, const int64_t*, float* const*, float* const*, float* const*, const int64_t* const*,
+     const int32_t*, hipStream_t)
 STUB(launch_quant_col, const uint16_t*, int64_t, int64_t, int64_t, int, int, int, uint8_t*, int64_t, float*,
      const float*, hipStream_t)
 STUB(launch_quant_tensor, const uint16_t*, int64_t, int64_t, int64_t, int, int, const float*, uint8_t*, int64_t, float*,
@@ -193,10 +194,10 @@ int main() {
             ca[j] = j % 3 ? F32(50 + j) : nullptr;
         }
         OK(fp8_quantize_row_batch(count, x.data(), rows.data(), 256, ld.data(), FP8_E4M3, 0, q.data(), ld.data(),
-                                  si.data(), am.data(), ca.data(), nullptr),
+                                  si.data(), am.data(), ca.data(), nullptr, nullptr, nullptr),
            "launch_quant_row_batch");
         OK(fp8_quantize_row_batch(count, x.data(), rows.data(), 256, ld.data(), FP8_E4M3, 0, q.data(), ld.data(),
-                                  si.data(), nullptr, nullptr, nullptr),
+                                  si.data(), nullptr, nullptr, nullptr, nullptr, nullptr),
            "launch_quant_row_batch");
         std::vector<const float*> sc(count);
         for (int j = 0; j < count; ++j) {
@@ -209,20 +210,56 @@ int main() {
         if (count > 1) {
             ld[count - 1] = 100;                                     // the last tensor's row stride is too small
             ERR(fp8_quantize_row_batch(count, x.data(), rows.data(), 256, ld.data(), FP8_E4M3, 0, q.data(), ld.data(),
-                                       si.data(), nullptr, nullptr, nullptr),
+                                       si.data(), nullptr, nullptr, nullptr, nullptr, nullptr),
                 IA);
         }
+        // grouped column amax: group counts and offsets (host arrays of count entries)
+        std::vector<const int64_t*> go(count);
+        std::vector<int32_t> gn(count);
+        for (int j = 0; j < count; ++j) {
+            ld[j] = 256;
+            ca[j] = F32(50 + j);
+            go[j] = j % 2 ? nullptr : reinterpret_cast<const int64_t*>(dev(80 + j));
+            gn[j] = j % 2 ? 0 : 3 + j;
+        }
+        OK(fp8_quantize_row_batch(count, x.data(), rows.data(), 256, ld.data(), FP8_E4M3, 0, q.data(), ld.data(),
+                                  si.data(), nullptr, ca.data(), go.data(), gn.data(), nullptr),
+           "launch_quant_row_batch");
+        gn[0] = 4097;
+        ERR(fp8_quantize_row_batch(count, x.data(), rows.data(), 256, ld.data(), FP8_E4M3, 0, q.data(), ld.data(),
+                                   si.data(), nullptr, ca.data(), go.data(), gn.data(), nullptr),
+            IA);
+        gn[0] = 2;
+        go[0] = nullptr;                                             // groups without offsets
+        ERR(fp8_quantize_row_batch(count, x.data(), rows.data(), 256, ld.data(), FP8_E4M3, 0, q.data(), ld.data(),
+                                   si.data(), nullptr, ca.data(), go.data(), gn.data(), nullptr),
+            IA);
+        go[0] = reinterpret_cast<const int64_t*>((char*)dev(80) + 4);   // misaligned offsets
+        ERR(fp8_quantize_row_batch(count, x.data(), rows.data(), 256, ld.data(), FP8_E4M3, 0, q.data(), ld.data(),
+                                   si.data(), nullptr, ca.data(), go.data(), gn.data(), nullptr),
+            AL);
     }
     {
         const uint16_t* x[1] = {U16(1)};
         int64_t rows[1] = {4}, ld[1] = {16};
         uint8_t* q[1] = {U8(2)};
         float* si[1] = {F32(3)};
-        ERR(fp8_quantize_row_batch(0, x, rows, 16, ld, FP8_E4M3, 0, q, ld, si, nullptr, nullptr, nullptr), IA);
-        ERR(fp8_quantize_row_batch(FP8_MAX_ROW_BATCH + 1, x, rows, 16, ld, FP8_E4M3, 0, q, ld, si, nullptr, nullptr,
+        ERR(fp8_quantize_row_batch(0, x, rows, 16, ld, FP8_E4M3, 0, q, ld, si, nullptr, nullptr, nullptr, nullptr,
                                    nullptr),
             IA);
-        ERR(fp8_quantize_row_batch(1, nullptr, rows, 16, ld, FP8_E4M3, 0, q, ld, si, nullptr, nullptr, nullptr), IA);
+        ERR(fp8_quantize_row_batch(FP8_MAX_ROW_BATCH + 1, x, rows, 16, ld, FP8_E4M3, 0, q, ld, si, nullptr, nullptr,
+                                   nullptr, nullptr, nullptr),
+            IA);
+        ERR(fp8_quantize_row_batch(1, nullptr, rows, 16, ld, FP8_E4M3, 0, q, ld, si, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr),
+            IA);
+        // grouped column amax with a layout the single-pass kernel does not take
+        float* ca[1] = {F32(4)};
+        const int64_t* go[1] = {reinterpret_cast<const int64_t*>(dev(5))};
+        int32_t gn[1] = {2};
+        int64_t ld12[1] = {12};
+        ERR(fp8_quantize_row_batch(1, x, rows, 12, ld12, FP8_E4M3, 0, q, ld12, si, nullptr, ca, go, gn, nullptr), AL);
+        ERR(fp8_quantize_row_batch(1, x, rows, 16, ld, FP8_E4M3, 0, q, ld, si, nullptr, nullptr, go, gn, nullptr), IA);
     }
 
     // colwise, transposed and not

@@ -193,8 +193,9 @@ def test_quantize_row_batch_rejects_bad_arguments(fp8):
     x, q, s = PP(FAKE, FAKE), PP(FAKE, FAKE), PP(FAKE, FAKE)
     rows, ld = P64(4, 8), P64(16, 16)
 
-    def call(count=2, x=x, rows=rows, cols=16, ldx=ld, fmt=0, margin=0, q=q, ldq=ld, s=s, a=None, ca=None):
-        return _call(fp8, f, count, x, rows, cols, ldx, fmt, margin, q, ldq, s, a, ca, None)
+    def call(count=2, x=x, rows=rows, cols=16, ldx=ld, fmt=0, margin=0, q=q, ldq=ld, s=s, a=None, ca=None, go=None,
+             gn=None):
+        return _call(fp8, f, count, x, rows, cols, ldx, fmt, margin, q, ldq, s, a, ca, go, gn, None)
 
     st, msg = call(count=0)
     assert st == 1 and "count" in msg
@@ -208,6 +209,19 @@ def test_quantize_row_batch_rejects_bad_arguments(fp8):
     assert call(x=PP(FAKE, ctypes.c_void_p(0x10001)))[0] == 2     # tensor 1 misaligned for bf16
     assert call(a=PP(None, ctypes.c_void_p(0x10002)))[0] == 2     # misaligned amax output
     assert call(ca=PP(ctypes.c_void_p(0x10002), None))[0] == 2    # misaligned column-amax output
+    # grouped column amax: group counts 0..4096, offsets required and 8-byte aligned, an output for every grouped
+    # tensor, the vector layout and cols <= 16384
+    G32 = ctypes.c_int32 * 2
+    ca = PP(FAKE, FAKE)
+    st, msg = call(ca=ca, go=PP(FAKE, None), gn=G32(4097, 0))
+    assert st == 1 and "col_groups" in msg
+    assert call(ca=ca, go=PP(None, None), gn=G32(3, 0))[0] == 1
+    assert call(ca=ca, go=None, gn=G32(3, 0))[0] == 1
+    assert call(ca=PP(None, FAKE), go=PP(FAKE, None), gn=G32(3, 0))[0] == 1
+    assert call(ca=ca, go=PP(ctypes.c_void_p(0x10004), None), gn=G32(3, 0))[0] == 2
+    assert call(ca=ca, go=PP(FAKE, None), gn=G32(3, 0), cols=12, ldx=P64(12, 12), ldq=P64(12, 12))[0] == 2
+    assert call(ca=ca, go=PP(FAKE, None), gn=G32(3, 0), cols=16392, ldx=P64(16392, 16392),
+                ldq=P64(16392, 16392))[0] == 3
 
 
 def test_quantize_tensor_batch_rejects_bad_arguments(fp8):

@@ -205,9 +205,12 @@ def test_c4_moe_grouped(fp8, orc):
 
 def test_c4b_moe_backward(fp8, orc):
     """The c4 expert layer's backward in the benchmark's launch configuration:
-    dY [16384 x 2048] rowwise e5m2; W^T, dY^T and X^T through the grouped
-    colwise cast (per-expert column scales, transposed into the 256-padded
-    grouped layout); dgrad dX_g = dY_g W_g as a grouped e5m2 x e4m3 product
+    the forward's rowwise cast of X and W leaves their per-group column amax
+    (token groups; each expert's weight rows) as side outputs, dY [16384 x
+    2048] is cast rowwise e5m2 with its per-expert column amax likewise; W^T,
+    dY^T and X^T through the grouped colwise cast with those amax ready
+    (per-expert column scales, transposed into the 256-padded grouped layout);
+    dgrad dX_g = dY_g W_g as a grouped e5m2 x e4m3 product
     over a strided view of W^T, wgrad dW_g = dY_g^T X_g as the ragged-K
     product (the persistent kernel at this size). Every code and scale, every
     output of both products."""
@@ -220,39 +223,57 @@ def test_c4b_moe_backward(fp8, orc):
     wflat = w["w"].reshape(g * n, k)
     woff = np.arange(g + 1, dtype=np.int64) * n
     off_d = torch.from_numpy(offsets).to("cuda:0")
+    woff_d = torch.from_numpy(woff).to("cuda:0")
+    xd, wd, dyd = dev_bf16(w["x"]), dev_bf16(wflat), dev_bf16(w["dy"])
+    say("c4b forward cast (per-group column amax side outputs)")
+    qx, qw = torch.empty((T, k), dtype=torch.uint8, device="cuda:0"), torch.empty((g * n, k), dtype=torch.uint8,
+                                                                                  device="cuda:0")
+    sx, sw = torch.empty(T, device="cuda:0"), torch.empty(g * n, device="cuda:0")
+    xta, wta = torch.empty((g, k), device="cuda:0"), torch.empty((g, k), device="cuda:0")
+    fp8.fp8_quantize_row_batch([xd, wd], 0, 0, [qx, qw], [sx, sw], None, [xta, wta], [off_d, woff_d])
     say("c4b quantize")
-    dyq, dys, _, _ = row_quant(fp8, dev_bf16(w["dy"]), 1)
+    dyq, dys = torch.empty((T, n), dtype=torch.uint8, device="cuda:0"), torch.empty(T, device="cuda:0")
+    dyta = torch.empty((g, n), device="cuda:0")
+    fp8.fp8_quantize_row_batch([dyd], 1, 0, [dyq], [dys], None, [dyta], [off_d])
     wt = torch.empty((k, g * n), dtype=torch.uint8, device="cuda:0")
-    wts, wta = torch.empty((g, k), device="cuda:0"), torch.empty((g, k), device="cuda:0")
-    fp8.fp8_grouped_quantize_col(dev_bf16(wflat), 0, 0, torch.from_numpy(woff).to("cuda:0"), wt, wts, wta)
+    wts = torch.empty((g, k), device="cuda:0")
+    fp8.fp8_grouped_quantize_col(wd, 0, 0, woff_d, wt, wts, wta, col_amax_ready=True)
     dyt = torch.zeros((n, L), dtype=torch.uint8, device="cuda:0")
-    dyts, dyta = torch.empty((g, n), device="cuda:0"), torch.empty((g, n), device="cuda:0")
-    fp8.fp8_grouped_quantize_col(dev_bf16(w["dy"]), 1, 0, off_d, dyt, dyts, dyta)
+    dyts = torch.empty((g, n), device="cuda:0")
+    fp8.fp8_grouped_quantize_col(dyd, 1, 0, off_d, dyt, dyts, dyta, col_amax_ready=True)
     xt = torch.zeros((k, L), dtype=torch.uint8, device="cuda:0")
-    xts, xta = torch.empty((g, k), device="cuda:0"), torch.empty((g, k), device="cuda:0")
-    fp8.fp8_grouped_quantize_col(dev_bf16(w["x"]), 0, 0, off_d, xt, xts, xta)
+    xts = torch.empty((g, k), device="cuda:0")
+    fp8.fp8_grouped_quantize_col(xd, 0, 0, off_d, xt, xts, xta, col_amax_ready=True)
     dx = torch.empty((T, k), dtype=torch.bfloat16, device="cuda:0")
     fp8.fp8_grouped_gemm_scaled(dyq, 1, torch.as_strided(wt, (g, k, n), (n, g * n, 1)), 0, off_d, dys, wts, dx)
     dw = torch.empty((g, n, k), dtype=torch.bfloat16, device="cuda:0")
     fp8.fp8_grouped_gemm_ragged_k(dyt, 1, xt, 0, off_d, T, dyts, xts, dw)
     torch.cuda.synchronize()
     say("c4b oracle quantize")
+    oqx, osx, _ = orc.quantize_row(w["x"], 0)
+    assert_codes_equal(qx.cpu().numpy(), oqx, "forward X codes")
+    assert_f32_bits_equal(sx.cpu().numpy(), osx, "forward X scale_inv")
+    del oqx, qx
+    oqw, osw, _ = orc.quantize_row(wflat, 0)
+    assert_codes_equal(qw.cpu().numpy(), oqw, "forward W codes")
+    assert_f32_bits_equal(sw.cpu().numpy(), osw, "forward W scale_inv")
+    del oqw, qw
     oqdy, osdy, _ = orc.quantize_row(w["dy"], 1)
     assert_codes_equal(dyq.cpu().numpy(), oqdy, "dY codes")
     assert_f32_bits_equal(dys.cpu().numpy(), osdy, "dY scale_inv")
     oqwt, oswt, oawt = orc.grouped_quantize_col(wflat, 0, woff, 256)
     assert_codes_equal(wt.cpu().numpy(), oqwt, "W^T codes")
     assert_f32_bits_equal(wts.cpu().numpy(), oswt, "W^T scale_inv")
-    assert_f32_bits_equal(wta.cpu().numpy(), oawt, "W^T amax")
+    assert_f32_bits_equal(wta.cpu().numpy(), oawt, "W per-expert column amax (forward side output)")
     oqdyt, osdyt, oadyt = orc.grouped_quantize_col(w["dy"], 1, offsets, 256)
     assert oqdyt.shape[1] <= L
     assert_codes_equal(dyt.cpu().numpy()[:, :oqdyt.shape[1]], oqdyt, "dY^T codes")
     assert_f32_bits_equal(dyts.cpu().numpy(), osdyt, "dY^T scale_inv")
-    assert_f32_bits_equal(dyta.cpu().numpy(), oadyt, "dY^T amax")
+    assert_f32_bits_equal(dyta.cpu().numpy(), oadyt, "dY per-expert column amax (row cast side output)")
     oqxt, osxt, oaxt = orc.grouped_quantize_col(w["x"], 0, offsets, 256)
     assert_codes_equal(xt.cpu().numpy()[:, :oqxt.shape[1]], oqxt, "X^T codes")
     assert_f32_bits_equal(xts.cpu().numpy(), osxt, "X^T scale_inv")
-    assert_f32_bits_equal(xta.cpu().numpy(), oaxt, "X^T amax")
+    assert_f32_bits_equal(xta.cpu().numpy(), oaxt, "X per-expert column amax (forward side output)")
     say("c4b dgrad check")
     dxh = dx.float().cpu().numpy()
     rows = 0

@@ -553,6 +553,71 @@ def test_quantize_row_batch_col_amax_parity(fp8, orc, fmt):
     assert np.isnan(got[3][4][1]) and np.isnan(got[3][4][100]) and np.isinf(got[3][4][0])
 
 
+def grouped_amax_oracle(orc, xb, offsets):
+    """Per-group column amax [G x cols] from the oracle's grouped colwise cast
+    (rows offsets[g] .. offsets[g+1]-1, clamped to the tensor)."""
+    return orc.grouped_quantize_col(xb, 0, offsets, 256)[2]
+
+
+GROUPED_AMAX = [
+    (136, [5, 0, 64, 1, 130, 0, 257, 3], 0, 0),      # one chunk per lane, empty groups, groups of 1 row
+    (1024, [300, 0, 1, 255, 257, 2000, 17], 5, 7),   # rows before the first group and after the last
+    (2048, [991, 0, 785, 1, 2000, 30], 0, 3),         # the MoE output-gradient width: 4 chunks per lane
+    (4096, [700, 0, 260, 1300, 2], 1, 0),            # 8 chunks per lane
+    (7168, [4994, 118, 0, 2115, 1408, 3], 0, 0),     # the MoE token shape: 16 chunks per lane
+    (16384, [300, 0, 129, 45], 0, 0),                # 32 chunks per lane (folded into LDS per row)
+]
+
+
+@pytest.mark.parametrize("cols,sizes,before,after", GROUPED_AMAX,
+                         ids=["short_rows", "ungrouped_rows", "dy_width", "8_chunks", "moe_tokens", "32_chunks"])
+def test_quantize_row_batch_grouped_col_amax(fp8, orc, cols, sizes, before, after):
+    """The per-group column amax as a side output of the rowwise cast, in one
+    batch with a tensor grouped by fixed blocks of rows (an expert's weight
+    rows), an ungrouped column amax and a tensor without one: every group's
+    amax bit-exact against the oracle's grouped colwise cast (empty groups 0,
+    NaN / Inf columns inside a group), codes and scales unchanged, nothing
+    written past the outputs."""
+    rng = np.random.default_rng(cols)
+    rows0 = before + sum(sizes) + after
+    off0 = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64) + before
+    x0 = rand_bf16(rows0, cols, seed=cols + 1)
+    g_nan = int(np.argmax(np.array(sizes) > 2))          # a group with rows: NaN in column 3, Inf in 5
+    r = int(off0[g_nan])
+    x0[r, 3] = 0x7FC1
+    x0[r + 1, 5] = 0xFF80
+    experts, per = 4, 96
+    x1 = rand_bf16(experts * per, cols, seed=cols + 2)
+    off1 = (np.arange(experts + 1) * per).astype(np.int64)
+    x2 = rand_bf16(33, cols, seed=cols + 3)
+    x3 = rand_bf16(7, cols, seed=cols + 4)
+    xbs = [x0, x1, x2, x3]
+    G = [len(sizes), experts, 0, 0]
+    xs = [dev_bf16(xb) for xb in xbs]
+    qs = [torch.empty(xb.shape, dtype=torch.uint8, device="cuda:0") for xb in xbs]
+    sis = [torch.empty(xb.shape[0], device="cuda:0") for xb in xbs]
+    bufs = [torch.full((max(g, 1) * cols + 1,), -1.0, device="cuda:0") for g in G]
+    cas = [bufs[0][:-1], bufs[1][:-1], bufs[2][:-1], None]
+    offs = [torch.from_numpy(off0).to("cuda:0"), torch.from_numpy(off1).to("cuda:0"), None, None]
+    say("row batch grouped col amax", cols, sizes, before, after)
+    fp8.fp8_quantize_row_batch(xs, 1, 0, qs, sis, None, cas, offs)
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert b[-1].item() == -1.0, "write past a column-amax output"
+    assert np.all(bufs[3].cpu().numpy() == -1.0)
+    for j, xb in enumerate(xbs):
+        oq, osi, _ = orc.quantize_row(xb, 1, 0)
+        assert_codes_equal(qs[j].cpu().numpy(), oq, f"codes of tensor {j}")
+        assert_f32_bits_equal(sis[j].cpu().numpy(), osi, f"scale_inv of tensor {j}")
+    got0 = cas[0].cpu().numpy().reshape(len(sizes), cols)
+    assert_f32_bits_equal(got0, grouped_amax_oracle(orc, x0, off0), "grouped column amax (token groups)")
+    assert np.isnan(got0[g_nan, 3]) and np.isinf(got0[g_nan, 5])
+    assert not got0[np.array(sizes) == 0].any(), "an empty group's amax is not 0"
+    got1 = cas[1].cpu().numpy().reshape(experts, cols)
+    assert_f32_bits_equal(got1, grouped_amax_oracle(orc, x1, off1), "grouped column amax (expert rows)")
+    assert_f32_bits_equal(cas[2].cpu().numpy(), orc.amax(x2, orc.AXIS_COL), "ungrouped column amax")
+
+
 @pytest.mark.parametrize("shape", [(3000, 8), (2500, 520), (5000, 4096), (2100, 8200), (2300, 14336),
                                    (900, 16384)])
 def test_quantize_row_col_amax_row_lengths(fp8, orc, shape):
