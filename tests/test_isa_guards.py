@@ -25,9 +25,10 @@ def asm(request):
 
 
 def kernels(text):
-    """name -> body of every kernel function in the assembly."""
+    """name -> body of every kernel function in the assembly (to its end label,
+    so code after an early s_endpgm is included)."""
     res = {}
-    for m in re.finditer(r"^(_Z\w+):\s*$(.*?)^\s*s_endpgm", text, flags=re.M | re.S):
+    for m in re.finditer(r"^(_Z\w+):[^\n]*$(.*?)^\.Lfunc_end\d+:", text, flags=re.M | re.S):
         res[m.group(1)] = m.group(2)
     return res
 
@@ -41,9 +42,14 @@ def test_no_scratch(asm):
 
 def test_m0_only_feeds_direct_loads(asm):
     name, text = asm
-    for kname, body in kernels(text).items():
+    found = kernels(text)
+    assert len(found) == len(re.findall(r"^\.Lfunc_end\d+:", text, flags=re.M)) > 0, "kernel bodies not found"
+    for kname, body in found.items():
         lines = [l.strip() for l in body.splitlines() if l.strip() and not l.strip().startswith(";")]
         for i, l in enumerate(lines):
             if re.search(r"\bm0\b", l):
                 assert re.match(r"s_mov_b32 m0, s\d+$", l), (kname, l)
-                assert lines[i + 1] == "s_nop 0" and re.match(r"global_load_lds_dword(x4)? ", lines[i + 2]), (kname, l)
+                # one wait state before a load with a VGPR address; five before one
+                # whose SGPR base came from v_readfirstlane
+                assert lines[i + 1] in ("s_nop 0", "s_nop 4") and \
+                    re.match(r"global_load_lds_dword(x4)? ", lines[i + 2]), (kname, l)
