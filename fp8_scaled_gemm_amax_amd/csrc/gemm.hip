@@ -1338,6 +1338,193 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Persistent grouped product (bf16 output, at most gpersist::kMaxGroups
+// groups, at least 256 rows in all): k_grouped_gemm_big's tiles in its
+// logical order (each XCD a contiguous run; within a group, runs of 4 m-tiles
+// sweep the n-tiles), taken as k_gemm_persist takes dense tiles: the next
+// tile's first two K steps load during the current tile's last two. Each
+// workgroup keeps the groups' tile prefix sums in LDS for the whole kernel and
+// finds each tile's group by binary search. A tile that would run past the
+// last row of the token matrix is shifted back to end there (and one past the
+// last column of B to end at column n), so every tile loads 256 whole rows with
+// one set of lane offsets; the rows it computes outside its group's m-tile
+// (another group's tokens, with this group's weights) are never stored.
+namespace gpersist {
+constexpr int kMaxGroups = 1024;
+constexpr int kPreOff = persist::kSmem;                    // after the persistent kernel's LDS
+constexpr int kSmem = kPreOff + (kMaxGroups + 1) * 4;      // (G + 1) int32 prefix sums: 150 KB
+constexpr int64_t kMaxK = 4096;                            // longer contractions keep k_grouped_gemm_big
+}  // namespace gpersist
+
+// One tile of the persistent grouped loop (every field wave-uniform).
+struct GpTile {
+    int grp;
+    int64_t row0, col0;     // first loaded row / column
+    int row_lo, row_hi;     // stored rows, relative to row0
+    int col_lo;             // first stored column, relative to col0
+};
+
+template <int FA, int FB>
+__global__ __launch_bounds__(256, 1) void k_grouped_gemm_persist(
+    const uint8_t* __restrict__ a, int64_t lda, const uint8_t* __restrict__ b, int64_t ldb, int64_t b_group_stride,
+    const int64_t* __restrict__ offsets, int g, int64_t total_m, int64_t n, int64_t k, const float* __restrict__ sa,
+    const float* __restrict__ sb, void* __restrict__ d, int64_t ldd, int vec_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[gpersist::kSmem];
+    const uint32_t tiles_n = (uint32_t)((n + big::BN - 1) / big::BN);
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    auto bounds = [&](int e, int64_t* lo, int64_t* hi) {
+        int64_t s = offsets[e], u = offsets[e + 1];
+        s = s < 0 ? 0 : (s > total_m ? total_m : s);
+        u = u < s ? s : (u > total_m ? total_m : u);
+        *lo = s;
+        *hi = u;
+    };
+    // prefix sums of the groups' tile counts (g <= 1024: up to 4 groups per thread)
+    int32_t* pre = reinterpret_cast<int32_t*>(smem + gpersist::kPreOff);
+    int32_t* wsum = reinterpret_cast<int32_t*>(smem + big::kScaleOff);
+    {
+        const int per = (g + 255) / 256;
+        const int e0 = t * per, e1 = e0 + per < g ? e0 + per : g;
+        int32_t mine = 0;
+        for (int e = e0; e < e1; ++e) {
+            int64_t lo, hi;
+            bounds(e, &lo, &hi);
+            mine += (int32_t)(((hi - lo + big::BM - 1) / big::BM) * tiles_n);
+        }
+        int32_t incl = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int32_t run = incl - mine;
+        for (uint32_t w = 0; w < wave; ++w) run += wsum[w];
+        for (int e = e0; e < e1; ++e) {
+            pre[e] = run;
+            int64_t lo, hi;
+            bounds(e, &lo, &hi);
+            run += (int32_t)(((hi - lo + big::BM - 1) / big::BM) * tiles_n);
+        }
+        if (t == 255) pre[g] = run;
+        __syncthreads();                                 // (also: wsum, in the scale area, is dead)
+    }
+    const uint32_t nt = (uint32_t)__builtin_amdgcn_readfirstlane(pre[g]);
+    const uint32_t G = gridDim.x;
+    if (blockIdx.x >= nt) return;                        // uniform over the workgroup
+    // logical tile of slot id (XCD-aware as k_grouped_gemm_big), its group and place
+    auto resolve = [&](uint32_t id, GpTile& tl) {
+        uint32_t ntt = nt, tn = tiles_n;
+        asm volatile("" : "+s"(ntt), "+s"(tn));
+        const uint32_t q = ntt / 8, rem = ntt % 8;
+        const uint32_t xcd = id % 8, idx = id / 8;
+        uint32_t lt = xcd * q + (xcd < rem ? xcd : rem) + idx;
+        int lo_e = 0, hi_e = g;                          // pre[lo_e] <= lt < pre[hi_e]
+        while (hi_e - lo_e > 1) {
+            const int mid = (lo_e + hi_e) >> 1;
+            if ((uint32_t)pre[mid] <= lt)
+                lo_e = mid;
+            else
+                hi_e = mid;
+        }
+        const int grp = __builtin_amdgcn_readfirstlane(lo_e);
+        lt -= (uint32_t)__builtin_amdgcn_readfirstlane(pre[grp]);
+        int64_t lo, hi;
+        bounds(grp, &lo, &hi);
+        lo = uniform64(lo);
+        hi = uniform64(hi);
+        const uint32_t tm = (uint32_t)((hi - lo + big::BM - 1) / big::BM);
+        constexpr uint32_t gm = 4;
+        const uint32_t span = gm * tn;
+        const uint32_t first_m = lt / span * gm;
+        const uint32_t gsize = tm - first_m < gm ? tm - first_m : gm;
+        const uint32_t u = lt % span;
+        const int64_t pm = first_m + u % gsize, pn = u / gsize;
+        const int64_t r = lo + pm * big::BM, c = pn * big::BN;
+        tl.grp = grp;
+        tl.row0 = r + big::BM > total_m ? total_m - big::BM : r;
+        tl.col0 = (c + big::BN > n && n >= big::BN) ? n - big::BN : c;
+        tl.row_lo = (int)(r - tl.row0);
+        tl.row_hi = (int)((hi < r + big::BM ? hi : r + big::BM) - tl.row0);
+        tl.col_lo = (int)(c - tl.col0);
+    };
+    uint32_t aoff[8], boff[8];
+    k128_lane_offsets(aoff, lda, total_m);
+    k128_lane_offsets(boff, ldb, n);
+    uint32_t id = blockIdx.x;
+    GpTile cur;
+    resolve(id, cur);
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kScaleOff)) + wave * 256;
+    auto issue_scales = [&](const GpTile& tl) {
+        const int64_t r = tl.row0 + t, c = tl.col0 + t;
+        lds_dma4(sbase, sa + (r < total_m ? r : total_m - 1));
+        lds_dma4(sbase + 1024, sb + (int64_t)tl.grp * n + (c < n ? c : n - 1));
+    };
+    const int64_t nk = k / k128::BK;                     // even, >= 2
+    const uint8_t* at = a + cur.row0 * lda;
+    const uint8_t* bt = b + (int64_t)cur.grp * b_group_stride + cur.col0 * ldb;
+    issue_scales(cur);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem + s * k128::kStage)) + wave * 8192;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma16_s(base + i * 1024, at + s * k128::BK, aoff[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma16_s(base + k128::kOpBytes + i * 1024, bt + s * k128::BK, boff[i]);
+    }
+    wait_vmcnt<16>();                                    // the scales and step 0 landed
+    v16f acc[4][4];
+    v8i f0[8];
+    u32x4 sx[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    __syncthreads();                                     // step 0 (all threads' loads) is in LDS
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        const int j = k128_frag(f);
+        f0[j] = big_join(k128_half<false>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 0),
+                         k128_half<false>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 1));
+    }
+    for (;;) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+        const uint32_t nid = id + G;
+        const GpTile done = cur;
+        const uint8_t* nat = at;                         // with no next tile: this tile's own first
+        const uint8_t* nbt = bt;                         // steps (valid addresses, never used)
+        if (nid < nt) {
+            resolve(nid, cur);
+            nat = a + cur.row0 * lda;
+            nbt = b + (int64_t)cur.grp * b_group_stride + cur.col0 * ldb;
+        }
+        for (int64_t p = 0; p < nk; p += 2) {
+            const bool last = p + 2 >= nk;
+            const uint8_t* la = last ? nat : at;
+            const uint8_t* lb = last ? nbt : bt;
+            const int64_t kl = last ? 0 : (p + 2) * k128::BK;
+            k128_step<FA, FB, 0, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl, nullptr, nullptr, 0,
+                                                          0);
+            k128_step<FA, FB, 1, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl + k128::BK, nullptr,
+                                                          nullptr, 0, 0);
+        }
+        at = nat;
+        bt = nbt;
+        const int64_t chi = n - done.col0;
+        chunk_epilogue<false>(smem, acc, d, ldd, done.row0, done.row_lo, done.row_hi, done.col0, done.col_lo,
+                              (int)(chi < 256 ? chi : 256), vec_out && done.col0 % 8 == 0);
+        if (nid >= nt) break;
+        id = nid;
+        __syncthreads();                                 // every wavefront is done with the scale area
+        issue_scales(cur);                               // (landed by the next tile's first mid-step wait)
+    }
+    wait_vmcnt<0>();
+}
+
 // One tile of the persistent ragged-K loop (every field wave-uniform).
 struct RaggedTile {
     uint32_t slot;
@@ -1545,6 +1732,16 @@ hipError_t grouped_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_
         ldb < (1 << 24)) {
         const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
         const int64_t grid = ((total_m + big::BM - 1) / big::BM + g) * ((n + big::BN - 1) / big::BN);
+        const int64_t cus = current_device_props().cus;
+        // bf16 output, short contractions, more tile slots than CUs: the persistent kernel
+        if constexpr (!OUT_F32) {
+            if (k <= gpersist::kMaxK && g <= gpersist::kMaxGroups && total_m >= big::BM && cus >= 8 && grid > cus &&
+                grid < ((int64_t)1 << 31)) {
+                hipLaunchKernelGGL((k_grouped_gemm_persist<FA, FB>), dim3((unsigned)(cus / 8 * 8)), dim3(256), 0, st,
+                                   a, lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out);
+                return hipGetLastError();
+            }
+        }
         const uint8_t* none = nullptr;
         hipLaunchKernelGGL((k_grouped_gemm_big<FA, FB, OUT_F32, false>), dim3((unsigned)grid), dim3(256), 0, st, a,
                            lda, b, ldb, stride, offsets, g, total_m, n, k, sa, sb, d, ldd, vec_out, none, (int64_t)0,

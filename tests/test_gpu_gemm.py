@@ -236,6 +236,48 @@ GROUPED_LARGE = [([0, 1000, 1, 255, 257, 0, 2583], 2048, 512, 0, 0, False),
                  ([600, 0, 3500, 100], 2048, 4096, 0, 0, False)]
 
 
+GROUPED_PERSIST = [([0, 1000, 1, 255, 257, 0, 2583, 60, 700], 3000, 512, 0, 0),
+                   ([100, 0, 156], 16400, 256, 1, 0),
+                   ([30000, 0, 25000, 15000], 200, 256, 0, 1),
+                   ([600, 0, 3500, 100, 2000], 2304, 4096, 1, 0),
+                   ([5000], 3100, 512, 0, 0)]
+
+
+@pytest.mark.parametrize("sizes,n,k,fa,fb", GROUPED_PERSIST,
+                         ids=["ragged_shifted", "one_tile_of_rows", "n_below_tile", "k4096", "one_group"])
+def test_grouped_gemm_parity_persistent(fp8, orc, sizes, n, k, fa, fb):
+    """Shapes that take the persistent grouped kernel (bf16 output, k <= 4096,
+    more tile slots than CUs): a group's partial last m-tile shifted back inside
+    the token matrix (its extra rows belong to other groups and are never
+    stored), 256 rows in all (every tile loads the whole matrix), n off the 256
+    grid (column tiles shifted back) and below one tile (clamped), the longest
+    contraction it takes, empty and one-row groups; every output against the
+    oracle. One group must equal the dense product (the same K loop)."""
+    g = len(sizes)
+    offsets = np.zeros(g + 1, np.int64)
+    offsets[1:] = np.cumsum(sizes)
+    total = int(offsets[-1])
+    assert total >= 256 and ((total + 255) // 256 + g) * ((n + 255) // 256) > 256 and k % 256 == 0
+    rng = np.random.default_rng(total + n + k + 1)
+    a = random_codes(rng, (total, k), fa)
+    b = random_codes(rng, (g, n, k), fb)
+    sa = np.exp2(rng.integers(-8, 2, total)).astype(np.float32) * np.float32(1.375)
+    sb = np.exp2(rng.integers(-8, 2, (g, n))).astype(np.float32)
+    say("grouped persistent", g, total, n, k, fa, fb)
+    got = gpu_grouped(fp8, a, fa, b, fb, offsets, sa, sb)
+    rows = 0
+    for e in range(g):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            rows += check_full(orc, got, orc.gemm_by_rows(a[lo:hi], fa, b[e], fb, sa[lo:hi], sb[e]),
+                               f"grouped persistent group {e}", row_offset=lo)
+    assert rows == total
+    if g == 1:
+        say("grouped persistent: one group vs dense")
+        dense = gpu_gemm(fp8, a, fa, b[0], fb, sa, sb[0], 1, 1)
+        assert np.array_equal(dense, got), "one group equals the dense GEMM"
+
+
 @pytest.mark.parametrize("sizes,n,k,fa,fb,out_f32", GROUPED_LARGE,
                          ids=["ragged", "g300", "one", "ragged_n", "long_k"])
 def test_grouped_gemm_parity_large_tiles(fp8, orc, sizes, n, k, fa, fb, out_f32):
