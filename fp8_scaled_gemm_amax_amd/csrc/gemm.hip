@@ -1220,10 +1220,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restri
                                                          const uint8_t* __restrict__ b, int64_t ldb, int64_t m,
                                                          int64_t n, int64_t k, const float* __restrict__ sa,
                                                          int sa_vec, const float* __restrict__ sb, int sb_vec,
-                                                         void* __restrict__ d, int64_t ldd, int vec_out) {
+                                                         void* __restrict__ d, int64_t ldd, int vec_out,
+                                                         int64_t tile_limit) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[persist::kSmem];
     const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
-    const int64_t nt = tiles_m * tiles_n, G = gridDim.x;
+    // tiles 0 .. tile_limit-1 of the order (the rest, if any, go to k_gemm_half)
+    const int64_t nt = tile_limit, G = gridDim.x;
     const int t = threadIdx.x;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nk = k / k128::BK;                     // even, >= 2
@@ -1693,6 +1695,259 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k_persist(
     wait_vmcnt<0>();
 }
 
+// Half tiles (256 x 128) for the last, partial round of the persistent dense
+// product: when the tiles left after the full rounds are at most half a round,
+// they run as twice as many 256 x 128 halves on a second launch instead of
+// leaving most CUs idle while a few finish them. Four wavefronts, each owning
+// 128 x 64 outputs (4 x 2 blocks of 32 x 32); the K128 step of the large-tile
+// kernels with 8 MFMAs per K half per wavefront and B's 128 rows in a 16 KB
+// operand; each wavefront stages its results through LDS one 32-row chunk at a
+// time.
+namespace t128 {
+constexpr int BM = 256, BN = 128;
+constexpr int kAOp = BM * 128;                    // A of a K128 stage: 32 KB
+constexpr int kStage = kAOp + BN * 128;           // 48 KB
+constexpr int kScaleOff = 2 * kStage;             // 256 row + 128 column scales
+constexpr int kChunkOff = kScaleOff + (BM + BN) * 4;
+constexpr int kChunk = 32 * 64 * 2;               // a wavefront's staged 32 x 64 bf16 chunk
+constexpr int kSmem = kChunkOff + 4 * kChunk;     // 113.5 KB
+}  // namespace t128
+
+// Fragment rows of the 256 x 128 tile: j < 4: A block j of the wavefront's
+// 128 rows; j = 4, 5: B block j - 4 of its 64 columns (rows of B).
+__device__ __forceinline__ int t128_row(int j) {
+    const int w = threadIdx.x >> 6;
+    return (j < 4 ? (w >> 1) * 128 + j * 32 : (w & 1) * 64 + (j - 4) * 32) + (threadIdx.x & 31);
+}
+// Fragment order of a step: A0, B0, B1, A1, A2, A3 (the MFMA sweep (mi, ni) =
+// (0,0), (0,1), (1,0), .. first needs them in that order).
+__device__ __forceinline__ int t128_frag(int f) { return f == 0 ? 0 : (f <= 2 ? f + 3 : f - 2); }
+
+// B's 4 loads per thread of a step (128 rows): load i of wavefront w fills rows
+// w * 32 + 8i .. + 7, as k128_lane_offsets does for A's 256 rows.
+__device__ __forceinline__ void t128_lane_offsets_b(uint32_t (&off)[4], int64_t ld, int64_t valid_rows) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint32_t ld32 = (uint32_t)ld;
+    const int last = (int)(valid_rows < 128 ? valid_rows : 128) - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = wave * 32 + i * 8 + (lane >> 3);
+        const int chunk = k128_slot(row, lane & 7);
+        const uint32_t r = (uint32_t)(row < last ? row : last);
+        off[i] = r * ld32 + (uint32_t)(chunk * 16);
+    }
+}
+
+// One K128 step of the 256 x 128 tile (the k128_step scheme: 8 MFMAs per K
+// half per wavefront, the second half's fragments read during the first half,
+// a mid-step wait and barrier, then the next step's first-half fragments read
+// and step p+2's 12 loads per thread issued during the second half).
+template <int FA, int FB, int CUR, bool NEXT, bool LOADS>
+__device__ __forceinline__ void t128_step(uint8_t* smem, v16f (&acc)[4][2], v8i (&f0)[6], const uint8_t* a,
+                                         const uint32_t (&aoff)[8], const uint8_t* b, const uint32_t (&boff)[4],
+                                         int64_t knext) {
+    const uint8_t* ta = smem + CUR * t128::kStage;
+    const uint8_t* tb = ta + t128::kAOp;
+    const uint8_t* na = smem + (CUR ^ 1) * t128::kStage;
+    const uint8_t* nb = na + t128::kAOp;
+    u32x4 h1[12];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int mi = i >> 1, ni = i & 1;
+        acc[mi][ni] = mfma64<FA, FB, false, 0>(f0[mi], f0[4 + ni], acc[mi][ni], 0u, 0u);
+        if (i < 6) {
+            const int j = t128_frag(i);
+            h1[2 * i] = k128_half<false>(j < 4 ? ta : tb, t128_row(j), 1, 0);
+            h1[2 * i + 1] = k128_half<false>(j < 4 ? ta : tb, t128_row(j), 1, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    v8i f1[6];
+#pragma unroll
+    for (int f = 0; f < 6; ++f) f1[t128_frag(f)] = big_join(h1[2 * f], h1[2 * f + 1]);
+    wait_vmcnt<0, 0>();
+    __syncthreads();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem + CUR * t128::kStage));
+    u32x4 h0[12];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int mi = i >> 1, ni = i & 1;
+        acc[mi][ni] = mfma64<FA, FB, false, 2>(f1[mi], f1[4 + ni], acc[mi][ni], 0u, 0u);
+        if (NEXT && i < 6) {
+            const int j = t128_frag(i);
+            h0[2 * i] = k128_half<false>(j < 4 ? na : nb, t128_row(j), 0, 0);
+            h0[2 * i + 1] = k128_half<false>(j < 4 ? na : nb, t128_row(j), 0, 1);
+        }
+        if (LOADS) {
+            lds_dma16_s(base + wave * 8192 + i * 1024, a + knext, aoff[i]);
+            if (i >= 4) lds_dma16_s(base + t128::kAOp + wave * 4096 + (i - 4) * 1024, b + knext, boff[i - 4]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NEXT) {
+#pragma unroll
+        for (int f = 0; f < 6; ++f) f0[t128_frag(f)] = big_join(h0[2 * f], h0[2 * f + 1]);
+    }
+}
+
+// The output block a chunk stores into.
+struct T128Out {
+    uint8_t* d;
+    int64_t row0, col0;     // first loaded row / column
+    int row_lo, row_hi;     // stored rows, relative to row0
+    int col_lo, col_hi;     // stored columns, relative to col0
+    int vec;                // 16-byte stores allowed
+};
+
+// Chunk MI of a finished tile: rows wm * 128 + 32 MI .. + 31, the wavefront's
+// 64 columns; d = acc * sa_row * sb_col, staged through the wavefront's LDS
+// chunk (4-row groups g: column c at g * 512 + unit (c / 2, swizzled) * 16 +
+// (c % 2) * 8) and stored as 16-byte row pieces, 8 lanes per 128-byte row.
+template <int MI>
+__device__ __forceinline__ void t128_chunk(uint8_t* smem, v16f (&acc)[4][2], const T128Out& o, int64_t ldd) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    asm volatile("" : "+a"(acc[MI][0]));
+    asm volatile("" : "+a"(acc[MI][1]));
+    const float* s_rows = reinterpret_cast<const float*>(smem + t128::kScaleOff);
+    const float* s_cols = s_rows + t128::BM;
+    const int r0 = wm * 128 + MI * 32;                   // first tile row of the chunk
+    const int c0 = wn * 64;                              // first tile column of the wavefront
+    uint8_t* ep = smem + t128::kChunkOff + wave * t128::kChunk;
+    auto off = [](int g, int c) {
+        const int u = c >> 1;
+        return g * 512 + (((u & ~3) | ((u ^ (u >> 3)) & 3)) << 4) + ((c & 1) << 3);
+    };
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const float sb = s_cols[c0 + ni * 32 + (lane & 31)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int g = 2 * q + (lane >> 5);           // rows 4g .. 4g+3 of the chunk
+            const u32x4 s4 = *reinterpret_cast<const u32x4*>(&s_rows[r0 + 4 * g]);
+            const int r = 4 * q;
+            v2f v01 = {acc[MI][ni][r] * __uint_as_float(s4[0]) * sb, acc[MI][ni][r + 1] * __uint_as_float(s4[1]) * sb};
+            v2f v23 = {acc[MI][ni][r + 2] * __uint_as_float(s4[2]) * sb,
+                       acc[MI][ni][r + 3] * __uint_as_float(s4[3]) * sb};
+            uint2 w;
+            w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, v2bf));
+            w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, v2bf));
+            *reinterpret_cast<uint2*>(ep + off(g, ni * 32 + (lane & 31))) = w;
+        }
+    }
+    wait_vmcnt<63, 0>();                                 // this wavefront's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int cc = lane & 7;                             // columns 8cc .. 8cc+7 of the wavefront's 64
+    const int g = lane >> 3;                             // rows 4g .. 4g+3 of the chunk
+    u32x4 un[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) un[k] = *reinterpret_cast<const u32x4*>(ep + off(g, 8 * cc + 2 * k));
+    const bool full = o.vec && r0 >= o.row_lo && r0 + 32 <= o.row_hi && c0 >= o.col_lo && c0 + 64 <= o.col_hi;
+    const int clo = o.col_lo - c0, chi = o.col_hi - c0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int lr = r0 + 4 * g + r;                   // tile row
+        const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
+        const int wlo = (r >> 1), whi = 2 + (r >> 1);
+        u32x4 row;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) row[k] = __builtin_amdgcn_perm(un[k][whi], un[k][wlo], sel);
+        uint16_t* dst = reinterpret_cast<uint16_t*>(o.d) + (o.row0 + lr) * ldd + o.col0 + c0 + 8 * cc;
+        if (full) {
+            __builtin_nontemporal_store(row, reinterpret_cast<u32x4*>(dst));
+        } else if (lr >= o.row_lo && lr < o.row_hi) {
+            for (int e = 0; e < 8; ++e)
+                if (8 * cc + e >= clo && 8 * cc + e < chi) dst[e] = (uint16_t)(row[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
+
+// One 256 x 128 half of tile `first + blockIdx.x / 2` in k_gemm_persist's
+// order: the tile's rows and columns as that kernel would take them (edge
+// tiles shifted back), the half's 128 columns from col0 + 128 (blockIdx.x % 2).
+template <int FA, int FB>
+__global__ __launch_bounds__(256, 1) void k_gemm_half(const uint8_t* __restrict__ a, int64_t lda,
+                                                      const uint8_t* __restrict__ b, int64_t ldb, int64_t m, int64_t n,
+                                                      int64_t k, const float* __restrict__ sa, int sa_vec,
+                                                      const float* __restrict__ sb, int sb_vec, void* __restrict__ d,
+                                                      int64_t ldd, int vec_out, int64_t first) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[t128::kSmem];
+    const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
+    int64_t pm, pn;
+    tile_coords32((uint32_t)(first + blockIdx.x / 2), (uint32_t)tiles_m, (uint32_t)tiles_n, &pm, &pn);
+    const int hsel = blockIdx.x & 1;
+    const int64_t r = pm * big::BM, c = pn * big::BN;
+    const int64_t row0 = (r + big::BM > m && m >= big::BM) ? m - big::BM : r;
+    const int64_t col0 = (c + big::BN > n && n >= big::BN) ? n - big::BN : c;
+    const int64_t hc0 = col0 + 128 * hsel;               // the half's first column
+    if (hc0 >= n) return;                                // (n < 256: no second half; uniform)
+    T128Out o;
+    o.d = reinterpret_cast<uint8_t*>(d);
+    o.row0 = row0;
+    o.col0 = hc0;
+    o.row_lo = (int)(r - row0);
+    o.row_hi = (int)(m - row0 < big::BM ? m - row0 : big::BM);
+    const int64_t clo = c - hc0, chi = (n - col0 < big::BN ? n - col0 : big::BN) - 128 * hsel;
+    o.col_lo = (int)(clo > 0 ? clo : 0);
+    o.col_hi = (int)(chi < 128 ? chi : 128);
+    o.vec = vec_out && hc0 % 8 == 0;
+    if (o.col_hi <= o.col_lo) return;                    // nothing of this half is stored (uniform)
+    const int t = threadIdx.x;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint32_t aoff[8], boff[4];
+    k128_lane_offsets(aoff, lda, m);
+    t128_lane_offsets_b(boff, ldb, n - hc0);
+    const uint8_t* at = a + row0 * lda;
+    const uint8_t* bt = b + hc0 * ldb;
+    {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem + t128::kScaleOff));
+        const int64_t rr = row0 + t, cc = hc0 + t;
+        lds_dma4(base + wave * 256, sa + (sa_vec ? (rr < m ? rr : m - 1) : 0));
+        if (wave < 2) lds_dma4(base + t128::BM * 4 + wave * 256, sb + (sb_vec ? (cc < n ? cc : n - 1) : 0));
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem + s * t128::kStage));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma16_s(base + wave * 8192 + i * 1024, at + s * k128::BK, aoff[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16_s(base + t128::kAOp + wave * 4096 + i * 1024, bt + s * k128::BK, boff[i]);
+    }
+    wait_vmcnt<12>();                                    // the scales and step 0 landed
+    __syncthreads();
+    v8i f0[6];
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        const int j = t128_frag(f);
+        f0[j] = big_join(k128_half<false>(j < 4 ? smem : smem + t128::kAOp, t128_row(j), 0, 0),
+                         k128_half<false>(j < 4 ? smem : smem + t128::kAOp, t128_row(j), 0, 1));
+    }
+    v16f acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
+    const int64_t nk = k / k128::BK;                     // even, >= 2
+    for (int64_t p = 0; p + 2 < nk; p += 2) {
+        t128_step<FA, FB, 0, true, true>(smem, acc, f0, at, aoff, bt, boff, (p + 2) * k128::BK);
+        t128_step<FA, FB, 1, true, true>(smem, acc, f0, at, aoff, bt, boff, (p + 3) * k128::BK);
+    }
+    t128_step<FA, FB, 0, true, false>(smem, acc, f0, at, aoff, bt, boff, 0);
+    t128_step<FA, FB, 1, false, false>(smem, acc, f0, at, aoff, bt, boff, 0);
+    t128_chunk<0>(smem, acc, o, ldd);
+    t128_chunk<1>(smem, acc, o, ldd);
+    t128_chunk<2>(smem, acc, o, ldd);
+    t128_chunk<3>(smem, acc, o, ldd);
+}
+
 template <int FA, int FB, bool OUT_F32>
 hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m, int64_t n, int64_t k,
                       const float* sa, int sa_vec, const float* sb, int sb_vec, void* d, int64_t ldd,
@@ -1707,8 +1962,15 @@ hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t l
         // epilogue would spill, and with one tile per workgroup it gains nothing)
         if constexpr (!OUT_F32) {
             if (big_tiles > cus && cus >= 8 && big_tiles < ((int64_t)1 << 31)) {
-                hipLaunchKernelGGL((k_gemm_persist<FA, FB, false>), dim3((unsigned)(cus / 8 * 8)), dim3(256), 0, st, a,
-                                   lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out);
+                // a last round of at most half the workgroups runs as twice as many 256 x 128 halves
+                const int64_t grid = cus / 8 * 8, rem = big_tiles % grid;
+                const int64_t limit = (rem > 0 && 2 * rem <= grid) ? big_tiles - rem : big_tiles;
+                hipLaunchKernelGGL((k_gemm_persist<FA, FB, false>), dim3((unsigned)grid), dim3(256), 0, st, a, lda, b,
+                                   ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess || limit == big_tiles) return e;
+                hipLaunchKernelGGL((k_gemm_half<FA, FB>), dim3((unsigned)(2 * rem)), dim3(256), 0, st, a, lda, b, ldb,
+                                   m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
                 return hipGetLastError();
             }
         }

@@ -187,16 +187,25 @@ def cmd_mfma(a):
 
 
 def cmd_traffic(a):
-    fetch, kname = _pick(counters(a.fetch, a.dispatch_mod, a.dispatch_rem), a.kernel)
-    write, _ = _pick(counters(a.write, a.dispatch_mod, a.dispatch_rem), a.kernel)
+    # one call of the product may launch several kernels (a persistent product
+    # and its half-tile tail): their per-dispatch bytes add up
+    ftab = counters(a.fetch, a.dispatch_mod, a.dispatch_rem)
+    wtab = counters(a.write, a.dispatch_mod, a.dispatch_rem)
+    fetch_kib, write_kib, names = 0.0, 0.0, []
+    for kern in a.kernel:
+        f, kname = _pick(ftab, kern)
+        w, _ = _pick(wtab, kern)
+        fetch_kib += f["FETCH_SIZE"]
+        write_kib += w["WRITE_SIZE"]
+        names.append(kname)
     cfetch, cname = _pick(counters(a.copy_fetch), a.copy_kernel)
     cwrite, _ = _pick(counters(a.copy_write), a.copy_kernel)
     f_read = a.copy_bytes / (cfetch["FETCH_SIZE"] * 1024.0)
     f_write = a.copy_bytes / (cwrite["WRITE_SIZE"] * 1024.0)
-    read = fetch["FETCH_SIZE"] * 1024.0 * f_read
-    written = write["WRITE_SIZE"] * 1024.0 * f_write
-    rec = {"kernel": kname, "bytes_per_launch": round(read + written), "read_bytes": round(read),
-           "write_bytes": round(written), "fetch_kib_raw": fetch["FETCH_SIZE"], "write_kib_raw": write["WRITE_SIZE"],
+    read = fetch_kib * 1024.0 * f_read
+    written = write_kib * 1024.0 * f_write
+    rec = {"kernel": " + ".join(names), "bytes_per_launch": round(read + written), "read_bytes": round(read),
+           "write_bytes": round(written), "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
            "copy_kernel": cname, "copy_bytes": a.copy_bytes, "read_factor": round(f_read, 4),
            "write_factor": round(f_write, 4), "sources": a.sources, "source_digest": source_digest(a.sources)}
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -225,8 +234,9 @@ def main(argv=None):
     mf = sub.add_parser("mfma")
     mf.add_argument("dir")
     t = sub.add_parser("traffic")
-    for opt in ("--key", "--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write", "--copy-kernel"):
+    for opt in ("--key", "--fetch", "--write", "--copy-fetch", "--copy-write", "--copy-kernel"):
         t.add_argument(opt, required=True)
+    t.add_argument("--kernel", nargs="+", required=True, help="the kernels one call launches (bytes summed)")
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--sources", nargs="+", required=True)
     for q in (mf, t):
