@@ -236,6 +236,36 @@ GROUPED_LARGE = [([0, 1000, 1, 255, 257, 0, 2583], 2048, 512, 0, 0, False),
                  ([600, 0, 3500, 100], 2048, 4096, 0, 0, False)]
 
 
+GROUPED_TAIL = [([0, 300, 1, 255, 257, 0, 700], 2300, 4352, 0, 0),
+                ([4000, 0, 1, 255, 257, 3500], 2100, 4352, 1, 0)]
+
+
+@pytest.mark.parametrize("sizes,n,k,fa,fb", GROUPED_TAIL, ids=["fewer_tiles_than_cus", "more_tiles_than_cus"])
+def test_grouped_gemm_parity_long_k_bf16(fp8, orc, sizes, n, k, fa, fb):
+    """Grouped products longer than the persistent form takes (k > 4096, bf16
+    output: one 256 x 256 tile per workgroup), with fewer (81) and more (306)
+    tiles than CUs, n off the 256 grid, empty and one-row groups. Every output
+    against the oracle."""
+    g = len(sizes)
+    offsets = np.zeros(g + 1, np.int64)
+    offsets[1:] = np.cumsum(sizes)
+    total = int(offsets[-1])
+    rng = np.random.default_rng(total + n + k + 2)
+    a = random_codes(rng, (total, k), fa)
+    b = random_codes(rng, (g, n, k), fb)
+    sa = np.exp2(rng.integers(-8, 2, total)).astype(np.float32) * np.float32(1.375)
+    sb = np.exp2(rng.integers(-8, 2, (g, n))).astype(np.float32)
+    say("grouped long k bf16", g, total, n, k, fa, fb)
+    got = gpu_grouped(fp8, a, fa, b, fb, offsets, sa, sb)
+    rows = 0
+    for e in range(g):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            rows += check_full(orc, got, orc.gemm_by_rows(a[lo:hi], fa, b[e], fb, sa[lo:hi], sb[e]),
+                               f"grouped long k group {e}", row_offset=lo)
+    assert rows == total
+
+
 GROUPED_PERSIST = [([0, 1000, 1, 255, 257, 0, 2583, 60, 700], 3000, 512, 0, 0),
                    ([100, 0, 156], 16400, 256, 1, 0),
                    ([30000, 0, 25000, 15000], 200, 256, 0, 1),
