@@ -594,12 +594,14 @@ __device__ __forceinline__ int k128_frag(int f) { return f == 0 ? 0 : (f <= 4 ? 
 //   per thread (the records xa / xb of K step 0 advanced by knext / 128 steps
 //   of xsa / xsb bytes), and step p+1's scales read into sx.
 // A step's MFMAs thus never wait for LDS reads issued after the barrier, and
-// the loads have a full step to land.
-template <int FA, int FB, int CUR, bool NEXT, bool LOADS, bool MX, bool SADDR = false>
+// the loads have a full step to land. With issue false (uniform) a LOADS step
+// skips its loads: the same code, so a K loop whose last pair loads nothing
+// needs no second copy of the steps.
+template <int FA, int FB, int CUR, bool NEXT, bool LOADS, bool MX, bool SADDR = false, bool ZERO = false>
 __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], v8i (&f0)[8], u32x4 (&sx)[2],
                                           const uint8_t* a, const uint32_t (&aoff)[8], const uint8_t* b,
                                           const uint32_t (&boff)[8], int64_t knext, const uint8_t* xa,
-                                          const uint8_t* xb, int64_t xsa, int64_t xsb) {
+                                          const uint8_t* xb, int64_t xsa, int64_t xsb, bool issue = true) {
     const uint8_t* ta = smem + CUR * k128::kStage;
     const uint8_t* tb = ta + k128::kOpBytes;
     const uint8_t* na = smem + (CUR ^ 1) * k128::kStage;
@@ -608,7 +610,7 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], v8i 
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int mi = i >> 2, ni = i & 3;
-        acc[mi][ni] = mfma64<FA, FB, MX, 0>(f0[mi], f0[4 + ni], acc[mi][ni], sx[0][mi], sx[1][ni]);
+        acc[mi][ni] = mfma64<FA, FB, MX, 0>(f0[mi], f0[4 + ni], ZERO ? v16f{} : acc[mi][ni], sx[0][mi], sx[1][ni]);
         const int j = k128_frag(i >> 1);
         h1[i] = k128_half<MX>(j < 4 ? ta : tb, big_row(j), 1, i & 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -635,7 +637,7 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], v8i 
             const int j = k128_frag(i >> 1);
             h0[i] = k128_half<MX>(j < 4 ? na : nb, big_row(j), 0, i & 1);
         }
-        if (LOADS) {
+        if (LOADS && issue) {
             if constexpr (SADDR) {
                 if (i < 8)
                     lds_dma16_s(dma_base + i * 1024, a + knext, aoff[i]);
@@ -664,7 +666,7 @@ __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], v8i 
     }
 }
 
-// The K loop of the large-tile kernels; k % 256 == 0 (k = 0: zero sums). The
+// The K loop of the large-tile kernels; k % 256 == 0, k > 0. The
 // epilogue's row and column scales go to the scale area: sa_lane / sb_lane
 // (thread t's row / column scale) or, with MX, 1 (the block scales are applied
 // inside the MFMAs; xa / xb are the K-step-0 scale records of A row mx_row(t)
@@ -700,7 +702,6 @@ __device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, i
             lds_dma4(sbase, sa_lane);
             lds_dma4(sbase + 1024, sb_lane);
         }
-        if (MX && nk == 0) return;                       // (the epilogue's barrier orders the scale area)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem + s * k128::kStage)) + wave * 8192;
@@ -729,15 +730,20 @@ __device__ __forceinline__ void k128_mainloop(uint8_t* smem, const uint8_t* a, i
             sx[1] = mx_scales(smem + big::kMxOff, 1);
         }
     }
-    for (int64_t p = 0; p + 2 < nk; p += 2) {
-        k128_step<FA, FB, 0, true, true, MX>(smem, acc, f0, sx, a, aoff, b, boff, (p + 2) * k128::BK, xa, xb, xsa,
-                                             xsb);
-        k128_step<FA, FB, 1, true, true, MX>(smem, acc, f0, sx, a, aoff, b, boff, (p + 3) * k128::BK, xa, xb, xsa,
-                                             xsb);
-    }
-    k128_step<FA, FB, 0, true, false, MX>(smem, acc, f0, sx, a, aoff, b, boff, 0, xa, xb, xsa, xsb);
-    k128_step<FA, FB, 1, false, false, MX>(smem, acc, f0, sx, a, aoff, b, boff, 0, xa, xb, xsa, xsb);
-    wait_vmcnt<0>();                                     // (nothing is outstanding: the last steps load nothing)
+    // one loop over the step pairs: one path, so the sums keep one register
+    // assignment from the zeroing to the epilogue. The last pair issues no
+    // loads; with MX it loads the tile's steps 0 and 1 again instead (valid
+    // addresses, never read: skipping the loads there costs registers)
+    int64_t p = 0;
+    do {                                                 // nk >= 2
+        const bool more = p + 2 < nk;
+        const int64_t kl = more ? (p + 2) * k128::BK : 0;
+        k128_step<FA, FB, 0, true, true, MX>(smem, acc, f0, sx, a, aoff, b, boff, kl, xa, xb, xsa, xsb, more || MX);
+        k128_step<FA, FB, 1, true, true, MX>(smem, acc, f0, sx, a, aoff, b, boff, kl + k128::BK, xa, xb, xsa, xsb,
+                                             more || MX);
+        p += 2;
+    } while (p < nk);
+    wait_vmcnt<0>();                                     // (MX: the last pair's loads landed)
 }
 
 // Staged bf16 block of the epilogue: group g of 4 rows, column c -> 8 bytes
@@ -880,6 +886,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const uint8_t* __restrict__
     big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, m - row0, col0, n - col0, vec_out);
 }
 
+// An MX tile with k = 0: zero sums, unit scales (the K loop needs k > 0).
+template <bool OUT_F32>
+__device__ __forceinline__ void mx_zero_tile(uint8_t* smem, void* __restrict__ d, int64_t ldd, int64_t row0,
+                                             int64_t rows, int64_t col0, int64_t cols, int vec_out) {
+    float* s = reinterpret_cast<float*>(smem + big::kScaleOff);
+    s[threadIdx.x] = 1.0f;                               // (the epilogue's barrier orders the scale area)
+    s[256 + threadIdx.x] = 1.0f;
+    v16f acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+    big_epilogue<OUT_F32>(smem, acc, d, ldd, row0, rows, col0, cols, vec_out);
+}
+
 // MX product: d = sum over 32-deep K blocks of the blocks' dot products times
 // 2^(xa - 127) * 2^(xb - 127), the E8M0 scales of row i's and column j's block
 // (K-step-major records: the scales of blocks 4j .. 4j+3 of row r are the
@@ -898,6 +921,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ 
     const int rt = mx_row(threadIdx.x);
     const uint8_t* xa_lane = xa + 4 * (row0 + rt < m ? row0 + rt : m - 1);
     const uint8_t* xb_lane = xb + 4 * (col0 + rt < n ? col0 + rt : n - 1);
+    if (k == 0) {
+        mx_zero_tile<OUT_F32>(smem, d, ldd, row0, m - row0, col0, n - col0, vec_out);
+        return;
+    }
     v16f acc[4][4];
     k128_mainloop<FA, FB, true>(smem, a + row0 * lda, lda, m - row0, b + col0 * ldb, ldb, n - col0, k, nullptr,
                                 nullptr, xa_lane, xb_lane, 4 * ld_xa, 4 * ld_xb, acc);
@@ -995,6 +1022,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_big(
     const int64_t pn = (lt % (gm * tiles_n)) / gsize;
     const int64_t row0 = lo + pm * big::BM, col0 = pn * big::BN;
     const uint8_t* bg = b + (int64_t)grp * b_group_stride;
+    if (MX && k == 0) {
+        mx_zero_tile<OUT_F32>(smem, d, ldd, row0, hi - row0, col0, n - col0, vec_out);
+        return;
+    }
     v16f acc[4][4];
     if constexpr (MX) {
         const int rt = mx_row(t);
@@ -1146,6 +1177,9 @@ __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4],
     uint8_t* ep = smem + persist::kEpiOff + wave * persist::kChunk;
     const int cc = lane & 15;
     const bool full_cols = vec_out && 8 * cc >= clo && 8 * cc + 8 <= chi;
+    // the wavefront stores all its 128 x 128 outputs as 16-byte vectors
+    // (uniform: most tiles), with no per-row or per-column test
+    const bool whole = vec_out && rlo <= 0 && rhi >= 128 && clo <= 0 && chi >= 128;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -1176,16 +1210,27 @@ __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4],
             u32x4 un[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) un[k] = *reinterpret_cast<const u32x4*>(ep + epi_off(gl, 8 * cc + 2 * k));
+            u32x4 rows[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
+                const int wlo = (r >> 1), whi = 2 + (r >> 1);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) rows[r][k] = __builtin_amdgcn_perm(un[k][whi], un[k][wlo], sel);
+            }
+            uint16_t* dst0 = reinterpret_cast<uint16_t*>(d) + (wrow0 + 4 * g) * ldd + wcol0 + 8 * cc;
+            if (whole) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    __builtin_nontemporal_store(rows[r], reinterpret_cast<u32x4*>(dst0 + r * ldd));
+                continue;
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int lr = 4 * g + r;
                 if (lr < rlo || lr >= rhi) continue;
-                const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
-                const int wlo = (r >> 1), whi = 2 + (r >> 1);
-                u32x4 row;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) row[k] = __builtin_amdgcn_perm(un[k][whi], un[k][wlo], sel);
-                uint16_t* dst = reinterpret_cast<uint16_t*>(d) + (wrow0 + lr) * ldd + wcol0 + 8 * cc;
+                const u32x4 row = rows[r];
+                uint16_t* dst = dst0 + r * ldd;
                 if (full_cols) {
                     __builtin_nontemporal_store(row, reinterpret_cast<u32x4*>(dst));
                 } else {
@@ -1274,12 +1319,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restri
                          k128_half<false>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 1));
     }
     for (;;) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
         const int64_t nid = id + G;
         const int64_t crow0 = row0, ccol0 = col0;
         const int crow_lo = row_lo, ccol_lo = col_lo;
@@ -1296,7 +1335,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restri
         }
         // steps p, p+1 load steps p+2, p+3; the last pair loads the next tile's
         // steps 0 and 1, and its second step reads the next tile's first fragments
-        for (int64_t p = 0; p < nk; p += 2) {
+        // the first step's MFMAs start the sums from zero (no zeroing pass)
+        {
+            const bool last = 2 >= nk;
+            const uint8_t* la = last ? nat : at;
+            const uint8_t* lb = last ? nbt : bt;
+            const int64_t kl = last ? 0 : 2 * k128::BK;
+            k128_step<FA, FB, 0, true, true, false, true, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl, nullptr,
+                                                                nullptr, 0, 0);
+            k128_step<FA, FB, 1, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl + k128::BK, nullptr,
+                                                          nullptr, 0, 0);
+        }
+        for (int64_t p = 2; p < nk; p += 2) {
             const bool last = p + 2 >= nk;
             const uint8_t* la = last ? nat : at;
             const uint8_t* lb = last ? nbt : bt;
@@ -1489,12 +1539,6 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_persist(
                          k128_half<false>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 1));
     }
     for (;;) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
         const uint32_t nid = id + G;
         const GpTile done = cur;
         const uint8_t* nat = at;                         // with no next tile: this tile's own first
@@ -1504,13 +1548,18 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_persist(
             nat = a + cur.row0 * lda;
             nbt = b + (int64_t)cur.grp * b_group_stride + cur.col0 * ldb;
         }
-        for (int64_t p = 0; p < nk; p += 2) {
+        // the first step's MFMAs start the sums from zero (no zeroing pass)
+        for (int64_t p = 0; p < nk; p += 2) {            // nk >= 2
             const bool last = p + 2 >= nk;
             const uint8_t* la = last ? nat : at;
             const uint8_t* lb = last ? nbt : bt;
             const int64_t kl = last ? 0 : (p + 2) * k128::BK;
-            k128_step<FA, FB, 0, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl, nullptr, nullptr, 0,
-                                                          0);
+            if (p == 0)
+                k128_step<FA, FB, 0, true, true, false, true, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl, nullptr,
+                                                                    nullptr, 0, 0);
+            else
+                k128_step<FA, FB, 0, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl, nullptr,
+                                                              nullptr, 0, 0);
             k128_step<FA, FB, 1, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl + k128::BK, nullptr,
                                                           nullptr, 0, 0);
         }
@@ -1649,6 +1698,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k_persist(
                                  k128_half<false>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 1));
             }
         }
+        const int64_t rhi = m - cur.row0, chi = n - cur.col0;
+        uint8_t* dg = reinterpret_cast<uint8_t*>(d) + (int64_t)cur.grp * d_group_stride * 2;
+        const int row_hi = (int)(rhi < 256 ? rhi : 256), col_hi = (int)(chi < 256 ? chi : 256);
+        const int vo = vec_out && cur.col0 % 8 == 0;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -1663,7 +1716,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k_persist(
             const uint8_t* nat = pre ? a + nxt.row0 * lda + nxt.p : at;
             const uint8_t* nbt = pre ? b + nxt.col0 * ldb + nxt.p : bt;
             const int64_t nk = cur.k / k128::BK;         // even, >= 2
-            for (int64_t p = 0; p < nk; p += 2) {
+            int64_t p = 0;
+            do {
                 const bool last = p + 2 >= nk;
                 const uint8_t* la = last ? nat : at;
                 const uint8_t* lb = last ? nbt : bt;
@@ -1672,8 +1726,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k_persist(
                                                               nullptr, 0, 0);
                 k128_step<FA, FB, 1, true, true, false, true>(smem, acc, f0, sx, la, aoff, lb, boff, kl + k128::BK,
                                                               nullptr, nullptr, 0, 0);
-            }
+                p += 2;
+            } while (p < nk);
             loaded = pre;
+            chunk_epilogue<false>(smem, acc, dg, ldd, cur.row0, cur.row_lo, row_hi, cur.col0, cur.col_lo, col_hi, vo);
         } else {                                         // empty group: 0 * sa * sb (cut: NaN row scales)
             wait_vmcnt<0>();
             __syncthreads();                             // every thread's scale loads landed
@@ -1682,11 +1738,18 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k_persist(
                 __syncthreads();
             }
             loaded = false;
+            // (its own epilogue call: the sums of the K loop and these zeros
+            // keep separate registers, with no copies between them)
+            v16f zero[4][4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) zero[mi][ni][r] = 0.0f;
+            chunk_epilogue<false>(smem, zero, dg, ldd, cur.row0, cur.row_lo, row_hi, cur.col0, cur.col_lo, col_hi,
+                                  vo);
         }
-        const int64_t rhi = m - cur.row0, chi = n - cur.col0;
-        uint8_t* dg = reinterpret_cast<uint8_t*>(d) + (int64_t)cur.grp * d_group_stride * 2;
-        chunk_epilogue<false>(smem, acc, dg, ldd, cur.row0, cur.row_lo, (int)(rhi < 256 ? rhi : 256), cur.col0,
-                              cur.col_lo, (int)(chi < 256 ? chi : 256), vec_out && cur.col0 % 8 == 0);
         if (!more) break;
         cur = nxt;
         __syncthreads();                                 // every wavefront is done with the scale area
@@ -1746,7 +1809,7 @@ __device__ __forceinline__ void t128_lane_offsets_b(uint32_t (&off)[4], int64_t 
 template <int FA, int FB, int CUR, bool NEXT, bool LOADS>
 __device__ __forceinline__ void t128_step(uint8_t* smem, v16f (&acc)[4][2], v8i (&f0)[6], const uint8_t* a,
                                          const uint32_t (&aoff)[8], const uint8_t* b, const uint32_t (&boff)[4],
-                                         int64_t knext) {
+                                         int64_t knext, bool issue = true) {
     const uint8_t* ta = smem + CUR * t128::kStage;
     const uint8_t* tb = ta + t128::kAOp;
     const uint8_t* na = smem + (CUR ^ 1) * t128::kStage;
@@ -1780,7 +1843,7 @@ __device__ __forceinline__ void t128_step(uint8_t* smem, v16f (&acc)[4][2], v8i 
             h0[2 * i] = k128_half<false>(j < 4 ? na : nb, t128_row(j), 0, 0);
             h0[2 * i + 1] = k128_half<false>(j < 4 ? na : nb, t128_row(j), 0, 1);
         }
-        if (LOADS) {
+        if (LOADS && issue) {
             lds_dma16_s(base + wave * 8192 + i * 1024, a + knext, aoff[i]);
             if (i >= 4) lds_dma16_s(base + t128::kAOp + wave * 4096 + (i - 4) * 1024, b + knext, boff[i - 4]);
         }
@@ -1936,12 +1999,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_half(const uint8_t* __restrict_
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
     const int64_t nk = k / k128::BK;                     // even, >= 2
-    for (int64_t p = 0; p + 2 < nk; p += 2) {
-        t128_step<FA, FB, 0, true, true>(smem, acc, f0, at, aoff, bt, boff, (p + 2) * k128::BK);
-        t128_step<FA, FB, 1, true, true>(smem, acc, f0, at, aoff, bt, boff, (p + 3) * k128::BK);
-    }
-    t128_step<FA, FB, 0, true, false>(smem, acc, f0, at, aoff, bt, boff, 0);
-    t128_step<FA, FB, 1, false, false>(smem, acc, f0, at, aoff, bt, boff, 0);
+    int64_t p = 0;
+    do {                                                 // one path (the last pair loads nothing)
+        const bool more = p + 2 < nk;
+        t128_step<FA, FB, 0, true, true>(smem, acc, f0, at, aoff, bt, boff, (p + 2) * k128::BK, more);
+        t128_step<FA, FB, 1, true, true>(smem, acc, f0, at, aoff, bt, boff, (p + 3) * k128::BK, more);
+        p += 2;
+    } while (p < nk);
     t128_chunk<0>(smem, acc, o, ldd);
     t128_chunk<1>(smem, acc, o, ldd);
     t128_chunk<2>(smem, acc, o, ldd);
