@@ -1247,19 +1247,45 @@ __device__ __forceinline__ void col_tile(const uint16_t* __restrict__ x, int64_t
     col_tile_store(tile, c0, cols, qt, ldqt, d0, d_end, vec_store);
 }
 
+// The colwise cast's workgroup takes kColTilesPerWg tiles side by side (128
+// rows x 256 columns): its loads of one row are a 512-byte run, and all 16 of a
+// thread's loads are issued before the first is cast. The grid's x runs over
+// the column blocks, so workgroups dispatched together read neighbouring runs
+// of the same rows; y (plus y_base, for grids over 65535 row tiles) over the
+// row tiles. The row tile 0 workgroups write scale_inv.
+constexpr int kColTilesPerWg = 4;
+
 template <int F>
 __global__ __launch_bounds__(kBlock) void k_quant_col_tiled(const uint16_t* __restrict__ x, int64_t rows,
                                                             int64_t cols, int64_t ldx, int margin,
                                                             uint8_t* __restrict__ qt, int64_t ldqt,
                                                             float* __restrict__ scale_inv,
-                                                            const float* __restrict__ col_amax, int vec_store) {
-    __shared__ float s_lds[kColTileC];
-    __shared__ int nan_lds[kColTileC];
-    __shared__ __attribute__((aligned(16))) uint32_t tile[kColTileC * kColTileR / 4];
-    const int64_t c0 = (int64_t)blockIdx.y * kColTileC;
-    const int64_t r0 = (int64_t)blockIdx.x * kColTileR;
-    col_scales_to_lds<F>(col_amax, c0, cols, margin, blockIdx.x == 0 ? scale_inv : nullptr, s_lds, nan_lds);
-    col_tile<F>(x, ldx, r0, rows, false, c0, cols, s_lds, nan_lds, tile, qt, ldqt, r0, rows, vec_store);
+                                                            const float* __restrict__ col_amax, int vec_store,
+                                                            int64_t y_base) {
+    constexpr int SC = kColTilesPerWg;
+    __shared__ float s_lds[kColTileC * SC];
+    __shared__ int nan_lds[kColTileC * SC];
+    __shared__ __attribute__((aligned(16))) uint32_t tile[SC][kColTileC * kColTileR / 4];
+    const int64_t c0 = (int64_t)blockIdx.x * kColTileC * SC;
+    const int64_t ty = y_base + blockIdx.y;
+    const int64_t r0 = ty * kColTileR;
+    if (threadIdx.x < kColTileC * SC) {
+        const int64_t c = c0 + threadIdx.x;
+        const float a = c < cols ? col_amax[c] : 0.0f;
+        const float sc = scale_from_amax<F>(a, margin);
+        s_lds[threadIdx.x] = sc;
+        nan_lds[threadIdx.x] = __builtin_isnan(a) ? 1 : 0;
+        if (ty == 0 && c < cols) scale_inv[c] = 1.0f / sc;
+    }
+    uint4 v[SC][4];
+#pragma unroll
+    for (int j = 0; j < SC; ++j) col_tile_load(v[j], x, ldx, r0, rows, false, c0 + kColTileC * j, cols);
+    __syncthreads();                                     // the column scales are in LDS
+#pragma unroll
+    for (int j = 0; j < SC; ++j) col_tile_encode<F>(v[j], s_lds + kColTileC * j, nan_lds + kColTileC * j, tile[j]);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SC; ++j) col_tile_store(tile[j], c0 + kColTileC * j, cols, qt, ldqt, r0, rows, vec_store);
 }
 
 // Dual cast of one tensor (rowwise codes and colwise-transposed codes, e.g.
@@ -1834,9 +1860,15 @@ hipError_t quant_col_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
     }
     if (vec_in) {
         const int vec_store = is_aligned(qt, 16) && ldqt % 16 == 0;
-        const dim3 grid((unsigned)((rows + kColTileR - 1) / kColTileR), (unsigned)((cols + kColTileC - 1) / kColTileC));
-        hipLaunchKernelGGL((k_quant_col_tiled<F>), grid, dim3(kBlock), 0, st, x, rows, cols, ldx, margin, qt, ldqt,
-                           scale_inv, col_amax, vec_store);
+        const int64_t gx = (cols + kColTileC * kColTilesPerWg - 1) / (kColTileC * kColTilesPerWg);
+        const int64_t ty = (rows + kColTileR - 1) / kColTileR;
+        for (int64_t y0 = 0; y0 < ty; y0 += 65535) {     // the grid's y is at most 65535
+            const int64_t gy = ty - y0 < 65535 ? ty - y0 : 65535;
+            hipLaunchKernelGGL((k_quant_col_tiled<F>), dim3((unsigned)gx, (unsigned)gy), dim3(kBlock), 0, st, x, rows,
+                               cols, ldx, margin, qt, ldqt, scale_inv, col_amax, vec_store, y0);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     } else {
         const dim3 grid((unsigned)((rows + kColRows - 1) / kColRows), (unsigned)((cols + kBlock - 1) / kBlock));
         hipLaunchKernelGGL((k_quant_col_scalar<F>), grid, dim3(kBlock), 0, st, x, rows, cols, ldx, margin, qt, ldqt,

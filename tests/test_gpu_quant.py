@@ -272,6 +272,19 @@ def test_quantize_col_layouts(fp8, orc, fmt, shape, ldqt):
     assert_f32_bits_equal(si, osi, "scale_inv")
 
 
+def test_quantize_col_over_65535_row_tiles(fp8, orc):
+    """More row tiles of 128 than one launch's grid y holds (65535): the cast
+    takes a second launch for the rows past 65535 * 128."""
+    rows, cols = 65535 * 128 + 200, 16
+    xb = rand_bf16(rows, cols, seed=23)
+    say("col over 65535 row tiles", rows, cols)
+    qt, si, ca = gpu_col(fp8, xb, 0, margin=1)
+    oqt, osi, oam = orc.quantize_col(xb, 0, 1)
+    assert_codes_equal(qt, oqt, "codes")
+    assert_f32_bits_equal(si, osi, "scale_inv")
+    assert_f32_bits_equal(ca, oam, "col amax")
+
+
 def test_quantize_col_with_ready_amax(fp8, orc):
     xb = rand_bf16(300, 136, seed=9)
     ready = orc.amax(xb, orc.AXIS_COL)
