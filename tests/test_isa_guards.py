@@ -48,7 +48,8 @@ def test_m0_only_feeds_direct_loads(asm):
         lines = [l.strip() for l in body.splitlines() if l.strip() and not l.strip().startswith(";")]
         for i, l in enumerate(lines):
             if re.search(r"\bm0\b", l):
-                assert re.match(r"s_mov_b32 m0, s\d+$", l), (kname, l)
+                # (from any scalar register: vcc_lo is one the allocator also hands out)
+                assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", l), (kname, l)
                 # one wait state before a load with a VGPR address; five before one
                 # whose SGPR base came from v_readfirstlane
                 assert lines[i + 1] in ("s_nop 0", "s_nop 4") and \
