@@ -1136,7 +1136,7 @@ constexpr int kSmem = big::kSmem + 4 * kChunk;       // 146 KB
 // stores rows row0 + [row_lo, row_hi) and columns col0 + [col_lo, col_hi),
 // d = acc * sa_row * sb_col with the tile's 256 row and 256 column scales in
 // the scale area; the stages are untouched.
-template <bool OUT_F32>
+template <bool OUT_F32, bool UNI = false>
 __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4], void* __restrict__ d, int64_t ldd,
                                                int64_t row0, int row_lo, int row_hi, int64_t col0, int col_lo,
                                                int col_hi, int vec_out) {
@@ -1157,6 +1157,9 @@ __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4],
     float sbj[4];
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) sbj[ni] = s_cols[wn * 128 + ni * 32 + (lane & 31)];
+    // UNI: one scale pair for the whole product (both scales scalar), applied
+    // as one factor sa * sb
+    const float sab = s_rows[0] * s_cols[0];
     if (OUT_F32) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
@@ -1169,7 +1172,8 @@ __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4],
                 for (int ni = 0; ni < 4; ++ni) {
                     const int lc = ni * 32 + (lane & 31);
                     if (lc < clo || lc >= chi) continue;
-                    reinterpret_cast<float*>(d)[(wrow0 + lr) * ldd + wcol0 + lc] = acc[mi][ni][r] * sai * sbj[ni];
+                    reinterpret_cast<float*>(d)[(wrow0 + lr) * ldd + wcol0 + lc] =
+                        UNI ? acc[mi][ni][r] * sab : acc[mi][ni][r] * sai * sbj[ni];
                 }
             }
         return;
@@ -1193,10 +1197,16 @@ __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4],
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni) {
                     const int r = 4 * q;
-                    v2f v01 = {acc[mi][ni][r] * __uint_as_float(s4[0]) * sbj[ni],
-                               acc[mi][ni][r + 1] * __uint_as_float(s4[1]) * sbj[ni]};
-                    v2f v23 = {acc[mi][ni][r + 2] * __uint_as_float(s4[2]) * sbj[ni],
-                               acc[mi][ni][r + 3] * __uint_as_float(s4[3]) * sbj[ni]};
+                    v2f v01, v23;
+                    if constexpr (UNI) {
+                        v01 = v2f{acc[mi][ni][r] * sab, acc[mi][ni][r + 1] * sab};
+                        v23 = v2f{acc[mi][ni][r + 2] * sab, acc[mi][ni][r + 3] * sab};
+                    } else {
+                        v01 = v2f{acc[mi][ni][r] * __uint_as_float(s4[0]) * sbj[ni],
+                                  acc[mi][ni][r + 1] * __uint_as_float(s4[1]) * sbj[ni]};
+                        v23 = v2f{acc[mi][ni][r + 2] * __uint_as_float(s4[2]) * sbj[ni],
+                                  acc[mi][ni][r + 3] * __uint_as_float(s4[3]) * sbj[ni]};
+                    }
                     uint2 w;
                     w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, v2bf));
                     w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, v2bf));
@@ -1260,7 +1270,9 @@ __device__ __forceinline__ void tile_coords32(uint32_t bid, uint32_t tiles_m, ui
     *pn = u / gsize;
 }
 
-template <int FA, int FB, bool OUT_F32>
+// UNI: both scales scalar (one scale pair for the whole product), applied as
+// the single factor sa * sb.
+template <int FA, int FB, bool OUT_F32, bool UNI>
 __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restrict__ a, int64_t lda,
                                                          const uint8_t* __restrict__ b, int64_t ldb, int64_t m,
                                                          int64_t n, int64_t k, const float* __restrict__ sa,
@@ -1359,8 +1371,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restri
         at = nat;
         bt = nbt;
         const int64_t rhi = m - crow0, chi = n - ccol0;
-        chunk_epilogue<OUT_F32>(smem, acc, d, ldd, crow0, crow_lo, (int)(rhi < 256 ? rhi : 256), ccol0, ccol_lo,
-                                (int)(chi < 256 ? chi : 256), vec_out && ccol0 % 8 == 0);
+        chunk_epilogue<OUT_F32, UNI>(smem, acc, d, ldd, crow0, crow_lo, (int)(rhi < 256 ? rhi : 256), ccol0, ccol_lo,
+                                     (int)(chi < 256 ? chi : 256), vec_out && ccol0 % 8 == 0);
         if (nid >= nt) break;
         id = nid;
         __syncthreads();                                 // every wavefront is done with the scale area
@@ -1868,7 +1880,7 @@ struct T128Out {
 // 64 columns; d = acc * sa_row * sb_col, staged through the wavefront's LDS
 // chunk (4-row groups g: column c at g * 512 + unit (c / 2, swizzled) * 16 +
 // (c % 2) * 8) and stored as 16-byte row pieces, 8 lanes per 128-byte row.
-template <int MI>
+template <int MI, bool UNI>
 __device__ __forceinline__ void t128_chunk(uint8_t* smem, v16f (&acc)[4][2], const T128Out& o, int64_t ldd) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
@@ -1886,6 +1898,7 @@ __device__ __forceinline__ void t128_chunk(uint8_t* smem, v16f (&acc)[4][2], con
         const int u = c >> 1;
         return g * 512 + (((u & ~3) | ((u ^ (u >> 3)) & 3)) << 4) + ((c & 1) << 3);
     };
+    const float sab = s_rows[0] * s_cols[0];             // UNI: one scale pair, one factor
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
         const float sb = s_cols[c0 + ni * 32 + (lane & 31)];
@@ -1894,9 +1907,15 @@ __device__ __forceinline__ void t128_chunk(uint8_t* smem, v16f (&acc)[4][2], con
             const int g = 2 * q + (lane >> 5);           // rows 4g .. 4g+3 of the chunk
             const u32x4 s4 = *reinterpret_cast<const u32x4*>(&s_rows[r0 + 4 * g]);
             const int r = 4 * q;
-            v2f v01 = {acc[MI][ni][r] * __uint_as_float(s4[0]) * sb, acc[MI][ni][r + 1] * __uint_as_float(s4[1]) * sb};
-            v2f v23 = {acc[MI][ni][r + 2] * __uint_as_float(s4[2]) * sb,
-                       acc[MI][ni][r + 3] * __uint_as_float(s4[3]) * sb};
+            v2f v01, v23;
+            if constexpr (UNI) {
+                v01 = v2f{acc[MI][ni][r] * sab, acc[MI][ni][r + 1] * sab};
+                v23 = v2f{acc[MI][ni][r + 2] * sab, acc[MI][ni][r + 3] * sab};
+            } else {
+                v01 = v2f{acc[MI][ni][r] * __uint_as_float(s4[0]) * sb, acc[MI][ni][r + 1] * __uint_as_float(s4[1]) * sb};
+                v23 = v2f{acc[MI][ni][r + 2] * __uint_as_float(s4[2]) * sb,
+                          acc[MI][ni][r + 3] * __uint_as_float(s4[3]) * sb};
+            }
             uint2 w;
             w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v01, v2bf));
             w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v23, v2bf));
@@ -1934,7 +1953,7 @@ __device__ __forceinline__ void t128_chunk(uint8_t* smem, v16f (&acc)[4][2], con
 // One 256 x 128 half of tile `first + blockIdx.x / 2` in k_gemm_persist's
 // order: the tile's rows and columns as that kernel would take them (edge
 // tiles shifted back), the half's 128 columns from col0 + 128 (blockIdx.x % 2).
-template <int FA, int FB>
+template <int FA, int FB, bool UNI>
 __global__ __launch_bounds__(256, 1) void k_gemm_half(const uint8_t* __restrict__ a, int64_t lda,
                                                       const uint8_t* __restrict__ b, int64_t ldb, int64_t m, int64_t n,
                                                       int64_t k, const float* __restrict__ sa, int sa_vec,
@@ -2006,10 +2025,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_half(const uint8_t* __restrict_
         t128_step<FA, FB, 1, true, true>(smem, acc, f0, at, aoff, bt, boff, (p + 3) * k128::BK, more);
         p += 2;
     } while (p < nk);
-    t128_chunk<0>(smem, acc, o, ldd);
-    t128_chunk<1>(smem, acc, o, ldd);
-    t128_chunk<2>(smem, acc, o, ldd);
-    t128_chunk<3>(smem, acc, o, ldd);
+    t128_chunk<0, UNI>(smem, acc, o, ldd);
+    t128_chunk<1, UNI>(smem, acc, o, ldd);
+    t128_chunk<2, UNI>(smem, acc, o, ldd);
+    t128_chunk<3, UNI>(smem, acc, o, ldd);
 }
 
 template <int FA, int FB, bool OUT_F32>
@@ -2029,12 +2048,22 @@ hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t l
                 // a last round of at most half the workgroups runs as twice as many 256 x 128 halves
                 const int64_t grid = cus / 8 * 8, rem = big_tiles % grid;
                 const int64_t limit = (rem > 0 && 2 * rem <= grid) ? big_tiles - rem : big_tiles;
-                hipLaunchKernelGGL((k_gemm_persist<FA, FB, false>), dim3((unsigned)grid), dim3(256), 0, st, a, lda, b,
-                                   ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
+                // scalar scales take the kernels' one-factor epilogue
+                const bool uni = !sa_vec && !sb_vec;
+                if (uni)
+                    hipLaunchKernelGGL((k_gemm_persist<FA, FB, false, true>), dim3((unsigned)grid), dim3(256), 0, st, a,
+                                       lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
+                else
+                    hipLaunchKernelGGL((k_gemm_persist<FA, FB, false, false>), dim3((unsigned)grid), dim3(256), 0, st, a,
+                                       lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
                 hipError_t e = hipGetLastError();
                 if (e != hipSuccess || limit == big_tiles) return e;
-                hipLaunchKernelGGL((k_gemm_half<FA, FB>), dim3((unsigned)(2 * rem)), dim3(256), 0, st, a, lda, b, ldb,
-                                   m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
+                if (uni)
+                    hipLaunchKernelGGL((k_gemm_half<FA, FB, true>), dim3((unsigned)(2 * rem)), dim3(256), 0, st, a, lda,
+                                       b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
+                else
+                    hipLaunchKernelGGL((k_gemm_half<FA, FB, false>), dim3((unsigned)(2 * rem)), dim3(256), 0, st, a,
+                                       lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
                 return hipGetLastError();
             }
         }

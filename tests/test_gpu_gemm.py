@@ -198,6 +198,22 @@ def test_gemm_parity_large_tiles(fp8, orc, shape, fa, fb, out_f32, ldd):
     assert_within(orc, got, y, bound, not out_f32, f"large {shape}")
 
 
+@pytest.mark.parametrize("shape,fa,fb", [((2304, 8192, 256), 0, 0), ((2350, 8100, 512), 1, 0)])
+def test_gemm_parity_persistent_scalar_scales(fp8, orc, shape, fa, fb):
+    """One scale per operand (tensorwise recipes): the persistent kernel and its
+    half-tile tail apply sa * sb as one factor. 288 / 320 tiles of 256 x 256:
+    one round of 256 plus a tail of 32 / 64 tiles run as 256 x 128 halves;
+    the second shape has ragged edges."""
+    m, n, k = shape
+    a, _ = operands(orc, m, k, fa, seed=m + 5)
+    b, _ = operands(orc, n, k, fb, seed=n + 6)
+    sa, sb = np.array([0.37], np.float32), np.array([2.5], np.float32)
+    say("gemm persistent scalar scales", shape, fa, fb)
+    y, bound = orc.gemm(a, fa, b, fb, sa, sb)
+    got = gpu_gemm(fp8, a, fa, b, fb, sa, sb, 0, 0)
+    assert_within(orc, got, y, bound, True, f"scalar scales {shape}")
+
+
 @pytest.mark.parametrize("fa,fb", [(1, 0), (0, 0)])
 def test_gemm_full_output_long_k(fp8, orc, fa, fb):
     """K = 14336 (the Llama3-8B backward's dgrad contraction) on 17 x 16 tiles of
