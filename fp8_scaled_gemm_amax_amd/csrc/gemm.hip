@@ -1136,7 +1136,7 @@ constexpr int kSmem = big::kSmem + 4 * kChunk;       // 146 KB
 // stores rows row0 + [row_lo, row_hi) and columns col0 + [col_lo, col_hi),
 // d = acc * sa_row * sb_col with the tile's 256 row and 256 column scales in
 // the scale area; the stages are untouched.
-template <bool OUT_F32, bool UNI = false>
+template <bool OUT_F32, bool UNI = false, int EPI = persist::kEpiOff>
 __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4], void* __restrict__ d, int64_t ldd,
                                                int64_t row0, int row_lo, int row_hi, int64_t col0, int col_lo,
                                                int col_hi, int vec_out) {
@@ -1178,7 +1178,7 @@ __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4],
             }
         return;
     }
-    uint8_t* ep = smem + persist::kEpiOff + wave * persist::kChunk;
+    uint8_t* ep = smem + EPI + wave * persist::kChunk;
     const int cc = lane & 15;
     const bool full_cols = vec_out && 8 * cc >= clo && 8 * cc + 8 <= chi;
     // the wavefront stores all its 128 x 128 outputs as 16-byte vectors
@@ -1377,6 +1377,139 @@ __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restri
         id = nid;
         __syncthreads();                                 // every wavefront is done with the scale area
         issue_scales(row0, col0);                        // (landed by the next tile's first mid-step wait)
+    }
+    wait_vmcnt<0>();
+}
+
+// Persistent MX product (bf16 output, k >= 256, more tiles than CUs): the
+// tiles of k_gemm_mx taken as k_gemm_persist takes dense ones (the next tile's
+// first two K steps, with their scale records, load during the current tile's
+// last two; edge tiles shifted back). The block scales are applied inside the
+// MFMAs, so the epilogue's scale area holds ones. LDS: the stages, the unit
+// scale area and the two record stages of k_gemm_mx, then the chunk epilogue's
+// area.
+namespace persist_mx {
+constexpr int kEpiOff = big::kSmemMx;
+constexpr int kSmem = big::kSmemMx + 4 * persist::kChunk;   // 150 KB
+}  // namespace persist_mx
+
+template <int FA, int FB>
+__global__ __launch_bounds__(256, 1) void k_gemm_persist_mx(const uint8_t* __restrict__ a, int64_t lda,
+                                                            const uint8_t* __restrict__ xa, int64_t ld_xa,
+                                                            const uint8_t* __restrict__ b, int64_t ldb,
+                                                            const uint8_t* __restrict__ xb, int64_t ld_xb, int64_t m,
+                                                            int64_t n, int64_t k, void* __restrict__ d, int64_t ldd,
+                                                            int vec_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[persist_mx::kSmem];
+    const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
+    const int64_t nt = tiles_m * tiles_n, G = gridDim.x;
+    const int t = threadIdx.x;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nk = k / k128::BK;                     // even, >= 2
+    auto lrow = [&](int64_t pm) {
+        const int64_t r = pm * big::BM;
+        return (r + big::BM > m && m >= big::BM) ? m - big::BM : r;
+    };
+    auto lcol = [&](int64_t pn) {
+        const int64_t c = pn * big::BN;
+        return (c + big::BN > n && n >= big::BN) ? n - big::BN : c;
+    };
+    // thread t's K-step-0 scale records: A row / B row mx_row(t) of the tile
+    const int rt = mx_row(t);
+    auto xa_of = [&](int64_t r0) { return xa + 4 * (r0 + rt < m ? r0 + rt : m - 1); };
+    auto xb_of = [&](int64_t c0) { return xb + 4 * (c0 + rt < n ? c0 + rt : n - 1); };
+    const int64_t xsa = 4 * ld_xa, xsb = 4 * ld_xb;
+    uint32_t aoff[8], boff[8];
+    k128_lane_offsets(aoff, lda, m);
+    k128_lane_offsets(boff, ldb, n);
+    int64_t id = blockIdx.x;                             // < nt (grid <= nt)
+    int64_t pm, pn;
+    tile_coords32((uint32_t)id, (uint32_t)tiles_m, (uint32_t)tiles_n, &pm, &pn);
+    int64_t row0 = lrow(pm), col0 = lcol(pn);
+    int row_lo = (int)(pm * big::BM - row0), col_lo = (int)(pn * big::BN - col0);
+    {
+        float* sc = reinterpret_cast<float*>(smem + big::kScaleOff);
+        sc[t] = 1.0f;                                    // (ordered by the barrier below)
+        sc[256 + t] = 1.0f;
+    }
+    const uint8_t* at = a + row0 * lda;
+    const uint8_t* bt = b + col0 * ldb;
+    const uint8_t* xat = xa_of(row0);
+    const uint8_t* xbt = xb_of(col0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem + s * k128::kStage)) + wave * 8192;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma16_s(base + i * 1024, at + s * k128::BK, aoff[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds_dma16_s(base + k128::kOpBytes + i * 1024, bt + s * k128::BK, boff[i]);
+        const uint32_t xbase =
+            __builtin_amdgcn_readfirstlane(lds_addr(smem + big::kMxOff + s * big::kMxStage)) + wave * 256;
+        lds_dma4(xbase, xat + s * xsa);
+        lds_dma4(xbase + 1024, xbt + s * xsb);
+    }
+    wait_vmcnt<18>();                                    // step 0 and its records landed
+    v16f acc[4][4];
+    v8i f0[8];
+    u32x4 sx[2];
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        const int j = k128_frag(f);
+        f0[j] = big_join(k128_half<true>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 0),
+                         k128_half<true>(j < 4 ? smem : smem + k128::kOpBytes, big_row(j), 0, 1));
+    }
+    sx[0] = mx_scales(smem + big::kMxOff, 0);
+    sx[1] = mx_scales(smem + big::kMxOff, 1);
+    for (;;) {
+        const int64_t nid = id + G;
+        const int64_t crow0 = row0, ccol0 = col0;
+        const int crow_lo = row_lo, ccol_lo = col_lo;
+        const uint8_t* nat = at;                         // with no next tile: this tile's own first
+        const uint8_t* nbt = bt;                         // steps (valid addresses, never used)
+        const uint8_t* nxat = xat;
+        const uint8_t* nxbt = xbt;
+        if (nid < nt) {
+            tile_coords32((uint32_t)nid, (uint32_t)tiles_m, (uint32_t)tiles_n, &pm, &pn);
+            row0 = lrow(pm);
+            col0 = lcol(pn);
+            row_lo = (int)(pm * big::BM - row0);
+            col_lo = (int)(pn * big::BN - col0);
+            nat = a + row0 * lda;
+            nbt = b + col0 * ldb;
+            nxat = xa_of(row0);
+            nxbt = xb_of(col0);
+        }
+        // the first step's MFMAs start the sums from zero
+        {
+            const bool last = 2 >= nk;
+            const int64_t kl = last ? 0 : 2 * k128::BK;
+            k128_step<FA, FB, 0, true, true, true, true, true>(smem, acc, f0, sx, last ? nat : at, aoff,
+                                                               last ? nbt : bt, boff, kl, last ? nxat : xat,
+                                                               last ? nxbt : xbt, xsa, xsb);
+            k128_step<FA, FB, 1, true, true, true, true>(smem, acc, f0, sx, last ? nat : at, aoff, last ? nbt : bt,
+                                                         boff, kl + k128::BK, last ? nxat : xat, last ? nxbt : xbt,
+                                                         xsa, xsb);
+        }
+        for (int64_t p = 2; p < nk; p += 2) {
+            const bool last = p + 2 >= nk;
+            const int64_t kl = last ? 0 : (p + 2) * k128::BK;
+            k128_step<FA, FB, 0, true, true, true, true>(smem, acc, f0, sx, last ? nat : at, aoff, last ? nbt : bt,
+                                                         boff, kl, last ? nxat : xat, last ? nxbt : xbt, xsa, xsb);
+            k128_step<FA, FB, 1, true, true, true, true>(smem, acc, f0, sx, last ? nat : at, aoff, last ? nbt : bt,
+                                                         boff, kl + k128::BK, last ? nxat : xat, last ? nxbt : xbt,
+                                                         xsa, xsb);
+        }
+        at = nat;
+        bt = nbt;
+        xat = nxat;
+        xbt = nxbt;
+        const int64_t rhi = m - crow0, chi = n - ccol0;
+        chunk_epilogue<false, true, persist_mx::kEpiOff>(smem, acc, d, ldd, crow0, crow_lo,
+                                                         (int)(rhi < 256 ? rhi : 256), ccol0, ccol_lo,
+                                                         (int)(chi < 256 ? chi : 256), vec_out && ccol0 % 8 == 0);
+        if (nid >= nt) break;
+        id = nid;
     }
     wait_vmcnt<0>();
 }
@@ -2118,6 +2251,14 @@ hipError_t gemm_mx_typed(const uint8_t* a, int64_t lda, const uint8_t* xa, int64
     const int64_t tiles = ((m + big::BM - 1) / big::BM) * ((n + big::BN - 1) / big::BN);
     if (tiles == 0) return hipSuccess;
     const int vec_out = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ldd % 8 == 0;
+    if constexpr (!OUT_F32) {
+        const int64_t cus = current_device_props().cus;
+        if (k > 0 && tiles > cus && cus >= 8 && tiles < ((int64_t)1 << 31)) {
+            hipLaunchKernelGGL((k_gemm_persist_mx<FA, FB>), dim3((unsigned)(cus / 8 * 8)), dim3(256), 0, st, a, lda,
+                               xa, ld_xa, b, ldb, xb, ld_xb, m, n, k, d, ldd, vec_out);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((k_gemm_mx<FA, FB, OUT_F32>), dim3((unsigned)tiles), dim3(256), 0, st, a, lda, xa, ld_xa, b,
                        ldb, xb, ld_xb, m, n, k, d, ldd, vec_out);
     return hipGetLastError();

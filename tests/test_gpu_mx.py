@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import workloads
-from helpers import SENTINEL, assert_codes_equal, check_guard, dev_bf16, dev_u8, guarded, say
+from helpers import SENTINEL, assert_codes_equal, check_full, check_guard, dev_bf16, dev_u8, guarded, say
 
 pytestmark = pytest.mark.gpu
 
@@ -170,6 +170,20 @@ def test_gemm_mx_parity(fp8, orc, m, n, k, fa, fb, out_f32):
     got = gpu_gemm_mx(fp8, a, fa, sa, b, fb, sb, out_f32)
     y, bound = orc.mx_gemm(a, fa, sa, b, fb, sb)
     assert_within(orc, got, y, bound, not out_f32, f"mx gemm {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k,fa,fb", [(2350, 8100, 512, 0, 0), (4352, 4200, 256, 1, 0)])
+def test_gemm_mx_persistent_parity(fp8, orc, m, n, k, fa, fb):
+    """More 256 x 256 tiles than CUs with bf16 output: the persistent MX kernel
+    (each workgroup walks several tiles, loading the next tile's first two K
+    steps and scale records during the current tile's last two); ragged edges
+    (shifted-back edge tiles), k = 256 (one step pair, which is also the
+    last), every output against the oracle."""
+    a, sa = mx_operands(orc, m, k, fa, seed=m + 3 * k)
+    b, sb = mx_operands(orc, n, k, fb, seed=n + 5 * k)
+    say("gemm mx persistent", m, n, k, fa, fb)
+    got = gpu_gemm_mx(fp8, a, fa, sa, b, fb, sb)
+    check_full(orc, got, orc.mx_gemm_by_rows(a, fa, sa, b, fb, sb), f"mx persistent {m}x{n}x{k}")
 
 
 def test_gemm_mx_random_codes_and_scales(fp8, orc):
