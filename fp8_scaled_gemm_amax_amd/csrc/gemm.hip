@@ -596,7 +596,9 @@ __device__ __forceinline__ int k128_frag(int f) { return f == 0 ? 0 : (f <= 4 ? 
 // A step's MFMAs thus never wait for LDS reads issued after the barrier, and
 // the loads have a full step to land. With issue false (uniform) a LOADS step
 // skips its loads: the same code, so a K loop whose last pair loads nothing
-// needs no second copy of the steps.
+// needs no second copy of the steps. With ZERO the first 16 MFMAs start from
+// zero instead of acc (a tile's first step: no zeroing pass). SADDR: the loads
+// take the SGPR-base form (a, b wave-uniform bases, aoff / boff lane offsets).
 template <int FA, int FB, int CUR, bool NEXT, bool LOADS, bool MX, bool SADDR = false, bool ZERO = false>
 __device__ __forceinline__ void k128_step(uint8_t* smem, v16f (&acc)[4][4], v8i (&f0)[8], u32x4 (&sx)[2],
                                           const uint8_t* a, const uint32_t (&aoff)[8], const uint8_t* b,
