@@ -1272,18 +1272,30 @@ __device__ __forceinline__ void tile_coords32(uint32_t bid, uint32_t tiles_m, ui
     *pn = u / gsize;
 }
 
+// A 256 x 128 half tile of the persistent order (defined with the half-tile
+// step below).
+template <int FA, int FB, bool UNI>
+__device__ __forceinline__ void half_tile(uint8_t* smem, const uint8_t* __restrict__ a, int64_t lda,
+                                          const uint8_t* __restrict__ b, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                                          const float* __restrict__ sa, int sa_vec, const float* __restrict__ sb,
+                                          int sb_vec, void* __restrict__ d, int64_t ldd, int vec_out, int64_t first,
+                                          int64_t hid);
+
 // UNI: both scales scalar (one scale pair for the whole product), applied as
-// the single factor sa * sb.
+// the single factor sa * sb. After its tile_limit whole tiles (the same number
+// for every workgroup) workgroup w < tail_halves takes half w of the remaining
+// tiles (a last round of at most half the workgroups runs as twice as many
+// 256 x 128 halves, so 2 rem CUs instead of rem finish it).
 template <int FA, int FB, bool OUT_F32, bool UNI>
 __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restrict__ a, int64_t lda,
                                                          const uint8_t* __restrict__ b, int64_t ldb, int64_t m,
                                                          int64_t n, int64_t k, const float* __restrict__ sa,
                                                          int sa_vec, const float* __restrict__ sb, int sb_vec,
                                                          void* __restrict__ d, int64_t ldd, int vec_out,
-                                                         int64_t tile_limit) {
+                                                         int64_t tile_limit, int64_t tail_halves) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[persist::kSmem];
     const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
-    // tiles 0 .. tile_limit-1 of the order (the rest, if any, go to k_gemm_half)
+    // tiles 0 .. tile_limit-1 of the order whole (the rest, if any, as halves at the end)
     const int64_t nt = tile_limit, G = gridDim.x;
     const int t = threadIdx.x;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1381,6 +1393,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restri
         issue_scales(row0, col0);                        // (landed by the next tile's first mid-step wait)
     }
     wait_vmcnt<0>();
+    // the tail: tiles tile_limit .. as 256 x 128 halves, one per workgroup
+    // (every workgroup has walked the same number of whole tiles)
+    if constexpr (!OUT_F32) {
+        if ((int64_t)blockIdx.x < tail_halves) {
+            __syncthreads();                             // the stages and the scale area are free
+            half_tile<FA, FB, UNI>(smem, a, lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out,
+                                   tile_limit, blockIdx.x);
+        }
+    }
 }
 
 // Persistent MX product (bf16 output, k >= 256, more tiles than CUs): the
@@ -1907,8 +1928,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_ragged_k_persist(
 
 // Half tiles (256 x 128) for the last, partial round of the persistent dense
 // product: when the tiles left after the full rounds are at most half a round,
-// they run as twice as many 256 x 128 halves on a second launch instead of
-// leaving most CUs idle while a few finish them. Four wavefronts, each owning
+// they run as twice as many 256 x 128 halves at the end of the persistent
+// kernel (half_tile) instead of leaving most CUs idle while a few finish them. Four wavefronts, each owning
 // 128 x 64 outputs (4 x 2 blocks of 32 x 32); the K128 step of the large-tile
 // kernels with 8 MFMAs per K half per wavefront and B's 128 rows in a 16 KB
 // operand; each wavefront stages its results through LDS one 32-row chunk at a
@@ -1922,6 +1943,7 @@ constexpr int kChunkOff = kScaleOff + (BM + BN) * 4;
 constexpr int kChunk = 32 * 64 * 2;               // a wavefront's staged 32 x 64 bf16 chunk
 constexpr int kSmem = kChunkOff + 4 * kChunk;     // 113.5 KB
 }  // namespace t128
+static_assert(t128::kSmem <= persist::kSmem, "the half tiles run in the persistent kernel's LDS");
 
 // Fragment rows of the 256 x 128 tile: j < 4: A block j of the wavefront's
 // 128 rows; j = 4, 5: B block j - 4 of its 64 columns (rows of B).
@@ -2088,17 +2110,19 @@ __device__ __forceinline__ void t128_chunk(uint8_t* smem, v16f (&acc)[4][2], con
 // One 256 x 128 half of tile `first + blockIdx.x / 2` in k_gemm_persist's
 // order: the tile's rows and columns as that kernel would take them (edge
 // tiles shifted back), the half's 128 columns from col0 + 128 (blockIdx.x % 2).
+// Half hid of the tile `first + hid / 2` of the persistent order (half
+// hid % 2: its first or last 128 columns), with t128::kSmem bytes of LDS at
+// smem; every branch is uniform over the workgroup.
 template <int FA, int FB, bool UNI>
-__global__ __launch_bounds__(256, 1) void k_gemm_half(const uint8_t* __restrict__ a, int64_t lda,
-                                                      const uint8_t* __restrict__ b, int64_t ldb, int64_t m, int64_t n,
-                                                      int64_t k, const float* __restrict__ sa, int sa_vec,
-                                                      const float* __restrict__ sb, int sb_vec, void* __restrict__ d,
-                                                      int64_t ldd, int vec_out, int64_t first) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[t128::kSmem];
+__device__ __forceinline__ void half_tile(uint8_t* smem, const uint8_t* __restrict__ a, int64_t lda,
+                                          const uint8_t* __restrict__ b, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                                          const float* __restrict__ sa, int sa_vec, const float* __restrict__ sb,
+                                          int sb_vec, void* __restrict__ d, int64_t ldd, int vec_out, int64_t first,
+                                          int64_t hid) {
     const int64_t tiles_m = (m + big::BM - 1) / big::BM, tiles_n = (n + big::BN - 1) / big::BN;
     int64_t pm, pn;
-    tile_coords32((uint32_t)(first + blockIdx.x / 2), (uint32_t)tiles_m, (uint32_t)tiles_n, &pm, &pn);
-    const int hsel = blockIdx.x & 1;
+    tile_coords32((uint32_t)(first + hid / 2), (uint32_t)tiles_m, (uint32_t)tiles_n, &pm, &pn);
+    const int hsel = (int)(hid & 1);
     const int64_t r = pm * big::BM, c = pn * big::BN;
     const int64_t row0 = (r + big::BM > m && m >= big::BM) ? m - big::BM : r;
     const int64_t col0 = (c + big::BN > n && n >= big::BN) ? n - big::BN : c;
@@ -2183,22 +2207,14 @@ hipError_t gemm_typed(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t l
                 // a last round of at most half the workgroups runs as twice as many 256 x 128 halves
                 const int64_t grid = cus / 8 * 8, rem = big_tiles % grid;
                 const int64_t limit = (rem > 0 && 2 * rem <= grid) ? big_tiles - rem : big_tiles;
-                // scalar scales take the kernels' one-factor epilogue
-                const bool uni = !sa_vec && !sb_vec;
-                if (uni)
+                // scalar scales take the kernel's one-factor epilogue
+                const int64_t halves = limit < big_tiles ? 2 * rem : 0;
+                if (!sa_vec && !sb_vec)
                     hipLaunchKernelGGL((k_gemm_persist<FA, FB, false, true>), dim3((unsigned)grid), dim3(256), 0, st, a,
-                                       lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
+                                       lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit, halves);
                 else
                     hipLaunchKernelGGL((k_gemm_persist<FA, FB, false, false>), dim3((unsigned)grid), dim3(256), 0, st, a,
-                                       lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
-                hipError_t e = hipGetLastError();
-                if (e != hipSuccess || limit == big_tiles) return e;
-                if (uni)
-                    hipLaunchKernelGGL((k_gemm_half<FA, FB, true>), dim3((unsigned)(2 * rem)), dim3(256), 0, st, a, lda,
-                                       b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
-                else
-                    hipLaunchKernelGGL((k_gemm_half<FA, FB, false>), dim3((unsigned)(2 * rem)), dim3(256), 0, st, a,
-                                       lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit);
+                                       lda, b, ldb, m, n, k, sa, sa_vec, sb, sb_vec, d, ldd, vec_out, limit, halves);
                 return hipGetLastError();
             }
         }
