@@ -1138,7 +1138,7 @@ constexpr int kSmem = big::kSmem + 4 * kChunk;       // 146 KB
 // stores rows row0 + [row_lo, row_hi) and columns col0 + [col_lo, col_hi),
 // d = acc * sa_row * sb_col with the tile's 256 row and 256 column scales in
 // the scale area; the stages are untouched.
-template <bool OUT_F32, bool UNI = false, int EPI = persist::kEpiOff>
+template <bool OUT_F32, bool UNI = false, int EPI = persist::kEpiOff, bool ONE = false>
 __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4], void* __restrict__ d, int64_t ldd,
                                                int64_t row0, int row_lo, int row_hi, int64_t col0, int col_lo,
                                                int col_hi, int vec_out) {
@@ -1200,7 +1200,10 @@ __device__ __forceinline__ void chunk_epilogue(uint8_t* smem, v16f (&acc)[4][4],
                 for (int ni = 0; ni < 4; ++ni) {
                     const int r = 4 * q;
                     v2f v01, v23;
-                    if constexpr (UNI) {
+                    if constexpr (ONE) {                 // the scales are 1 (MX: applied in the MFMAs)
+                        v01 = v2f{acc[mi][ni][r], acc[mi][ni][r + 1]};
+                        v23 = v2f{acc[mi][ni][r + 2], acc[mi][ni][r + 3]};
+                    } else if constexpr (UNI) {
                         v01 = v2f{acc[mi][ni][r] * sab, acc[mi][ni][r + 1] * sab};
                         v23 = v2f{acc[mi][ni][r + 2] * sab, acc[mi][ni][r + 3] * sab};
                     } else {
@@ -1408,9 +1411,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_persist(const uint8_t* __restri
 // tiles of k_gemm_mx taken as k_gemm_persist takes dense ones (the next tile's
 // first two K steps, with their scale records, load during the current tile's
 // last two; edge tiles shifted back). The block scales are applied inside the
-// MFMAs, so the epilogue's scale area holds ones. LDS: the stages, the unit
-// scale area and the two record stages of k_gemm_mx, then the chunk epilogue's
-// area.
+// MFMAs, so the epilogue stores the sums as they are (ONE). LDS: the stages,
+// the (unit) scale area and the two record stages of k_gemm_mx, then the chunk
+// epilogue's area.
 namespace persist_mx {
 constexpr int kEpiOff = big::kSmemMx;
 constexpr int kSmem = big::kSmemMx + 4 * persist::kChunk;   // 150 KB
@@ -1528,7 +1531,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_persist_mx(const uint8_t* __res
         xat = nxat;
         xbt = nxbt;
         const int64_t rhi = m - crow0, chi = n - ccol0;
-        chunk_epilogue<false, true, persist_mx::kEpiOff>(smem, acc, d, ldd, crow0, crow_lo,
+        chunk_epilogue<false, true, persist_mx::kEpiOff, true>(smem, acc, d, ldd, crow0, crow_lo,
                                                          (int)(rhi < 256 ? rhi : 256), ccol0, ccol_lo,
                                                          (int)(chi < 256 ? chi : 256), vec_out && ccol0 % 8 == 0);
         if (nid >= nt) break;
