@@ -214,6 +214,20 @@ def test_gemm_parity_persistent_scalar_scales(fp8, orc, shape, fa, fb):
     assert_within(orc, got, y, bound, True, f"scalar scales {shape}")
 
 
+def test_gemm_persistent_whole_last_round(fp8, orc):
+    """450 tiles of 256 x 256: one round of 256 and a last round of 194 tiles,
+    more than half the workgroups, so it runs as whole tiles (no half-tile
+    tail); every output against the oracle."""
+    m, n, k = 4608, 6400, 256
+    a, sa = operands(orc, m, k, 0, seed=41)
+    b, sb = operands(orc, n, k, 0, seed=42)
+    say("gemm persistent whole last round", (m, n, k))
+    d = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+    fp8.fp8_gemm_scaled(dev_u8(a), 0, dev_u8(b), 0, dev_f32(sa), 1, dev_f32(sb), 1, d)
+    torch.cuda.synchronize()
+    check_full(orc, d, orc.gemm_by_rows(a, 0, b, 0, sa, sb), f"whole last round {(m, n, k)}")
+
+
 @pytest.mark.parametrize("fa,fb", [(1, 0), (0, 0)])
 def test_gemm_full_output_long_k(fp8, orc, fa, fb):
     """K = 14336 (the Llama3-8B backward's dgrad contraction) on 17 x 16 tiles of
